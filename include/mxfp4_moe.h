@@ -1,0 +1,191 @@
+/*
+ * mxfp4_moe.h -- C ABI of the MI355X (gfx950) MXFP4 mixture-of-experts
+ * expert block: forward and activation-gradient (dX) backward over frozen
+ * expert weights that stay packed as MXFP4.
+ *
+ * Sources (cited by page title and section):
+ *  [P1] "Add MXFP4 training support via a dequantize-on-the-fly fallback"
+ *       (huggingface/transformers pull request 47464), "What this does",
+ *       "Why (the silent-gradient trap)", "Relation to the backward triton
+ *       kernels": the expert block (top-k router, GPT-OSS expert loop),
+ *       packed weights never modified, gradients needed only for the inputs
+ *       and the adapters of a frozen base.
+ *  [P3] "Integrate finegrained kernels: SOTA performance and per-module
+ *       quantization" (pull request 49658), commit notes: gate|up rows
+ *       interleaved (gate j at row 2j, up j at 2j+1) and split stride-2 by
+ *       the fused GLU epilogue; a per-expert bias operand in both GEMMs,
+ *       passed as null when absent; the routing-weighted reduce; row-wise
+ *       MXFP4 quantizers with UE8M0 scales, one launch per tensor; guards
+ *       that refuse (rather than re-permute or fall back) before a launch.
+ *  [OCP] OCP Microscaling Formats (MX) v1.0: E2M1 elements, E8M0 scales.
+ *
+ * Conventions for every entry point
+ *  - All tensors are dense, row-major (last dimension contiguous), in
+ *    device memory owned by the caller.  The library allocates no device
+ *    memory; scratch comes in through `workspace`.
+ *  - bf16 tensors are passed as uint16_t bit patterns.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Work is
+ *    enqueued on it asynchronously with no host synchronisation, so calls
+ *    can be captured into a HIP graph.
+ *  - All validation happens on the host before anything is enqueued; on a
+ *    non-zero return nothing was enqueued (except MXFP4_EHIP, which reports
+ *    a failed launch) and mxfp4_last_error() describes the problem.
+ *  - Calls that share a workspace must be ordered on one stream.
+ */
+#ifndef MXFP4_MOE_H
+#define MXFP4_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+#define MXFP4_OK 0
+#define MXFP4_EINVAL (-1)       /* null required pointer or a count < 1 */
+#define MXFP4_EUNSUPPORTED (-2) /* a shape or option outside the contract */
+#define MXFP4_EWORKSPACE (-3)   /* workspace smaller than the query says */
+#define MXFP4_EHIP (-4)         /* a HIP call or launch failed */
+
+/* Layer shape and activation constants.
+ *  T tokens, H hidden, I intermediate, E experts, k experts per token.
+ *  Requirements: T >= 1; H % 64 == 0 and I % 64 == 0 (whole 32-element
+ *  scale blocks, [P3] group-32 guard, in 64-element K steps);
+ *  1 <= k <= min(E, 8); E <= 256; T * k < 2^31; lora_rank in {0, 16}.
+ *  swiglu_alpha, swiglu_limit: the clamped SwiGLU constants (GPT-OSS uses
+ *  1.702 and 7).  lora_scale multiplies the LoRA delta (1.0 when
+ *  lora_alpha equals the rank). */
+typedef struct mxfp4_moe_dims {
+  int64_t T;
+  int64_t H;
+  int64_t I;
+  int32_t E;
+  int32_t k;
+  float swiglu_alpha;
+  float swiglu_limit;
+  int32_t lora_rank;
+  float lora_scale;
+} mxfp4_moe_dims;
+
+/* Frozen layer parameters ([P3] MXFP4 layout; weights never written).
+ *  router_w  fp32 [E, H];    router_b fp32 [E] or NULL (zero bias)
+ *  gu_codes  uint8 [E, 2I, H/2]  two E2M1 codes per byte, element 2m in
+ *            the low nibble; rows interleaved gate/up ([P3]): gate j at
+ *            row 2j, up j at row 2j+1.  A stacked [gate; up] tensor is NOT
+ *            detected (the bytes cannot tell) and gives wrong results.
+ *  gu_scales uint8 [E, 2I, H/32] UE8M0, value 2^(s-127); s = 255 is NaN
+ *  gu_bias   bf16 [E, 2I] (same interleaved row order) or NULL
+ *  dn_codes  uint8 [E, H, I/2];  dn_scales uint8 [E, H, I/32]
+ *  dn_bias   bf16 [E, H] or NULL
+ *  lora_A    bf16 [E, r, I] and lora_B bf16 [E, H, r]: per-expert LoRA on
+ *            the down projection, y += scale * (a A_e^T) B_e^T; both NULL
+ *            when lora_rank == 0, both required otherwise. */
+typedef struct mxfp4_moe_weights {
+  const float* router_w;
+  const float* router_b;
+  const uint8_t* gu_codes;
+  const uint8_t* gu_scales;
+  const uint16_t* gu_bias;
+  const uint8_t* dn_codes;
+  const uint8_t* dn_scales;
+  const uint16_t* dn_bias;
+  const uint16_t* lora_A;
+  const uint16_t* lora_B;
+} mxfp4_moe_weights;
+
+/* State the forward saves for the backward (caller-owned device buffers,
+ * R = T * k routed rows, flat row f = t * k + j for token t, slot j).
+ *  topk_idx       int32 [T, k]   selected experts, logit descending, ties
+ *                                to the lower index
+ *  topk_w         fp32  [T, k]   softmax over the k selected logits
+ *  expert_offsets int32 [E + 1]  exclusive prefix sum of the expert
+ *                                histogram; offsets[E] = R
+ *  sorted_rows    int32 [R]      flat rows grouped by expert, ascending f
+ *                                within an expert (stable)
+ *  h              bf16  [R, 2I]  gate_up output incl. bias, sorted order
+ *  a              bf16  [R, I]   SwiGLU output, sorted order
+ *  lora_v         bf16  [R, r]   a A_e^T (sorted order); required iff
+ *                                lora_rank > 0, else NULL */
+typedef struct mxfp4_moe_saved {
+  int32_t* topk_idx;
+  float* topk_w;
+  int32_t* expert_offsets;
+  int32_t* sorted_rows;
+  uint16_t* h;
+  uint16_t* a;
+  uint16_t* lora_v;
+} mxfp4_moe_saved;
+
+/* Workspace modes for mxfp4_moe_workspace_bytes. */
+#define MXFP4_WS_FORWARD 0        /* mxfp4_moe_forward, saved == NULL */
+#define MXFP4_WS_FORWARD_SAVED 1  /* mxfp4_moe_forward, saved != NULL */
+#define MXFP4_WS_BACKWARD 2       /* mxfp4_moe_backward_dx */
+
+/* Bytes of device workspace an entry point needs for these dims (0 if
+ * the dims are invalid; mxfp4_last_error() then says why).  The workspace
+ * must be 256-byte aligned. */
+size_t mxfp4_moe_workspace_bytes(const mxfp4_moe_dims* dims, int mode);
+
+/* Expert-block forward ([P1] "What this does": top-k router, then the
+ * GPT-OSS expert math; [P3] fused bias + stride-2 GLU epilogue and the
+ * routing-weighted reduce):
+ *   logits l[t,e] = sum_h x[t,h] Wr[e,h] + br[e]  (products summed in fp64,
+ *                   rounded once to fp32 before the top-k decision)
+ *   top-k experts, softmax over the k selected logits -> w[t,j]
+ *   h = x Wgu_e^T + bgu_e;  a = min(g,L) sig(alpha min(g,L)) (clamp(u,-L,L)+1)
+ *       with g = h[2i], u = h[2i+1]
+ *   y = a Wd_e^T + bd_e (+ lora_scale (a A_e^T) B_e^T)
+ *   out[t] = sum_j w[t,j] y_(t,j)   (fp32 sum in slot order, then bf16)
+ * x bf16 [T, H] in; out bf16 [T, H] out.  saved may be NULL (inference);
+ * otherwise every buffer it names is written. */
+int mxfp4_moe_forward(const mxfp4_moe_dims* dims, const mxfp4_moe_weights* w,
+                      const uint16_t* x, uint16_t* out, const mxfp4_moe_saved* saved,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Activation-gradient backward of the expert block for the loss
+ * sum(dY * out), base weights and biases frozen ([P1]: LoRA training needs
+ * gradients only for the inputs and the adapters):
+ *   per routed row f = (t, j), expert e:
+ *     dw_f = dY_t . y_f;   da = w_f dY_t Wd_e (+ LoRA: dv = s w_f dY_t B_e,
+ *     da += dv A_e);  (dg, du) = SwiGLU'(h) * da (no gradient through a
+ *     clamped input beyond its bound);  dx_f = dh Wgu_e
+ *   router: dl_j = w_j (dw_j - sum_i w_i dw_i)
+ *   dX[t] = sum_j dx_(t,j) + sum_j dl_j Wr[idx_j]          (bf16 out)
+ *   dA_e = sum_f dv_f^T a_f  [E, r, I];  dB_e = s sum_f (w_f dY_t)^T v_f
+ *   [E, H, r]; both fp32, overwritten, required iff lora_rank > 0.
+ * saved: the buffers a forward with the same dims, weights and x filled.
+ * dy bf16 [T, H] in; dx bf16 [T, H] out. */
+int mxfp4_moe_backward_dx(const mxfp4_moe_dims* dims, const mxfp4_moe_weights* w,
+                          const mxfp4_moe_saved* saved, const uint16_t* dy, uint16_t* dx,
+                          float* dA, float* dB, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/* Row-wise MXFP4 quantisation, one launch ([P3] note on the row-wise
+ * quantizers).  w fp32 [rows, K] -> codes uint8 [rows, K/2] (low nibble =
+ * even element), scales uint8 [rows, K/32].  Per 32-block: e = the smallest
+ * integer with 6 * 2^e >= max|x| (= ceil(log2(amax/6))), clamped to
+ * [-127, 127] (amax = 0 gives -127); scale byte e + 127; code = nearest
+ * E2M1 value to x / 2^e, ties to the even code, sign kept (so -0.0 and
+ * small negatives give code 8).  K % 32 == 0.  NaN/Inf inputs are outside
+ * the contract. */
+int mxfp4_quantize(const float* w, int64_t rows, int64_t K, uint8_t* codes, uint8_t* scales,
+                   void* stream);
+
+/* Dequantisation (the decode used inside every GEMM, exported for tests):
+ * out[n, k] = e2m1(code) * 2^(scale - 127), exactly (every such value is a
+ * float32, and a bf16 when finite; [P3] note that dequantisation is
+ * bit-reproducible).  out_dtype 0 = fp32, 1 = bf16.  K % 32 == 0.
+ * Scale byte 255 gives a NaN. */
+int mxfp4_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t K,
+                     int out_dtype, void* out, void* stream);
+
+/* Message for the last non-zero return on this thread ("" if none). */
+const char* mxfp4_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXFP4_MOE_H */

@@ -1,0 +1,268 @@
+// C ABI of the MXFP4 MoE expert block: host-side validation, workspace
+// layout and launch sequencing.  Declarations and the contract live in
+// include/mxfp4_moe.h.  Every check runs before the first enqueue, so an
+// invalid call leaves the stream untouched ("Integrate finegrained kernels
+// ...": guards refuse before the kernel is reached rather than fall back).
+#include "mxfp4_moe.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return MXFP4_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+constexpr size_t ALIGN = 256;
+size_t up(size_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
+
+struct Layout {
+  // offsets into the workspace; SIZE_MAX = not placed
+  size_t topk_idx = SIZE_MAX, topk_w = SIZE_MAX, offsets = SIZE_MAX, sorted_rows = SIZE_MAX,
+         a = SIZE_MAX, blk_hist = SIZE_MAX, tiles = SIZE_MAX, num_tiles = SIZE_MAX,
+         y_w = SIZE_MAX, dh = SIZE_MAX, dw_part = SIZE_MAX, dxr = SIZE_MAX;
+  size_t total = 0;
+  size_t put(size_t bytes) {
+    size_t at = total;
+    total += up(bytes);
+    return at;
+  }
+};
+
+int check_dims(const mxfp4_moe_dims* d) {
+  if (!d) return fail(MXFP4_EINVAL, "dims is NULL");
+  if (d->T < 1 || d->H < 1 || d->I < 1 || d->E < 1 || d->k < 1)
+    return fail(MXFP4_EINVAL, "T, H, I, E and k must be >= 1 (T=%lld H=%lld I=%lld E=%d k=%d)",
+                (long long)d->T, (long long)d->H, (long long)d->I, d->E, d->k);
+  if (d->H % 64 || d->I % 64)
+    return fail(MXFP4_EUNSUPPORTED, "H and I must be multiples of 64 (H=%lld I=%lld)",
+                (long long)d->H, (long long)d->I);
+  if (d->E > 256) return fail(MXFP4_EUNSUPPORTED, "E=%d > 256", d->E);
+  if (d->k > d->E || d->k > 8) return fail(MXFP4_EUNSUPPORTED, "k=%d must be <= min(E, 8)", d->k);
+  if (d->T * d->k >= (int64_t(1) << 31))
+    return fail(MXFP4_EUNSUPPORTED, "T*k = %lld routed rows exceed int32", (long long)(d->T * d->k));
+  if (d->H > (int64_t(1) << 20) || d->I > (int64_t(1) << 20))
+    return fail(MXFP4_EUNSUPPORTED, "H and I must be <= 2^20");
+  if (d->lora_rank != 0)
+    return fail(MXFP4_EUNSUPPORTED, "lora_rank=%d: only 0 is supported by this build",
+                d->lora_rank);
+  return MXFP4_OK;
+}
+
+Layout layout(const mxfp4_moe_dims& d, int mode) {
+  Layout L;
+  const size_t R = (size_t)(d.T * d.k);
+  const int maxt = mxmoe::max_tiles((int64_t)R, d.E);
+  if (mode == MXFP4_WS_FORWARD || mode == MXFP4_WS_FORWARD_SAVED) {
+    if (mode == MXFP4_WS_FORWARD) {
+      L.topk_idx = L.put(R * 4);
+      L.topk_w = L.put(R * 4);
+      L.offsets = L.put((size_t)(d.E + 1) * 4);
+      L.sorted_rows = L.put(R * 4);
+      L.a = L.put(R * (size_t)d.I * 2);
+    }
+    L.blk_hist = L.put((size_t)mxmoe::router_blocks(d.T) * d.E * 4);
+    L.tiles = L.put((size_t)maxt * sizeof(mxmoe::Tile));
+    L.num_tiles = L.put(4);
+    L.y_w = L.put(R * (size_t)d.H * 4);
+  } else {
+    L.tiles = L.put((size_t)maxt * sizeof(mxmoe::Tile));
+    L.num_tiles = L.put(4);
+    L.dh = L.put(R * (size_t)d.I * 2 * 2);
+    L.dw_part = L.put(R * (size_t)mxmoe::bwd_down_ntiles((int)d.I) * 4);
+    L.dxr = L.put(R * (size_t)d.H * 4);
+  }
+  return L;
+}
+
+template <class T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+int check_weights(const mxfp4_moe_weights* w) {
+  if (!w) return fail(MXFP4_EINVAL, "weights is NULL");
+  if (!w->router_w || !w->gu_codes || !w->gu_scales || !w->dn_codes || !w->dn_scales)
+    return fail(MXFP4_EINVAL, "router_w, gu_codes, gu_scales, dn_codes and dn_scales are required");
+  if (!aligned(w->router_w, 16) || !aligned(w->gu_codes, 16) || !aligned(w->dn_codes, 16))
+    return fail(MXFP4_EINVAL, "router_w, gu_codes and dn_codes must be 16-byte aligned");
+  if ((w->gu_bias && !aligned(w->gu_bias, 2)) || (w->dn_bias && !aligned(w->dn_bias, 2)))
+    return fail(MXFP4_EINVAL, "biases must be 2-byte aligned");
+  return MXFP4_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(MXFP4_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return MXFP4_OK;
+}
+
+#define LAUNCH(call, name)                          \
+  do {                                              \
+    int rc_ = hip_status((call), name);             \
+    if (rc_ != MXFP4_OK) return rc_;                \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* mxfp4_last_error(void) { return g_err; }
+
+size_t mxfp4_moe_workspace_bytes(const mxfp4_moe_dims* dims, int mode) {
+  if (check_dims(dims) != MXFP4_OK) return 0;
+  if (mode < MXFP4_WS_FORWARD || mode > MXFP4_WS_BACKWARD) {
+    fail(MXFP4_EINVAL, "unknown workspace mode %d", mode);
+    return 0;
+  }
+  ok();
+  return layout(*dims, mode).total;
+}
+
+int mxfp4_moe_forward(const mxfp4_moe_dims* dims, const mxfp4_moe_weights* w, const uint16_t* x,
+                      uint16_t* out, const mxfp4_moe_saved* saved, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  rc = check_weights(w);
+  if (rc) return rc;
+  const mxfp4_moe_dims& d = *dims;
+  if (!x || !out) return fail(MXFP4_EINVAL, "x and out are required");
+  if (!aligned(x, 16) || !aligned(out, 16)) return fail(MXFP4_EINVAL, "x and out must be 16-byte aligned");
+  if (saved) {
+    if (!saved->topk_idx || !saved->topk_w || !saved->expert_offsets || !saved->sorted_rows ||
+        !saved->h || !saved->a)
+      return fail(MXFP4_EINVAL, "saved: topk_idx, topk_w, expert_offsets, sorted_rows, h, a are required");
+    if (!aligned(saved->h, 16) || !aligned(saved->a, 16))
+      return fail(MXFP4_EINVAL, "saved h and a must be 16-byte aligned");
+  }
+  const int mode = saved ? MXFP4_WS_FORWARD_SAVED : MXFP4_WS_FORWARD;
+  const Layout L = layout(d, mode);
+  if (!workspace || workspace_bytes < L.total)
+    return fail(MXFP4_EWORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, L.total);
+  if (!aligned(workspace, ALIGN)) return fail(MXFP4_EINVAL, "workspace must be 256-byte aligned");
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int T = (int)d.T, H = (int)d.H, I = (int)d.I, E = d.E, k = d.k;
+  const int64_t R = d.T * d.k;
+  int32_t* topk_idx = saved ? saved->topk_idx : at<int32_t>(workspace, L.topk_idx);
+  float* topk_w = saved ? saved->topk_w : at<float>(workspace, L.topk_w);
+  int32_t* offsets = saved ? saved->expert_offsets : at<int32_t>(workspace, L.offsets);
+  int32_t* sorted_rows = saved ? saved->sorted_rows : at<int32_t>(workspace, L.sorted_rows);
+  uint16_t* a = saved ? saved->a : at<uint16_t>(workspace, L.a);
+  uint16_t* h = saved ? saved->h : nullptr;
+  int32_t* blk_hist = at<int32_t>(workspace, L.blk_hist);
+  mxmoe::Tile* tiles = at<mxmoe::Tile>(workspace, L.tiles);
+  int32_t* num_tiles = at<int32_t>(workspace, L.num_tiles);
+  float* y_w = at<float>(workspace, L.y_w);
+  const int maxt = mxmoe::max_tiles(R, E);
+
+  LAUNCH(mxmoe::launch_router(x, w->router_w, w->router_b, T, H, E, k, topk_idx, topk_w, blk_hist, s),
+         "router");
+  LAUNCH(mxmoe::launch_scan(blk_hist, mxmoe::router_blocks(T), E, offsets, s), "scan");
+  LAUNCH(mxmoe::launch_scatter(topk_idx, blk_hist, T, k, E, sorted_rows, s), "scatter");
+  LAUNCH(mxmoe::launch_build_tiles(offsets, E, tiles, num_tiles, s), "tiles");
+  LAUNCH(mxmoe::launch_gate_up(x, w->gu_codes, w->gu_scales, w->gu_bias, sorted_rows, tiles,
+                               num_tiles, maxt, H, I, k, d.swiglu_alpha, d.swiglu_limit, h, a, s),
+         "gate_up");
+  LAUNCH(mxmoe::launch_down(a, w->dn_codes, w->dn_scales, w->dn_bias, topk_w, sorted_rows, tiles,
+                            num_tiles, maxt, H, I, y_w, s),
+         "down");
+  LAUNCH(mxmoe::launch_combine(y_w, d.T, H, k, out, s), "combine");
+  return ok();
+}
+
+int mxfp4_moe_backward_dx(const mxfp4_moe_dims* dims, const mxfp4_moe_weights* w,
+                          const mxfp4_moe_saved* saved, const uint16_t* dy, uint16_t* dx,
+                          float* dA, float* dB, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  rc = check_weights(w);
+  if (rc) return rc;
+  const mxfp4_moe_dims& d = *dims;
+  if (!saved || !saved->topk_idx || !saved->topk_w || !saved->expert_offsets ||
+      !saved->sorted_rows || !saved->h || !saved->a)
+    return fail(MXFP4_EINVAL, "saved state with topk_idx, topk_w, expert_offsets, sorted_rows, h, a is required");
+  if (!dy || !dx) return fail(MXFP4_EINVAL, "dy and dx are required");
+  if (!aligned(dy, 16) || !aligned(dx, 16) || !aligned(saved->h, 16) || !aligned(saved->a, 16))
+    return fail(MXFP4_EINVAL, "dy, dx, saved h and a must be 16-byte aligned");
+  (void)dA;
+  (void)dB;
+  const Layout L = layout(d, MXFP4_WS_BACKWARD);
+  if (!workspace || workspace_bytes < L.total)
+    return fail(MXFP4_EWORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, L.total);
+  if (!aligned(workspace, ALIGN)) return fail(MXFP4_EINVAL, "workspace must be 256-byte aligned");
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int H = (int)d.H, I = (int)d.I, E = d.E, k = d.k;
+  const int64_t R = d.T * d.k;
+  mxmoe::Tile* tiles = at<mxmoe::Tile>(workspace, L.tiles);
+  int32_t* num_tiles = at<int32_t>(workspace, L.num_tiles);
+  uint16_t* dh = at<uint16_t>(workspace, L.dh);
+  float* dw_part = at<float>(workspace, L.dw_part);
+  float* dxr = at<float>(workspace, L.dxr);
+  const int maxt = mxmoe::max_tiles(R, E);
+
+  LAUNCH(mxmoe::launch_build_tiles(saved->expert_offsets, E, tiles, num_tiles, s), "tiles");
+  LAUNCH(mxmoe::launch_bwd_down(dy, w->dn_codes, w->dn_scales, saved->topk_w, saved->sorted_rows,
+                                tiles, num_tiles, maxt, saved->h, saved->a, H, I, k,
+                                d.swiglu_alpha, d.swiglu_limit, dh, dw_part, s),
+         "bwd_down");
+  LAUNCH(mxmoe::launch_bwd_gate_up(dh, w->gu_codes, w->gu_scales, saved->sorted_rows, tiles,
+                                   num_tiles, maxt, H, I, dxr, s),
+         "bwd_gate_up");
+  LAUNCH(mxmoe::launch_bwd_combine(dy, dxr, dw_part, mxmoe::bwd_down_ntiles(I), saved->topk_idx,
+                                   saved->topk_w, w->dn_bias, w->router_w, d.T, H, k, dx, s),
+         "bwd_combine");
+  return ok();
+}
+
+int mxfp4_quantize(const float* w, int64_t rows, int64_t K, uint8_t* codes, uint8_t* scales,
+                   void* stream) {
+  if (!w || !codes || !scales) return fail(MXFP4_EINVAL, "w, codes and scales are required");
+  if (rows < 1 || K < 1) return fail(MXFP4_EINVAL, "rows and K must be >= 1");
+  if (K % 32) return fail(MXFP4_EUNSUPPORTED, "K=%lld is not a multiple of 32", (long long)K);
+  if (rows * K / 4 / 256 >= (int64_t(1) << 31)) return fail(MXFP4_EUNSUPPORTED, "tensor too large");
+  if (!aligned(w, 16) || !aligned(codes, 2))
+    return fail(MXFP4_EINVAL, "w must be 16-byte and codes 2-byte aligned");
+  LAUNCH(mxmoe::launch_quantize(w, rows, K, codes, scales, static_cast<hipStream_t>(stream)),
+         "quantize");
+  return ok();
+}
+
+int mxfp4_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t K,
+                     int out_dtype, void* out, void* stream) {
+  if (!codes || !scales || !out) return fail(MXFP4_EINVAL, "codes, scales and out are required");
+  if (rows < 1 || K < 1) return fail(MXFP4_EINVAL, "rows and K must be >= 1");
+  if (K % 32) return fail(MXFP4_EUNSUPPORTED, "K=%lld is not a multiple of 32", (long long)K);
+  if (out_dtype != 0 && out_dtype != 1) return fail(MXFP4_EINVAL, "out_dtype must be 0 or 1");
+  if (rows * K / 8 / 256 >= (int64_t(1) << 31)) return fail(MXFP4_EUNSUPPORTED, "tensor too large");
+  if (!aligned(codes, 4) || !aligned(out, 16))
+    return fail(MXFP4_EINVAL, "codes must be 4-byte and out 16-byte aligned");
+  LAUNCH(mxmoe::launch_dequantize(codes, scales, rows, K, out_dtype, out,
+                                  static_cast<hipStream_t>(stream)),
+         "dequantize");
+  return ok();
+}
+
+}  // extern "C"

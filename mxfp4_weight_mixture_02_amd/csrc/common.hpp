@@ -1,0 +1,97 @@
+// Device-side helpers shared by the gfx950 kernels of the MXFP4 MoE library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxmoe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float((uint32_t)b << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even (inputs are finite).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+// UE8M0 scale byte -> the fp32 operand of the scaled fp4 conversions.  The
+// hardware takes the exponent field of that operand as the E8M0 scale, so
+// the byte goes straight into the exponent bits (byte 0 means 2^-127).
+__device__ __forceinline__ float scale_operand(uint32_t s) {
+  return __uint_as_float(s << 23);
+}
+
+// Eight E2M1 codes (one dword, element 2m in the low nibble of byte m) times
+// 2^(s-127) -> eight bf16, exactly.  The packed result of each conversion
+// is moved as a whole dword: the two bf16 halves are never extracted one by
+// one.
+__device__ __forceinline__ u32x4 dequant8_bf16(uint32_t codes, float scale) {
+  u32x4 r;
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 0));
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 1));
+  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 2));
+  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 3));
+  return r;
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// bf16 bits of a gate (is_up = false) or up pre-activation for the saved
+// state.  Round to nearest even, except that a value the rounding would move
+// across a clamp bound (gate: +limit; up: -limit and +limit) is moved one
+// ulp back to the side its fp32 value is on, so the backward takes the
+// same clamp decisions as the forward did.
+__device__ __forceinline__ uint32_t saved_preact_bf16(float v, float limit, bool is_up) {
+  uint32_t b = f32_to_bf16(v);
+  const float r = bf16_to_f32((uint16_t)b);
+  if ((v > limit) != (r > limit)) b = (v > limit) ? b + 1 : b - 1;         // positive side
+  if (is_up && ((v < -limit) != (r < -limit))) b = (v < -limit) ? b + 1 : b - 1;  // negative
+  return b;
+}
+
+// Clamped SwiGLU of GPT-OSS: gate clamped above, up clamped both sides.
+__device__ __forceinline__ float swiglu(float g, float u, float alpha, float limit) {
+  float gc = fminf(g, limit);
+  float uc = fminf(fmaxf(u, -limit), limit);
+  float sig = 1.0f / (1.0f + expf(-alpha * gc));
+  return gc * sig * (uc + 1.0f);
+}
+
+// d/dg and d/du of swiglu times da; no gradient beyond a clamp bound.
+__device__ __forceinline__ void swiglu_grad(float g, float u, float da, float alpha, float limit,
+                                            float* dg, float* du) {
+  float gc = fminf(g, limit);
+  float uc = fminf(fmaxf(u, -limit), limit);
+  float sig = 1.0f / (1.0f + expf(-alpha * gc));
+  float dgc = da * (uc + 1.0f) * sig * (1.0f + alpha * gc * (1.0f - sig));
+  float duc = da * gc * sig;
+  *dg = (g <= limit) ? dgc : 0.0f;
+  *du = (u >= -limit && u <= limit) ? duc : 0.0f;
+}
+
+// One tile of routed rows of one expert for the grouped GEMMs.
+struct Tile {
+  int32_t expert;
+  int32_t row0;  // first sorted position
+  int32_t rows;  // 1..MT
+  int32_t pad;
+};
+
+constexpr int MT = 128;      // routed rows per GEMM tile
+constexpr int KC = 64;       // K elements per main-loop step
+constexpr int LDS_ROW = 72;  // bf16 per staged row (64 + 8 padding)
+
+}  // namespace mxmoe

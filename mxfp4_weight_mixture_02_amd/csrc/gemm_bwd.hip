@@ -1,0 +1,388 @@
+// Backward (dX) grouped expert GEMMs on gfx950 MFMA, over the same packed
+// MXFP4 weights the forward reads, now contracted over their stored row
+// axis ("Add MXFP4 training support via a dequantize-on-the-fly fallback":
+// the backward of the frozen base only needs input and adapter gradients;
+// the fallback recomputes dequantisation, which here happens once per
+// workgroup tile in LDS).
+//
+// bwd_down:    da_u[p, i] = sum_h dY[t(p), h] * deq(Wd[e, h, i])
+//              epilogue: dw partial sum_i da_u * a, then the SwiGLU backward
+//              with da = w * da_u on the saved h, writing dh interleaved
+//              (dh[2i] = d/dgate, dh[2i+1] = d/dup).
+// bwd_gate_up: dxr[p, h] = sum_n dh[p, n] * deq(Wgu[e, n, h]), written to the
+//              routed row's own slot for an ordered combine.
+// bwd_combine: dX[t] = sum_j dxr[(t,j)] + sum_j dl_j * Wr[idx_j], with the
+//              softmax-over-selected gradient dl_j = w_j (dw_j - sum_i w_i dw_i).
+//
+// Transposed operand.  The MFMA wants 8 consecutive contraction elements
+// per lane, but the packed rows run along the output axis and the UE8M0
+// scales are blocked along it too.  Each thread therefore loads an 8x8
+// block (8 stored rows x one dword of 8 codes), decodes each row with its
+// own scale (one scaled conversion per code pair), transposes the 8x8 bf16
+// block in registers with byte permutes, and writes 8 contraction-ordered
+// 16-byte rows into LDS; the MFMA A-operand is then one 16-byte LDS read.
+// Output tiling and accumulator layout are those of the forward GEMMs.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace mxmoe {
+
+template <int WN>
+struct BwdTile {
+  static constexpr int NTHR = 64 * WN;
+  static constexpr int NT = 64 * WN;         // output columns per workgroup
+  static constexpr int PPT = MT * 8 / NTHR;  // 16-byte B pieces per thread per step
+  static constexpr int OB = NT / 8;          // 8-column blocks across the tile
+};
+
+// Raw codes and scales of one thread's 8x8 block for one K step.
+struct RawBlock {
+  uint32_t code[8];
+  uint32_t scale[8];
+};
+
+__device__ __forceinline__ void load_block(RawBlock& rb, const uint8_t* __restrict__ code0,
+                                           const uint8_t* __restrict__ scale0, int64_t crow,
+                                           int64_t srow, bool live) {
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    rb.code[r] = live ? *reinterpret_cast<const uint32_t*>(code0 + r * crow) : 0u;
+    rb.scale[r] = live ? scale0[r * srow] : 0u;
+  }
+}
+
+// Decode the 8x8 block and store it transposed: dst row o (0..7) gets the
+// 8 contraction-ordered bf16 of output column o.
+__device__ __forceinline__ void store_block_t(const RawBlock& rb, uint16_t* dst_row0) {
+  u32x4 R[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) R[r] = dequant8_bf16(rb.code[r], scale_operand(rb.scale[r]));
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    u32x4 lo, hi;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      lo[m] = __builtin_amdgcn_perm(R[2 * m + 1][j], R[2 * m][j], 0x05040100u);
+      hi[m] = __builtin_amdgcn_perm(R[2 * m + 1][j], R[2 * m][j], 0x07060302u);
+    }
+    *reinterpret_cast<u32x4*>(dst_row0 + (2 * j) * LDS_ROW) = lo;
+    *reinterpret_cast<u32x4*>(dst_row0 + (2 * j + 1) * LDS_ROW) = hi;
+  }
+}
+
+// Main loop shared by the two backward GEMMs.  W is stored [C rows][O
+// cols] (packed along O); this workgroup produces output columns o0.. for
+// routed rows whose contraction vectors are brow[j] (length C).
+template <int WN>
+__device__ __forceinline__ void bwd_mainloop(const uint16_t* const (&brow)[BwdTile<WN>::PPT],
+                                             const uint8_t* __restrict__ wcode,
+                                             const uint8_t* __restrict__ wscale, int C, int O,
+                                             int o0, bool wave_live,
+                                             uint16_t (*ws)[BwdTile<WN>::NT][LDS_ROW],
+                                             uint16_t (*xs)[MT][LDS_ROW], f32x16 (&acc)[2][4]) {
+  using BT = BwdTile<WN>;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hlf = lane >> 5;
+  const int nsteps = C / KC;
+  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+  const int64_t crow = O / 2, srow = O / 32;
+
+  // this thread's 8x8 weight block: rows 8*cb.., output columns 8*ob..
+  const int cb = tid / BT::OB, ob = tid % BT::OB;
+  const int ocol = o0 + 8 * ob;
+  const bool blive = ocol < O;
+  const uint8_t* bcode = wcode + (int64_t)(8 * cb) * crow + ocol / 2;
+  const uint8_t* bscale = wscale + (int64_t)(8 * cb) * srow + ocol / 32;
+  uint16_t* const wdst0 = &ws[0][8 * ob][8 * cb];
+  uint16_t* const wdst1 = &ws[1][8 * ob][8 * cb];
+
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[rb][tb][r] = 0.0f;
+
+  u32x4 xv[BT::PPT];
+  RawBlock raw;
+#pragma unroll
+  for (int j = 0; j < BT::PPT; ++j)
+    xv[j] = brow[j] ? *reinterpret_cast<const u32x4*>(brow[j]) : zero4;
+  load_block(raw, bcode, bscale, crow, srow, blive);
+#pragma unroll
+  for (int j = 0; j < BT::PPT; ++j) {
+    int q = tid + j * BT::NTHR;
+    *reinterpret_cast<u32x4*>(&xs[0][q >> 3][(q & 7) * 8]) = xv[j];
+  }
+  store_block_t(raw, wdst0);
+  __syncthreads();
+
+  for (int c = 0; c < nsteps; ++c) {
+    const int buf = c & 1;
+    const bool more = c + 1 < nsteps;
+    if (more) {
+#pragma unroll
+      for (int j = 0; j < BT::PPT; ++j)
+        xv[j] = brow[j] ? *reinterpret_cast<const u32x4*>(brow[j] + (c + 1) * KC) : zero4;
+      load_block(raw, bcode + (int64_t)(c + 1) * KC * crow, bscale + (int64_t)(c + 1) * KC * srow,
+                 crow, srow, blive);
+    }
+    if (wave_live) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const bf16x8 a0 =
+            *reinterpret_cast<const bf16x8*>(&ws[buf][wave * 64 + l32][hlf * 32 + s * 8]);
+        const bf16x8 a1 =
+            *reinterpret_cast<const bf16x8*>(&ws[buf][wave * 64 + 32 + l32][hlf * 32 + s * 8]);
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+          const bf16x8 b =
+              *reinterpret_cast<const bf16x8*>(&xs[buf][tb * 32 + l32][hlf * 32 + s * 8]);
+          acc[0][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b, acc[0][tb], 0, 0, 0);
+          acc[1][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b, acc[1][tb], 0, 0, 0);
+        }
+      }
+    }
+    if (more) {
+#pragma unroll
+      for (int j = 0; j < BT::PPT; ++j) {
+        int q = tid + j * BT::NTHR;
+        *reinterpret_cast<u32x4*>(&xs[buf ^ 1][q >> 3][(q & 7) * 8]) = xv[j];
+      }
+      store_block_t(raw, buf ? wdst0 : wdst1);
+    }
+    __syncthreads();
+  }
+}
+
+template <int WN>
+__global__ __launch_bounds__(64 * WN) void bwd_down_kernel(
+    const uint16_t* __restrict__ dy, const uint8_t* __restrict__ codes,
+    const uint8_t* __restrict__ scales, const float* __restrict__ topk_w,
+    const int32_t* __restrict__ sorted_rows, const Tile* __restrict__ tiles,
+    const int32_t* __restrict__ num_tiles, const uint16_t* __restrict__ hsv,
+    const uint16_t* __restrict__ asv, int H, int I, int k, float alpha, float limit,
+    uint16_t* __restrict__ dh, float* __restrict__ dw_part) {
+  using BT = BwdTile<WN>;
+  __shared__ __attribute__((aligned(16))) uint16_t ws[2][BT::NT][LDS_ROW];
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2][MT][LDS_ROW];
+  __shared__ float red[WN][MT];
+  if ((int)blockIdx.y >= *num_tiles) return;
+  const Tile tl = tiles[blockIdx.y];
+  const int o0 = blockIdx.x * BT::NT;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hlf = lane >> 5;
+  const int e = tl.expert;
+
+  const uint16_t* brow[BT::PPT];
+#pragma unroll
+  for (int j = 0; j < BT::PPT; ++j) {
+    int q = tid + j * BT::NTHR;
+    int r = q >> 3;
+    if (r < tl.rows) {
+      int f = sorted_rows[tl.row0 + r];
+      brow[j] = dy + (int64_t)(f / k) * H + (q & 7) * 8;
+    } else {
+      brow[j] = nullptr;
+    }
+  }
+  // Wd is stored [H rows][I cols]: contraction over h (C = H), output i (O = I)
+  const bool wave_live = o0 + wave * 64 < I;
+  const uint8_t* wcode = codes + (int64_t)e * H * (I / 2);
+  const uint8_t* wscale = scales + (int64_t)e * H * (I / 32);
+  f32x16 acc[2][4];
+  bwd_mainloop<WN>(brow, wcode, wscale, H, I, o0, wave_live, ws, xs, acc);
+
+  const int N2 = 2 * I;
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb) {
+    const int rt = tb * 32 + l32;
+    float dwp = 0.0f;
+    if (wave_live && rt < tl.rows) {
+      const int64_t p = tl.row0 + rt;
+      const float wf = topk_w[sorted_rows[p]];
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int i4 = o0 + wave * 64 + rb * 32 + 8 * q + 4 * hlf;
+          const u32x2 av = *reinterpret_cast<const u32x2*>(asv + p * I + i4);
+          const u32x4 hv = *reinterpret_cast<const u32x4*>(hsv + p * N2 + 2 * i4);
+          u32x4 out;
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            const float du_ = acc[rb][tb][4 * q + m];
+            const uint32_t aw = av[m >> 1];
+            const float a_m = bf16_to_f32((uint16_t)((m & 1) ? (aw >> 16) : (aw & 0xFFFFu)));
+            dwp += du_ * a_m;
+            const uint32_t hw = hv[m];
+            const float g = bf16_to_f32((uint16_t)(hw & 0xFFFFu));
+            const float u = bf16_to_f32((uint16_t)(hw >> 16));
+            float dg, dup;
+            swiglu_grad(g, u, wf * du_, alpha, limit, &dg, &dup);
+            out[m] = pack_bf16x2(dg, dup);
+          }
+          *reinterpret_cast<u32x4*>(dh + p * N2 + 2 * i4) = out;
+        }
+      }
+    }
+    dwp += __shfl_xor(dwp, 32);
+    if (hlf == 0) red[wave][rt] = dwp;
+  }
+  __syncthreads();
+  if (tid < tl.rows) {
+    float s = 0.0f;
+#pragma unroll
+    for (int w = 0; w < WN; ++w) s += red[w][tid];
+    const int64_t f = sorted_rows[tl.row0 + tid];
+    dw_part[f * gridDim.x + blockIdx.x] = s;
+  }
+}
+
+template <int WN>
+__global__ __launch_bounds__(64 * WN) void bwd_gate_up_kernel(
+    const uint16_t* __restrict__ dh, const uint8_t* __restrict__ codes,
+    const uint8_t* __restrict__ scales, const int32_t* __restrict__ sorted_rows,
+    const Tile* __restrict__ tiles, const int32_t* __restrict__ num_tiles, int H, int I,
+    float* __restrict__ dxr) {
+  using BT = BwdTile<WN>;
+  __shared__ __attribute__((aligned(16))) uint16_t ws[2][BT::NT][LDS_ROW];
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2][MT][LDS_ROW];
+  if ((int)blockIdx.y >= *num_tiles) return;
+  const Tile tl = tiles[blockIdx.y];
+  const int o0 = blockIdx.x * BT::NT;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hlf = lane >> 5;
+  const int e = tl.expert;
+  const int N2 = 2 * I;
+
+  const uint16_t* brow[BT::PPT];
+#pragma unroll
+  for (int j = 0; j < BT::PPT; ++j) {
+    int q = tid + j * BT::NTHR;
+    int r = q >> 3;
+    brow[j] = (r < tl.rows) ? dh + (int64_t)(tl.row0 + r) * N2 + (q & 7) * 8 : nullptr;
+  }
+  // Wgu is stored [2I rows][H cols]: contraction over n (C = 2I), output h (O = H)
+  const bool wave_live = o0 + wave * 64 < H;
+  const uint8_t* wcode = codes + (int64_t)e * N2 * (H / 2);
+  const uint8_t* wscale = scales + (int64_t)e * N2 * (H / 32);
+  f32x16 acc[2][4];
+  bwd_mainloop<WN>(brow, wcode, wscale, N2, H, o0, wave_live, ws, xs, acc);
+  if (!wave_live) return;
+
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb) {
+    const int rt = tb * 32 + l32;
+    if (rt >= tl.rows) continue;
+    const int64_t f = sorted_rows[tl.row0 + rt];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int h4 = o0 + wave * 64 + rb * 32 + 8 * q + 4 * hlf;
+        f32x4 v;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) v[m] = acc[rb][tb][4 * q + m];
+        *reinterpret_cast<f32x4*>(dxr + f * H + h4) = v;
+      }
+  }
+}
+
+// One workgroup (256 threads) per token.
+__global__ __launch_bounds__(256) void bwd_combine_kernel(
+    const uint16_t* __restrict__ dy, const float* __restrict__ dxr,
+    const float* __restrict__ dw_part, int n_dw_part, const int32_t* __restrict__ topk_idx,
+    const float* __restrict__ topk_w, const uint16_t* __restrict__ dn_bias,
+    const float* __restrict__ router_w, int H, int k, uint16_t* __restrict__ dx) {
+  __shared__ float red[4][8];
+  __shared__ float dl[8];
+  __shared__ int32_t ex[8];
+  const int64_t t = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid < k) ex[tid] = topk_idx[t * k + tid];
+  __syncthreads();
+  // dY . bd[e_j] for each slot (the bias part of dw_j = dY . y_j)
+  float part[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) part[j] = 0.0f;
+  if (dn_bias) {
+    for (int h = tid; h < H; h += 256) {
+      const float g = bf16_to_f32(dy[t * H + h]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (j < k) part[j] += g * bf16_to_f32(dn_bias[(int64_t)ex[j] * H + h]);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    float v = part[j];
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    if (lane == 0 && j < k) red[wave][j] = v;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float dw[8], w[8], sw = 0.0f;
+    for (int j = 0; j < k; ++j) {
+      const int64_t f = t * k + j;
+      float s = red[0][j] + red[1][j] + red[2][j] + red[3][j];
+      for (int q = 0; q < n_dw_part; ++q) s += dw_part[f * n_dw_part + q];
+      dw[j] = s;
+      w[j] = topk_w[f];
+      sw += w[j] * s;
+    }
+    for (int j = 0; j < k; ++j) dl[j] = w[j] * (dw[j] - sw);
+  }
+  __syncthreads();
+  const int H4 = H / 4;
+  for (int c = tid; c < H4; c += 256) {
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < k; ++j) {
+      const f32x4 v = reinterpret_cast<const f32x4*>(dxr + (t * k + j) * H)[c];
+      const f32x4 r = reinterpret_cast<const f32x4*>(router_w + (int64_t)ex[j] * H)[c];
+      const float d = dl[j];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) s[m] += v[m] + d * r[m];
+    }
+    u32x2 o = {pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3])};
+    reinterpret_cast<u32x2*>(dx + t * H)[c] = o;
+  }
+}
+
+constexpr int BWD_WN = 4;
+
+int bwd_down_ntiles(int I) { return (I + BwdTile<BWD_WN>::NT - 1) / BwdTile<BWD_WN>::NT; }
+
+hipError_t launch_bwd_down(const uint16_t* dy, const uint8_t* codes, const uint8_t* scales,
+                           const float* topk_w, const int32_t* sorted_rows, const Tile* tiles,
+                           const int32_t* num_tiles, int max_tiles, const uint16_t* h,
+                           const uint16_t* a, int H, int I, int k, float alpha, float limit,
+                           uint16_t* dh, float* dw_part, hipStream_t s) {
+  dim3 grid(bwd_down_ntiles(I), max_tiles);
+  hipLaunchKernelGGL(bwd_down_kernel<BWD_WN>, grid, dim3(64 * BWD_WN), 0, s, dy, codes, scales,
+                     topk_w, sorted_rows, tiles, num_tiles, h, a, H, I, k, alpha, limit, dh,
+                     dw_part);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_gate_up(const uint16_t* dh, const uint8_t* codes, const uint8_t* scales,
+                              const int32_t* sorted_rows, const Tile* tiles,
+                              const int32_t* num_tiles, int max_tiles, int H, int I,
+                              float* dxr, hipStream_t s) {
+  constexpr int NT = BwdTile<BWD_WN>::NT;
+  dim3 grid((H + NT - 1) / NT, max_tiles);
+  hipLaunchKernelGGL(bwd_gate_up_kernel<BWD_WN>, grid, dim3(64 * BWD_WN), 0, s, dh, codes,
+                     scales, sorted_rows, tiles, num_tiles, H, I, dxr);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_combine(const uint16_t* dy, const float* dxr, const float* dw_part,
+                              int n_dw_part, const int32_t* topk_idx, const float* topk_w,
+                              const uint16_t* dn_bias, const float* router_w, int64_t T, int H,
+                              int k, uint16_t* dx, hipStream_t s) {
+  hipLaunchKernelGGL(bwd_combine_kernel, dim3((unsigned)T), dim3(256), 0, s, dy, dxr, dw_part,
+                     n_dw_part, topk_idx, topk_w, dn_bias, router_w, H, k, dx);
+  return hipGetLastError();
+}
+
+}  // namespace mxmoe

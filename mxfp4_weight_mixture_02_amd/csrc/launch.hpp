@@ -1,0 +1,61 @@
+// Host-side launchers of the library's kernels (internal; the public
+// surface is include/mxfp4_moe.h).  Every launcher only enqueues work on
+// `s`; shapes were validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxmoe {
+
+struct Tile;
+
+// quant.hip
+hipError_t launch_quantize(const float* w, int64_t rows, int64_t K, uint8_t* codes,
+                           uint8_t* scales, hipStream_t s);
+hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows,
+                             int64_t K, int out_bf16, void* out, hipStream_t s);
+
+// route.hip
+constexpr int ROUTER_TOKENS = 8;  // tokens per router workgroup
+int router_blocks(int64_t T);
+hipError_t launch_router(const uint16_t* x, const float* wr, const float* br, int T, int H,
+                         int E, int k, int32_t* topk_idx, float* topk_w, int32_t* blk_hist,
+                         hipStream_t s);
+hipError_t launch_scan(int32_t* blk_hist, int nblk, int E, int32_t* offsets, hipStream_t s);
+hipError_t launch_scatter(const int32_t* topk_idx, const int32_t* blk_base, int T, int k, int E,
+                          int32_t* sorted_rows, hipStream_t s);
+int max_tiles(int64_t R, int E);
+hipError_t launch_build_tiles(const int32_t* offsets, int E, Tile* tiles, int32_t* num_tiles,
+                              hipStream_t s);
+
+// gemm_fwd.hip
+hipError_t launch_gate_up(const uint16_t* x, const uint8_t* codes, const uint8_t* scales,
+                          const uint16_t* bias, const int32_t* sorted_rows, const Tile* tiles,
+                          const int32_t* num_tiles, int max_tiles, int H, int I, int k,
+                          float alpha, float limit, uint16_t* h_out, uint16_t* a_out,
+                          hipStream_t s);
+hipError_t launch_down(const uint16_t* a, const uint8_t* codes, const uint8_t* scales,
+                       const uint16_t* bias, const float* topk_w, const int32_t* sorted_rows,
+                       const Tile* tiles, const int32_t* num_tiles, int max_tiles, int H, int I,
+                       float* y_w, hipStream_t s);
+hipError_t launch_combine(const float* y_w, int64_t T, int H, int k, uint16_t* out,
+                          hipStream_t s);
+
+// gemm_bwd.hip
+int bwd_down_ntiles(int I);
+hipError_t launch_bwd_down(const uint16_t* dy, const uint8_t* codes, const uint8_t* scales,
+                           const float* topk_w, const int32_t* sorted_rows, const Tile* tiles,
+                           const int32_t* num_tiles, int max_tiles, const uint16_t* h,
+                           const uint16_t* a, int H, int I, int k, float alpha, float limit,
+                           uint16_t* dh, float* dw_part, hipStream_t s);
+hipError_t launch_bwd_gate_up(const uint16_t* dh, const uint8_t* codes, const uint8_t* scales,
+                              const int32_t* sorted_rows, const Tile* tiles,
+                              const int32_t* num_tiles, int max_tiles, int H, int I,
+                              float* dxr, hipStream_t s);
+hipError_t launch_bwd_combine(const uint16_t* dy, const float* dxr, const float* dw_part,
+                              int n_dw_part, const int32_t* topk_idx, const float* topk_w,
+                              const uint16_t* dn_bias, const float* router_w, int64_t T, int H,
+                              int k, uint16_t* dx, hipStream_t s);
+
+}  // namespace mxmoe

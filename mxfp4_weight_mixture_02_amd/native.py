@@ -1,0 +1,274 @@
+"""ctypes binding of libmxfp4_moe.so (include/mxfp4_moe.h).
+
+Argument marshalling only: every step of the expert block runs in the HIP
+library.  torch provides device memory and the current stream.  There is
+no CPU fallback: if the library is missing or no GPU is present, the calls
+raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from dataclasses import dataclass
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmxfp4_moe.so")
+HEADER = os.path.join(os.path.dirname(_PKG), "include", "mxfp4_moe.h")
+
+MXFP4_OK = 0
+WS_FORWARD, WS_FORWARD_SAVED, WS_BACKWARD = 0, 1, 2
+ERRORS = {-1: "EINVAL", -2: "EUNSUPPORTED", -3: "EWORKSPACE", -4: "EHIP"}
+
+
+class Mxfp4Error(RuntimeError):
+    def __init__(self, fn, code, msg):
+        super().__init__(f"{fn} failed: {ERRORS.get(code, code)}: {msg}")
+        self.code = code
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int64), ("H", ctypes.c_int64), ("I", ctypes.c_int64),
+                ("E", ctypes.c_int32), ("k", ctypes.c_int32),
+                ("swiglu_alpha", ctypes.c_float), ("swiglu_limit", ctypes.c_float),
+                ("lora_rank", ctypes.c_int32), ("lora_scale", ctypes.c_float)]
+
+
+class Weights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("router_w", "router_b", "gu_codes", "gu_scales", "gu_bias",
+                 "dn_codes", "dn_scales", "dn_bias", "lora_A", "lora_B")]
+
+
+class Saved(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("topk_idx", "topk_w", "expert_offsets", "sorted_rows", "h", "a", "lora_v")]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m mxfp4_weight_mixture_02_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        L.mxfp4_last_error.restype = ctypes.c_char_p
+        L.mxfp4_last_error.argtypes = []
+        L.mxfp4_moe_workspace_bytes.restype = ctypes.c_size_t
+        L.mxfp4_moe_workspace_bytes.argtypes = [ctypes.POINTER(Dims), i32]
+        L.mxfp4_moe_forward.restype = i32
+        L.mxfp4_moe_forward.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Weights), vp, vp,
+                                        ctypes.POINTER(Saved), vp, ctypes.c_size_t, vp]
+        L.mxfp4_moe_backward_dx.restype = i32
+        L.mxfp4_moe_backward_dx.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Weights),
+                                            ctypes.POINTER(Saved), vp, vp, vp, vp, vp,
+                                            ctypes.c_size_t, vp]
+        L.mxfp4_quantize.restype = i32
+        L.mxfp4_quantize.argtypes = [vp, i64, i64, vp, vp, vp]
+        L.mxfp4_dequantize.restype = i32
+        L.mxfp4_dequantize.argtypes = [vp, vp, i64, i64, i32, vp, vp]
+        _lib = L
+    return _lib
+
+
+def header_symbols() -> list[str]:
+    """Function names declared in include/mxfp4_moe.h."""
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(mxfp4_\w+)\s*\(", txt, re.M)))
+
+
+def _check(fn, rc):
+    if rc != MXFP4_OK:
+        raise Mxfp4Error(fn, rc, lib().mxfp4_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dev(t, dtype, name):
+    if t is None:
+        return None
+    if not t.is_cuda or t.dtype != dtype or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} CUDA tensor")
+    return t
+
+
+# --------------------------------------------------------------- quantise
+
+def mxfp4_quantize(w: torch.Tensor):
+    """fp32 [..., K] -> (codes uint8 [..., K/2], scales uint8 [..., K/32])."""
+    w = _dev(w, torch.float32, "w")
+    K = w.shape[-1]
+    rows = w.numel() // K
+    codes = torch.empty(w.shape[:-1] + (K // 2,), dtype=torch.uint8, device=w.device)
+    scales = torch.empty(w.shape[:-1] + (K // 32,), dtype=torch.uint8, device=w.device)
+    _check("mxfp4_quantize", lib().mxfp4_quantize(_ptr(w), rows, K, _ptr(codes), _ptr(scales),
+                                                  _stream()))
+    return codes, scales
+
+
+def mxfp4_dequantize(codes: torch.Tensor, scales: torch.Tensor, dtype=torch.float32):
+    codes = _dev(codes, torch.uint8, "codes")
+    scales = _dev(scales, torch.uint8, "scales")
+    K = codes.shape[-1] * 2
+    rows = codes.numel() // codes.shape[-1]
+    out = torch.empty(codes.shape[:-1] + (K,), dtype=dtype, device=codes.device)
+    code = {torch.float32: 0, torch.bfloat16: 1}[dtype]
+    _check("mxfp4_dequantize", lib().mxfp4_dequantize(_ptr(codes), _ptr(scales), rows, K, code,
+                                                      _ptr(out), _stream()))
+    return out
+
+
+# ------------------------------------------------------------- the block
+
+@dataclass
+class MoeLayer:
+    """Device tensors of one layer (layouts as in include/mxfp4_moe.h)."""
+    router_w: torch.Tensor            # fp32 [E, H]
+    router_b: torch.Tensor | None     # fp32 [E]
+    gu_codes: torch.Tensor            # uint8 [E, 2I, H/2]
+    gu_scales: torch.Tensor           # uint8 [E, 2I, H/32]
+    gu_bias: torch.Tensor | None      # bf16 [E, 2I]
+    dn_codes: torch.Tensor            # uint8 [E, H, I/2]
+    dn_scales: torch.Tensor           # uint8 [E, H, I/32]
+    dn_bias: torch.Tensor | None      # bf16 [E, H]
+    k: int
+    alpha: float = 1.702
+    limit: float = 7.0
+    lora_A: torch.Tensor | None = None
+    lora_B: torch.Tensor | None = None
+    lora_scale: float = 1.0
+
+    @property
+    def E(self):
+        return self.gu_codes.shape[0]
+
+    @property
+    def H(self):
+        return self.gu_codes.shape[2] * 2
+
+    @property
+    def I(self):
+        return self.gu_codes.shape[1] // 2
+
+    def dims(self, T):
+        r = 0 if self.lora_A is None else self.lora_A.shape[1]
+        return Dims(T, self.H, self.I, self.E, self.k, self.alpha, self.limit, r, self.lora_scale)
+
+    def weights(self):
+        _dev(self.router_w, torch.float32, "router_w")
+        _dev(self.router_b, torch.float32, "router_b")
+        for n in ("gu_codes", "gu_scales", "dn_codes", "dn_scales"):
+            _dev(getattr(self, n), torch.uint8, n)
+        for n in ("gu_bias", "dn_bias", "lora_A", "lora_B"):
+            _dev(getattr(self, n), torch.bfloat16, n)
+        return Weights(*[_ptr(getattr(self, n)) for n, _ in Weights._fields_])
+
+
+@dataclass
+class SavedState:
+    topk_idx: torch.Tensor       # int32 [T, k]
+    topk_w: torch.Tensor         # fp32 [T, k]
+    expert_offsets: torch.Tensor  # int32 [E + 1]
+    sorted_rows: torch.Tensor    # int32 [T*k]
+    h: torch.Tensor              # bf16 [T*k, 2I]
+    a: torch.Tensor              # bf16 [T*k, I]
+    lora_v: torch.Tensor | None = None
+
+    @staticmethod
+    def empty(layer: MoeLayer, T: int, device):
+        R = T * layer.k
+        r = 0 if layer.lora_A is None else layer.lora_A.shape[1]
+        return SavedState(
+            torch.empty((T, layer.k), dtype=torch.int32, device=device),
+            torch.empty((T, layer.k), dtype=torch.float32, device=device),
+            torch.empty((layer.E + 1,), dtype=torch.int32, device=device),
+            torch.empty((R,), dtype=torch.int32, device=device),
+            torch.empty((R, 2 * layer.I), dtype=torch.bfloat16, device=device),
+            torch.empty((R, layer.I), dtype=torch.bfloat16, device=device),
+            torch.empty((R, r), dtype=torch.bfloat16, device=device) if r else None)
+
+    def struct(self):
+        return Saved(*[_ptr(getattr(self, n)) for n, _ in Saved._fields_])
+
+
+class Workspace:
+    """Grow-only device workspace, reused across calls on one stream."""
+
+    def __init__(self):
+        self.buf = None
+
+    def get(self, nbytes, device):
+        if self.buf is None or self.buf.numel() < nbytes or self.buf.device != device:
+            self.buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        return self.buf
+
+
+_WS = Workspace()
+
+
+def workspace_bytes(layer: MoeLayer, T: int, mode: int) -> int:
+    d = layer.dims(T)
+    n = lib().mxfp4_moe_workspace_bytes(ctypes.byref(d), mode)
+    if n == 0:
+        raise Mxfp4Error("mxfp4_moe_workspace_bytes", -1, lib().mxfp4_last_error().decode())
+    return n
+
+
+def mxfp4_moe_forward(layer: MoeLayer, x: torch.Tensor, saved: SavedState | bool | None = None,
+                      out: torch.Tensor | None = None, workspace: Workspace | None = None):
+    """Expert-block forward.  ``saved=True`` allocates and fills the state
+    the backward needs.  Returns (out, saved)."""
+    x = _dev(x, torch.bfloat16, "x")
+    T = x.shape[0]
+    if saved is True:
+        saved = SavedState.empty(layer, T, x.device)
+    if out is None:
+        out = torch.empty_like(x)
+    mode = WS_FORWARD_SAVED if saved else WS_FORWARD
+    nbytes = workspace_bytes(layer, T, mode)
+    ws = (workspace or _WS).get(nbytes, x.device)
+    d = layer.dims(T)
+    w = layer.weights()
+    sv = saved.struct() if saved else None
+    rc = lib().mxfp4_moe_forward(ctypes.byref(d), ctypes.byref(w), _ptr(x), _ptr(out),
+                                 ctypes.byref(sv) if sv is not None else None,
+                                 _ptr(ws), ws.numel(), _stream())
+    _check("mxfp4_moe_forward", rc)
+    return out, saved
+
+
+def mxfp4_moe_backward_dx(layer: MoeLayer, saved: SavedState, dy: torch.Tensor,
+                          dx: torch.Tensor | None = None, workspace: Workspace | None = None):
+    """dX (and, with LoRA, dA/dB) for the loss sum(dy * out).  Returns
+    (dx, dA, dB)."""
+    dy = _dev(dy, torch.bfloat16, "dy")
+    T = dy.shape[0]
+    if dx is None:
+        dx = torch.empty_like(dy)
+    dA = dB = None
+    if layer.lora_A is not None:
+        dA = torch.empty(layer.lora_A.shape, dtype=torch.float32, device=dy.device)
+        dB = torch.empty(layer.lora_B.shape, dtype=torch.float32, device=dy.device)
+    nbytes = workspace_bytes(layer, T, WS_BACKWARD)
+    ws = (workspace or _WS).get(nbytes, dy.device)
+    d = layer.dims(T)
+    w = layer.weights()
+    sv = saved.struct()
+    rc = lib().mxfp4_moe_backward_dx(ctypes.byref(d), ctypes.byref(w), ctypes.byref(sv),
+                                     _ptr(dy), _ptr(dx), _ptr(dA), _ptr(dB), _ptr(ws),
+                                     ws.numel(), _stream())
+    _check("mxfp4_moe_backward_dx", rc)
+    return dx, dA, dB

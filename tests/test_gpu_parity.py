@@ -1,0 +1,248 @@
+"""GPU parity of the HIP path against the float64 oracle, through the C ABI.
+
+Integers (quantised bytes, dequantised bits, routing indices, expert
+offsets, the permutation) must match bit for bit; floating-point results
+(routing weights, the saved h and a, out, dX) must reach
+max|g - r| / max|r| <= 2e-2 and cosine >= 0.9999 against the oracle.
+Full-size layers compare the routing of every token and the outputs of a
+seeded sample of tokens, whose rows the oracle computes one by one.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import moe_synth as syn
+from mxfp4_weight_mixture_02_amd import (Mxfp4Error, mxfp4_dequantize, mxfp4_moe_backward_dx,
+                                         mxfp4_moe_forward, mxfp4_quantize)
+from oracle import moe, mxfp4
+
+from gpu_helpers import (DEV, assert_close, assert_routing_equal, bf16_tensor, device_layer,
+                         min_topk_gap, oracle_layer, to_f64)
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+# ------------------------------------------------------------ MXFP4 codec
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_dequantize_every_byte_and_scale(dtype):
+    _say(f"dequantize exhaustive {dtype}")
+    codes = np.tile(np.arange(256, dtype=np.uint8), (256, 1))          # [256 rows, 256 B]
+    scales = np.repeat(np.arange(256, dtype=np.uint8)[:, None], 16, 1)  # one scale per row
+    got = mxfp4_dequantize(torch.from_numpy(codes).to(DEV), torch.from_numpy(scales).to(DEV),
+                           dtype)
+    torch.cuda.synchronize()
+    ref = mxfp4.dequantize(codes, scales)
+    with np.errstate(over="ignore"):
+        ref32 = ref.astype(np.float32)
+    g = got.float().cpu().numpy()
+    nan = np.isnan(ref32)
+    assert np.all(np.isnan(g[nan]))
+    assert np.array_equal(g[~nan].view(np.uint32), ref32[~nan].view(np.uint32))
+
+
+def _quant_cases():
+    rng = np.random.default_rng(21)
+    out = {
+        "normal_0.02": (rng.standard_normal((64, 2880)) * 0.02).astype(np.float32),
+        "wide_range": (rng.standard_normal((32, 256)) *
+                       10.0 ** rng.integers(-38, 37, (32, 1))).astype(np.float32),
+        "zeros_and_neg_zero": (np.zeros((4, 64)) * np.array([1, -1, 1, -1])[:, None]).astype(np.float32),
+    }
+    # exact E2M1 midpoints and neighbours times a power of two per block
+    # (each block's amax is exactly 6 * 2^e, so the midpoints stay midpoints)
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0], np.float32)
+    m7 = mids[:7]
+    blk = np.concatenate([mids, -mids, np.nextafter(m7, np.float32(0)),
+                          np.nextafter(m7, np.float32(7)), [np.float32(-6.0), np.float32(4.0)]])
+    assert blk.size == 32
+    e = rng.integers(-100, 100, 16).astype(np.float32)
+    out["midpoints"] = np.stack([blk * np.float32(2.0) ** ee for ee in e]).astype(np.float32)
+    out["tiny_subnormal"] = (rng.standard_normal((8, 64)) * 1e-41).astype(np.float32)
+    out["one_block"] = np.linspace(-6, 6, 32, dtype=np.float32)[None, :]
+    return out
+
+
+@pytest.mark.parametrize("name", list(_quant_cases().keys()))
+def test_quantize_bytes_match_oracle(name):
+    _say(f"quantize {name}")
+    w = _quant_cases()[name]
+    c, s = mxfp4_quantize(torch.from_numpy(w).to(DEV))
+    torch.cuda.synchronize()
+    rc, rs = mxfp4.quantize(w)
+    assert np.array_equal(s.cpu().numpy(), rs), "scales differ"
+    assert np.array_equal(c.cpu().numpy(), rc), "codes differ"
+
+
+# ------------------------------------------------------------- small layers
+
+def _run_layer(s, x_scale=1.0, with_bias=True, backward=True, T=None):
+    T = s.T if T is None else T
+    _say(f"layer {s.name} T={T} H={s.H} I={s.I} E={s.E} k={s.k} x_scale={x_scale} bias={with_bias}")
+    dl = device_layer(s, with_bias=with_bias)
+    ol, _ = oracle_layer(s, with_bias=with_bias)
+    # the oracle's quantised bytes must equal the GPU's
+    assert np.array_equal(dl.gu_codes.cpu().numpy(), ol.gu_codes)
+    assert np.array_equal(dl.dn_scales.cpu().numpy(), ol.dn_scales)
+    xb = syn.tokens(s, T, scale=x_scale)
+    x = bf16_tensor(xb).to(DEV)
+    out, sv = mxfp4_moe_forward(dl, x, saved=True)
+    torch.cuda.synchronize()
+    ref, r, cache = moe.forward(ol, xb)
+    assert_routing_equal(sv, r)
+    assert_close(to_f64(out), ref, "out")
+    # saved state, in sorted order
+    rows = r.sorted_rows
+    href = np.stack([cache[int(f)][0] for f in rows])
+    aref = np.stack([cache[int(f)][1] for f in rows])
+    assert_close(to_f64(sv.h), href, "saved h")
+    assert_close(to_f64(sv.a), aref, "saved a")
+    res = {"out": out, "saved": sv, "routing": r}
+    if backward:
+        dyb = syn.upstream_grad(s, T)
+        dx, _, _ = mxfp4_moe_backward_dx(dl, sv, bf16_tensor(dyb).to(DEV))
+        torch.cuda.synchronize()
+        dref, _, _ = moe.backward_dx(ol, xb, dyb)
+        assert_close(to_f64(dx), dref, "dX")
+        res["dx"] = dx
+    return res
+
+
+def test_tiny_forward_backward():
+    _run_layer(syn.spec("tiny"))
+
+
+def test_tiny_clamp_exercise():
+    # activations x64 push |h| past the SwiGLU limit on both branches
+    s = syn.spec("tiny")
+    ol, _ = oracle_layer(s)
+    _, _, cache = moe.forward(ol, syn.tokens(s, scale=64.0))
+    h = np.stack([c[0] for c in cache.values()])
+    assert np.any(h[:, 0::2] > 7) and np.any(np.abs(h[:, 1::2]) > 7)
+    _run_layer(s, x_scale=64.0)
+
+
+def test_tiny_without_biases():
+    _run_layer(syn.spec("tiny"), with_bias=False)
+
+
+@pytest.mark.parametrize("T", [1, 3, 17])
+def test_ragged_token_counts(T):
+    _run_layer(syn.spec("tiny"), T=T)
+
+
+def test_dense_special_case():
+    _run_layer(syn.spec("tiny", E=1, k=1, T=40))
+
+
+def test_multi_tile_ragged_tails():
+    # >128 rows per expert (several row tiles, ragged last tile), gate_up
+    # output 640 = 2.5 column tiles, down output 192 < one column tile,
+    # three 64-wide K steps in gate_up and five in down
+    _run_layer(syn.spec("tiny", T=300, H=192, I=320, E=3, k=2))
+
+
+def test_many_experts_top8():
+    _run_layer(syn.spec("tiny", T=64, H=128, I=128, E=64, k=8))
+
+
+def test_forward_is_deterministic():
+    s = syn.spec("tiny", T=200, H=128, I=192, E=8, k=4)
+    dl = device_layer(s)
+    x = bf16_tensor(syn.tokens(s)).to(DEV)
+    o1, s1 = mxfp4_moe_forward(dl, x, saved=True)
+    o2, s2 = mxfp4_moe_forward(dl, x, saved=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    for n in ("topk_idx", "topk_w", "expert_offsets", "sorted_rows", "h", "a"):
+        assert torch.equal(getattr(s1, n).view(torch.uint8), getattr(s2, n).view(torch.uint8)), n
+
+
+def test_inference_forward_equals_saved_forward():
+    s = syn.spec("tiny", T=77)
+    dl = device_layer(s)
+    x = bf16_tensor(syn.tokens(s)).to(DEV)
+    o1, _ = mxfp4_moe_forward(dl, x, saved=None)
+    o2, _ = mxfp4_moe_forward(dl, x, saved=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
+def test_unsupported_shape_raises():
+    s = syn.spec("tiny")
+    dl = device_layer(s)
+    x = bf16_tensor(syn.tokens(s)).to(DEV)
+    dl.k = 5  # k > E
+    with pytest.raises(Mxfp4Error):
+        mxfp4_moe_forward(dl, x)
+
+
+# --------------------------------------------------------- full-size layers
+
+def _full_size(name, T=None, n_sample=6, backward=True, seed=0):
+    s = syn.spec(name) if T is None else syn.spec(name, T=T)
+    T = s.T
+    _say(f"full-size {name} T={T}: building device layer")
+    dl = device_layer(s)
+    xb = syn.tokens(s, T)
+    x = bf16_tensor(xb).to(DEV)
+    _say("forward")
+    out, sv = mxfp4_moe_forward(dl, x, saved=True)
+    torch.cuda.synchronize()
+    # routing of every token: bit-exact
+    rl = moe.Layer(router_w=syn.router_weight(s), router_b=syn.router_bias(s),
+                   gu_codes=np.zeros((s.E, 2, 1), np.uint8), gu_scales=None, gu_bias=None,
+                   dn_codes=None, dn_scales=None, dn_bias=None, k=s.k)
+    r = moe.route(rl, xb)
+    _say(f"min k/k+1 logit gap {min_topk_gap(r, s.k):.3e}")
+    assert_routing_equal(sv, r)
+    rng = np.random.default_rng(seed)
+    toks = np.sort(rng.choice(T, size=min(n_sample, T), replace=False))
+    touched = np.unique(r.idx[toks])
+    _say(f"oracle: {len(touched)} experts for tokens {toks.tolist()}")
+    ol, _ = oracle_layer(s, experts=touched)
+    # the GPU quantizer's bytes equal the oracle's on every expert it needed
+    for e in touched[:4]:
+        assert np.array_equal(dl.gu_codes[e].cpu().numpy(), ol.gu_codes[e])
+        assert np.array_equal(dl.dn_codes[e].cpu().numpy(), ol.dn_codes[e])
+        assert np.array_equal(dl.gu_scales[e].cpu().numpy(), ol.gu_scales[e])
+    ref, _, cache = moe.forward(ol, xb, tokens=toks, routing=r)
+    assert_close(to_f64(out)[toks], ref[toks], "out (sampled tokens)")
+    # saved a/h for the sampled rows (sorted positions of their flat rows)
+    pos = np.empty(T * s.k, np.int64)
+    pos[r.sorted_rows] = np.arange(T * s.k)
+    fl = np.array(sorted(cache.keys()))
+    assert_close(to_f64(sv.a)[pos[fl]], np.stack([cache[int(f)][1] for f in fl]), "saved a")
+    if backward:
+        _say("backward")
+        dyb = syn.upstream_grad(s, T)
+        dx, _, _ = mxfp4_moe_backward_dx(dl, sv, bf16_tensor(dyb).to(DEV))
+        torch.cuda.synchronize()
+        dref, _, _ = moe.backward_dx(ol, xb, dyb, tokens=toks, routing=r)
+        assert_close(to_f64(dx)[toks], dref[toks], "dX (sampled tokens)")
+        assert torch.isfinite(dx.float()).all()
+    assert torch.isfinite(out.float()).all()
+
+
+@pytest.mark.timeout(900)
+def test_gpt_oss_20b_layer_2048_tokens():
+    _full_size("20b_2048")
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("T", [1, 8, 64])
+def test_gpt_oss_20b_layer_decode(T):
+    _full_size("20b_decode", T=T, n_sample=min(T, 4), backward=(T == 64))
+
+
+@pytest.mark.timeout(900)
+def test_gpt_oss_120b_layer_zipf_8192_tokens():
+    _full_size("120b_8192_zipf", n_sample=4)
