@@ -1,0 +1,257 @@
+#!/usr/bin/env python3
+"""Throughput of the MXFP4 MoE expert block on one MI355X.
+
+A step is one pass of the whole hot path on the gpt-oss-20b-shaped layer
+(2048 tokens, hidden 2880, intermediate 2880, 32 experts, top-4, MXFP4
+expert weights): the forward with saved state (router, permutation, gate_up
++ SwiGLU, down + weighted combine) followed by the dX backward.  Inputs
+and weights are synthetic (seeded, the layer's real shapes) and resident in
+HBM before the timed region.
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode]
+
+Prints one JSON line.  `value` is forward + dX TFLOP/s counting the expert
+GEMMs' algorithmic flops (2 * T*k * 3 * H * I per pass, two passes); the
+line also carries the forward-only rate, the decode-size weight-streaming
+rates (GB/s over the packed weights and scales of the experts a step
+touches, eight rotating weight copies so that nothing is served from the
+last-level cache), per-kernel times, the roofline entry of the dominant
+kernel (timed with HIP events on the library's stream) and the CPU
+oracle's rate on a bounded sample.
+"""
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("MoE layer TFLOP/s fwd & fwd+dX-bwd (gpt-oss-20b shape, 2048 tok); decode GB/s")
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=8)
+    return ap.parse_args()
+
+
+def kernel_times(lib):
+    n = lib.mxfp4_moe_kernel_times(None, None, None, 0)
+    names = (ctypes.c_char_p * n)()
+    ms = (ctypes.c_double * n)()
+    cnt = (ctypes.c_int * n)()
+    lib.mxfp4_moe_kernel_times(names, ms, cnt, n)
+    return {names[i].decode(): (ms[i], cnt[i]) for i in range(n)}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE={world}).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import moe_synth as syn
+    from mxfp4_weight_mixture_02_amd import (MoeLayer, SavedState, Workspace, lib,
+                                             mxfp4_moe_backward_dx, mxfp4_moe_forward,
+                                             mxfp4_quantize)
+
+    L = lib()
+    L.mxfp4_moe_kernel_timing.argtypes = [ctypes.c_int]
+    L.mxfp4_moe_kernel_times.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                         ctypes.c_int]
+    dev = "cuda:0"
+    s = syn.spec("20b_2048")
+    T, H, I, E, k = s.T, s.H, s.I, s.E, s.k
+    R = T * k
+
+    def bf(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    # ---- layer: fp32 draws quantised on the GPU, one expert at a time
+    gu_c = torch.empty((E, 2 * I, H // 2), dtype=torch.uint8, device=dev)
+    gu_s = torch.empty((E, 2 * I, H // 32), dtype=torch.uint8, device=dev)
+    dn_c = torch.empty((E, H, I // 2), dtype=torch.uint8, device=dev)
+    dn_s = torch.empty((E, H, I // 32), dtype=torch.uint8, device=dev)
+    gws = syn.all_experts(syn.gate_up_weight, s)
+    for e in range(E):
+        c, sc = mxfp4_quantize(torch.from_numpy(gws[e]).to(dev))
+        gu_c[e].copy_(c)
+        gu_s[e].copy_(sc)
+    del gws
+    dws = syn.all_experts(syn.down_weight, s)
+    for e in range(E):
+        c, sc = mxfp4_quantize(torch.from_numpy(dws[e]).to(dev))
+        dn_c[e].copy_(c)
+        dn_s[e].copy_(sc)
+    del dws
+    layer = MoeLayer(torch.from_numpy(syn.router_weight(s)).to(dev),
+                     torch.from_numpy(syn.router_bias(s)).to(dev), gu_c, gu_s,
+                     bf(syn.gate_up_bias(s)), dn_c, dn_s, bf(syn.down_bias(s)), k=k)
+    x = bf(syn.tokens(s))
+    dy = bf(syn.upstream_grad(s))
+    saved = SavedState.empty(layer, T, dev)
+    out = torch.empty_like(x)
+    dx = torch.empty_like(x)
+    wsf, wsb = Workspace(), Workspace()
+
+    def step():
+        mxfp4_moe_forward(layer, x, saved=saved, out=out, workspace=wsf)
+        mxfp4_moe_backward_dx(layer, saved, dy, dx=dx, workspace=wsb)
+
+    flops_pass = 2.0 * R * 3 * H * I
+    flops_step = 2 * flops_pass
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+    value = flops_step / dt / 1e12
+
+    # ---- the same steps with per-kernel HIP events on the library's stream
+    L.mxfp4_moe_kernel_timing(1)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    dt_inst = (time.perf_counter() - t0) / args.steps
+    kt = kernel_times(L)
+    L.mxfp4_moe_kernel_timing(0)
+    kernels = {n: round(ms / c * 1e3, 2) for n, (ms, c) in kt.items()}   # us per launch
+    gemm_flops = {"gate_up": 2.0 * R * 2 * I * H, "down": 2.0 * R * H * I,
+                  "bwd_down": 2.0 * R * H * I, "bwd_gate_up": 2.0 * R * 2 * I * H}
+    dom = max(gemm_flops, key=lambda n: kt[n][0])
+    avg_s = kt[dom][0] / kt[dom][1] / 1e3
+    achieved = gemm_flops[dom] / avg_s / 1e12
+    roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "avg_launch_us": round(avg_s * 1e6, 1),
+                "flop_per_launch": gemm_flops[dom]}
+
+    # ---- forward only (inference: no saved state)
+    for _ in range(args.warmup):
+        mxfp4_moe_forward(layer, x, out=out, workspace=wsf)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        mxfp4_moe_forward(layer, x, out=out, workspace=wsf)
+    torch.cuda.synchronize()
+    dt_fwd = (time.perf_counter() - t0) / args.steps
+    fwd_tflops = flops_pass / dt_fwd / 1e12
+
+    # ---- decode sizes, eight rotating copies of the expert weights
+    decode = {}
+    if not args.no_decode:
+        copies = [layer]
+        for _ in range(7):
+            copies.append(MoeLayer(layer.router_w, layer.router_b, gu_c.clone(), gu_s.clone(),
+                                   layer.gu_bias, dn_c.clone(), dn_s.clone(), layer.dn_bias, k=k))
+        per_expert = (2 * I * H // 2 + 2 * I * H // 32) + (H * I // 2 + H * I // 32)
+        for Td in syn.DECODE_TOKENS:
+            xd = bf(syn.tokens(s, Td))
+            wsd = Workspace()
+            _, sv = mxfp4_moe_forward(layer, xd, saved=True, workspace=wsd)
+            torch.cuda.synchronize()
+            touched = int(torch.unique(sv.topk_idx).numel())
+            od = torch.empty_like(xd)
+            nrep = max(8, args.steps) * 8
+            for i in range(16):
+                mxfp4_moe_forward(copies[i % 8], xd, out=od, workspace=wsd)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for i in range(nrep):
+                mxfp4_moe_forward(copies[i % 8], xd, out=od, workspace=wsd)
+            torch.cuda.synchronize()
+            dtd = (time.perf_counter() - t0) / nrep
+            decode[str(Td)] = {"us": round(dtd * 1e6, 1), "experts": touched,
+                               "GB/s": round(touched * per_expert / dtd / 1e9, 1),
+                               "frac_hbm": round(touched * per_expert / dtd / 1e9 / PEAK_HBM_GBS, 4)}
+        del copies
+
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(dt * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "gpt-oss-20b MoE layer, 2048 tokens, forward (saved) + dX backward",
+                   "T": T, "H": H, "I": I, "E": E, "k": k, "weights": "MXFP4 (E2M1 + UE8M0/32)",
+                   "parallelism": "none (1 GPU)"},
+        "fwd_tflops": round(fwd_tflops, 2), "fwd_ms": round(dt_fwd * 1e3, 4),
+        "ms_per_step_with_kernel_events": round(dt_inst * 1e3, 4),
+        "kernel_us": kernels, "decode": decode, "roofline": roofline,
+    }
+
+    # ---- CPU oracle on a bounded sample of the same workload
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(s, args.cpu_sample_tokens)
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(s, n_tok):
+    """The float64 oracle, as it stands, on n_tok tokens of the layer:
+    routing over all tokens, then forward and dX for the sample."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import moe_synth as syn
+    from oracle import moe, mxfp4
+
+    xb = syn.tokens(s)
+    dyb = syn.upstream_grad(s)
+    rl = moe.Layer(router_w=syn.router_weight(s), router_b=syn.router_bias(s),
+                   gu_codes=np.zeros((s.E, 2, 1), np.uint8), gu_scales=None, gu_bias=None,
+                   dn_codes=None, dn_scales=None, dn_bias=None, k=s.k)
+    r = moe.route(rl, xb)
+    toks = np.arange(n_tok)
+    touched = sorted(set(int(e) for e in np.unique(r.idx[toks])))
+    gu_c = np.zeros((s.E, 2 * s.I, s.H // 2), np.uint8)
+    gu_s = np.zeros((s.E, 2 * s.I, s.H // 32), np.uint8)
+    dn_c = np.zeros((s.E, s.H, s.I // 2), np.uint8)
+    dn_s = np.zeros((s.E, s.H, s.I // 32), np.uint8)
+    from concurrent.futures import ThreadPoolExecutor
+
+    def q(e):
+        return e, mxfp4.quantize(syn.gate_up_weight(s, e)), mxfp4.quantize(syn.down_weight(s, e))
+
+    with ThreadPoolExecutor(8) as ex:
+        for e, (a, b), (c, d) in ex.map(q, touched):
+            gu_c[e], gu_s[e], dn_c[e], dn_s[e] = a, b, c, d
+    ol = moe.Layer(syn.router_weight(s), syn.router_bias(s), gu_c, gu_s, syn.gate_up_bias(s),
+                   dn_c, dn_s, syn.down_bias(s), k=s.k)
+    t0 = time.perf_counter()
+    r2 = moe.route(ol, xb)
+    moe.forward(ol, xb, tokens=toks, routing=r2)
+    moe.backward_dx(ol, xb, dyb, tokens=toks, routing=r2)
+    dt = time.perf_counter() - t0
+    flops = 2 * (2.0 * n_tok * s.k * 3 * s.H * s.I)
+    blas = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s",
+            "cores": max(blas) if blas else 1, "kind": "oracle",
+            "seconds": round(dt, 2),
+            "sample": f"{n_tok} tokens ({n_tok * s.k} routed rows, {len(touched)} experts) of the "
+                      f"2048-token gpt-oss-20b layer: routing of all tokens, forward + dX for the "
+                      f"sample, float64 numpy (BLAS matmuls multi-threaded, dequant single-threaded)"}
+
+
+if __name__ == "__main__":
+    main()

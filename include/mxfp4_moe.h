@@ -53,7 +53,8 @@ extern "C" {
  *  T tokens, H hidden, I intermediate, E experts, k experts per token.
  *  Requirements: T >= 1; H % 64 == 0 and I % 64 == 0 (whole 32-element
  *  scale blocks, [P3] group-32 guard, in 64-element K steps);
- *  1 <= k <= min(E, 8); E <= 256; T * k < 2^31; lora_rank in {0, 16}.
+ *  1 <= k <= min(E, 8); E <= 256; T * k < 2^31; T * H < 2^31;
+ *  H, I <= 2^20; lora_rank in {0, 16}.
  *  swiglu_alpha, swiglu_limit: the clamped SwiGLU constants (GPT-OSS uses
  *  1.702 and 7).  lora_scale multiplies the LoRA delta (1.0 when
  *  lora_alpha equals the rank). */
@@ -180,6 +181,18 @@ int mxfp4_quantize(const float* w, int64_t rows, int64_t K, uint8_t* codes, uint
  * Scale byte 255 gives a NaN. */
 int mxfp4_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t K,
                      int out_dtype, void* out, void* stream);
+
+/* Per-kernel timing, for measurement.  mxfp4_moe_kernel_timing(1) clears
+ * the totals and makes every later forward/backward call record a HIP event
+ * before and after each kernel it launches, on that call's stream;
+ * mxfp4_moe_kernel_timing(0) stops recording.  mxfp4_moe_kernel_times
+ * waits for the recorded events, adds their elapsed times to per-kernel
+ * totals and copies up to max_kernels entries: the kernel's name (a static
+ * string), total milliseconds and launch count.  Returns the number of
+ * distinct kernels seen, or a negative error code.  Off by default;
+ * process-wide, not for concurrent use from several threads. */
+int mxfp4_moe_kernel_timing(int enable);
+int mxfp4_moe_kernel_times(const char** names, double* total_ms, int* launches, int max_kernels);
 
 /* Message for the last non-zero return on this thread ("" if none). */
 const char* mxfp4_last_error(void);

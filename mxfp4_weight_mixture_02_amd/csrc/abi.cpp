@@ -10,6 +10,8 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
+#include <vector>
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -63,6 +65,8 @@ int check_dims(const mxfp4_moe_dims* d) {
     return fail(MXFP4_EUNSUPPORTED, "T*k = %lld routed rows exceed int32", (long long)(d->T * d->k));
   if (d->H > (int64_t(1) << 20) || d->I > (int64_t(1) << 20))
     return fail(MXFP4_EUNSUPPORTED, "H and I must be <= 2^20");
+  if (d->T * d->H >= (int64_t(1) << 31))
+    return fail(MXFP4_EUNSUPPORTED, "T*H = %lld elements exceed int32", (long long)(d->T * d->H));
   if (d->lora_rank != 0)
     return fail(MXFP4_EUNSUPPORTED, "lora_rank=%d: only 0 is supported by this build",
                 d->lora_rank);
@@ -116,10 +120,79 @@ int hip_status(hipError_t e, const char* what) {
   return MXFP4_OK;
 }
 
-#define LAUNCH(call, name)                          \
-  do {                                              \
-    int rc_ = hip_status((call), name);             \
-    if (rc_ != MXFP4_OK) return rc_;                \
+// Optional per-kernel event timing (mxfp4_moe_kernel_timing).
+struct KernelTimer {
+  struct Pending {
+    const char* name;
+    hipEvent_t start, stop;
+  };
+  struct Total {
+    const char* name;
+    double ms;
+    int launches;
+  };
+  std::mutex mu;
+  bool on = false;
+  std::vector<hipEvent_t> pool;
+  std::vector<Pending> pending;
+  std::vector<Total> totals;
+
+  hipEvent_t take() {
+    if (!pool.empty()) {
+      hipEvent_t e = pool.back();
+      pool.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+  void drain() {
+    for (auto& p : pending) {
+      float ms = 0.0f;
+      if (hipEventSynchronize(p.stop) == hipSuccess &&
+          hipEventElapsedTime(&ms, p.start, p.stop) == hipSuccess) {
+        bool found = false;
+        for (auto& t : totals)
+          if (strcmp(t.name, p.name) == 0) {
+            t.ms += ms;
+            t.launches += 1;
+            found = true;
+          }
+        if (!found) totals.push_back({p.name, (double)ms, 1});
+      }
+      pool.push_back(p.start);
+      pool.push_back(p.stop);
+    }
+    pending.clear();
+  }
+};
+KernelTimer g_timer;
+
+// Enqueue one kernel; with timing on, bracket it with events on stream s.
+template <class F>
+int launch_timed(F&& enqueue, const char* name, hipStream_t s) {
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  const bool on = g_timer.on;
+  if (on) {
+    std::lock_guard<std::mutex> g(g_timer.mu);
+    e0 = g_timer.take();
+    e1 = g_timer.take();
+    if (e0) (void)hipEventRecord(e0, s);
+  }
+  int rc = hip_status(enqueue(), name);
+  if (on && e0 && e1) {
+    (void)hipEventRecord(e1, s);
+    std::lock_guard<std::mutex> g(g_timer.mu);
+    g_timer.pending.push_back({name, e0, e1});
+  }
+  return rc;
+}
+
+#define LAUNCH(call, name)                                            \
+  do {                                                                \
+    int rc_ = launch_timed([&]() { return (call); }, name, s);        \
+    if (rc_ != MXFP4_OK) return rc_;                                  \
   } while (0)
 
 }  // namespace
@@ -127,6 +200,27 @@ int hip_status(hipError_t e, const char* what) {
 extern "C" {
 
 const char* mxfp4_last_error(void) { return g_err; }
+
+int mxfp4_moe_kernel_timing(int enable) {
+  std::lock_guard<std::mutex> g(g_timer.mu);
+  g_timer.drain();
+  g_timer.totals.clear();
+  g_timer.on = enable != 0;
+  return ok();
+}
+
+int mxfp4_moe_kernel_times(const char** names, double* total_ms, int* launches, int max_kernels) {
+  std::lock_guard<std::mutex> g(g_timer.mu);
+  g_timer.drain();
+  const int n = (int)g_timer.totals.size();
+  for (int i = 0; i < n && i < max_kernels; ++i) {
+    if (names) names[i] = g_timer.totals[i].name;
+    if (total_ms) total_ms[i] = g_timer.totals[i].ms;
+    if (launches) launches[i] = g_timer.totals[i].launches;
+  }
+  ok();
+  return n;
+}
 
 size_t mxfp4_moe_workspace_bytes(const mxfp4_moe_dims* dims, int mode) {
   if (check_dims(dims) != MXFP4_OK) return 0;
@@ -223,7 +317,7 @@ int mxfp4_moe_backward_dx(const mxfp4_moe_dims* dims, const mxfp4_moe_weights* w
   float* dxr = at<float>(workspace, L.dxr);
   const int maxt = mxmoe::max_tiles(R, E);
 
-  LAUNCH(mxmoe::launch_build_tiles(saved->expert_offsets, E, tiles, num_tiles, s), "tiles");
+  LAUNCH(mxmoe::launch_build_tiles(saved->expert_offsets, E, tiles, num_tiles, s), "bwd_tiles");
   LAUNCH(mxmoe::launch_bwd_down(dy, w->dn_codes, w->dn_scales, saved->topk_w, saved->sorted_rows,
                                 tiles, num_tiles, maxt, saved->h, saved->a, H, I, k,
                                 d.swiglu_alpha, d.swiglu_limit, dh, dw_part, s),
@@ -245,8 +339,8 @@ int mxfp4_quantize(const float* w, int64_t rows, int64_t K, uint8_t* codes, uint
   if (rows * K / 4 / 256 >= (int64_t(1) << 31)) return fail(MXFP4_EUNSUPPORTED, "tensor too large");
   if (!aligned(w, 16) || !aligned(codes, 2))
     return fail(MXFP4_EINVAL, "w must be 16-byte and codes 2-byte aligned");
-  LAUNCH(mxmoe::launch_quantize(w, rows, K, codes, scales, static_cast<hipStream_t>(stream)),
-         "quantize");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  LAUNCH(mxmoe::launch_quantize(w, rows, K, codes, scales, s), "quantize");
   return ok();
 }
 
@@ -259,9 +353,8 @@ int mxfp4_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows, 
   if (rows * K / 8 / 256 >= (int64_t(1) << 31)) return fail(MXFP4_EUNSUPPORTED, "tensor too large");
   if (!aligned(codes, 4) || !aligned(out, 16))
     return fail(MXFP4_EINVAL, "codes must be 4-byte and out 16-byte aligned");
-  LAUNCH(mxmoe::launch_dequantize(codes, scales, rows, K, out_dtype, out,
-                                  static_cast<hipStream_t>(stream)),
-         "dequantize");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  LAUNCH(mxmoe::launch_dequantize(codes, scales, rows, K, out_dtype, out, s), "dequantize");
   return ok();
 }
 

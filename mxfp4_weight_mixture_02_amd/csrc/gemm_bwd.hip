@@ -43,11 +43,11 @@ struct RawBlock {
 
 __device__ __forceinline__ void load_block(RawBlock& rb, const uint8_t* __restrict__ code0,
                                            const uint8_t* __restrict__ scale0, int64_t crow,
-                                           int64_t srow, bool live) {
+                                           int64_t srow) {
 #pragma unroll
   for (int r = 0; r < 8; ++r) {
-    rb.code[r] = live ? *reinterpret_cast<const uint32_t*>(code0 + r * crow) : 0u;
-    rb.scale[r] = live ? scale0[r * srow] : 0u;
+    rb.code[r] = *reinterpret_cast<const uint32_t*>(code0 + r * crow);
+    rb.scale[r] = scale0[r * srow];
   }
 }
 
@@ -72,25 +72,110 @@ __device__ __forceinline__ void store_block_t(const RawBlock& rb, uint16_t* dst_
 
 // Main loop shared by the two backward GEMMs.  W is stored [C rows][O
 // cols] (packed along O); this workgroup produces output columns o0.. for
-// routed rows whose contraction vectors are brow[j] (length C).
+// routed rows whose contraction vectors are brow[j] (length C).  Rows past
+// the tile point at its first row and weight blocks past the last output
+// column at the first one, so every load is unconditional (the affected
+// products are never stored); only the first NRB 32-row blocks hold rows.
+//
+// Pipeline: global loads run two K steps ahead.  In step c a thread issues
+// the loads of step c+2 (activation pieces and its raw 8x8 weight block),
+// stores the step c+1 data it loaded one step earlier into the other LDS
+// buffers (the weight block decoded and transposed on the way), then the
+// waves run the MFMAs of step c from LDS; one barrier per step.  Step
+// indices are clamped at the end instead of branching around loads, so the
+// compiler's wait counts stay exact.  The loop is unrolled by two so every
+// register set has a fixed name.
+template <int WN>
+struct BwdPipe {
+  u32x4 xv[2][BwdTile<WN>::PPT];
+  RawBlock raw[2];
+};
+
+template <int WN, int PAR>
+__device__ __forceinline__ void bwd_issue(BwdPipe<WN>& pp, const uint16_t* const (&brow)[BwdTile<WN>::PPT],
+                                          const uint8_t* bcode, const uint8_t* bscale,
+                                          int64_t crow, int64_t srow, int c) {
+#pragma unroll
+  for (int j = 0; j < BwdTile<WN>::PPT; ++j)
+    pp.xv[PAR][j] = *reinterpret_cast<const u32x4*>(brow[j] + c * KC);
+  load_block(pp.raw[PAR], bcode + (int64_t)c * KC * crow, bscale + (int64_t)c * KC * srow, crow,
+             srow);
+}
+
+template <int WN, int PAR>
+__device__ __forceinline__ void bwd_stage(const BwdPipe<WN>& pp, uint16_t* wdst,
+                                          uint16_t (*xs)[MT][LDS_ROW]) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int j = 0; j < BwdTile<WN>::PPT; ++j) {
+    int q = tid + j * BwdTile<WN>::NTHR;
+    *reinterpret_cast<u32x4*>(&xs[PAR][q >> 3][(q & 7) * 8]) = pp.xv[PAR][j];
+  }
+  store_block_t(pp.raw[PAR], wdst);
+}
+
+template <int WN, int NRB, int PAR>
+__device__ __forceinline__ void bwd_step(BwdPipe<WN>& pp, const uint16_t* const (&brow)[BwdTile<WN>::PPT],
+                                         const uint8_t* bcode, const uint8_t* bscale,
+                                         int64_t crow, int64_t srow, int c, int nsteps,
+                                         uint16_t* wdst_next,
+                                         uint16_t (*ws)[BwdTile<WN>::NT][LDS_ROW],
+                                         uint16_t (*xs)[MT][LDS_ROW], f32x16 (&acc)[2][4]) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hlf = lane >> 5;
+  bwd_issue<WN, PAR>(pp, brow, bcode, bscale, crow, srow, min(c + 2, nsteps - 1));
+  bwd_stage<WN, PAR ^ 1>(pp, wdst_next, xs);
+#pragma unroll
+  for (int st = 0; st < 4; ++st) {
+    const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(&ws[PAR][wave * 64 + l32][hlf * 32 + st * 8]);
+    const bf16x8 a1 =
+        *reinterpret_cast<const bf16x8*>(&ws[PAR][wave * 64 + 32 + l32][hlf * 32 + st * 8]);
+#pragma unroll
+    for (int tb = 0; tb < NRB; ++tb) {
+      const bf16x8 b = *reinterpret_cast<const bf16x8*>(&xs[PAR][tb * 32 + l32][hlf * 32 + st * 8]);
+      acc[0][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b, acc[0][tb], 0, 0, 0);
+      acc[1][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b, acc[1][tb], 0, 0, 0);
+    }
+  }
+  __syncthreads();
+}
+
+template <int WN, int NRB>
+__device__ __forceinline__ void bwd_mainloop_n(const uint16_t* const (&brow)[BwdTile<WN>::PPT],
+                                               const uint8_t* bcode, const uint8_t* bscale,
+                                               int64_t crow, int64_t srow, int nsteps,
+                                               uint16_t* wdst0, uint16_t* wdst1,
+                                               uint16_t (*ws)[BwdTile<WN>::NT][LDS_ROW],
+                                               uint16_t (*xs)[MT][LDS_ROW], f32x16 (&acc)[2][4]) {
+  BwdPipe<WN> pp;
+  bwd_issue<WN, 0>(pp, brow, bcode, bscale, crow, srow, 0);
+  bwd_issue<WN, 1>(pp, brow, bcode, bscale, crow, srow, min(1, nsteps - 1));
+  bwd_stage<WN, 0>(pp, wdst0, xs);
+  __syncthreads();
+  int c = 0;
+  for (; c + 1 < nsteps; c += 2) {
+    bwd_step<WN, NRB, 0>(pp, brow, bcode, bscale, crow, srow, c, nsteps, wdst1, ws, xs, acc);
+    bwd_step<WN, NRB, 1>(pp, brow, bcode, bscale, crow, srow, c + 1, nsteps, wdst0, ws, xs, acc);
+  }
+  if (c < nsteps)
+    bwd_step<WN, NRB, 0>(pp, brow, bcode, bscale, crow, srow, c, nsteps, wdst1, ws, xs, acc);
+}
+
 template <int WN>
 __device__ __forceinline__ void bwd_mainloop(const uint16_t* const (&brow)[BwdTile<WN>::PPT],
                                              const uint8_t* __restrict__ wcode,
                                              const uint8_t* __restrict__ wscale, int C, int O,
-                                             int o0, bool wave_live,
+                                             int o0, int nrb,
                                              uint16_t (*ws)[BwdTile<WN>::NT][LDS_ROW],
                                              uint16_t (*xs)[MT][LDS_ROW], f32x16 (&acc)[2][4]) {
   using BT = BwdTile<WN>;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int l32 = lane & 31, hlf = lane >> 5;
+  const int tid = threadIdx.x;
   const int nsteps = C / KC;
-  const u32x4 zero4 = {0u, 0u, 0u, 0u};
   const int64_t crow = O / 2, srow = O / 32;
 
   // this thread's 8x8 weight block: rows 8*cb.., output columns 8*ob..
   const int cb = tid / BT::OB, ob = tid % BT::OB;
-  const int ocol = o0 + 8 * ob;
-  const bool blive = ocol < O;
+  const int ocol = (o0 + 8 * ob < O) ? o0 + 8 * ob : 0;
   const uint8_t* bcode = wcode + (int64_t)(8 * cb) * crow + ocol / 2;
   const uint8_t* bscale = wscale + (int64_t)(8 * cb) * srow + ocol / 32;
   uint16_t* const wdst0 = &ws[0][8 * ob][8 * cb];
@@ -103,55 +188,11 @@ __device__ __forceinline__ void bwd_mainloop(const uint16_t* const (&brow)[BwdTi
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[rb][tb][r] = 0.0f;
 
-  u32x4 xv[BT::PPT];
-  RawBlock raw;
-#pragma unroll
-  for (int j = 0; j < BT::PPT; ++j)
-    xv[j] = brow[j] ? *reinterpret_cast<const u32x4*>(brow[j]) : zero4;
-  load_block(raw, bcode, bscale, crow, srow, blive);
-#pragma unroll
-  for (int j = 0; j < BT::PPT; ++j) {
-    int q = tid + j * BT::NTHR;
-    *reinterpret_cast<u32x4*>(&xs[0][q >> 3][(q & 7) * 8]) = xv[j];
-  }
-  store_block_t(raw, wdst0);
-  __syncthreads();
-
-  for (int c = 0; c < nsteps; ++c) {
-    const int buf = c & 1;
-    const bool more = c + 1 < nsteps;
-    if (more) {
-#pragma unroll
-      for (int j = 0; j < BT::PPT; ++j)
-        xv[j] = brow[j] ? *reinterpret_cast<const u32x4*>(brow[j] + (c + 1) * KC) : zero4;
-      load_block(raw, bcode + (int64_t)(c + 1) * KC * crow, bscale + (int64_t)(c + 1) * KC * srow,
-                 crow, srow, blive);
-    }
-    if (wave_live) {
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const bf16x8 a0 =
-            *reinterpret_cast<const bf16x8*>(&ws[buf][wave * 64 + l32][hlf * 32 + s * 8]);
-        const bf16x8 a1 =
-            *reinterpret_cast<const bf16x8*>(&ws[buf][wave * 64 + 32 + l32][hlf * 32 + s * 8]);
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-          const bf16x8 b =
-              *reinterpret_cast<const bf16x8*>(&xs[buf][tb * 32 + l32][hlf * 32 + s * 8]);
-          acc[0][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b, acc[0][tb], 0, 0, 0);
-          acc[1][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b, acc[1][tb], 0, 0, 0);
-        }
-      }
-    }
-    if (more) {
-#pragma unroll
-      for (int j = 0; j < BT::PPT; ++j) {
-        int q = tid + j * BT::NTHR;
-        *reinterpret_cast<u32x4*>(&xs[buf ^ 1][q >> 3][(q & 7) * 8]) = xv[j];
-      }
-      store_block_t(raw, buf ? wdst0 : wdst1);
-    }
-    __syncthreads();
+  switch (nrb) {
+    case 1: bwd_mainloop_n<WN, 1>(brow, bcode, bscale, crow, srow, nsteps, wdst0, wdst1, ws, xs, acc); break;
+    case 2: bwd_mainloop_n<WN, 2>(brow, bcode, bscale, crow, srow, nsteps, wdst0, wdst1, ws, xs, acc); break;
+    case 3: bwd_mainloop_n<WN, 3>(brow, bcode, bscale, crow, srow, nsteps, wdst0, wdst1, ws, xs, acc); break;
+    default: bwd_mainloop_n<WN, 4>(brow, bcode, bscale, crow, srow, nsteps, wdst0, wdst1, ws, xs, acc); break;
   }
 }
 
@@ -179,19 +220,15 @@ __global__ __launch_bounds__(64 * WN) void bwd_down_kernel(
   for (int j = 0; j < BT::PPT; ++j) {
     int q = tid + j * BT::NTHR;
     int r = q >> 3;
-    if (r < tl.rows) {
-      int f = sorted_rows[tl.row0 + r];
-      brow[j] = dy + (int64_t)(f / k) * H + (q & 7) * 8;
-    } else {
-      brow[j] = nullptr;
-    }
+    const int f = sorted_rows[tl.row0 + (r < tl.rows ? r : 0)];
+    brow[j] = dy + (int64_t)(f / k) * H + (q & 7) * 8;
   }
   // Wd is stored [H rows][I cols]: contraction over h (C = H), output i (O = I)
   const bool wave_live = o0 + wave * 64 < I;
   const uint8_t* wcode = codes + (int64_t)e * H * (I / 2);
   const uint8_t* wscale = scales + (int64_t)e * H * (I / 32);
   f32x16 acc[2][4];
-  bwd_mainloop<WN>(brow, wcode, wscale, H, I, o0, wave_live, ws, xs, acc);
+  bwd_mainloop<WN>(brow, wcode, wscale, H, I, o0, (tl.rows + 31) / 32, ws, xs, acc);
 
   const int N2 = 2 * I;
 #pragma unroll
@@ -261,14 +298,14 @@ __global__ __launch_bounds__(64 * WN) void bwd_gate_up_kernel(
   for (int j = 0; j < BT::PPT; ++j) {
     int q = tid + j * BT::NTHR;
     int r = q >> 3;
-    brow[j] = (r < tl.rows) ? dh + (int64_t)(tl.row0 + r) * N2 + (q & 7) * 8 : nullptr;
+    brow[j] = dh + (int64_t)(tl.row0 + (r < tl.rows ? r : 0)) * N2 + (q & 7) * 8;
   }
   // Wgu is stored [2I rows][H cols]: contraction over n (C = 2I), output h (O = H)
   const bool wave_live = o0 + wave * 64 < H;
   const uint8_t* wcode = codes + (int64_t)e * N2 * (H / 2);
   const uint8_t* wscale = scales + (int64_t)e * N2 * (H / 32);
   f32x16 acc[2][4];
-  bwd_mainloop<WN>(brow, wcode, wscale, N2, H, o0, wave_live, ws, xs, acc);
+  bwd_mainloop<WN>(brow, wcode, wscale, N2, H, o0, (tl.rows + 31) / 32, ws, xs, acc);
   if (!wave_live) return;
 
 #pragma unroll

@@ -43,22 +43,108 @@ struct FwdTile {
 };
 
 // Main loop shared by both forward GEMMs.  brow[j] points at the start of
-// the activation row for B piece j (already offset by its 8-element piece),
-// or is null for rows past the tile.  Weights: wrow = first weight row of
-// this lane (row block 0), N rows per expert, K columns.
+// the activation row for B piece j (already offset by its 8-element piece);
+// rows past the tile point at the tile's first row, so every load is
+// unconditional (their columns of the product are never stored).  Only the
+// first NRB 32-row blocks of the tile hold rows: the MFMAs of the others
+// are not issued.  wcode/wscale point at this lane's first weight row
+// (row block 0) and are valid even for a wave past the last weight row,
+// whose results are dropped.
+//
+// Pipeline: global loads run two K steps ahead.  In step c the lane decodes
+// the weights of step c (loaded two steps earlier), issues the loads of step
+// c+2 into the registers just freed, writes the activations of step c+1
+// (loaded one step earlier) into the other LDS buffer, then runs the MFMAs
+// of step c; one barrier per step.  Near the end the step index of a load
+// is clamped to the last step instead of branching, so the compiler's wait
+// counts stay exact (a branch around a load makes it wait for all loads).
+// The loop is unrolled by two so every register set has a fixed name.
+template <int WN>
+struct FwdPipe {
+  using FT = FwdTile<WN>;
+  u32x4 xv[2][FT::PPT];  // activation pieces, by step parity
+  u32x4 wv[2][2];        // raw codes, [parity][row block]
+  uint32_t sv[2][2];     // raw scales
+};
+
+template <int WN, int PAR>
+__device__ __forceinline__ void fwd_issue(FwdPipe<WN>& pp, const uint16_t* const (&brow)[FwdTile<WN>::PPT],
+                                          const uint8_t* wp0, const uint8_t* wp1,
+                                          const uint8_t* sp0, const uint8_t* sp1, int c) {
+#pragma unroll
+  for (int j = 0; j < FwdTile<WN>::PPT; ++j)
+    pp.xv[PAR][j] = *reinterpret_cast<const u32x4*>(brow[j] + c * KC);
+  pp.wv[PAR][0] = *reinterpret_cast<const u32x4*>(wp0 + c * 32);
+  pp.wv[PAR][1] = *reinterpret_cast<const u32x4*>(wp1 + c * 32);
+  pp.sv[PAR][0] = sp0[c * 2];
+  pp.sv[PAR][1] = sp1[c * 2];
+}
+
+template <int WN, int PAR>
+__device__ __forceinline__ void fwd_stage_x(const FwdPipe<WN>& pp, uint16_t (*xs)[MT][LDS_ROW]) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int j = 0; j < FwdTile<WN>::PPT; ++j) {
+    int q = tid + j * FwdTile<WN>::NTHR;
+    *reinterpret_cast<u32x4*>(&xs[PAR][q >> 3][(q & 7) * 8]) = pp.xv[PAR][j];
+  }
+}
+
+template <int WN, int NRB, int PAR>
+__device__ __forceinline__ void fwd_step(FwdPipe<WN>& pp, const uint16_t* const (&brow)[FwdTile<WN>::PPT],
+                                         const uint8_t* wp0, const uint8_t* wp1,
+                                         const uint8_t* sp0, const uint8_t* sp1, int c, int nsteps,
+                                         uint16_t (*xs)[MT][LDS_ROW], f32x16 (&acc)[2][4]) {
+  const int lane = threadIdx.x & 63;
+  const int l32 = lane & 31, hlf = lane >> 5;
+  bf16x8 a[2][4];
+  const float sc0 = scale_operand(pp.sv[PAR][0]), sc1 = scale_operand(pp.sv[PAR][1]);
+#pragma unroll
+  for (int st = 0; st < 4; ++st) {
+    a[0][st] = as_bf16x8(dequant8_bf16(pp.wv[PAR][0][st], sc0));
+    a[1][st] = as_bf16x8(dequant8_bf16(pp.wv[PAR][1][st], sc1));
+  }
+  fwd_issue<WN, PAR>(pp, brow, wp0, wp1, sp0, sp1, min(c + 2, nsteps - 1));
+  fwd_stage_x<WN, PAR ^ 1>(pp, xs);
+#pragma unroll
+  for (int st = 0; st < 4; ++st) {
+#pragma unroll
+    for (int tb = 0; tb < NRB; ++tb) {
+      const bf16x8 b = *reinterpret_cast<const bf16x8*>(&xs[PAR][tb * 32 + l32][hlf * 32 + st * 8]);
+      acc[0][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0][st], b, acc[0][tb], 0, 0, 0);
+      acc[1][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1][st], b, acc[1][tb], 0, 0, 0);
+    }
+  }
+  __syncthreads();
+}
+
+template <int WN, int NRB>
+__device__ __forceinline__ void fwd_mainloop_n(const uint16_t* const (&brow)[FwdTile<WN>::PPT],
+                                               const uint8_t* wp0, const uint8_t* wp1,
+                                               const uint8_t* sp0, const uint8_t* sp1, int nsteps,
+                                               uint16_t (*xs)[MT][LDS_ROW], f32x16 (&acc)[2][4]) {
+  FwdPipe<WN> pp;
+  fwd_issue<WN, 0>(pp, brow, wp0, wp1, sp0, sp1, 0);
+  fwd_issue<WN, 1>(pp, brow, wp0, wp1, sp0, sp1, min(1, nsteps - 1));
+  fwd_stage_x<WN, 0>(pp, xs);
+  __syncthreads();
+  int c = 0;
+  for (; c + 1 < nsteps; c += 2) {
+    fwd_step<WN, NRB, 0>(pp, brow, wp0, wp1, sp0, sp1, c, nsteps, xs, acc);
+    fwd_step<WN, NRB, 1>(pp, brow, wp0, wp1, sp0, sp1, c + 1, nsteps, xs, acc);
+  }
+  if (c < nsteps) fwd_step<WN, NRB, 0>(pp, brow, wp0, wp1, sp0, sp1, c, nsteps, xs, acc);
+}
+
 template <int WN>
 __device__ __forceinline__ void fwd_mainloop(const uint16_t* const (&brow)[FwdTile<WN>::PPT],
                                              const uint8_t* __restrict__ wcode,
-                                             const uint8_t* __restrict__ wscale, int K,
-                                             bool wave_live, uint16_t (*xs)[MT][LDS_ROW],
-                                             f32x16 (&acc)[2][4]) {
-  using FT = FwdTile<WN>;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int l32 = lane & 31, hlf = lane >> 5;
+                                             const uint8_t* __restrict__ wscale, int K, int nrb,
+                                             uint16_t (*xs)[MT][LDS_ROW], f32x16 (&acc)[2][4]) {
+  const int lane = threadIdx.x & 63;
+  const int hlf = lane >> 5;
   const int64_t KB = K / 2, KS = K / 32;
   const int nsteps = K / KC;
-  const u32x4 zero4 = {0u, 0u, 0u, 0u};
-
   const uint8_t* wp0 = wcode + hlf * 16;
   const uint8_t* wp1 = wp0 + 32 * KB;
   const uint8_t* sp0 = wscale + hlf;
@@ -71,73 +157,16 @@ __device__ __forceinline__ void fwd_mainloop(const uint16_t* const (&brow)[FwdTi
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[rb][tb][r] = 0.0f;
 
-  u32x4 xv[FT::PPT];
-  u32x4 wv0 = zero4, wv1 = zero4;
-  uint32_t s0 = 0, s1 = 0;
-#pragma unroll
-  for (int j = 0; j < FT::PPT; ++j)
-    xv[j] = brow[j] ? *reinterpret_cast<const u32x4*>(brow[j]) : zero4;
-  if (wave_live) {
-    wv0 = *reinterpret_cast<const u32x4*>(wp0);
-    wv1 = *reinterpret_cast<const u32x4*>(wp1);
-    s0 = sp0[0];
-    s1 = sp1[0];
-  }
-#pragma unroll
-  for (int j = 0; j < FT::PPT; ++j) {
-    int q = tid + j * FT::NTHR;
-    *reinterpret_cast<u32x4*>(&xs[0][q >> 3][(q & 7) * 8]) = xv[j];
-  }
-  __syncthreads();
-
-  for (int c = 0; c < nsteps; ++c) {
-    const int buf = c & 1;
-    const bool more = c + 1 < nsteps;
-    u32x4 nwv0 = zero4, nwv1 = zero4;
-    uint32_t ns0 = 0, ns1 = 0;
-    if (more) {
-#pragma unroll
-      for (int j = 0; j < FT::PPT; ++j)
-        xv[j] = brow[j] ? *reinterpret_cast<const u32x4*>(brow[j] + (c + 1) * KC) : zero4;
-      if (wave_live) {
-        nwv0 = *reinterpret_cast<const u32x4*>(wp0 + (c + 1) * 32);
-        nwv1 = *reinterpret_cast<const u32x4*>(wp1 + (c + 1) * 32);
-        ns0 = sp0[(c + 1) * 2];
-        ns1 = sp1[(c + 1) * 2];
-      }
-    }
-    if (wave_live) {
-      const float sc0 = scale_operand(s0), sc1 = scale_operand(s1);
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const bf16x8 a0 = as_bf16x8(dequant8_bf16(wv0[s], sc0));
-        const bf16x8 a1 = as_bf16x8(dequant8_bf16(wv1[s], sc1));
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-          const bf16x8 b =
-              *reinterpret_cast<const bf16x8*>(&xs[buf][tb * 32 + l32][hlf * 32 + s * 8]);
-          acc[0][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b, acc[0][tb], 0, 0, 0);
-          acc[1][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b, acc[1][tb], 0, 0, 0);
-        }
-      }
-    }
-    if (more) {
-#pragma unroll
-      for (int j = 0; j < FT::PPT; ++j) {
-        int q = tid + j * FT::NTHR;
-        *reinterpret_cast<u32x4*>(&xs[buf ^ 1][q >> 3][(q & 7) * 8]) = xv[j];
-      }
-      wv0 = nwv0;
-      wv1 = nwv1;
-      s0 = ns0;
-      s1 = ns1;
-    }
-    __syncthreads();
+  switch (nrb) {
+    case 1: fwd_mainloop_n<WN, 1>(brow, wp0, wp1, sp0, sp1, nsteps, xs, acc); break;
+    case 2: fwd_mainloop_n<WN, 2>(brow, wp0, wp1, sp0, sp1, nsteps, xs, acc); break;
+    case 3: fwd_mainloop_n<WN, 3>(brow, wp0, wp1, sp0, sp1, nsteps, xs, acc); break;
+    default: fwd_mainloop_n<WN, 4>(brow, wp0, wp1, sp0, sp1, nsteps, xs, acc); break;
   }
 }
 
 template <int WN>
-__global__ __launch_bounds__(64 * WN) void gate_up_kernel(
+__global__ __launch_bounds__(64 * WN, 2) void gate_up_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, const uint16_t* __restrict__ bias,
     const int32_t* __restrict__ sorted_rows, const Tile* __restrict__ tiles,
@@ -158,19 +187,15 @@ __global__ __launch_bounds__(64 * WN) void gate_up_kernel(
   for (int j = 0; j < FT::PPT; ++j) {
     int q = tid + j * FT::NTHR;
     int r = q >> 3;
-    if (r < tl.rows) {
-      int f = sorted_rows[tl.row0 + r];
-      brow[j] = x + (int64_t)(f / k) * H + (q & 7) * 8;
-    } else {
-      brow[j] = nullptr;
-    }
+    const int f = sorted_rows[tl.row0 + (r < tl.rows ? r : 0)];
+    brow[j] = x + (int64_t)(f / k) * H + (q & 7) * 8;
   }
-  const int wrow = n0 + wave * 64 + l32;
   const bool wave_live = n0 + wave * 64 < N;
+  const int wrow = (wave_live ? n0 + wave * 64 : 0) + l32;
   const uint8_t* wcode = codes + ((int64_t)e * N + wrow) * (H / 2);
   const uint8_t* wscale = scales + ((int64_t)e * N + wrow) * (H / 32);
   f32x16 acc[2][4];
-  fwd_mainloop<WN>(brow, wcode, wscale, H, wave_live, xs, acc);
+  fwd_mainloop<WN>(brow, wcode, wscale, H, (tl.rows + 31) / 32, xs, acc);
   if (!wave_live) return;
 
 #pragma unroll
@@ -207,7 +232,7 @@ __global__ __launch_bounds__(64 * WN) void gate_up_kernel(
 }
 
 template <int WN>
-__global__ __launch_bounds__(64 * WN) void down_kernel(
+__global__ __launch_bounds__(64 * WN, 2) void down_kernel(
     const uint16_t* __restrict__ a, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, const uint16_t* __restrict__ bias,
     const float* __restrict__ topk_w, const int32_t* __restrict__ sorted_rows,
@@ -228,14 +253,14 @@ __global__ __launch_bounds__(64 * WN) void down_kernel(
   for (int j = 0; j < FT::PPT; ++j) {
     int q = tid + j * FT::NTHR;
     int r = q >> 3;
-    brow[j] = (r < tl.rows) ? a + (int64_t)(tl.row0 + r) * I + (q & 7) * 8 : nullptr;
+    brow[j] = a + (int64_t)(tl.row0 + (r < tl.rows ? r : 0)) * I + (q & 7) * 8;
   }
-  const int wrow = n0 + wave * 64 + l32;
   const bool wave_live = n0 + wave * 64 < N;
+  const int wrow = (wave_live ? n0 + wave * 64 : 0) + l32;
   const uint8_t* wcode = codes + ((int64_t)e * N + wrow) * (I / 2);
   const uint8_t* wscale = scales + ((int64_t)e * N + wrow) * (I / 32);
   f32x16 acc[2][4];
-  fwd_mainloop<WN>(brow, wcode, wscale, I, wave_live, xs, acc);
+  fwd_mainloop<WN>(brow, wcode, wscale, I, (tl.rows + 31) / 32, xs, acc);
   if (!wave_live) return;
 
 #pragma unroll

@@ -15,64 +15,70 @@
 namespace mxmoe {
 
 constexpr int RT = ROUTER_TOKENS;
-constexpr int RH = 32;  // hidden elements staged per router step
 
 int router_blocks(int64_t T) { return (int)((T + RT - 1) / RT); }
 
-// One workgroup of 256 threads routes RT tokens.  Thread i owns expert
-// i % E for the tokens i / E, i / E + G, ... (G = 256 / E groups).  The
-// bf16 x fp32 products are exact in fp64 and are summed in fp64; the logit
-// is rounded once to fp32 and the top-k decision is taken on it.
+// One workgroup of 256 threads routes RT tokens.  Each of the four waves
+// takes a quarter of the hidden dimension; lane l owns the (token, expert)
+// pairs p = l + 64m (token p / E, expert p % E), so with E <= 64 a lane's
+// router-weight row is loaded once per step and used for RT*E/64 tokens.
+// The bf16 x fp32 products are exact in fp64 and are summed in fp64 (each
+// lane in h order within its quarter, then the four quarters in order);
+// the logit is rounded once to fp32 and the top-k decision is taken on it.
+template <int NPL>  // pairs per lane: ceil(RT * E / 64), rounded up to a power of two
 __global__ __launch_bounds__(256) void router_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ wr, const float* __restrict__ br,
     int T, int H, int E, int k, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
     int32_t* __restrict__ blk_hist) {
-  __shared__ float ws[RH][257];       // router weight chunk, [h][e]
-  __shared__ float xs[RT][RH + 1];    // activations chunk
-  __shared__ float lg[RT][257];       // logits
+  __shared__ double part[4][RT * 256];
+  __shared__ float lg[RT][257];
   __shared__ int32_t hist[256];
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t0 = blockIdx.x * RT;
-  const int G = 256 / E;              // token groups
-  const int e_own = tid % E;
-  const int g_own = tid / E;          // >= G: idle lane
-  constexpr int TPT = RT;             // upper bound of tokens per thread
-  double acc[TPT];
-#pragma unroll
-  for (int j = 0; j < TPT; ++j) acc[j] = 0.0;
+  const int P = RT * E;                   // pairs in this block
+  const int hq = H / 4;                   // this wave's share of h (H % 64 == 0)
+  const int h0 = wave * hq;
 
-  for (int h0 = 0; h0 < H; h0 += RH) {
-    for (int q = tid; q < E * RH; q += 256) {
-      int e = q / RH, hh = q % RH;
-      ws[hh][e] = wr[(int64_t)e * H + h0 + hh];
-    }
-    for (int q = tid; q < RT * RH; q += 256) {
-      int tt = q / RH, hh = q % RH;
-      int t = t0 + tt;
-      xs[tt][hh] = (t < T) ? bf16_to_f32(x[(int64_t)t * H + h0 + hh]) : 0.0f;
-    }
-    __syncthreads();
-    if (g_own < G) {
-      for (int hh = 0; hh < RH; ++hh) {
-        double wv = (double)ws[hh][e_own];
+  double acc[NPL];
+  int wo[NPL], xo[NPL];                   // element offsets of the pair's rows; -1 = none
 #pragma unroll
-        for (int j = 0; j < TPT; ++j) {
-          int tt = g_own + j * G;
-          if (tt < RT) acc[j] = fma((double)xs[tt][hh], wv, acc[j]);
-        }
-      }
-    }
-    __syncthreads();
+  for (int m = 0; m < NPL; ++m) {
+    acc[m] = 0.0;
+    const int p = lane + 64 * m;
+    const int tt = p / E, e = p % E;
+    const bool live = p < P && t0 + tt < T;
+    wo[m] = live ? e * H + h0 : -1;
+    xo[m] = live ? (t0 + tt) * H + h0 : -1;
   }
-  if (g_own < G) {
-    double b = br ? (double)br[e_own] : 0.0;
+  for (int h = 0; h < hq; h += 4) {
 #pragma unroll
-    for (int j = 0; j < TPT; ++j) {
-      int tt = g_own + j * G;
-      if (tt < RT) lg[tt][e_own] = (float)(acc[j] + b);
+    for (int m = 0; m < NPL; ++m) {
+      if (wo[m] < 0) continue;
+      const f32x4 wv = *reinterpret_cast<const f32x4*>(wr + wo[m] + h);
+      const u32x2 xv = *reinterpret_cast<const u32x2*>(x + (int64_t)xo[m] + h);
+      double a = acc[m];
+      a = fma((double)__uint_as_float(xv[0] << 16), (double)wv[0], a);
+      a = fma((double)__uint_as_float(xv[0] & 0xFFFF0000u), (double)wv[1], a);
+      a = fma((double)__uint_as_float(xv[1] << 16), (double)wv[2], a);
+      a = fma((double)__uint_as_float(xv[1] & 0xFFFF0000u), (double)wv[3], a);
+      acc[m] = a;
     }
+  }
+#pragma unroll
+  for (int m = 0; m < NPL; ++m) {
+    const int p = lane + 64 * m;
+    if (p < P) part[wave][p] = acc[m];
   }
   hist[tid] = 0;
+  __syncthreads();
+  for (int p = tid; p < P; p += 256) {
+    const int tt = p / E, e = p % E;
+    double v = part[0][p] + part[1][p];
+    v += part[2][p];
+    v += part[3][p];
+    if (br) v += (double)br[e];
+    lg[tt][e] = (float)v;
+  }
   __syncthreads();
 
   // top-k per token: k passes of an arg-max, ties to the lower index
@@ -211,8 +217,17 @@ __global__ __launch_bounds__(256) void tiles_kernel(const int32_t* __restrict__ 
 hipError_t launch_router(const uint16_t* x, const float* wr, const float* br, int T, int H,
                          int E, int k, int32_t* topk_idx, float* topk_w, int32_t* blk_hist,
                          hipStream_t s) {
-  hipLaunchKernelGGL(router_kernel, dim3(router_blocks(T)), dim3(256), 0, s, x, wr, br, T, H, E,
-                     k, topk_idx, topk_w, blk_hist);
+  const int npl = (RT * E + 63) / 64;
+  dim3 g(router_blocks(T)), b(256);
+#define ROUTER(N) hipLaunchKernelGGL(router_kernel<N>, g, b, 0, s, x, wr, br, T, H, E, k, \
+                                     topk_idx, topk_w, blk_hist)
+  if (npl <= 1) ROUTER(1);
+  else if (npl <= 2) ROUTER(2);
+  else if (npl <= 4) ROUTER(4);
+  else if (npl <= 8) ROUTER(8);
+  else if (npl <= 16) ROUTER(16);
+  else ROUTER(32);
+#undef ROUTER
   return hipGetLastError();
 }
 

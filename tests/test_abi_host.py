@@ -10,7 +10,8 @@ from mxfp4_weight_mixture_02_amd import native
 from mxfp4_weight_mixture_02_amd.native import Dims, Saved, Weights
 
 EXPECTED = {"mxfp4_moe_workspace_bytes", "mxfp4_moe_forward", "mxfp4_moe_backward_dx",
-            "mxfp4_quantize", "mxfp4_dequantize", "mxfp4_last_error"}
+            "mxfp4_quantize", "mxfp4_dequantize", "mxfp4_last_error",
+            "mxfp4_moe_kernel_timing", "mxfp4_moe_kernel_times"}
 
 
 @pytest.fixture(scope="module")
@@ -117,3 +118,10 @@ def test_quantize_validation(L):
     assert L.mxfp4_dequantize(FAKE, FAKE, 4, 64, 2, FAKE, None) == -1
     assert L.mxfp4_dequantize(FAKE, FAKE, 4, 40, 0, FAKE, None) == -2
     assert L.mxfp4_dequantize(FAKE, FAKE, 4, 64, 0, FAKE + 8, None) == -1
+
+
+def test_kernel_timing_toggles_without_gpu(L):
+    L.mxfp4_moe_kernel_timing.argtypes = [ctypes.c_int]
+    assert L.mxfp4_moe_kernel_timing(1) == 0
+    assert L.mxfp4_moe_kernel_times(None, None, None, 0) == 0   # nothing recorded
+    assert L.mxfp4_moe_kernel_timing(0) == 0
