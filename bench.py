@@ -42,6 +42,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=8)
+    ap.add_argument("--profile", action="store_true",
+                    help="for rocprofv3 runs: one 256 MiB device-to-device copy (a known-size "
+                         "calibration for the traffic counters), then warmup + steps of the "
+                         "forward + dX step, nothing else")
     return ap.parse_args()
 
 
@@ -115,6 +119,18 @@ def main():
 
     flops_pass = 2.0 * R * 3 * H * I
     flops_step = 2 * flops_pass
+
+    if args.profile:
+        src = torch.empty(64 << 20, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        for _ in range(args.warmup + args.steps):
+            step()
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_steps": args.steps, "copy_bytes": src.numel() * 4}), flush=True)
+        return
 
     for _ in range(args.warmup):
         step()

@@ -63,8 +63,9 @@ int check_dims(const mxfp4_moe_dims* d) {
   if (d->k > d->E || d->k > 8) return fail(MXFP4_EUNSUPPORTED, "k=%d must be <= min(E, 8)", d->k);
   if (d->T * d->k >= (int64_t(1) << 31))
     return fail(MXFP4_EUNSUPPORTED, "T*k = %lld routed rows exceed int32", (long long)(d->T * d->k));
-  if (d->H > (int64_t(1) << 20) || d->I > (int64_t(1) << 20))
-    return fail(MXFP4_EUNSUPPORTED, "H and I must be <= 2^20");
+  if (d->H > 8192 || d->I > (int64_t(1) << 20))
+    return fail(MXFP4_EUNSUPPORTED, "H must be <= 8192 and I <= 2^20 (H=%lld I=%lld)",
+                (long long)d->H, (long long)d->I);
   if (d->T * d->H >= (int64_t(1) << 31))
     return fail(MXFP4_EUNSUPPORTED, "T*H = %lld elements exceed int32", (long long)(d->T * d->H));
   if (d->lora_rank != 0)

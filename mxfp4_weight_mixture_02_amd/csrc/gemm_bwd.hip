@@ -127,9 +127,10 @@ __device__ __forceinline__ void bwd_step(BwdPipe<WN>& pp, const uint16_t* const 
   bwd_stage<WN, PAR ^ 1>(pp, wdst_next, xs);
 #pragma unroll
   for (int st = 0; st < 4; ++st) {
-    const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(&ws[PAR][wave * 64 + l32][hlf * 32 + st * 8]);
-    const bf16x8 a1 =
-        *reinterpret_cast<const bf16x8*>(&ws[PAR][wave * 64 + 32 + l32][hlf * 32 + st * 8]);
+    const int r0 = wave * 64 + l32, r1 = r0 + 32;
+    const int lcb = 4 * hlf + st;
+    const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(&ws[PAR][r0][(lcb ^ ((r0 >> 4) & 7)) * 8]);
+    const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(&ws[PAR][r1][(lcb ^ ((r1 >> 4) & 7)) * 8]);
 #pragma unroll
     for (int tb = 0; tb < NRB; ++tb) {
       const bf16x8 b = *reinterpret_cast<const bf16x8*>(&xs[PAR][tb * 32 + l32][hlf * 32 + st * 8]);
@@ -178,8 +179,12 @@ __device__ __forceinline__ void bwd_mainloop(const uint16_t* const (&brow)[BwdTi
   const int ocol = (o0 + 8 * ob < O) ? o0 + 8 * ob : 0;
   const uint8_t* bcode = wcode + (int64_t)(8 * cb) * crow + ocol / 2;
   const uint8_t* bscale = wscale + (int64_t)(8 * cb) * srow + ocol / 32;
-  uint16_t* const wdst0 = &ws[0][8 * ob][8 * cb];
-  uint16_t* const wdst1 = &ws[1][8 * ob][8 * cb];
+  // column block swizzle: 16-byte block c of row r sits at c ^ ((r >> 4) & 7),
+  // which spreads both these transposed writes and the MFMA reads over all
+  // banks (all 8 rows of this thread's block share r >> 4 = ob >> 1)
+  const int pcb = cb ^ ((ob >> 1) & 7);
+  uint16_t* const wdst0 = &ws[0][8 * ob][8 * pcb];
+  uint16_t* const wdst1 = &ws[1][8 * ob][8 * pcb];
 
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb)

@@ -18,71 +18,113 @@ constexpr int RT = ROUTER_TOKENS;
 
 int router_blocks(int64_t T) { return (int)((T + RT - 1) / RT); }
 
-// One workgroup of 256 threads routes RT tokens.  Each of the four waves
-// takes a quarter of the hidden dimension; lane l owns the (token, expert)
-// pairs p = l + 64m (token p / E, expert p % E), so with E <= 64 a lane's
-// router-weight row is loaded once per step and used for RT*E/64 tokens.
-// The bf16 x fp32 products are exact in fp64 and are summed in fp64 (each
-// lane in h order within its quarter, then the four quarters in order);
-// the logit is rounded once to fp32 and the top-k decision is taken on it.
-template <int NPL>  // pairs per lane: ceil(RT * E / 64), rounded up to a power of two
+// One workgroup of 256 threads routes RT tokens.  The tokens' activations
+// are staged in LDS once; each wave then takes experts wave, wave + 4, ...
+// and for each holds the expert's router-weight row in registers, spread
+// over the lanes along h (lane l owns h = 4l + 256j .. +3), while the other
+// expert's row is already in flight (two register sets, loop unrolled by
+// two).  Every lane forms partial dot products with all RT tokens; a
+// butterfly over the wave sums them.  The bf16 x fp32 products are exact in
+// fp64 and every partial and total sum is fp64; the logit is rounded once
+// to fp32 and the top-k decision is taken on it.
+constexpr int RCH = 12;             // float4 chunks of a row per lane: h < 256 * RCH = 3072
+constexpr int RH = 256 * RCH;
+
+__device__ __forceinline__ void router_load_row(f32x4 (&w)[RCH], const float* __restrict__ row,
+                                                int H, int h0, int lane) {
+#pragma unroll
+  for (int j = 0; j < RCH; ++j) {
+    const int h = h0 + 4 * lane + 256 * j;
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    w[j] = (h < H) ? *reinterpret_cast<const f32x4*>(row + h) : z;
+  }
+}
+
+__device__ __forceinline__ void router_dot_row(const f32x4 (&w)[RCH], const uint16_t* xs, int H,
+                                               int h0, int lane, double (&acc)[RT]) {
+#pragma unroll
+  for (int j = 0; j < RCH; ++j) {
+    const int h = h0 + 4 * lane + 256 * j;
+    if (h < H) {
+#pragma unroll
+      for (int tt = 0; tt < RT; ++tt) {
+        const u32x2 xv = *reinterpret_cast<const u32x2*>(xs + tt * H + h);
+        double a = acc[tt];
+        a = fma((double)__uint_as_float(xv[0] << 16), (double)w[j][0], a);
+        a = fma((double)__uint_as_float(xv[0] & 0xFFFF0000u), (double)w[j][1], a);
+        a = fma((double)__uint_as_float(xv[1] << 16), (double)w[j][2], a);
+        a = fma((double)__uint_as_float(xv[1] & 0xFFFF0000u), (double)w[j][3], a);
+        acc[tt] = a;
+      }
+    }
+  }
+}
+
+// Sum over the wave (fixed butterfly order) and store the RT logits of e.
+__device__ __forceinline__ void router_finish(double (&acc)[RT], int e, const float* br,
+                                              int lane, float (*lg)[257]) {
+#pragma unroll
+  for (int tt = 0; tt < RT; ++tt) {
+    double v = acc[tt];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    if (lane == 0) lg[tt][e] = (float)(v + (br ? (double)br[e] : 0.0));
+    acc[tt] = 0.0;
+  }
+}
+
 __global__ __launch_bounds__(256) void router_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ wr, const float* __restrict__ br,
     int T, int H, int E, int k, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
     int32_t* __restrict__ blk_hist) {
-  __shared__ double part[4][RT * 256];
+  extern __shared__ __attribute__((aligned(16))) uint16_t xs[];   // [RT][H]
   __shared__ float lg[RT][257];
   __shared__ int32_t hist[256];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t0 = blockIdx.x * RT;
-  const int P = RT * E;                   // pairs in this block
-  const int hq = H / 4;                   // this wave's share of h (H % 64 == 0)
-  const int h0 = wave * hq;
+  const int nt = min(RT, T - t0);
 
-  double acc[NPL];
-  int wo[NPL], xo[NPL];                   // element offsets of the pair's rows; -1 = none
-#pragma unroll
-  for (int m = 0; m < NPL; ++m) {
-    acc[m] = 0.0;
-    const int p = lane + 64 * m;
-    const int tt = p / E, e = p % E;
-    const bool live = p < P && t0 + tt < T;
-    wo[m] = live ? e * H + h0 : -1;
-    xo[m] = live ? (t0 + tt) * H + h0 : -1;
-  }
-  for (int h = 0; h < hq; h += 4) {
-#pragma unroll
-    for (int m = 0; m < NPL; ++m) {
-      if (wo[m] < 0) continue;
-      const f32x4 wv = *reinterpret_cast<const f32x4*>(wr + wo[m] + h);
-      const u32x2 xv = *reinterpret_cast<const u32x2*>(x + (int64_t)xo[m] + h);
-      double a = acc[m];
-      a = fma((double)__uint_as_float(xv[0] << 16), (double)wv[0], a);
-      a = fma((double)__uint_as_float(xv[0] & 0xFFFF0000u), (double)wv[1], a);
-      a = fma((double)__uint_as_float(xv[1] << 16), (double)wv[2], a);
-      a = fma((double)__uint_as_float(xv[1] & 0xFFFF0000u), (double)wv[3], a);
-      acc[m] = a;
-    }
-  }
-#pragma unroll
-  for (int m = 0; m < NPL; ++m) {
-    const int p = lane + 64 * m;
-    if (p < P) part[wave][p] = acc[m];
+  // stage the tokens (rows past T are zero)
+  const int row8 = H / 8;  // 16-byte pieces per row
+  for (int q = tid; q < RT * row8; q += 256) {
+    const int tt = q / row8, c = q % row8;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    reinterpret_cast<u32x4*>(xs)[q] =
+        tt < nt ? reinterpret_cast<const u32x4*>(x + (int64_t)(t0 + tt) * H)[c] : z;
   }
   hist[tid] = 0;
   __syncthreads();
-  for (int p = tid; p < P; p += 256) {
-    const int tt = p / E, e = p % E;
-    double v = part[0][p] + part[1][p];
-    v += part[2][p];
-    v += part[3][p];
-    if (br) v += (double)br[e];
-    lg[tt][e] = (float)v;
+
+  double acc[RT];
+#pragma unroll
+  for (int tt = 0; tt < RT; ++tt) acc[tt] = 0.0;
+  f32x4 w0[RCH], w1[RCH];
+  if (H <= RH) {
+    // whole rows in registers; the next expert's row loads during this one
+    int e = wave;
+    if (e < E) router_load_row(w0, wr + (int64_t)e * H, H, 0, lane);
+    for (; e < E; e += 8) {
+      if (e + 4 < E) router_load_row(w1, wr + (int64_t)(e + 4) * H, H, 0, lane);
+      router_dot_row(w0, xs, H, 0, lane, acc);
+      router_finish(acc, e, br, lane, lg);
+      if (e + 4 >= E) break;
+      if (e + 8 < E) router_load_row(w0, wr + (int64_t)(e + 8) * H, H, 0, lane);
+      router_dot_row(w1, xs, H, 0, lane, acc);
+      router_finish(acc, e + 4, br, lane, lg);
+    }
+  } else {
+    for (int e = wave; e < E; e += 4) {
+      for (int h0 = 0; h0 < H; h0 += RH) {
+        router_load_row(w0, wr + (int64_t)e * H, H, h0, lane);
+        router_dot_row(w0, xs, H, h0, lane, acc);
+      }
+      router_finish(acc, e, br, lane, lg);
+    }
   }
   __syncthreads();
 
   // top-k per token: k passes of an arg-max, ties to the lower index
-  if (tid < RT && t0 + tid < T) {
+  if (tid < nt) {
     const int tt = tid;
     uint64_t taken[4] = {0, 0, 0, 0};
     float sel[8];
@@ -217,17 +259,9 @@ __global__ __launch_bounds__(256) void tiles_kernel(const int32_t* __restrict__ 
 hipError_t launch_router(const uint16_t* x, const float* wr, const float* br, int T, int H,
                          int E, int k, int32_t* topk_idx, float* topk_w, int32_t* blk_hist,
                          hipStream_t s) {
-  const int npl = (RT * E + 63) / 64;
-  dim3 g(router_blocks(T)), b(256);
-#define ROUTER(N) hipLaunchKernelGGL(router_kernel<N>, g, b, 0, s, x, wr, br, T, H, E, k, \
-                                     topk_idx, topk_w, blk_hist)
-  if (npl <= 1) ROUTER(1);
-  else if (npl <= 2) ROUTER(2);
-  else if (npl <= 4) ROUTER(4);
-  else if (npl <= 8) ROUTER(8);
-  else if (npl <= 16) ROUTER(16);
-  else ROUTER(32);
-#undef ROUTER
+  const size_t lds = (size_t)RT * H * sizeof(uint16_t);
+  hipLaunchKernelGGL(router_kernel, dim3(router_blocks(T)), dim3(256), lds, s, x, wr, br, T, H, E,
+                     k, topk_idx, topk_w, blk_hist);
   return hipGetLastError();
 }
 
