@@ -63,9 +63,9 @@ int check_dims(const mxfp4_moe_dims* d) {
   if (d->k > d->E || d->k > 8) return fail(MXFP4_EUNSUPPORTED, "k=%d must be <= min(E, 8)", d->k);
   if (d->T * d->k >= (int64_t(1) << 31))
     return fail(MXFP4_EUNSUPPORTED, "T*k = %lld routed rows exceed int32", (long long)(d->T * d->k));
-  if (d->H > 8192 || d->I > (int64_t(1) << 20))
-    return fail(MXFP4_EUNSUPPORTED, "H must be <= 8192 and I <= 2^20 (H=%lld I=%lld)",
-                (long long)d->H, (long long)d->I);
+  if (d->H > 5120 || d->I > 5120 || !mxmoe::fwd_step_k((int)d->H) || !mxmoe::fwd_step_k((int)d->I))
+    return fail(MXFP4_EUNSUPPORTED, "H and I must be <= 5120 (H=%lld I=%lld)", (long long)d->H,
+                (long long)d->I);
   if (d->T * d->H >= (int64_t(1) << 31))
     return fail(MXFP4_EUNSUPPORTED, "T*H = %lld elements exceed int32", (long long)(d->T * d->H));
   if (d->lora_rank != 0)
@@ -109,8 +109,9 @@ int check_weights(const mxfp4_moe_weights* w) {
   if (!w) return fail(MXFP4_EINVAL, "weights is NULL");
   if (!w->router_w || !w->gu_codes || !w->gu_scales || !w->dn_codes || !w->dn_scales)
     return fail(MXFP4_EINVAL, "router_w, gu_codes, gu_scales, dn_codes and dn_scales are required");
-  if (!aligned(w->router_w, 16) || !aligned(w->gu_codes, 16) || !aligned(w->dn_codes, 16))
-    return fail(MXFP4_EINVAL, "router_w, gu_codes and dn_codes must be 16-byte aligned");
+  if (!aligned(w->router_w, 16) || !aligned(w->gu_codes, 16) || !aligned(w->dn_codes, 16) ||
+      !aligned(w->gu_scales, 16) || !aligned(w->dn_scales, 16))
+    return fail(MXFP4_EINVAL, "router_w and the codes and scales must be 16-byte aligned");
   if ((w->gu_bias && !aligned(w->gu_bias, 2)) || (w->dn_bias && !aligned(w->dn_bias, 2)))
     return fail(MXFP4_EINVAL, "biases must be 2-byte aligned");
   return MXFP4_OK;

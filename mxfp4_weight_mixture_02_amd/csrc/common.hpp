@@ -82,6 +82,22 @@ __device__ __forceinline__ void swiglu_grad(float g, float u, float da, float al
   *du = (u >= -limit && u <= limit) ? duc : 0.0f;
 }
 
+// s_waitcnt immediate: wait until at most vm vector-memory and lgkm LDS /
+// scalar-memory operations of this wave are outstanding (expcnt untouched).
+__device__ constexpr int waitcnt_imm(int vm, int lgkm) {
+  return (vm & 15) | (7 << 4) | ((lgkm & 15) << 8) | ((vm >> 4) << 14);
+}
+
+// Workgroup barrier without the memory fence of __syncthreads(): that fence
+// makes the compiler wait for every outstanding global load first, which
+// would drain a software pipeline's prefetches at every step.  Callers wait
+// for exactly the loads and LDS writes the other waves need before calling.
+__device__ __forceinline__ void barrier_only() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // One tile of routed rows of one expert for the grouped GEMMs.
 struct Tile {
   int32_t expert;
@@ -89,6 +105,27 @@ struct Tile {
   int32_t rows;  // 1..MT
   int32_t pad;
 };
+
+// Work item of a grouped-GEMM workgroup.  Workgroups are dealt to the 8
+// XCDs round-robin by block index, and each XCD has its own L2.  With L live
+// work items (row tiles x column tiles, column tile fastest), XCD i gets the
+// contiguous range of items [start_i, start_i + L/8 (+1)), so the column
+// tiles of a row tile (same activations) and consecutive row tiles of an
+// expert (same weights) run together on one L2.  Returns false for blocks
+// past the live items.
+__device__ __forceinline__ bool xcd_work_item(int live_row_tiles, int col_tiles, int* row_tile,
+                                              int* col_tile) {
+  const int L = live_row_tiles * col_tiles;
+  const int b = blockIdx.x;
+  if (b >= L) return false;
+  const int xcd = b & 7, idx = b >> 3;
+  const int base = L >> 3, extra = L & 7;
+  const int start = xcd * base + min(xcd, extra);
+  const int item = start + idx;
+  *row_tile = item / col_tiles;
+  *col_tile = item % col_tiles;
+  return true;
+}
 
 constexpr int MT = 128;      // routed rows per GEMM tile
 constexpr int KC = 64;       // K elements per main-loop step

@@ -124,6 +124,7 @@ __device__ __forceinline__ void bwd_step(BwdPipe<WN>& pp, const uint16_t* const 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hlf = lane >> 5;
   bwd_issue<WN, PAR>(pp, brow, bcode, bscale, crow, srow, min(c + 2, nsteps - 1));
+  __builtin_amdgcn_sched_barrier(0);  // keep the loads at the top of the step
   bwd_stage<WN, PAR ^ 1>(pp, wdst_next, xs);
 #pragma unroll
   for (int st = 0; st < 4; ++st) {
@@ -213,9 +214,11 @@ __global__ __launch_bounds__(64 * WN) void bwd_down_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t ws[2][BT::NT][LDS_ROW];
   __shared__ __attribute__((aligned(16))) uint16_t xs[2][MT][LDS_ROW];
   __shared__ float red[WN][MT];
-  if ((int)blockIdx.y >= *num_tiles) return;
-  const Tile tl = tiles[blockIdx.y];
-  const int o0 = blockIdx.x * BT::NT;
+  int mt, ot;
+  const int otiles = (I + BT::NT - 1) / BT::NT;
+  if (!xcd_work_item(*num_tiles, otiles, &mt, &ot)) return;
+  const Tile tl = tiles[mt];
+  const int o0 = ot * BT::NT;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hlf = lane >> 5;
   const int e = tl.expert;
@@ -277,7 +280,7 @@ __global__ __launch_bounds__(64 * WN) void bwd_down_kernel(
 #pragma unroll
     for (int w = 0; w < WN; ++w) s += red[w][tid];
     const int64_t f = sorted_rows[tl.row0 + tid];
-    dw_part[f * gridDim.x + blockIdx.x] = s;
+    dw_part[f * otiles + ot] = s;
   }
 }
 
@@ -290,9 +293,11 @@ __global__ __launch_bounds__(64 * WN) void bwd_gate_up_kernel(
   using BT = BwdTile<WN>;
   __shared__ __attribute__((aligned(16))) uint16_t ws[2][BT::NT][LDS_ROW];
   __shared__ __attribute__((aligned(16))) uint16_t xs[2][MT][LDS_ROW];
-  if ((int)blockIdx.y >= *num_tiles) return;
-  const Tile tl = tiles[blockIdx.y];
-  const int o0 = blockIdx.x * BT::NT;
+  int mt, ot;
+  const int otiles = (H + BT::NT - 1) / BT::NT;
+  if (!xcd_work_item(*num_tiles, otiles, &mt, &ot)) return;
+  const Tile tl = tiles[mt];
+  const int o0 = ot * BT::NT;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hlf = lane >> 5;
   const int e = tl.expert;
@@ -400,7 +405,7 @@ hipError_t launch_bwd_down(const uint16_t* dy, const uint8_t* codes, const uint8
                            const int32_t* num_tiles, int max_tiles, const uint16_t* h,
                            const uint16_t* a, int H, int I, int k, float alpha, float limit,
                            uint16_t* dh, float* dw_part, hipStream_t s) {
-  dim3 grid(bwd_down_ntiles(I), max_tiles);
+  dim3 grid(bwd_down_ntiles(I) * max_tiles);
   hipLaunchKernelGGL(bwd_down_kernel<BWD_WN>, grid, dim3(64 * BWD_WN), 0, s, dy, codes, scales,
                      topk_w, sorted_rows, tiles, num_tiles, h, a, H, I, k, alpha, limit, dh,
                      dw_part);
@@ -412,7 +417,7 @@ hipError_t launch_bwd_gate_up(const uint16_t* dh, const uint8_t* codes, const ui
                               const int32_t* num_tiles, int max_tiles, int H, int I,
                               float* dxr, hipStream_t s) {
   constexpr int NT = BwdTile<BWD_WN>::NT;
-  dim3 grid((H + NT - 1) / NT, max_tiles);
+  dim3 grid(((H + NT - 1) / NT) * max_tiles);
   hipLaunchKernelGGL(bwd_gate_up_kernel<BWD_WN>, grid, dim3(64 * BWD_WN), 0, s, dh, codes,
                      scales, sorted_rows, tiles, num_tiles, H, I, dxr);
   return hipGetLastError();

@@ -9,23 +9,39 @@
 //          the routing weight and written to the routed row's own slot, so
 //          the combine can sum a token's k slots in a fixed order.
 //
-// Tiling (per workgroup): MT = 128 routed rows of one expert x 64*WN weight
-// rows; WN waves, each owning 64 weight rows (two 32-row MFMA blocks) for
-// all 128 rows (four 32-column blocks): 8 accumulators of 32x32 fp32.
-// The product is computed transposed, D[n][p] = W[n][:] . X[p][:], so that
-// the weights are the MFMA A-operand: each lane loads 16 bytes (32 codes)
-// of one weight row straight from global memory and decodes them in
-// registers with the scaled fp4->bf16 conversion (one UE8M0 scale per 32
-// codes); nothing of the weights goes through LDS and no lane decodes a
-// weight another lane also decodes.  The routed activation rows are the
-// B-operand, staged through LDS (double buffered, one barrier per 64-wide
-// K step) because every wave reads all 128 of them.
+// Tiling.  A workgroup computes MT = 128 routed rows of one expert against
+// NT = 512 weight rows with 4 waves, one per SIMD; wave w owns weight rows
+// 128w..128w+127 (four 32-row MFMA blocks) for all 128 routed rows (four
+// 32-column blocks): 16 accumulators of 32x32 fp32 in the accumulation
+// registers, which a single wave per SIMD may use in full.  Each decoded
+// weight fragment and each activation fragment read from LDS feeds four
+// MFMAs.  The product is computed transposed, D[n][p] = W[n][:] . X[p][:],
+// so the weights are the MFMA A-operand: a lane reads its weight rows
+// straight from global memory and decodes the codes in registers with the
+// scaled fp4 -> bf16 conversion; no weight passes through LDS and no weight
+// is decoded twice.  The routed activation rows are the B-operand, shared
+// by the four waves through LDS.  The 512 x (K/32) UE8M0 scale panel of the
+// workgroup's weight rows is one contiguous span of memory; it is copied
+// into LDS once.
 //
-// K order inside a 64-wide step: lane half h (lanes 32h..32h+31) holds the
-// codes of elements 32h..32h+31 and feeds elements 32h+8s..32h+8s+7 to MFMA
-// step s; the B-operand reads the same elements, so each MFMA contracts
-// matching K indices (the hardware pairs A and B by lane group and
-// register slot).
+// Pipeline.  K advances in steps of 64; loads run NST - 1 steps ahead: the
+// activations of a step go straight from global memory into one of NST LDS
+// stages (the gfx950 global-to-LDS load; no registers), the lane's codes
+// into one of NST register slots.  In step c a wave issues the loads of
+// step c + NST - 1, runs the MFMAs of step c, waits until its loads of step
+// c + 1 have landed, and meets the others at the step's one barrier.  The
+// loop is unrolled by NST so every stage and slot has a fixed name; loads
+// are never under a branch (rows past the tile or past N are clamped to
+// valid rows, their results dropped), so the compiler's own wait counts
+// stay exact.
+//
+// K order inside a step: lane half h (lanes 32h..32h+31) holds the codes of
+// elements 32h..32h+31 of its row and feeds elements 32h+8s..32h+8s+7 to MFMA
+// sub-step s; the B-operand reads the same elements, so each MFMA contracts
+// matching K indices (the hardware pairs A and B by lane group and register
+// slot).  An activation row of a stage is 128 bytes = eight 16-byte slots;
+// column block g of row r sits in slot g ^ ((r >> 1) & 7), which makes the
+// 16 rows a half-wave reads land on 16 distinct bank groups.
 //
 // In the 32x32 accumulator a lane holds column p = lane % 32 and rows
 // 8*(r/4) + 4*(lane/32) + r%4 for r = 0..15: gate/up pairs (2j, 2j+1) sit in
@@ -35,172 +51,199 @@
 
 namespace mxmoe {
 
-template <int WN>
-struct FwdTile {
-  static constexpr int NTHR = 64 * WN;
-  static constexpr int NT = 64 * WN;             // weight rows per workgroup
-  static constexpr int PPT = MT * 8 / NTHR;      // 16-byte B pieces per thread per step
-};
+constexpr int FWN = 4;                 // waves per workgroup, one per SIMD
+constexpr int FRB = 4;                 // 32-row weight blocks per wave
+constexpr int FNTHR = 64 * FWN;
+constexpr int FNT = 32 * FRB * FWN;    // weight rows per workgroup (512)
+constexpr int LDS_BYTES = 160 * 1024;  // gfx950 LDS per workgroup
+constexpr int FKS = 64;                // K per step
+constexpr int NST = 4;                 // pipeline stages
+constexpr int XSTAGE = MT * FKS * 2;   // bytes of one activation stage (16 KB)
+constexpr int XCHUNKS = XSTAGE / 1024 / FWN;    // 1 KB global-to-LDS chunks per wave per step
+constexpr int PANEL_MAX = LDS_BYTES - NST * XSTAGE;
+constexpr int FWD_MAXK = PANEL_MAX / FNT * 32;   // largest K whose scale panel fits
+constexpr int LOADS_PER_STEP = XCHUNKS + FRB;    // vector loads a lane issues per step
 
-// Main loop shared by both forward GEMMs.  brow[j] points at the start of
-// the activation row for B piece j (already offset by its 8-element piece);
-// rows past the tile point at the tile's first row, so every load is
-// unconditional (their columns of the product are never stored).  Only the
-// first NRB 32-row blocks of the tile hold rows: the MFMAs of the others
-// are not issued.  wcode/wscale point at this lane's first weight row
-// (row block 0) and are valid even for a wave past the last weight row,
-// whose results are dropped.
-//
-// Pipeline: global loads run two K steps ahead.  In step c the lane decodes
-// the weights of step c (loaded two steps earlier), issues the loads of step
-// c+2 into the registers just freed, writes the activations of step c+1
-// (loaded one step earlier) into the other LDS buffer, then runs the MFMAs
-// of step c; one barrier per step.  Near the end the step index of a load
-// is clamped to the last step instead of branching, so the compiler's wait
-// counts stay exact (a branch around a load makes it wait for all loads).
-// The loop is unrolled by two so every register set has a fixed name.
-template <int WN>
+__device__ constexpr int vmcnt_imm(int n) { return waitcnt_imm(n, 15); }
+
 struct FwdPipe {
-  using FT = FwdTile<WN>;
-  u32x4 xv[2][FT::PPT];  // activation pieces, by step parity
-  u32x4 wv[2][2];        // raw codes, [parity][row block]
-  uint32_t sv[2][2];     // raw scales
+  const uint16_t* xrow[XCHUNKS];   // activation rows this lane stages
+  int xcol[XCHUNKS];               // element offset of its 16-byte slot within a step
+  const uint8_t* wp;               // this lane's codes, row block 0 (+ lane half)
+  int64_t rbstride;                // bytes between its row blocks (32 rows)
+  const uint8_t* srow;             // scale panel row of row block 0 in LDS
+  int sbstride;                    // panel bytes between row blocks
+  uint8_t* xs;                     // LDS stages
+  int nsteps;
 };
 
-template <int WN, int PAR>
-__device__ __forceinline__ void fwd_issue(FwdPipe<WN>& pp, const uint16_t* const (&brow)[FwdTile<WN>::PPT],
-                                          const uint8_t* wp0, const uint8_t* wp1,
-                                          const uint8_t* sp0, const uint8_t* sp1, int c) {
+// Loads of step c into stage/slot SL: activations global -> LDS directly,
+// codes into registers.
+template <int SL>
+__device__ __forceinline__ void fwd_issue(const FwdPipe& p, u32x4 (&codes)[NST][FRB], int c) {
+  const int wave = threadIdx.x >> 6;
 #pragma unroll
-  for (int j = 0; j < FwdTile<WN>::PPT; ++j)
-    pp.xv[PAR][j] = *reinterpret_cast<const u32x4*>(brow[j] + c * KC);
-  pp.wv[PAR][0] = *reinterpret_cast<const u32x4*>(wp0 + c * 32);
-  pp.wv[PAR][1] = *reinterpret_cast<const u32x4*>(wp1 + c * 32);
-  pp.sv[PAR][0] = sp0[c * 2];
-  pp.sv[PAR][1] = sp1[c * 2];
+  for (int j = 0; j < XCHUNKS; ++j)
+    __builtin_amdgcn_global_load_lds(p.xrow[j] + c * FKS + p.xcol[j],
+                                     p.xs + SL * XSTAGE + (XCHUNKS * wave + j) * 1024, 16, 0, 0);
+#pragma unroll
+  for (int rb = 0; rb < FRB; ++rb)
+    codes[SL][rb] = *reinterpret_cast<const u32x4*>(p.wp + rb * p.rbstride + c * 32);
 }
 
-template <int WN, int PAR>
-__device__ __forceinline__ void fwd_stage_x(const FwdPipe<WN>& pp, uint16_t (*xs)[MT][LDS_ROW]) {
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int j = 0; j < FwdTile<WN>::PPT; ++j) {
-    int q = tid + j * FwdTile<WN>::NTHR;
-    *reinterpret_cast<u32x4*>(&xs[PAR][q >> 3][(q & 7) * 8]) = pp.xv[PAR][j];
-  }
-}
-
-template <int WN, int NRB, int PAR>
-__device__ __forceinline__ void fwd_step(FwdPipe<WN>& pp, const uint16_t* const (&brow)[FwdTile<WN>::PPT],
-                                         const uint8_t* wp0, const uint8_t* wp1,
-                                         const uint8_t* sp0, const uint8_t* sp1, int c, int nsteps,
-                                         uint16_t (*xs)[MT][LDS_ROW], f32x16 (&acc)[2][4]) {
+template <int SL, int NRB>
+__device__ __forceinline__ void fwd_compute(const FwdPipe& p, const u32x4 (&codes)[NST][FRB], int c,
+                                            f32x16 (&acc)[FRB][4]) {
   const int lane = threadIdx.x & 63;
   const int l32 = lane & 31, hlf = lane >> 5;
-  bf16x8 a[2][4];
-  const float sc0 = scale_operand(pp.sv[PAR][0]), sc1 = scale_operand(pp.sv[PAR][1]);
+  float sc[FRB];
 #pragma unroll
-  for (int st = 0; st < 4; ++st) {
-    a[0][st] = as_bf16x8(dequant8_bf16(pp.wv[PAR][0][st], sc0));
-    a[1][st] = as_bf16x8(dequant8_bf16(pp.wv[PAR][1][st], sc1));
-  }
-  fwd_issue<WN, PAR>(pp, brow, wp0, wp1, sp0, sp1, min(c + 2, nsteps - 1));
-  fwd_stage_x<WN, PAR ^ 1>(pp, xs);
+  for (int rb = 0; rb < FRB; ++rb) sc[rb] = scale_operand(p.srow[rb * p.sbstride + 2 * c + hlf]);
+  const uint8_t* st = p.xs + SL * XSTAGE;
 #pragma unroll
-  for (int st = 0; st < 4; ++st) {
+  for (int s = 0; s < 4; ++s) {
+    const int g = 4 * hlf + s;
+    bf16x8 b[NRB];
 #pragma unroll
     for (int tb = 0; tb < NRB; ++tb) {
-      const bf16x8 b = *reinterpret_cast<const bf16x8*>(&xs[PAR][tb * 32 + l32][hlf * 32 + st * 8]);
-      acc[0][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0][st], b, acc[0][tb], 0, 0, 0);
-      acc[1][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1][st], b, acc[1][tb], 0, 0, 0);
+      const int r = tb * 32 + l32;
+      b[tb] = *reinterpret_cast<const bf16x8*>(st + r * 128 + 16 * (g ^ ((r >> 1) & 7)));
+    }
+#pragma unroll
+    for (int rb = 0; rb < FRB; ++rb) {
+      const bf16x8 a = as_bf16x8(dequant8_bf16(codes[SL][rb][s], sc[rb]));
+#pragma unroll
+      for (int tb = 0; tb < NRB; ++tb)
+        acc[rb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[tb], acc[rb][tb], 0, 0, 0);
     }
   }
-  __syncthreads();
 }
 
-template <int WN, int NRB>
-__device__ __forceinline__ void fwd_mainloop_n(const uint16_t* const (&brow)[FwdTile<WN>::PPT],
-                                               const uint8_t* wp0, const uint8_t* wp1,
-                                               const uint8_t* sp0, const uint8_t* sp1, int nsteps,
-                                               uint16_t (*xs)[MT][LDS_ROW], f32x16 (&acc)[2][4]) {
-  FwdPipe<WN> pp;
-  fwd_issue<WN, 0>(pp, brow, wp0, wp1, sp0, sp1, 0);
-  fwd_issue<WN, 1>(pp, brow, wp0, wp1, sp0, sp1, min(1, nsteps - 1));
-  fwd_stage_x<WN, 0>(pp, xs);
-  __syncthreads();
+// One pipeline step: issue step c + NST - 1, compute step c, wait for this
+// wave's loads of step c + 1, barrier.  A lane issues LOADS_PER_STEP vector
+// loads per step (activations first, then codes), in step order, so after
+// issuing step c + NST - 1 the loads newer than step c + 1's activations
+// number FRB + LOADS_PER_STEP * (NST - 2).
+template <int SL, int NRB>
+__device__ __forceinline__ void fwd_step(const FwdPipe& p, u32x4 (&codes)[NST][FRB], int c,
+                                         f32x16 (&acc)[FRB][4]) {
+  fwd_issue<(SL + NST - 1) % NST>(p, codes, min(c + NST - 1, p.nsteps - 1));
+  __builtin_amdgcn_sched_barrier(0);
+  fwd_compute<SL, NRB>(p, codes, c, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(FRB + LOADS_PER_STEP * (NST - 2)));
+  barrier_only();
+}
+
+template <int NRB>
+__device__ __forceinline__ void fwd_loop(const FwdPipe& p, f32x16 (&acc)[FRB][4]) {
+  u32x4 codes[NST][FRB];
+  const int last = p.nsteps - 1;
+  fwd_issue<0>(p, codes, 0);
+  fwd_issue<1>(p, codes, min(1, last));
+  fwd_issue<2>(p, codes, min(2, last));
+  // the scale panel was written with ordinary LDS stores
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(FRB + LOADS_PER_STEP * (NST - 2), 0));
+  barrier_only();
   int c = 0;
-  for (; c + 1 < nsteps; c += 2) {
-    fwd_step<WN, NRB, 0>(pp, brow, wp0, wp1, sp0, sp1, c, nsteps, xs, acc);
-    fwd_step<WN, NRB, 1>(pp, brow, wp0, wp1, sp0, sp1, c + 1, nsteps, xs, acc);
+  for (; c + NST <= p.nsteps; c += NST) {
+    fwd_step<0, NRB>(p, codes, c + 0, acc);
+    fwd_step<1, NRB>(p, codes, c + 1, acc);
+    fwd_step<2, NRB>(p, codes, c + 2, acc);
+    fwd_step<3, NRB>(p, codes, c + 3, acc);
   }
-  if (c < nsteps) fwd_step<WN, NRB, 0>(pp, brow, wp0, wp1, sp0, sp1, c, nsteps, xs, acc);
+  const int rem = p.nsteps - c;
+  if (rem > 0) fwd_step<0, NRB>(p, codes, c + 0, acc);
+  if (rem > 1) fwd_step<1, NRB>(p, codes, c + 1, acc);
+  if (rem > 2) fwd_step<2, NRB>(p, codes, c + 2, acc);
+  // drain: nothing may still be writing LDS when the workgroup ends
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 }
 
-template <int WN>
-__device__ __forceinline__ void fwd_mainloop(const uint16_t* const (&brow)[FwdTile<WN>::PPT],
-                                             const uint8_t* __restrict__ wcode,
-                                             const uint8_t* __restrict__ wscale, int K, int nrb,
-                                             uint16_t (*xs)[MT][LDS_ROW], f32x16 (&acc)[2][4]) {
-  const int lane = threadIdx.x & 63;
+// Shared body of both forward GEMMs up to the accumulators.  xrow[j]: the
+// activation row this lane stages for chunk j (clamped to the tile's first
+// row past the tile).  wrow_local: first weight row of this lane within the
+// workgroup's rows (row blocks follow 32 rows apart; clamped for waves past
+// N).
+__device__ __forceinline__ void fwd_body(const uint16_t* const (&xrow)[XCHUNKS],
+                                         const uint8_t* __restrict__ codes_e,
+                                         const uint8_t* __restrict__ scales_e, int K, int n0,
+                                         int nrows, int wrow_local, int nrb, uint8_t* lds,
+                                         f32x16 (&acc)[FRB][4]) {
+  static_assert(NST == 4, "the main loop is unrolled for 4 stages");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hlf = lane >> 5;
-  const int64_t KB = K / 2, KS = K / 32;
-  const int nsteps = K / KC;
-  const uint8_t* wp0 = wcode + hlf * 16;
-  const uint8_t* wp1 = wp0 + 32 * KB;
-  const uint8_t* sp0 = wscale + hlf;
-  const uint8_t* sp1 = sp0 + 32 * KS;
+  uint8_t* panel = lds + NST * XSTAGE;
+  const int KB32 = K / 32;
 
+  // scale panel: nrows * K/32 contiguous bytes, 16-byte aligned
+  {
+    const u32x4* src = reinterpret_cast<const u32x4*>(scales_e + (int64_t)n0 * KB32);
+    u32x4* dst = reinterpret_cast<u32x4*>(panel);
+    const int n16 = nrows * KB32 / 16;
+    for (int q = tid; q < n16; q += FNTHR) dst[q] = src[q];
+  }
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
+  for (int rb = 0; rb < FRB; ++rb)
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[rb][tb][r] = 0.0f;
 
+  FwdPipe p;
+#pragma unroll
+  for (int j = 0; j < XCHUNKS; ++j) {
+    const int row = (XCHUNKS * wave + j) * 8 + lane / 8;   // row of the tile this lane stages
+    p.xrow[j] = xrow[j];
+    p.xcol[j] = 8 * ((lane & 7) ^ ((row >> 1) & 7));       // global column block of its slot
+  }
+  const int64_t rowbytes = K / 2;
+  p.wp = codes_e + (int64_t)(n0 + wrow_local) * rowbytes + hlf * 16;
+  p.rbstride = 32 * rowbytes;
+  p.srow = panel + wrow_local * KB32;
+  p.sbstride = 32 * KB32;
+  p.xs = lds;
+  p.nsteps = K / FKS;
   switch (nrb) {
-    case 1: fwd_mainloop_n<WN, 1>(brow, wp0, wp1, sp0, sp1, nsteps, xs, acc); break;
-    case 2: fwd_mainloop_n<WN, 2>(brow, wp0, wp1, sp0, sp1, nsteps, xs, acc); break;
-    case 3: fwd_mainloop_n<WN, 3>(brow, wp0, wp1, sp0, sp1, nsteps, xs, acc); break;
-    default: fwd_mainloop_n<WN, 4>(brow, wp0, wp1, sp0, sp1, nsteps, xs, acc); break;
+    case 1: fwd_loop<1>(p, acc); break;
+    case 2: fwd_loop<2>(p, acc); break;
+    case 3: fwd_loop<3>(p, acc); break;
+    default: fwd_loop<4>(p, acc); break;
   }
 }
 
-template <int WN>
-__global__ __launch_bounds__(64 * WN, 2) void gate_up_kernel(
+__global__ __launch_bounds__(FNTHR) void gate_up_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, const uint16_t* __restrict__ bias,
     const int32_t* __restrict__ sorted_rows, const Tile* __restrict__ tiles,
     const int32_t* __restrict__ num_tiles, int H, int I, int k, float alpha, float limit,
     uint16_t* __restrict__ h_out, uint16_t* __restrict__ a_out) {
-  using FT = FwdTile<WN>;
-  __shared__ __attribute__((aligned(16))) uint16_t xs[2][MT][LDS_ROW];
-  if ((int)blockIdx.y >= *num_tiles) return;
-  const Tile tl = tiles[blockIdx.y];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
   const int N = 2 * I;
-  const int n0 = blockIdx.x * FT::NT;
+  int mt, nt;
+  if (!xcd_work_item(*num_tiles, (N + FNT - 1) / FNT, &mt, &nt)) return;
+  const Tile tl = tiles[mt];
+  const int n0 = nt * FNT;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hlf = lane >> 5;
   const int e = tl.expert;
 
-  const uint16_t* brow[FT::PPT];
+  const uint16_t* xrow[XCHUNKS];
 #pragma unroll
-  for (int j = 0; j < FT::PPT; ++j) {
-    int q = tid + j * FT::NTHR;
-    int r = q >> 3;
+  for (int j = 0; j < XCHUNKS; ++j) {
+    const int r = (XCHUNKS * wave + j) * 8 + lane / 8;
     const int f = sorted_rows[tl.row0 + (r < tl.rows ? r : 0)];
-    brow[j] = x + (int64_t)(f / k) * H + (q & 7) * 8;
+    xrow[j] = x + (int64_t)(f / k) * H;
   }
-  const bool wave_live = n0 + wave * 64 < N;
-  const int wrow = (wave_live ? n0 + wave * 64 : 0) + l32;
-  const uint8_t* wcode = codes + ((int64_t)e * N + wrow) * (H / 2);
-  const uint8_t* wscale = scales + ((int64_t)e * N + wrow) * (H / 32);
-  f32x16 acc[2][4];
-  fwd_mainloop<WN>(brow, wcode, wscale, H, (tl.rows + 31) / 32, xs, acc);
-  if (!wave_live) return;
-
+  const int nrows = min(FNT, N - n0);
+  f32x16 acc[FRB][4];
+  fwd_body(xrow, codes + (int64_t)e * N * (H / 2), scales + (int64_t)e * N * (H / 32), H, n0,
+           nrows, (wave * 32 * FRB < nrows ? wave * 32 * FRB : 0) + l32, (tl.rows + 31) / 32, lds,
+           acc);
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    const int nb = n0 + wave * 64 + rb * 32 + 4 * hlf;  // + 8q + (r % 4)
+  for (int rb = 0; rb < FRB; ++rb) {
+    if (n0 + wave * 32 * FRB + rb * 32 >= N) continue;   // row block past the last weight row
+    const int nb = n0 + wave * 32 * FRB + rb * 32 + 4 * hlf;  // + 8q + (r % 4)
     float bv[4][4];
 #pragma unroll
     for (int q = 0; q < 4; ++q)
@@ -231,41 +274,37 @@ __global__ __launch_bounds__(64 * WN, 2) void gate_up_kernel(
   }
 }
 
-template <int WN>
-__global__ __launch_bounds__(64 * WN, 2) void down_kernel(
+__global__ __launch_bounds__(FNTHR) void down_kernel(
     const uint16_t* __restrict__ a, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, const uint16_t* __restrict__ bias,
     const float* __restrict__ topk_w, const int32_t* __restrict__ sorted_rows,
     const Tile* __restrict__ tiles, const int32_t* __restrict__ num_tiles, int H, int I,
     float* __restrict__ y_w) {
-  using FT = FwdTile<WN>;
-  __shared__ __attribute__((aligned(16))) uint16_t xs[2][MT][LDS_ROW];
-  if ((int)blockIdx.y >= *num_tiles) return;
-  const Tile tl = tiles[blockIdx.y];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
   const int N = H;
-  const int n0 = blockIdx.x * FT::NT;
+  int mt, nt;
+  if (!xcd_work_item(*num_tiles, (N + FNT - 1) / FNT, &mt, &nt)) return;
+  const Tile tl = tiles[mt];
+  const int n0 = nt * FNT;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hlf = lane >> 5;
   const int e = tl.expert;
 
-  const uint16_t* brow[FT::PPT];
+  const uint16_t* xrow[XCHUNKS];
 #pragma unroll
-  for (int j = 0; j < FT::PPT; ++j) {
-    int q = tid + j * FT::NTHR;
-    int r = q >> 3;
-    brow[j] = a + (int64_t)(tl.row0 + (r < tl.rows ? r : 0)) * I + (q & 7) * 8;
+  for (int j = 0; j < XCHUNKS; ++j) {
+    const int r = (XCHUNKS * wave + j) * 8 + lane / 8;
+    xrow[j] = a + (int64_t)(tl.row0 + (r < tl.rows ? r : 0)) * I;
   }
-  const bool wave_live = n0 + wave * 64 < N;
-  const int wrow = (wave_live ? n0 + wave * 64 : 0) + l32;
-  const uint8_t* wcode = codes + ((int64_t)e * N + wrow) * (I / 2);
-  const uint8_t* wscale = scales + ((int64_t)e * N + wrow) * (I / 32);
-  f32x16 acc[2][4];
-  fwd_mainloop<WN>(brow, wcode, wscale, I, (tl.rows + 31) / 32, xs, acc);
-  if (!wave_live) return;
-
+  const int nrows = min(FNT, N - n0);
+  f32x16 acc[FRB][4];
+  fwd_body(xrow, codes + (int64_t)e * N * (I / 2), scales + (int64_t)e * N * (I / 32), I, n0,
+           nrows, (wave * 32 * FRB < nrows ? wave * 32 * FRB : 0) + l32, (tl.rows + 31) / 32, lds,
+           acc);
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    const int nb = n0 + wave * 64 + rb * 32 + 4 * hlf;
+  for (int rb = 0; rb < FRB; ++rb) {
+    if (n0 + wave * 32 * FRB + rb * 32 >= N) continue;   // row block past the last weight row
+    const int nb = n0 + wave * 32 * FRB + rb * 32 + 4 * hlf;
     float bv[4][4];
 #pragma unroll
     for (int q = 0; q < 4; ++q)
@@ -305,17 +344,18 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   reinterpret_cast<u32x2*>(out)[i] = o;
 }
 
-constexpr int FWD_WN = 4;
+// K step of the forward GEMMs for a contraction length K (0: unsupported).
+int fwd_step_k(int K) { return (K % FKS == 0 && K <= FWD_MAXK) ? FKS : 0; }
 
 hipError_t launch_gate_up(const uint16_t* x, const uint8_t* codes, const uint8_t* scales,
                           const uint16_t* bias, const int32_t* sorted_rows, const Tile* tiles,
                           const int32_t* num_tiles, int max_tiles, int H, int I, int k,
                           float alpha, float limit, uint16_t* h_out, uint16_t* a_out,
                           hipStream_t s) {
-  constexpr int NT = FwdTile<FWD_WN>::NT;
-  dim3 grid((2 * I + NT - 1) / NT, max_tiles);
-  hipLaunchKernelGGL(gate_up_kernel<FWD_WN>, grid, dim3(64 * FWD_WN), 0, s, x, codes, scales,
-                     bias, sorted_rows, tiles, num_tiles, H, I, k, alpha, limit, h_out, a_out);
+  if (!fwd_step_k(H)) return hipErrorInvalidValue;
+  dim3 grid(((2 * I + FNT - 1) / FNT) * max_tiles), block(FNTHR);
+  hipLaunchKernelGGL(gate_up_kernel, grid, block, 0, s, x, codes, scales, bias, sorted_rows,
+                     tiles, num_tiles, H, I, k, alpha, limit, h_out, a_out);
   return hipGetLastError();
 }
 
@@ -323,10 +363,10 @@ hipError_t launch_down(const uint16_t* a, const uint8_t* codes, const uint8_t* s
                        const uint16_t* bias, const float* topk_w, const int32_t* sorted_rows,
                        const Tile* tiles, const int32_t* num_tiles, int max_tiles, int H, int I,
                        float* y_w, hipStream_t s) {
-  constexpr int NT = FwdTile<FWD_WN>::NT;
-  dim3 grid((H + NT - 1) / NT, max_tiles);
-  hipLaunchKernelGGL(down_kernel<FWD_WN>, grid, dim3(64 * FWD_WN), 0, s, a, codes, scales, bias,
-                     topk_w, sorted_rows, tiles, num_tiles, H, I, y_w);
+  if (!fwd_step_k(I)) return hipErrorInvalidValue;
+  dim3 grid(((H + FNT - 1) / FNT) * max_tiles), block(FNTHR);
+  hipLaunchKernelGGL(down_kernel, grid, block, 0, s, a, codes, scales, bias, topk_w, sorted_rows,
+                     tiles, num_tiles, H, I, y_w);
   return hipGetLastError();
 }
 

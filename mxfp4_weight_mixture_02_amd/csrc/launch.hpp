@@ -30,6 +30,7 @@ hipError_t launch_build_tiles(const int32_t* offsets, int E, Tile* tiles, int32_
                               hipStream_t s);
 
 // gemm_fwd.hip
+int fwd_step_k(int K);   // K step of the forward GEMMs for contraction length K; 0 = unsupported
 hipError_t launch_gate_up(const uint16_t* x, const uint8_t* codes, const uint8_t* scales,
                           const uint16_t* bias, const int32_t* sorted_rows, const Tile* tiles,
                           const int32_t* num_tiles, int max_tiles, int H, int I, int k,
