@@ -204,7 +204,7 @@ def _lora_v(layer, e, a):
     return a @ bf16_to_f64(layer.lora_A[e]).T            # [rows, r]
 
 
-def forward(layer: Layer, x_bits, tokens=None, routing: Routing | None = None):
+def forward(layer: Layer, x_bits, tokens=None, routing: Routing | None = None, experts=None):
     """Expert-block forward.  Returns (out float64 [T, H], routing, cache).
 
     out[t] = sum_j w[t, j] * y_(t, j), where for expert e = idx[t, j]
@@ -213,9 +213,11 @@ def forward(layer: Layer, x_bits, tokens=None, routing: Routing | None = None):
       y = a @ Wd[e].T + bd[e] (+ s * (a @ A_e.T) @ B_e.T with LoRA)
 
     ``tokens`` (optional index array) restricts the expert loop to those
-    tokens; the other rows of ``out`` stay zero.  Routing is always for all
-    tokens (it is what the permutation is defined on).  ``cache`` maps each
-    flat row f that was computed to (h, a, y) for the backward and tests.
+    tokens; the other rows of ``out`` stay zero.  ``experts`` (optional)
+    restricts it to those experts: ``out`` then holds only their share.
+    Routing is always for all tokens (it is what the permutation is defined
+    on).  ``cache`` maps each flat row f that was computed to (h, a, y) for
+    the backward and tests.
     """
     x = bf16_to_f64(x_bits)
     T, H = x.shape
@@ -228,6 +230,8 @@ def forward(layer: Layer, x_bits, tokens=None, routing: Routing | None = None):
     out = np.zeros((T, H))
     cache = {}
     for e in range(layer.E):
+        if experts is not None and e not in experts:
+            continue
         rows = _expert_rows(r, e, k, mask)
         if rows.size == 0:
             continue
@@ -247,7 +251,7 @@ def forward(layer: Layer, x_bits, tokens=None, routing: Routing | None = None):
 # ---------------------------------------------------------------- backward
 
 def backward_dx(layer: Layer, x_bits, dy_bits, tokens=None, routing: Routing | None = None,
-                want_lora=True):
+                want_lora=True, experts=None):
     """Gradient of L = sum(dY * out) with respect to x (and the LoRA
     adapters), base weights and biases frozen ([P1]: only the input and
     adapter gradients are needed for LoRA training).
@@ -265,6 +269,9 @@ def backward_dx(layer: Layer, x_bits, dy_bits, tokens=None, routing: Routing | N
     LoRA: dB_e = s * sum_f g_y^T v_f, dA_e = sum_f dv^T a_f.
 
     ``tokens`` restricts dX to those tokens (then dA/dB cover only them).
+    ``experts`` restricts the expert loop to those experts: dA/dB are then
+    exact for them (zero elsewhere) and dX holds only their share, so the
+    router term, which needs every slot of a token, is left out.
     Returns (dX float64 [T, H], dA [E, r, I] or None, dB [E, H, r] or None).
     """
     x = bf16_to_f64(x_bits)
@@ -283,6 +290,8 @@ def backward_dx(layer: Layer, x_bits, dy_bits, tokens=None, routing: Routing | N
     dB = np.zeros(layer.lora_B.shape) if lora else None
     wflat = r.w.reshape(-1)
     for e in range(layer.E):
+        if experts is not None and e not in experts:
+            continue
         rows = _expert_rows(r, e, k, mask)
         if rows.size == 0:
             continue
@@ -312,6 +321,8 @@ def backward_dx(layer: Layer, x_bits, dy_bits, tokens=None, routing: Routing | N
         dh[:, 0::2] = dg
         dh[:, 1::2] = du
         np.add.at(dX, t, dh @ Wgu)
+    if experts is not None:
+        return dX, dA, dB
     # router path through the softmax over the selected logits
     Wr = layer.router_w.astype(np.float64)
     dwt = dw.reshape(T, k)

@@ -359,3 +359,51 @@ def test_backward_token_subset_matches_full():
     toks = np.array([1, 2, 9])
     part, _, _ = moe.backward_dx(L, x, dY, tokens=toks)
     np.testing.assert_allclose(part[toks], full[toks], rtol=1e-13, atol=1e-15)
+
+
+def test_expert_subsets_partition_the_block():
+    # the experts= restriction splits the expert loop: per-expert outputs
+    # and adapter gradients add up to the unrestricted ones
+    s = syn.spec("tiny", lora_rank=16)
+    L = oracle_layer(s)
+    L.lora_scale = 3.0
+    x = syn.tokens(s)
+    dY = syn.upstream_grad(s)
+    out, r, _ = moe.forward(L, x)
+    _, dA, dB = moe.backward_dx(L, x, dY)
+    acc = np.zeros_like(out)
+    for e in range(s.E):
+        oe, _, _ = moe.forward(L, x, routing=r, experts=[e])
+        acc += oe
+        _, dAe, dBe = moe.backward_dx(L, x, dY, routing=r, experts=[e])
+        np.testing.assert_allclose(dAe[e], dA[e], rtol=1e-12, atol=1e-15)
+        np.testing.assert_allclose(dBe[e], dB[e], rtol=1e-12, atol=1e-15)
+        others = [i for i in range(s.E) if i != e]
+        assert not np.any(dAe[others]) and not np.any(dBe[others])
+    np.testing.assert_allclose(acc, out, rtol=1e-12, atol=1e-15)
+
+
+def test_lora_gradients_against_scale_derivative():
+    # The adapter delta enters y as s * (v B^T), so with the routing fixed
+    # L(s) is affine in s and dL/ds = <dB, B> / s = <dA, A> / s: both inner
+    # products equal s times the slope of the loss between two scales.
+    s = syn.spec("tiny", lora_rank=16)
+    L = oracle_layer(s)
+    x = syn.tokens(s)
+    dY = moe.bf16_to_f64(syn.upstream_grad(s))
+    r = moe.route(L, x)
+    sc = 2.5
+    L.lora_scale = sc
+    _, dA, dB = moe.backward_dx(L, x, syn.upstream_grad(s), routing=r)
+    vals = []
+    for s_ in (0.0, 1.0):
+        L.lora_scale = s_
+        out, _, _ = moe.forward(L, x, routing=r)
+        vals.append(float(np.sum(dY * out)))
+    slope = vals[1] - vals[0]
+    A = moe.bf16_to_f64(L.lora_A)
+    B = moe.bf16_to_f64(L.lora_B)
+    ipA, ipB = float(np.sum(dA * A)), float(np.sum(dB * B))
+    assert abs(slope) > 1e-6
+    assert abs(ipB - sc * slope) <= 1e-10 * abs(sc * slope)
+    assert abs(ipA - sc * slope) <= 1e-10 * abs(sc * slope)
