@@ -82,8 +82,12 @@ typedef struct mxfp4_moe_dims {
  *  dn_codes  uint8 [E, H, I/2];  dn_scales uint8 [E, H, I/32]
  *  dn_bias   bf16 [E, H] or NULL
  *  lora_A    bf16 [E, r, I] and lora_B bf16 [E, H, r]: per-expert LoRA on
- *            the down projection, y += scale * (a A_e^T) B_e^T; both NULL
- *            when lora_rank == 0, both required otherwise. */
+ *            the down projection ([P1] "What this does": adapters train on
+ *            the frozen MXFP4 base), y += scale * (a A_e^T) B_e^T.  Both
+ *            NULL when lora_rank == 0 (MXFP4_EINVAL otherwise), both
+ *            required and 16-byte aligned when lora_rank == 16.  Inside the
+ *            down GEMMs, scale * v and the rank-space gradient enter the
+ *            bf16 matrix cores as a hi + lo bf16 pair (about 17 bits). */
 typedef struct mxfp4_moe_weights {
   const float* router_w;
   const float* router_b;
@@ -108,8 +112,9 @@ typedef struct mxfp4_moe_weights {
  *                                within an expert (stable)
  *  h              bf16  [R, 2I]  gate_up output incl. bias, sorted order
  *  a              bf16  [R, I]   SwiGLU output, sorted order
- *  lora_v         bf16  [R, r]   a A_e^T (sorted order); required iff
- *                                lora_rank > 0, else NULL */
+ *  lora_v         fp32  [R, r]   v = a A_e^T (sorted order, before the
+ *                                lora_scale); required iff lora_rank > 0,
+ *                                else ignored; 16-byte aligned */
 typedef struct mxfp4_moe_saved {
   int32_t* topk_idx;
   float* topk_w;
@@ -117,7 +122,7 @@ typedef struct mxfp4_moe_saved {
   int32_t* sorted_rows;
   uint16_t* h;
   uint16_t* a;
-  uint16_t* lora_v;
+  float* lora_v;
 } mxfp4_moe_saved;
 
 /* Workspace modes for mxfp4_moe_workspace_bytes. */

@@ -42,7 +42,8 @@ struct Layout {
   // offsets into the workspace; SIZE_MAX = not placed
   size_t topk_idx = SIZE_MAX, topk_w = SIZE_MAX, offsets = SIZE_MAX, sorted_rows = SIZE_MAX,
          a = SIZE_MAX, blk_hist = SIZE_MAX, tiles = SIZE_MAX, num_tiles = SIZE_MAX,
-         y_w = SIZE_MAX, dh = SIZE_MAX, dw_part = SIZE_MAX, dxr = SIZE_MAX;
+         y_w = SIZE_MAX, dh = SIZE_MAX, dw_part = SIZE_MAX, dxr = SIZE_MAX,
+         lora_v = SIZE_MAX, lora_At = SIZE_MAX, lora_Bt = SIZE_MAX, lora_dvu = SIZE_MAX;
   size_t total = 0;
   size_t put(size_t bytes) {
     size_t at = total;
@@ -68,9 +69,11 @@ int check_dims(const mxfp4_moe_dims* d) {
                 (long long)d->I);
   if (d->T * d->H >= (int64_t(1) << 31))
     return fail(MXFP4_EUNSUPPORTED, "T*H = %lld elements exceed int32", (long long)(d->T * d->H));
-  if (d->lora_rank != 0)
-    return fail(MXFP4_EUNSUPPORTED, "lora_rank=%d: only 0 is supported by this build",
-                d->lora_rank);
+  if (d->lora_rank != 0 && d->lora_rank != mxmoe::LORA_R)
+    return fail(MXFP4_EUNSUPPORTED, "lora_rank=%d: supported ranks are 0 and %d", d->lora_rank,
+                mxmoe::LORA_R);
+  if (d->lora_rank && !(d->lora_scale == d->lora_scale && d->lora_scale - d->lora_scale == 0.0f))
+    return fail(MXFP4_EINVAL, "lora_scale must be finite");
   return MXFP4_OK;
 }
 
@@ -85,6 +88,7 @@ Layout layout(const mxfp4_moe_dims& d, int mode) {
       L.offsets = L.put((size_t)(d.E + 1) * 4);
       L.sorted_rows = L.put(R * 4);
       L.a = L.put(R * (size_t)d.I * 2);
+      if (d.lora_rank) L.lora_v = L.put(R * (size_t)d.lora_rank * 4);
     }
     L.blk_hist = L.put((size_t)mxmoe::router_blocks(d.T) * d.E * 4);
     L.tiles = L.put((size_t)maxt * sizeof(mxmoe::Tile));
@@ -96,6 +100,11 @@ Layout layout(const mxfp4_moe_dims& d, int mode) {
     L.dh = L.put(R * (size_t)d.I * 2 * 2);
     L.dw_part = L.put(R * (size_t)mxmoe::bwd_down_ntiles((int)d.I) * 4);
     L.dxr = L.put(R * (size_t)d.H * 4);
+    if (d.lora_rank) {
+      L.lora_At = L.put((size_t)d.E * d.I * d.lora_rank * 2);
+      L.lora_Bt = L.put((size_t)d.E * d.H * d.lora_rank * 2);
+      L.lora_dvu = L.put(R * (size_t)d.lora_rank * 4);
+    }
   }
   return L;
 }
@@ -105,8 +114,16 @@ T* at(void* ws, size_t off) {
   return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
 }
 
-int check_weights(const mxfp4_moe_weights* w) {
+int check_weights(const mxfp4_moe_weights* w, const mxfp4_moe_dims& d) {
   if (!w) return fail(MXFP4_EINVAL, "weights is NULL");
+  if (d.lora_rank) {
+    if (!w->lora_A || !w->lora_B)
+      return fail(MXFP4_EINVAL, "lora_rank=%d needs lora_A and lora_B", d.lora_rank);
+    if (!aligned(w->lora_A, 16) || !aligned(w->lora_B, 16))
+      return fail(MXFP4_EINVAL, "lora_A and lora_B must be 16-byte aligned");
+  } else if (w->lora_A || w->lora_B) {
+    return fail(MXFP4_EINVAL, "lora_A/lora_B given but lora_rank is 0");
+  }
   if (!w->router_w || !w->gu_codes || !w->gu_scales || !w->dn_codes || !w->dn_scales)
     return fail(MXFP4_EINVAL, "router_w, gu_codes, gu_scales, dn_codes and dn_scales are required");
   if (!aligned(w->router_w, 16) || !aligned(w->gu_codes, 16) || !aligned(w->dn_codes, 16) ||
@@ -239,7 +256,7 @@ int mxfp4_moe_forward(const mxfp4_moe_dims* dims, const mxfp4_moe_weights* w, co
                       size_t workspace_bytes, void* stream) {
   int rc = check_dims(dims);
   if (rc) return rc;
-  rc = check_weights(w);
+  rc = check_weights(w, *dims);
   if (rc) return rc;
   const mxfp4_moe_dims& d = *dims;
   if (!x || !out) return fail(MXFP4_EINVAL, "x and out are required");
@@ -250,6 +267,8 @@ int mxfp4_moe_forward(const mxfp4_moe_dims* dims, const mxfp4_moe_weights* w, co
       return fail(MXFP4_EINVAL, "saved: topk_idx, topk_w, expert_offsets, sorted_rows, h, a are required");
     if (!aligned(saved->h, 16) || !aligned(saved->a, 16))
       return fail(MXFP4_EINVAL, "saved h and a must be 16-byte aligned");
+    if (d.lora_rank && (!saved->lora_v || !aligned(saved->lora_v, 16)))
+      return fail(MXFP4_EINVAL, "lora_rank > 0: saved lora_v is required, 16-byte aligned");
   }
   const int mode = saved ? MXFP4_WS_FORWARD_SAVED : MXFP4_WS_FORWARD;
   const Layout L = layout(d, mode);
@@ -270,6 +289,7 @@ int mxfp4_moe_forward(const mxfp4_moe_dims* dims, const mxfp4_moe_weights* w, co
   mxmoe::Tile* tiles = at<mxmoe::Tile>(workspace, L.tiles);
   int32_t* num_tiles = at<int32_t>(workspace, L.num_tiles);
   float* y_w = at<float>(workspace, L.y_w);
+  float* lora_v = !d.lora_rank ? nullptr : saved ? saved->lora_v : at<float>(workspace, L.lora_v);
   const int maxt = mxmoe::max_tiles(R, E);
 
   LAUNCH(mxmoe::launch_router(x, w->router_w, w->router_b, T, H, E, k, topk_idx, topk_w, blk_hist, s),
@@ -280,8 +300,13 @@ int mxfp4_moe_forward(const mxfp4_moe_dims* dims, const mxfp4_moe_weights* w, co
   LAUNCH(mxmoe::launch_gate_up(x, w->gu_codes, w->gu_scales, w->gu_bias, sorted_rows, tiles,
                                num_tiles, maxt, H, I, k, d.swiglu_alpha, d.swiglu_limit, h, a, s),
          "gate_up");
+  if (d.lora_rank)
+    LAUNCH(mxmoe::launch_lora_proj(a, false, sorted_rows, k, w->lora_A, I, tiles, num_tiles, maxt,
+                                   1.0f, lora_v, s),
+           "lora_v");
   LAUNCH(mxmoe::launch_down(a, w->dn_codes, w->dn_scales, w->dn_bias, topk_w, sorted_rows, tiles,
-                            num_tiles, maxt, H, I, y_w, s),
+                            num_tiles, maxt, H, I, d.lora_rank ? w->lora_B : nullptr, lora_v,
+                            d.lora_scale, y_w, s),
          "down");
   LAUNCH(mxmoe::launch_combine(y_w, d.T, H, k, out, s), "combine");
   return ok();
@@ -293,7 +318,7 @@ int mxfp4_moe_backward_dx(const mxfp4_moe_dims* dims, const mxfp4_moe_weights* w
                           void* stream) {
   int rc = check_dims(dims);
   if (rc) return rc;
-  rc = check_weights(w);
+  rc = check_weights(w, *dims);
   if (rc) return rc;
   const mxfp4_moe_dims& d = *dims;
   if (!saved || !saved->topk_idx || !saved->topk_w || !saved->expert_offsets ||
@@ -302,8 +327,11 @@ int mxfp4_moe_backward_dx(const mxfp4_moe_dims* dims, const mxfp4_moe_weights* w
   if (!dy || !dx) return fail(MXFP4_EINVAL, "dy and dx are required");
   if (!aligned(dy, 16) || !aligned(dx, 16) || !aligned(saved->h, 16) || !aligned(saved->a, 16))
     return fail(MXFP4_EINVAL, "dy, dx, saved h and a must be 16-byte aligned");
-  (void)dA;
-  (void)dB;
+  if (d.lora_rank) {
+    if (!saved->lora_v || !aligned(saved->lora_v, 16))
+      return fail(MXFP4_EINVAL, "lora_rank > 0: saved lora_v is required, 16-byte aligned");
+    if (!dA || !dB) return fail(MXFP4_EINVAL, "lora_rank > 0: dA and dB are required");
+  }
   const Layout L = layout(d, MXFP4_WS_BACKWARD);
   if (!workspace || workspace_bytes < L.total)
     return fail(MXFP4_EWORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, L.total);
@@ -318,12 +346,35 @@ int mxfp4_moe_backward_dx(const mxfp4_moe_dims* dims, const mxfp4_moe_weights* w
   float* dw_part = at<float>(workspace, L.dw_part);
   float* dxr = at<float>(workspace, L.dxr);
   const int maxt = mxmoe::max_tiles(R, E);
+  const int r = d.lora_rank;
+  uint16_t* lora_At = r ? at<uint16_t>(workspace, L.lora_At) : nullptr;
+  uint16_t* lora_Bt = r ? at<uint16_t>(workspace, L.lora_Bt) : nullptr;
+  float* lora_dvu = r ? at<float>(workspace, L.lora_dvu) : nullptr;
 
   LAUNCH(mxmoe::launch_build_tiles(saved->expert_offsets, E, tiles, num_tiles, s), "bwd_tiles");
+  if (r) {
+    LAUNCH(mxmoe::launch_transpose_bf16(w->lora_A, E, r, I, lora_At, s), "lora_transpose");
+    LAUNCH(mxmoe::launch_transpose_bf16(w->lora_B, E, H, r, lora_Bt, s), "lora_transpose");
+    // dv_u = s dY_t B_e over the token rows of dY
+    LAUNCH(mxmoe::launch_lora_proj(dy, true, saved->sorted_rows, k, lora_Bt, H, tiles, num_tiles,
+                                   maxt, d.lora_scale, lora_dvu, s),
+           "lora_dvu");
+  }
   LAUNCH(mxmoe::launch_bwd_down(dy, w->dn_codes, w->dn_scales, saved->topk_w, saved->sorted_rows,
                                 tiles, num_tiles, maxt, saved->h, saved->a, H, I, k,
-                                d.swiglu_alpha, d.swiglu_limit, dh, dw_part, s),
+                                d.swiglu_alpha, d.swiglu_limit, lora_At, lora_dvu, dh, dw_part, s),
          "bwd_down");
+  if (r) {
+    // dA_e[j, i] = sum_p w_p dv_u[p, j] a[p, i];  dB_e[h, j] = s sum_p w_p dY[t(p), h] v[p, j]
+    LAUNCH(mxmoe::launch_lora_grad(saved->a, false, I, saved->sorted_rows, k, lora_dvu,
+                                   saved->topk_w, 1.0f, saved->expert_offsets, E, dA,
+                                   (int64_t)r * I, 1, I, s),
+           "lora_grad");
+    LAUNCH(mxmoe::launch_lora_grad(dy, true, H, saved->sorted_rows, k, saved->lora_v,
+                                   saved->topk_w, d.lora_scale, saved->expert_offsets, E, dB,
+                                   (int64_t)H * r, r, 1, s),
+           "lora_grad");
+  }
   LAUNCH(mxmoe::launch_bwd_gate_up(dh, w->gu_codes, w->gu_scales, saved->sorted_rows, tiles,
                                    num_tiles, maxt, H, I, dxr, s),
          "bwd_gate_up");

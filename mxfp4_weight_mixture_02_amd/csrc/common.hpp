@@ -49,6 +49,23 @@ __device__ __forceinline__ u32x4 dequant8_bf16(uint32_t codes, float scale) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// Eight fp32 values v (two f32x4), times s, as a pair of bf16 vectors with
+// hi + lo = s*v to about 2^-17 relative: hi = bf16(s*v), lo = bf16(s*v - hi).
+// Two bf16 MFMAs over (hi, lo) then carry an fp32 operand.
+__device__ __forceinline__ void split_bf16x8(f32x4 v0, f32x4 v1, float s, bf16x8* hi, bf16x8* lo) {
+  u32x4 h, l;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const float x0 = s * (m < 2 ? v0[2 * m] : v1[2 * m - 4]);
+    const float x1 = s * (m < 2 ? v0[2 * m + 1] : v1[2 * m - 3]);
+    const uint32_t b0 = f32_to_bf16(x0), b1 = f32_to_bf16(x1);
+    h[m] = b0 | (b1 << 16);
+    l[m] = pack_bf16x2(x0 - bf16_to_f32((uint16_t)b0), x1 - bf16_to_f32((uint16_t)b1));
+  }
+  *hi = as_bf16x8(h);
+  *lo = as_bf16x8(l);
+}
+
 // bf16 bits of a gate (is_up = false) or up pre-activation for the saved
 // state.  Round to nearest even, except that a value the rounding would move
 // across a clamp bound (gate: +limit; up: -limit and +limit) is moved one
@@ -130,5 +147,6 @@ __device__ __forceinline__ bool xcd_work_item(int live_row_tiles, int col_tiles,
 constexpr int MT = 128;      // routed rows per GEMM tile
 constexpr int KC = 64;       // K elements per main-loop step
 constexpr int LDS_ROW = 72;  // bf16 per staged row (64 + 8 padding)
+constexpr int LORA_R = 16;   // supported LoRA rank: one 16-deep MFMA contraction
 
 }  // namespace mxmoe

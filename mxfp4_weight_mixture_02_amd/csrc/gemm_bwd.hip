@@ -209,6 +209,7 @@ __global__ __launch_bounds__(64 * WN) void bwd_down_kernel(
     const int32_t* __restrict__ sorted_rows, const Tile* __restrict__ tiles,
     const int32_t* __restrict__ num_tiles, const uint16_t* __restrict__ hsv,
     const uint16_t* __restrict__ asv, int H, int I, int k, float alpha, float limit,
+    const uint16_t* __restrict__ lora_At, const float* __restrict__ lora_dvu,
     uint16_t* __restrict__ dh, float* __restrict__ dw_part) {
   using BT = BwdTile<WN>;
   __shared__ __attribute__((aligned(16))) uint16_t ws[2][BT::NT][LDS_ROW];
@@ -237,6 +238,29 @@ __global__ __launch_bounds__(64 * WN) void bwd_down_kernel(
   const uint8_t* wscale = scales + (int64_t)e * H * (I / 32);
   f32x16 acc[2][4];
   bwd_mainloop<WN>(brow, wcode, wscale, H, I, o0, (tl.rows + 31) / 32, ws, xs, acc);
+  if (lora_At) {
+    // + dv_u A_e (dv_u = s dY B_e, unweighted like the accumulators): a
+    // 16-deep contraction, A-operand = rows of A_e^T, B-operand = dv_u as
+    // hi + lo bf16.  Through the accumulators it also reaches the dw
+    // partial: sum_i (dv_u A_e)_i a_i = dv_u . v, the adapter's share of dY . y.
+    bf16x8 vh[4], vl[4];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      const float* vp = lora_dvu + (int64_t)(tl.row0 + min(tb * 32 + l32, tl.rows - 1)) * LORA_R + 8 * hlf;
+      split_bf16x8(*reinterpret_cast<const f32x4*>(vp), *reinterpret_cast<const f32x4*>(vp + 4),
+                   1.0f, &vh[tb], &vl[tb]);
+    }
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const int i = o0 + wave * 64 + rb * 32 + l32;
+      const bf16x8 aw = as_bf16x8(*reinterpret_cast<const u32x4*>(lora_At + ((int64_t)e * I + (i < I ? i : 0)) * LORA_R + 8 * hlf));
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        acc[rb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw, vh[tb], acc[rb][tb], 0, 0, 0);
+        acc[rb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw, vl[tb], acc[rb][tb], 0, 0, 0);
+      }
+    }
+  }
 
   const int N2 = 2 * I;
 #pragma unroll
@@ -404,11 +428,12 @@ hipError_t launch_bwd_down(const uint16_t* dy, const uint8_t* codes, const uint8
                            const float* topk_w, const int32_t* sorted_rows, const Tile* tiles,
                            const int32_t* num_tiles, int max_tiles, const uint16_t* h,
                            const uint16_t* a, int H, int I, int k, float alpha, float limit,
-                           uint16_t* dh, float* dw_part, hipStream_t s) {
+                           const uint16_t* lora_At, const float* lora_dvu, uint16_t* dh,
+                           float* dw_part, hipStream_t s) {
   dim3 grid(bwd_down_ntiles(I) * max_tiles);
   hipLaunchKernelGGL(bwd_down_kernel<BWD_WN>, grid, dim3(64 * BWD_WN), 0, s, dy, codes, scales,
-                     topk_w, sorted_rows, tiles, num_tiles, h, a, H, I, k, alpha, limit, dh,
-                     dw_part);
+                     topk_w, sorted_rows, tiles, num_tiles, h, a, H, I, k, alpha, limit,
+                     lora_At, lora_dvu, dh, dw_part);
   return hipGetLastError();
 }
 

@@ -279,6 +279,7 @@ __global__ __launch_bounds__(FNTHR) void down_kernel(
     const uint8_t* __restrict__ scales, const uint16_t* __restrict__ bias,
     const float* __restrict__ topk_w, const int32_t* __restrict__ sorted_rows,
     const Tile* __restrict__ tiles, const int32_t* __restrict__ num_tiles, int H, int I,
+    const uint16_t* __restrict__ lora_B, const float* __restrict__ lora_v, float lora_scale,
     float* __restrict__ y_w) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
   const int N = H;
@@ -301,6 +302,28 @@ __global__ __launch_bounds__(FNTHR) void down_kernel(
   fwd_body(xrow, codes + (int64_t)e * N * (I / 2), scales + (int64_t)e * N * (I / 32), I, n0,
            nrows, (wave * 32 * FRB < nrows ? wave * 32 * FRB : 0) + l32, (tl.rows + 31) / 32, lds,
            acc);
+  if (lora_B) {
+    // + s v B_e^T: one more 16-deep contraction over the rank, A-operand =
+    // B_e rows (the weight rows of this wave), B-operand = s v as hi + lo bf16
+    bf16x8 vh[4], vl[4];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      const float* vp = lora_v + (int64_t)(tl.row0 + min(tb * 32 + l32, tl.rows - 1)) * LORA_R + 8 * hlf;
+      split_bf16x8(*reinterpret_cast<const f32x4*>(vp), *reinterpret_cast<const f32x4*>(vp + 4),
+                   lora_scale, &vh[tb], &vl[tb]);
+    }
+#pragma unroll
+    for (int rb = 0; rb < FRB; ++rb) {
+      const int n = n0 + wave * 32 * FRB + rb * 32 + l32;
+      if (n - l32 >= N) continue;
+      const bf16x8 bw = as_bf16x8(*reinterpret_cast<const u32x4*>(lora_B + ((int64_t)e * N + n) * LORA_R + 8 * hlf));
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        acc[rb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bw, vh[tb], acc[rb][tb], 0, 0, 0);
+        acc[rb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bw, vl[tb], acc[rb][tb], 0, 0, 0);
+      }
+    }
+  }
 #pragma unroll
   for (int rb = 0; rb < FRB; ++rb) {
     if (n0 + wave * 32 * FRB + rb * 32 >= N) continue;   // row block past the last weight row
@@ -362,11 +385,12 @@ hipError_t launch_gate_up(const uint16_t* x, const uint8_t* codes, const uint8_t
 hipError_t launch_down(const uint16_t* a, const uint8_t* codes, const uint8_t* scales,
                        const uint16_t* bias, const float* topk_w, const int32_t* sorted_rows,
                        const Tile* tiles, const int32_t* num_tiles, int max_tiles, int H, int I,
+                       const uint16_t* lora_B, const float* lora_v, float lora_scale,
                        float* y_w, hipStream_t s) {
   if (!fwd_step_k(I)) return hipErrorInvalidValue;
   dim3 grid(((H + FNT - 1) / FNT) * max_tiles), block(FNTHR);
   hipLaunchKernelGGL(down_kernel, grid, block, 0, s, a, codes, scales, bias, topk_w, sorted_rows,
-                     tiles, num_tiles, H, I, y_w);
+                     tiles, num_tiles, H, I, lora_B, lora_v, lora_scale, y_w);
   return hipGetLastError();
 }
 

@@ -198,7 +198,7 @@ class SavedState:
             torch.empty((R,), dtype=torch.int32, device=device),
             torch.empty((R, 2 * layer.I), dtype=torch.bfloat16, device=device),
             torch.empty((R, layer.I), dtype=torch.bfloat16, device=device),
-            torch.empty((R, r), dtype=torch.bfloat16, device=device) if r else None)
+            torch.empty((R, r), dtype=torch.float32, device=device) if r else None)
 
     def struct(self):
         return Saved(*[_ptr(getattr(self, n)) for n, _ in Saved._fields_])
@@ -251,17 +251,23 @@ def mxfp4_moe_forward(layer: MoeLayer, x: torch.Tensor, saved: SavedState | bool
 
 
 def mxfp4_moe_backward_dx(layer: MoeLayer, saved: SavedState, dy: torch.Tensor,
-                          dx: torch.Tensor | None = None, workspace: Workspace | None = None):
-    """dX (and, with LoRA, dA/dB) for the loss sum(dy * out).  Returns
-    (dx, dA, dB)."""
+                          dx: torch.Tensor | None = None, workspace: Workspace | None = None,
+                          dA: torch.Tensor | None = None, dB: torch.Tensor | None = None):
+    """dX (and, with LoRA, dA/dB, overwritten) for the loss sum(dy * out).
+    Returns (dx, dA, dB)."""
     dy = _dev(dy, torch.bfloat16, "dy")
     T = dy.shape[0]
     if dx is None:
         dx = torch.empty_like(dy)
-    dA = dB = None
     if layer.lora_A is not None:
-        dA = torch.empty(layer.lora_A.shape, dtype=torch.float32, device=dy.device)
-        dB = torch.empty(layer.lora_B.shape, dtype=torch.float32, device=dy.device)
+        if dA is None:
+            dA = torch.empty(layer.lora_A.shape, dtype=torch.float32, device=dy.device)
+        if dB is None:
+            dB = torch.empty(layer.lora_B.shape, dtype=torch.float32, device=dy.device)
+        _dev(dA, torch.float32, "dA")
+        _dev(dB, torch.float32, "dB")
+    else:
+        dA = dB = None
     nbytes = workspace_bytes(layer, T, WS_BACKWARD)
     ws = (workspace or _WS).get(nbytes, dy.device)
     d = layer.dims(T)

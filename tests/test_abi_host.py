@@ -125,3 +125,40 @@ def test_kernel_timing_toggles_without_gpu(L):
     assert L.mxfp4_moe_kernel_timing(1) == 0
     assert L.mxfp4_moe_kernel_times(None, None, None, 0) == 0   # nothing recorded
     assert L.mxfp4_moe_kernel_timing(0) == 0
+
+
+def test_lora_validation(L):
+    d = _dims(lora_rank=16)
+    # rank 16 is accepted and needs room for v (forward) and the transposed
+    # adapters and dv_u (backward)
+    f0 = L.mxfp4_moe_workspace_bytes(ctypes.byref(d), 0)
+    b = L.mxfp4_moe_workspace_bytes(ctypes.byref(d), 2)
+    d0 = _dims()
+    assert f0 > L.mxfp4_moe_workspace_bytes(ctypes.byref(d0), 0)
+    assert b > L.mxfp4_moe_workspace_bytes(ctypes.byref(d0), 2)
+    for r in (8, 32):
+        assert L.mxfp4_moe_workspace_bytes(ctypes.byref(_dims(lora_rank=r)), 0) == 0
+    nan = _dims(lora_rank=16, lora_scale=float("nan"))
+    assert L.mxfp4_moe_workspace_bytes(ctypes.byref(nan), 0) == 0
+    # adapters missing / given without a rank / misaligned
+    rc = L.mxfp4_moe_forward(ctypes.byref(d), ctypes.byref(_weights()), FAKE, FAKE, None, FAKE,
+                             f0, None)
+    assert rc == -1 and "lora_A" in _err(L)
+    rc = L.mxfp4_moe_forward(ctypes.byref(d0), ctypes.byref(_weights(lora_A=FAKE, lora_B=FAKE)),
+                             FAKE, FAKE, None, FAKE, f0, None)
+    assert rc == -1 and "lora_rank is 0" in _err(L)
+    rc = L.mxfp4_moe_forward(ctypes.byref(d), ctypes.byref(_weights(lora_A=FAKE + 8, lora_B=FAKE)),
+                             FAKE, FAKE, None, FAKE, f0, None)
+    assert rc == -1 and "aligned" in _err(L)
+    w = _weights(lora_A=FAKE, lora_B=FAKE)
+    # saved forward without lora_v
+    f1 = L.mxfp4_moe_workspace_bytes(ctypes.byref(d), 1)
+    sv = Saved(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0)
+    rc = L.mxfp4_moe_forward(ctypes.byref(d), ctypes.byref(w), FAKE, FAKE, ctypes.byref(sv),
+                             FAKE, f1, None)
+    assert rc == -1 and "lora_v" in _err(L)
+    # backward without dA/dB
+    sv = Saved(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    rc = L.mxfp4_moe_backward_dx(ctypes.byref(d), ctypes.byref(w), ctypes.byref(sv), FAKE, FAKE,
+                                 None, FAKE, FAKE, b, None)
+    assert rc == -1 and "dA and dB" in _err(L)

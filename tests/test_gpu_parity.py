@@ -84,11 +84,13 @@ def test_quantize_bytes_match_oracle(name):
 
 # ------------------------------------------------------------- small layers
 
-def _run_layer(s, x_scale=1.0, with_bias=True, backward=True, T=None):
+def _run_layer(s, x_scale=1.0, with_bias=True, backward=True, T=None, lora_scale=1.0):
     T = s.T if T is None else T
-    _say(f"layer {s.name} T={T} H={s.H} I={s.I} E={s.E} k={s.k} x_scale={x_scale} bias={with_bias}")
+    _say(f"layer {s.name} T={T} H={s.H} I={s.I} E={s.E} k={s.k} x_scale={x_scale} bias={with_bias}"
+         f" lora_rank={s.lora_rank} lora_scale={lora_scale}")
     dl = device_layer(s, with_bias=with_bias)
     ol, _ = oracle_layer(s, with_bias=with_bias)
+    dl.lora_scale = ol.lora_scale = lora_scale
     # the oracle's quantised bytes must equal the GPU's
     assert np.array_equal(dl.gu_codes.cpu().numpy(), ol.gu_codes)
     assert np.array_equal(dl.dn_scales.cpu().numpy(), ol.dn_scales)
@@ -105,13 +107,20 @@ def _run_layer(s, x_scale=1.0, with_bias=True, backward=True, T=None):
     aref = np.stack([cache[int(f)][1] for f in rows])
     assert_close(to_f64(sv.h), href, "saved h")
     assert_close(to_f64(sv.a), aref, "saved a")
+    if s.lora_rank:
+        ex = np.searchsorted(r.offsets, np.arange(T * s.k), side="right") - 1
+        vref = np.stack([moe._lora_v(ol, ex[i], aref[i][None])[0] for i in range(T * s.k)])
+        assert_close(to_f64(sv.lora_v), vref, "saved lora_v")
     res = {"out": out, "saved": sv, "routing": r}
     if backward:
         dyb = syn.upstream_grad(s, T)
-        dx, _, _ = mxfp4_moe_backward_dx(dl, sv, bf16_tensor(dyb).to(DEV))
+        dx, dA, dB = mxfp4_moe_backward_dx(dl, sv, bf16_tensor(dyb).to(DEV))
         torch.cuda.synchronize()
-        dref, _, _ = moe.backward_dx(ol, xb, dyb)
+        dref, dAref, dBref = moe.backward_dx(ol, xb, dyb)
         assert_close(to_f64(dx), dref, "dX")
+        if s.lora_rank:
+            assert_close(to_f64(dA), dAref, "dA")
+            assert_close(to_f64(dB), dBref, "dB")
         res["dx"] = dx
     return res
 
@@ -152,6 +161,36 @@ def test_multi_tile_ragged_tails():
 
 def test_many_experts_top8():
     _run_layer(syn.spec("tiny", T=64, H=128, I=128, E=64, k=8))
+
+
+@pytest.mark.parametrize("lora_scale", [1.0, 32.0])
+def test_lora_tiny(lora_scale):
+    # scale 32 makes the adapter delta comparable to the base output
+    _run_layer(syn.spec("tiny", lora_rank=16), lora_scale=lora_scale)
+
+
+def test_lora_multi_tile_ragged_tails():
+    _run_layer(syn.spec("tiny", T=300, H=192, I=320, E=3, k=2, lora_rank=16), lora_scale=8.0)
+
+
+def test_lora_empty_expert_gets_zero_gradients():
+    # E = 16 experts, 3 tokens, k = 2: most experts receive no rows; their
+    # dA/dB must come back as zeros (overwritten, not left stale)
+    s = syn.spec("tiny", T=3, E=16, k=2, lora_rank=16)
+    dl = device_layer(s)
+    x = bf16_tensor(syn.tokens(s)).to(DEV)
+    _, sv = mxfp4_moe_forward(dl, x, saved=True)
+    dy = bf16_tensor(syn.upstream_grad(s)).to(DEV)
+    dA = torch.full(dl.lora_A.shape, float("nan"), dtype=torch.float32, device=DEV)
+    dB = torch.full(dl.lora_B.shape, float("nan"), dtype=torch.float32, device=DEV)
+    _, dA, dB = mxfp4_moe_backward_dx(dl, sv, dy, dA=dA, dB=dB)
+    torch.cuda.synchronize()
+    off = sv.expert_offsets.cpu().numpy()
+    empty = np.nonzero(off[1:] == off[:-1])[0]
+    assert len(empty) >= 8
+    assert torch.isfinite(dA).all() and torch.isfinite(dB).all()
+    assert not dA[empty].any() and not dB[empty].any()
+    _run_layer(s, lora_scale=4.0)
 
 
 def test_forward_is_deterministic():
@@ -207,8 +246,13 @@ def _full_size(name, T=None, n_sample=6, backward=True, seed=0):
     rng = np.random.default_rng(seed)
     toks = np.sort(rng.choice(T, size=min(n_sample, T), replace=False))
     touched = np.unique(r.idx[toks])
-    _say(f"oracle: {len(touched)} experts for tokens {toks.tolist()}")
-    ol, _ = oracle_layer(s, experts=touched)
+    # with LoRA: the expert with the fewest rows gets its adapter gradients
+    # checked in full (every row of it)
+    hist = np.diff(r.offsets)
+    e_full = int(np.argmin(np.where(hist > 0, hist, np.iinfo(np.int64).max)))
+    need = np.union1d(touched, [e_full]) if s.lora_rank else touched
+    _say(f"oracle: {len(need)} experts for tokens {toks.tolist()}")
+    ol, _ = oracle_layer(s, experts=need)
     # the GPU quantizer's bytes equal the oracle's on every expert it needed
     for e in touched[:4]:
         assert np.array_equal(dl.gu_codes[e].cpu().numpy(), ol.gu_codes[e])
@@ -220,15 +264,29 @@ def _full_size(name, T=None, n_sample=6, backward=True, seed=0):
     pos = np.empty(T * s.k, np.int64)
     pos[r.sorted_rows] = np.arange(T * s.k)
     fl = np.array(sorted(cache.keys()))
-    assert_close(to_f64(sv.a)[pos[fl]], np.stack([cache[int(f)][1] for f in fl]), "saved a")
+    aref = np.stack([cache[int(f)][1] for f in fl])
+    assert_close(to_f64(sv.a)[pos[fl]], aref, "saved a")
+    if s.lora_rank:
+        ef = np.searchsorted(r.offsets, pos[fl], side="right") - 1
+        vref = np.stack([moe._lora_v(ol, ef[i], aref[i][None])[0] for i in range(len(fl))])
+        assert_close(to_f64(sv.lora_v)[pos[fl]], vref, "saved lora_v (sampled rows)")
     if backward:
         _say("backward")
         dyb = syn.upstream_grad(s, T)
-        dx, _, _ = mxfp4_moe_backward_dx(dl, sv, bf16_tensor(dyb).to(DEV))
+        dx, dA, dB = mxfp4_moe_backward_dx(dl, sv, bf16_tensor(dyb).to(DEV))
         torch.cuda.synchronize()
         dref, _, _ = moe.backward_dx(ol, xb, dyb, tokens=toks, routing=r)
         assert_close(to_f64(dx)[toks], dref[toks], "dX (sampled tokens)")
         assert torch.isfinite(dx.float()).all()
+        if s.lora_rank:
+            _say(f"adapter gradients of expert {e_full} ({hist[e_full]} rows)")
+            _, dAr, dBr = moe.backward_dx(ol, xb, dyb, routing=r, experts=[e_full])
+            assert_close(to_f64(dA[e_full]), dAr[e_full], "dA (one expert, all rows)")
+            assert_close(to_f64(dB[e_full]), dBr[e_full], "dB (one expert, all rows)")
+            # every expert: <dA, A> = <dB, B> (both are s * dL/ds)
+            ipA = float((dA.double() * dl.lora_A.double()).sum())
+            ipB = float((dB.double() * dl.lora_B.double()).sum())
+            assert abs(ipA - ipB) <= 1e-2 * max(abs(ipA), abs(ipB)), (ipA, ipB)
     assert torch.isfinite(out.float()).all()
 
 
@@ -241,6 +299,11 @@ def test_gpt_oss_20b_layer_2048_tokens():
 @pytest.mark.parametrize("T", [1, 8, 64])
 def test_gpt_oss_20b_layer_decode(T):
     _full_size("20b_decode", T=T, n_sample=min(T, 4), backward=(T == 64))
+
+
+@pytest.mark.timeout(900)
+def test_gpt_oss_20b_layer_16384_tokens_lora():
+    _full_size("20b_16384_lora", n_sample=4)
 
 
 @pytest.mark.timeout(900)
