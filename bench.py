@@ -15,7 +15,8 @@ GEMMs' algorithmic flops (2 * T*k * 3 * H * I per pass, two passes); the
 line also carries the forward-only rate, the decode-size weight-streaming
 rates (GB/s over the packed weights and scales of the experts a step
 touches, eight rotating weight copies so that nothing is served from the
-last-level cache), per-kernel times, the roofline entry of the dominant
+last-level cache; timed as HIP-graph replays of eight forwards, with the
+eager per-call time beside it), per-kernel times, the roofline entry of the dominant
 kernel (timed with HIP events on the library's stream) and the CPU
 oracle's rate on a bounded sample.
 """
@@ -190,18 +191,51 @@ def main():
             torch.cuda.synchronize()
             touched = int(torch.unique(sv.topk_idx).numel())
             od = torch.empty_like(xd)
-            nrep = max(8, args.steps) * 8
             for i in range(16):
                 mxfp4_moe_forward(copies[i % 8], xd, out=od, workspace=wsd)
             torch.cuda.synchronize()
+            # eager: one Python call per forward (includes the host's launch cost)
+            nrep = 8 * max(8, args.steps)
             t0 = time.perf_counter()
             for i in range(nrep):
                 mxfp4_moe_forward(copies[i % 8], xd, out=od, workspace=wsd)
             torch.cuda.synchronize()
-            dtd = (time.perf_counter() - t0) / nrep
-            decode[str(Td)] = {"us": round(dtd * 1e6, 1), "experts": touched,
+            dt_eager = (time.perf_counter() - t0) / nrep
+            # per-kernel GPU time from the library's events (eager)
+            L.mxfp4_moe_kernel_timing(1)
+            for i in range(8):
+                mxfp4_moe_forward(copies[i % 8], xd, out=od, workspace=wsd)
+            kd = {n: round(ms / c * 1e3, 2) for n, (ms, c) in kernel_times(L).items()}
+            L.mxfp4_moe_kernel_timing(0)
+            # graph replay: the eight forwards (one per weight copy) captured once
+            g = torch.cuda.CUDAGraph()
+            cs = torch.cuda.Stream()
+            cs.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(cs):
+                with torch.cuda.graph(g, stream=cs):
+                    for i in range(8):
+                        mxfp4_moe_forward(copies[i], xd, out=od, workspace=wsd)
+            torch.cuda.current_stream().wait_stream(cs)
+            for _ in range(3):
+                g.replay()
+            torch.cuda.synchronize()
+            ref = od.clone()
+            nrep_g = max(8, args.steps)
+            t0 = time.perf_counter()
+            for _ in range(nrep_g):
+                g.replay()
+            torch.cuda.synchronize()
+            dtd = (time.perf_counter() - t0) / (8 * nrep_g)
+            # the replayed result equals an eager forward on the last copy
+            mxfp4_moe_forward(copies[7], xd, out=od, workspace=wsd)
+            torch.cuda.synchronize()
+            assert torch.equal(ref.view(torch.int16), od.view(torch.int16))
+            del g
+            decode[str(Td)] = {"us": round(dtd * 1e6, 2), "us_eager": round(dt_eager * 1e6, 1),
+                               "experts": touched,
                                "GB/s": round(touched * per_expert / dtd / 1e9, 1),
-                               "frac_hbm": round(touched * per_expert / dtd / 1e9 / PEAK_HBM_GBS, 4)}
+                               "frac_hbm": round(touched * per_expert / dtd / 1e9 / PEAK_HBM_GBS, 4),
+                               "kernel_us": kd}
         del copies
 
     line = {

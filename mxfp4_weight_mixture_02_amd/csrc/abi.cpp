@@ -36,6 +36,8 @@ int ok() {
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 constexpr size_t ALIGN = 256;
+// Routed-row count up to which the forward takes the decode kernels.
+constexpr int64_t DECODE_MAX_ROWS = 256;
 size_t up(size_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
 
 struct Layout {
@@ -43,7 +45,8 @@ struct Layout {
   size_t topk_idx = SIZE_MAX, topk_w = SIZE_MAX, offsets = SIZE_MAX, sorted_rows = SIZE_MAX,
          a = SIZE_MAX, blk_hist = SIZE_MAX, tiles = SIZE_MAX, num_tiles = SIZE_MAX,
          y_w = SIZE_MAX, dh = SIZE_MAX, dw_part = SIZE_MAX, dxr = SIZE_MAX,
-         lora_v = SIZE_MAX, lora_At = SIZE_MAX, lora_Bt = SIZE_MAX, lora_dvu = SIZE_MAX;
+         lora_v = SIZE_MAX, lora_At = SIZE_MAX, lora_Bt = SIZE_MAX, lora_dvu = SIZE_MAX,
+         logits = SIZE_MAX;
   size_t total = 0;
   size_t put(size_t bytes) {
     size_t at = total;
@@ -90,6 +93,7 @@ Layout layout(const mxfp4_moe_dims& d, int mode) {
       L.a = L.put(R * (size_t)d.I * 2);
       if (d.lora_rank) L.lora_v = L.put(R * (size_t)d.lora_rank * 4);
     }
+    L.logits = L.put((size_t)d.T * d.E * 4);
     L.blk_hist = L.put((size_t)mxmoe::router_blocks(d.T) * d.E * 4);
     L.tiles = L.put((size_t)maxt * sizeof(mxmoe::Tile));
     L.num_tiles = L.put(4);
@@ -292,11 +296,33 @@ int mxfp4_moe_forward(const mxfp4_moe_dims* dims, const mxfp4_moe_weights* w, co
   float* lora_v = !d.lora_rank ? nullptr : saved ? saved->lora_v : at<float>(workspace, L.lora_v);
   const int maxt = mxmoe::max_tiles(R, E);
 
-  LAUNCH(mxmoe::launch_router(x, w->router_w, w->router_b, T, H, E, k, topk_idx, topk_w, blk_hist, s),
-         "router");
-  LAUNCH(mxmoe::launch_scan(blk_hist, mxmoe::router_blocks(T), E, offsets, s), "scan");
-  LAUNCH(mxmoe::launch_scatter(topk_idx, blk_hist, T, k, E, sorted_rows, s), "scatter");
-  LAUNCH(mxmoe::launch_build_tiles(offsets, E, tiles, num_tiles, s), "tiles");
+  float* logits = at<float>(workspace, L.logits);
+  LAUNCH(mxmoe::launch_logits(x, w->router_w, w->router_b, T, H, E, logits, s), "router_logits");
+  if (R <= mxmoe::PLAN_MAX_ROWS) {
+    // top-k, histogram, offsets, permutation and tiles in one workgroup
+    LAUNCH(mxmoe::launch_plan(logits, T, E, k, topk_idx, topk_w, offsets, sorted_rows, tiles,
+                              num_tiles, s),
+           "route_plan");
+  } else {
+    LAUNCH(mxmoe::launch_topk(logits, T, E, k, topk_idx, topk_w, blk_hist, s), "router_topk");
+    LAUNCH(mxmoe::launch_scan(blk_hist, mxmoe::router_blocks(T), E, offsets, s), "scan");
+    LAUNCH(mxmoe::launch_scatter(topk_idx, blk_hist, T, k, E, sorted_rows, s), "scatter");
+    LAUNCH(mxmoe::launch_build_tiles(offsets, E, tiles, num_tiles, s), "tiles");
+  }
+  // few rows per expert: the weight-streaming decode kernels (no LoRA there)
+  const bool decode = R <= DECODE_MAX_ROWS && !d.lora_rank && H <= mxmoe::dec_max_k() &&
+                      I <= mxmoe::dec_max_k();
+  if (decode) {
+    LAUNCH(mxmoe::launch_dec_gate_up(x, w->gu_codes, w->gu_scales, w->gu_bias, sorted_rows, tiles,
+                                     num_tiles, maxt, R, H, I, k, d.swiglu_alpha, d.swiglu_limit,
+                                     h, a, s),
+           "dec_gate_up");
+    LAUNCH(mxmoe::launch_dec_down(a, w->dn_codes, w->dn_scales, w->dn_bias, topk_w, sorted_rows,
+                                  tiles, num_tiles, maxt, R, H, I, y_w, s),
+           "dec_down");
+    LAUNCH(mxmoe::launch_combine(y_w, d.T, H, k, out, s), "combine");
+    return ok();
+  }
   LAUNCH(mxmoe::launch_gate_up(x, w->gu_codes, w->gu_scales, w->gu_bias, sorted_rows, tiles,
                                num_tiles, maxt, H, I, k, d.swiglu_alpha, d.swiglu_limit, h, a, s),
          "gate_up");

@@ -86,6 +86,8 @@ __device__ __forceinline__ void fwd_issue(const FwdPipe& p, u32x4 (&codes)[NST][
   for (int j = 0; j < XCHUNKS; ++j)
     __builtin_amdgcn_global_load_lds(p.xrow[j] + c * FKS + p.xcol[j],
                                      p.xs + SL * XSTAGE + (XCHUNKS * wave + j) * 1024, 16, 0, 0);
+  // the counted waits below assume this issue order: activations, then codes
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int rb = 0; rb < FRB; ++rb)
     codes[SL][rb] = *reinterpret_cast<const u32x4*>(p.wp + rb * p.rbstride + c * 32);
@@ -122,8 +124,10 @@ __device__ __forceinline__ void fwd_compute(const FwdPipe& p, const u32x4 (&code
 // One pipeline step: issue step c + NST - 1, compute step c, wait for this
 // wave's loads of step c + 1, barrier.  A lane issues LOADS_PER_STEP vector
 // loads per step (activations first, then codes), in step order, so after
-// issuing step c + NST - 1 the loads newer than step c + 1's activations
-// number FRB + LOADS_PER_STEP * (NST - 2).
+// issuing step c + NST - 1 the loads newer than all of step c + 1's number
+// LOADS_PER_STEP * (NST - 2).  Waiting for step c + 1's codes too (not only
+// its activations) keeps the compiler's own wait for the code registers
+// from falling back to a full drain at the top of the unrolled loop.
 template <int SL, int NRB>
 __device__ __forceinline__ void fwd_step(const FwdPipe& p, u32x4 (&codes)[NST][FRB], int c,
                                          f32x16 (&acc)[FRB][4]) {
@@ -131,7 +135,7 @@ __device__ __forceinline__ void fwd_step(const FwdPipe& p, u32x4 (&codes)[NST][F
   __builtin_amdgcn_sched_barrier(0);
   fwd_compute<SL, NRB>(p, codes, c, acc);
   __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(FRB + LOADS_PER_STEP * (NST - 2)));
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS_PER_STEP * (NST - 2)));
   barrier_only();
 }
 
@@ -139,11 +143,18 @@ template <int NRB>
 __device__ __forceinline__ void fwd_loop(const FwdPipe& p, f32x16 (&acc)[FRB][4]) {
   u32x4 codes[NST][FRB];
   const int last = p.nsteps - 1;
+  // The prologue's loads must stay in issue order ahead of the wait: the
+  // compiler may otherwise sink the register loads below it, and the count
+  // would then release before stage 0 has landed.
+  __builtin_amdgcn_sched_barrier(0);
   fwd_issue<0>(p, codes, 0);
+  __builtin_amdgcn_sched_barrier(0);
   fwd_issue<1>(p, codes, min(1, last));
+  __builtin_amdgcn_sched_barrier(0);
   fwd_issue<2>(p, codes, min(2, last));
+  __builtin_amdgcn_sched_barrier(0);
   // the scale panel was written with ordinary LDS stores
-  __builtin_amdgcn_s_waitcnt(waitcnt_imm(FRB + LOADS_PER_STEP * (NST - 2), 0));
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(LOADS_PER_STEP * (NST - 2), 0));
   barrier_only();
   int c = 0;
   for (; c + NST <= p.nsteps; c += NST) {

@@ -17,11 +17,16 @@ hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, int64_
                              int64_t K, int out_bf16, void* out, hipStream_t s);
 
 // route.hip
-constexpr int ROUTER_TOKENS = 8;  // tokens per router workgroup
+constexpr int ROUTER_TOKENS = 8;    // tokens per top-k workgroup (one histogram row each)
+constexpr int PLAN_MAX_ROWS = 256;  // routed rows up to which one workgroup plans the routing
 int router_blocks(int64_t T);
-hipError_t launch_router(const uint16_t* x, const float* wr, const float* br, int T, int H,
-                         int E, int k, int32_t* topk_idx, float* topk_w, int32_t* blk_hist,
-                         hipStream_t s);
+hipError_t launch_logits(const uint16_t* x, const float* wr, const float* br, int T, int H,
+                         int E, float* logits, hipStream_t s);
+hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* topk_idx, float* topk_w,
+                       int32_t* blk_hist, hipStream_t s);
+hipError_t launch_plan(const float* logits, int T, int E, int k, int32_t* topk_idx, float* topk_w,
+                       int32_t* offsets, int32_t* sorted_rows, Tile* tiles, int32_t* num_tiles,
+                       hipStream_t s);
 hipError_t launch_scan(int32_t* blk_hist, int nblk, int E, int32_t* offsets, hipStream_t s);
 hipError_t launch_scatter(const int32_t* topk_idx, const int32_t* blk_base, int T, int k, int E,
                           int32_t* sorted_rows, hipStream_t s);
@@ -45,6 +50,19 @@ hipError_t launch_down(const uint16_t* a, const uint8_t* codes, const uint8_t* s
                        float* y_w, hipStream_t s);
 hipError_t launch_combine(const float* y_w, int64_t T, int H, int k, uint16_t* out,
                           hipStream_t s);
+
+// gemm_dec.hip: forward GEMMs for few rows per expert (weight-streaming)
+int dec_max_k();   // largest contraction length the decode kernels take
+hipError_t launch_dec_gate_up(const uint16_t* x, const uint8_t* codes, const uint8_t* scales,
+                              const uint16_t* bias, const int32_t* sorted_rows, const Tile* tiles,
+                              const int32_t* num_tiles, int max_tiles, int64_t R, int H, int I, int k,
+                              float alpha, float limit, uint16_t* h_out, uint16_t* a_out,
+                              hipStream_t s);
+hipError_t launch_dec_down(const uint16_t* a, const uint8_t* codes, const uint8_t* scales,
+                           const uint16_t* bias, const float* topk_w, const int32_t* sorted_rows,
+                           const Tile* tiles, const int32_t* num_tiles, int max_tiles, int64_t R,
+                           int H, int I,
+                           float* y_w, hipStream_t s);
 
 // gemm_bwd.hip
 int bwd_down_ntiles(int I);

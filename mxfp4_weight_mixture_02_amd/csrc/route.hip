@@ -4,11 +4,14 @@
 // The pages ("Add MXFP4 training support via a dequantize-on-the-fly
 // fallback", "What this does") run a top-k router before the per-expert
 // loop; the finegrained-kernels note on the bias operand describes the
-// grouped path that orders routed rows by expert.  Here the permutation is
-// a deterministic counting sort: per-workgroup histograms, one scan over
-// (expert, workgroup), then each workgroup scatters its rows in ascending
-// flat-row order.  No atomics on global memory, so the result is identical
-// run to run.
+// grouped path that orders routed rows by expert.  Here the logits come
+// from the fp64 matrix cores (exact products, fp64 sums, one rounding to
+// fp32), and the permutation is a deterministic counting sort: per-
+// workgroup histograms, one scan over (expert, workgroup), then each
+// workgroup scatters its rows in ascending flat-row order.  For few routed
+// rows (decode sizes) one workgroup does top-k, histogram, scan, scatter
+// and the tile list in a single launch.  No atomics on global memory, so
+// the result is identical run to run.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -18,140 +21,215 @@ constexpr int RT = ROUTER_TOKENS;
 
 int router_blocks(int64_t T) { return (int)((T + RT - 1) / RT); }
 
-// One workgroup of 256 threads routes RT tokens.  The tokens' activations
-// are staged in LDS once; each wave then takes experts wave, wave + 4, ...
-// and for each holds the expert's router-weight row in registers, spread
-// over the lanes along h (lane l owns h = 4l + 256j .. +3), while the other
-// expert's row is already in flight (two register sets, loop unrolled by
-// two).  Every lane forms partial dot products with all RT tokens; a
-// butterfly over the wave sums them.  The bf16 x fp32 products are exact in
-// fp64 and every partial and total sum is fp64; the logit is rounded once
-// to fp32 and the top-k decision is taken on it.
-constexpr int RCH = 12;             // float4 chunks of a row per lane: h < 256 * RCH = 3072
-constexpr int RH = 256 * RCH;
+// Router logits on the fp64 matrix cores.  l[t, e] = sum_h x[t, h] Wr[e, h]
+// + b[e]: the bf16 x fp32 products are exact in fp64 and are summed in fp64,
+// then the logit is rounded once to fp32 (the routing decision is taken on
+// that value).  A workgroup of LG_W waves computes one 16-token x 16-expert
+// tile with v_mfma_f64_16x16x4f64, wave w over the w-th of LG_W contiguous
+// ranges of h: lane l feeds A[i = l%16][kk = l/16] (token i) and B[kk][j =
+// l%16] (expert j) and holds D[4r + l/16][l%16] in register r.  The
+// contraction index of MFMA step s is mapped to h = base + 8*kk + s, so
+// over 8 steps a lane reads 8 consecutive h of its token row and of its
+// expert row (one 16-byte and one 32-byte load per 32 h).  The LG_W partial
+// tiles are summed through LDS in wave order.  Rows past T or E are clamped
+// and dropped.
+constexpr int LG_CH = 32;   // h per chunk (8 MFMA steps of 4)
+constexpr int LG_W = 16;    // waves per workgroup (h ranges)
+constexpr int LG_P = 6;     // chunks a wave has in flight (H <= 3072: all of them)
 
-__device__ __forceinline__ void router_load_row(f32x4 (&w)[RCH], const float* __restrict__ row,
-                                                int H, int h0, int lane) {
+__device__ __forceinline__ void lg_load(const uint16_t* xp, const float* wp, int c, u32x4& xv,
+                                        f32x4& w0, f32x4& w1) {
+  xv = *reinterpret_cast<const u32x4*>(xp + c * LG_CH);
+  w0 = *reinterpret_cast<const f32x4*>(wp + c * LG_CH);
+  w1 = *reinterpret_cast<const f32x4*>(wp + c * LG_CH + 4);
+}
+
+__device__ __forceinline__ void lg_mfma(const u32x4& xv, const f32x4& w0, const f32x4& w1,
+                                        f64x4& acc) {
 #pragma unroll
-  for (int j = 0; j < RCH; ++j) {
-    const int h = h0 + 4 * lane + 256 * j;
-    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    w[j] = (h < H) ? *reinterpret_cast<const f32x4*>(row + h) : z;
+  for (int s = 0; s < 8; ++s) {
+    const uint32_t xw = xv[s >> 1];
+    const float xf = __uint_as_float((s & 1) ? (xw & 0xFFFF0000u) : (xw << 16));
+    const float wf = (s < 4) ? w0[s] : w1[s - 4];
+    acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)xf, (double)wf, acc, 0, 0, 0);
   }
 }
 
-__device__ __forceinline__ void router_dot_row(const f32x4 (&w)[RCH], const uint16_t* xs, int H,
-                                               int h0, int lane, double (&acc)[RT]) {
+__global__ __launch_bounds__(64 * LG_W) void logits_kernel(const uint16_t* __restrict__ x,
+                                                           const float* __restrict__ wr,
+                                                           const float* __restrict__ br, int T,
+                                                           int H, int E,
+                                                           float* __restrict__ logits) {
+  __shared__ double red[LG_W][4][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int ntt = (T + 15) / 16;
+  const int tt = blockIdx.x % ntt, et = blockIdx.x / ntt;
+  const int nch = H / LG_CH;
+  const int c0 = wave * nch / LG_W, c1 = (wave + 1) * nch / LG_W;
+  const int i = lane & 15, kk = lane >> 4;
+  const int t = min(tt * 16 + i, T - 1), e = min(et * 16 + i, E - 1);
+  const uint16_t* xp = x + (int64_t)t * H + 8 * kk;
+  const float* wp = wr + (int64_t)e * H + 8 * kk;
+  f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+  // all of this wave's loads first (up to LG_P chunks at a time), then the MFMAs
+  for (int cb = c0; cb < c1; cb += LG_P) {
+    u32x4 xv[LG_P];
+    f32x4 w0[LG_P], w1[LG_P];
 #pragma unroll
-  for (int j = 0; j < RCH; ++j) {
-    const int h = h0 + 4 * lane + 256 * j;
-    if (h < H) {
+    for (int q = 0; q < LG_P; ++q) lg_load(xp, wp, min(cb + q, c1 - 1), xv[q], w0[q], w1[q]);
 #pragma unroll
-      for (int tt = 0; tt < RT; ++tt) {
-        const u32x2 xv = *reinterpret_cast<const u32x2*>(xs + tt * H + h);
-        double a = acc[tt];
-        a = fma((double)__uint_as_float(xv[0] << 16), (double)w[j][0], a);
-        a = fma((double)__uint_as_float(xv[0] & 0xFFFF0000u), (double)w[j][1], a);
-        a = fma((double)__uint_as_float(xv[1] << 16), (double)w[j][2], a);
-        a = fma((double)__uint_as_float(xv[1] & 0xFFFF0000u), (double)w[j][3], a);
-        acc[tt] = a;
+    for (int q = 0; q < LG_P; ++q)
+      if (cb + q < c1) lg_mfma(xv[q], w0[q], w1[q], acc);
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) red[wave][r][lane] = acc[r];
+  __syncthreads();
+  if (wave == 0) {
+    const int ex = et * 16 + i;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int tok = tt * 16 + 4 * r + kk;
+      double sum = 0.0;
+#pragma unroll
+      for (int w = 0; w < LG_W; ++w) sum += red[w][r][lane];
+      if (tok < T && ex < E) logits[(int64_t)tok * E + ex] = (float)(sum + (br ? (double)br[ex] : 0.0));
+    }
+  }
+}
+
+// Top-k and softmax of token t by one wave.  Lane l holds the logits of
+// experts l, l + 64, l + 128, l + 192.  k rounds of a wave arg-max (larger
+// logit first, ties to the lower expert) pick the slots in order; the
+// softmax runs over the k selected logits.  Lane 0 writes the slots and
+// counts them in the LDS histogram; with `mask` and `ex` (LDS), it also
+// sets the token's expert bits (mask[t * 8 + e / 32] bit e % 32) and
+// records each slot's expert.
+__device__ __forceinline__ void topk_one(const float* __restrict__ logits, int E, int k, int t,
+                                         int lane, int32_t* __restrict__ topk_idx,
+                                         float* __restrict__ topk_w, int32_t* hist,
+                                         uint32_t* mask, int32_t* ex) {
+  float v[4];
+  uint32_t live = 0;   // bit q: expert lane + 64q exists and is not yet taken
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = lane + 64 * q;
+    v[q] = 0.0f;
+    if (e < E) {
+      live |= 1u << q;
+      v[q] = logits[(int64_t)t * E + e];
+    }
+  }
+  float sel0 = 0.0f, z[8], zsum = 0.0f;
+  int idx[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (j < k) {
+      float bv = 0.0f;
+      int bi = -1;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (((live >> q) & 1u) && (bi < 0 || v[q] > bv)) { bv = v[q]; bi = lane + 64 * q; }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        const float ov = __shfl_xor(bv, o);
+        const int oi = __shfl_xor(bi, o);
+        if (oi >= 0 && (bi < 0 || ov > bv || (ov == bv && oi < bi))) { bv = ov; bi = oi; }
+      }
+      if (j == 0) sel0 = bv;
+      idx[j] = bi;
+      if ((bi & 63) == lane) live &= ~(1u << (bi >> 6));
+      z[j] = expf(bv - sel0);
+      zsum += z[j];
+    }
+  }
+  if (lane == 0) {
+    const int64_t f0 = (int64_t)t * k;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j < k) {
+        topk_idx[f0 + j] = idx[j];
+        topk_w[f0 + j] = z[j] / zsum;
+        atomicAdd(&hist[idx[j]], 1);   // counts only: order does not matter
+        if (mask) mask[t * 8 + (idx[j] >> 5)] |= 1u << (idx[j] & 31);
+        if (ex) ex[f0 + j] = idx[j];
       }
     }
   }
 }
 
-// Sum over the wave (fixed butterfly order) and store the RT logits of e.
-__device__ __forceinline__ void router_finish(double (&acc)[RT], int e, const float* br,
-                                              int lane, float (*lg)[257]) {
-#pragma unroll
-  for (int tt = 0; tt < RT; ++tt) {
-    double v = acc[tt];
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-    if (lane == 0) lg[tt][e] = (float)(v + (br ? (double)br[e] : 0.0));
-    acc[tt] = 0.0;
-  }
-}
-
-__global__ __launch_bounds__(256) void router_kernel(
-    const uint16_t* __restrict__ x, const float* __restrict__ wr, const float* __restrict__ br,
-    int T, int H, int E, int k, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
-    int32_t* __restrict__ blk_hist) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t xs[];   // [RT][H]
-  __shared__ float lg[RT][257];
+// RT tokens per workgroup, two per wave; writes the workgroup's expert
+// histogram for the scan.
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T, int E,
+                                                   int k, int32_t* __restrict__ topk_idx,
+                                                   float* __restrict__ topk_w,
+                                                   int32_t* __restrict__ blk_hist) {
   __shared__ int32_t hist[256];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int t0 = blockIdx.x * RT;
-  const int nt = min(RT, T - t0);
-
-  // stage the tokens (rows past T are zero)
-  const int row8 = H / 8;  // 16-byte pieces per row
-  for (int q = tid; q < RT * row8; q += 256) {
-    const int tt = q / row8, c = q % row8;
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    reinterpret_cast<u32x4*>(xs)[q] =
-        tt < nt ? reinterpret_cast<const u32x4*>(x + (int64_t)(t0 + tt) * H)[c] : z;
-  }
   hist[tid] = 0;
   __syncthreads();
-
-  double acc[RT];
 #pragma unroll
-  for (int tt = 0; tt < RT; ++tt) acc[tt] = 0.0;
-  f32x4 w0[RCH], w1[RCH];
-  if (H <= RH) {
-    // whole rows in registers; the next expert's row loads during this one
-    int e = wave;
-    if (e < E) router_load_row(w0, wr + (int64_t)e * H, H, 0, lane);
-    for (; e < E; e += 8) {
-      if (e + 4 < E) router_load_row(w1, wr + (int64_t)(e + 4) * H, H, 0, lane);
-      router_dot_row(w0, xs, H, 0, lane, acc);
-      router_finish(acc, e, br, lane, lg);
-      if (e + 4 >= E) break;
-      if (e + 8 < E) router_load_row(w0, wr + (int64_t)(e + 8) * H, H, 0, lane);
-      router_dot_row(w1, xs, H, 0, lane, acc);
-      router_finish(acc, e + 4, br, lane, lg);
-    }
-  } else {
-    for (int e = wave; e < E; e += 4) {
-      for (int h0 = 0; h0 < H; h0 += RH) {
-        router_load_row(w0, wr + (int64_t)e * H, H, h0, lane);
-        router_dot_row(w0, xs, H, h0, lane, acc);
-      }
-      router_finish(acc, e, br, lane, lg);
-    }
-  }
-  __syncthreads();
-
-  // top-k per token: k passes of an arg-max, ties to the lower index
-  if (tid < nt) {
-    const int tt = tid;
-    uint64_t taken[4] = {0, 0, 0, 0};
-    float sel[8];
-    int idx[8];
-    for (int j = 0; j < k; ++j) {
-      int best = -1;
-      float bv = 0.0f;
-      for (int e = 0; e < E; ++e) {
-        if ((taken[e >> 6] >> (e & 63)) & 1) continue;
-        float v = lg[tt][e];
-        if (best < 0 || v > bv) { best = e; bv = v; }
-      }
-      taken[best >> 6] |= 1ull << (best & 63);
-      idx[j] = best;
-      sel[j] = bv;
-    }
-    float z[8], sum = 0.0f;
-    for (int j = 0; j < k; ++j) { z[j] = expf(sel[j] - sel[0]); sum += z[j]; }
-    const int64_t f0 = (int64_t)(t0 + tt) * k;
-    for (int j = 0; j < k; ++j) {
-      topk_idx[f0 + j] = idx[j];
-      topk_w[f0 + j] = z[j] / sum;
-      atomicAdd(&hist[idx[j]], 1);  // counts only: order does not matter
-    }
+  for (int q = 0; q < RT / 4; ++q) {
+    const int t = blockIdx.x * RT + wave * (RT / 4) + q;
+    if (t < T) topk_one(logits, E, k, t, lane, topk_idx, topk_w, hist, nullptr, nullptr);
   }
   __syncthreads();
   if (tid < E) blk_hist[(int64_t)blockIdx.x * E + tid] = hist[tid];
+}
+
+// Few routed rows (R = T*k <= PLAN_MAX_ROWS, so T <= 256): top-k,
+// histogram, offsets, the stable permutation and the tile list in one
+// workgroup of 1024 threads.  Row f = (t, j) of expert e goes to offsets[e]
+// + (number of tokens t' < t that chose e), which keeps ascending f within
+// an expert; the count comes from the tokens' expert bitmasks.
+__global__ __launch_bounds__(1024) void plan_kernel(
+    const float* __restrict__ logits, int T, int E, int k, int32_t* __restrict__ topk_idx,
+    float* __restrict__ topk_w, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_rows,
+    Tile* __restrict__ tiles, int32_t* __restrict__ num_tiles) {
+  __shared__ int32_t hist[256];
+  __shared__ int32_t off[257];
+  __shared__ int32_t tstart[257];
+  __shared__ uint32_t mask[PLAN_MAX_ROWS * 8];
+  __shared__ int32_t ex[PLAN_MAX_ROWS];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid < 256) hist[tid] = 0;
+  for (int q = tid; q < T * 8; q += 1024) mask[q] = 0u;
+  __syncthreads();
+  for (int t = wave; t < T; t += 16)
+    topk_one(logits, E, k, t, lane, topk_idx, topk_w, hist, mask, ex);
+  __syncthreads();
+  if (tid == 0) {
+    int32_t run = 0, trun = 0;
+    for (int e = 0; e < E; ++e) {
+      off[e] = run;
+      tstart[e] = trun;
+      run += hist[e];
+      trun += (hist[e] + MT - 1) / MT;
+    }
+    off[E] = run;
+    *num_tiles = trun;
+  }
+  __syncthreads();
+  if (tid <= E) offsets[tid] = off[tid];
+  if (tid < E) {
+    const int32_t n = hist[tid];
+    for (int32_t q = 0; q * MT < n; ++q) {
+      Tile tl;
+      tl.expert = tid;
+      tl.row0 = off[tid] + q * MT;
+      tl.rows = min(MT, n - q * MT);
+      tl.pad = 0;
+      tiles[tstart[tid] + q] = tl;
+    }
+  }
+  if (tid < T * k) {
+    const int t = tid / k;
+    const int e = ex[tid];
+    const int w = e >> 5;
+    const uint32_t bit = 1u << (e & 31);
+    int rank = 0;
+    for (int u = 0; u < t; ++u) rank += (mask[u * 8 + w] & bit) ? 1 : 0;
+    sorted_rows[off[e] + rank] = tid;
+  }
 }
 
 // One workgroup of 1024 threads.  In place, blk_hist[b][e] becomes the
@@ -224,7 +302,9 @@ __global__ __launch_bounds__(64) void scatter_kernel(const int32_t* __restrict__
   }
 }
 
-int max_tiles(int64_t R, int E) { return (int)((R + MT - 1) / MT) + E; }
+// Upper bound on the tile count: sum_e ceil(n_e / MT) <= R / MT + (number
+// of non-empty experts), and at most min(E, R) experts are non-empty.
+int max_tiles(int64_t R, int E) { return (int)((R + MT - 1) / MT + (R < E ? R : E)); }
 
 // Tiles of at most MT sorted rows, expert by expert (one workgroup).
 __global__ __launch_bounds__(256) void tiles_kernel(const int32_t* __restrict__ offsets, int E,
@@ -256,12 +336,28 @@ __global__ __launch_bounds__(256) void tiles_kernel(const int32_t* __restrict__ 
   }
 }
 
-hipError_t launch_router(const uint16_t* x, const float* wr, const float* br, int T, int H,
-                         int E, int k, int32_t* topk_idx, float* topk_w, int32_t* blk_hist,
-                         hipStream_t s) {
-  const size_t lds = (size_t)RT * H * sizeof(uint16_t);
-  hipLaunchKernelGGL(router_kernel, dim3(router_blocks(T)), dim3(256), lds, s, x, wr, br, T, H, E,
-                     k, topk_idx, topk_w, blk_hist);
+hipError_t launch_logits(const uint16_t* x, const float* wr, const float* br, int T, int H,
+                         int E, float* logits, hipStream_t s) {
+  if (H % LG_CH) return hipErrorInvalidValue;
+  const int64_t blocks = (int64_t)((T + 15) / 16) * ((E + 15) / 16);
+  hipLaunchKernelGGL(logits_kernel, dim3((unsigned)blocks), dim3(64 * LG_W), 0, s, x, wr, br, T, H,
+                     E, logits);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* topk_idx, float* topk_w,
+                       int32_t* blk_hist, hipStream_t s) {
+  hipLaunchKernelGGL(topk_kernel, dim3(router_blocks(T)), dim3(256), 0, s, logits, T, E, k,
+                     topk_idx, topk_w, blk_hist);
+  return hipGetLastError();
+}
+
+hipError_t launch_plan(const float* logits, int T, int E, int k, int32_t* topk_idx, float* topk_w,
+                       int32_t* offsets, int32_t* sorted_rows, Tile* tiles, int32_t* num_tiles,
+                       hipStream_t s) {
+  if ((int64_t)T * k > PLAN_MAX_ROWS) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, logits, T, E, k, topk_idx, topk_w,
+                     offsets, sorted_rows, tiles, num_tiles);
   return hipGetLastError();
 }
 

@@ -205,6 +205,43 @@ def test_forward_is_deterministic():
         assert torch.equal(getattr(s1, n).view(torch.uint8), getattr(s2, n).view(torch.uint8)), n
 
 
+@pytest.mark.parametrize("shape", [dict(T=16), dict(T=64, H=128, I=128, E=64, k=8),
+                                   dict(T=300, H=192, I=320, E=3, k=2),
+                                   dict(T=40, E=16, k=4, lora_rank=16)])
+def test_results_do_not_depend_on_buffer_contents(shape):
+    # Every buffer the library reads must have been written by the same
+    # call: with the workspace, the output and the saved state pre-filled
+    # with NaN (bytes 0xFF), forward and backward reproduce the results of a
+    # call on zeroed buffers bit for bit.
+    from mxfp4_weight_mixture_02_amd import SavedState, Workspace
+    s = syn.spec("tiny", **shape)
+    _say(f"buffer-contents check {shape}")
+    dl = device_layer(s)
+    x = bf16_tensor(syn.tokens(s)).to(DEV)
+    dy = bf16_tensor(syn.upstream_grad(s)).to(DEV)
+    res = []
+    for fill in (0x00, 0xFF, 0xFF):
+        ws = Workspace()
+        ws.get(1 << 24, x.device).fill_(fill)
+        sv = SavedState.empty(dl, s.T, x.device)
+        for n in ("topk_idx", "topk_w", "expert_offsets", "sorted_rows", "h", "a", "lora_v"):
+            t = getattr(sv, n)
+            if t is not None:
+                t.view(torch.uint8).fill_(fill)
+        out = torch.empty_like(x)
+        out.view(torch.uint8).fill_(fill)
+        mxfp4_moe_forward(dl, x, saved=sv, out=out, workspace=ws)
+        ws.buf.fill_(fill)
+        dx = torch.empty_like(x)
+        dx.view(torch.uint8).fill_(fill)
+        _, dA, dB = mxfp4_moe_backward_dx(dl, sv, dy, dx=dx, workspace=ws)
+        torch.cuda.synchronize()
+        res.append([out, sv.h, sv.a, dx] + ([dA, dB, sv.lora_v] if s.lora_rank else []))
+    for r in res[1:]:
+        for g, ref in zip(r, res[0]):
+            assert torch.equal(g.view(torch.uint8), ref.view(torch.uint8))
+
+
 def test_inference_forward_equals_saved_forward():
     s = syn.spec("tiny", T=77)
     dl = device_layer(s)
