@@ -69,10 +69,8 @@ __device__ constexpr int vmcnt_imm(int n) { return waitcnt_imm(n, 15); }
 struct FwdPipe {
   const uint16_t* xrow[XCHUNKS];   // activation rows this lane stages
   int xcol[XCHUNKS];               // element offset of its 16-byte slot within a step
-  const uint8_t* wp;               // this lane's codes, row block 0 (+ lane half)
-  int64_t rbstride;                // bytes between its row blocks (32 rows)
-  const uint8_t* srow;             // scale panel row of row block 0 in LDS
-  int sbstride;                    // panel bytes between row blocks
+  const uint8_t* wp[FRB];          // this lane's codes per row block (+ lane half)
+  const uint8_t* srow[FRB];        // its scale panel rows in LDS
   uint8_t* xs;                     // LDS stages
   int nsteps;
 };
@@ -90,7 +88,7 @@ __device__ __forceinline__ void fwd_issue(const FwdPipe& p, u32x4 (&codes)[NST][
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int rb = 0; rb < FRB; ++rb)
-    codes[SL][rb] = *reinterpret_cast<const u32x4*>(p.wp + rb * p.rbstride + c * 32);
+    codes[SL][rb] = *reinterpret_cast<const u32x4*>(p.wp[rb] + c * 32);
 }
 
 template <int SL, int NRB>
@@ -100,7 +98,7 @@ __device__ __forceinline__ void fwd_compute(const FwdPipe& p, const u32x4 (&code
   const int l32 = lane & 31, hlf = lane >> 5;
   float sc[FRB];
 #pragma unroll
-  for (int rb = 0; rb < FRB; ++rb) sc[rb] = scale_operand(p.srow[rb * p.sbstride + 2 * c + hlf]);
+  for (int rb = 0; rb < FRB; ++rb) sc[rb] = scale_operand(p.srow[rb][2 * c + hlf]);
   const uint8_t* st = p.xs + SL * XSTAGE;
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
@@ -209,10 +207,14 @@ __device__ __forceinline__ void fwd_body(const uint16_t* const (&xrow)[XCHUNKS],
     p.xcol[j] = 8 * ((lane & 7) ^ ((row >> 1) & 7));       // global column block of its slot
   }
   const int64_t rowbytes = K / 2;
-  p.wp = codes_e + (int64_t)(n0 + wrow_local) * rowbytes + hlf * 16;
-  p.rbstride = 32 * rowbytes;
-  p.srow = panel + wrow_local * KB32;
-  p.sbstride = 32 * KB32;
+  // row blocks past the workgroup's rows (the last column tile can hold
+  // fewer than 128 rows per wave) read its last row; their results are dropped
+#pragma unroll
+  for (int rb = 0; rb < FRB; ++rb) {
+    const int r = min(wrow_local + 32 * rb, nrows - 1);
+    p.wp[rb] = codes_e + (int64_t)(n0 + r) * rowbytes + hlf * 16;
+    p.srow[rb] = panel + r * KB32;
+  }
   p.xs = lds;
   p.nsteps = K / FKS;
   switch (nrb) {
@@ -285,6 +287,10 @@ __global__ __launch_bounds__(FNTHR) void gate_up_kernel(
   }
 }
 
+// LORA: add the rank-16 delta s (v B_e^T) (a template parameter: a runtime
+// branch around these MFMAs makes the compiler spill accumulators inside
+// the main loop).
+template <bool LORA>
 __global__ __launch_bounds__(FNTHR) void down_kernel(
     const uint16_t* __restrict__ a, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, const uint16_t* __restrict__ bias,
@@ -310,28 +316,26 @@ __global__ __launch_bounds__(FNTHR) void down_kernel(
   }
   const int nrows = min(FNT, N - n0);
   f32x16 acc[FRB][4];
+  const int wrow_local = (wave * 32 * FRB < nrows ? wave * 32 * FRB : 0) + l32;
   fwd_body(xrow, codes + (int64_t)e * N * (I / 2), scales + (int64_t)e * N * (I / 32), I, n0,
-           nrows, (wave * 32 * FRB < nrows ? wave * 32 * FRB : 0) + l32, (tl.rows + 31) / 32, lds,
-           acc);
-  if (lora_B) {
+           nrows, wrow_local, (tl.rows + 31) / 32, lds, acc);
+  if (LORA) {
     // + s v B_e^T: one more 16-deep contraction over the rank, A-operand =
-    // B_e rows (the weight rows of this wave), B-operand = s v as hi + lo bf16
-    bf16x8 vh[4], vl[4];
+    // B_e rows (this lane's weight rows), B-operand = s v as hi + lo bf16;
+    // one token block at a time to keep few registers live
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
       const float* vp = lora_v + (int64_t)(tl.row0 + min(tb * 32 + l32, tl.rows - 1)) * LORA_R + 8 * hlf;
+      bf16x8 vh, vl;
       split_bf16x8(*reinterpret_cast<const f32x4*>(vp), *reinterpret_cast<const f32x4*>(vp + 4),
-                   lora_scale, &vh[tb], &vl[tb]);
-    }
+                   lora_scale, &vh, &vl);
 #pragma unroll
-    for (int rb = 0; rb < FRB; ++rb) {
-      const int n = n0 + wave * 32 * FRB + rb * 32 + l32;
-      if (n - l32 >= N) continue;
-      const bf16x8 bw = as_bf16x8(*reinterpret_cast<const u32x4*>(lora_B + ((int64_t)e * N + n) * LORA_R + 8 * hlf));
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
-        acc[rb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bw, vh[tb], acc[rb][tb], 0, 0, 0);
-        acc[rb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bw, vl[tb], acc[rb][tb], 0, 0, 0);
+      for (int rb = 0; rb < FRB; ++rb) {
+        const int r = min(wrow_local + 32 * rb, nrows - 1);
+        const bf16x8 bw = as_bf16x8(*reinterpret_cast<const u32x4*>(
+            lora_B + ((int64_t)e * N + n0 + r) * LORA_R + 8 * hlf));
+        acc[rb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bw, vh, acc[rb][tb], 0, 0, 0);
+        acc[rb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bw, vl, acc[rb][tb], 0, 0, 0);
       }
     }
   }
@@ -400,8 +404,12 @@ hipError_t launch_down(const uint16_t* a, const uint8_t* codes, const uint8_t* s
                        float* y_w, hipStream_t s) {
   if (!fwd_step_k(I)) return hipErrorInvalidValue;
   dim3 grid(((H + FNT - 1) / FNT) * max_tiles), block(FNTHR);
-  hipLaunchKernelGGL(down_kernel, grid, block, 0, s, a, codes, scales, bias, topk_w, sorted_rows,
-                     tiles, num_tiles, H, I, lora_B, lora_v, lora_scale, y_w);
+  if (lora_B)
+    hipLaunchKernelGGL(down_kernel<true>, grid, block, 0, s, a, codes, scales, bias, topk_w,
+                       sorted_rows, tiles, num_tiles, H, I, lora_B, lora_v, lora_scale, y_w);
+  else
+    hipLaunchKernelGGL(down_kernel<false>, grid, block, 0, s, a, codes, scales, bias, topk_w,
+                       sorted_rows, tiles, num_tiles, H, I, lora_B, lora_v, lora_scale, y_w);
   return hipGetLastError();
 }
 
