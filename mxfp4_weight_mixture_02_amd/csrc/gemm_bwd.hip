@@ -84,7 +84,8 @@ __device__ __forceinline__ void store_block_t(const RawBlock& rb, uint16_t* dst_
 // waves run the MFMAs of step c from LDS; one barrier per step.  Step
 // indices are clamped at the end instead of branching around loads, so the
 // compiler's wait counts stay exact.  The loop is unrolled by two so every
-// register set has a fixed name.
+// register set has a fixed name.  The step's barrier waits for LDS stores
+// only, so the loads of step c + 2 stay in flight across it.
 template <int WN>
 struct BwdPipe {
   u32x4 xv[2][BwdTile<WN>::PPT];
@@ -139,7 +140,13 @@ __device__ __forceinline__ void bwd_step(BwdPipe<WN>& pp, const uint16_t* const 
       acc[1][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b, acc[1][tb], 0, 0, 0);
     }
   }
-  __syncthreads();
+  // The next step reads what this one staged: wait for this wave's LDS
+  // stores (lgkmcnt) only.  A fenced __syncthreads would also drain the
+  // global loads of step c + 2 issued above; their registers get the
+  // compiler's own counted waits where they are used.
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+  barrier_only();
 }
 
 template <int WN, int NRB>
