@@ -16,24 +16,49 @@
 //
 // Transposed operand.  The MFMA wants 8 consecutive contraction elements
 // per lane, but the packed rows run along the output axis and the UE8M0
-// scales are blocked along it too.  Each thread therefore loads an 8x8
-// block (8 stored rows x one dword of 8 codes), decodes each row with its
-// own scale (one scaled conversion per code pair), transposes the 8x8 bf16
-// block in registers with byte permutes, and writes 8 contraction-ordered
-// 16-byte rows into LDS; the MFMA A-operand is then one 16-byte LDS read.
-// Output tiling and accumulator layout are those of the forward GEMMs.
+// scales are blocked along it too.  Each thread therefore loads 8x8 blocks
+// (8 stored rows x one dword of 8 codes), decodes each row with its own
+// scale (one scaled conversion per code pair), transposes the bf16 block in
+// registers with byte permutes, and writes 8 contraction-ordered 16-byte
+// rows into LDS; the MFMA A-operand is then one 16-byte LDS read.
+//
+// Tiling.  A workgroup computes 512 output columns x 128 routed rows with 4
+// waves, one per SIMD; wave w owns output columns 128w..128w+127 (four
+// 32-column MFMA blocks) for all 128 rows (four 32-row blocks): 16
+// accumulators of 32x32 fp32, all 256 accumulation registers.  Per K step
+// of 64 a wave reads 4 A- and 4 B-fragments per 16 MFMAs from LDS, which
+// keeps LDS traffic (reads plus the staging writes) under the MFMA time.
+//
+// LDS: the transposed weights [512][64] bf16 and the activations [128][64]
+// bf16, both double-buffered, exactly 160 KB, no padding.  Row r's eight
+// 16-byte blocks are permuted by XOR with f(r) = (r ^ (r >> 3)) & 7 for
+// the weights and r & 7 for the activations; the MFMA reads (32
+// consecutive rows, one logical block), the transposed writes (rows 8j+c
+// for 64 consecutive j) and the activation writes (8 blocks of one row)
+// then each touch 8 distinct 16-byte bank groups per 8 lanes.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace mxmoe {
 
-template <int WN>
-struct BwdTile {
-  static constexpr int NTHR = 64 * WN;
-  static constexpr int NT = 64 * WN;         // output columns per workgroup
-  static constexpr int PPT = MT * 8 / NTHR;  // 16-byte B pieces per thread per step
-  static constexpr int OB = NT / 8;          // 8-column blocks across the tile
-};
+constexpr int BW = 4;                      // waves per workgroup, one per SIMD
+constexpr int BTHR = 64 * BW;
+constexpr int BRB = 4;                     // 32-column output blocks per wave
+constexpr int BNT = 32 * BRB * BW;         // output columns per workgroup (512)
+constexpr int BKC = 64;                    // contraction per step
+constexpr int BBLK = (BKC / 8) * (BNT / 8) / BTHR;   // 8x8 weight blocks per thread per step (2)
+constexpr int BPPT = MT * 8 / BTHR;        // 16-byte activation pieces per thread per step (4)
+constexpr int WS_BYTES = BNT * BKC * 2;    // one weight buffer (64 KB)
+constexpr int XS_BYTES = MT * BKC * 2;     // one activation buffer (16 KB)
+constexpr int BLDS = 2 * WS_BYTES + 2 * XS_BYTES;    // 160 KB
+static_assert(BBLK == 2 && BPPT == 4, "thread work assumed below");
+
+__device__ __forceinline__ int ws_off(int row, int blk) {
+  return row * 128 + ((blk ^ ((row ^ (row >> 3)) & 7)) << 4);
+}
+__device__ __forceinline__ int xs_off(int row, int blk) {
+  return row * 128 + ((blk ^ (row & 7)) << 4);
+}
 
 // Raw codes and scales of one thread's 8x8 block for one K step.
 struct RawBlock {
@@ -51,9 +76,10 @@ __device__ __forceinline__ void load_block(RawBlock& rb, const uint8_t* __restri
   }
 }
 
-// Decode the 8x8 block and store it transposed: dst row o (0..7) gets the
-// 8 contraction-ordered bf16 of output column o.
-__device__ __forceinline__ void store_block_t(const RawBlock& rb, uint16_t* dst_row0) {
+// Decode the 8x8 block (contraction rows 8cb.., output columns 8ob..) and
+// store it transposed: weight row 8ob + j gets the 8 contraction-ordered
+// bf16 of output column j, in logical block cb.
+__device__ __forceinline__ void store_block_t(const RawBlock& rb, uint8_t* ws, int ob, int cb) {
   u32x4 R[8];
 #pragma unroll
   for (int r = 0; r < 8; ++r) R[r] = dequant8_bf16(rb.code[r], scale_operand(rb.scale[r]));
@@ -65,80 +91,77 @@ __device__ __forceinline__ void store_block_t(const RawBlock& rb, uint16_t* dst_
       lo[m] = __builtin_amdgcn_perm(R[2 * m + 1][j], R[2 * m][j], 0x05040100u);
       hi[m] = __builtin_amdgcn_perm(R[2 * m + 1][j], R[2 * m][j], 0x07060302u);
     }
-    *reinterpret_cast<u32x4*>(dst_row0 + (2 * j) * LDS_ROW) = lo;
-    *reinterpret_cast<u32x4*>(dst_row0 + (2 * j + 1) * LDS_ROW) = hi;
+    *reinterpret_cast<u32x4*>(ws + ws_off(8 * ob + 2 * j, cb)) = lo;
+    *reinterpret_cast<u32x4*>(ws + ws_off(8 * ob + 2 * j + 1, cb)) = hi;
   }
 }
 
-// Main loop shared by the two backward GEMMs.  W is stored [C rows][O
-// cols] (packed along O); this workgroup produces output columns o0.. for
-// routed rows whose contraction vectors are brow[j] (length C).  Rows past
-// the tile point at its first row and weight blocks past the last output
-// column at the first one, so every load is unconditional (the affected
-// products are never stored); only the first NRB 32-row blocks hold rows.
-//
-// Pipeline: global loads run two K steps ahead.  In step c a thread issues
-// the loads of step c+2 (activation pieces and its raw 8x8 weight block),
-// stores the step c+1 data it loaded one step earlier into the other LDS
-// buffers (the weight block decoded and transposed on the way), then the
-// waves run the MFMAs of step c from LDS; one barrier per step.  Step
-// indices are clamped at the end instead of branching around loads, so the
-// compiler's wait counts stay exact.  The loop is unrolled by two so every
-// register set has a fixed name.  The step's barrier waits for LDS stores
-// only, so the loads of step c + 2 stay in flight across it.
-template <int WN>
+// Per-thread state of the two-deep pipeline: registers of steps c+1 and c+2.
 struct BwdPipe {
-  u32x4 xv[2][BwdTile<WN>::PPT];
-  RawBlock raw[2];
+  u32x4 xv[2][BPPT];
+  RawBlock raw[2][BBLK];
 };
 
-template <int WN, int PAR>
-__device__ __forceinline__ void bwd_issue(BwdPipe<WN>& pp, const uint16_t* const (&brow)[BwdTile<WN>::PPT],
-                                          const uint8_t* bcode, const uint8_t* bscale,
-                                          int64_t crow, int64_t srow, int c) {
+struct BwdArgs {
+  const uint16_t* brow[BPPT];   // activation rows this thread stages (+ its 8-element piece)
+  const uint8_t* bcode[BBLK];   // its weight blocks' first code row, at step 0
+  const uint8_t* bscale[BBLK];  // and first scale row
+  int64_t crow, srow;           // bytes between stored rows (codes, scales)
+  int nsteps;
+};
+
+template <int PAR>
+__device__ __forceinline__ void bwd_issue(BwdPipe& pp, const BwdArgs& g, int c) {
 #pragma unroll
-  for (int j = 0; j < BwdTile<WN>::PPT; ++j)
-    pp.xv[PAR][j] = *reinterpret_cast<const u32x4*>(brow[j] + c * KC);
-  load_block(pp.raw[PAR], bcode + (int64_t)c * KC * crow, bscale + (int64_t)c * KC * srow, crow,
-             srow);
+  for (int j = 0; j < BPPT; ++j) pp.xv[PAR][j] = *reinterpret_cast<const u32x4*>(g.brow[j] + c * BKC);
+#pragma unroll
+  for (int i = 0; i < BBLK; ++i)
+    load_block(pp.raw[PAR][i], g.bcode[i] + (int64_t)c * BKC * g.crow,
+               g.bscale[i] + (int64_t)c * BKC * g.srow, g.crow, g.srow);
 }
 
-template <int WN, int PAR>
-__device__ __forceinline__ void bwd_stage(const BwdPipe<WN>& pp, uint16_t* wdst,
-                                          uint16_t (*xs)[MT][LDS_ROW]) {
+template <int PAR>
+__device__ __forceinline__ void bwd_stage(const BwdPipe& pp, uint8_t* lds) {
   const int tid = threadIdx.x;
+  uint8_t* ws = lds + PAR * WS_BYTES;
+  uint8_t* xs = lds + 2 * WS_BYTES + PAR * XS_BYTES;
 #pragma unroll
-  for (int j = 0; j < BwdTile<WN>::PPT; ++j) {
-    int q = tid + j * BwdTile<WN>::NTHR;
-    *reinterpret_cast<u32x4*>(&xs[PAR][q >> 3][(q & 7) * 8]) = pp.xv[PAR][j];
+  for (int j = 0; j < BPPT; ++j) {
+    const int q = tid + j * BTHR;
+    *reinterpret_cast<u32x4*>(xs + xs_off(q >> 3, q & 7)) = pp.xv[PAR][j];
   }
-  store_block_t(pp.raw[PAR], wdst);
+#pragma unroll
+  for (int i = 0; i < BBLK; ++i) {
+    const int q = tid + i * BTHR;
+    store_block_t(pp.raw[PAR][i], ws, q & 63, q >> 6);
+  }
 }
 
-template <int WN, int NRB, int PAR>
-__device__ __forceinline__ void bwd_step(BwdPipe<WN>& pp, const uint16_t* const (&brow)[BwdTile<WN>::PPT],
-                                         const uint8_t* bcode, const uint8_t* bscale,
-                                         int64_t crow, int64_t srow, int c, int nsteps,
-                                         uint16_t* wdst_next,
-                                         uint16_t (*ws)[BwdTile<WN>::NT][LDS_ROW],
-                                         uint16_t (*xs)[MT][LDS_ROW], f32x16 (&acc)[2][4]) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+template <int NRB, int PAR>
+__device__ __forceinline__ void bwd_step(BwdPipe& pp, const BwdArgs& g, int c, uint8_t* lds,
+                                         f32x16 (&acc)[BRB][4]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l32 = lane & 31, hlf = lane >> 5;
-  bwd_issue<WN, PAR>(pp, brow, bcode, bscale, crow, srow, min(c + 2, nsteps - 1));
+  bwd_issue<PAR>(pp, g, min(c + 2, g.nsteps - 1));
   __builtin_amdgcn_sched_barrier(0);  // keep the loads at the top of the step
-  bwd_stage<WN, PAR ^ 1>(pp, wdst_next, xs);
+  bwd_stage<PAR ^ 1>(pp, lds);
+  const uint8_t* ws = lds + PAR * WS_BYTES;
+  const uint8_t* xs = lds + 2 * WS_BYTES + PAR * XS_BYTES;
 #pragma unroll
   for (int st = 0; st < 4; ++st) {
-    const int r0 = wave * 64 + l32, r1 = r0 + 32;
-    const int lcb = 4 * hlf + st;
-    const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(&ws[PAR][r0][(lcb ^ ((r0 >> 4) & 7)) * 8]);
-    const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(&ws[PAR][r1][(lcb ^ ((r1 >> 4) & 7)) * 8]);
+    const int lb = 4 * hlf + st;
+    bf16x8 a[BRB], b[NRB];
 #pragma unroll
-    for (int tb = 0; tb < NRB; ++tb) {
-      const bf16x8 b = *reinterpret_cast<const bf16x8*>(&xs[PAR][tb * 32 + l32][hlf * 32 + st * 8]);
-      acc[0][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b, acc[0][tb], 0, 0, 0);
-      acc[1][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b, acc[1][tb], 0, 0, 0);
-    }
+    for (int rb = 0; rb < BRB; ++rb)
+      a[rb] = *reinterpret_cast<const bf16x8*>(ws + ws_off(wave * 32 * BRB + rb * 32 + l32, lb));
+#pragma unroll
+    for (int tb = 0; tb < NRB; ++tb)
+      b[tb] = *reinterpret_cast<const bf16x8*>(xs + xs_off(tb * 32 + l32, lb));
+#pragma unroll
+    for (int rb = 0; rb < BRB; ++rb)
+#pragma unroll
+      for (int tb = 0; tb < NRB; ++tb)
+        acc[rb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[rb], b[tb], acc[rb][tb], 0, 0, 0);
   }
   // The next step reads what this one staged: wait for this wave's LDS
   // stores (lgkmcnt) only.  A fenced __syncthreads would also drain the
@@ -149,68 +172,74 @@ __device__ __forceinline__ void bwd_step(BwdPipe<WN>& pp, const uint16_t* const 
   barrier_only();
 }
 
-template <int WN, int NRB>
-__device__ __forceinline__ void bwd_mainloop_n(const uint16_t* const (&brow)[BwdTile<WN>::PPT],
-                                               const uint8_t* bcode, const uint8_t* bscale,
-                                               int64_t crow, int64_t srow, int nsteps,
-                                               uint16_t* wdst0, uint16_t* wdst1,
-                                               uint16_t (*ws)[BwdTile<WN>::NT][LDS_ROW],
-                                               uint16_t (*xs)[MT][LDS_ROW], f32x16 (&acc)[2][4]) {
-  BwdPipe<WN> pp;
-  bwd_issue<WN, 0>(pp, brow, bcode, bscale, crow, srow, 0);
-  bwd_issue<WN, 1>(pp, brow, bcode, bscale, crow, srow, min(1, nsteps - 1));
-  bwd_stage<WN, 0>(pp, wdst0, xs);
+// Pipeline: global loads run two K steps ahead.  In step c a thread issues
+// the loads of step c+2, stores the step c+1 data it loaded one step
+// earlier into the other LDS buffers (the weight blocks decoded and
+// transposed on the way), then the waves run the MFMAs of step c from LDS;
+// one barrier per step.  Step indices are clamped at the end instead of
+// branching around loads, so the compiler's wait counts stay exact.  The
+// loop is unrolled by two so every register set has a fixed name.
+template <int NRB>
+__device__ __forceinline__ void bwd_loop(const BwdArgs& g, uint8_t* lds, f32x16 (&acc)[BRB][4]) {
+  BwdPipe pp;
+  bwd_issue<0>(pp, g, 0);
+  bwd_issue<1>(pp, g, min(1, g.nsteps - 1));
+  bwd_stage<0>(pp, lds);
   __syncthreads();
   int c = 0;
-  for (; c + 1 < nsteps; c += 2) {
-    bwd_step<WN, NRB, 0>(pp, brow, bcode, bscale, crow, srow, c, nsteps, wdst1, ws, xs, acc);
-    bwd_step<WN, NRB, 1>(pp, brow, bcode, bscale, crow, srow, c + 1, nsteps, wdst0, ws, xs, acc);
+  for (; c + 1 < g.nsteps; c += 2) {
+    bwd_step<NRB, 0>(pp, g, c, lds, acc);
+    bwd_step<NRB, 1>(pp, g, c + 1, lds, acc);
   }
-  if (c < nsteps)
-    bwd_step<WN, NRB, 0>(pp, brow, bcode, bscale, crow, srow, c, nsteps, wdst1, ws, xs, acc);
+  if (c < g.nsteps) bwd_step<NRB, 0>(pp, g, c, lds, acc);
+  __syncthreads();   // LDS is free for the epilogue
 }
 
-template <int WN>
-__device__ __forceinline__ void bwd_mainloop(const uint16_t* const (&brow)[BwdTile<WN>::PPT],
+// Main loop shared by the two backward GEMMs.  W is stored [C rows][O
+// cols] (packed along O); this workgroup produces output columns o0..o0+511
+// for routed rows whose contraction vectors are brow[j] (length C).  Rows
+// past the tile point at its first row and weight blocks past the last
+// output column at the first one, so every load is unconditional (the
+// affected products are never stored); only the first NRB 32-row blocks
+// hold rows.
+__device__ __forceinline__ void bwd_mainloop(const uint16_t* const (&brow)[BPPT],
                                              const uint8_t* __restrict__ wcode,
                                              const uint8_t* __restrict__ wscale, int C, int O,
-                                             int o0, int nrb,
-                                             uint16_t (*ws)[BwdTile<WN>::NT][LDS_ROW],
-                                             uint16_t (*xs)[MT][LDS_ROW], f32x16 (&acc)[2][4]) {
-  using BT = BwdTile<WN>;
+                                             int o0, int nrb, uint8_t* lds,
+                                             f32x16 (&acc)[BRB][4]) {
   const int tid = threadIdx.x;
-  const int nsteps = C / KC;
-  const int64_t crow = O / 2, srow = O / 32;
-
-  // this thread's 8x8 weight block: rows 8*cb.., output columns 8*ob..
-  const int cb = tid / BT::OB, ob = tid % BT::OB;
-  const int ocol = (o0 + 8 * ob < O) ? o0 + 8 * ob : 0;
-  const uint8_t* bcode = wcode + (int64_t)(8 * cb) * crow + ocol / 2;
-  const uint8_t* bscale = wscale + (int64_t)(8 * cb) * srow + ocol / 32;
-  // column block swizzle: 16-byte block c of row r sits at c ^ ((r >> 4) & 7),
-  // which spreads both these transposed writes and the MFMA reads over all
-  // banks (all 8 rows of this thread's block share r >> 4 = ob >> 1)
-  const int pcb = cb ^ ((ob >> 1) & 7);
-  uint16_t* const wdst0 = &ws[0][8 * ob][8 * pcb];
-  uint16_t* const wdst1 = &ws[1][8 * ob][8 * pcb];
-
+  BwdArgs g;
+  g.nsteps = C / BKC;
+  g.crow = O / 2;
+  g.srow = O / 32;
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
+  for (int j = 0; j < BPPT; ++j) g.brow[j] = brow[j];
+#pragma unroll
+  for (int i = 0; i < BBLK; ++i) {
+    const int q = tid + i * BTHR;
+    const int cb = q >> 6, ob = q & 63;
+    const int ocol = (o0 + 8 * ob < O) ? o0 + 8 * ob : 0;
+    g.bcode[i] = wcode + (int64_t)(8 * cb) * g.crow + ocol / 2;
+    g.bscale[i] = wscale + (int64_t)(8 * cb) * g.srow + ocol / 32;
+  }
+#pragma unroll
+  for (int rb = 0; rb < BRB; ++rb)
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[rb][tb][r] = 0.0f;
-
   switch (nrb) {
-    case 1: bwd_mainloop_n<WN, 1>(brow, bcode, bscale, crow, srow, nsteps, wdst0, wdst1, ws, xs, acc); break;
-    case 2: bwd_mainloop_n<WN, 2>(brow, bcode, bscale, crow, srow, nsteps, wdst0, wdst1, ws, xs, acc); break;
-    case 3: bwd_mainloop_n<WN, 3>(brow, bcode, bscale, crow, srow, nsteps, wdst0, wdst1, ws, xs, acc); break;
-    default: bwd_mainloop_n<WN, 4>(brow, bcode, bscale, crow, srow, nsteps, wdst0, wdst1, ws, xs, acc); break;
+    case 1: bwd_loop<1>(g, lds, acc); break;
+    case 2: bwd_loop<2>(g, lds, acc); break;
+    case 3: bwd_loop<3>(g, lds, acc); break;
+    default: bwd_loop<4>(g, lds, acc); break;
   }
 }
 
-template <int WN>
-__global__ __launch_bounds__(64 * WN) void bwd_down_kernel(
+// LORA: add dv_u A_e (a template parameter: a runtime branch around these
+// MFMAs makes the compiler spill accumulators).
+template <bool LORA>
+__global__ __launch_bounds__(BTHR) void bwd_down_kernel(
     const uint16_t* __restrict__ dy, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, const float* __restrict__ topk_w,
     const int32_t* __restrict__ sorted_rows, const Tile* __restrict__ tiles,
@@ -218,70 +247,66 @@ __global__ __launch_bounds__(64 * WN) void bwd_down_kernel(
     const uint16_t* __restrict__ asv, int H, int I, int k, float alpha, float limit,
     const uint16_t* __restrict__ lora_At, const float* __restrict__ lora_dvu,
     uint16_t* __restrict__ dh, float* __restrict__ dw_part) {
-  using BT = BwdTile<WN>;
-  __shared__ __attribute__((aligned(16))) uint16_t ws[2][BT::NT][LDS_ROW];
-  __shared__ __attribute__((aligned(16))) uint16_t xs[2][MT][LDS_ROW];
-  __shared__ float red[WN][MT];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[BLDS];
   int mt, ot;
-  const int otiles = (I + BT::NT - 1) / BT::NT;
+  const int otiles = (I + BNT - 1) / BNT;
   if (!xcd_work_item(*num_tiles, otiles, &mt, &ot)) return;
   const Tile tl = tiles[mt];
-  const int o0 = ot * BT::NT;
+  const int o0 = ot * BNT;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hlf = lane >> 5;
   const int e = tl.expert;
 
-  const uint16_t* brow[BT::PPT];
+  const uint16_t* brow[BPPT];
 #pragma unroll
-  for (int j = 0; j < BT::PPT; ++j) {
-    int q = tid + j * BT::NTHR;
-    int r = q >> 3;
+  for (int j = 0; j < BPPT; ++j) {
+    const int q = tid + j * BTHR;
+    const int r = q >> 3;
     const int f = sorted_rows[tl.row0 + (r < tl.rows ? r : 0)];
     brow[j] = dy + (int64_t)(f / k) * H + (q & 7) * 8;
   }
   // Wd is stored [H rows][I cols]: contraction over h (C = H), output i (O = I)
-  const bool wave_live = o0 + wave * 64 < I;
   const uint8_t* wcode = codes + (int64_t)e * H * (I / 2);
   const uint8_t* wscale = scales + (int64_t)e * H * (I / 32);
-  f32x16 acc[2][4];
-  bwd_mainloop<WN>(brow, wcode, wscale, H, I, o0, (tl.rows + 31) / 32, ws, xs, acc);
-  if (lora_At) {
+  f32x16 acc[BRB][4];
+  bwd_mainloop(brow, wcode, wscale, H, I, o0, (tl.rows + 31) / 32, lds, acc);
+  if (LORA) {
     // + dv_u A_e (dv_u = s dY B_e, unweighted like the accumulators): a
     // 16-deep contraction, A-operand = rows of A_e^T, B-operand = dv_u as
     // hi + lo bf16.  Through the accumulators it also reaches the dw
     // partial: sum_i (dv_u A_e)_i a_i = dv_u . v, the adapter's share of dY . y.
-    bf16x8 vh[4], vl[4];
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
       const float* vp = lora_dvu + (int64_t)(tl.row0 + min(tb * 32 + l32, tl.rows - 1)) * LORA_R + 8 * hlf;
+      bf16x8 vh, vl;
       split_bf16x8(*reinterpret_cast<const f32x4*>(vp), *reinterpret_cast<const f32x4*>(vp + 4),
-                   1.0f, &vh[tb], &vl[tb]);
-    }
+                   1.0f, &vh, &vl);
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      const int i = o0 + wave * 64 + rb * 32 + l32;
-      const bf16x8 aw = as_bf16x8(*reinterpret_cast<const u32x4*>(lora_At + ((int64_t)e * I + (i < I ? i : 0)) * LORA_R + 8 * hlf));
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
-        acc[rb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw, vh[tb], acc[rb][tb], 0, 0, 0);
-        acc[rb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw, vl[tb], acc[rb][tb], 0, 0, 0);
+      for (int rb = 0; rb < BRB; ++rb) {
+        const int i = o0 + wave * 32 * BRB + rb * 32 + l32;
+        const bf16x8 aw = as_bf16x8(*reinterpret_cast<const u32x4*>(
+            lora_At + ((int64_t)e * I + (i < I ? i : 0)) * LORA_R + 8 * hlf));
+        acc[rb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw, vh, acc[rb][tb], 0, 0, 0);
+        acc[rb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw, vl, acc[rb][tb], 0, 0, 0);
       }
     }
   }
 
+  float* red = reinterpret_cast<float*>(lds);   // [BW][MT], after the main loop's last barrier
   const int N2 = 2 * I;
 #pragma unroll
   for (int tb = 0; tb < 4; ++tb) {
     const int rt = tb * 32 + l32;
     float dwp = 0.0f;
-    if (wave_live && rt < tl.rows) {
+    if (rt < tl.rows) {
       const int64_t p = tl.row0 + rt;
       const float wf = topk_w[sorted_rows[p]];
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
+      for (int rb = 0; rb < BRB; ++rb) {
+        if (o0 + wave * 32 * BRB + rb * 32 >= I) continue;   // column block past I
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int i4 = o0 + wave * 64 + rb * 32 + 8 * q + 4 * hlf;
+          const int i4 = o0 + wave * 32 * BRB + rb * 32 + 8 * q + 4 * hlf;
           const u32x2 av = *reinterpret_cast<const u32x2*>(asv + p * I + i4);
           const u32x4 hv = *reinterpret_cast<const u32x4*>(hsv + p * N2 + 2 * i4);
           u32x4 out;
@@ -303,51 +328,46 @@ __global__ __launch_bounds__(64 * WN) void bwd_down_kernel(
       }
     }
     dwp += __shfl_xor(dwp, 32);
-    if (hlf == 0) red[wave][rt] = dwp;
+    if (hlf == 0) red[wave * MT + rt] = dwp;
   }
   __syncthreads();
   if (tid < tl.rows) {
     float s = 0.0f;
 #pragma unroll
-    for (int w = 0; w < WN; ++w) s += red[w][tid];
+    for (int w = 0; w < BW; ++w) s += red[w * MT + tid];
     const int64_t f = sorted_rows[tl.row0 + tid];
     dw_part[f * otiles + ot] = s;
   }
 }
 
-template <int WN>
-__global__ __launch_bounds__(64 * WN) void bwd_gate_up_kernel(
+__global__ __launch_bounds__(BTHR) void bwd_gate_up_kernel(
     const uint16_t* __restrict__ dh, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, const int32_t* __restrict__ sorted_rows,
     const Tile* __restrict__ tiles, const int32_t* __restrict__ num_tiles, int H, int I,
     float* __restrict__ dxr) {
-  using BT = BwdTile<WN>;
-  __shared__ __attribute__((aligned(16))) uint16_t ws[2][BT::NT][LDS_ROW];
-  __shared__ __attribute__((aligned(16))) uint16_t xs[2][MT][LDS_ROW];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[BLDS];
   int mt, ot;
-  const int otiles = (H + BT::NT - 1) / BT::NT;
+  const int otiles = (H + BNT - 1) / BNT;
   if (!xcd_work_item(*num_tiles, otiles, &mt, &ot)) return;
   const Tile tl = tiles[mt];
-  const int o0 = ot * BT::NT;
+  const int o0 = ot * BNT;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hlf = lane >> 5;
   const int e = tl.expert;
   const int N2 = 2 * I;
 
-  const uint16_t* brow[BT::PPT];
+  const uint16_t* brow[BPPT];
 #pragma unroll
-  for (int j = 0; j < BT::PPT; ++j) {
-    int q = tid + j * BT::NTHR;
-    int r = q >> 3;
+  for (int j = 0; j < BPPT; ++j) {
+    const int q = tid + j * BTHR;
+    const int r = q >> 3;
     brow[j] = dh + (int64_t)(tl.row0 + (r < tl.rows ? r : 0)) * N2 + (q & 7) * 8;
   }
   // Wgu is stored [2I rows][H cols]: contraction over n (C = 2I), output h (O = H)
-  const bool wave_live = o0 + wave * 64 < H;
   const uint8_t* wcode = codes + (int64_t)e * N2 * (H / 2);
   const uint8_t* wscale = scales + (int64_t)e * N2 * (H / 32);
-  f32x16 acc[2][4];
-  bwd_mainloop<WN>(brow, wcode, wscale, N2, H, o0, (tl.rows + 31) / 32, ws, xs, acc);
-  if (!wave_live) return;
+  f32x16 acc[BRB][4];
+  bwd_mainloop(brow, wcode, wscale, N2, H, o0, (tl.rows + 31) / 32, lds, acc);
 
 #pragma unroll
   for (int tb = 0; tb < 4; ++tb) {
@@ -355,15 +375,17 @@ __global__ __launch_bounds__(64 * WN) void bwd_gate_up_kernel(
     if (rt >= tl.rows) continue;
     const int64_t f = sorted_rows[tl.row0 + rt];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int rb = 0; rb < BRB; ++rb) {
+      if (o0 + wave * 32 * BRB + rb * 32 >= H) continue;   // column block past H
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int h4 = o0 + wave * 64 + rb * 32 + 8 * q + 4 * hlf;
+        const int h4 = o0 + wave * 32 * BRB + rb * 32 + 8 * q + 4 * hlf;
         f32x4 v;
 #pragma unroll
         for (int m = 0; m < 4; ++m) v[m] = acc[rb][tb][4 * q + m];
         *reinterpret_cast<f32x4*>(dxr + f * H + h4) = v;
       }
+    }
   }
 }
 
@@ -427,9 +449,7 @@ __global__ __launch_bounds__(256) void bwd_combine_kernel(
   }
 }
 
-constexpr int BWD_WN = 4;
-
-int bwd_down_ntiles(int I) { return (I + BwdTile<BWD_WN>::NT - 1) / BwdTile<BWD_WN>::NT; }
+int bwd_down_ntiles(int I) { return (I + BNT - 1) / BNT; }
 
 hipError_t launch_bwd_down(const uint16_t* dy, const uint8_t* codes, const uint8_t* scales,
                            const float* topk_w, const int32_t* sorted_rows, const Tile* tiles,
@@ -437,10 +457,16 @@ hipError_t launch_bwd_down(const uint16_t* dy, const uint8_t* codes, const uint8
                            const uint16_t* a, int H, int I, int k, float alpha, float limit,
                            const uint16_t* lora_At, const float* lora_dvu, uint16_t* dh,
                            float* dw_part, hipStream_t s) {
+  if (H % BKC || I % 64) return hipErrorInvalidValue;
   dim3 grid(bwd_down_ntiles(I) * max_tiles);
-  hipLaunchKernelGGL(bwd_down_kernel<BWD_WN>, grid, dim3(64 * BWD_WN), 0, s, dy, codes, scales,
-                     topk_w, sorted_rows, tiles, num_tiles, h, a, H, I, k, alpha, limit,
-                     lora_At, lora_dvu, dh, dw_part);
+  if (lora_At)
+    hipLaunchKernelGGL(bwd_down_kernel<true>, grid, dim3(BTHR), 0, s, dy, codes, scales, topk_w,
+                       sorted_rows, tiles, num_tiles, h, a, H, I, k, alpha, limit, lora_At,
+                       lora_dvu, dh, dw_part);
+  else
+    hipLaunchKernelGGL(bwd_down_kernel<false>, grid, dim3(BTHR), 0, s, dy, codes, scales, topk_w,
+                       sorted_rows, tiles, num_tiles, h, a, H, I, k, alpha, limit, lora_At,
+                       lora_dvu, dh, dw_part);
   return hipGetLastError();
 }
 
@@ -448,10 +474,10 @@ hipError_t launch_bwd_gate_up(const uint16_t* dh, const uint8_t* codes, const ui
                               const int32_t* sorted_rows, const Tile* tiles,
                               const int32_t* num_tiles, int max_tiles, int H, int I,
                               float* dxr, hipStream_t s) {
-  constexpr int NT = BwdTile<BWD_WN>::NT;
-  dim3 grid(((H + NT - 1) / NT) * max_tiles);
-  hipLaunchKernelGGL(bwd_gate_up_kernel<BWD_WN>, grid, dim3(64 * BWD_WN), 0, s, dh, codes,
-                     scales, sorted_rows, tiles, num_tiles, H, I, dxr);
+  if ((2 * I) % BKC || H % 64) return hipErrorInvalidValue;
+  dim3 grid(((H + BNT - 1) / BNT) * max_tiles);
+  hipLaunchKernelGGL(bwd_gate_up_kernel, grid, dim3(BTHR), 0, s, dh, codes, scales, sorted_rows,
+                     tiles, num_tiles, H, I, dxr);
   return hipGetLastError();
 }
 
