@@ -42,7 +42,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=8)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=16)
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the 120b skewed-routing and 16384-token LoRA workloads")
     ap.add_argument("--profile", action="store_true",
                     help="for rocprofv3 runs: one 256 MiB device-to-device copy (a known-size "
                          "calibration for the traffic counters), then warmup + steps of the "
@@ -264,6 +266,18 @@ def main():
                                "kernel_us": kd}
         del copies
 
+    # ---- the other full-size workloads (not the headline): the gpt-oss-120b
+    # layer with Zipf-skewed routing (forward + dX) and the 16384-token LoRA
+    # training step (forward, recompute forward, dX backward with dA/dB)
+    extra = {}
+    if not args.no_extra:
+        del saved, wsf, wsb
+        torch.cuda.empty_cache()
+        extra["120b_8192_zipf_fwd_dx"] = extra_workload(
+            syn.spec("120b_8192_zipf"), args, lora=False)
+        extra["20b_16384_lora_train_step"] = extra_workload(
+            syn.spec("20b_16384_lora"), args, lora=True)
+
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(dt * 1e3, 4),
@@ -275,12 +289,95 @@ def main():
         "fwd_tflops": round(fwd_tflops, 2), "fwd_ms": round(dt_fwd * 1e3, 4),
         "ms_per_step_with_kernel_events": round(dt_inst * 1e3, 4),
         "kernel_us": kernels, "decode": decode, "roofline": roofline,
+        "workloads": extra,
     }
 
     # ---- CPU oracle on a bounded sample of the same workload
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(s, args.cpu_sample_tokens)
     print(json.dumps(line), flush=True)
+
+
+def extra_workload(s, args, lora):
+    """Throughput of one more full-size layer.  Expert weights ~N(0, 0.02)
+    are drawn on the GPU (torch's generator, fixed seed) and quantised by the
+    library; router weights, router bias (the Zipf skew), tokens and the
+    upstream gradient come from the seeded generators.  Without LoRA a step
+    is forward (saved) + dX; with LoRA it is the training step of a
+    checkpointed layer: forward, recompute forward (saved), dX + dA/dB."""
+    import numpy as np
+    import torch
+
+    import moe_synth as syn
+    from mxfp4_weight_mixture_02_amd import (MoeLayer, SavedState, Workspace,
+                                             mxfp4_moe_backward_dx, mxfp4_moe_forward,
+                                             mxfp4_quantize)
+    dev = "cuda:0"
+    T, H, I, E, k = s.T, s.H, s.I, s.E, s.k
+    R = T * k
+    g = torch.Generator(device=dev).manual_seed(s.seed)
+    gu_c = torch.empty((E, 2 * I, H // 2), dtype=torch.uint8, device=dev)
+    gu_s = torch.empty((E, 2 * I, H // 32), dtype=torch.uint8, device=dev)
+    dn_c = torch.empty((E, H, I // 2), dtype=torch.uint8, device=dev)
+    dn_s = torch.empty((E, H, I // 32), dtype=torch.uint8, device=dev)
+    for e in range(E):
+        c, sc = mxfp4_quantize(torch.randn((2 * I, H), generator=g, device=dev) * 0.02)
+        gu_c[e].copy_(c)
+        gu_s[e].copy_(sc)
+        c, sc = mxfp4_quantize(torch.randn((H, I), generator=g, device=dev) * 0.02)
+        dn_c[e].copy_(c)
+        dn_s[e].copy_(sc)
+
+    def bf(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    layer = MoeLayer(torch.from_numpy(syn.router_weight(s)).to(dev),
+                     torch.from_numpy(syn.router_bias(s)).to(dev), gu_c, gu_s,
+                     (torch.randn((E, 2 * I), generator=g, device=dev) * 0.01).bfloat16(),
+                     dn_c, dn_s, (torch.randn((E, H), generator=g, device=dev) * 0.01).bfloat16(),
+                     k=k)
+    if lora:
+        layer.lora_A = bf(syn.lora_a(s))
+        layer.lora_B = bf(syn.lora_b(s))
+    x = bf(syn.tokens(s))
+    dy = bf(syn.upstream_grad(s))
+    sv = SavedState.empty(layer, T, dev)
+    out = torch.empty_like(x)
+    dx = torch.empty_like(x)
+    wsf, wsb = Workspace(), Workspace()
+    dA = dB = None
+    if lora:
+        dA = torch.empty(layer.lora_A.shape, dtype=torch.float32, device=dev)
+        dB = torch.empty(layer.lora_B.shape, dtype=torch.float32, device=dev)
+
+    def step():
+        if lora:
+            mxfp4_moe_forward(layer, x, out=out, workspace=wsf)
+        mxfp4_moe_forward(layer, x, saved=sv, out=out, workspace=wsf)
+        mxfp4_moe_backward_dx(layer, sv, dy, dx=dx, workspace=wsb, dA=dA, dB=dB)
+
+    steps = max(3, args.steps // 4)
+    for _ in range(2):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    passes = 3 if lora else 2
+    flops = passes * 2.0 * R * 3 * H * I
+    if lora:
+        flops += 6 * 2.0 * R * 16 * (H + I) / 2   # v, y delta, dv_u, da delta, dA, dB
+    hist = torch.bincount(sv.topk_idx.flatten().long(), minlength=E)
+    res = {"T": T, "E": E, "k": k, "ms_per_step": round(dt * 1e3, 3),
+           "TFLOP/s": round(flops / dt / 1e12, 2), "steps": steps,
+           "step": ("forward, recompute forward (saved), dX + dA/dB backward" if lora
+                    else "forward (saved) + dX backward"),
+           "max_rows_per_expert": int(hist.max()), "empty_experts": int((hist == 0).sum())}
+    del layer, sv, wsf, wsb, gu_c, gu_s, dn_c, dn_s
+    torch.cuda.empty_cache()
+    return res
 
 
 def cpu_baseline(s, n_tok):

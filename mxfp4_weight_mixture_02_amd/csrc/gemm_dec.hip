@@ -158,10 +158,11 @@ static size_t dec_lds_bytes(int K, int rb) {
 }
 
 // Weight rows per workgroup: 32 while few rows are routed (so the grid
-// still covers the chip), up to 128 when more are, so that one staging of
-// the activation rows serves more weight rows.
+// still covers the chip), 64 when more are, so that one staging of the
+// activation rows serves more weight rows (128 drops to one wave per SIMD
+// and measured slower).
 static int dec_rb(int64_t R, int N) {
-  int rb = R <= 16 ? 1 : R <= 64 ? 2 : 4;
+  int rb = R <= 16 ? 1 : 2;
   while (rb > 1 && N % (32 * rb)) rb >>= 1;
   return rb;
 }
