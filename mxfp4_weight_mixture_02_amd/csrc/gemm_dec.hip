@@ -4,147 +4,152 @@
 //
 // With T*k <= 256 an expert owns a handful of rows, so the work is bound by
 // reading its weights once (13.2 MB per gpt-oss-20b expert), not by MFMA.
-// A workgroup takes one tile (one expert's rows, at most 128) and 32 weight
-// rows; its 4 waves split the contraction K into 4 contiguous ranges.  Each
-// wave issues every code and scale load of its range before computing, so a
-// workgroup keeps 32 x K/2 bytes in flight at once, and the grid (tiles x
-// N/32 workgroups) covers the chip even at one token.  The routed rows'
-// activations are staged in LDS in groups of 8 and fed as the MFMA
-// B-operand (columns 8..31 of the 32-wide block repeat them and are
-// dropped); the codes stay in registers across groups.  The 4 partial
-// accumulators are summed through LDS (over the staged rows, once every
-// wave has finished reading them), and wave w finishes accumulator
-// registers 4w..4w+3: gate/up pairs still sit in neighbouring registers of
-// one lane, so the bias + clamped SwiGLU epilogue is the forward GEMM's.
+// A workgroup takes one tile (one expert's rows, at most 128) and WPB x 32
+// weight rows; each wave owns 32 rows over the whole contraction and
+// streams their codes in chunks of DD K-steps, two chunks in registers (the
+// next one in flight while the current one is computed), so no wave waits
+// on another after the activation rows are staged.  The routed rows'
+// activations are staged in LDS in groups of DG (8 or 16) and fed as the
+// MFMA B-operand (columns past the group repeat its last row and are
+// dropped); a larger group re-streams the codes.  The accumulator layout and
+// the bias + clamped SwiGLU epilogue are those of the forward GEMMs: gate/up
+// pairs sit in neighbouring registers of one lane.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace mxmoe {
 
-constexpr int DW = 4;                    // waves per workgroup (K split)
-constexpr int DG = 8;                    // routed rows per activation group
-constexpr int DSTEPS = 12;               // max 64-wide K steps per wave
-constexpr int DEC_MAXK = DW * DSTEPS * 64;
+constexpr int DEC_MAXK = 3072;           // contraction lengths the kernels take
 constexpr int DEC_XPAD = 8;              // bf16 of padding per staged row
 
 int dec_max_k() { return DEC_MAXK; }
 
-template <bool GATE_UP, int RB>
-__global__ __launch_bounds__(64 * DW) void dec_kernel(
+constexpr int DD = 9;                    // K steps (64 wide) per streamed chunk
+
+struct DecChunk {
+  u32x4 c[DD];
+};
+
+// Codes of chunk ch (steps DD*ch ..), clamped to the last step.
+__device__ __forceinline__ void dec_issue(DecChunk& b, const uint8_t* wrow, int ch, int nsteps) {
+#pragma unroll
+  for (int i = 0; i < DD; ++i) {
+    const int c = min(ch * DD + i, nsteps - 1);
+    b.c[i] = *reinterpret_cast<const u32x4*>(wrow + c * 32);
+  }
+}
+
+// srow: this lane's row of the scale panel in LDS (+ lane half)
+__device__ __forceinline__ void dec_compute(const DecChunk& b, const uint16_t* xb,
+                                            const uint8_t* srow, int ch, int nsteps,
+                                            f32x16& acc) {
+#pragma unroll
+  for (int i = 0; i < DD; ++i) {
+    const int c = ch * DD + i;
+    if (c < nsteps) {
+      const float sc = scale_operand(srow[2 * c]);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const bf16x8 a = as_bf16x8(dequant8_bf16(b.c[i][s], sc));
+        const bf16x8 bb = *reinterpret_cast<const bf16x8*>(xb + 64 * c + 8 * s);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bb, acc, 0, 0, 0);
+      }
+    }
+  }
+}
+
+template <bool GATE_UP>
+__global__ __launch_bounds__(512) void dec_kernel(
     const uint16_t* __restrict__ src,      // gate_up: x [T, K]; down: a [R, K] (sorted)
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
     const uint16_t* __restrict__ bias, const float* __restrict__ topk_w,
     const int32_t* __restrict__ sorted_rows, const Tile* __restrict__ tiles,
-    const int32_t* __restrict__ num_tiles, int K, int N, int k, float alpha, float limit,
+    const int32_t* __restrict__ num_tiles, int K, int N, int k, int DG, float alpha, float limit,
     uint16_t* __restrict__ h_out, uint16_t* __restrict__ a_out, float* __restrict__ y_w) {
+  // LDS: the scale panel of the workgroup's weight rows [32 * wpb][K / 32]
+  // (one contiguous span of the scale tensor, copied in 16-byte pieces), then
+  // the activation group [DG][K + DEC_XPAD] bf16
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  const int nrb = N / (32 * RB);
-  const int tile = blockIdx.x / nrb, rb0 = (blockIdx.x % nrb) * RB;
+  const int wpb = blockDim.x >> 6;
+  const int nblk = (N + 32 * wpb - 1) / (32 * wpb);
+  const int tile = blockIdx.x / nblk, rbk = blockIdx.x % nblk;
   if (tile >= *num_tiles) return;
   const Tile tl = tiles[tile];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hlf = lane >> 5;
   const int e = tl.expert;
-  const int xrow = K + DEC_XPAD;                       // staged row stride (bf16)
-  uint16_t* xs = reinterpret_cast<uint16_t*>(lds);      // [DG][xrow]
-  float* red = reinterpret_cast<float*>(lds);          // [DW][RB][16][64], reuses xs
-
-  // this wave's K steps; per row block its row of codes and scales
+  const int xrow = K + DEC_XPAD;
+  const int n0 = (rbk * wpb + wave) * 32;      // this wave's first weight row
+  const bool live = n0 < N;                    // N % 32 == 0: a block is all in or out
+  const int n = live ? n0 + l32 : l32;
+  const uint8_t* wrow = codes + ((int64_t)e * N + n) * (K / 2) + hlf * 16;
   const int nsteps = K / 64;
-  const int per = (nsteps + DW - 1) / DW;
-  const int c0 = min(wave * per, nsteps), cnt = min(per, nsteps - c0);
-  u32x4 cv[RB][DSTEPS];
-  uint32_t sv[RB][DSTEPS];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int n = (rb0 + rb) * 32 + l32;
-    const uint8_t* wrow = codes + ((int64_t)e * N + n) * (K / 2) + hlf * 16;
-    const uint8_t* srow = scales + ((int64_t)e * N + n) * (K / 32) + hlf;
-#pragma unroll
-    for (int i = 0; i < DSTEPS; ++i) {
-      const int c = c0 + min(i, cnt - 1);             // clamped: never past the row
-      cv[rb][i] = *reinterpret_cast<const u32x4*>(wrow + c * 32);
-      sv[rb][i] = srow[2 * c];
-    }
+  const int nch = (nsteps + DD - 1) / DD;
+  const int npieces = K / 8;
+  uint8_t* panel = lds;
+  uint16_t* xs = reinterpret_cast<uint16_t*>(lds + 32 * wpb * (K / 32));
+  {
+    const int r0 = rbk * wpb * 32;
+    const int n16 = min(32 * wpb, N - r0) * (K / 32) / 16;
+    const u32x4* ps = reinterpret_cast<const u32x4*>(scales + ((int64_t)e * N + r0) * (K / 32));
+    for (int q = tid; q < n16; q += blockDim.x) reinterpret_cast<u32x4*>(panel)[q] = ps[q];
   }
+  const uint8_t* srow = panel + (live ? wave * 32 + l32 : 0) * (K / 32) + hlf;
 
   for (int g0 = 0; g0 < tl.rows; g0 += DG) {
     // stage the group's activation rows (only the ones that exist)
     const int ng = min(DG, tl.rows - g0);
-    for (int q = tid; q < ng * (K / 8); q += 64 * DW) {
-      const int p = q / (K / 8), col = (q % (K / 8)) * 8;
+    for (int q = tid; q < ng * npieces; q += blockDim.x) {
+      const int p = q / npieces, col = (q % npieces) * 8;
       const int rt = tl.row0 + g0 + p;
-      const int64_t srow_ = GATE_UP ? (int64_t)(sorted_rows[rt] / k) : (int64_t)rt;
+      const int64_t sr = GATE_UP ? (int64_t)(sorted_rows[rt] / k) : (int64_t)rt;
       *reinterpret_cast<u32x4*>(xs + p * xrow + col) =
-          *reinterpret_cast<const u32x4*>(src + srow_ * K + col);
+          *reinterpret_cast<const u32x4*>(src + sr * K + col);
     }
     __syncthreads();
-    f32x16 acc[RB];
+    f32x16 acc;
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[rb][r] = 0.0f;
-    // B-operand column l32 reads row min(l32 % 8, ng - 1): columns past the
-    // group repeat its last row and are dropped
-    const uint16_t* xb = xs + min(l32 & (DG - 1), ng - 1) * xrow + 32 * hlf;
-#pragma unroll
-    for (int i = 0; i < DSTEPS; ++i) {
-      if (i < cnt) {
-        const int c = c0 + i;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const bf16x8 b = *reinterpret_cast<const bf16x8*>(xb + 64 * c + 8 * s);
-#pragma unroll
-          for (int rb = 0; rb < RB; ++rb) {
-            const bf16x8 a = as_bf16x8(dequant8_bf16(cv[rb][i][s], scale_operand(sv[rb][i])));
-            acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[rb], 0, 0, 0);
-          }
-        }
+    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+    if (live) {
+      // B-operand column l32 reads row min(l32 % DG, ng - 1)
+      const uint16_t* xb = xs + min(l32 % DG, ng - 1) * xrow + 32 * hlf;
+      DecChunk b0, b1;
+      dec_issue(b0, wrow, 0, nsteps);
+      for (int ch = 0; ch < nch; ch += 2) {
+        dec_issue(b1, wrow, min(ch + 1, nch - 1), nsteps);
+        dec_compute(b0, xb, srow, ch, nsteps, acc);
+        if (ch + 1 >= nch) break;
+        dec_issue(b0, wrow, min(ch + 2, nch - 1), nsteps);
+        dec_compute(b1, xb, srow, ch + 1, nsteps, acc);
       }
-    }
-    // sum the K-range partials: wave w finishes registers 4w..4w+3 of
-    // every row block
-    __syncthreads();   // every wave is done reading xs
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) red[((wave * RB + rb) * 16 + r) * 64 + lane] = acc[rb][r];
-    __syncthreads();
-    const int p = g0 + l32;
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      float v[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float sum = 0.0f;
-#pragma unroll
-        for (int w = 0; w < DW; ++w) sum += red[((w * RB + rb) * 16 + 4 * wave + i) * 64 + lane];
-        v[i] = sum;
-      }
-      // lane: column p of the group, weight rows nb + i
+      // lane: column p = l32 of the group, weight rows nb + i (registers 4q + i)
+      const int p = g0 + l32;
       if (l32 < DG && p < tl.rows) {
-        const int nb = (rb0 + rb) * 32 + 8 * wave + 4 * hlf;
-        float bv[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) bv[i] = bias ? bf16_to_f32(bias[(int64_t)e * N + nb + i]) : 0.0f;
         const int64_t rho = tl.row0 + p;
-        if (GATE_UP) {
-          const int I = N / 2;
-          const float g0v = v[0] + bv[0], u0 = v[1] + bv[1], g1v = v[2] + bv[2], u1 = v[3] + bv[3];
-          if (h_out) {
-            u32x2 hv = {saved_preact_bf16(g0v, limit, false) | (saved_preact_bf16(u0, limit, true) << 16),
-                        saved_preact_bf16(g1v, limit, false) | (saved_preact_bf16(u1, limit, true) << 16)};
-            *reinterpret_cast<u32x2*>(h_out + rho * N + nb) = hv;
-          }
-          *reinterpret_cast<uint32_t*>(a_out + rho * I + nb / 2) =
-              pack_bf16x2(swiglu(g0v, u0, alpha, limit), swiglu(g1v, u1, alpha, limit));
-        } else {
-          const int64_t f = sorted_rows[rho];
-          const float wf = topk_w[f];
-          f32x4 y;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) y[i] = wf * (v[i] + bv[i]);
-          *reinterpret_cast<f32x4*>(y_w + f * N + nb) = y;
+        for (int q = 0; q < 4; ++q) {
+          const int nb = n0 + 8 * q + 4 * hlf;
+          float v[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            v[i] = acc[4 * q + i] + (bias ? bf16_to_f32(bias[(int64_t)e * N + nb + i]) : 0.0f);
+          if (GATE_UP) {
+            const int I = N / 2;
+            if (h_out) {
+              u32x2 hv = {saved_preact_bf16(v[0], limit, false) | (saved_preact_bf16(v[1], limit, true) << 16),
+                          saved_preact_bf16(v[2], limit, false) | (saved_preact_bf16(v[3], limit, true) << 16)};
+              *reinterpret_cast<u32x2*>(h_out + rho * N + nb) = hv;
+            }
+            *reinterpret_cast<uint32_t*>(a_out + rho * I + nb / 2) =
+                pack_bf16x2(swiglu(v[0], v[1], alpha, limit), swiglu(v[2], v[3], alpha, limit));
+          } else {
+            const int64_t f = sorted_rows[rho];
+            const float wf = topk_w[f];
+            f32x4 y;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) y[i] = wf * v[i];
+            *reinterpret_cast<f32x4*>(y_w + f * N + nb) = y;
+          }
         }
       }
     }
@@ -152,39 +157,178 @@ __global__ __launch_bounds__(64 * DW) void dec_kernel(
   }
 }
 
-static size_t dec_lds_bytes(int K, int rb) {
-  const size_t xs = (size_t)DG * (K + DEC_XPAD) * 2, red = (size_t)DW * rb * 16 * 64 * 4;
-  return xs > red ? xs : red;
-}
-
-// Weight rows per workgroup: 32 while few rows are routed (so the grid
-// still covers the chip), 64 when more are, so that one staging of the
-// activation rows serves more weight rows (128 drops to one wave per SIMD
-// and measured slower).
-static int dec_rb(int64_t R, int N) {
-  int rb = R <= 16 ? 1 : 2;
-  while (rb > 1 && N % (32 * rb)) rb >>= 1;
-  return rb;
-}
+// Very few routed rows (T*k <= 16: a few experts, a row or two each): the
+// streaming kernel's one-wave-per-32-rows grid is too small to keep enough
+// bytes in flight, so here the 4 waves of a workgroup split one 32-row
+// block's contraction and issue every code load of their K quarter up
+// front.  The partial accumulators are summed through LDS in wave order
+// (over the staged rows, once every wave has read them) and wave w finishes
+// accumulator registers 4w..4w+3 (gate/up pairs stay in one lane).
+constexpr int KW = 4;                        // waves per workgroup (K quarters)
+constexpr int KSTEPS = DEC_MAXK / 64 / KW;   // K steps per wave at most (12)
 
 template <bool GATE_UP>
-static hipError_t dec_launch(int rb, int max_tiles, int K, int N, hipStream_t s,
+__global__ __launch_bounds__(64 * KW) void dec_ksplit_kernel(
+    const uint16_t* __restrict__ src, const uint8_t* __restrict__ codes,
+    const uint8_t* __restrict__ scales, const uint16_t* __restrict__ bias,
+    const float* __restrict__ topk_w, const int32_t* __restrict__ sorted_rows,
+    const Tile* __restrict__ tiles, const int32_t* __restrict__ num_tiles, int K, int N, int k,
+    int DG, float alpha, float limit, uint16_t* __restrict__ h_out, uint16_t* __restrict__ a_out,
+    float* __restrict__ y_w) {
+  // LDS: scale panel [32][K / 32], then the activation group [DG][K + DEC_XPAD]
+  // bf16, which the partial sums [KW][16][64] fp32 reuse after the MFMAs
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int nrb = N / 32;
+  const int tile = blockIdx.x / nrb, rb = blockIdx.x % nrb;
+  if (tile >= *num_tiles) return;
+  const Tile tl = tiles[tile];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hlf = lane >> 5;
+  const int e = tl.expert;
+  const int xrow = K + DEC_XPAD;
+  uint8_t* panel = lds;
+  uint16_t* xs = reinterpret_cast<uint16_t*>(lds + K);   // the panel is 32 x K/32 = K bytes
+  float* red = reinterpret_cast<float*>(xs);
+
+  const int nsteps = K / 64;
+  const int per = (nsteps + KW - 1) / KW;
+  const int c0 = min(wave * per, nsteps), cnt = min(per, nsteps - c0);
+  const int n = rb * 32 + l32;
+  const uint8_t* wrow = codes + ((int64_t)e * N + n) * (K / 2) + hlf * 16;
+  u32x4 cv[KSTEPS];
+#pragma unroll
+  for (int i = 0; i < KSTEPS; ++i) {
+    const int c = c0 + min(i, cnt - 1);               // clamped: never past the row
+    cv[i] = *reinterpret_cast<const u32x4*>(wrow + c * 32);
+  }
+  {
+    const u32x4* ps = reinterpret_cast<const u32x4*>(scales + ((int64_t)e * N + rb * 32) * (K / 32));
+    for (int q = tid; q < K / 16; q += 64 * KW) reinterpret_cast<u32x4*>(panel)[q] = ps[q];
+  }
+  const uint8_t* srow = panel + l32 * (K / 32) + hlf;
+  const int npieces = K / 8;
+
+  for (int g0 = 0; g0 < tl.rows; g0 += DG) {
+    const int ng = min(DG, tl.rows - g0);
+    for (int q = tid; q < ng * npieces; q += 64 * KW) {
+      const int p = q / npieces, col = (q % npieces) * 8;
+      const int rt = tl.row0 + g0 + p;
+      const int64_t sr = GATE_UP ? (int64_t)(sorted_rows[rt] / k) : (int64_t)rt;
+      *reinterpret_cast<u32x4*>(xs + p * xrow + col) =
+          *reinterpret_cast<const u32x4*>(src + sr * K + col);
+    }
+    __syncthreads();
+    f32x16 acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+    const uint16_t* xb = xs + min(l32 % DG, ng - 1) * xrow + 32 * hlf;
+#pragma unroll
+    for (int i = 0; i < KSTEPS; ++i) {
+      if (i < cnt) {
+        const int c = c0 + i;
+        const float sc = scale_operand(srow[2 * c]);
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+          const bf16x8 a = as_bf16x8(dequant8_bf16(cv[i][s4], sc));
+          const bf16x8 b = *reinterpret_cast<const bf16x8*>(xb + 64 * c + 8 * s4);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+        }
+      }
+    }
+    __syncthreads();   // every wave is done reading xs
+#pragma unroll
+    for (int r = 0; r < 16; ++r) red[(wave * 16 + r) * 64 + lane] = acc[r];
+    __syncthreads();
+    float v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float sum = 0.0f;
+#pragma unroll
+      for (int w = 0; w < KW; ++w) sum += red[(w * 16 + 4 * wave + i) * 64 + lane];
+      v[i] = sum;
+    }
+    // lane: column p = l32 of the group, weight rows nb + i
+    const int p = g0 + l32;
+    if (l32 < DG && p < tl.rows) {
+      const int nb = rb * 32 + 8 * wave + 4 * hlf;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] += bias ? bf16_to_f32(bias[(int64_t)e * N + nb + i]) : 0.0f;
+      const int64_t rho = tl.row0 + p;
+      if (GATE_UP) {
+        const int I = N / 2;
+        if (h_out) {
+          u32x2 hv = {saved_preact_bf16(v[0], limit, false) | (saved_preact_bf16(v[1], limit, true) << 16),
+                      saved_preact_bf16(v[2], limit, false) | (saved_preact_bf16(v[3], limit, true) << 16)};
+          *reinterpret_cast<u32x2*>(h_out + rho * N + nb) = hv;
+        }
+        *reinterpret_cast<uint32_t*>(a_out + rho * I + nb / 2) =
+            pack_bf16x2(swiglu(v[0], v[1], alpha, limit), swiglu(v[2], v[3], alpha, limit));
+      } else {
+        const int64_t f = sorted_rows[rho];
+        const float wf = topk_w[f];
+        f32x4 y;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) y[i] = wf * v[i];
+        *reinterpret_cast<f32x4*>(y_w + f * N + nb) = y;
+      }
+    }
+    __syncthreads();   // LDS is restaged for the next group
+  }
+}
+
+// Launch shape from the routed-row count: few rows -> 2 waves (64 weight
+// rows) per workgroup so the grid covers the chip; more rows -> up to 8
+// waves (256 weight rows) sharing one staging of the activation group (at
+// most R rows, 8 or 16 at a time).  Splitting K over waves measured slower.
+template <bool GATE_UP>
+static hipError_t dec_launch_stream(int64_t R, int max_tiles, int K, int N, hipStream_t s,
                              const uint16_t* src, const uint8_t* codes, const uint8_t* scales,
                              const uint16_t* bias, const float* topk_w,
                              const int32_t* sorted_rows, const Tile* tiles,
                              const int32_t* num_tiles, int k, float alpha, float limit,
                              uint16_t* h_out, uint16_t* a_out, float* y_w) {
-  const dim3 grid(max_tiles * (N / (32 * rb))), block(64 * DW);
-  const size_t lds = dec_lds_bytes(K, rb);
-#define DEC_ARGS src, codes, scales, bias, topk_w, sorted_rows, tiles, num_tiles, K, N, k, alpha, \
-                 limit, h_out, a_out, y_w
-  switch (rb) {
-    case 1: hipLaunchKernelGGL((dec_kernel<GATE_UP, 1>), grid, block, lds, s, DEC_ARGS); break;
-    case 2: hipLaunchKernelGGL((dec_kernel<GATE_UP, 2>), grid, block, lds, s, DEC_ARGS); break;
-    default: hipLaunchKernelGGL((dec_kernel<GATE_UP, 4>), grid, block, lds, s, DEC_ARGS); break;
+  if (K % 64 || K > DEC_MAXK || N % 32) return hipErrorInvalidValue;
+  const int wpb = R <= 64 ? 4 : 8;
+  const int dg = R <= 64 ? (int)(R < 8 ? R : 8) : 16;   // an expert owns at most R rows
+  const int nblk = (N + 32 * wpb - 1) / (32 * wpb);
+  const size_t lds = (size_t)32 * wpb * (K / 32) + (size_t)dg * (K + DEC_XPAD) * 2;
+  // dynamic LDS above 64 KB (16 staged rows) must be allowed explicitly
+  static bool lds_attr_set = false;
+  if (!lds_attr_set) {
+    const int most = 16 * (DEC_MAXK + DEC_XPAD) * 2 + 256 * (DEC_MAXK / 32);
+    const hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&dec_kernel<GATE_UP>),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, most);
+    if (err != hipSuccess) return err;
+    lds_attr_set = true;
   }
+  const dim3 grid(max_tiles * nblk), block(64 * wpb);
+#define DEC_ARGS src, codes, scales, bias, topk_w, sorted_rows, tiles, num_tiles, K, N, k, dg, \
+                 alpha, limit, h_out, a_out, y_w
+  hipLaunchKernelGGL((dec_kernel<GATE_UP>), grid, block, lds, s, DEC_ARGS);
 #undef DEC_ARGS
   return hipGetLastError();
+}
+
+template <bool GATE_UP>
+static hipError_t dec_launch(int64_t R, int max_tiles, int K, int N, hipStream_t s,
+                             const uint16_t* src, const uint8_t* codes, const uint8_t* scales,
+                             const uint16_t* bias, const float* topk_w,
+                             const int32_t* sorted_rows, const Tile* tiles,
+                             const int32_t* num_tiles, int k, float alpha, float limit,
+                             uint16_t* h_out, uint16_t* a_out, float* y_w) {
+  if (K % 64 || K > DEC_MAXK || N % 32) return hipErrorInvalidValue;
+  if (R <= 16) {
+    const int dg = (int)(R < 8 ? R : 8);
+    const size_t xb = (size_t)dg * (K + DEC_XPAD) * 2, rb = (size_t)KW * 16 * 64 * 4;
+    hipLaunchKernelGGL(dec_ksplit_kernel<GATE_UP>, dim3(max_tiles * (N / 32)), dim3(64 * KW),
+                       (size_t)K + (xb > rb ? xb : rb), s, src, codes, scales, bias, topk_w,
+                       sorted_rows, tiles, num_tiles, K, N, k, dg, alpha, limit, h_out, a_out,
+                       y_w);
+    return hipGetLastError();
+  }
+  return dec_launch_stream<GATE_UP>(R, max_tiles, K, N, s, src, codes, scales, bias, topk_w,
+                                    sorted_rows, tiles, num_tiles, k, alpha, limit, h_out, a_out,
+                                    y_w);
 }
 
 hipError_t launch_dec_gate_up(const uint16_t* x, const uint8_t* codes, const uint8_t* scales,
@@ -192,22 +336,16 @@ hipError_t launch_dec_gate_up(const uint16_t* x, const uint8_t* codes, const uin
                               const int32_t* num_tiles, int max_tiles, int64_t R, int H, int I, int k,
                               float alpha, float limit, uint16_t* h_out, uint16_t* a_out,
                               hipStream_t s) {
-  if (H % 64 || H > DEC_MAXK || I % 32) return hipErrorInvalidValue;
-  const int N = 2 * I;
-  return dec_launch<true>(dec_rb(R, N), max_tiles, H, N, s, x, codes, scales,
-                          bias, nullptr, sorted_rows, tiles, num_tiles, k, alpha, limit, h_out,
-                          a_out, nullptr);
+  return dec_launch<true>(R, max_tiles, H, 2 * I, s, x, codes, scales, bias, nullptr, sorted_rows,
+                          tiles, num_tiles, k, alpha, limit, h_out, a_out, nullptr);
 }
 
 hipError_t launch_dec_down(const uint16_t* a, const uint8_t* codes, const uint8_t* scales,
                            const uint16_t* bias, const float* topk_w, const int32_t* sorted_rows,
                            const Tile* tiles, const int32_t* num_tiles, int max_tiles, int64_t R,
-                           int H, int I,
-                           float* y_w, hipStream_t s) {
-  if (I % 64 || I > DEC_MAXK || H % 32) return hipErrorInvalidValue;
-  return dec_launch<false>(dec_rb(R, H), max_tiles, I, H, s, a, codes, scales,
-                           bias, topk_w, sorted_rows, tiles, num_tiles, 1, 0.0f, 0.0f, nullptr,
-                           nullptr, y_w);
+                           int H, int I, float* y_w, hipStream_t s) {
+  return dec_launch<false>(R, max_tiles, I, H, s, a, codes, scales, bias, topk_w, sorted_rows,
+                           tiles, num_tiles, 1, 0.0f, 0.0f, nullptr, nullptr, y_w);
 }
 
 }  // namespace mxmoe
