@@ -22,12 +22,13 @@
 // registers with byte permutes, and writes 8 contraction-ordered 16-byte
 // rows into LDS; the MFMA A-operand is then one 16-byte LDS read.
 //
-// Tiling.  A workgroup computes 512 output columns x 128 routed rows with 4
-// waves, one per SIMD; wave w owns output columns 128w..128w+127 (four
-// 32-column MFMA blocks) for all 128 rows (four 32-row blocks): 16
-// accumulators of 32x32 fp32, all 256 accumulation registers.  Per K step
-// of 64 a wave reads 4 A- and 4 B-fragments per 16 MFMAs from LDS, which
-// keeps LDS traffic (reads plus the staging writes) under the MFMA time.
+// Tiling.  A workgroup computes 512 output columns x 128 routed rows with 8
+// waves, two per SIMD; wave w owns output columns 64w..64w+63 (two
+// 32-column MFMA blocks) for all 128 rows (four 32-row blocks): 8
+// accumulators of 32x32 fp32.  Per K step of 64 a wave reads 2 A- and 4
+// B-fragments per 8 MFMAs from LDS; the second wave per SIMD hides the
+// other's LDS and load waits (measured faster than one wave with four
+// column blocks, which reads less LDS per MFMA).
 //
 // LDS: the transposed weights [512][64] bf16 and the activations [128][64]
 // bf16, both double-buffered, exactly 160 KB, no padding.  Row r's eight
@@ -41,17 +42,17 @@
 
 namespace mxmoe {
 
-constexpr int BW = 4;                      // waves per workgroup, one per SIMD
+constexpr int BW = 8;                      // waves per workgroup, two per SIMD
 constexpr int BTHR = 64 * BW;
-constexpr int BRB = 4;                     // 32-column output blocks per wave
+constexpr int BRB = 2;                     // 32-column output blocks per wave
 constexpr int BNT = 32 * BRB * BW;         // output columns per workgroup (512)
 constexpr int BKC = 64;                    // contraction per step
-constexpr int BBLK = (BKC / 8) * (BNT / 8) / BTHR;   // 8x8 weight blocks per thread per step (2)
-constexpr int BPPT = MT * 8 / BTHR;        // 16-byte activation pieces per thread per step (4)
+constexpr int BBLK = (BKC / 8) * (BNT / 8) / BTHR;   // 8x8 weight blocks per thread per step (1)
+constexpr int BPPT = MT * 8 / BTHR;        // 16-byte activation pieces per thread per step (2)
 constexpr int WS_BYTES = BNT * BKC * 2;    // one weight buffer (64 KB)
 constexpr int XS_BYTES = MT * BKC * 2;     // one activation buffer (16 KB)
 constexpr int BLDS = 2 * WS_BYTES + 2 * XS_BYTES;    // 160 KB
-static_assert(BBLK == 2 && BPPT == 4, "thread work assumed below");
+static_assert(BNT == 512, "thread work assumed below");
 
 __device__ __forceinline__ int ws_off(int row, int blk) {
   return row * 128 + ((blk ^ ((row ^ (row >> 3)) & 7)) << 4);
@@ -79,21 +80,34 @@ __device__ __forceinline__ void load_block(RawBlock& rb, const uint8_t* __restri
 // Decode the 8x8 block (contraction rows 8cb.., output columns 8ob..) and
 // store it transposed: weight row 8ob + j gets the 8 contraction-ordered
 // bf16 of output column j, in logical block cb.
-__device__ __forceinline__ void store_block_t(const RawBlock& rb, uint8_t* ws, int ob, int cb) {
-  u32x4 R[8];
+// Column pair (2J, 2J+1) of the block's 8 rows, decoded with each row's
+// scale, split into two contraction-ordered weight rows with byte permutes.
+template <int J>
+__device__ __forceinline__ void store_block_col(const RawBlock& rb, uint8_t* ws, int ob, int cb) {
+  uint32_t d[8];
 #pragma unroll
-  for (int r = 0; r < 8; ++r) R[r] = dequant8_bf16(rb.code[r], scale_operand(rb.scale[r]));
+  for (int r = 0; r < 8; ++r)
+    d[r] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(
+                                            rb.code[r], scale_operand(rb.scale[r]), J));
+  u32x4 lo, hi;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    u32x4 lo, hi;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      lo[m] = __builtin_amdgcn_perm(R[2 * m + 1][j], R[2 * m][j], 0x05040100u);
-      hi[m] = __builtin_amdgcn_perm(R[2 * m + 1][j], R[2 * m][j], 0x07060302u);
-    }
-    *reinterpret_cast<u32x4*>(ws + ws_off(8 * ob + 2 * j, cb)) = lo;
-    *reinterpret_cast<u32x4*>(ws + ws_off(8 * ob + 2 * j + 1, cb)) = hi;
+  for (int m = 0; m < 4; ++m) {
+    lo[m] = __builtin_amdgcn_perm(d[2 * m + 1], d[2 * m], 0x05040100u);
+    hi[m] = __builtin_amdgcn_perm(d[2 * m + 1], d[2 * m], 0x07060302u);
   }
+  *reinterpret_cast<u32x4*>(ws + ws_off(8 * ob + 2 * J, cb)) = lo;
+  *reinterpret_cast<u32x4*>(ws + ws_off(8 * ob + 2 * J + 1, cb)) = hi;
+}
+
+// Decode the 8x8 block (contraction rows 8cb.., output columns 8ob..) and
+// store it transposed: weight row 8ob + j gets the 8 contraction-ordered
+// bf16 of output column j, in logical block cb.  One column pair at a time
+// keeps 8 decoded dwords live instead of 32.
+__device__ __forceinline__ void store_block_t(const RawBlock& rb, uint8_t* ws, int ob, int cb) {
+  store_block_col<0>(rb, ws, ob, cb);
+  store_block_col<1>(rb, ws, ob, cb);
+  store_block_col<2>(rb, ws, ob, cb);
+  store_block_col<3>(rb, ws, ob, cb);
 }
 
 // Per-thread state of the two-deep pipeline: registers of steps c+1 and c+2.
@@ -133,7 +147,7 @@ __device__ __forceinline__ void bwd_stage(const BwdPipe& pp, uint8_t* lds) {
 #pragma unroll
   for (int i = 0; i < BBLK; ++i) {
     const int q = tid + i * BTHR;
-    store_block_t(pp.raw[PAR][i], ws, q & 63, q >> 6);
+    store_block_t(pp.raw[PAR][i], ws, q & (BNT / 8 - 1), q / (BNT / 8));
   }
 }
 
@@ -217,7 +231,7 @@ __device__ __forceinline__ void bwd_mainloop(const uint16_t* const (&brow)[BPPT]
 #pragma unroll
   for (int i = 0; i < BBLK; ++i) {
     const int q = tid + i * BTHR;
-    const int cb = q >> 6, ob = q & 63;
+    const int cb = q / (BNT / 8), ob = q & (BNT / 8 - 1);
     const int ocol = (o0 + 8 * ob < O) ? o0 + 8 * ob : 0;
     g.bcode[i] = wcode + (int64_t)(8 * cb) * g.crow + ocol / 2;
     g.bscale[i] = wscale + (int64_t)(8 * cb) * g.srow + ocol / 32;

@@ -10,17 +10,18 @@
 //          the combine can sum a token's k slots in a fixed order.
 //
 // Tiling.  A workgroup computes MT = 128 routed rows of one expert against
-// NT = 512 weight rows with 4 waves, one per SIMD; wave w owns weight rows
-// 128w..128w+127 (four 32-row MFMA blocks) for all 128 routed rows (four
-// 32-column blocks): 16 accumulators of 32x32 fp32 in the accumulation
-// registers, which a single wave per SIMD may use in full.  Each decoded
-// weight fragment and each activation fragment read from LDS feeds four
-// MFMAs.  The product is computed transposed, D[n][p] = W[n][:] . X[p][:],
+// NT = 512 weight rows with 8 waves, two per SIMD; wave w owns weight rows
+// 64w..64w+63 (two 32-row MFMA blocks) for all 128 routed rows (four
+// 32-column blocks): 8 accumulators of 32x32 fp32 (128 accumulation
+// registers).  Each decoded weight fragment feeds four MFMAs and each
+// activation fragment read from LDS two; the second wave per SIMD hides
+// the other's load and LDS waits (measured faster than one wave with four
+// weight blocks).  The product is computed transposed, D[n][p] = W[n][:] . X[p][:],
 // so the weights are the MFMA A-operand: a lane reads its weight rows
 // straight from global memory and decodes the codes in registers with the
 // scaled fp4 -> bf16 conversion; no weight passes through LDS and no weight
 // is decoded twice.  The routed activation rows are the B-operand, shared
-// by the four waves through LDS.  The 512 x (K/32) UE8M0 scale panel of the
+// by the eight waves through LDS.  The 512 x (K/32) UE8M0 scale panel of the
 // workgroup's weight rows is one contiguous span of memory; it is copied
 // into LDS once.
 //
@@ -51,8 +52,8 @@
 
 namespace mxmoe {
 
-constexpr int FWN = 4;                 // waves per workgroup, one per SIMD
-constexpr int FRB = 4;                 // 32-row weight blocks per wave
+constexpr int FWN = 8;                 // waves per workgroup, two per SIMD
+constexpr int FRB = 2;                 // 32-row weight blocks per wave
 constexpr int FNTHR = 64 * FWN;
 constexpr int FNT = 32 * FRB * FWN;    // weight rows per workgroup (512)
 constexpr int LDS_BYTES = 160 * 1024;  // gfx950 LDS per workgroup
