@@ -116,6 +116,33 @@ __device__ __forceinline__ void barrier_only() {
   asm volatile("" ::: "memory");
 }
 
+// Epilogue staging.  With the weights as the MFMA A-operand, the 32x32
+// accumulator of a block gives lane l the output row l % 32 and, for a
+// wave's two blocks rb and q, m = 0..3, the columns 32 rb + 8 q + 4 (l/32)
+// + m: 16-byte column chunk c4 = 8 rb + 2 q + l/32 of a 64-column strip.
+// Stores straight from that layout write 8-16 bytes into each of 32 rows
+// per instruction; whole-row stores measured faster (by 2-7% of the GEMM
+// time).  So each wave passes its strip through a private LDS region, 32
+// rows at a time, and writes back row-contiguous 16-byte pieces.  Rows of
+// RB bytes are split into 16-byte chunks; chunk c of row r sits at slot
+// c ^ (r mod (RB/16)), so both access patterns spread over the banks.
+// The row stores are non-temporal: the outputs are consumed by a later
+// kernel, and streaming them past the caches measured slightly faster than
+// letting them displace the weights and activations still being read.
+template <int RB>
+__device__ __forceinline__ int stg_off(int r, int c) {
+  return r * RB + ((c ^ (r & (RB / 16 - 1))) << 4);
+}
+
+// Orders this wave's LDS writes before its later LDS reads of other lanes'
+// data (and those reads before the next writes): a compiler barrier for
+// memory and a wait for the wave's outstanding LDS operations.
+__device__ __forceinline__ void wave_lds_sync() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+  asm volatile("" ::: "memory");
+}
+
 // One tile of routed rows of one expert for the grouped GEMMs.
 struct Tile {
   int32_t expert;

@@ -306,23 +306,44 @@ __global__ __launch_bounds__(BTHR) void bwd_down_kernel(
     }
   }
 
-  float* red = reinterpret_cast<float*>(lds);   // [BW][MT], after the main loop's last barrier
+  // Epilogue through LDS (the main loop ended with a barrier).  Per 32-row
+  // block a wave stages its rows of a (64 bf16) and h (128 bf16) with
+  // row-contiguous loads, reads them back in the accumulator layout, writes
+  // dh over h in place and stores dh rows whole.
   const int N2 = 2 * I;
+  const int ow = o0 + wave * 32 * BRB;        // this wave's first output column
+  const bool active = ow < I;                 // I % 64 == 0: a wave's 64 columns are all in or out
+  uint8_t* ast = lds + wave * 12288;          // a strip: 32 rows x 64 bf16 (128-byte rows)
+  uint8_t* hst = ast + 4096;                  // h / dh strip: 32 rows x 128 bf16 (256-byte rows)
+  float* red = reinterpret_cast<float*>(lds + BW * 12288);   // [BW][MT]
 #pragma unroll
   for (int tb = 0; tb < 4; ++tb) {
-    const int rt = tb * 32 + l32;
     float dwp = 0.0f;
-    if (rt < tl.rows) {
-      const int64_t p = tl.row0 + rt;
-      const float wf = topk_w[sorted_rows[p]];
+    if (active && tb * 32 < tl.rows) {
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const int r = it * 8 + (lane >> 3), c = lane & 7;
+        const int64_t p = tl.row0 + min(tb * 32 + r, tl.rows - 1);
+        *reinterpret_cast<u32x4*>(ast + stg_off<128>(r, c)) =
+            *reinterpret_cast<const u32x4*>(asv + p * I + ow + 8 * c);
+      }
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        const int r = it * 4 + (lane >> 4), c = lane & 15;
+        const int64_t p = tl.row0 + min(tb * 32 + r, tl.rows - 1);
+        *reinterpret_cast<u32x4*>(hst + stg_off<256>(r, c)) =
+            *reinterpret_cast<const u32x4*>(hsv + p * N2 + 2 * ow + 8 * c);
+      }
+      const float wf = topk_w[sorted_rows[tl.row0 + min(tb * 32 + l32, tl.rows - 1)]];
+      wave_lds_sync();
 #pragma unroll
       for (int rb = 0; rb < BRB; ++rb) {
-        if (o0 + wave * 32 * BRB + rb * 32 >= I) continue;   // column block past I
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int i4 = o0 + wave * 32 * BRB + rb * 32 + 8 * q + 4 * hlf;
-          const u32x2 av = *reinterpret_cast<const u32x2*>(asv + p * I + i4);
-          const u32x4 hv = *reinterpret_cast<const u32x4*>(hsv + p * N2 + 2 * i4);
+          const int c4 = 8 * rb + 2 * q + hlf;    // columns 4 c4 .. 4 c4 + 3 of the strip
+          const u32x2 av = *reinterpret_cast<const u32x2*>(ast + stg_off<128>(l32, c4 >> 1) + 8 * (c4 & 1));
+          uint8_t* hp = hst + stg_off<256>(l32, c4);
+          const u32x4 hv = *reinterpret_cast<const u32x4*>(hp);
           u32x4 out;
 #pragma unroll
           for (int m = 0; m < 4; ++m) {
@@ -337,12 +358,22 @@ __global__ __launch_bounds__(BTHR) void bwd_down_kernel(
             swiglu_grad(g, u, wf * du_, alpha, limit, &dg, &dup);
             out[m] = pack_bf16x2(dg, dup);
           }
-          *reinterpret_cast<u32x4*>(dh + p * N2 + 2 * i4) = out;
+          *reinterpret_cast<u32x4*>(hp) = out;
         }
       }
+      wave_lds_sync();
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        const int r = it * 4 + (lane >> 4), c = lane & 15;
+        const int rt = tb * 32 + r;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(hst + stg_off<256>(r, c));
+        if (rt < tl.rows) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dh + (int64_t)(tl.row0 + rt) * N2 + 2 * ow + 8 * c));
+      }
+      wave_lds_sync();
+      if (tb * 32 + l32 >= tl.rows) dwp = 0.0f;
     }
     dwp += __shfl_xor(dwp, 32);
-    if (hlf == 0) red[wave * MT + rt] = dwp;
+    if (hlf == 0) red[wave * MT + tb * 32 + l32] = dwp;
   }
   __syncthreads();
   if (tid < tl.rows) {
@@ -383,23 +414,33 @@ __global__ __launch_bounds__(BTHR) void bwd_gate_up_kernel(
   f32x16 acc[BRB][4];
   bwd_mainloop(brow, wcode, wscale, N2, H, o0, (tl.rows + 31) / 32, lds, acc);
 
+  // Epilogue through LDS (the main loop ended with a barrier).
+  const int ow = o0 + wave * 32 * BRB;
+  if (ow >= H) return;                        // H % 64 == 0: a wave's columns are all in or out
+  uint8_t* yst = lds + wave * 8192;           // 32 rows x 64 fp32 (256-byte rows)
 #pragma unroll
   for (int tb = 0; tb < 4; ++tb) {
-    const int rt = tb * 32 + l32;
-    if (rt >= tl.rows) continue;
-    const int64_t f = sorted_rows[tl.row0 + rt];
+    if (tb * 32 >= tl.rows) break;
+    const int32_t f = sorted_rows[tl.row0 + min(tb * 32 + l32, tl.rows - 1)];
 #pragma unroll
-    for (int rb = 0; rb < BRB; ++rb) {
-      if (o0 + wave * 32 * BRB + rb * 32 >= H) continue;   // column block past H
+    for (int rb = 0; rb < BRB; ++rb)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int h4 = o0 + wave * 32 * BRB + rb * 32 + 8 * q + 4 * hlf;
         f32x4 v;
 #pragma unroll
         for (int m = 0; m < 4; ++m) v[m] = acc[rb][tb][4 * q + m];
-        *reinterpret_cast<f32x4*>(dxr + f * H + h4) = v;
+        *reinterpret_cast<f32x4*>(yst + stg_off<256>(l32, 8 * rb + 2 * q + hlf)) = v;
       }
+    wave_lds_sync();
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int r = it * 4 + (lane >> 4), c = lane & 15;
+      const int rt = tb * 32 + r;
+      const int64_t fr = __shfl(f, r);
+      const f32x4 v = *reinterpret_cast<const f32x4*>(yst + stg_off<256>(r, c));
+      if (rt < tl.rows) __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(dxr + fr * H + ow + 4 * c));
     }
+    wave_lds_sync();
   }
 }
 

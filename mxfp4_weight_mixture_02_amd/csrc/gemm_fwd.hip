@@ -254,37 +254,61 @@ __global__ __launch_bounds__(FNTHR) void gate_up_kernel(
   fwd_body(xrow, codes + (int64_t)e * N * (H / 2), scales + (int64_t)e * N * (H / 32), H, n0,
            nrows, (wave * 32 * FRB < nrows ? wave * 32 * FRB : 0) + l32, (tl.rows + 31) / 32, lds,
            acc);
+  // Epilogue through LDS: every wave's loads have landed (fwd_loop drained
+  // them) and every wave is past its last stage read.
+  barrier_only();
+  const int wcol = wave * 32 * FRB;           // this wave's first weight row in the tile
+  if (n0 + wcol >= N) return;                 // N % 64 == 0: a wave's 64 rows are all in or all out
+  uint8_t* hst = lds + wave * 6144;           // h strip: 32 rows x 64 bf16 (128-byte rows)
+  uint8_t* ast = hst + 4096;                  // a strip: 32 rows x 32 bf16 (64-byte rows)
+  float bv[FRB][4][4];
 #pragma unroll
-  for (int rb = 0; rb < FRB; ++rb) {
-    if (n0 + wave * 32 * FRB + rb * 32 >= N) continue;   // row block past the last weight row
-    const int nb = n0 + wave * 32 * FRB + rb * 32 + 4 * hlf;  // + 8q + (r % 4)
-    float bv[4][4];
+  for (int rb = 0; rb < FRB; ++rb)
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        bv[q][i] = bias ? bf16_to_f32(bias[(int64_t)e * N + nb + 8 * q + i]) : 0.0f;
+        bv[rb][q][i] = bias ? bf16_to_f32(bias[(int64_t)e * N + n0 + wcol + rb * 32 + 8 * q + 4 * hlf + i]) : 0.0f;
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-      const int rt = tb * 32 + l32;
-      if (rt >= tl.rows) continue;
-      const int64_t p = tl.row0 + rt;
+  for (int tb = 0; tb < 4; ++tb) {
+    if (tb * 32 >= tl.rows) break;
+#pragma unroll
+    for (int rb = 0; rb < FRB; ++rb)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const float g0 = acc[rb][tb][4 * q + 0] + bv[q][0];
-        const float u0 = acc[rb][tb][4 * q + 1] + bv[q][1];
-        const float g1 = acc[rb][tb][4 * q + 2] + bv[q][2];
-        const float u1 = acc[rb][tb][4 * q + 3] + bv[q][3];
-        const int n = nb + 8 * q;
+        const float g0 = acc[rb][tb][4 * q + 0] + bv[rb][q][0];
+        const float u0 = acc[rb][tb][4 * q + 1] + bv[rb][q][1];
+        const float g1 = acc[rb][tb][4 * q + 2] + bv[rb][q][2];
+        const float u1 = acc[rb][tb][4 * q + 3] + bv[rb][q][3];
         if (h_out) {
           u32x2 hv = {saved_preact_bf16(g0, limit, false) | (saved_preact_bf16(u0, limit, true) << 16),
                       saved_preact_bf16(g1, limit, false) | (saved_preact_bf16(u1, limit, true) << 16)};
-          *reinterpret_cast<u32x2*>(h_out + p * N + n) = hv;
+          *reinterpret_cast<u32x2*>(hst + stg_off<128>(l32, 4 * rb + q) + 8 * hlf) = hv;
         }
-        *reinterpret_cast<uint32_t*>(a_out + p * I + n / 2) =
+        // a columns 16 rb + 4 q + 2 hlf, +1
+        *reinterpret_cast<uint32_t*>(ast + stg_off<64>(l32, 2 * rb + (q >> 1)) + 8 * (q & 1) + 4 * hlf) =
             pack_bf16x2(swiglu(g0, u0, alpha, limit), swiglu(g1, u1, alpha, limit));
       }
+    wave_lds_sync();
+    if (h_out) {
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const int r = it * 8 + (lane >> 3), c = lane & 7;
+        const int rt = tb * 32 + r;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(hst + stg_off<128>(r, c));
+        if (rt < tl.rows)
+          __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(h_out + (int64_t)(tl.row0 + rt) * N + n0 + wcol + 8 * c));
+      }
     }
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int r = it * 16 + (lane >> 2), c = lane & 3;
+      const int rt = tb * 32 + r;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(ast + stg_off<64>(r, c));
+      if (rt < tl.rows)
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(a_out + (int64_t)(tl.row0 + rt) * I + (n0 + wcol) / 2 + 8 * c));
+    }
+    wave_lds_sync();
   }
 }
 
@@ -340,30 +364,42 @@ __global__ __launch_bounds__(FNTHR) void down_kernel(
       }
     }
   }
+  barrier_only();   // as in gate_up: LDS is free for the epilogue
+  const int wcol = wave * 32 * FRB;
+  if (n0 + wcol >= N) return;
+  uint8_t* yst = lds + wave * 8192;           // y strip: 32 rows x 64 fp32 (256-byte rows)
+  float bv[FRB][4][4];
 #pragma unroll
-  for (int rb = 0; rb < FRB; ++rb) {
-    if (n0 + wave * 32 * FRB + rb * 32 >= N) continue;   // row block past the last weight row
-    const int nb = n0 + wave * 32 * FRB + rb * 32 + 4 * hlf;
-    float bv[4][4];
+  for (int rb = 0; rb < FRB; ++rb)
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        bv[q][i] = bias ? bf16_to_f32(bias[(int64_t)e * N + nb + 8 * q + i]) : 0.0f;
+        bv[rb][q][i] = bias ? bf16_to_f32(bias[(int64_t)e * N + n0 + wcol + rb * 32 + 8 * q + 4 * hlf + i]) : 0.0f;
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-      const int rt = tb * 32 + l32;
-      if (rt >= tl.rows) continue;
-      const int64_t f = sorted_rows[tl.row0 + rt];
-      const float wf = topk_w[f];
+  for (int tb = 0; tb < 4; ++tb) {
+    if (tb * 32 >= tl.rows) break;
+    const int32_t f = sorted_rows[tl.row0 + min(tb * 32 + l32, tl.rows - 1)];
+    const float wf = topk_w[f];
+#pragma unroll
+    for (int rb = 0; rb < FRB; ++rb)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         f32x4 y;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) y[i] = wf * (acc[rb][tb][4 * q + i] + bv[q][i]);
-        *reinterpret_cast<f32x4*>(y_w + f * N + nb + 8 * q) = y;
+        for (int i = 0; i < 4; ++i) y[i] = wf * (acc[rb][tb][4 * q + i] + bv[rb][q][i]);
+        *reinterpret_cast<f32x4*>(yst + stg_off<256>(l32, 8 * rb + 2 * q + hlf)) = y;
       }
+    wave_lds_sync();
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int r = it * 4 + (lane >> 4), c = lane & 15;
+      const int rt = tb * 32 + r;
+      const int64_t fr = __shfl(f, r);
+      const f32x4 v = *reinterpret_cast<const f32x4*>(yst + stg_off<256>(r, c));
+      if (rt < tl.rows) __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(y_w + fr * N + n0 + wcol + 4 * c));
     }
+    wave_lds_sync();
   }
 }
 
