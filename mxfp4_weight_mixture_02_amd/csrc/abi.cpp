@@ -46,7 +46,7 @@ struct Layout {
          a = SIZE_MAX, blk_hist = SIZE_MAX, tiles = SIZE_MAX, num_tiles = SIZE_MAX,
          y_w = SIZE_MAX, dh = SIZE_MAX, dw_part = SIZE_MAX, dxr = SIZE_MAX,
          lora_v = SIZE_MAX, lora_At = SIZE_MAX, lora_Bt = SIZE_MAX, lora_dvu = SIZE_MAX,
-         logits = SIZE_MAX;
+         logits = SIZE_MAX, logit_part = SIZE_MAX;
   size_t total = 0;
   size_t put(size_t bytes) {
     size_t at = total;
@@ -94,6 +94,8 @@ Layout layout(const mxfp4_moe_dims& d, int mode) {
       if (d.lora_rank) L.lora_v = L.put(R * (size_t)d.lora_rank * 4);
     }
     L.logits = L.put((size_t)d.T * d.E * 4);
+    if (mxmoe::plan_fits(d.T, d.E, d.k))
+      L.logit_part = L.put((size_t)mxmoe::plan_hs_parts((int)d.T, d.E, (int)d.H) * d.T * d.E * 8);
     L.blk_hist = L.put((size_t)mxmoe::router_blocks(d.T) * d.E * 4);
     L.tiles = L.put((size_t)maxt * sizeof(mxmoe::Tile));
     L.num_tiles = L.put(4);
@@ -297,13 +299,16 @@ int mxfp4_moe_forward(const mxfp4_moe_dims* dims, const mxfp4_moe_weights* w, co
   const int maxt = mxmoe::max_tiles(R, E);
 
   float* logits = at<float>(workspace, L.logits);
-  LAUNCH(mxmoe::launch_logits(x, w->router_w, w->router_b, T, H, E, logits, s), "router_logits");
-  if (R <= mxmoe::PLAN_MAX_ROWS) {
-    // top-k, histogram, offsets, permutation and tiles in one workgroup
-    LAUNCH(mxmoe::launch_plan(logits, T, E, k, topk_idx, topk_w, offsets, sorted_rows, tiles,
-                              num_tiles, s),
+  if (mxmoe::plan_fits(d.T, E, k)) {
+    // partial logits over many CUs, then one workgroup for the logits,
+    // top-k, offsets, permutation and tiles
+    double* part = at<double>(workspace, L.logit_part);
+    LAUNCH(mxmoe::launch_plan_logits(x, w->router_w, T, H, E, part, s), "router_logits");
+    LAUNCH(mxmoe::launch_plan(part, w->router_b, T, H, E, k, topk_idx, topk_w, offsets,
+                              sorted_rows, tiles, num_tiles, s),
            "route_plan");
   } else {
+    LAUNCH(mxmoe::launch_logits(x, w->router_w, w->router_b, T, H, E, logits, s), "router_logits");
     LAUNCH(mxmoe::launch_topk(logits, T, E, k, topk_idx, topk_w, blk_hist, s), "router_topk");
     LAUNCH(mxmoe::launch_scan(blk_hist, mxmoe::router_blocks(T), E, offsets, s), "scan");
     LAUNCH(mxmoe::launch_scatter(topk_idx, blk_hist, T, k, E, sorted_rows, s), "scatter");

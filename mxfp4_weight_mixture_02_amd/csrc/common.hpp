@@ -143,6 +143,25 @@ __device__ __forceinline__ void wave_lds_sync() {
   asm volatile("" ::: "memory");
 }
 
+// Block-wide staging of n 16-byte pieces from global memory into LDS:
+// piece q is load(q) -> store(q, v).  A loop of "load, store" pays one
+// memory round trip per iteration, because the store waits for its load;
+// here every thread issues up to MAXP loads (indices clamped to n - 1)
+// before its first store, so a batch costs one round trip.
+template <int MAXP, class Load, class Store>
+__device__ __forceinline__ void stage_lds(int n, int tid, int nthr, Load load, Store store) {
+  for (int b = 0; b < n; b += MAXP * nthr) {
+    u32x4 v[MAXP];
+#pragma unroll
+    for (int u = 0; u < MAXP; ++u) v[u] = load(min(b + tid + u * nthr, n - 1));
+#pragma unroll
+    for (int u = 0; u < MAXP; ++u) {
+      const int q = b + tid + u * nthr;
+      if (q < n) store(q, v[u]);
+    }
+  }
+}
+
 // One tile of routed rows of one expert for the grouped GEMMs.
 struct Tile {
   int32_t expert;

@@ -92,20 +92,25 @@ __global__ __launch_bounds__(512) void dec_kernel(
     const int r0 = rbk * wpb * 32;
     const int n16 = min(32 * wpb, N - r0) * (K / 32) / 16;
     const u32x4* ps = reinterpret_cast<const u32x4*>(scales + ((int64_t)e * N + r0) * (K / 32));
-    for (int q = tid; q < n16; q += blockDim.x) reinterpret_cast<u32x4*>(panel)[q] = ps[q];
+    stage_lds<4>(n16, tid, blockDim.x, [&](int q) { return ps[q]; },
+                 [&](int q, u32x4 v) { reinterpret_cast<u32x4*>(panel)[q] = v; });
   }
   const uint8_t* srow = panel + (live ? wave * 32 + l32 : 0) * (K / 32) + hlf;
 
   for (int g0 = 0; g0 < tl.rows; g0 += DG) {
     // stage the group's activation rows (only the ones that exist)
     const int ng = min(DG, tl.rows - g0);
-    for (int q = tid; q < ng * npieces; q += blockDim.x) {
-      const int p = q / npieces, col = (q % npieces) * 8;
-      const int rt = tl.row0 + g0 + p;
-      const int64_t sr = GATE_UP ? (int64_t)(sorted_rows[rt] / k) : (int64_t)rt;
-      *reinterpret_cast<u32x4*>(xs + p * xrow + col) =
-          *reinterpret_cast<const u32x4*>(src + sr * K + col);
-    }
+    stage_lds<8>(
+        ng * npieces, tid, blockDim.x,
+        [&](int q) {
+          const int p = q / npieces, col = (q % npieces) * 8;
+          const int rt = tl.row0 + g0 + p;
+          const int64_t sr = GATE_UP ? (int64_t)(sorted_rows[rt] / k) : (int64_t)rt;
+          return *reinterpret_cast<const u32x4*>(src + sr * K + col);
+        },
+        [&](int q, u32x4 v) {
+          *reinterpret_cast<u32x4*>(xs + (q / npieces) * xrow + (q % npieces) * 8) = v;
+        });
     __syncthreads();
     f32x16 acc;
 #pragma unroll
@@ -203,20 +208,25 @@ __global__ __launch_bounds__(64 * KW) void dec_ksplit_kernel(
   }
   {
     const u32x4* ps = reinterpret_cast<const u32x4*>(scales + ((int64_t)e * N + rb * 32) * (K / 32));
-    for (int q = tid; q < K / 16; q += 64 * KW) reinterpret_cast<u32x4*>(panel)[q] = ps[q];
+    stage_lds<1>(K / 16, tid, 64 * KW, [&](int q) { return ps[q]; },
+                 [&](int q, u32x4 v) { reinterpret_cast<u32x4*>(panel)[q] = v; });
   }
   const uint8_t* srow = panel + l32 * (K / 32) + hlf;
   const int npieces = K / 8;
 
   for (int g0 = 0; g0 < tl.rows; g0 += DG) {
     const int ng = min(DG, tl.rows - g0);
-    for (int q = tid; q < ng * npieces; q += 64 * KW) {
-      const int p = q / npieces, col = (q % npieces) * 8;
-      const int rt = tl.row0 + g0 + p;
-      const int64_t sr = GATE_UP ? (int64_t)(sorted_rows[rt] / k) : (int64_t)rt;
-      *reinterpret_cast<u32x4*>(xs + p * xrow + col) =
-          *reinterpret_cast<const u32x4*>(src + sr * K + col);
-    }
+    stage_lds<8>(
+        ng * npieces, tid, 64 * KW,
+        [&](int q) {
+          const int p = q / npieces, col = (q % npieces) * 8;
+          const int rt = tl.row0 + g0 + p;
+          const int64_t sr = GATE_UP ? (int64_t)(sorted_rows[rt] / k) : (int64_t)rt;
+          return *reinterpret_cast<const u32x4*>(src + sr * K + col);
+        },
+        [&](int q, u32x4 v) {
+          *reinterpret_cast<u32x4*>(xs + (q / npieces) * xrow + (q % npieces) * 8) = v;
+        });
     __syncthreads();
     f32x16 acc;
 #pragma unroll

@@ -190,8 +190,8 @@ __device__ __forceinline__ void fwd_body(const uint16_t* const (&xrow)[XCHUNKS],
   {
     const u32x4* src = reinterpret_cast<const u32x4*>(scales_e + (int64_t)n0 * KB32);
     u32x4* dst = reinterpret_cast<u32x4*>(panel);
-    const int n16 = nrows * KB32 / 16;
-    for (int q = tid; q < n16; q += FNTHR) dst[q] = src[q];
+    stage_lds<6>(nrows * KB32 / 16, tid, FNTHR, [&](int q) { return src[q]; },
+                 [&](int q, u32x4 v) { dst[q] = v; });
   }
 #pragma unroll
   for (int rb = 0; rb < FRB; ++rb)

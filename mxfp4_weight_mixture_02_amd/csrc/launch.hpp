@@ -24,9 +24,17 @@ hipError_t launch_logits(const uint16_t* x, const float* wr, const float* br, in
                          int E, float* logits, hipStream_t s);
 hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* topk_idx, float* topk_w,
                        int32_t* blk_hist, hipStream_t s);
-hipError_t launch_plan(const float* logits, int T, int E, int k, int32_t* topk_idx, float* topk_w,
-                       int32_t* offsets, int32_t* sorted_rows, Tile* tiles, int32_t* num_tiles,
-                       hipStream_t s);
+// Planned routing (plan_fits: R = T*k <= PLAN_MAX_ROWS and T*E <= 4096):
+// partial fp64 logits over plan_hs_parts(T, E, H) ranges of h (part: that
+// many x T x E doubles), then one workgroup for the logits, top-k, offsets,
+// permutation and tiles.
+bool plan_fits(int64_t T, int E, int k);
+int plan_hs_parts(int T, int E, int H);
+hipError_t launch_plan_logits(const uint16_t* x, const float* wr, int T, int H, int E,
+                              double* part, hipStream_t s);
+hipError_t launch_plan(const double* part, const float* br, int T, int H, int E, int k,
+                       int32_t* topk_idx, float* topk_w, int32_t* offsets, int32_t* sorted_rows,
+                       Tile* tiles, int32_t* num_tiles, hipStream_t s);
 hipError_t launch_scan(int32_t* blk_hist, int nblk, int E, int32_t* offsets, hipStream_t s);
 hipError_t launch_scatter(const int32_t* topk_idx, const int32_t* blk_base, int T, int k, int E,
                           int32_t* sorted_rows, hipStream_t s);

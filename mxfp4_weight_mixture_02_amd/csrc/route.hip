@@ -97,6 +97,63 @@ __global__ __launch_bounds__(64 * LG_W) void logits_kernel(const uint16_t* __res
   }
 }
 
+// Router logits for few tokens (the planned path).  The same 16x16 fp64
+// MFMA tiles as logits_kernel, but one wave per (tile, range of h) and
+// many workgroups, so the router weights stream through many CUs at once:
+// part[hs][t][e] is range hs's fp64 partial sum, and plan_kernel adds the
+// ranges in order, adds the bias and rounds once to fp32.  Within a range,
+// chunk c - c0 goes to accumulator (c - c0) mod 4 (four independent MFMA
+// chains instead of one), and the four are added in a fixed order.
+constexpr int LP_P = 8;     // chunks in flight per wave
+__global__ __launch_bounds__(64) void logits_part_kernel(const uint16_t* __restrict__ x,
+                                                         const float* __restrict__ wr, int T,
+                                                         int H, int E, int hs_parts,
+                                                         double* __restrict__ part) {
+  const int lane = threadIdx.x;
+  const int ntt = (T + 15) / 16;
+  const int hs = blockIdx.x % hs_parts, tile = blockIdx.x / hs_parts;
+  const int tt = tile % ntt, et = tile / ntt;
+  const int nch = H / LG_CH;
+  const int c0 = hs * nch / hs_parts, c1 = (hs + 1) * nch / hs_parts;
+  const int i = lane & 15, kk = lane >> 4;
+  const int t = min(tt * 16 + i, T - 1), e = min(et * 16 + i, E - 1);
+  const uint16_t* xp = x + (int64_t)t * H + 8 * kk;
+  const float* wp = wr + (int64_t)e * H + 8 * kk;
+  f64x4 acc[4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a) acc[a] = f64x4{0.0, 0.0, 0.0, 0.0};
+  for (int cb = c0; cb < c1; cb += LP_P) {
+    u32x4 xv[LP_P];
+    f32x4 w0[LP_P], w1[LP_P];
+#pragma unroll
+    for (int q = 0; q < LP_P; ++q) lg_load(xp, wp, min(cb + q, c1 - 1), xv[q], w0[q], w1[q]);
+#pragma unroll
+    for (int q = 0; q < LP_P; ++q)
+      if (cb + q < c1) lg_mfma(xv[q], w0[q], w1[q], acc[q % 4]);
+  }
+  const f64x4 sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  const int ex = et * 16 + i;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int tok = tt * 16 + 4 * r + kk;
+    if (tok < T && ex < E) part[((int64_t)hs * T + tok) * E + ex] = sum[r];
+  }
+}
+
+// Ranges of h per 16x16 logit tile in logits_part_kernel: about 128 waves
+// in all, at most 64 ranges and at least one 32-element chunk of h per
+// range, and at most PLAN_PARTS partial sums (plan_kernel stages them all
+// in LDS).  The planned path requires T*E <= PLAN_LOGITS <= PLAN_PARTS.
+constexpr int PLAN_PARTS = 16384;
+constexpr int PLAN_LOGITS = 4096;
+int plan_hs_parts(int T, int E, int H) {
+  const int tiles = ((T + 15) / 16) * ((E + 15) / 16);
+  int hs = min(128 / tiles, 64);
+  hs = min(hs, PLAN_PARTS / (T * E));
+  hs = min(hs, H / LG_CH);
+  return max(hs, 1);
+}
+
 // Top-k and softmax of token t by one wave.  Lane l holds the logits of
 // experts l, l + 64, l + 128, l + 192.  k rounds of a wave arg-max (larger
 // logit first, ties to the lower expert) pick the slots in order; the
@@ -149,7 +206,7 @@ __device__ __forceinline__ void topk_one(const float* __restrict__ logits, int E
       if (j < k) {
         topk_idx[f0 + j] = idx[j];
         topk_w[f0 + j] = z[j] / zsum;
-        atomicAdd(&hist[idx[j]], 1);   // counts only: order does not matter
+        if (hist) atomicAdd(&hist[idx[j]], 1);   // counts only: order does not matter
         if (mask) mask[t * 8 + (idx[j] >> 5)] |= 1u << (idx[j] & 31);
         if (ex) ex[f0 + j] = idx[j];
       }
@@ -176,42 +233,168 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
   if (tid < E) blk_hist[(int64_t)blockIdx.x * E + tid] = hist[tid];
 }
 
-// Few routed rows (R = T*k <= PLAN_MAX_ROWS, so T <= 256): top-k,
-// histogram, offsets, the stable permutation and the tile list in one
-// workgroup of 1024 threads.  Row f = (t, j) of expert e goes to offsets[e]
-// + (number of tokens t' < t that chose e), which keeps ascending f within
-// an expert; the count comes from the tokens' expert bitmasks.
+// Top-k and softmax of token t by one wave, from logits in LDS, without
+// cross-lane reductions: lane l owns experts l + 64q and counts, for each,
+// the experts that beat it (a larger logit, or an equal one with a lower
+// index).  An expert with count j < k is slot j.  The selected logits go
+// through the wave's LDS slots zs[8]; lane 0 forms the softmax over them in
+// slot order (exponents relative to slot 0).  Same selection and the same
+// arithmetic as topk_one.
+// NQ = ceil(E / 64) expert slots per lane (a template parameter: the
+// count loop is VALU-bound, and slots that do not exist must cost nothing).
+template <int NQ>
+__device__ __forceinline__ void topk_rank(const float* lg, int E, int k, int t, int lane,
+                                          int32_t* __restrict__ topk_idx,
+                                          float* __restrict__ topk_w, int32_t* ex, float* zs) {
+  const float* lt = lg + (int64_t)t * E;
+  float v[NQ];
+  int rank[NQ];
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    v[q] = lt[min(lane + 64 * q, E - 1)];
+    rank[q] = 0;
+  }
+  for (int b0 = 0; b0 < E; b0 += 8) {
+    float o[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o[j] = lt[min(b0 + j, E - 1)];
+    const int nj = min(8, E - b0);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j < nj) {
+        const int e2 = b0 + j;
+#pragma unroll
+        for (int q = 0; q < NQ; ++q)
+          rank[q] += (o[j] > v[q] || (o[j] == v[q] && e2 < lane + 64 * q)) ? 1 : 0;
+      }
+    }
+  }
+  wave_lds_sync();   // the previous token's zs reads are done
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    const int e = lane + 64 * q;
+    if (e < E && rank[q] < k) {
+      const int64_t f = (int64_t)t * k + rank[q];
+      topk_idx[f] = e;
+      ex[f] = e;
+      zs[rank[q]] = v[q];
+    }
+  }
+  wave_lds_sync();
+  if (lane == 0) {
+    const float sel0 = zs[0];
+    float z[8], zsum = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j < k) {
+        z[j] = expf(zs[j] - sel0);
+        zsum += z[j];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (j < k) topk_w[(int64_t)t * k + j] = z[j] / zsum;
+  }
+}
+
+// Few routed rows (R = T*k <= PLAN_MAX_ROWS, so T <= 256): the logits from
+// logits_part_kernel's partial sums, top-k (topk_rank), expert counts, offsets, the
+// stable permutation and the tile list in one workgroup of 1024 threads
+// (16 waves), with T*E <= PLAN_LOGITS so the logits stay in LDS.  Counts
+// and ranks come
+// from wave ballots over the flat rows in ascending order, so row f = (t,
+// j) of expert e lands at offsets[e] + (number of earlier rows routed to
+// e): ascending f within an expert.
 __global__ __launch_bounds__(1024) void plan_kernel(
-    const float* __restrict__ logits, int T, int E, int k, int32_t* __restrict__ topk_idx,
-    float* __restrict__ topk_w, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_rows,
-    Tile* __restrict__ tiles, int32_t* __restrict__ num_tiles) {
-  __shared__ int32_t hist[256];
+    const double* __restrict__ part, int hs_parts, const float* __restrict__ br, int T, int E,
+    int k, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_rows, Tile* __restrict__ tiles,
+    int32_t* __restrict__ num_tiles) {
+  __shared__ float lg[PLAN_LOGITS];
+  __shared__ double pst[PLAN_PARTS];
+  __shared__ float zs[16][8];
+  __shared__ int32_t ex[PLAN_MAX_ROWS];
+  __shared__ int32_t cnt[256];
   __shared__ int32_t off[257];
   __shared__ int32_t tstart[257];
-  __shared__ uint32_t mask[PLAN_MAX_ROWS * 8];
-  __shared__ int32_t ex[PLAN_MAX_ROWS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (tid < 256) hist[tid] = 0;
-  for (int q = tid; q < T * 8; q += 1024) mask[q] = 0u;
+  const int TE = T * E, R = T * k;
+  // every partial sum into LDS (up to 16 independent loads per thread),
+  // then each logit's ranges added in order (16 LDS reads in flight)
+  const int P = hs_parts * TE;
+  {
+    double v[PLAN_PARTS / 1024];   // all loads issued before the first store
+#pragma unroll
+    for (int u = 0; u < PLAN_PARTS / 1024; ++u) v[u] = part[min(tid + u * 1024, P - 1)];
+#pragma unroll
+    for (int u = 0; u < PLAN_PARTS / 1024; ++u)
+      if (tid + u * 1024 < P) pst[tid + u * 1024] = v[u];
+  }
   __syncthreads();
-  for (int t = wave; t < T; t += 16)
-    topk_one(logits, E, k, t, lane, topk_idx, topk_w, hist, mask, ex);
-  __syncthreads();
-  if (tid == 0) {
-    int32_t run = 0, trun = 0;
-    for (int e = 0; e < E; ++e) {
-      off[e] = run;
-      tstart[e] = trun;
-      run += hist[e];
-      trun += (hist[e] + MT - 1) / MT;
+  for (int q = tid; q < TE; q += 1024) {
+    double sum = 0.0;
+    for (int h0 = 0; h0 < hs_parts; h0 += 16) {
+      double v[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) v[j] = pst[min(h0 + j, hs_parts - 1) * TE + q];
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (h0 + j < hs_parts) sum += v[j];
     }
-    off[E] = run;
-    *num_tiles = trun;
+    lg[q] = (float)(sum + (br ? (double)br[q % E] : 0.0));
+  }
+  __syncthreads();
+  if (E <= 64)
+    for (int t = wave; t < T; t += 16) topk_rank<1>(lg, E, k, t, lane, topk_idx, topk_w, ex, zs[wave]);
+  else if (E <= 128)
+    for (int t = wave; t < T; t += 16) topk_rank<2>(lg, E, k, t, lane, topk_idx, topk_w, ex, zs[wave]);
+  else
+    for (int t = wave; t < T; t += 16) topk_rank<4>(lg, E, k, t, lane, topk_idx, topk_w, ex, zs[wave]);
+  __syncthreads();
+  for (int e = wave; e < E; e += 16) {
+    int c = 0;
+    for (int f0 = 0; f0 < R; f0 += 64) {
+      const int f = f0 + lane;
+      c += __popcll(__ballot(f < R && ex[f] == e));
+    }
+    if (lane == 0) cnt[e] = c;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    // exclusive scans of the counts and of the tiles per expert; lane l
+    // owns experts 4l .. 4l+3
+    int c[4], tc[4], sc = 0, st = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = 4 * lane + q;
+      c[q] = e < E ? cnt[e] : 0;
+      tc[q] = (c[q] + MT - 1) / MT;
+      sc += c[q];
+      st += tc[q];
+    }
+    int ic = sc, it = st;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int oc = __shfl_up(ic, d), ot = __shfl_up(it, d);
+      if (lane >= d) { ic += oc; it += ot; }
+    }
+    int rc = ic - sc, rt = it - st;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = 4 * lane + q;
+      if (e < E) { off[e] = rc; tstart[e] = rt; }
+      rc += c[q];
+      rt += tc[q];
+    }
+    if (lane == 63) {
+      off[E] = ic;
+      *num_tiles = it;
+    }
   }
   __syncthreads();
   if (tid <= E) offsets[tid] = off[tid];
   if (tid < E) {
-    const int32_t n = hist[tid];
+    const int32_t n = cnt[tid];
     for (int32_t q = 0; q * MT < n; ++q) {
       Tile tl;
       tl.expert = tid;
@@ -221,14 +404,15 @@ __global__ __launch_bounds__(1024) void plan_kernel(
       tiles[tstart[tid] + q] = tl;
     }
   }
-  if (tid < T * k) {
-    const int t = tid / k;
-    const int e = ex[tid];
-    const int w = e >> 5;
-    const uint32_t bit = 1u << (e & 31);
-    int rank = 0;
-    for (int u = 0; u < t; ++u) rank += (mask[u * 8 + w] & bit) ? 1 : 0;
-    sorted_rows[off[e] + rank] = tid;
+  for (int e = wave; e < E; e += 16) {
+    int base = off[e];
+    for (int f0 = 0; f0 < R; f0 += 64) {
+      const int f = f0 + lane;
+      const bool m = f < R && ex[f] == e;
+      const unsigned long long b = __ballot(m);
+      if (m) sorted_rows[base + __popcll(b & ((1ull << lane) - 1ull))] = f;
+      base += __popcll(b);
+    }
   }
 }
 
@@ -352,12 +536,23 @@ hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* topk_i
   return hipGetLastError();
 }
 
-hipError_t launch_plan(const float* logits, int T, int E, int k, int32_t* topk_idx, float* topk_w,
-                       int32_t* offsets, int32_t* sorted_rows, Tile* tiles, int32_t* num_tiles,
-                       hipStream_t s) {
-  if ((int64_t)T * k > PLAN_MAX_ROWS) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, logits, T, E, k, topk_idx, topk_w,
-                     offsets, sorted_rows, tiles, num_tiles);
+hipError_t launch_plan_logits(const uint16_t* x, const float* wr, int T, int H, int E,
+                              double* part, hipStream_t s) {
+  if (H % LG_CH) return hipErrorInvalidValue;
+  const int hs = plan_hs_parts(T, E, H);
+  const int blocks = ((T + 15) / 16) * ((E + 15) / 16) * hs;
+  hipLaunchKernelGGL(logits_part_kernel, dim3(blocks), dim3(64), 0, s, x, wr, T, H, E, hs, part);
+  return hipGetLastError();
+}
+
+bool plan_fits(int64_t T, int E, int k) { return T * k <= PLAN_MAX_ROWS && T * E <= PLAN_LOGITS; }
+
+hipError_t launch_plan(const double* part, const float* br, int T, int H, int E, int k,
+                       int32_t* topk_idx, float* topk_w, int32_t* offsets, int32_t* sorted_rows,
+                       Tile* tiles, int32_t* num_tiles, hipStream_t s) {
+  if (!plan_fits(T, E, k)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, part, plan_hs_parts(T, E, H), br, T,
+                     E, k, topk_idx, topk_w, offsets, sorted_rows, tiles, num_tiles);
   return hipGetLastError();
 }
 
