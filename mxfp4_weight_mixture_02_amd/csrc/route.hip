@@ -9,9 +9,10 @@
 // fp32), and the permutation is a deterministic counting sort: per-
 // workgroup histograms, one scan over (expert, workgroup), then each
 // workgroup scatters its rows in ascending flat-row order.  For few routed
-// rows (decode sizes) one workgroup does top-k, histogram, scan, scatter
-// and the tile list in a single launch.  No atomics on global memory, so
-// the result is identical run to run.
+// rows (decode sizes) the logits are split over many workgroups as fp64
+// partial sums, and one workgroup then does the sums, top-k, counts, scan,
+// permutation and the tile list.  No atomics on global memory, and every
+// sum in a fixed order, so the result is identical run to run.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -35,7 +36,8 @@ int router_blocks(int64_t T) { return (int)((T + RT - 1) / RT); }
 // and dropped.
 constexpr int LG_CH = 32;   // h per chunk (8 MFMA steps of 4)
 constexpr int LG_W = 16;    // waves per workgroup (h ranges)
-constexpr int LG_P = 6;     // chunks a wave has in flight (H <= 3072: all of them)
+constexpr int LG_P = 6;     // chunks a logits_kernel wave has in flight (H <= 3072: all)
+constexpr int LP_P = 8;     // chunks a logits_part_kernel wave has in flight
 
 __device__ __forceinline__ void lg_load(const uint16_t* xp, const float* wp, int c, u32x4& xv,
                                         f32x4& w0, f32x4& w1) {
@@ -70,8 +72,12 @@ __global__ __launch_bounds__(64 * LG_W) void logits_kernel(const uint16_t* __res
   const int t = min(tt * 16 + i, T - 1), e = min(et * 16 + i, E - 1);
   const uint16_t* xp = x + (int64_t)t * H + 8 * kk;
   const float* wp = wr + (int64_t)e * H + 8 * kk;
-  f64x4 acc = {0.0, 0.0, 0.0, 0.0};
-  // all of this wave's loads first (up to LG_P chunks at a time), then the MFMAs
+  // all of this wave's loads first (up to LG_P chunks at a time), then the
+  // MFMAs: chunk c - c0 into accumulator (c - c0) mod 4 (four independent
+  // chains), added in a fixed order at the end
+  f64x4 acc[4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a) acc[a] = f64x4{0.0, 0.0, 0.0, 0.0};
   for (int cb = c0; cb < c1; cb += LG_P) {
     u32x4 xv[LG_P];
     f32x4 w0[LG_P], w1[LG_P];
@@ -79,10 +85,11 @@ __global__ __launch_bounds__(64 * LG_W) void logits_kernel(const uint16_t* __res
     for (int q = 0; q < LG_P; ++q) lg_load(xp, wp, min(cb + q, c1 - 1), xv[q], w0[q], w1[q]);
 #pragma unroll
     for (int q = 0; q < LG_P; ++q)
-      if (cb + q < c1) lg_mfma(xv[q], w0[q], w1[q], acc);
+      if (cb + q < c1) lg_mfma(xv[q], w0[q], w1[q], acc[q % 4]);
   }
+  const f64x4 sum4 = (acc[0] + acc[1]) + (acc[2] + acc[3]);
 #pragma unroll
-  for (int r = 0; r < 4; ++r) red[wave][r][lane] = acc[r];
+  for (int r = 0; r < 4; ++r) red[wave][r][lane] = sum4[r];
   __syncthreads();
   if (wave == 0) {
     const int ex = et * 16 + i;
@@ -104,7 +111,6 @@ __global__ __launch_bounds__(64 * LG_W) void logits_kernel(const uint16_t* __res
 // ranges in order, adds the bias and rounds once to fp32.  Within a range,
 // chunk c - c0 goes to accumulator (c - c0) mod 4 (four independent MFMA
 // chains instead of one), and the four are added in a fixed order.
-constexpr int LP_P = 8;     // chunks in flight per wave
 __global__ __launch_bounds__(64) void logits_part_kernel(const uint16_t* __restrict__ x,
                                                          const float* __restrict__ wr, int T,
                                                          int H, int E, int hs_parts,
@@ -154,99 +160,22 @@ int plan_hs_parts(int T, int E, int H) {
   return max(hs, 1);
 }
 
-// Top-k and softmax of token t by one wave.  Lane l holds the logits of
-// experts l, l + 64, l + 128, l + 192.  k rounds of a wave arg-max (larger
-// logit first, ties to the lower expert) pick the slots in order; the
-// softmax runs over the k selected logits.  Lane 0 writes the slots and
-// counts them in the LDS histogram; with `mask` and `ex` (LDS), it also
-// sets the token's expert bits (mask[t * 8 + e / 32] bit e % 32) and
-// records each slot's expert.
-__device__ __forceinline__ void topk_one(const float* __restrict__ logits, int E, int k, int t,
-                                         int lane, int32_t* __restrict__ topk_idx,
-                                         float* __restrict__ topk_w, int32_t* hist,
-                                         uint32_t* mask, int32_t* ex) {
-  float v[4];
-  uint32_t live = 0;   // bit q: expert lane + 64q exists and is not yet taken
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int e = lane + 64 * q;
-    v[q] = 0.0f;
-    if (e < E) {
-      live |= 1u << q;
-      v[q] = logits[(int64_t)t * E + e];
-    }
-  }
-  float sel0 = 0.0f, z[8], zsum = 0.0f;
-  int idx[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    if (j < k) {
-      float bv = 0.0f;
-      int bi = -1;
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        if (((live >> q) & 1u) && (bi < 0 || v[q] > bv)) { bv = v[q]; bi = lane + 64 * q; }
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        const float ov = __shfl_xor(bv, o);
-        const int oi = __shfl_xor(bi, o);
-        if (oi >= 0 && (bi < 0 || ov > bv || (ov == bv && oi < bi))) { bv = ov; bi = oi; }
-      }
-      if (j == 0) sel0 = bv;
-      idx[j] = bi;
-      if ((bi & 63) == lane) live &= ~(1u << (bi >> 6));
-      z[j] = expf(bv - sel0);
-      zsum += z[j];
-    }
-  }
-  if (lane == 0) {
-    const int64_t f0 = (int64_t)t * k;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (j < k) {
-        topk_idx[f0 + j] = idx[j];
-        topk_w[f0 + j] = z[j] / zsum;
-        if (hist) atomicAdd(&hist[idx[j]], 1);   // counts only: order does not matter
-        if (mask) mask[t * 8 + (idx[j] >> 5)] |= 1u << (idx[j] & 31);
-        if (ex) ex[f0 + j] = idx[j];
-      }
-    }
-  }
-}
-
-// RT tokens per workgroup, two per wave; writes the workgroup's expert
-// histogram for the scan.
-__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T, int E,
-                                                   int k, int32_t* __restrict__ topk_idx,
-                                                   float* __restrict__ topk_w,
-                                                   int32_t* __restrict__ blk_hist) {
-  __shared__ int32_t hist[256];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  hist[tid] = 0;
-  __syncthreads();
-#pragma unroll
-  for (int q = 0; q < RT / 4; ++q) {
-    const int t = blockIdx.x * RT + wave * (RT / 4) + q;
-    if (t < T) topk_one(logits, E, k, t, lane, topk_idx, topk_w, hist, nullptr, nullptr);
-  }
-  __syncthreads();
-  if (tid < E) blk_hist[(int64_t)blockIdx.x * E + tid] = hist[tid];
-}
-
-// Top-k and softmax of token t by one wave, from logits in LDS, without
-// cross-lane reductions: lane l owns experts l + 64q and counts, for each,
-// the experts that beat it (a larger logit, or an equal one with a lower
-// index).  An expert with count j < k is slot j.  The selected logits go
-// through the wave's LDS slots zs[8]; lane 0 forms the softmax over them in
-// slot order (exponents relative to slot 0).  Same selection and the same
-// arithmetic as topk_one.
-// NQ = ceil(E / 64) expert slots per lane (a template parameter: the
-// count loop is VALU-bound, and slots that do not exist must cost nothing).
+// Top-k and softmax of token t by one wave, from its row lt of E logits in
+// LDS, without cross-lane reductions (a chain of wave shuffles per
+// selection round measured several times slower): lane l owns experts l +
+// 64q (q < NQ = ceil(E / 64), a template parameter, since this count loop
+// is VALU-bound) and counts, for each, the experts that beat it (a larger
+// logit, or an equal one with a lower index).  The expert with count j < k
+// is slot j: the k largest logits in descending order, ties to the lower
+// index.  The selected logits go through the wave's LDS slots zs[8]; lane
+// 0 forms the softmax over them in slot order (exponents relative to slot
+// 0).  With `ex` (LDS) slot (t, j)'s expert is also recorded there; with
+// `hist` (LDS) each selected expert is counted.
 template <int NQ>
-__device__ __forceinline__ void topk_rank(const float* lg, int E, int k, int t, int lane,
+__device__ __forceinline__ void topk_rank(const float* lt, int E, int k, int t, int lane,
                                           int32_t* __restrict__ topk_idx,
-                                          float* __restrict__ topk_w, int32_t* ex, float* zs) {
-  const float* lt = lg + (int64_t)t * E;
+                                          float* __restrict__ topk_w, int32_t* ex, int32_t* hist,
+                                          float* zs) {
   float v[NQ];
   int rank[NQ];
 #pragma unroll
@@ -276,7 +205,8 @@ __device__ __forceinline__ void topk_rank(const float* lg, int E, int k, int t, 
     if (e < E && rank[q] < k) {
       const int64_t f = (int64_t)t * k + rank[q];
       topk_idx[f] = e;
-      ex[f] = e;
+      if (ex) ex[f] = e;
+      if (hist) atomicAdd(&hist[e], 1);   // counts only: order does not matter
       zs[rank[q]] = v[q];
     }
   }
@@ -295,6 +225,40 @@ __device__ __forceinline__ void topk_rank(const float* lg, int E, int k, int t, 
     for (int j = 0; j < 8; ++j)
       if (j < k) topk_w[(int64_t)t * k + j] = z[j] / zsum;
   }
+}
+
+// RT tokens per workgroup, two per wave (rank-count selection on the
+// tokens' logits staged in LDS); writes the workgroup's expert histogram
+// for the scan.
+template <int NQ>
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T, int E,
+                                                   int k, int32_t* __restrict__ topk_idx,
+                                                   float* __restrict__ topk_w,
+                                                   int32_t* __restrict__ blk_hist) {
+  __shared__ int32_t hist[256];
+  __shared__ float lgs[RT * 256];
+  __shared__ float zs[4][8];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t0 = blockIdx.x * RT;
+  const int nt = min(RT, T - t0);
+  hist[tid] = 0;
+  {
+    const int n = nt * E;   // the block's logits are contiguous
+    float v[RT];
+#pragma unroll
+    for (int u = 0; u < RT; ++u) v[u] = logits[(int64_t)t0 * E + min(tid + u * 256, n - 1)];
+#pragma unroll
+    for (int u = 0; u < RT; ++u)
+      if (tid + u * 256 < n) lgs[tid + u * 256] = v[u];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < RT / 4; ++q) {
+    const int i = wave * (RT / 4) + q;
+    if (i < nt) topk_rank<NQ>(lgs + i * E, E, k, t0 + i, lane, topk_idx, topk_w, nullptr, hist, zs[wave]);
+  }
+  __syncthreads();
+  if (tid < E) blk_hist[(int64_t)blockIdx.x * E + tid] = hist[tid];
 }
 
 // Few routed rows (R = T*k <= PLAN_MAX_ROWS, so T <= 256): the logits from
@@ -345,11 +309,14 @@ __global__ __launch_bounds__(1024) void plan_kernel(
   }
   __syncthreads();
   if (E <= 64)
-    for (int t = wave; t < T; t += 16) topk_rank<1>(lg, E, k, t, lane, topk_idx, topk_w, ex, zs[wave]);
+    for (int t = wave; t < T; t += 16)
+      topk_rank<1>(lg + t * E, E, k, t, lane, topk_idx, topk_w, ex, nullptr, zs[wave]);
   else if (E <= 128)
-    for (int t = wave; t < T; t += 16) topk_rank<2>(lg, E, k, t, lane, topk_idx, topk_w, ex, zs[wave]);
+    for (int t = wave; t < T; t += 16)
+      topk_rank<2>(lg + t * E, E, k, t, lane, topk_idx, topk_w, ex, nullptr, zs[wave]);
   else
-    for (int t = wave; t < T; t += 16) topk_rank<4>(lg, E, k, t, lane, topk_idx, topk_w, ex, zs[wave]);
+    for (int t = wave; t < T; t += 16)
+      topk_rank<4>(lg + t * E, E, k, t, lane, topk_idx, topk_w, ex, nullptr, zs[wave]);
   __syncthreads();
   for (int e = wave; e < E; e += 16) {
     int c = 0;
@@ -431,8 +398,15 @@ __global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ blk_hi
   const int e = tid % E, c = tid / E;
   int32_t sum = 0;
   if (c < C) {
-    int b1 = min(nblk, (c + 1) * per);
-    for (int b = c * per; b < b1; ++b) sum += blk_hist[(int64_t)b * E + e];
+    const int b1 = min(nblk, (c + 1) * per);
+    for (int b0 = c * per; b0 < b1; b0 += 16) {   // 16 loads in flight
+      int32_t v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) v[u] = blk_hist[(int64_t)min(b0 + u, b1 - 1) * E + e];
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        if (b0 + u < b1) sum += v[u];
+    }
   }
   part[tid] = sum;
   __syncthreads();
@@ -455,11 +429,18 @@ __global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ blk_hi
   if (tid <= E) offsets[tid] = off[tid];
   if (c < C) {
     int32_t run = off[e] + part[tid];
-    int b1 = min(nblk, (c + 1) * per);
-    for (int b = c * per; b < b1; ++b) {
-      int32_t v = blk_hist[(int64_t)b * E + e];
-      blk_hist[(int64_t)b * E + e] = run;
-      run += v;
+    const int b1 = min(nblk, (c + 1) * per);
+    for (int b0 = c * per; b0 < b1; b0 += 16) {
+      int32_t v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) v[u] = blk_hist[(int64_t)min(b0 + u, b1 - 1) * E + e];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        if (b0 + u < b1) {
+          blk_hist[(int64_t)(b0 + u) * E + e] = run;
+          run += v[u];
+        }
+      }
     }
   }
 }
@@ -495,13 +476,17 @@ __global__ __launch_bounds__(256) void tiles_kernel(const int32_t* __restrict__ 
                                                     Tile* __restrict__ tiles,
                                                     int32_t* __restrict__ num_tiles) {
   __shared__ int32_t start[257];
+  __shared__ int32_t offs[257];
   const int tid = threadIdx.x;
+  // offsets into LDS in one parallel load (a serial loop over global
+  // memory would pay a round trip per expert)
+  for (int e = tid; e <= E; e += 256) offs[e] = offsets[e];
+  __syncthreads();
   if (tid == 0) {
     int32_t run = 0;
     for (int e = 0; e < E; ++e) {
       start[e] = run;
-      int32_t n = offsets[e + 1] - offsets[e];
-      run += (n + MT - 1) / MT;
+      run += (offs[e + 1] - offs[e] + MT - 1) / MT;
     }
     start[E] = run;
     *num_tiles = run;
@@ -531,8 +516,15 @@ hipError_t launch_logits(const uint16_t* x, const float* wr, const float* br, in
 
 hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* topk_idx, float* topk_w,
                        int32_t* blk_hist, hipStream_t s) {
-  hipLaunchKernelGGL(topk_kernel, dim3(router_blocks(T)), dim3(256), 0, s, logits, T, E, k,
-                     topk_idx, topk_w, blk_hist);
+  if (E <= 64)
+    hipLaunchKernelGGL(topk_kernel<1>, dim3(router_blocks(T)), dim3(256), 0, s, logits, T, E, k,
+                       topk_idx, topk_w, blk_hist);
+  else if (E <= 128)
+    hipLaunchKernelGGL(topk_kernel<2>, dim3(router_blocks(T)), dim3(256), 0, s, logits, T, E, k,
+                       topk_idx, topk_w, blk_hist);
+  else
+    hipLaunchKernelGGL(topk_kernel<4>, dim3(router_blocks(T)), dim3(256), 0, s, logits, T, E, k,
+                       topk_idx, topk_w, blk_hist);
   return hipGetLastError();
 }
 
