@@ -54,13 +54,15 @@ def parse():
 
 # HBM bytes per launch of the GEMM kernels from rocprofv3 FETCH_SIZE and
 # WRITE_SIZE (scaled by the 256 MiB copy calibration: reads 2.0x, writes
-# 1.0x), taken on the kernel source whose SHA-256 prefix is recorded; the
-# figure is reported only while that source is unchanged.
+# 1.0x), taken on the kernel source whose SHA-256 prefixes are recorded
+# (the kernel's file and the shared device header); the figure is reported
+# only while both are unchanged.
 TRAFFIC = {
-    "gate_up": ("gemm_fwd.hip", "8b78b24dbca26d10", 844.5e6),
-    "down": ("gemm_fwd.hip", "8b78b24dbca26d10", 359.1e6),
-    "bwd_down": ("gemm_bwd.hip", "e58fe845fc2cd2c4", 570.7e6),
-    "bwd_gate_up": ("gemm_bwd.hip", "e58fe845fc2cd2c4", 787.0e6),
+    # kernel: (source file, SHA-256 prefix of that file and of common.hpp, bytes per launch)
+    "gate_up": ("gemm_fwd.hip", "20dcfcc8b6b1b4a4", "4bbb1e5bcd556976", 755.7e6),
+    "down": ("gemm_fwd.hip", "20dcfcc8b6b1b4a4", "4bbb1e5bcd556976", 352.1e6),
+    "bwd_down": ("gemm_bwd.hip", "ffaf1aef3bce8b58", "4bbb1e5bcd556976", 606.0e6),
+    "bwd_gate_up": ("gemm_bwd.hip", "ffaf1aef3bce8b58", "4bbb1e5bcd556976", 770.0e6),
 }
 
 
@@ -69,13 +71,14 @@ def counted_traffic(kernel):
     entry = TRAFFIC.get(kernel)
     if entry is None:
         return None
-    src, sha, nbytes = entry
-    path = os.path.join(ROOT, "mxfp4_weight_mixture_02_amd", "csrc", src)
+    src, sha, sha_common, nbytes = entry
+    csrc = os.path.join(ROOT, "mxfp4_weight_mixture_02_amd", "csrc")
     try:
-        cur = hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+        cur = hashlib.sha256(open(os.path.join(csrc, src), "rb").read()).hexdigest()[:16]
+        cur_common = hashlib.sha256(open(os.path.join(csrc, "common.hpp"), "rb").read()).hexdigest()[:16]
     except OSError:
         return None
-    return nbytes if cur == sha else None
+    return nbytes if (cur, cur_common) == (sha, sha_common) else None
 
 
 def kernel_times(lib):
