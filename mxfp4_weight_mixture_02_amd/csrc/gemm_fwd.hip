@@ -52,24 +52,34 @@
 
 namespace mxmoe {
 
-constexpr int FWN = 8;                 // waves per workgroup, two per SIMD
 constexpr int FRB = 2;                 // 32-row weight blocks per wave
-constexpr int FNTHR = 64 * FWN;
-constexpr int FNT = 32 * FRB * FWN;    // weight rows per workgroup (512)
-constexpr int LDS_BYTES = 160 * 1024;  // gfx950 LDS per workgroup
 constexpr int FKS = 64;                // K per step
-constexpr int NST = 4;                 // pipeline stages
 constexpr int XSTAGE = MT * FKS * 2;   // bytes of one activation stage (16 KB)
-constexpr int XCHUNKS = XSTAGE / 1024 / FWN;    // 1 KB global-to-LDS chunks per wave per step
-constexpr int PANEL_MAX = LDS_BYTES - NST * XSTAGE;
-constexpr int FWD_MAXK = PANEL_MAX / FNT * 32;   // largest K whose scale panel fits
-constexpr int LOADS_PER_STEP = XCHUNKS + FRB;    // vector loads a lane issues per step
+
+// Workgroup shapes.  W = 8: eight waves (two per SIMD), 512 weight rows,
+// four stages, all 160 KB of LDS (one workgroup per CU).  W = 4: four waves,
+// 256 weight rows, three stages, 80 KB (two workgroups per CU, so one's
+// prologue and epilogue overlap the other's main loop; measured faster for
+// gate_up, slower for down).
+template <int W>
+struct FwdShape {
+  static constexpr int NTHR = 64 * W;
+  static constexpr int NT = 32 * FRB * W;                 // weight rows per workgroup
+  static constexpr int LDS = W == 8 ? 160 * 1024 : 80 * 1024;
+  static constexpr int NST = W == 8 ? 4 : 3;              // pipeline stages
+  static constexpr int XCH = XSTAGE / 1024 / W;           // 1 KB global-to-LDS chunks per wave per step
+  static constexpr int LPS = XCH + FRB;                   // vector loads a lane issues per step
+  static constexpr int MAXK = (LDS - NST * XSTAGE) / NT * 32;   // largest K whose scale panel fits
+};
 
 __device__ constexpr int vmcnt_imm(int n) { return waitcnt_imm(n, 15); }
 
+// Per-lane pipeline state (the first FwdShape<W>::XCH activation entries
+// are used).
+constexpr int XCH_MAX = 4;
 struct FwdPipe {
-  const uint16_t* xrow[XCHUNKS];   // activation rows this lane stages
-  int xcol[XCHUNKS];               // element offset of its 16-byte slot within a step
+  const uint16_t* xrow[XCH_MAX];   // activation rows this lane stages
+  int xcol[XCH_MAX];               // element offset of its 16-byte slot within a step
   const uint8_t* wp[FRB];          // this lane's codes per row block (+ lane half)
   const uint8_t* srow[FRB];        // its scale panel rows in LDS
   uint8_t* xs;                     // LDS stages
@@ -78,13 +88,15 @@ struct FwdPipe {
 
 // Loads of step c into stage/slot SL: activations global -> LDS directly,
 // codes into registers.
-template <int SL>
-__device__ __forceinline__ void fwd_issue(const FwdPipe& p, u32x4 (&codes)[NST][FRB], int c) {
+// (codes: u32x4 [NST][FRB], taken as a deduced type)
+template <int W, int SL, class Codes>
+__device__ __forceinline__ void fwd_issue(const FwdPipe& p, Codes& codes, int c) {
+  constexpr int XCH = FwdShape<W>::XCH;
   const int wave = threadIdx.x >> 6;
 #pragma unroll
-  for (int j = 0; j < XCHUNKS; ++j)
+  for (int j = 0; j < XCH; ++j)
     __builtin_amdgcn_global_load_lds(p.xrow[j] + c * FKS + p.xcol[j],
-                                     p.xs + SL * XSTAGE + (XCHUNKS * wave + j) * 1024, 16, 0, 0);
+                                     p.xs + SL * XSTAGE + (XCH * wave + j) * 1024, 16, 0, 0);
   // the counted waits below assume this issue order: activations, then codes
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -92,8 +104,8 @@ __device__ __forceinline__ void fwd_issue(const FwdPipe& p, u32x4 (&codes)[NST][
     codes[SL][rb] = *reinterpret_cast<const u32x4*>(p.wp[rb] + c * 32);
 }
 
-template <int SL, int NRB>
-__device__ __forceinline__ void fwd_compute(const FwdPipe& p, const u32x4 (&codes)[NST][FRB], int c,
+template <int W, int SL, int NRB, class Codes>
+__device__ __forceinline__ void fwd_compute(const FwdPipe& p, const Codes& codes, int c,
                                             f32x16 (&acc)[FRB][4]) {
   const int lane = threadIdx.x & 63;
   const int l32 = lane & 31, hlf = lane >> 5;
@@ -121,51 +133,57 @@ __device__ __forceinline__ void fwd_compute(const FwdPipe& p, const u32x4 (&code
 }
 
 // One pipeline step: issue step c + NST - 1, compute step c, wait for this
-// wave's loads of step c + 1, barrier.  A lane issues LOADS_PER_STEP vector
-// loads per step (activations first, then codes), in step order, so after
-// issuing step c + NST - 1 the loads newer than all of step c + 1's number
-// LOADS_PER_STEP * (NST - 2).  Waiting for step c + 1's codes too (not only
-// its activations) keeps the compiler's own wait for the code registers
-// from falling back to a full drain at the top of the unrolled loop.
-template <int SL, int NRB>
-__device__ __forceinline__ void fwd_step(const FwdPipe& p, u32x4 (&codes)[NST][FRB], int c,
+// wave's loads of step c + 1, barrier.  A lane issues LPS vector loads per
+// step (activations first, then codes), in step order, so after issuing
+// step c + NST - 1 the loads newer than all of step c + 1's number
+// LPS * (NST - 2).  Waiting for step c + 1's codes too (not only its
+// activations) keeps the compiler's own wait for the code registers from
+// falling back to a full drain at the top of the unrolled loop.
+template <int W, int SL, int NRB, class Codes>
+__device__ __forceinline__ void fwd_step(const FwdPipe& p, Codes& codes, int c,
                                          f32x16 (&acc)[FRB][4]) {
-  fwd_issue<(SL + NST - 1) % NST>(p, codes, min(c + NST - 1, p.nsteps - 1));
+  constexpr int NST = FwdShape<W>::NST;
+  fwd_issue<W, (SL + NST - 1) % NST>(p, codes, min(c + NST - 1, p.nsteps - 1));
   __builtin_amdgcn_sched_barrier(0);
-  fwd_compute<SL, NRB>(p, codes, c, acc);
+  fwd_compute<W, SL, NRB>(p, codes, c, acc);
   __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS_PER_STEP * (NST - 2)));
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(FwdShape<W>::LPS * (NST - 2)));
   barrier_only();
 }
 
-template <int NRB>
+template <int W, int NRB>
 __device__ __forceinline__ void fwd_loop(const FwdPipe& p, f32x16 (&acc)[FRB][4]) {
+  constexpr int NST = FwdShape<W>::NST;
+  static_assert(NST == 3 || NST == 4, "the main loop is unrolled for 3 or 4 stages");
   u32x4 codes[NST][FRB];
   const int last = p.nsteps - 1;
   // The prologue's loads must stay in issue order ahead of the wait: the
   // compiler may otherwise sink the register loads below it, and the count
   // would then release before stage 0 has landed.
   __builtin_amdgcn_sched_barrier(0);
-  fwd_issue<0>(p, codes, 0);
+  fwd_issue<W, 0>(p, codes, 0);
   __builtin_amdgcn_sched_barrier(0);
-  fwd_issue<1>(p, codes, min(1, last));
+  fwd_issue<W, 1>(p, codes, min(1, last));
   __builtin_amdgcn_sched_barrier(0);
-  fwd_issue<2>(p, codes, min(2, last));
-  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (NST == 4) {
+    fwd_issue<W, 2>(p, codes, min(2, last));
+    __builtin_amdgcn_sched_barrier(0);
+  }
   // the scale panel was written with ordinary LDS stores
-  __builtin_amdgcn_s_waitcnt(waitcnt_imm(LOADS_PER_STEP * (NST - 2), 0));
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(FwdShape<W>::LPS * (NST - 2), 0));
   barrier_only();
   int c = 0;
   for (; c + NST <= p.nsteps; c += NST) {
-    fwd_step<0, NRB>(p, codes, c + 0, acc);
-    fwd_step<1, NRB>(p, codes, c + 1, acc);
-    fwd_step<2, NRB>(p, codes, c + 2, acc);
-    fwd_step<3, NRB>(p, codes, c + 3, acc);
+    fwd_step<W, 0, NRB>(p, codes, c + 0, acc);
+    fwd_step<W, 1, NRB>(p, codes, c + 1, acc);
+    fwd_step<W, 2, NRB>(p, codes, c + 2, acc);
+    if constexpr (NST == 4) fwd_step<W, 3, NRB>(p, codes, c + 3, acc);
   }
   const int rem = p.nsteps - c;
-  if (rem > 0) fwd_step<0, NRB>(p, codes, c + 0, acc);
-  if (rem > 1) fwd_step<1, NRB>(p, codes, c + 1, acc);
-  if (rem > 2) fwd_step<2, NRB>(p, codes, c + 2, acc);
+  if (rem > 0) fwd_step<W, 0, NRB>(p, codes, c + 0, acc);
+  if (rem > 1) fwd_step<W, 1, NRB>(p, codes, c + 1, acc);
+  if constexpr (NST == 4)
+    if (rem > 2) fwd_step<W, 2, NRB>(p, codes, c + 2, acc);
   // drain: nothing may still be writing LDS when the workgroup ends
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 }
@@ -175,22 +193,23 @@ __device__ __forceinline__ void fwd_loop(const FwdPipe& p, f32x16 (&acc)[FRB][4]
 // row past the tile).  wrow_local: first weight row of this lane within the
 // workgroup's rows (row blocks follow 32 rows apart; clamped for waves past
 // N).
-__device__ __forceinline__ void fwd_body(const uint16_t* const (&xrow)[XCHUNKS],
+template <int W>
+__device__ __forceinline__ void fwd_body(const uint16_t* const* xrow,
                                          const uint8_t* __restrict__ codes_e,
                                          const uint8_t* __restrict__ scales_e, int K, int n0,
                                          int nrows, int wrow_local, int nrb, uint8_t* lds,
                                          f32x16 (&acc)[FRB][4]) {
-  static_assert(NST == 4, "the main loop is unrolled for 4 stages");
+  constexpr int XCH = FwdShape<W>::XCH;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hlf = lane >> 5;
-  uint8_t* panel = lds + NST * XSTAGE;
+  uint8_t* panel = lds + FwdShape<W>::NST * XSTAGE;
   const int KB32 = K / 32;
 
   // scale panel: nrows * K/32 contiguous bytes, 16-byte aligned
   {
     const u32x4* src = reinterpret_cast<const u32x4*>(scales_e + (int64_t)n0 * KB32);
     u32x4* dst = reinterpret_cast<u32x4*>(panel);
-    stage_lds<6>(nrows * KB32 / 16, tid, FNTHR, [&](int q) { return src[q]; },
+    stage_lds<6>(nrows * KB32 / 16, tid, FwdShape<W>::NTHR, [&](int q) { return src[q]; },
                  [&](int q, u32x4 v) { dst[q] = v; });
   }
 #pragma unroll
@@ -200,12 +219,13 @@ __device__ __forceinline__ void fwd_body(const uint16_t* const (&xrow)[XCHUNKS],
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[rb][tb][r] = 0.0f;
 
+  static_assert(XCH <= XCH_MAX, "activation chunks per wave");
   FwdPipe p;
 #pragma unroll
-  for (int j = 0; j < XCHUNKS; ++j) {
-    const int row = (XCHUNKS * wave + j) * 8 + lane / 8;   // row of the tile this lane stages
+  for (int j = 0; j < XCH; ++j) {
+    const int row = (XCH * wave + j) * 8 + lane / 8;   // row of the tile this lane stages
     p.xrow[j] = xrow[j];
-    p.xcol[j] = 8 * ((lane & 7) ^ ((row >> 1) & 7));       // global column block of its slot
+    p.xcol[j] = 8 * ((lane & 7) ^ ((row >> 1) & 7));   // global column block of its slot
   }
   const int64_t rowbytes = K / 2;
   // row blocks past the workgroup's rows (the last column tile can hold
@@ -219,20 +239,25 @@ __device__ __forceinline__ void fwd_body(const uint16_t* const (&xrow)[XCHUNKS],
   p.xs = lds;
   p.nsteps = K / FKS;
   switch (nrb) {
-    case 1: fwd_loop<1>(p, acc); break;
-    case 2: fwd_loop<2>(p, acc); break;
-    case 3: fwd_loop<3>(p, acc); break;
-    default: fwd_loop<4>(p, acc); break;
+    case 1: fwd_loop<W, 1>(p, acc); break;
+    case 2: fwd_loop<W, 2>(p, acc); break;
+    case 3: fwd_loop<W, 3>(p, acc); break;
+    default: fwd_loop<W, 4>(p, acc); break;
   }
 }
 
-__global__ __launch_bounds__(FNTHR) void gate_up_kernel(
+// Two waves per SIMD in either shape (amdgpu_waves_per_eu keeps the W = 4
+// kernel within the registers of two waves, so two workgroups fit a CU).
+template <int W>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2, 2))) void gate_up_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, const uint16_t* __restrict__ bias,
     const int32_t* __restrict__ sorted_rows, const Tile* __restrict__ tiles,
     const int32_t* __restrict__ num_tiles, int H, int I, int k, float alpha, float limit,
     uint16_t* __restrict__ h_out, uint16_t* __restrict__ a_out) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
+  using S = FwdShape<W>;
+  constexpr int XCHUNKS = S::XCH, FNT = S::NT;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[S::LDS];
   const int N = 2 * I;
   int mt, nt;
   if (!xcd_work_item(*num_tiles, (N + FNT - 1) / FNT, &mt, &nt)) return;
@@ -251,7 +276,7 @@ __global__ __launch_bounds__(FNTHR) void gate_up_kernel(
   }
   const int nrows = min(FNT, N - n0);
   f32x16 acc[FRB][4];
-  fwd_body(xrow, codes + (int64_t)e * N * (H / 2), scales + (int64_t)e * N * (H / 32), H, n0,
+  fwd_body<W>(xrow, codes + (int64_t)e * N * (H / 2), scales + (int64_t)e * N * (H / 32), H, n0,
            nrows, (wave * 32 * FRB < nrows ? wave * 32 * FRB : 0) + l32, (tl.rows + 31) / 32, lds,
            acc);
   // Epilogue through LDS: every wave's loads have landed (fwd_loop drained
@@ -316,14 +341,16 @@ __global__ __launch_bounds__(FNTHR) void gate_up_kernel(
 // branch around these MFMAs makes the compiler spill accumulators inside
 // the main loop).
 template <bool LORA>
-__global__ __launch_bounds__(FNTHR) void down_kernel(
+__global__ __launch_bounds__(FwdShape<8>::NTHR) void down_kernel(
     const uint16_t* __restrict__ a, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, const uint16_t* __restrict__ bias,
     const float* __restrict__ topk_w, const int32_t* __restrict__ sorted_rows,
     const Tile* __restrict__ tiles, const int32_t* __restrict__ num_tiles, int H, int I,
     const uint16_t* __restrict__ lora_B, const float* __restrict__ lora_v, float lora_scale,
     float* __restrict__ y_w) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
+  using S = FwdShape<8>;
+  constexpr int XCHUNKS = S::XCH, FNT = S::NT;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[S::LDS];
   const int N = H;
   int mt, nt;
   if (!xcd_work_item(*num_tiles, (N + FNT - 1) / FNT, &mt, &nt)) return;
@@ -342,7 +369,7 @@ __global__ __launch_bounds__(FNTHR) void down_kernel(
   const int nrows = min(FNT, N - n0);
   f32x16 acc[FRB][4];
   const int wrow_local = (wave * 32 * FRB < nrows ? wave * 32 * FRB : 0) + l32;
-  fwd_body(xrow, codes + (int64_t)e * N * (I / 2), scales + (int64_t)e * N * (I / 32), I, n0,
+  fwd_body<8>(xrow, codes + (int64_t)e * N * (I / 2), scales + (int64_t)e * N * (I / 32), I, n0,
            nrows, wrow_local, (tl.rows + 31) / 32, lds, acc);
   if (LORA) {
     // + s v B_e^T: one more 16-deep contraction over the rank, A-operand =
@@ -420,7 +447,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 }
 
 // K step of the forward GEMMs for a contraction length K (0: unsupported).
-int fwd_step_k(int K) { return (K % FKS == 0 && K <= FWD_MAXK) ? FKS : 0; }
+int fwd_step_k(int K) { return (K % FKS == 0 && K <= FwdShape<8>::MAXK) ? FKS : 0; }
 
 hipError_t launch_gate_up(const uint16_t* x, const uint8_t* codes, const uint8_t* scales,
                           const uint16_t* bias, const int32_t* sorted_rows, const Tile* tiles,
@@ -428,9 +455,17 @@ hipError_t launch_gate_up(const uint16_t* x, const uint8_t* codes, const uint8_t
                           float alpha, float limit, uint16_t* h_out, uint16_t* a_out,
                           hipStream_t s) {
   if (!fwd_step_k(H)) return hipErrorInvalidValue;
-  dim3 grid(((2 * I + FNT - 1) / FNT) * max_tiles), block(FNTHR);
-  hipLaunchKernelGGL(gate_up_kernel, grid, block, 0, s, x, codes, scales, bias, sorted_rows,
-                     tiles, num_tiles, H, I, k, alpha, limit, h_out, a_out);
+  if (H <= FwdShape<4>::MAXK) {
+    using S = FwdShape<4>;
+    hipLaunchKernelGGL(gate_up_kernel<4>, dim3(((2 * I + S::NT - 1) / S::NT) * max_tiles),
+                       dim3(S::NTHR), 0, s, x, codes, scales, bias, sorted_rows, tiles, num_tiles,
+                       H, I, k, alpha, limit, h_out, a_out);
+  } else {
+    using S = FwdShape<8>;
+    hipLaunchKernelGGL(gate_up_kernel<8>, dim3(((2 * I + S::NT - 1) / S::NT) * max_tiles),
+                       dim3(S::NTHR), 0, s, x, codes, scales, bias, sorted_rows, tiles, num_tiles,
+                       H, I, k, alpha, limit, h_out, a_out);
+  }
   return hipGetLastError();
 }
 
@@ -440,7 +475,8 @@ hipError_t launch_down(const uint16_t* a, const uint8_t* codes, const uint8_t* s
                        const uint16_t* lora_B, const float* lora_v, float lora_scale,
                        float* y_w, hipStream_t s) {
   if (!fwd_step_k(I)) return hipErrorInvalidValue;
-  dim3 grid(((H + FNT - 1) / FNT) * max_tiles), block(FNTHR);
+  using S = FwdShape<8>;
+  dim3 grid(((H + S::NT - 1) / S::NT) * max_tiles), block(S::NTHR);
   if (lora_B)
     hipLaunchKernelGGL(down_kernel<true>, grid, block, 0, s, a, codes, scales, bias, topk_w,
                        sorted_rows, tiles, num_tiles, H, I, lora_B, lora_v, lora_scale, y_w);

@@ -163,6 +163,13 @@ def test_many_experts_top8():
     _run_layer(syn.spec("tiny", T=64, H=128, I=128, E=64, k=8))
 
 
+def test_wide_hidden_size():
+    # H = 4160 > 4096: gate_up takes the eight-wave, 512-row workgroup shape
+    # (the scale panel of a 256-row workgroup no longer fits its 80 KB), and
+    # K = H = 65 steps of 64 leaves a ragged last group of the unrolled loop
+    _run_layer(syn.spec("tiny", T=300, H=4160, I=192, E=3, k=2))
+
+
 @pytest.mark.parametrize("lora_scale", [1.0, 32.0])
 def test_lora_tiny(lora_scale):
     # scale 32 makes the adapter delta comparable to the base output
