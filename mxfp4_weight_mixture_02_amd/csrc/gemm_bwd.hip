@@ -444,7 +444,12 @@ __global__ __launch_bounds__(BTHR) void bwd_gate_up_kernel(
   }
 }
 
-// One workgroup (256 threads) per token.
+// One workgroup (256 threads) per token.  Slot j's dw = the sum of its
+// column-tile partials (in tile order) + dY . bd[e_j] (a fixed-order block
+// reduction); then dX[t] = sum_j dxr[(t,j)] + dl_j Wr[e_j].  The bias dot
+// reads dY and the slots' bias rows in 16-byte pieces, one batch of k + 1
+// loads per piece (2-byte loads in a "load, use" loop paid a memory round
+// trip per element group), and the dw partials go through LDS.
 __global__ __launch_bounds__(256) void bwd_combine_kernel(
     const uint16_t* __restrict__ dy, const float* __restrict__ dxr,
     const float* __restrict__ dw_part, int n_dw_part, const int32_t* __restrict__ topk_idx,
@@ -453,37 +458,50 @@ __global__ __launch_bounds__(256) void bwd_combine_kernel(
   __shared__ float red[4][8];
   __shared__ float dl[8];
   __shared__ int32_t ex[8];
+  __shared__ float dwps[8 * 16];
   const int64_t t = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (tid < k) ex[tid] = topk_idx[t * k + tid];
+  for (int q = tid; q < k * n_dw_part; q += 256) dwps[q] = dw_part[t * k * n_dw_part + q];
   __syncthreads();
-  // dY . bd[e_j] for each slot (the bias part of dw_j = dY . y_j)
   float part[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) part[j] = 0.0f;
   if (dn_bias) {
-    for (int h = tid; h < H; h += 256) {
-      const float g = bf16_to_f32(dy[t * H + h]);
+    for (int c = tid; c < H / 8; c += 256) {
+      const u32x4 g = reinterpret_cast<const u32x4*>(dy + t * H)[c];
+      u32x4 b[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j)
-        if (j < k) part[j] += g * bf16_to_f32(dn_bias[(int64_t)ex[j] * H + h]);
+        if (j < k) b[j] = reinterpret_cast<const u32x4*>(dn_bias + (int64_t)ex[j] * H)[c];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (j < k) {
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            part[j] += bf16_to_f32((uint16_t)(g[m] & 0xFFFFu)) * bf16_to_f32((uint16_t)(b[j][m] & 0xFFFFu));
+            part[j] += bf16_to_f32((uint16_t)(g[m] >> 16)) * bf16_to_f32((uint16_t)(b[j][m] >> 16));
+          }
+        }
+      }
     }
   }
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    float v = part[j];
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-    if (lane == 0 && j < k) red[wave][j] = v;
+    if (j < k) {
+      float v = part[j];
+      for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+      if (lane == 0) red[wave][j] = v;
+    }
   }
   __syncthreads();
   if (tid == 0) {
     float dw[8], w[8], sw = 0.0f;
     for (int j = 0; j < k; ++j) {
-      const int64_t f = t * k + j;
       float s = red[0][j] + red[1][j] + red[2][j] + red[3][j];
-      for (int q = 0; q < n_dw_part; ++q) s += dw_part[f * n_dw_part + q];
+      for (int q = 0; q < n_dw_part; ++q) s += dwps[j * n_dw_part + q];
       dw[j] = s;
-      w[j] = topk_w[f];
+      w[j] = topk_w[t * k + j];
       sw += w[j] * s;
     }
     for (int j = 0; j < k; ++j) dl[j] = w[j] * (dw[j] - sw);
