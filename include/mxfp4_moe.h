@@ -54,8 +54,8 @@ extern "C" {
  *  Requirements: T >= 1; H % 64 == 0 and I % 64 == 0 (whole 32-element
  *  scale blocks, [P3] group-32 guard, in 64-element K steps);
  *  1 <= k <= min(E, 8); E <= 256; T * k < 2^31; T * H < 2^31;
- *  H, I <= 5120; lora_rank in {0, 16}.  Weight, scale, activation and
- *  output pointers 16-byte aligned.
+ *  H, I <= 5120; lora_rank in {0, 16}.  Weight, scale, bias, activation
+ *  and output pointers 16-byte aligned.
  *  swiglu_alpha, swiglu_limit: the clamped SwiGLU constants (GPT-OSS uses
  *  1.702 and 7).  lora_scale multiplies the LoRA delta (1.0 when
  *  lora_alpha equals the rank). */

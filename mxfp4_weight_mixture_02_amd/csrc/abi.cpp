@@ -135,8 +135,8 @@ int check_weights(const mxfp4_moe_weights* w, const mxfp4_moe_dims& d) {
   if (!aligned(w->router_w, 16) || !aligned(w->gu_codes, 16) || !aligned(w->dn_codes, 16) ||
       !aligned(w->gu_scales, 16) || !aligned(w->dn_scales, 16))
     return fail(MXFP4_EINVAL, "router_w and the codes and scales must be 16-byte aligned");
-  if ((w->gu_bias && !aligned(w->gu_bias, 2)) || (w->dn_bias && !aligned(w->dn_bias, 2)))
-    return fail(MXFP4_EINVAL, "biases must be 2-byte aligned");
+  if ((w->gu_bias && !aligned(w->gu_bias, 16)) || (w->dn_bias && !aligned(w->dn_bias, 16)))
+    return fail(MXFP4_EINVAL, "biases must be 16-byte aligned");
   return MXFP4_OK;
 }
 

@@ -135,9 +135,10 @@ __global__ __launch_bounds__(512) void dec_kernel(
         for (int q = 0; q < 4; ++q) {
           const int nb = n0 + 8 * q + 4 * hlf;
           float v[4];
+          const u32x2 bw = bias ? *reinterpret_cast<const u32x2*>(bias + (int64_t)e * N + nb) : u32x2{0u, 0u};
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            v[i] = acc[4 * q + i] + (bias ? bf16_to_f32(bias[(int64_t)e * N + nb + i]) : 0.0f);
+            v[i] = acc[4 * q + i] + bf16_to_f32((uint16_t)(bw[i >> 1] >> (16 * (i & 1))));
           if (GATE_UP) {
             const int I = N / 2;
             if (h_out) {
@@ -261,8 +262,11 @@ __global__ __launch_bounds__(64 * KW) void dec_ksplit_kernel(
     const int p = g0 + l32;
     if (l32 < DG && p < tl.rows) {
       const int nb = rb * 32 + 8 * wave + 4 * hlf;
+      {
+        const u32x2 bw = bias ? *reinterpret_cast<const u32x2*>(bias + (int64_t)e * N + nb) : u32x2{0u, 0u};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] += bias ? bf16_to_f32(bias[(int64_t)e * N + nb + i]) : 0.0f;
+        for (int i = 0; i < 4; ++i) v[i] += bf16_to_f32((uint16_t)(bw[i >> 1] >> (16 * (i & 1))));
+      }
       const int64_t rho = tl.row0 + p;
       if (GATE_UP) {
         const int I = N / 2;

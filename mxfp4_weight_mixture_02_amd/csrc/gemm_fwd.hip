@@ -246,6 +246,26 @@ __device__ __forceinline__ void fwd_body(const uint16_t* const* xrow,
   }
 }
 
+// The bias of a lane's accumulator rows, rb * 32 + 8 q + i (i < 4) from
+// base: four consecutive bf16 per (rb, q), one 8-byte load each (base is a
+// multiple of 4 elements and the bias 16-byte aligned); zeros without bias.
+__device__ __forceinline__ void load_bias_rows(const uint16_t* __restrict__ bias, int64_t base,
+                                               float (&bv)[FRB][4][4]) {
+  u32x2 raw[FRB][4];
+#pragma unroll
+  for (int rb = 0; rb < FRB; ++rb)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      raw[rb][q] = bias ? *reinterpret_cast<const u32x2*>(bias + base + rb * 32 + 8 * q) : u32x2{0u, 0u};
+#pragma unroll
+  for (int rb = 0; rb < FRB; ++rb)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        bv[rb][q][i] = bf16_to_f32((uint16_t)(raw[rb][q][i >> 1] >> (16 * (i & 1))));
+}
+
 // Two waves per SIMD in either shape (amdgpu_waves_per_eu keeps the W = 4
 // kernel within the registers of two waves, so two workgroups fit a CU).
 template <int W>
@@ -287,13 +307,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   uint8_t* hst = lds + wave * 6144;           // h strip: 32 rows x 64 bf16 (128-byte rows)
   uint8_t* ast = hst + 4096;                  // a strip: 32 rows x 32 bf16 (64-byte rows)
   float bv[FRB][4][4];
-#pragma unroll
-  for (int rb = 0; rb < FRB; ++rb)
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        bv[rb][q][i] = bias ? bf16_to_f32(bias[(int64_t)e * N + n0 + wcol + rb * 32 + 8 * q + 4 * hlf + i]) : 0.0f;
+  load_bias_rows(bias, (int64_t)e * N + n0 + wcol + 4 * hlf, bv);
 #pragma unroll
   for (int tb = 0; tb < 4; ++tb) {
     if (tb * 32 >= tl.rows) break;
@@ -396,13 +410,7 @@ __global__ __launch_bounds__(FwdShape<8>::NTHR) void down_kernel(
   if (n0 + wcol >= N) return;
   uint8_t* yst = lds + wave * 8192;           // y strip: 32 rows x 64 fp32 (256-byte rows)
   float bv[FRB][4][4];
-#pragma unroll
-  for (int rb = 0; rb < FRB; ++rb)
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        bv[rb][q][i] = bias ? bf16_to_f32(bias[(int64_t)e * N + n0 + wcol + rb * 32 + 8 * q + 4 * hlf + i]) : 0.0f;
+  load_bias_rows(bias, (int64_t)e * N + n0 + wcol + 4 * hlf, bv);
 #pragma unroll
   for (int tb = 0; tb < 4; ++tb) {
     if (tb * 32 >= tl.rows) break;

@@ -91,6 +91,11 @@ def test_forward_validation(L):
     bad = _dims(H=80)
     rc = L.mxfp4_moe_forward(ctypes.byref(bad), ctypes.byref(w), FAKE, FAKE, None, FAKE, ws, None)
     assert rc == -2
+    # biases are read in 8- and 16-byte pieces: a bias off 16-byte alignment is refused
+    for field in ("gu_bias", "dn_bias"):
+        rc = L.mxfp4_moe_forward(ctypes.byref(d), ctypes.byref(_weights(**{field: FAKE + 2})),
+                                 FAKE, FAKE, None, FAKE, ws, None)
+        assert rc == -1 and "bias" in _err(L)
     sv = Saved(FAKE, FAKE, FAKE, 0, FAKE, FAKE, 0)   # sorted_rows missing
     rc = L.mxfp4_moe_forward(ctypes.byref(d), ctypes.byref(w), FAKE, FAKE, ctypes.byref(sv),
                              FAKE, ws, None)
