@@ -90,63 +90,91 @@ __global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __r
   out[i] = in[b * per + (int64_t)r * R2 + c];
 }
 
-// G[e][c][j] = sum over the sorted rows p of expert e, in order, of
+// G[e][c][j] = sum over the sorted rows p of expert e of
 // (scale * topk_w[sorted_rows[p]] * P[p][j]) * Q[row(p)][c], written to
 // out[e * e_stride + c * c_stride + j * j_stride]; row(p) as in lora_proj.
-// One thread per column c (all 16 rank columns), 64 rows per round: the
-// scaled P rows and the source rows of a round are staged in LDS, then each
-// thread issues its 64 independent loads before the FMAs.  The sum order is
-// fixed, so the result is deterministic; an expert with no rows gets zeros.
+// A workgroup takes 128 columns of one expert: lane l of each wave owns
+// columns 2l and 2l+1 (one 4-byte load of Q per row), and the expert's rows
+// go in rounds of 64, wave w taking rounds w, w + 4, ..  For its round a
+// wave stages the 64 scaled P rows in its own LDS slice (lane = row), then
+// issues the 64 loads of its columns before the 2048 FMAs.  The four waves'
+// partial sums are added in wave order at the end, so the result is
+// deterministic; an expert with no rows gets zeros.  C % 64 == 0.
+constexpr int LG_RB = 64;     // rows per round
+constexpr int LG_COLS = 128;  // columns per workgroup
 template <bool GATHER>
 __global__ __launch_bounds__(256) void lora_grad_kernel(
     const uint16_t* __restrict__ Q, int C, const int32_t* __restrict__ sorted_rows, int k,
     const float* __restrict__ P, const float* __restrict__ topk_w, float scale,
     const int32_t* __restrict__ offsets, float* __restrict__ out, int64_t e_stride,
     int c_stride, int j_stride) {
-  constexpr int RB = 64;
-  __shared__ __attribute__((aligned(16))) float ps[RB][LORA_R];
-  __shared__ int64_t qrow[RB];
+  __shared__ __attribute__((aligned(16))) float ps[4][LG_RB][LORA_R];
+  __shared__ int64_t qrow[4][LG_RB];
+  __shared__ float red[4][LG_COLS][LORA_R + 1];
   const int e = blockIdx.y;
-  const int tid = threadIdx.x;
-  const int c = blockIdx.x * 256 + tid;
-  const int cc = min(c, C - 1);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c0 = blockIdx.x * LG_COLS;
+  const int cc = min(c0 + 2 * lane, C - 2);
   const int p0 = offsets[e], p1 = offsets[e + 1];
-  float acc[LORA_R];
+  const int nrounds = (p1 - p0 + LG_RB - 1) / LG_RB;
+  float acc[2][LORA_R];
 #pragma unroll
-  for (int j = 0; j < LORA_R; ++j) acc[j] = 0.0f;
-  for (int pb = p0; pb < p1; pb += RB) {
-    const int n = min(RB, p1 - pb);
-    __syncthreads();   // the previous round's LDS reads are done
-    for (int q = tid; q < RB * LORA_R; q += 256) {
-      const int r = q / LORA_R, j = q % LORA_R;
-      float v = 0.0f;
-      if (r < n) {
-        const int64_t p = pb + r;
-        v = scale * topk_w[sorted_rows[p]] * P[p * LORA_R + j];
+  for (int j = 0; j < LORA_R; ++j) acc[0][j] = acc[1][j] = 0.0f;
+  for (int r = wave; r < nrounds; r += 4) {
+    const int pb = p0 + r * LG_RB;
+    const int n = min(LG_RB, p1 - pb);
+    {
+      // lane = row: its scaled P row (zero past the expert) and source row
+      const int64_t p = pb + min(lane, n - 1);
+      const int32_t f = sorted_rows[p];
+      const f32x4* pr = reinterpret_cast<const f32x4*>(P + p * LORA_R);
+      f32x4 v[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[q] = pr[q];
+      const float w = lane < n ? scale * topk_w[f] : 0.0f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        f32x4 t;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) t[m] = w * v[q][m];
+        *reinterpret_cast<f32x4*>(&ps[wave][lane][4 * q]) = t;
       }
-      ps[r][j] = v;   // rows past the expert weigh 0
+      qrow[wave][lane] = GATHER ? (int64_t)(f / k) : p;
     }
-    if (tid < RB) {
-      const int64_t p = pb + min(tid, n - 1);
-      qrow[tid] = GATHER ? (int64_t)(sorted_rows[p] / k) : p;
-    }
-    __syncthreads();
-    float qv[RB];
+    wave_lds_sync();
+    uint32_t qv[LG_RB];
 #pragma unroll
-    for (int r = 0; r < RB; ++r) qv[r] = bf16_to_f32(Q[qrow[r] * C + cc]);
+    for (int i = 0; i < LG_RB; ++i) qv[i] = *reinterpret_cast<const uint32_t*>(Q + qrow[wave][i] * C + cc);
 #pragma unroll
-    for (int r = 0; r < RB; ++r) {
+    for (int i = 0; i < LG_RB; ++i) {
+      const float qa = bf16_to_f32((uint16_t)(qv[i] & 0xFFFFu));
+      const float qb = bf16_to_f32((uint16_t)(qv[i] >> 16));
 #pragma unroll
       for (int j4 = 0; j4 < LORA_R / 4; ++j4) {
-        const f32x4 pv = *reinterpret_cast<const f32x4*>(&ps[r][4 * j4]);
+        const f32x4 pv = *reinterpret_cast<const f32x4*>(&ps[wave][i][4 * j4]);
 #pragma unroll
-        for (int m = 0; m < 4; ++m) acc[4 * j4 + m] += qv[r] * pv[m];
+        for (int m = 0; m < 4; ++m) {
+          acc[0][4 * j4 + m] += qa * pv[m];
+          acc[1][4 * j4 + m] += qb * pv[m];
+        }
       }
     }
+    wave_lds_sync();   // this round's LDS reads are done before the next staging
   }
-  if (c >= C) return;
 #pragma unroll
-  for (int j = 0; j < LORA_R; ++j) out[(int64_t)e * e_stride + (int64_t)c * c_stride + (int64_t)j * j_stride] = acc[j];
+  for (int j = 0; j < LORA_R; ++j) {
+    red[wave][2 * lane][j] = acc[0][j];
+    red[wave][2 * lane + 1][j] = acc[1][j];
+  }
+  __syncthreads();
+  for (int q = tid; q < LG_COLS * LORA_R; q += 256) {
+    const int col = q / LORA_R, j = q % LORA_R;
+    const int c = c0 + col;
+    if (c < C) {
+      const float s = ((red[0][col][j] + red[1][col][j]) + red[2][col][j]) + red[3][col][j];
+      out[(int64_t)e * e_stride + (int64_t)c * c_stride + (int64_t)j * j_stride] = s;
+    }
+  }
 }
 
 hipError_t launch_lora_proj(const uint16_t* src, bool gather, const int32_t* sorted_rows, int k,
@@ -174,7 +202,8 @@ hipError_t launch_lora_grad(const uint16_t* Q, bool gather, int C, const int32_t
                             int k, const float* P, const float* topk_w, float scale,
                             const int32_t* offsets, int E, float* out, int64_t e_stride,
                             int c_stride, int j_stride, hipStream_t s) {
-  dim3 grid((C + 255) / 256, E);
+  if (C % 64) return hipErrorInvalidValue;
+  dim3 grid((C + LG_COLS - 1) / LG_COLS, E);
   if (gather)
     hipLaunchKernelGGL(lora_grad_kernel<true>, grid, dim3(256), 0, s, Q, C, sorted_rows, k, P,
                        topk_w, scale, offsets, out, e_stride, c_stride, j_stride);
