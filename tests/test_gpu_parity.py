@@ -163,6 +163,25 @@ def test_many_experts_top8():
     _run_layer(syn.spec("tiny", T=64, H=128, I=128, E=64, k=8))
 
 
+@pytest.mark.timeout(600)
+def test_maximum_hidden_sizes():
+    # H = I = 5120, the largest the library takes: 80 K-steps per GEMM, the
+    # eight-wave gate_up, 160 h-chunks in the router, R = 320 > 256 routed
+    # rows (the many-token routing path and the general GEMMs)
+    _run_layer(syn.spec("tiny", T=160, H=5120, I=5120, E=3, k=2))
+
+
+def test_256_experts_top8_many_tokens():
+    # E = 256 (four experts per lane in the top-k), k = 8; T * E > 4096, so
+    # the many-token routing path; R = 256 takes the decode GEMMs
+    _run_layer(syn.spec("tiny", T=32, H=64, I=64, E=256, k=8))
+
+
+def test_256_experts_top8_planned():
+    # the one-workgroup routing plan with four experts per lane (T * E = 4096)
+    _run_layer(syn.spec("tiny", T=16, H=64, I=64, E=256, k=8))
+
+
 def test_wide_hidden_size():
     # H = 4160 > 4096: gate_up takes the eight-wave, 512-row workgroup shape
     # (the scale panel of a 256-row workgroup no longer fits its 80 KB), and
