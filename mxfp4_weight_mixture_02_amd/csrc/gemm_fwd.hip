@@ -10,20 +10,21 @@
 //          the combine can sum a token's k slots in a fixed order.
 //
 // Tiling.  A workgroup computes MT = 128 routed rows of one expert against
-// NT = 512 weight rows with 8 waves, two per SIMD; wave w owns weight rows
-// 64w..64w+63 (two 32-row MFMA blocks) for all 128 routed rows (four
-// 32-column blocks): 8 accumulators of 32x32 fp32 (128 accumulation
-// registers).  Each decoded weight fragment feeds four MFMAs and each
-// activation fragment read from LDS two; the second wave per SIMD hides
-// the other's load and LDS waits (measured faster than one wave with four
-// weight blocks).  The product is computed transposed, D[n][p] = W[n][:] . X[p][:],
-// so the weights are the MFMA A-operand: a lane reads its weight rows
-// straight from global memory and decodes the codes in registers with the
-// scaled fp4 -> bf16 conversion; no weight passes through LDS and no weight
-// is decoded twice.  The routed activation rows are the B-operand, shared
-// by the eight waves through LDS.  The 512 x (K/32) UE8M0 scale panel of the
-// workgroup's weight rows is one contiguous span of memory; it is copied
-// into LDS once.
+// NT = 64 W weight rows with W waves (FwdShape: W = 8, one 160 KB workgroup
+// per CU, for down; W = 4, two 80 KB workgroups per CU, for gate_up); two
+// waves per SIMD either way.  Wave w owns weight rows 64w..64w+63 (two
+// 32-row MFMA blocks) for all 128 routed rows (four 32-column blocks): 8
+// accumulators of 32x32 fp32 (128 accumulation registers).  Each decoded
+// weight fragment feeds four MFMAs and each activation fragment read from
+// LDS two; the second wave per SIMD hides the other's load and LDS waits
+// (measured faster than one wave with four weight blocks).  The product is
+// computed transposed, D[n][p] = W[n][:] . X[p][:], so the weights are the
+// MFMA A-operand: a lane reads its weight rows straight from global memory
+// and decodes the codes in registers with the scaled fp4 -> bf16
+// conversion; no weight passes through LDS and no weight is decoded twice.
+// The routed activation rows are the B-operand, shared by the workgroup's
+// waves through LDS.  The NT x (K/32) UE8M0 scale panel of the workgroup's
+// weight rows is one contiguous span of memory; it is copied into LDS once.
 //
 // Pipeline.  K advances in steps of 64; loads run NST - 1 steps ahead: the
 // activations of a step go straight from global memory into one of NST LDS
