@@ -67,13 +67,15 @@ struct RawBlock {
   uint32_t scale[8];
 };
 
-__device__ __forceinline__ void load_block(RawBlock& rb, const uint8_t* __restrict__ code0,
-                                           const uint8_t* __restrict__ scale0, int64_t crow,
-                                           int64_t srow) {
+// Addresses are the expert's (workgroup-uniform) bases plus 32-bit offsets:
+// one register per address instead of a 64-bit pointer pair.
+__device__ __forceinline__ void load_block(RawBlock& rb, const uint8_t* __restrict__ cbase,
+                                           const uint8_t* __restrict__ sbase, uint32_t coff,
+                                           uint32_t soff, uint32_t crow, uint32_t srow) {
 #pragma unroll
   for (int r = 0; r < 8; ++r) {
-    rb.code[r] = *reinterpret_cast<const uint32_t*>(code0 + r * crow);
-    rb.scale[r] = scale0[r * srow];
+    rb.code[r] = *reinterpret_cast<const uint32_t*>(cbase + (coff + r * crow));
+    rb.scale[r] = sbase[soff + r * srow];
   }
 }
 
@@ -118,9 +120,11 @@ struct BwdPipe {
 
 struct BwdArgs {
   const uint16_t* brow[BPPT];   // activation rows this thread stages (+ its 8-element piece)
-  const uint8_t* bcode[BBLK];   // its weight blocks' first code row, at step 0
-  const uint8_t* bscale[BBLK];  // and first scale row
-  int64_t crow, srow;           // bytes between stored rows (codes, scales)
+  const uint8_t* wcode;         // the expert's codes and scales (workgroup-uniform)
+  const uint8_t* wscale;
+  uint32_t bcode[BBLK];         // byte offset of its weight blocks' first code row, at step 0
+  uint32_t bscale[BBLK];        // and of the first scale row (an expert is < 4 GiB)
+  uint32_t crow, srow;          // bytes between stored rows (codes, scales)
   int nsteps;
 };
 
@@ -130,8 +134,8 @@ __device__ __forceinline__ void bwd_issue(BwdPipe& pp, const BwdArgs& g, int c) 
   for (int j = 0; j < BPPT; ++j) pp.xv[PAR][j] = *reinterpret_cast<const u32x4*>(g.brow[j] + c * BKC);
 #pragma unroll
   for (int i = 0; i < BBLK; ++i)
-    load_block(pp.raw[PAR][i], g.bcode[i] + (int64_t)c * BKC * g.crow,
-               g.bscale[i] + (int64_t)c * BKC * g.srow, g.crow, g.srow);
+    load_block(pp.raw[PAR][i], g.wcode, g.wscale, g.bcode[i] + (uint32_t)c * BKC * g.crow,
+               g.bscale[i] + (uint32_t)c * BKC * g.srow, g.crow, g.srow);
 }
 
 template <int PAR>
@@ -226,6 +230,8 @@ __device__ __forceinline__ void bwd_mainloop(const uint16_t* const (&brow)[BPPT]
   g.nsteps = C / BKC;
   g.crow = O / 2;
   g.srow = O / 32;
+  g.wcode = wcode;
+  g.wscale = wscale;
 #pragma unroll
   for (int j = 0; j < BPPT; ++j) g.brow[j] = brow[j];
 #pragma unroll
@@ -233,8 +239,8 @@ __device__ __forceinline__ void bwd_mainloop(const uint16_t* const (&brow)[BPPT]
     const int q = tid + i * BTHR;
     const int cb = q / (BNT / 8), ob = q & (BNT / 8 - 1);
     const int ocol = (o0 + 8 * ob < O) ? o0 + 8 * ob : 0;
-    g.bcode[i] = wcode + (int64_t)(8 * cb) * g.crow + ocol / 2;
-    g.bscale[i] = wscale + (int64_t)(8 * cb) * g.srow + ocol / 32;
+    g.bcode[i] = (uint32_t)(8 * cb) * g.crow + ocol / 2;
+    g.bscale[i] = (uint32_t)(8 * cb) * g.srow + ocol / 32;
   }
 #pragma unroll
   for (int rb = 0; rb < BRB; ++rb)
