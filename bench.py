@@ -59,10 +59,10 @@ def parse():
 # only while both are unchanged.
 TRAFFIC = {
     # kernel: (source file, SHA-256 prefix of that file and of common.hpp, bytes per launch)
-    "gate_up": ("gemm_fwd.hip", "6257e4bbc758d085", "4bbb1e5bcd556976", 820.8e6),
-    "down": ("gemm_fwd.hip", "6257e4bbc758d085", "4bbb1e5bcd556976", 352.0e6),
-    "bwd_down": ("gemm_bwd.hip", "4aa0105deb281225", "4bbb1e5bcd556976", 606.5e6),
-    "bwd_gate_up": ("gemm_bwd.hip", "4aa0105deb281225", "4bbb1e5bcd556976", 769.9e6),
+    "gate_up": ("gemm_fwd.hip", "6257e4bbc758d085", "4bbb1e5bcd556976", 818.7e6),
+    "down": ("gemm_fwd.hip", "6257e4bbc758d085", "4bbb1e5bcd556976", 352.1e6),
+    "bwd_down": ("gemm_bwd.hip", "fee408d81a700fad", "4bbb1e5bcd556976", 560.3e6),
+    "bwd_gate_up": ("gemm_bwd.hip", "fee408d81a700fad", "4bbb1e5bcd556976", 710.7e6),
 }
 
 
