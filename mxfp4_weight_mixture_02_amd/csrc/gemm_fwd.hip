@@ -79,9 +79,11 @@ __device__ constexpr int vmcnt_imm(int n) { return waitcnt_imm(n, 15); }
 // are used).
 constexpr int XCH_MAX = 4;
 struct FwdPipe {
-  const uint16_t* xrow[XCH_MAX];   // activation rows this lane stages
+  const uint16_t* xbase;           // activations (workgroup-uniform)
+  uint32_t xrow[XCH_MAX];          // element offsets of the rows this lane stages
   int xcol[XCH_MAX];               // element offset of its 16-byte slot within a step
-  const uint8_t* wp[FRB];          // this lane's codes per row block (+ lane half)
+  const uint8_t* wbase;            // the expert's codes (workgroup-uniform)
+  uint32_t wp[FRB];                // byte offsets of this lane's codes per row block (+ lane half)
   const uint8_t* srow[FRB];        // its scale panel rows in LDS
   uint8_t* xs;                     // LDS stages
   int nsteps;
@@ -96,13 +98,13 @@ __device__ __forceinline__ void fwd_issue(const FwdPipe& p, Codes& codes, int c)
   const int wave = threadIdx.x >> 6;
 #pragma unroll
   for (int j = 0; j < XCH; ++j)
-    __builtin_amdgcn_global_load_lds(p.xrow[j] + c * FKS + p.xcol[j],
+    __builtin_amdgcn_global_load_lds(p.xbase + (p.xrow[j] + (uint32_t)(c * FKS + p.xcol[j])),
                                      p.xs + SL * XSTAGE + (XCH * wave + j) * 1024, 16, 0, 0);
   // the counted waits below assume this issue order: activations, then codes
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int rb = 0; rb < FRB; ++rb)
-    codes[SL][rb] = *reinterpret_cast<const u32x4*>(p.wp[rb] + c * 32);
+    codes[SL][rb] = *reinterpret_cast<const u32x4*>(p.wbase + (p.wp[rb] + (uint32_t)c * 32));
 }
 
 template <int W, int SL, int NRB, class Codes>
@@ -195,7 +197,7 @@ __device__ __forceinline__ void fwd_loop(const FwdPipe& p, f32x16 (&acc)[FRB][4]
 // workgroup's rows (row blocks follow 32 rows apart; clamped for waves past
 // N).
 template <int W>
-__device__ __forceinline__ void fwd_body(const uint16_t* const* xrow,
+__device__ __forceinline__ void fwd_body(const uint16_t* xbase, const uint32_t* xrow,
                                          const uint8_t* __restrict__ codes_e,
                                          const uint8_t* __restrict__ scales_e, int K, int n0,
                                          int nrows, int wrow_local, int nrb, uint8_t* lds,
@@ -234,9 +236,11 @@ __device__ __forceinline__ void fwd_body(const uint16_t* const* xrow,
 #pragma unroll
   for (int rb = 0; rb < FRB; ++rb) {
     const int r = min(wrow_local + 32 * rb, nrows - 1);
-    p.wp[rb] = codes_e + (int64_t)(n0 + r) * rowbytes + hlf * 16;
+    p.wp[rb] = (uint32_t)(n0 + r) * (uint32_t)rowbytes + hlf * 16;
     p.srow[rb] = panel + r * KB32;
   }
+  p.xbase = xbase;
+  p.wbase = codes_e;
   p.xs = lds;
   p.nsteps = K / FKS;
   switch (nrb) {
@@ -288,16 +292,16 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   const int l32 = lane & 31, hlf = lane >> 5;
   const int e = tl.expert;
 
-  const uint16_t* xrow[XCHUNKS];
+  uint32_t xrow[XCHUNKS];   // element offsets into x (T * H < 2^31)
 #pragma unroll
   for (int j = 0; j < XCHUNKS; ++j) {
     const int r = (XCHUNKS * wave + j) * 8 + lane / 8;
     const int f = sorted_rows[tl.row0 + (r < tl.rows ? r : 0)];
-    xrow[j] = x + (int64_t)(f / k) * H;
+    xrow[j] = (uint32_t)(f / k) * (uint32_t)H;
   }
   const int nrows = min(FNT, N - n0);
   f32x16 acc[FRB][4];
-  fwd_body<W>(xrow, codes + (int64_t)e * N * (H / 2), scales + (int64_t)e * N * (H / 32), H, n0,
+  fwd_body<W>(x, xrow, codes + (int64_t)e * N * (H / 2), scales + (int64_t)e * N * (H / 32), H, n0,
            nrows, (wave * 32 * FRB < nrows ? wave * 32 * FRB : 0) + l32, (tl.rows + 31) / 32, lds,
            acc);
   // Epilogue through LDS: every wave's loads have landed (fwd_loop drained
@@ -375,16 +379,16 @@ __global__ __launch_bounds__(FwdShape<8>::NTHR) void down_kernel(
   const int l32 = lane & 31, hlf = lane >> 5;
   const int e = tl.expert;
 
-  const uint16_t* xrow[XCHUNKS];
+  uint32_t xrow[XCHUNKS];   // element offsets from the tile's first row of a
 #pragma unroll
   for (int j = 0; j < XCHUNKS; ++j) {
     const int r = (XCHUNKS * wave + j) * 8 + lane / 8;
-    xrow[j] = a + (int64_t)(tl.row0 + (r < tl.rows ? r : 0)) * I;
+    xrow[j] = (uint32_t)(r < tl.rows ? r : 0) * (uint32_t)I;
   }
   const int nrows = min(FNT, N - n0);
   f32x16 acc[FRB][4];
   const int wrow_local = (wave * 32 * FRB < nrows ? wave * 32 * FRB : 0) + l32;
-  fwd_body<8>(xrow, codes + (int64_t)e * N * (I / 2), scales + (int64_t)e * N * (I / 32), I, n0,
+  fwd_body<8>(a + (int64_t)tl.row0 * I, xrow, codes + (int64_t)e * N * (I / 2), scales + (int64_t)e * N * (I / 32), I, n0,
            nrows, wrow_local, (tl.rows + 31) / 32, lds, acc);
   if (LORA) {
     // + s v B_e^T: one more 16-deep contraction over the rank, A-operand =
