@@ -59,10 +59,10 @@ def parse():
 # only while both are unchanged.
 TRAFFIC = {
     # kernel: (source file, SHA-256 prefix of that file and of common.hpp, bytes per launch)
-    "gate_up": ("gemm_fwd.hip", "6257e4bbc758d085", "4bbb1e5bcd556976", 818.7e6),
-    "down": ("gemm_fwd.hip", "6257e4bbc758d085", "4bbb1e5bcd556976", 352.1e6),
-    "bwd_down": ("gemm_bwd.hip", "fee408d81a700fad", "4bbb1e5bcd556976", 560.3e6),
-    "bwd_gate_up": ("gemm_bwd.hip", "fee408d81a700fad", "4bbb1e5bcd556976", 710.7e6),
+    "gate_up": ("gemm_fwd.hip", "6257e4bbc758d085", "0346944025f84710", 818.7e6),
+    "down": ("gemm_fwd.hip", "6257e4bbc758d085", "0346944025f84710", 352.1e6),
+    "bwd_down": ("gemm_bwd.hip", "fee408d81a700fad", "0346944025f84710", 560.3e6),
+    "bwd_gate_up": ("gemm_bwd.hip", "fee408d81a700fad", "0346944025f84710", 710.7e6),
 }
 
 

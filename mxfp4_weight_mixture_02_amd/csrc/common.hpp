@@ -192,8 +192,6 @@ __device__ __forceinline__ bool xcd_work_item(int live_row_tiles, int col_tiles,
 }
 
 constexpr int MT = 128;      // routed rows per GEMM tile
-constexpr int KC = 64;       // K elements per main-loop step
-constexpr int LDS_ROW = 72;  // bf16 per staged row (64 + 8 padding)
 constexpr int LORA_R = 16;   // supported LoRA rank: one 16-deep MFMA contraction
 
 }  // namespace mxmoe
