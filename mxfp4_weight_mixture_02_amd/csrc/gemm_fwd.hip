@@ -109,30 +109,65 @@ __device__ __forceinline__ void fwd_issue(const FwdPipe& p, Codes& codes, int c)
 
 template <int W, int SL, int NRB, class Codes>
 __device__ __forceinline__ void fwd_compute(const FwdPipe& p, const Codes& codes, int c,
-                                            f32x16 (&acc)[FRB][4]) {
+                                            float (&sc)[FRB], f32x16 (&acc)[FRB][4]) {
   const int lane = threadIdx.x & 63;
   const int l32 = lane & 31, hlf = lane >> 5;
-  float sc[FRB];
-#pragma unroll
-  for (int rb = 0; rb < FRB; ++rb) sc[rb] = scale_operand(p.srow[rb][2 * c + hlf]);
   const uint8_t* st = p.xs + SL * XSTAGE;
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
+  // Sub-step s's B-operand fragments and decoded weights are double
+  // buffered: sub-step s + 1's LDS reads and decodes are issued while the
+  // MFMAs of sub-step s run, so neither the LDS latency nor the conversions
+  // sit between two MFMAs.
+  bf16x8 b[2][NRB], a[2][FRB];
+  auto read_b = [&](int s, bf16x8(&bb)[NRB]) {
     const int g = 4 * hlf + s;
-    bf16x8 b[NRB];
 #pragma unroll
     for (int tb = 0; tb < NRB; ++tb) {
       const int r = tb * 32 + l32;
-      b[tb] = *reinterpret_cast<const bf16x8*>(st + r * 128 + 16 * (g ^ ((r >> 1) & 7)));
+      bb[tb] = *reinterpret_cast<const bf16x8*>(st + r * 128 + 16 * (g ^ ((r >> 1) & 7)));
+    }
+  };
+  read_b(0, b[0]);
+#pragma unroll
+  for (int rb = 0; rb < FRB; ++rb) a[0][rb] = as_bf16x8(dequant8_bf16(codes[SL][rb][0], sc[rb]));
+  __builtin_amdgcn_sched_barrier(0);
+  uint32_t scn[FRB];   // the next step's scale bytes (the panel never changes)
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int cur = s & 1, nxt = cur ^ 1;
+    if (s < 3) read_b(s + 1, b[nxt]);
+    if (s == 1) {
+      const int cn = min(c + 1, p.nsteps - 1);
+#pragma unroll
+      for (int rb = 0; rb < FRB; ++rb) scn[rb] = p.srow[rb][2 * cn + hlf];
     }
 #pragma unroll
-    for (int rb = 0; rb < FRB; ++rb) {
-      const bf16x8 a = as_bf16x8(dequant8_bf16(codes[SL][rb][s], sc[rb]));
+    for (int rb = 0; rb < FRB; ++rb)
 #pragma unroll
       for (int tb = 0; tb < NRB; ++tb)
-        acc[rb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[tb], acc[rb][tb], 0, 0, 0);
+        acc[rb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cur][rb], b[cur][tb], acc[rb][tb], 0, 0, 0);
+    if (s < 3) {
+#pragma unroll
+      for (int rb = 0; rb < FRB; ++rb)
+        a[nxt][rb] = as_bf16x8(dequant8_bf16(codes[SL][rb][s + 1], sc[rb]));
+      // issue order: one MFMA, the next sub-step's LDS reads, then each
+      // further MFMA followed by its share of the next sub-step's conversions
+      constexpr int NM = FRB * NRB, NV = 4 * FRB;
+      constexpr int PER = (NV + NM - 2) / (NM > 1 ? NM - 1 : 1);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (s == 1)
+        __builtin_amdgcn_sched_group_barrier(0x100, NRB + FRB, 0);
+      else
+        __builtin_amdgcn_sched_group_barrier(0x100, NRB, 0);
+#pragma unroll
+      for (int i = 1; i < NM; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if ((i - 1) * PER < NV) __builtin_amdgcn_sched_group_barrier(0x002, PER, 0);
+      }
     }
+    __builtin_amdgcn_sched_barrier(0);
   }
+#pragma unroll
+  for (int rb = 0; rb < FRB; ++rb) sc[rb] = scale_operand(scn[rb]);
 }
 
 // One pipeline step: issue step c + NST - 1, compute step c, wait for this
@@ -143,12 +178,12 @@ __device__ __forceinline__ void fwd_compute(const FwdPipe& p, const Codes& codes
 // activations) keeps the compiler's own wait for the code registers from
 // falling back to a full drain at the top of the unrolled loop.
 template <int W, int SL, int NRB, class Codes>
-__device__ __forceinline__ void fwd_step(const FwdPipe& p, Codes& codes, int c,
+__device__ __forceinline__ void fwd_step(const FwdPipe& p, Codes& codes, int c, float (&sc)[FRB],
                                          f32x16 (&acc)[FRB][4]) {
   constexpr int NST = FwdShape<W>::NST;
   fwd_issue<W, (SL + NST - 1) % NST>(p, codes, min(c + NST - 1, p.nsteps - 1));
   __builtin_amdgcn_sched_barrier(0);
-  fwd_compute<W, SL, NRB>(p, codes, c, acc);
+  fwd_compute<W, SL, NRB>(p, codes, c, sc, acc);
   __builtin_amdgcn_sched_barrier(0);
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(FwdShape<W>::LPS * (NST - 2)));
   barrier_only();
@@ -175,18 +210,22 @@ __device__ __forceinline__ void fwd_loop(const FwdPipe& p, f32x16 (&acc)[FRB][4]
   // the scale panel was written with ordinary LDS stores
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(FwdShape<W>::LPS * (NST - 2), 0));
   barrier_only();
+  const int hlf = (threadIdx.x & 63) >> 5;
+  float sc[FRB];
+#pragma unroll
+  for (int rb = 0; rb < FRB; ++rb) sc[rb] = scale_operand(p.srow[rb][hlf]);
   int c = 0;
   for (; c + NST <= p.nsteps; c += NST) {
-    fwd_step<W, 0, NRB>(p, codes, c + 0, acc);
-    fwd_step<W, 1, NRB>(p, codes, c + 1, acc);
-    fwd_step<W, 2, NRB>(p, codes, c + 2, acc);
-    if constexpr (NST == 4) fwd_step<W, 3, NRB>(p, codes, c + 3, acc);
+    fwd_step<W, 0, NRB>(p, codes, c + 0, sc, acc);
+    fwd_step<W, 1, NRB>(p, codes, c + 1, sc, acc);
+    fwd_step<W, 2, NRB>(p, codes, c + 2, sc, acc);
+    if constexpr (NST == 4) fwd_step<W, 3, NRB>(p, codes, c + 3, sc, acc);
   }
   const int rem = p.nsteps - c;
-  if (rem > 0) fwd_step<W, 0, NRB>(p, codes, c + 0, acc);
-  if (rem > 1) fwd_step<W, 1, NRB>(p, codes, c + 1, acc);
+  if (rem > 0) fwd_step<W, 0, NRB>(p, codes, c + 0, sc, acc);
+  if (rem > 1) fwd_step<W, 1, NRB>(p, codes, c + 1, sc, acc);
   if constexpr (NST == 4)
-    if (rem > 2) fwd_step<W, 2, NRB>(p, codes, c + 2, acc);
+    if (rem > 2) fwd_step<W, 2, NRB>(p, codes, c + 2, sc, acc);
   // drain: nothing may still be writing LDS when the workgroup ends
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 }
