@@ -39,7 +39,7 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=16)
@@ -59,8 +59,8 @@ def parse():
 # only while both are unchanged.
 TRAFFIC = {
     # kernel: (source file, SHA-256 prefix of that file and of common.hpp, bytes per launch)
-    "gate_up": ("gemm_fwd.hip", "6257e4bbc758d085", "0346944025f84710", 818.7e6),
-    "down": ("gemm_fwd.hip", "6257e4bbc758d085", "0346944025f84710", 352.1e6),
+    "gate_up": ("gemm_fwd.hip", "b311ed8b3923a77e", "0346944025f84710", 834.3e6),
+    "down": ("gemm_fwd.hip", "b311ed8b3923a77e", "0346944025f84710", 346.0e6),
     "bwd_down": ("gemm_bwd.hip", "fee408d81a700fad", "0346944025f84710", 560.3e6),
     "bwd_gate_up": ("gemm_bwd.hip", "fee408d81a700fad", "0346944025f84710", 710.7e6),
 }
