@@ -17,15 +17,18 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float((uint32_t)b << 16);
 }
 
-// fp32 -> bf16 bits, round to nearest even (inputs are finite).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// fp32 -> bf16 bits, round to nearest even: gfx950's conversion instruction
+// (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
+// Two fp32 -> packed bf16 (lo in the low half), one conversion instruction.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
 // UE8M0 scale byte -> the fp32 operand of the scaled fp4 conversions.  The
@@ -80,11 +83,19 @@ __device__ __forceinline__ uint32_t saved_preact_bf16(float v, float limit, bool
   return b;
 }
 
+// Logistic sigmoid from the hardware base-2 exponential and reciprocal
+// (v_exp_f32, v_rcp_f32; about 1 ulp each).  Every caller rounds its result
+// to bf16 (2^-9 relative), so the library expf and a correctly rounded
+// division would only cost instructions.  z -> -inf gives 1/inf = 0.
+__device__ __forceinline__ float sigmoid_hw(float z) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * 1.4426950408889634f));
+}
+
 // Clamped SwiGLU of GPT-OSS: gate clamped above, up clamped both sides.
 __device__ __forceinline__ float swiglu(float g, float u, float alpha, float limit) {
   float gc = fminf(g, limit);
   float uc = fminf(fmaxf(u, -limit), limit);
-  float sig = 1.0f / (1.0f + expf(-alpha * gc));
+  float sig = sigmoid_hw(alpha * gc);
   return gc * sig * (uc + 1.0f);
 }
 
@@ -93,7 +104,7 @@ __device__ __forceinline__ void swiglu_grad(float g, float u, float da, float al
                                             float* dg, float* du) {
   float gc = fminf(g, limit);
   float uc = fminf(fmaxf(u, -limit), limit);
-  float sig = 1.0f / (1.0f + expf(-alpha * gc));
+  float sig = sigmoid_hw(alpha * gc);
   float dgc = da * (uc + 1.0f) * sig * (1.0f + alpha * gc * (1.0f - sig));
   float duc = da * gc * sig;
   *dg = (g <= limit) ? dgc : 0.0f;
