@@ -125,6 +125,26 @@ typedef struct mxfp4_moe_saved {
   float* lora_v;
 } mxfp4_moe_saved;
 
+/* Byte sizes of the saved-state buffers for given dims (one field per
+ * mxfp4_moe_saved buffer, same order; lora_v is 0 when lora_rank == 0).
+ * The caller allocates them (each 16-byte aligned) and passes their
+ * addresses in mxfp4_moe_saved; the library never allocates them ([P1]
+ * "What this does": the transients belong to the caller's framework). */
+typedef struct mxfp4_moe_saved_sizes {
+  size_t topk_idx;
+  size_t topk_w;
+  size_t expert_offsets;
+  size_t sorted_rows;
+  size_t h;
+  size_t a;
+  size_t lora_v;
+} mxfp4_moe_saved_sizes;
+
+/* Fills *out for dims.  Returns MXFP4_OK, MXFP4_EINVAL (null out, or dims
+ * with a count < 1) or MXFP4_EUNSUPPORTED (dims outside the contract); on
+ * an error *out is left untouched. */
+int mxfp4_moe_saved_bytes(const mxfp4_moe_dims* dims, mxfp4_moe_saved_sizes* out);
+
 /* Workspace modes for mxfp4_moe_workspace_bytes. */
 #define MXFP4_WS_FORWARD 0        /* mxfp4_moe_forward, saved == NULL */
 #define MXFP4_WS_FORWARD_SAVED 1  /* mxfp4_moe_forward, saved != NULL */

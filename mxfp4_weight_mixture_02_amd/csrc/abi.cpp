@@ -257,6 +257,24 @@ size_t mxfp4_moe_workspace_bytes(const mxfp4_moe_dims* dims, int mode) {
   return layout(*dims, mode).total;
 }
 
+int mxfp4_moe_saved_bytes(const mxfp4_moe_dims* dims, mxfp4_moe_saved_sizes* out) {
+  const int rc = check_dims(dims);
+  if (rc) return rc;
+  if (!out) return fail(MXFP4_EINVAL, "out is required");
+  const mxfp4_moe_dims& d = *dims;
+  const size_t T = (size_t)d.T, R = T * (size_t)d.k, I = (size_t)d.I;
+  mxfp4_moe_saved_sizes z;
+  z.topk_idx = T * d.k * sizeof(int32_t);
+  z.topk_w = T * d.k * sizeof(float);
+  z.expert_offsets = ((size_t)d.E + 1) * sizeof(int32_t);
+  z.sorted_rows = R * sizeof(int32_t);
+  z.h = R * 2 * I * sizeof(uint16_t);
+  z.a = R * I * sizeof(uint16_t);
+  z.lora_v = R * (size_t)d.lora_rank * sizeof(float);
+  *out = z;
+  return ok();
+}
+
 int mxfp4_moe_forward(const mxfp4_moe_dims* dims, const mxfp4_moe_weights* w, const uint16_t* x,
                       uint16_t* out, const mxfp4_moe_saved* saved, void* workspace,
                       size_t workspace_bytes, void* stream) {

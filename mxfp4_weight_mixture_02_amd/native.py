@@ -47,6 +47,10 @@ class Saved(ctypes.Structure):
                 ("topk_idx", "topk_w", "expert_offsets", "sorted_rows", "h", "a", "lora_v")]
 
 
+class SavedSizes(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n, _ in Saved._fields_]
+
+
 _lib = None
 
 
@@ -63,6 +67,8 @@ def lib() -> ctypes.CDLL:
         L.mxfp4_last_error.argtypes = []
         L.mxfp4_moe_workspace_bytes.restype = ctypes.c_size_t
         L.mxfp4_moe_workspace_bytes.argtypes = [ctypes.POINTER(Dims), i32]
+        L.mxfp4_moe_saved_bytes.restype = i32
+        L.mxfp4_moe_saved_bytes.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(SavedSizes)]
         L.mxfp4_moe_forward.restype = i32
         L.mxfp4_moe_forward.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Weights), vp, vp,
                                         ctypes.POINTER(Saved), vp, ctypes.c_size_t, vp]
@@ -189,16 +195,24 @@ class SavedState:
 
     @staticmethod
     def empty(layer: MoeLayer, T: int, device):
+        """Caller-owned buffers of the sizes mxfp4_moe_saved_bytes gives."""
         R = T * layer.k
         r = 0 if layer.lora_A is None else layer.lora_A.shape[1]
-        return SavedState(
-            torch.empty((T, layer.k), dtype=torch.int32, device=device),
-            torch.empty((T, layer.k), dtype=torch.float32, device=device),
-            torch.empty((layer.E + 1,), dtype=torch.int32, device=device),
-            torch.empty((R,), dtype=torch.int32, device=device),
-            torch.empty((R, 2 * layer.I), dtype=torch.bfloat16, device=device),
-            torch.empty((R, layer.I), dtype=torch.bfloat16, device=device),
-            torch.empty((R, r), dtype=torch.float32, device=device) if r else None)
+        nbytes = saved_bytes(layer, T)
+        shapes = {"topk_idx": ((T, layer.k), torch.int32), "topk_w": ((T, layer.k), torch.float32),
+                  "expert_offsets": ((layer.E + 1,), torch.int32), "sorted_rows": ((R,), torch.int32),
+                  "h": ((R, 2 * layer.I), torch.bfloat16), "a": ((R, layer.I), torch.bfloat16),
+                  "lora_v": ((R, r), torch.float32)}
+        bufs = {}
+        for n, (shape, dt) in shapes.items():
+            if nbytes[n] == 0:
+                bufs[n] = None
+                continue
+            t = torch.empty(shape, dtype=dt, device=device)
+            if t.numel() * t.element_size() != nbytes[n]:
+                raise Mxfp4Error("mxfp4_moe_saved_bytes", -1, f"{n}: {nbytes[n]} bytes, shape {shape}")
+            bufs[n] = t
+        return SavedState(**bufs)
 
     def struct(self):
         return Saved(*[_ptr(getattr(self, n)) for n, _ in Saved._fields_])
@@ -217,6 +231,14 @@ class Workspace:
 
 
 _WS = Workspace()
+
+
+def saved_bytes(layer: MoeLayer, T: int) -> dict:
+    """Byte size of each saved-state buffer (mxfp4_moe_saved_bytes)."""
+    d = layer.dims(T)
+    z = SavedSizes()
+    _check("mxfp4_moe_saved_bytes", lib().mxfp4_moe_saved_bytes(ctypes.byref(d), ctypes.byref(z)))
+    return {n: getattr(z, n) for n, _ in SavedSizes._fields_}
 
 
 def workspace_bytes(layer: MoeLayer, T: int, mode: int) -> int:
