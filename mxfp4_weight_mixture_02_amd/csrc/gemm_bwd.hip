@@ -456,75 +456,88 @@ __global__ __launch_bounds__(BTHR) void bwd_gate_up_kernel(
 // reads dY and the slots' bias rows in 16-byte pieces, one batch of k + 1
 // loads per piece (2-byte loads in a "load, use" loop paid a memory round
 // trip per element group), and the dw partials go through LDS.
+template <int K>
 __global__ __launch_bounds__(256) void bwd_combine_kernel(
     const uint16_t* __restrict__ dy, const float* __restrict__ dxr,
     const float* __restrict__ dw_part, int n_dw_part, const int32_t* __restrict__ topk_idx,
     const float* __restrict__ topk_w, const uint16_t* __restrict__ dn_bias,
-    const float* __restrict__ router_w, int H, int k, uint16_t* __restrict__ dx) {
-  __shared__ float red[4][8];
-  __shared__ float dl[8];
-  __shared__ int32_t ex[8];
-  __shared__ float dwps[8 * 16];
+    const float* __restrict__ router_w, int H, uint16_t* __restrict__ dx) {
+  __shared__ float red[4][K];
+  __shared__ float dl[K];
+  __shared__ int32_t ex[K];
+  __shared__ float dwps[K * 20];   // k slots x ceil(I / 256) <= 20 column tiles
   const int64_t t = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (tid < k) ex[tid] = topk_idx[t * k + tid];
-  for (int q = tid; q < k * n_dw_part; q += 256) dwps[q] = dw_part[t * k * n_dw_part + q];
-  __syncthreads();
-  float part[8];
+  const int H4 = H / 4;
+  // this thread's first piece of every slot's dxr, loaded before the bias
+  // dot so its latency overlaps that phase (index clamped; used only when
+  // the piece exists)
+  f32x4 v0[K];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) part[j] = 0.0f;
+  for (int j = 0; j < K; ++j)
+    v0[j] = reinterpret_cast<const f32x4*>(dxr + (t * K + j) * H)[min(tid, H4 - 1)];
+  if (tid < K) ex[tid] = topk_idx[t * K + tid];
+  for (int q = tid; q < K * n_dw_part; q += 256) dwps[q] = dw_part[t * K * n_dw_part + q];
+  __syncthreads();
+  float part[K];
+#pragma unroll
+  for (int j = 0; j < K; ++j) part[j] = 0.0f;
   if (dn_bias) {
     for (int c = tid; c < H / 8; c += 256) {
       const u32x4 g = reinterpret_cast<const u32x4*>(dy + t * H)[c];
-      u32x4 b[8];
+      u32x4 b[K];
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        if (j < k) b[j] = reinterpret_cast<const u32x4*>(dn_bias + (int64_t)ex[j] * H)[c];
+      for (int j = 0; j < K; ++j) b[j] = reinterpret_cast<const u32x4*>(dn_bias + (int64_t)ex[j] * H)[c];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if (j < k) {
+      for (int j = 0; j < K; ++j) {
 #pragma unroll
-          for (int m = 0; m < 4; ++m) {
-            part[j] += bf16_to_f32((uint16_t)(g[m] & 0xFFFFu)) * bf16_to_f32((uint16_t)(b[j][m] & 0xFFFFu));
-            part[j] += bf16_to_f32((uint16_t)(g[m] >> 16)) * bf16_to_f32((uint16_t)(b[j][m] >> 16));
-          }
+        for (int m = 0; m < 4; ++m) {
+          part[j] += bf16_to_f32((uint16_t)(g[m] & 0xFFFFu)) * bf16_to_f32((uint16_t)(b[j][m] & 0xFFFFu));
+          part[j] += bf16_to_f32((uint16_t)(g[m] >> 16)) * bf16_to_f32((uint16_t)(b[j][m] >> 16));
         }
       }
     }
   }
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    if (j < k) {
-      float v = part[j];
-      for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-      if (lane == 0) red[wave][j] = v;
-    }
+  for (int j = 0; j < K; ++j) {
+    float v = part[j];
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    if (lane == 0) red[wave][j] = v;
   }
   __syncthreads();
   if (tid == 0) {
-    float dw[8], w[8], sw = 0.0f;
-    for (int j = 0; j < k; ++j) {
+    float dw[K], w[K], sw = 0.0f;
+    for (int j = 0; j < K; ++j) {
       float s = red[0][j] + red[1][j] + red[2][j] + red[3][j];
       for (int q = 0; q < n_dw_part; ++q) s += dwps[j * n_dw_part + q];
       dw[j] = s;
-      w[j] = topk_w[t * k + j];
+      w[j] = topk_w[t * K + j];
       sw += w[j] * s;
     }
-    for (int j = 0; j < k; ++j) dl[j] = w[j] * (dw[j] - sw);
+    for (int j = 0; j < K; ++j) dl[j] = w[j] * (dw[j] - sw);
   }
   __syncthreads();
-  const int H4 = H / 4;
-  for (int c = tid; c < H4; c += 256) {
+  // dX piece c from the slots' dxr pieces v, in slot order
+  auto emit = [&](int c, const f32x4 (&v)[K]) {
+    f32x4 r[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) r[j] = reinterpret_cast<const f32x4*>(router_w + (int64_t)ex[j] * H)[c];
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; ++j) {
-      const f32x4 v = reinterpret_cast<const f32x4*>(dxr + (t * k + j) * H)[c];
-      const f32x4 r = reinterpret_cast<const f32x4*>(router_w + (int64_t)ex[j] * H)[c];
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
       const float d = dl[j];
 #pragma unroll
-      for (int m = 0; m < 4; ++m) s[m] += v[m] + d * r[m];
+      for (int m = 0; m < 4; ++m) s[m] += v[j][m] + d * r[j][m];
     }
     u32x2 o = {pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3])};
     reinterpret_cast<u32x2*>(dx + t * H)[c] = o;
+  };
+  if (tid < H4) emit(tid, v0);
+  for (int c = tid + 256; c < H4; c += 256) {
+    f32x4 v[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) v[j] = reinterpret_cast<const f32x4*>(dxr + (t * K + j) * H)[c];
+    emit(c, v);
   }
 }
 
@@ -564,8 +577,18 @@ hipError_t launch_bwd_combine(const uint16_t* dy, const float* dxr, const float*
                               int n_dw_part, const int32_t* topk_idx, const float* topk_w,
                               const uint16_t* dn_bias, const float* router_w, int64_t T, int H,
                               int k, uint16_t* dx, hipStream_t s) {
-  hipLaunchKernelGGL(bwd_combine_kernel, dim3((unsigned)T), dim3(256), 0, s, dy, dxr, dw_part,
-                     n_dw_part, topk_idx, topk_w, dn_bias, router_w, H, k, dx);
+  if (n_dw_part > 20) return hipErrorInvalidValue;
+#define BWD_COMBINE(KK)                                                                        \
+  case KK:                                                                                     \
+    hipLaunchKernelGGL(bwd_combine_kernel<KK>, dim3((unsigned)T), dim3(256), 0, s, dy, dxr,    \
+                       dw_part, n_dw_part, topk_idx, topk_w, dn_bias, router_w, H, dx);        \
+    break;
+  switch (k) {
+    BWD_COMBINE(1) BWD_COMBINE(2) BWD_COMBINE(3) BWD_COMBINE(4)
+    BWD_COMBINE(5) BWD_COMBINE(6) BWD_COMBINE(7) BWD_COMBINE(8)
+    default: return hipErrorInvalidValue;
+  }
+#undef BWD_COMBINE
   return hipGetLastError();
 }
 
