@@ -482,17 +482,22 @@ __global__ __launch_bounds__(FwdShape<8>::NTHR) void down_kernel(
   }
 }
 
-// out[t, :] = sum_j y_w[t*k + j, :] in slot order, rounded once to bf16.
+// out[t, :] = sum_j y_w[t*k + j, :] in slot order, rounded once to bf16
+// (K = k, a template parameter, so the slot loop unrolls without guards).
+template <int K>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y_w, int64_t n4,
-                                                      int H4, int k, uint16_t* __restrict__ out) {
+                                                      int H4, uint16_t* __restrict__ out) {
   int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n4) return;
   int64_t t = i / H4, c = i % H4;
-  const f32x4* src = reinterpret_cast<const f32x4*>(y_w) + t * k * H4 + c;
-  f32x4 s = src[0];
-  for (int j = 1; j < k; ++j) {
-    f32x4 v = src[(int64_t)j * H4];
-    s[0] += v[0]; s[1] += v[1]; s[2] += v[2]; s[3] += v[3];
+  const f32x4* src = reinterpret_cast<const f32x4*>(y_w) + t * K * H4 + c;
+  f32x4 v[K];
+#pragma unroll
+  for (int j = 0; j < K; ++j) v[j] = src[(int64_t)j * H4];
+  f32x4 s = v[0];
+#pragma unroll
+  for (int j = 1; j < K; ++j) {
+    s[0] += v[j][0]; s[1] += v[j][1]; s[2] += v[j][2]; s[3] += v[j][3];
   }
   u32x2 o = {pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3])};
   reinterpret_cast<u32x2*>(out)[i] = o;
@@ -541,8 +546,16 @@ hipError_t launch_down(const uint16_t* a, const uint8_t* codes, const uint8_t* s
 hipError_t launch_combine(const float* y_w, int64_t T, int H, int k, uint16_t* out,
                           hipStream_t s) {
   int64_t n4 = T * H / 4;
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, y_w,
-                     n4, H / 4, k, out);
+  const dim3 grid((unsigned)((n4 + 255) / 256));
+#define COMBINE(KK)                                                                      \
+  case KK:                                                                               \
+    hipLaunchKernelGGL(combine_kernel<KK>, grid, dim3(256), 0, s, y_w, n4, H / 4, out);  \
+    break;
+  switch (k) {
+    COMBINE(1) COMBINE(2) COMBINE(3) COMBINE(4) COMBINE(5) COMBINE(6) COMBINE(7) COMBINE(8)
+    default: return hipErrorInvalidValue;
+  }
+#undef COMBINE
   return hipGetLastError();
 }
 
