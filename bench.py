@@ -59,10 +59,10 @@ def parse():
 # only while both are unchanged.
 TRAFFIC = {
     # kernel: (source file, SHA-256 prefix of that file and of common.hpp, bytes per launch)
-    "gate_up": ("gemm_fwd.hip", "b311ed8b3923a77e", "06a63ec8e71d21b0", 830.3e6),
-    "down": ("gemm_fwd.hip", "b311ed8b3923a77e", "06a63ec8e71d21b0", 347.4e6),
-    "bwd_down": ("gemm_bwd.hip", "fee408d81a700fad", "06a63ec8e71d21b0", 559.0e6),
-    "bwd_gate_up": ("gemm_bwd.hip", "fee408d81a700fad", "06a63ec8e71d21b0", 710.7e6),
+    "gate_up": ("gemm_fwd.hip", "c6e403bf2e999f05", "06a63ec8e71d21b0", 832.6e6),
+    "down": ("gemm_fwd.hip", "c6e403bf2e999f05", "06a63ec8e71d21b0", 346.5e6),
+    "bwd_down": ("gemm_bwd.hip", "057a1fbac2e4ac76", "06a63ec8e71d21b0", 559.2e6),
+    "bwd_gate_up": ("gemm_bwd.hip", "057a1fbac2e4ac76", "06a63ec8e71d21b0", 710.9e6),
 }
 
 
