@@ -148,6 +148,16 @@ def test_ragged_token_counts(T):
     _run_layer(syn.spec("tiny"), T=T)
 
 
+@pytest.mark.parametrize("T", [8, 9, 32, 33, 128, 129])
+def test_kernel_dispatch_boundaries(T):
+    # tiny layer, k = 2: R = T * k on both sides of every switch of the
+    # forward -- the K-split decode kernel (R <= 16), the decode kernels'
+    # activation groups of 8 (R <= 64) or 16, the decode kernels and the
+    # general GEMMs (R <= 256), and the one-workgroup routing plan (R <= 256)
+    _say(f"dispatch boundary T={T} R={2 * T}")
+    _run_layer(syn.spec("tiny"), T=T)
+
+
 def test_dense_special_case():
     _run_layer(syn.spec("tiny", E=1, k=1, T=40))
 
