@@ -328,9 +328,9 @@ int mxfp4_moe_forward(const mxfp4_moe_dims* dims, const mxfp4_moe_weights* w, co
   } else {
     LAUNCH(mxmoe::launch_logits(x, w->router_w, w->router_b, T, H, E, logits, s), "router_logits");
     LAUNCH(mxmoe::launch_topk(logits, T, E, k, topk_idx, topk_w, blk_hist, s), "router_topk");
-    LAUNCH(mxmoe::launch_scan(blk_hist, mxmoe::router_blocks(T), E, offsets, s), "scan");
+    LAUNCH(mxmoe::launch_scan(blk_hist, mxmoe::router_blocks(T), E, offsets, tiles, num_tiles, s),
+           "scan");
     LAUNCH(mxmoe::launch_scatter(topk_idx, blk_hist, T, k, E, sorted_rows, s), "scatter");
-    LAUNCH(mxmoe::launch_build_tiles(offsets, E, tiles, num_tiles, s), "tiles");
   }
   // few rows per expert: the weight-streaming decode kernels (no LoRA there)
   const bool decode = R <= DECODE_MAX_ROWS && !d.lora_rank && H <= mxmoe::dec_max_k() &&

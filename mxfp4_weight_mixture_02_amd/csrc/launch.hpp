@@ -35,7 +35,8 @@ hipError_t launch_plan_logits(const uint16_t* x, const float* wr, int T, int H, 
 hipError_t launch_plan(const double* part, const float* br, int T, int H, int E, int k,
                        int32_t* topk_idx, float* topk_w, int32_t* offsets, int32_t* sorted_rows,
                        Tile* tiles, int32_t* num_tiles, hipStream_t s);
-hipError_t launch_scan(int32_t* blk_hist, int nblk, int E, int32_t* offsets, hipStream_t s);
+hipError_t launch_scan(int32_t* blk_hist, int nblk, int E, int32_t* offsets, Tile* tiles,
+                       int32_t* num_tiles, hipStream_t s);   // also writes the tile list
 hipError_t launch_scatter(const int32_t* topk_idx, const int32_t* blk_base, int T, int k, int E,
                           int32_t* sorted_rows, hipStream_t s);
 int max_tiles(int64_t R, int E);

@@ -383,15 +383,48 @@ __global__ __launch_bounds__(1024) void plan_kernel(
   }
 }
 
+// Tiles of at most MT sorted rows, expert by expert, from the E + 1
+// offsets in LDS (offs); start is LDS scratch of E + 1 entries.  Called by
+// every thread of one workgroup; ends with the tile list written.
+__device__ __forceinline__ void write_tiles(const int32_t* offs, int E, int32_t* start,
+                                            Tile* __restrict__ tiles,
+                                            int32_t* __restrict__ num_tiles) {
+  const int tid = threadIdx.x;
+  if (tid == 0) {
+    int32_t run = 0;
+    for (int e = 0; e < E; ++e) {
+      start[e] = run;
+      run += (offs[e + 1] - offs[e] + MT - 1) / MT;
+    }
+    start[E] = run;
+    *num_tiles = run;
+  }
+  __syncthreads();
+  if (tid < E) {
+    const int32_t o = offs[tid], n = offs[tid + 1] - o;
+    for (int32_t q = 0; q * MT < n; ++q) {
+      Tile tl;
+      tl.expert = tid;
+      tl.row0 = o + q * MT;
+      tl.rows = min(MT, n - q * MT);
+      tl.pad = 0;
+      tiles[start[tid] + q] = tl;
+    }
+  }
+}
+
 // One workgroup of 1024 threads.  In place, blk_hist[b][e] becomes the
 // first sorted position of workgroup b's rows of expert e:
 // offsets[e] + sum_{b' < b} count[b'][e].  offsets = exclusive scan of the
 // expert totals (E + 1 entries).
 __global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ blk_hist, int nblk,
-                                                    int E, int32_t* __restrict__ offsets) {
+                                                    int E, int32_t* __restrict__ offsets,
+                                                    Tile* __restrict__ tiles,
+                                                    int32_t* __restrict__ num_tiles) {
   __shared__ int32_t part[1024];
   __shared__ int32_t total[256];
   __shared__ int32_t off[257];
+  __shared__ int32_t tstart[257];
   const int tid = threadIdx.x;
   const int C = 1024 / E;                    // chunks of workgroups
   const int per = (nblk + C - 1) / C;
@@ -427,6 +460,8 @@ __global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ blk_hi
   }
   __syncthreads();
   if (tid <= E) offsets[tid] = off[tid];
+  // the GEMMs' tile list from the offsets (no separate launch)
+  write_tiles(off, E, tstart, tiles, num_tiles);
   if (c < C) {
     int32_t run = off[e] + part[tid];
     const int b1 = min(nblk, (c + 1) * per);
@@ -471,7 +506,8 @@ __global__ __launch_bounds__(64) void scatter_kernel(const int32_t* __restrict__
 // of non-empty experts), and at most min(E, R) experts are non-empty.
 int max_tiles(int64_t R, int E) { return (int)((R + MT - 1) / MT + (R < E ? R : E)); }
 
-// Tiles of at most MT sorted rows, expert by expert (one workgroup).
+// Tiles of at most MT sorted rows, expert by expert (one workgroup), from
+// offsets in global memory (the backward rebuilds the forward's list).
 __global__ __launch_bounds__(256) void tiles_kernel(const int32_t* __restrict__ offsets, int E,
                                                     Tile* __restrict__ tiles,
                                                     int32_t* __restrict__ num_tiles) {
@@ -482,27 +518,7 @@ __global__ __launch_bounds__(256) void tiles_kernel(const int32_t* __restrict__ 
   // memory would pay a round trip per expert)
   for (int e = tid; e <= E; e += 256) offs[e] = offsets[e];
   __syncthreads();
-  if (tid == 0) {
-    int32_t run = 0;
-    for (int e = 0; e < E; ++e) {
-      start[e] = run;
-      run += (offs[e + 1] - offs[e] + MT - 1) / MT;
-    }
-    start[E] = run;
-    *num_tiles = run;
-  }
-  __syncthreads();
-  if (tid < E) {
-    int32_t o = offsets[tid], n = offsets[tid + 1] - o;
-    for (int32_t q = 0; q * MT < n; ++q) {
-      Tile tl;
-      tl.expert = tid;
-      tl.row0 = o + q * MT;
-      tl.rows = min(MT, n - q * MT);
-      tl.pad = 0;
-      tiles[start[tid] + q] = tl;
-    }
-  }
+  write_tiles(offs, E, start, tiles, num_tiles);
 }
 
 hipError_t launch_logits(const uint16_t* x, const float* wr, const float* br, int T, int H,
@@ -548,8 +564,10 @@ hipError_t launch_plan(const double* part, const float* br, int T, int H, int E,
   return hipGetLastError();
 }
 
-hipError_t launch_scan(int32_t* blk_hist, int nblk, int E, int32_t* offsets, hipStream_t s) {
-  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, blk_hist, nblk, E, offsets);
+hipError_t launch_scan(int32_t* blk_hist, int nblk, int E, int32_t* offsets, Tile* tiles,
+                       int32_t* num_tiles, hipStream_t s) {
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, blk_hist, nblk, E, offsets, tiles,
+                     num_tiles);
   return hipGetLastError();
 }
 
