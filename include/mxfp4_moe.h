@@ -164,7 +164,8 @@ size_t mxfp4_moe_workspace_bytes(const mxfp4_moe_dims* dims, int mode);
  *   h = x Wgu_e^T + bgu_e;  a = min(g,L) sig(alpha min(g,L)) (clamp(u,-L,L)+1)
  *       with g = h[2i], u = h[2i+1]
  *   y = a Wd_e^T + bd_e (+ lora_scale (a A_e^T) B_e^T)
- *   out[t] = sum_j w[t,j] y_(t,j)   (fp32 sum in slot order, then bf16)
+ *   out[t] = sum_j w[t,j] y_(t,j)   (each term w y rounded to bf16, then
+ *                                    an fp32 sum in slot order, then bf16)
  * x bf16 [T, H] in; out bf16 [T, H] out.  saved may be NULL (inference);
  * otherwise every buffer it names is written. */
 int mxfp4_moe_forward(const mxfp4_moe_dims* dims, const mxfp4_moe_weights* w,
@@ -179,7 +180,8 @@ int mxfp4_moe_forward(const mxfp4_moe_dims* dims, const mxfp4_moe_weights* w,
  *     da += dv A_e);  (dg, du) = SwiGLU'(h) * da (no gradient through a
  *     clamped input beyond its bound);  dx_f = dh Wgu_e
  *   router: dl_j = w_j (dw_j - sum_i w_i dw_i)
- *   dX[t] = sum_j dx_(t,j) + sum_j dl_j Wr[idx_j]          (bf16 out)
+ *   dX[t] = sum_j dx_(t,j) + sum_j dl_j Wr[idx_j]          (bf16 out;
+ *           each dx_(t,j) rounded to bf16, the sum taken in fp32)
  *   dA_e = sum_f dv_f^T a_f  [E, r, I];  dB_e = s sum_f (w_f dY_t)^T v_f
  *   [E, H, r]; both fp32, overwritten, required iff lora_rank > 0.
  * saved: the buffers a forward with the same dims, weights and x filled.

@@ -99,13 +99,13 @@ Layout layout(const mxfp4_moe_dims& d, int mode) {
     L.blk_hist = L.put((size_t)mxmoe::router_blocks(d.T) * d.E * 4);
     L.tiles = L.put((size_t)maxt * sizeof(mxmoe::Tile));
     L.num_tiles = L.put(4);
-    L.y_w = L.put(R * (size_t)d.H * 4);
+    L.y_w = L.put(R * (size_t)d.H * 2);
   } else {
     L.tiles = L.put((size_t)maxt * sizeof(mxmoe::Tile));
     L.num_tiles = L.put(4);
     L.dh = L.put(R * (size_t)d.I * 2 * 2);
     L.dw_part = L.put(R * (size_t)mxmoe::bwd_down_ntiles((int)d.I) * 4);
-    L.dxr = L.put(R * (size_t)d.H * 4);
+    L.dxr = L.put(R * (size_t)d.H * 2);
     if (d.lora_rank) {
       L.lora_At = L.put((size_t)d.E * d.I * d.lora_rank * 2);
       L.lora_Bt = L.put((size_t)d.E * d.H * d.lora_rank * 2);
@@ -312,7 +312,7 @@ int mxfp4_moe_forward(const mxfp4_moe_dims* dims, const mxfp4_moe_weights* w, co
   int32_t* blk_hist = at<int32_t>(workspace, L.blk_hist);
   mxmoe::Tile* tiles = at<mxmoe::Tile>(workspace, L.tiles);
   int32_t* num_tiles = at<int32_t>(workspace, L.num_tiles);
-  float* y_w = at<float>(workspace, L.y_w);
+  uint16_t* y_w = at<uint16_t>(workspace, L.y_w);
   float* lora_v = !d.lora_rank ? nullptr : saved ? saved->lora_v : at<float>(workspace, L.lora_v);
   const int maxt = mxmoe::max_tiles(R, E);
 
@@ -393,7 +393,7 @@ int mxfp4_moe_backward_dx(const mxfp4_moe_dims* dims, const mxfp4_moe_weights* w
   int32_t* num_tiles = at<int32_t>(workspace, L.num_tiles);
   uint16_t* dh = at<uint16_t>(workspace, L.dh);
   float* dw_part = at<float>(workspace, L.dw_part);
-  float* dxr = at<float>(workspace, L.dxr);
+  uint16_t* dxr = at<uint16_t>(workspace, L.dxr);
   const int maxt = mxmoe::max_tiles(R, E);
   const int r = d.lora_rank;
   uint16_t* lora_At = r ? at<uint16_t>(workspace, L.lora_At) : nullptr;

@@ -395,7 +395,7 @@ __global__ __launch_bounds__(BTHR) void bwd_gate_up_kernel(
     const uint16_t* __restrict__ dh, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, const int32_t* __restrict__ sorted_rows,
     const Tile* __restrict__ tiles, const int32_t* __restrict__ num_tiles, int H, int I,
-    float* __restrict__ dxr) {
+    uint16_t* __restrict__ dxr) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[BLDS];
   int mt, ot;
   const int otiles = (H + BNT - 1) / BNT;
@@ -423,7 +423,7 @@ __global__ __launch_bounds__(BTHR) void bwd_gate_up_kernel(
   // Epilogue through LDS (the main loop ended with a barrier).
   const int ow = o0 + wave * 32 * BRB;
   if (ow >= H) return;                        // H % 64 == 0: a wave's columns are all in or out
-  uint8_t* yst = lds + wave * 8192;           // 32 rows x 64 fp32 (256-byte rows)
+  uint8_t* yst = lds + wave * 4096;           // 32 rows x 64 bf16 (128-byte rows)
 #pragma unroll
   for (int tb = 0; tb < 4; ++tb) {
     if (tb * 32 >= tl.rows) break;
@@ -432,19 +432,18 @@ __global__ __launch_bounds__(BTHR) void bwd_gate_up_kernel(
     for (int rb = 0; rb < BRB; ++rb)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        f32x4 v;
-#pragma unroll
-        for (int m = 0; m < 4; ++m) v[m] = acc[rb][tb][4 * q + m];
-        *reinterpret_cast<f32x4*>(yst + stg_off<256>(l32, 8 * rb + 2 * q + hlf)) = v;
+        const f32x16& a = acc[rb][tb];
+        const u32x2 v = {pack_bf16x2(a[4 * q], a[4 * q + 1]), pack_bf16x2(a[4 * q + 2], a[4 * q + 3])};
+        *reinterpret_cast<u32x2*>(yst + stg_off<128>(l32, 4 * rb + q) + 8 * hlf) = v;
       }
     wave_lds_sync();
 #pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int r = it * 4 + (lane >> 4), c = lane & 15;
+    for (int it = 0; it < 4; ++it) {
+      const int r = it * 8 + (lane >> 3), c = lane & 7;
       const int rt = tb * 32 + r;
       const int64_t fr = __shfl(f, r);
-      const f32x4 v = *reinterpret_cast<const f32x4*>(yst + stg_off<256>(r, c));
-      if (rt < tl.rows) __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(dxr + fr * H + ow + 4 * c));
+      const u32x4 v = *reinterpret_cast<const u32x4*>(yst + stg_off<128>(r, c));
+      if (rt < tl.rows) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dxr + fr * H + ow + 8 * c));
     }
     wave_lds_sync();
   }
@@ -458,7 +457,7 @@ __global__ __launch_bounds__(BTHR) void bwd_gate_up_kernel(
 // trip per element group), and the dw partials go through LDS.
 template <int K>
 __global__ __launch_bounds__(256) void bwd_combine_kernel(
-    const uint16_t* __restrict__ dy, const float* __restrict__ dxr,
+    const uint16_t* __restrict__ dy, const uint16_t* __restrict__ dxr,
     const float* __restrict__ dw_part, int n_dw_part, const int32_t* __restrict__ topk_idx,
     const float* __restrict__ topk_w, const uint16_t* __restrict__ dn_bias,
     const float* __restrict__ router_w, int H, uint16_t* __restrict__ dx) {
@@ -472,10 +471,10 @@ __global__ __launch_bounds__(256) void bwd_combine_kernel(
   // this thread's first piece of every slot's dxr, loaded before the bias
   // dot so its latency overlaps that phase (index clamped; used only when
   // the piece exists)
-  f32x4 v0[K];
+  u32x2 v0[K];
 #pragma unroll
   for (int j = 0; j < K; ++j)
-    v0[j] = reinterpret_cast<const f32x4*>(dxr + (t * K + j) * H)[min(tid, H4 - 1)];
+    v0[j] = reinterpret_cast<const u32x2*>(dxr + (t * K + j) * H)[min(tid, H4 - 1)];
   if (tid < K) ex[tid] = topk_idx[t * K + tid];
   for (int q = tid; q < K * n_dw_part; q += 256) dwps[q] = dw_part[t * K * n_dw_part + q];
   __syncthreads();
@@ -517,8 +516,8 @@ __global__ __launch_bounds__(256) void bwd_combine_kernel(
     for (int j = 0; j < K; ++j) dl[j] = w[j] * (dw[j] - sw);
   }
   __syncthreads();
-  // dX piece c from the slots' dxr pieces v, in slot order
-  auto emit = [&](int c, const f32x4 (&v)[K]) {
+  // dX piece c from the slots' dxr pieces v (4 bf16 each), in slot order
+  auto emit = [&](int c, const u32x2 (&v)[K]) {
     f32x4 r[K];
 #pragma unroll
     for (int j = 0; j < K; ++j) r[j] = reinterpret_cast<const f32x4*>(router_w + (int64_t)ex[j] * H)[c];
@@ -527,16 +526,17 @@ __global__ __launch_bounds__(256) void bwd_combine_kernel(
     for (int j = 0; j < K; ++j) {
       const float d = dl[j];
 #pragma unroll
-      for (int m = 0; m < 4; ++m) s[m] += v[j][m] + d * r[j][m];
+      for (int m = 0; m < 4; ++m)
+        s[m] += bf16_to_f32((uint16_t)(v[j][m >> 1] >> (16 * (m & 1)))) + d * r[j][m];
     }
     u32x2 o = {pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3])};
     reinterpret_cast<u32x2*>(dx + t * H)[c] = o;
   };
   if (tid < H4) emit(tid, v0);
   for (int c = tid + 256; c < H4; c += 256) {
-    f32x4 v[K];
+    u32x2 v[K];
 #pragma unroll
-    for (int j = 0; j < K; ++j) v[j] = reinterpret_cast<const f32x4*>(dxr + (t * K + j) * H)[c];
+    for (int j = 0; j < K; ++j) v[j] = reinterpret_cast<const u32x2*>(dxr + (t * K + j) * H)[c];
     emit(c, v);
   }
 }
@@ -565,7 +565,7 @@ hipError_t launch_bwd_down(const uint16_t* dy, const uint8_t* codes, const uint8
 hipError_t launch_bwd_gate_up(const uint16_t* dh, const uint8_t* codes, const uint8_t* scales,
                               const int32_t* sorted_rows, const Tile* tiles,
                               const int32_t* num_tiles, int max_tiles, int H, int I,
-                              float* dxr, hipStream_t s) {
+                              uint16_t* dxr, hipStream_t s) {
   if ((2 * I) % BKC || H % 64) return hipErrorInvalidValue;
   dim3 grid(((H + BNT - 1) / BNT) * max_tiles);
   hipLaunchKernelGGL(bwd_gate_up_kernel, grid, dim3(BTHR), 0, s, dh, codes, scales, sorted_rows,
@@ -573,7 +573,7 @@ hipError_t launch_bwd_gate_up(const uint16_t* dh, const uint8_t* codes, const ui
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_combine(const uint16_t* dy, const float* dxr, const float* dw_part,
+hipError_t launch_bwd_combine(const uint16_t* dy, const uint16_t* dxr, const float* dw_part,
                               int n_dw_part, const int32_t* topk_idx, const float* topk_w,
                               const uint16_t* dn_bias, const float* router_w, int64_t T, int H,
                               int k, uint16_t* dx, hipStream_t s) {

@@ -65,7 +65,7 @@ __global__ __launch_bounds__(512) void dec_kernel(
     const uint16_t* __restrict__ bias, const float* __restrict__ topk_w,
     const int32_t* __restrict__ sorted_rows, const Tile* __restrict__ tiles,
     const int32_t* __restrict__ num_tiles, int K, int N, int k, int DG, float alpha, float limit,
-    uint16_t* __restrict__ h_out, uint16_t* __restrict__ a_out, float* __restrict__ y_w) {
+    uint16_t* __restrict__ h_out, uint16_t* __restrict__ a_out, uint16_t* __restrict__ y_w) {
   // LDS: the scale panel of the workgroup's weight rows [32 * wpb][K / 32]
   // (one contiguous span of the scale tensor, copied in 16-byte pieces), then
   // the activation group [DG][K + DEC_XPAD] bf16
@@ -151,10 +151,8 @@ __global__ __launch_bounds__(512) void dec_kernel(
           } else {
             const int64_t f = sorted_rows[rho];
             const float wf = topk_w[f];
-            f32x4 y;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) y[i] = wf * v[i];
-            *reinterpret_cast<f32x4*>(y_w + f * N + nb) = y;
+            const u32x2 y = {pack_bf16x2(wf * v[0], wf * v[1]), pack_bf16x2(wf * v[2], wf * v[3])};
+            *reinterpret_cast<u32x2*>(y_w + f * N + nb) = y;
           }
         }
       }
@@ -180,7 +178,7 @@ __global__ __launch_bounds__(64 * KW) void dec_ksplit_kernel(
     const float* __restrict__ topk_w, const int32_t* __restrict__ sorted_rows,
     const Tile* __restrict__ tiles, const int32_t* __restrict__ num_tiles, int K, int N, int k,
     int DG, float alpha, float limit, uint16_t* __restrict__ h_out, uint16_t* __restrict__ a_out,
-    float* __restrict__ y_w) {
+    uint16_t* __restrict__ y_w) {
   // LDS: scale panel [32][K / 32], then the activation group [DG][K + DEC_XPAD]
   // bf16, which the partial sums [KW][16][64] fp32 reuse after the MFMAs
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -280,10 +278,8 @@ __global__ __launch_bounds__(64 * KW) void dec_ksplit_kernel(
       } else {
         const int64_t f = sorted_rows[rho];
         const float wf = topk_w[f];
-        f32x4 y;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) y[i] = wf * v[i];
-        *reinterpret_cast<f32x4*>(y_w + f * N + nb) = y;
+        const u32x2 y = {pack_bf16x2(wf * v[0], wf * v[1]), pack_bf16x2(wf * v[2], wf * v[3])};
+        *reinterpret_cast<u32x2*>(y_w + f * N + nb) = y;
       }
     }
     __syncthreads();   // LDS is restaged for the next group
@@ -300,7 +296,7 @@ static hipError_t dec_launch_stream(int64_t R, int max_tiles, int K, int N, hipS
                              const uint16_t* bias, const float* topk_w,
                              const int32_t* sorted_rows, const Tile* tiles,
                              const int32_t* num_tiles, int k, float alpha, float limit,
-                             uint16_t* h_out, uint16_t* a_out, float* y_w) {
+                             uint16_t* h_out, uint16_t* a_out, uint16_t* y_w) {
   if (K % 64 || K > DEC_MAXK || N % 32) return hipErrorInvalidValue;
   const int wpb = R <= 64 ? 4 : 8;
   const int dg = R <= 64 ? (int)(R < 8 ? R : 8) : 16;   // an expert owns at most R rows
@@ -329,7 +325,7 @@ static hipError_t dec_launch(int64_t R, int max_tiles, int K, int N, hipStream_t
                              const uint16_t* bias, const float* topk_w,
                              const int32_t* sorted_rows, const Tile* tiles,
                              const int32_t* num_tiles, int k, float alpha, float limit,
-                             uint16_t* h_out, uint16_t* a_out, float* y_w) {
+                             uint16_t* h_out, uint16_t* a_out, uint16_t* y_w) {
   if (K % 64 || K > DEC_MAXK || N % 32) return hipErrorInvalidValue;
   if (R <= 16) {
     const int dg = (int)(R < 8 ? R : 8);
@@ -357,7 +353,7 @@ hipError_t launch_dec_gate_up(const uint16_t* x, const uint8_t* codes, const uin
 hipError_t launch_dec_down(const uint16_t* a, const uint8_t* codes, const uint8_t* scales,
                            const uint16_t* bias, const float* topk_w, const int32_t* sorted_rows,
                            const Tile* tiles, const int32_t* num_tiles, int max_tiles, int64_t R,
-                           int H, int I, float* y_w, hipStream_t s) {
+                           int H, int I, uint16_t* y_w, hipStream_t s) {
   return dec_launch<false>(R, max_tiles, I, H, s, a, codes, scales, bias, topk_w, sorted_rows,
                            tiles, num_tiles, 1, 0.0f, 0.0f, nullptr, nullptr, y_w);
 }

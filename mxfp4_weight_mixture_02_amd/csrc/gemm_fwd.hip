@@ -405,7 +405,7 @@ __global__ __launch_bounds__(FwdShape<8>::NTHR) void down_kernel(
     const float* __restrict__ topk_w, const int32_t* __restrict__ sorted_rows,
     const Tile* __restrict__ tiles, const int32_t* __restrict__ num_tiles, int H, int I,
     const uint16_t* __restrict__ lora_B, const float* __restrict__ lora_v, float lora_scale,
-    float* __restrict__ y_w) {
+    uint16_t* __restrict__ y_w) {
   using S = FwdShape<8>;
   constexpr int XCHUNKS = S::XCH, FNT = S::NT;
   __shared__ __attribute__((aligned(16))) uint8_t lds[S::LDS];
@@ -452,7 +452,7 @@ __global__ __launch_bounds__(FwdShape<8>::NTHR) void down_kernel(
   barrier_only();   // as in gate_up: LDS is free for the epilogue
   const int wcol = wave * 32 * FRB;
   if (n0 + wcol >= N) return;
-  uint8_t* yst = lds + wave * 8192;           // y strip: 32 rows x 64 fp32 (256-byte rows)
+  uint8_t* yst = lds + wave * 4096;           // y strip: 32 rows x 64 bf16 (128-byte rows)
   float bv[FRB][4][4];
   load_bias_rows(bias, (int64_t)e * N + n0 + wcol + 4 * hlf, bv);
 #pragma unroll
@@ -464,40 +464,45 @@ __global__ __launch_bounds__(FwdShape<8>::NTHR) void down_kernel(
     for (int rb = 0; rb < FRB; ++rb)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        f32x4 y;
+        float y[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) y[i] = wf * (acc[rb][tb][4 * q + i] + bv[rb][q][i]);
-        *reinterpret_cast<f32x4*>(yst + stg_off<256>(l32, 8 * rb + 2 * q + hlf)) = y;
+        const u32x2 yv = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+        *reinterpret_cast<u32x2*>(yst + stg_off<128>(l32, 4 * rb + q) + 8 * hlf) = yv;
       }
     wave_lds_sync();
 #pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int r = it * 4 + (lane >> 4), c = lane & 15;
+    for (int it = 0; it < 4; ++it) {
+      const int r = it * 8 + (lane >> 3), c = lane & 7;
       const int rt = tb * 32 + r;
       const int64_t fr = __shfl(f, r);
-      const f32x4 v = *reinterpret_cast<const f32x4*>(yst + stg_off<256>(r, c));
-      if (rt < tl.rows) __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(y_w + fr * N + n0 + wcol + 4 * c));
+      const u32x4 v = *reinterpret_cast<const u32x4*>(yst + stg_off<128>(r, c));
+      if (rt < tl.rows) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(y_w + fr * N + n0 + wcol + 8 * c));
     }
     wave_lds_sync();
   }
 }
 
-// out[t, :] = sum_j y_w[t*k + j, :] in slot order, rounded once to bf16
-// (K = k, a template parameter, so the slot loop unrolls without guards).
+// out[t, :] = sum_j y_w[t*k + j, :] in slot order, summed in fp32 and
+// rounded once to bf16 (K = k, a template parameter, so the slot loop
+// unrolls without guards).  y_w holds each slot's weighted output in bf16.
 template <int K>
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y_w, int64_t n4,
+__global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ y_w, int64_t n4,
                                                       int H4, uint16_t* __restrict__ out) {
   int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n4) return;
   int64_t t = i / H4, c = i % H4;
-  const f32x4* src = reinterpret_cast<const f32x4*>(y_w) + t * K * H4 + c;
-  f32x4 v[K];
+  const u32x2* src = reinterpret_cast<const u32x2*>(y_w) + t * K * H4 + c;
+  u32x2 v[K];
 #pragma unroll
   for (int j = 0; j < K; ++j) v[j] = src[(int64_t)j * H4];
-  f32x4 s = v[0];
+  f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int j = 1; j < K; ++j) {
-    s[0] += v[j][0]; s[1] += v[j][1]; s[2] += v[j][2]; s[3] += v[j][3];
+  for (int j = 0; j < K; ++j) {
+    s[0] += bf16_to_f32((uint16_t)(v[j][0] & 0xFFFFu));
+    s[1] += bf16_to_f32((uint16_t)(v[j][0] >> 16));
+    s[2] += bf16_to_f32((uint16_t)(v[j][1] & 0xFFFFu));
+    s[3] += bf16_to_f32((uint16_t)(v[j][1] >> 16));
   }
   u32x2 o = {pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3])};
   reinterpret_cast<u32x2*>(out)[i] = o;
@@ -530,7 +535,7 @@ hipError_t launch_down(const uint16_t* a, const uint8_t* codes, const uint8_t* s
                        const uint16_t* bias, const float* topk_w, const int32_t* sorted_rows,
                        const Tile* tiles, const int32_t* num_tiles, int max_tiles, int H, int I,
                        const uint16_t* lora_B, const float* lora_v, float lora_scale,
-                       float* y_w, hipStream_t s) {
+                       uint16_t* y_w, hipStream_t s) {
   if (!fwd_step_k(I)) return hipErrorInvalidValue;
   using S = FwdShape<8>;
   dim3 grid(((H + S::NT - 1) / S::NT) * max_tiles), block(S::NTHR);
@@ -543,7 +548,7 @@ hipError_t launch_down(const uint16_t* a, const uint8_t* codes, const uint8_t* s
   return hipGetLastError();
 }
 
-hipError_t launch_combine(const float* y_w, int64_t T, int H, int k, uint16_t* out,
+hipError_t launch_combine(const uint16_t* y_w, int64_t T, int H, int k, uint16_t* out,
                           hipStream_t s) {
   int64_t n4 = T * H / 4;
   const dim3 grid((unsigned)((n4 + 255) / 256));

@@ -56,8 +56,8 @@ hipError_t launch_down(const uint16_t* a, const uint8_t* codes, const uint8_t* s
                        const uint16_t* bias, const float* topk_w, const int32_t* sorted_rows,
                        const Tile* tiles, const int32_t* num_tiles, int max_tiles, int H, int I,
                        const uint16_t* lora_B, const float* lora_v, float lora_scale,
-                       float* y_w, hipStream_t s);
-hipError_t launch_combine(const float* y_w, int64_t T, int H, int k, uint16_t* out,
+                       uint16_t* y_w, hipStream_t s);
+hipError_t launch_combine(const uint16_t* y_w, int64_t T, int H, int k, uint16_t* out,
                           hipStream_t s);
 
 // gemm_dec.hip: forward GEMMs for few rows per expert (weight-streaming)
@@ -71,7 +71,7 @@ hipError_t launch_dec_down(const uint16_t* a, const uint8_t* codes, const uint8_
                            const uint16_t* bias, const float* topk_w, const int32_t* sorted_rows,
                            const Tile* tiles, const int32_t* num_tiles, int max_tiles, int64_t R,
                            int H, int I,
-                           float* y_w, hipStream_t s);
+                           uint16_t* y_w, hipStream_t s);
 
 // gemm_bwd.hip
 int bwd_down_ntiles(int I);
@@ -84,8 +84,8 @@ hipError_t launch_bwd_down(const uint16_t* dy, const uint8_t* codes, const uint8
 hipError_t launch_bwd_gate_up(const uint16_t* dh, const uint8_t* codes, const uint8_t* scales,
                               const int32_t* sorted_rows, const Tile* tiles,
                               const int32_t* num_tiles, int max_tiles, int H, int I,
-                              float* dxr, hipStream_t s);
-hipError_t launch_bwd_combine(const uint16_t* dy, const float* dxr, const float* dw_part,
+                              uint16_t* dxr, hipStream_t s);
+hipError_t launch_bwd_combine(const uint16_t* dy, const uint16_t* dxr, const float* dw_part,
                               int n_dw_part, const int32_t* topk_idx, const float* topk_w,
                               const uint16_t* dn_bias, const float* router_w, int64_t T, int H,
                               int k, uint16_t* dx, hipStream_t s);
