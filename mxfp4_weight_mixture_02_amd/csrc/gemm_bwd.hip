@@ -467,14 +467,14 @@ __global__ __launch_bounds__(256) void bwd_combine_kernel(
   __shared__ float dwps[K * 20];   // k slots x ceil(I / 256) <= 20 column tiles
   const int64_t t = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int H4 = H / 4;
+  const int H8 = H / 8;   // 16-byte pieces (8 bf16) per row
   // this thread's first piece of every slot's dxr, loaded before the bias
   // dot so its latency overlaps that phase (index clamped; used only when
   // the piece exists)
-  u32x2 v0[K];
+  u32x4 v0[K];
 #pragma unroll
   for (int j = 0; j < K; ++j)
-    v0[j] = reinterpret_cast<const u32x2*>(dxr + (t * K + j) * H)[min(tid, H4 - 1)];
+    v0[j] = reinterpret_cast<const u32x4*>(dxr + (t * K + j) * H)[min(tid, H8 - 1)];
   if (tid < K) ex[tid] = topk_idx[t * K + tid];
   for (int q = tid; q < K * n_dw_part; q += 256) dwps[q] = dw_part[t * K * n_dw_part + q];
   __syncthreads();
@@ -516,27 +516,32 @@ __global__ __launch_bounds__(256) void bwd_combine_kernel(
     for (int j = 0; j < K; ++j) dl[j] = w[j] * (dw[j] - sw);
   }
   __syncthreads();
-  // dX piece c from the slots' dxr pieces v (4 bf16 each), in slot order
-  auto emit = [&](int c, const u32x2 (&v)[K]) {
-    f32x4 r[K];
+  // dX piece c (8 columns) from the slots' dxr pieces v, in slot order
+  auto emit = [&](int c, const u32x4 (&v)[K]) {
+    f32x4 r[K][2];
 #pragma unroll
-    for (int j = 0; j < K; ++j) r[j] = reinterpret_cast<const f32x4*>(router_w + (int64_t)ex[j] * H)[c];
-    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < K; ++j) {
+      const f32x4* rw = reinterpret_cast<const f32x4*>(router_w + (int64_t)ex[j] * H) + 2 * c;
+      r[j][0] = rw[0];
+      r[j][1] = rw[1];
+    }
+    float s[8] = {};
 #pragma unroll
     for (int j = 0; j < K; ++j) {
       const float d = dl[j];
 #pragma unroll
-      for (int m = 0; m < 4; ++m)
-        s[m] += bf16_to_f32((uint16_t)(v[j][m >> 1] >> (16 * (m & 1)))) + d * r[j][m];
+      for (int m = 0; m < 8; ++m)
+        s[m] += bf16_to_f32((uint16_t)(v[j][m >> 1] >> (16 * (m & 1)))) + d * r[j][m >> 2][m & 3];
     }
-    u32x2 o = {pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3])};
-    reinterpret_cast<u32x2*>(dx + t * H)[c] = o;
+    const u32x4 o = {pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3]), pack_bf16x2(s[4], s[5]),
+                     pack_bf16x2(s[6], s[7])};
+    reinterpret_cast<u32x4*>(dx + t * H)[c] = o;
   };
-  if (tid < H4) emit(tid, v0);
-  for (int c = tid + 256; c < H4; c += 256) {
-    u32x2 v[K];
+  if (tid < H8) emit(tid, v0);
+  for (int c = tid + 256; c < H8; c += 256) {
+    u32x4 v[K];
 #pragma unroll
-    for (int j = 0; j < K; ++j) v[j] = reinterpret_cast<const u32x2*>(dxr + (t * K + j) * H)[c];
+    for (int j = 0; j < K; ++j) v[j] = reinterpret_cast<const u32x4*>(dxr + (t * K + j) * H)[c];
     emit(c, v);
   }
 }
@@ -577,7 +582,7 @@ hipError_t launch_bwd_combine(const uint16_t* dy, const uint16_t* dxr, const flo
                               int n_dw_part, const int32_t* topk_idx, const float* topk_w,
                               const uint16_t* dn_bias, const float* router_w, int64_t T, int H,
                               int k, uint16_t* dx, hipStream_t s) {
-  if (n_dw_part > 20) return hipErrorInvalidValue;
+  if (n_dw_part > 20 || H % 8) return hipErrorInvalidValue;
 #define BWD_COMBINE(KK)                                                                        \
   case KK:                                                                                     \
     hipLaunchKernelGGL(bwd_combine_kernel<KK>, dim3((unsigned)T), dim3(256), 0, s, dy, dxr,    \

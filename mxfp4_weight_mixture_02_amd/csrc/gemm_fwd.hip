@@ -486,26 +486,28 @@ __global__ __launch_bounds__(FwdShape<8>::NTHR) void down_kernel(
 // out[t, :] = sum_j y_w[t*k + j, :] in slot order, summed in fp32 and
 // rounded once to bf16 (K = k, a template parameter, so the slot loop
 // unrolls without guards).  y_w holds each slot's weighted output in bf16.
+// Each thread takes one 16-byte piece (8 columns) of a token's row.
 template <int K>
-__global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ y_w, int64_t n4,
-                                                      int H4, uint16_t* __restrict__ out) {
+__global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ y_w, int64_t n8,
+                                                      int H8, uint16_t* __restrict__ out) {
   int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n4) return;
-  int64_t t = i / H4, c = i % H4;
-  const u32x2* src = reinterpret_cast<const u32x2*>(y_w) + t * K * H4 + c;
-  u32x2 v[K];
+  if (i >= n8) return;
+  int64_t t = i / H8, c = i % H8;
+  const u32x4* src = reinterpret_cast<const u32x4*>(y_w) + t * K * H8 + c;
+  u32x4 v[K];
 #pragma unroll
-  for (int j = 0; j < K; ++j) v[j] = src[(int64_t)j * H4];
-  f32x4 s = {0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < K; ++j) v[j] = src[(int64_t)j * H8];
+  float s[8] = {};
 #pragma unroll
-  for (int j = 0; j < K; ++j) {
-    s[0] += bf16_to_f32((uint16_t)(v[j][0] & 0xFFFFu));
-    s[1] += bf16_to_f32((uint16_t)(v[j][0] >> 16));
-    s[2] += bf16_to_f32((uint16_t)(v[j][1] & 0xFFFFu));
-    s[3] += bf16_to_f32((uint16_t)(v[j][1] >> 16));
-  }
-  u32x2 o = {pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3])};
-  reinterpret_cast<u32x2*>(out)[i] = o;
+  for (int j = 0; j < K; ++j)
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      s[2 * m] += bf16_to_f32((uint16_t)(v[j][m] & 0xFFFFu));
+      s[2 * m + 1] += bf16_to_f32((uint16_t)(v[j][m] >> 16));
+    }
+  const u32x4 o = {pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3]), pack_bf16x2(s[4], s[5]),
+                   pack_bf16x2(s[6], s[7])};
+  reinterpret_cast<u32x4*>(out)[i] = o;
 }
 
 // K step of the forward GEMMs for a contraction length K (0: unsupported).
@@ -550,11 +552,12 @@ hipError_t launch_down(const uint16_t* a, const uint8_t* codes, const uint8_t* s
 
 hipError_t launch_combine(const uint16_t* y_w, int64_t T, int H, int k, uint16_t* out,
                           hipStream_t s) {
-  int64_t n4 = T * H / 4;
-  const dim3 grid((unsigned)((n4 + 255) / 256));
+  if (H % 8) return hipErrorInvalidValue;
+  int64_t n8 = T * H / 8;
+  const dim3 grid((unsigned)((n8 + 255) / 256));
 #define COMBINE(KK)                                                                      \
   case KK:                                                                               \
-    hipLaunchKernelGGL(combine_kernel<KK>, grid, dim3(256), 0, s, y_w, n4, H / 4, out);  \
+    hipLaunchKernelGGL(combine_kernel<KK>, grid, dim3(256), 0, s, y_w, n8, H / 8, out);  \
     break;
   switch (k) {
     COMBINE(1) COMBINE(2) COMBINE(3) COMBINE(4) COMBINE(5) COMBINE(6) COMBINE(7) COMBINE(8)
