@@ -34,6 +34,7 @@ def assert_close(got, ref, what, max_rel=MAX_REL, min_cos=MIN_COS):
     scale = np.abs(r).max()
     rel = np.abs(g - r).max() / scale if scale > 0 else np.abs(g).max()
     cos = float(g @ r / (np.linalg.norm(g) * np.linalg.norm(r))) if scale > 0 else 1.0
+    print(f"{what}: max_rel={rel:.3e} cos={cos:.8f}", flush=True)
     assert rel <= max_rel and cos >= min_cos, f"{what}: max_rel={rel:.3e} cos={cos:.8f}"
     return rel, cos
 
