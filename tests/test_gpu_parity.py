@@ -288,6 +288,59 @@ def test_inference_forward_equals_saved_forward():
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
 
 
+@pytest.mark.parametrize("shape", [dict(T=200, H=128, I=192, E=8, k=4),
+                                   dict(T=4, E=8, k=2),
+                                   dict(T=40, E=16, k=4, lora_rank=16)])
+def test_graph_replay_matches_eager(shape):
+    # Forward (saved) + backward captured once in a HIP graph.  Before each
+    # of three replays an eager forward + backward on other tokens rewrites
+    # every buffer the graph uses (outputs, saved state, workspaces); each
+    # replay must then reproduce the eager results on the captured tokens
+    # bit for bit.  T = 4 takes the decode-size path (plan + weight-
+    # streaming GEMMs), the others the general path.
+    from mxfp4_weight_mixture_02_amd import SavedState, Workspace
+    s = syn.spec("tiny", **shape)
+    _say(f"graph replay {shape}")
+    dl = device_layer(s)
+    x = bf16_tensor(syn.tokens(s)).to(DEV)
+    x2 = x.flip(0).contiguous()
+    dy = bf16_tensor(syn.upstream_grad(s)).to(DEV)
+    sv = SavedState.empty(dl, s.T, DEV)
+    out, dx = torch.empty_like(x), torch.empty_like(x)
+    lora = dl.lora_A is not None
+    dA = torch.empty(dl.lora_A.shape, dtype=torch.float32, device=DEV) if lora else None
+    dB = torch.empty(dl.lora_B.shape, dtype=torch.float32, device=DEV) if lora else None
+    wsf, wsb = Workspace(), Workspace()
+
+    def run(xin):
+        mxfp4_moe_forward(dl, xin, saved=sv, out=out, workspace=wsf)
+        mxfp4_moe_backward_dx(dl, sv, dy, dx=dx, workspace=wsb, dA=dA, dB=dB)
+
+    def results():
+        return [out, dx, sv.h, sv.a] + ([dA, dB] if lora else [])
+
+    run(x)
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in results()]
+    g = torch.cuda.CUDAGraph()
+    cs = torch.cuda.Stream()
+    cs.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cs):
+        with torch.cuda.graph(g, stream=cs):
+            run(x)
+    torch.cuda.current_stream().wait_stream(cs)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        run(x2)
+        torch.cuda.synchronize()
+        assert not torch.equal(out.view(torch.int16), ref[0].view(torch.int16))
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (got, want) in enumerate(zip(results(), ref)):
+            assert torch.equal(got.view(torch.uint8), want.view(torch.uint8)), (rep, i)
+    del g
+
+
 def test_unsupported_shape_raises():
     s = syn.spec("tiny")
     dl = device_layer(s)
