@@ -167,10 +167,15 @@ int plan_hs_parts(int T, int E, int H) {
 // is VALU-bound) and counts, for each, the experts that beat it (a larger
 // logit, or an equal one with a lower index).  The expert with count j < k
 // is slot j: the k largest logits in descending order, ties to the lower
-// index.  The selected logits go through the wave's LDS slots zs[8]; lane
-// 0 forms the softmax over them in slot order (exponents relative to slot
-// 0).  With `ex` (LDS) slot (t, j)'s expert is also recorded there; with
-// `hist` (LDS) each selected expert is counted.
+// index.  The row is read in chunks of 32 logits, all of a chunk's LDS
+// reads issued before the first compare (one wait per chunk), and the
+// counts use integer masks, not branches (8-logit chunks with guarded
+// compares measured 1.8 us per token for E = 32).  The selected logits go
+// through the wave's LDS slots zs[8]; lane j < k forms the softmax
+// denominator over them in slot order (exponents relative to slot 0, the
+// same sum in every lane) and writes slot j's weight.  With `ex` (LDS) slot
+// (t, j)'s expert is also recorded there; with `hist` (LDS) each selected
+// expert is counted.
 template <int NQ>
 __device__ __forceinline__ void topk_rank(const float* lt, int E, int k, int t, int lane,
                                           int32_t* __restrict__ topk_idx,
@@ -183,18 +188,18 @@ __device__ __forceinline__ void topk_rank(const float* lt, int E, int k, int t, 
     v[q] = lt[min(lane + 64 * q, E - 1)];
     rank[q] = 0;
   }
-  for (int b0 = 0; b0 < E; b0 += 8) {
-    float o[8];
+  for (int b0 = 0; b0 < E; b0 += 32) {
+    float o[32];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) o[j] = lt[min(b0 + j, E - 1)];
-    const int nj = min(8, E - b0);
+    for (int j = 0; j < 32; ++j) o[j] = lt[min(b0 + j, E - 1)];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (j < nj) {
-        const int e2 = b0 + j;
+    for (int j = 0; j < 32; ++j) {
+      const int e2 = b0 + j;
+      const int live = e2 < E;
 #pragma unroll
-        for (int q = 0; q < NQ; ++q)
-          rank[q] += (o[j] > v[q] || (o[j] == v[q] && e2 < lane + 64 * q)) ? 1 : 0;
+      for (int q = 0; q < NQ; ++q) {
+        const int beats = (int)(o[j] > v[q]) | ((int)(o[j] == v[q]) & (int)(e2 < lane + 64 * q));
+        rank[q] += live & beats;
       }
     }
   }
@@ -211,19 +216,18 @@ __device__ __forceinline__ void topk_rank(const float* lt, int E, int k, int t, 
     }
   }
   wave_lds_sync();
-  if (lane == 0) {
+  if (lane < k) {
     const float sel0 = zs[0];
-    float z[8], zsum = 0.0f;
+    float zsum = 0.0f, zl = 0.0f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       if (j < k) {
-        z[j] = expf(zs[j] - sel0);
-        zsum += z[j];
+        const float z = expf(zs[j] - sel0);
+        zsum += z;
+        if (j == lane) zl = z;
       }
     }
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (j < k) topk_w[(int64_t)t * k + j] = z[j] / zsum;
+    topk_w[(int64_t)t * k + lane] = zl / zsum;
   }
 }
 
