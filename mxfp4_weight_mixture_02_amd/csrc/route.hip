@@ -161,14 +161,16 @@ int plan_hs_parts(int T, int E, int H) {
 }
 
 // Top-k and softmax of token t by one wave, from its row lt of E logits in
-// LDS, without cross-lane reductions (a chain of wave shuffles per
-// selection round measured several times slower): lane l owns experts l +
+// LDS, without a cross-lane reduction per selection round (a chain of wave
+// shuffles per round measured several times slower): lane l owns experts l +
 // 64q (q < NQ = ceil(E / 64), a template parameter, since this count loop
 // is VALU-bound) and counts, for each, the experts that beat it (a larger
 // logit, or an equal one with a lower index).  The expert with count j < k
 // is slot j: the k largest logits in descending order, ties to the lower
-// index.  The row is read in chunks of 32 logits, all of a chunk's LDS
-// reads issued before the first compare (one wait per chunk), and the
+// index.  With E <= 32 the two wave halves split the row (16 compares per
+// lane, one shuffle to add the halves).  Otherwise the row is read in
+// chunks of 32 logits, all of a chunk's LDS reads issued before the first
+// compare (one wait per chunk), and the
 // counts use integer masks, not branches (8-logit chunks with guarded
 // compares measured 1.8 us per token for E = 32).  The selected logits go
 // through the wave's LDS slots zs[8]; lane j < k forms the softmax
@@ -183,12 +185,33 @@ __device__ __forceinline__ void topk_rank(const float* lt, int E, int k, int t, 
                                           float* zs) {
   float v[NQ];
   int rank[NQ];
+  if (NQ == 1 && E <= 32) {
+    // both halves of the wave: lane l takes expert l mod 32 against half
+    // l / 32 of the row (16 logits), and the two partial counts are added
+    // (lanes 32..63 own no expert: l >= 32 >= E)
+    const int e = lane & 31, h = lane >> 5;
+    const float ve = lt[min(e, E - 1)];
+    float o[16];
 #pragma unroll
-  for (int q = 0; q < NQ; ++q) {
-    v[q] = lt[min(lane + 64 * q, E - 1)];
-    rank[q] = 0;
+    for (int j = 0; j < 16; ++j) o[j] = lt[min(16 * h + j, E - 1)];
+    int r = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int e2 = 16 * h + j;
+      const int beats = (int)(o[j] > ve) | ((int)(o[j] == ve) & (int)(e2 < e));
+      r += (int)(e2 < E) & beats;
+    }
+    r += __shfl_xor(r, 32);
+    v[0] = ve;
+    rank[0] = r;
+  } else {
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      v[q] = lt[min(lane + 64 * q, E - 1)];
+      rank[q] = 0;
+    }
   }
-  for (int b0 = 0; b0 < E; b0 += 32) {
+  for (int b0 = (NQ == 1 && E <= 32) ? E : 0; b0 < E; b0 += 32) {
     float o[32];
 #pragma unroll
     for (int j = 0; j < 32; ++j) o[j] = lt[min(b0 + j, E - 1)];
