@@ -59,10 +59,10 @@ def parse():
 # only while both are unchanged.
 TRAFFIC = {
     # kernel: (source file, SHA-256 prefix of that file and of common.hpp, bytes per launch)
-    "gate_up": ("gemm_fwd.hip", "b3f0b704ee34d5b0", "06a63ec8e71d21b0", 830.5e6),
-    "down": ("gemm_fwd.hip", "b3f0b704ee34d5b0", "06a63ec8e71d21b0", 304.9e6),
-    "bwd_down": ("gemm_bwd.hip", "fd2f311176483e78", "06a63ec8e71d21b0", 558.9e6),
-    "bwd_gate_up": ("gemm_bwd.hip", "fd2f311176483e78", "06a63ec8e71d21b0", 664.3e6),
+    "gate_up": ("gemm_fwd.hip", "b3f0b704ee34d5b0", "06a63ec8e71d21b0", 834.2e6),
+    "down": ("gemm_fwd.hip", "b3f0b704ee34d5b0", "06a63ec8e71d21b0", 305.3e6),
+    "bwd_down": ("gemm_bwd.hip", "fd2f311176483e78", "06a63ec8e71d21b0", 559.0e6),
+    "bwd_gate_up": ("gemm_bwd.hip", "fd2f311176483e78", "06a63ec8e71d21b0", 664.0e6),
 }
 
 
