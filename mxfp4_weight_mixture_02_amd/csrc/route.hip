@@ -322,17 +322,39 @@ __global__ __launch_bounds__(1024) void plan_kernel(
       if (tid + u * 1024 < P) pst[tid + u * 1024] = v[u];
   }
   __syncthreads();
-  for (int q = tid; q < TE; q += 1024) {
-    double sum = 0.0;
-    for (int h0 = 0; h0 < hs_parts; h0 += 16) {
-      double v[16];
+  if (TE > 512) {
+    for (int q = tid; q < TE; q += 1024) {
+      double sum = 0.0;
+      for (int h0 = 0; h0 < hs_parts; h0 += 16) {
+        double v[16];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) v[j] = pst[min(h0 + j, hs_parts - 1) * TE + q];
+        for (int j = 0; j < 16; ++j) v[j] = pst[min(h0 + j, hs_parts - 1) * TE + q];
 #pragma unroll
-      for (int j = 0; j < 16; ++j)
-        if (h0 + j < hs_parts) sum += v[j];
+        for (int j = 0; j < 16; ++j)
+          if (h0 + j < hs_parts) sum += v[j];
+      }
+      lg[q] = (float)(sum + (br ? (double)br[q % E] : 0.0));
     }
-    lg[q] = (float)(sum + (br ? (double)br[q % E] : 0.0));
+  } else {
+    // few logits: G consecutive lanes per logit (G = 2 .. 16, G * TE <=
+    // 1024); lane g sums ranges g, g + G, ... in order, and an xor-shuffle
+    // tree adds the group's sums (each step adds the same two values in
+    // every lane of a pair, so all lanes hold the same, fixed-order total)
+    const int G = TE > 256 ? 2 : TE > 128 ? 4 : TE > 64 ? 8 : 16;
+    const int q = tid / G, g = tid % G;
+    double sum = 0.0;
+    if (q < TE) {
+      for (int h0 = g; h0 < hs_parts; h0 += 16 * G) {
+        double v[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) v[j] = pst[min(h0 + j * G, hs_parts - 1) * TE + q];
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          if (h0 + j * G < hs_parts) sum += v[j];
+      }
+    }
+    for (int m = 1; m < G; m <<= 1) sum += __shfl_xor(sum, m);
+    if (q < TE && g == 0) lg[q] = (float)(sum + (br ? (double)br[q % E] : 0.0));
   }
   __syncthreads();
   if (E <= 64)
