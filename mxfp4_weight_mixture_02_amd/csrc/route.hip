@@ -315,11 +315,13 @@ __global__ __launch_bounds__(1024) void plan_kernel(
   const int P = hs_parts * TE;
   {
     double v[PLAN_PARTS / 1024];   // all loads issued before the first store
-#pragma unroll
-    for (int u = 0; u < PLAN_PARTS / 1024; ++u) v[u] = part[min(tid + u * 1024, P - 1)];
+    const int nu = (P + 1023) / 1024;   // load rounds needed (uniform)
 #pragma unroll
     for (int u = 0; u < PLAN_PARTS / 1024; ++u)
-      if (tid + u * 1024 < P) pst[tid + u * 1024] = v[u];
+      if (u < nu) v[u] = part[min(tid + u * 1024, P - 1)];
+#pragma unroll
+    for (int u = 0; u < PLAN_PARTS / 1024; ++u)
+      if (u < nu && tid + u * 1024 < P) pst[tid + u * 1024] = v[u];
   }
   __syncthreads();
   if (TE > 512) {
