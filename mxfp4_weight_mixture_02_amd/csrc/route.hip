@@ -131,8 +131,11 @@ __global__ __launch_bounds__(64) void logits_part_kernel(const uint16_t* __restr
   for (int cb = c0; cb < c1; cb += LP_P) {
     u32x4 xv[LP_P];
     f32x4 w0[LP_P], w1[LP_P];
+    // only the chunks that exist are loaded (a range holds few chunks when
+    // there are many ranges; the guard is uniform)
 #pragma unroll
-    for (int q = 0; q < LP_P; ++q) lg_load(xp, wp, min(cb + q, c1 - 1), xv[q], w0[q], w1[q]);
+    for (int q = 0; q < LP_P; ++q)
+      if (cb + q < c1) lg_load(xp, wp, cb + q, xv[q], w0[q], w1[q]);
 #pragma unroll
     for (int q = 0; q < LP_P; ++q)
       if (cb + q < c1) lg_mfma(xv[q], w0[q], w1[q], acc[q % 4]);
