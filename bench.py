@@ -174,6 +174,35 @@ def main():
     dt = (time.perf_counter() - t0) / args.steps
     value = flops_step / dt / 1e12
 
+    # ---- per-step distribution (HIP events between consecutive steps on the
+    # stream the library launches on) and the step as one HIP-graph replay
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    evs[0].record()
+    for i in range(args.steps):
+        step()
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    per_step = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)])
+    step_stats = {"median": round(float(np.median(per_step)), 4),
+                  "p10": round(float(np.percentile(per_step, 10)), 4),
+                  "p90": round(float(np.percentile(per_step, 90)), 4)}
+    gstep = torch.cuda.CUDAGraph()
+    cs = torch.cuda.Stream()
+    cs.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cs):
+        with torch.cuda.graph(gstep, stream=cs):
+            step()
+    torch.cuda.current_stream().wait_stream(cs)
+    for _ in range(3):
+        gstep.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        gstep.replay()
+    torch.cuda.synchronize()
+    dt_graph = (time.perf_counter() - t0) / args.steps
+    del gstep
+
     # ---- the same steps with per-kernel HIP events on the library's stream
     L.mxfp4_moe_kernel_timing(1)
     torch.cuda.synchronize()
@@ -290,6 +319,8 @@ def main():
                    "T": T, "H": H, "I": I, "E": E, "k": k, "weights": "MXFP4 (E2M1 + UE8M0/32)",
                    "parallelism": "none (1 GPU)"},
         "fwd_tflops": round(fwd_tflops, 2), "fwd_ms": round(dt_fwd * 1e3, 4),
+        "ms_per_step_stats": step_stats,
+        "ms_per_step_graph": round(dt_graph * 1e3, 4),
         "ms_per_step_with_kernel_events": round(dt_inst * 1e3, 4),
         "kernel_us": kernels, "decode": decode, "roofline": roofline,
         "workloads": extra,
@@ -384,22 +415,27 @@ def extra_workload(s, args, lora):
 
 
 def cpu_baseline(s, n_tok):
-    """The float64 oracle, as it stands, on n_tok tokens of the layer:
-    routing over all tokens, then forward and dX for the sample."""
+    """The float64 oracle, as it stands, on the host cores: routing of all
+    tokens, then forward and dX for a sample of n_tok tokens, each phase
+    timed on its own; then the forward + dX of a quarter of the sample with
+    the BLAS pool held to one thread (the per-core rate).  `value` is the
+    sample's forward + dX flops over its forward + dX time (routing is
+    reported apart).  The oracle's cost per token is dominated by
+    dequantizing the weights of every expert the sample touches (about 0.5 s
+    per expert on one core), so its rate grows with the sample."""
     import numpy as np
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     import moe_synth as syn
     from oracle import moe, mxfp4
 
     xb = syn.tokens(s)
     dyb = syn.upstream_grad(s)
+    toks = np.arange(n_tok)
     rl = moe.Layer(router_w=syn.router_weight(s), router_b=syn.router_bias(s),
                    gu_codes=np.zeros((s.E, 2, 1), np.uint8), gu_scales=None, gu_bias=None,
                    dn_codes=None, dn_scales=None, dn_bias=None, k=s.k)
-    r = moe.route(rl, xb)
-    toks = np.arange(n_tok)
-    touched = sorted(set(int(e) for e in np.unique(r.idx[toks])))
+    touched = sorted(set(int(e) for e in np.unique(moe.route(rl, xb).idx[toks])))
     gu_c = np.zeros((s.E, 2 * s.I, s.H // 2), np.uint8)
     gu_s = np.zeros((s.E, 2 * s.I, s.H // 32), np.uint8)
     dn_c = np.zeros((s.E, s.H, s.I // 2), np.uint8)
@@ -415,18 +451,34 @@ def cpu_baseline(s, n_tok):
     ol = moe.Layer(syn.router_weight(s), syn.router_bias(s), gu_c, gu_s, syn.gate_up_bias(s),
                    dn_c, dn_s, syn.down_bias(s), k=s.k)
     t0 = time.perf_counter()
-    r2 = moe.route(ol, xb)
-    moe.forward(ol, xb, tokens=toks, routing=r2)
-    moe.backward_dx(ol, xb, dyb, tokens=toks, routing=r2)
-    dt = time.perf_counter() - t0
-    flops = 2 * (2.0 * n_tok * s.k * 3 * s.H * s.I)
+    r = moe.route(ol, xb)
+    t_route = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    moe.forward(ol, xb, tokens=toks, routing=r)
+    t_fwd = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    moe.backward_dx(ol, xb, dyb, tokens=toks, routing=r)
+    t_bwd = time.perf_counter() - t0
+    per_tok = 2 * (2.0 * s.k * 3 * s.H * s.I)          # forward + dX flops per token
+    n1 = max(1, n_tok // 4)
+    with threadpool_limits(limits=1, user_api="blas"):
+        t0 = time.perf_counter()
+        moe.forward(ol, xb, tokens=toks[:n1], routing=r)
+        moe.backward_dx(ol, xb, dyb, tokens=toks[:n1], routing=r)
+        t_one = time.perf_counter() - t0
     blas = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s",
-            "cores": max(blas) if blas else 1, "kind": "oracle",
-            "seconds": round(dt, 2),
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    return {"value": round(n_tok * per_tok / (t_fwd + t_bwd) / 1e12, 6), "unit": "TFLOP/s",
+            "cores": cores, "blas_threads": max(blas) if blas else 1, "kind": "oracle",
+            "seconds": {"route_all_tokens": round(t_route, 3), "forward": round(t_fwd, 2),
+                        "backward_dx": round(t_bwd, 2)},
+            "per_core": {"value": round(n1 * per_tok / t_one / 1e12, 6), "unit": "TFLOP/s",
+                         "tokens": n1, "seconds": round(t_one, 2)},
             "sample": f"{n_tok} tokens ({n_tok * s.k} routed rows, {len(touched)} experts) of the "
-                      f"2048-token gpt-oss-20b layer: routing of all tokens, forward + dX for the "
-                      f"sample, float64 numpy (BLAS matmuls multi-threaded, dequant single-threaded)"}
+                      f"2048-token gpt-oss-20b layer: routing of all {s.T} tokens, then forward + "
+                      f"dX for the sample, float64 numpy on the host's cores (BLAS matmuls "
+                      f"multi-threaded, dequant single-threaded); per_core: {n1} tokens, BLAS "
+                      f"held to one thread"}
 
 
 if __name__ == "__main__":

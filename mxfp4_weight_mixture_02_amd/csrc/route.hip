@@ -163,38 +163,56 @@ int plan_hs_parts(int T, int E, int H) {
   return max(hs, 1);
 }
 
-// Top-k and softmax of token t by one wave, from its row lt of E logits in
-// LDS, without a cross-lane reduction per selection round (a chain of wave
-// shuffles per round measured several times slower): lane l owns experts l +
-// 64q (q < NQ = ceil(E / 64), a template parameter, since this count loop
-// is VALU-bound) and counts, for each, the experts that beat it (a larger
-// logit, or an equal one with a lower index).  The expert with count j < k
-// is slot j: the k largest logits in descending order, ties to the lower
-// index.  With E <= 32 the two wave halves split the row (16 compares per
-// lane, one shuffle to add the halves).  Otherwise the row is read in
-// chunks of 32 logits, all of a chunk's LDS reads issued before the first
-// compare (one wait per chunk), and the
-// counts use integer masks, not branches (8-logit chunks with guarded
-// compares measured 1.8 us per token for E = 32).  The selected logits go
-// through the wave's LDS slots zs[8]; lane j < k forms the softmax
-// denominator over them in slot order (exponents relative to slot 0, the
-// same sum in every lane) and writes slot j's weight.  With `ex` (LDS) slot
-// (t, j)'s expert is also recorded there; with `hist` (LDS) each selected
-// expert is counted.
+// Total-order key of a logit for the top-k: larger key = larger logit,
+// -0.0 and +0.0 equal, and NaN below every number (-inf included), all NaNs
+// equal.  Ties then go to the lower expert index, which is the order of a
+// stable sort of the negated logits with NaN last.  On keys, "beats" is a
+// strict total order, so the k selected experts are always distinct and
+// every token adds exactly k rows to the histogram, whatever its values.
+__device__ __forceinline__ int32_t order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u << 1) == 0u) u = 0u;   // -0.0 -> +0.0
+  const int32_t b = (int32_t)u;
+  return (f != f) ? INT32_MIN : (b ^ ((b >> 31) & 0x7FFFFFFF));
+}
+
+// The logit back from its key (exact for numbers; -0.0 comes back as +0.0,
+// a NaN key as a NaN).
+__device__ __forceinline__ float key_value(int32_t k) {
+  return __uint_as_float((uint32_t)(k ^ ((k >> 31) & 0x7FFFFFFF)));
+}
+
+// Top-k and softmax of token t by one wave, from its row lt of E logit keys
+// (order_key) in LDS, without a cross-lane reduction per selection round (a
+// chain of wave shuffles per round measured several times slower): lane l
+// owns experts l + 64q (q < NQ = ceil(E / 64), a template parameter, since
+// this count loop is VALU-bound) and counts, for each, the experts that
+// beat it (a larger key, or an equal one with a lower index).  The expert
+// with count j < k is slot j: the k largest logits in descending order,
+// ties to the lower index.  With E <= 32 the two wave halves split the row
+// (16 compares per lane, one shuffle to add the halves).  Otherwise the row
+// is read in chunks of 32 keys, all of a chunk's LDS reads issued before
+// the first compare (one wait per chunk), and the counts use integer masks,
+// not branches (8-logit chunks with guarded compares measured 1.8 us per
+// token for E = 32).  The selected logits go through the wave's LDS slots
+// zs[8]; lane j < k forms the softmax denominator over them in slot order
+// (exponents relative to slot 0, the same sum in every lane) and writes
+// slot j's weight.  With `ex` (LDS) slot (t, j)'s expert is also recorded
+// there; with `hist` (LDS) each selected expert is counted.
 template <int NQ>
-__device__ __forceinline__ void topk_rank(const float* lt, int E, int k, int t, int lane,
+__device__ __forceinline__ void topk_rank(const int32_t* lt, int E, int k, int t, int lane,
                                           int32_t* __restrict__ topk_idx,
                                           float* __restrict__ topk_w, int32_t* ex, int32_t* hist,
                                           float* zs) {
-  float v[NQ];
+  int32_t v[NQ];
   int rank[NQ];
   if (NQ == 1 && E <= 32) {
     // both halves of the wave: lane l takes expert l mod 32 against half
     // l / 32 of the row (16 logits), and the two partial counts are added
     // (lanes 32..63 own no expert: l >= 32 >= E)
     const int e = lane & 31, h = lane >> 5;
-    const float ve = lt[min(e, E - 1)];
-    float o[16];
+    const int32_t ve = lt[min(e, E - 1)];
+    int32_t o[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) o[j] = lt[min(16 * h + j, E - 1)];
     int r = 0;
@@ -215,7 +233,7 @@ __device__ __forceinline__ void topk_rank(const float* lt, int E, int k, int t, 
     }
   }
   for (int b0 = (NQ == 1 && E <= 32) ? E : 0; b0 < E; b0 += 32) {
-    float o[32];
+    int32_t o[32];
 #pragma unroll
     for (int j = 0; j < 32; ++j) o[j] = lt[min(b0 + j, E - 1)];
 #pragma unroll
@@ -238,7 +256,7 @@ __device__ __forceinline__ void topk_rank(const float* lt, int E, int k, int t, 
       topk_idx[f] = e;
       if (ex) ex[f] = e;
       if (hist) atomicAdd(&hist[e], 1);   // counts only: order does not matter
-      zs[rank[q]] = v[q];
+      zs[rank[q]] = key_value(v[q]);
     }
   }
   wave_lds_sync();
@@ -266,7 +284,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
                                                    float* __restrict__ topk_w,
                                                    int32_t* __restrict__ blk_hist) {
   __shared__ int32_t hist[256];
-  __shared__ float lgs[RT * 256];
+  __shared__ int32_t lgs[RT * 256];   // logit keys
   __shared__ float zs[4][8];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t0 = blockIdx.x * RT;
@@ -279,7 +297,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
     for (int u = 0; u < RT; ++u) v[u] = logits[(int64_t)t0 * E + min(tid + u * 256, n - 1)];
 #pragma unroll
     for (int u = 0; u < RT; ++u)
-      if (tid + u * 256 < n) lgs[tid + u * 256] = v[u];
+      if (tid + u * 256 < n) lgs[tid + u * 256] = order_key(v[u]);
   }
   __syncthreads();
 #pragma unroll
@@ -304,7 +322,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(
     int k, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
     int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_rows, Tile* __restrict__ tiles,
     int32_t* __restrict__ num_tiles) {
-  __shared__ float lg[PLAN_LOGITS];
+  __shared__ int32_t lg[PLAN_LOGITS];   // logit keys
   __shared__ double pst[PLAN_PARTS];
   __shared__ float zs[16][8];
   __shared__ int32_t ex[PLAN_MAX_ROWS];
@@ -338,7 +356,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(
         for (int j = 0; j < 16; ++j)
           if (h0 + j < hs_parts) sum += v[j];
       }
-      lg[q] = (float)(sum + (br ? (double)br[q % E] : 0.0));
+      lg[q] = order_key((float)(sum + (br ? (double)br[q % E] : 0.0)));
     }
   } else {
     // few logits: G consecutive lanes per logit (G = 2 .. 16, G * TE <=
@@ -359,7 +377,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(
       }
     }
     for (int m = 1; m < G; m <<= 1) sum += __shfl_xor(sum, m);
-    if (q < TE && g == 0) lg[q] = (float)(sum + (br ? (double)br[q % E] : 0.0));
+    if (q < TE && g == 0) lg[q] = order_key((float)(sum + (br ? (double)br[q % E] : 0.0)));
   }
   __syncthreads();
   if (E <= 64)

@@ -111,6 +111,18 @@ def _dev(t, dtype, name):
     return t
 
 
+def _shape(t, shape, dtype, name, optional=False):
+    """Refuse a tensor whose shape or dtype differs from what the C ABI will
+    assume (it sees only pointers, so a mismatch would read or write out of
+    bounds).  Runs before the device checks and on any device."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError(f"{name}: expected {dtype} {tuple(shape)}, got {t.dtype} {tuple(t.shape)}")
+
+
 # --------------------------------------------------------------- quantise
 
 def mxfp4_quantize(w: torch.Tensor):
@@ -173,7 +185,31 @@ class MoeLayer:
         r = 0 if self.lora_A is None else self.lora_A.shape[1]
         return Dims(T, self.H, self.I, self.E, self.k, self.alpha, self.limit, r, self.lora_scale)
 
+    def check_shapes(self):
+        """Every parameter's shape and dtype against E, H, I (and the rank)."""
+        if self.gu_codes.dim() != 3 or min(self.gu_codes.shape) < 1:
+            raise ValueError(f"gu_codes must be [E, 2I, H/2], got {tuple(self.gu_codes.shape)}")
+        E, H, I = self.E, self.H, self.I
+        u8, bf = torch.uint8, torch.bfloat16
+        _shape(self.router_w, (E, H), torch.float32, "router_w")
+        _shape(self.router_b, (E,), torch.float32, "router_b", optional=True)
+        _shape(self.gu_codes, (E, 2 * I, H // 2), u8, "gu_codes")
+        _shape(self.gu_scales, (E, 2 * I, H // 32), u8, "gu_scales")
+        _shape(self.gu_bias, (E, 2 * I), bf, "gu_bias", optional=True)
+        _shape(self.dn_codes, (E, H, I // 2), u8, "dn_codes")
+        _shape(self.dn_scales, (E, H, I // 32), u8, "dn_scales")
+        _shape(self.dn_bias, (E, H), bf, "dn_bias", optional=True)
+        if (self.lora_A is None) != (self.lora_B is None):
+            raise ValueError("lora_A and lora_B go together")
+        if self.lora_A is not None:
+            if self.lora_A.dim() != 3:
+                raise ValueError(f"lora_A must be [E, r, I], got {tuple(self.lora_A.shape)}")
+            r = self.lora_A.shape[1]
+            _shape(self.lora_A, (E, r, I), bf, "lora_A")
+            _shape(self.lora_B, (E, H, r), bf, "lora_B")
+
     def weights(self):
+        self.check_shapes()
         _dev(self.router_w, torch.float32, "router_w")
         _dev(self.router_b, torch.float32, "router_b")
         for n in ("gu_codes", "gu_scales", "dn_codes", "dn_scales"):
@@ -214,7 +250,22 @@ class SavedState:
             bufs[n] = t
         return SavedState(**bufs)
 
+    def check_shapes(self, layer: MoeLayer, T: int):
+        """Every buffer against the sizes a call with T tokens uses."""
+        R = T * layer.k
+        r = 0 if layer.lora_A is None else layer.lora_A.shape[1]
+        _shape(self.topk_idx, (T, layer.k), torch.int32, "saved.topk_idx")
+        _shape(self.topk_w, (T, layer.k), torch.float32, "saved.topk_w")
+        _shape(self.expert_offsets, (layer.E + 1,), torch.int32, "saved.expert_offsets")
+        _shape(self.sorted_rows, (R,), torch.int32, "saved.sorted_rows")
+        _shape(self.h, (R, 2 * layer.I), torch.bfloat16, "saved.h")
+        _shape(self.a, (R, layer.I), torch.bfloat16, "saved.a")
+        _shape(self.lora_v, (R, r), torch.float32, "saved.lora_v", optional=(r == 0))
+
     def struct(self):
+        for n, _ in Saved._fields_:
+            t = getattr(self, n)
+            _dev(t, t.dtype if t is not None else None, f"saved.{n}")
         return Saved(*[_ptr(getattr(self, n)) for n, _ in Saved._fields_])
 
 
@@ -253,12 +304,21 @@ def mxfp4_moe_forward(layer: MoeLayer, x: torch.Tensor, saved: SavedState | bool
                       out: torch.Tensor | None = None, workspace: Workspace | None = None):
     """Expert-block forward.  ``saved=True`` allocates and fills the state
     the backward needs.  Returns (out, saved)."""
-    x = _dev(x, torch.bfloat16, "x")
+    layer.check_shapes()
+    if x.dim() != 2:
+        raise ValueError(f"x must be [T, H], got {tuple(x.shape)}")
     T = x.shape[0]
+    _shape(x, (T, layer.H), torch.bfloat16, "x")
+    if out is not None:
+        _shape(out, (T, layer.H), torch.bfloat16, "out")
+    if saved is not None and saved is not True and saved is not False:
+        saved.check_shapes(layer, T)
+    x = _dev(x, torch.bfloat16, "x")
     if saved is True:
         saved = SavedState.empty(layer, T, x.device)
     if out is None:
         out = torch.empty_like(x)
+    _dev(out, torch.bfloat16, "out")
     mode = WS_FORWARD_SAVED if saved else WS_FORWARD
     nbytes = workspace_bytes(layer, T, mode)
     ws = (workspace or _WS).get(nbytes, x.device)
@@ -277,11 +337,25 @@ def mxfp4_moe_backward_dx(layer: MoeLayer, saved: SavedState, dy: torch.Tensor,
                           dA: torch.Tensor | None = None, dB: torch.Tensor | None = None):
     """dX (and, with LoRA, dA/dB, overwritten) for the loss sum(dy * out).
     Returns (dx, dA, dB)."""
-    dy = _dev(dy, torch.bfloat16, "dy")
+    layer.check_shapes()
+    if dy.dim() != 2:
+        raise ValueError(f"dy must be [T, H], got {tuple(dy.shape)}")
     T = dy.shape[0]
+    _shape(dy, (T, layer.H), torch.bfloat16, "dy")
+    if dx is not None:
+        _shape(dx, (T, layer.H), torch.bfloat16, "dx")
+    saved.check_shapes(layer, T)
+    lora = layer.lora_A is not None
+    if lora:
+        if dA is not None:
+            _shape(dA, tuple(layer.lora_A.shape), torch.float32, "dA")
+        if dB is not None:
+            _shape(dB, tuple(layer.lora_B.shape), torch.float32, "dB")
+    dy = _dev(dy, torch.bfloat16, "dy")
     if dx is None:
         dx = torch.empty_like(dy)
-    if layer.lora_A is not None:
+    _dev(dx, torch.bfloat16, "dx")
+    if lora:
         if dA is None:
             dA = torch.empty(layer.lora_A.shape, dtype=torch.float32, device=dy.device)
         if dB is None:

@@ -100,6 +100,37 @@ def oracle_layer(s, experts=None, with_bias=True, threads=8):
     return L, experts
 
 
+def cache_dequant(ol: moe.Layer, experts, threads=16):
+    """Dequantize the given experts' weights once, in parallel, with the
+    oracle's own ``dequantize``, and make ``ol.gate_up(e)`` / ``ol.down(e)``
+    return those arrays (the forward and the backward would otherwise
+    decode every expert again; the arithmetic is unchanged)."""
+    experts = sorted(set(int(e) for e in experts))
+
+    def one(e):
+        return e, mxfp4.dequantize(ol.gu_codes[e], ol.gu_scales[e]), \
+            mxfp4.dequantize(ol.dn_codes[e], ol.dn_scales[e])
+
+    gu, dn = {}, {}
+    with ThreadPoolExecutor(threads) as ex:
+        for e, g, d in ex.map(one, experts):
+            gu[e], dn[e] = g, d
+    ol.gate_up = gu.__getitem__
+    ol.down = dn.__getitem__
+    return ol
+
+
+def assert_bytes_equal(dl, ol, experts=None):
+    """The GPU quantizer's codes and scales equal the oracle's, byte for
+    byte, on every listed expert (all by default), for both projections."""
+    experts = range(ol.E) if experts is None else experts
+    for name in ("gu_codes", "gu_scales", "dn_codes", "dn_scales"):
+        g = getattr(dl, name)
+        r = getattr(ol, name)
+        for e in experts:
+            assert np.array_equal(g[e].cpu().numpy(), r[e]), f"{name}[{e}] differs"
+
+
 def assert_routing_equal(saved, r: moe.Routing):
     """Indices, offsets and the permutation are integers: bit-exact.  The
     routing weights are floats: tolerance."""

@@ -4,8 +4,13 @@ Integers (quantised bytes, dequantised bits, routing indices, expert
 offsets, the permutation) must match bit for bit; floating-point results
 (routing weights, the saved h and a, out, dX) must reach
 max|g - r| / max|r| <= 2e-2 and cosine >= 0.9999 against the oracle.
-Full-size layers compare the routing of every token and the outputs of a
-seeded sample of tokens, whose rows the oracle computes one by one.
+Full-size layers: the 2048-token gpt-oss-20b layer and its decode sizes are
+compared whole (every token's out and dX, every routed row's saved h and a);
+the skewed 120b layer compares every row of its hottest expert (dozens of
+row tiles and a ragged last one) and of a single-tile expert, plus out and
+dX of sampled tokens; the 16384-token LoRA layer runs the checkpointing
+sequence (forward, recompute forward, backward) and checks the recompute
+bit for bit and dX on 64 tokens.
 """
 import math
 import sys
@@ -19,8 +24,8 @@ from mxfp4_weight_mixture_02_amd import (Mxfp4Error, mxfp4_dequantize, mxfp4_moe
                                          mxfp4_moe_forward, mxfp4_quantize)
 from oracle import moe, mxfp4
 
-from gpu_helpers import (DEV, assert_close, assert_routing_equal, bf16_tensor, device_layer,
-                         min_topk_gap, oracle_layer, to_f64)
+from gpu_helpers import (DEV, assert_bytes_equal, assert_close, assert_routing_equal, bf16_tensor,
+                         cache_dequant, device_layer, min_topk_gap, oracle_layer, to_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -91,9 +96,8 @@ def _run_layer(s, x_scale=1.0, with_bias=True, backward=True, T=None, lora_scale
     dl = device_layer(s, with_bias=with_bias)
     ol, _ = oracle_layer(s, with_bias=with_bias)
     dl.lora_scale = ol.lora_scale = lora_scale
-    # the oracle's quantised bytes must equal the GPU's
-    assert np.array_equal(dl.gu_codes.cpu().numpy(), ol.gu_codes)
-    assert np.array_equal(dl.dn_scales.cpu().numpy(), ol.dn_scales)
+    # the oracle's quantised bytes must equal the GPU's (all four tensors)
+    assert_bytes_equal(dl, ol)
     xb = syn.tokens(s, T, scale=x_scale)
     x = bf16_tensor(xb).to(DEV)
     out, sv = mxfp4_moe_forward(dl, x, saved=True)
@@ -350,88 +354,202 @@ def test_unsupported_shape_raises():
         mxfp4_moe_forward(dl, x)
 
 
+# --------------------------------------------------------- non-finite input
+
+@pytest.mark.parametrize("T", [16, 200])
+def test_non_finite_tokens_still_route_k_distinct_experts(T):
+    # Tokens holding a NaN or an Inf give NaN or infinite logits.  The top-k
+    # orders on a total key (NaN lowest, ties to the lower index, the order
+    # of the oracle's stable sort), so such a token still takes k distinct
+    # experts and adds exactly k rows: offsets[E] = T * k, the permutation
+    # equals the oracle's and every other token's results are computed.
+    # T = 16 takes the one-workgroup routing plan, T = 200 the many-token
+    # path (R = 400 routed rows).
+    s = syn.spec("tiny", T=T)
+    _say(f"non-finite tokens T={T}")
+    xb = syn.tokens(s, T).copy()
+    xb[1, 5] = 0x7FC0                  # NaN: every logit NaN
+    xb[3, 0] = 0x7F80                  # +Inf
+    xb[6, :] = 0xFF80                  # -Inf everywhere: logits +-Inf and NaN
+    xb[9, 7] = 0x7F80
+    xb[9, 8] = 0xFF80                  # +Inf and -Inf in one token
+    bad = np.array([1, 3, 6, 9])
+    good = np.setdiff1d(np.arange(T), bad)
+    dl = device_layer(s)
+    ol, _ = oracle_layer(s)
+    x = bf16_tensor(xb).to(DEV)
+    out, sv = mxfp4_moe_forward(dl, x, saved=True)
+    dyb = syn.upstream_grad(s, T)
+    dx, _, _ = mxfp4_moe_backward_dx(dl, sv, bf16_tensor(dyb).to(DEV))
+    torch.cuda.synchronize()
+    with np.errstate(invalid="ignore", over="ignore"):
+        ref, r, _ = moe.forward(ol, xb)
+        dref, _, _ = moe.backward_dx(ol, xb, dyb, tokens=good, routing=r)
+    idx = sv.topk_idx.cpu().numpy()
+    assert np.array_equal(idx, r.idx)
+    assert all(len(set(row)) == s.k for row in idx)
+    off = sv.expert_offsets.cpu().numpy()
+    assert off[-1] == T * s.k and np.array_equal(off, r.offsets)
+    assert np.array_equal(sv.sorted_rows.cpu().numpy(), r.sorted_rows)
+    assert_close(to_f64(out)[good], ref[good], "out (finite tokens)")
+    assert_close(to_f64(dx)[good], dref[good], "dX (finite tokens)")
+
+
 # --------------------------------------------------------- full-size layers
 
-def _full_size(name, T=None, n_sample=6, backward=True, seed=0):
-    s = syn.spec(name) if T is None else syn.spec(name, T=T)
-    T = s.T
-    _say(f"full-size {name} T={T}: building device layer")
+def _device_and_routing(s, T):
+    _say(f"full-size {s.name} T={T}: building device layer")
     dl = device_layer(s)
     xb = syn.tokens(s, T)
-    x = bf16_tensor(xb).to(DEV)
-    _say("forward")
-    out, sv = mxfp4_moe_forward(dl, x, saved=True)
-    torch.cuda.synchronize()
-    # routing of every token: bit-exact
     rl = moe.Layer(router_w=syn.router_weight(s), router_b=syn.router_bias(s),
                    gu_codes=np.zeros((s.E, 2, 1), np.uint8), gu_scales=None, gu_bias=None,
                    dn_codes=None, dn_scales=None, dn_bias=None, k=s.k)
     r = moe.route(rl, xb)
     _say(f"min k/k+1 logit gap {min_topk_gap(r, s.k):.3e}")
+    return dl, xb, r
+
+
+def _sorted_positions(r, R):
+    pos = np.empty(R, np.int64)
+    pos[r.sorted_rows] = np.arange(R)
+    return pos
+
+
+def _whole_layer(name, T=None):
+    """Every token and every routed row of the layer against the oracle."""
+    s = syn.spec(name) if T is None else syn.spec(name, T=T)
+    T = s.T
+    dl, xb, r = _device_and_routing(s, T)
+    x = bf16_tensor(xb).to(DEV)
+    out, sv = mxfp4_moe_forward(dl, x, saved=True)
+    dyb = syn.upstream_grad(s, T)
+    dx, _, _ = mxfp4_moe_backward_dx(dl, sv, bf16_tensor(dyb).to(DEV))
+    torch.cuda.synchronize()
     assert_routing_equal(sv, r)
-    rng = np.random.default_rng(seed)
-    toks = np.sort(rng.choice(T, size=min(n_sample, T), replace=False))
-    touched = np.unique(r.idx[toks])
-    # with LoRA: the expert with the fewest rows gets its adapter gradients
-    # checked in full (every row of it)
-    hist = np.diff(r.offsets)
-    e_full = int(np.argmin(np.where(hist > 0, hist, np.iinfo(np.int64).max)))
-    need = np.union1d(touched, [e_full]) if s.lora_rank else touched
-    _say(f"oracle: {len(need)} experts for tokens {toks.tolist()}")
-    ol, _ = oracle_layer(s, experts=need)
-    # the GPU quantizer's bytes equal the oracle's on every expert it needed
-    for e in touched[:4]:
-        assert np.array_equal(dl.gu_codes[e].cpu().numpy(), ol.gu_codes[e])
-        assert np.array_equal(dl.dn_codes[e].cpu().numpy(), ol.dn_codes[e])
-        assert np.array_equal(dl.gu_scales[e].cpu().numpy(), ol.gu_scales[e])
-    ref, _, cache = moe.forward(ol, xb, tokens=toks, routing=r)
-    assert_close(to_f64(out)[toks], ref[toks], "out (sampled tokens)")
-    # saved a/h for the sampled rows (sorted positions of their flat rows)
-    pos = np.empty(T * s.k, np.int64)
-    pos[r.sorted_rows] = np.arange(T * s.k)
-    fl = np.array(sorted(cache.keys()))
-    aref = np.stack([cache[int(f)][1] for f in fl])
-    assert_close(to_f64(sv.a)[pos[fl]], aref, "saved a")
-    if s.lora_rank:
-        ef = np.searchsorted(r.offsets, pos[fl], side="right") - 1
-        vref = np.stack([moe._lora_v(ol, ef[i], aref[i][None])[0] for i in range(len(fl))])
-        assert_close(to_f64(sv.lora_v)[pos[fl]], vref, "saved lora_v (sampled rows)")
-    if backward:
-        _say("backward")
-        dyb = syn.upstream_grad(s, T)
-        dx, dA, dB = mxfp4_moe_backward_dx(dl, sv, bf16_tensor(dyb).to(DEV))
-        torch.cuda.synchronize()
-        dref, _, _ = moe.backward_dx(ol, xb, dyb, tokens=toks, routing=r)
-        assert_close(to_f64(dx)[toks], dref[toks], "dX (sampled tokens)")
-        assert torch.isfinite(dx.float()).all()
-        if s.lora_rank:
-            _say(f"adapter gradients of expert {e_full} ({hist[e_full]} rows)")
-            _, dAr, dBr = moe.backward_dx(ol, xb, dyb, routing=r, experts=[e_full])
-            assert_close(to_f64(dA[e_full]), dAr[e_full], "dA (one expert, all rows)")
-            assert_close(to_f64(dB[e_full]), dBr[e_full], "dB (one expert, all rows)")
-            # every expert: <dA, A> = <dB, B> (both are s * dL/ds)
-            ipA = float((dA.double() * dl.lora_A.double()).sum())
-            ipB = float((dB.double() * dl.lora_B.double()).sum())
-            assert abs(ipA - ipB) <= 1e-2 * max(abs(ipA), abs(ipB)), (ipA, ipB)
-    assert torch.isfinite(out.float()).all()
+    touched = np.unique(r.idx)
+    _say(f"oracle: {len(touched)} experts, all {T} tokens")
+    ol, _ = oracle_layer(s, experts=touched, threads=16)
+    assert_bytes_equal(dl, ol, touched)
+    cache_dequant(ol, touched)
+    ref, _, cache = moe.forward(ol, xb, routing=r)
+    assert_close(to_f64(out), ref, "out (all tokens)")
+    rows = r.sorted_rows
+    assert_close(to_f64(sv.h), np.stack([cache[int(f)][0] for f in rows]), "saved h (all rows)")
+    assert_close(to_f64(sv.a), np.stack([cache[int(f)][1] for f in rows]), "saved a (all rows)")
+    del cache
+    _say("oracle backward")
+    dref, _, _ = moe.backward_dx(ol, xb, dyb, routing=r)
+    assert_close(to_f64(dx), dref, "dX (all tokens)")
+    assert torch.isfinite(out.float()).all() and torch.isfinite(dx.float()).all()
 
 
 @pytest.mark.timeout(900)
 def test_gpt_oss_20b_layer_2048_tokens():
-    _full_size("20b_2048")
+    _whole_layer("20b_2048")
 
 
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("T", [1, 8, 64])
 def test_gpt_oss_20b_layer_decode(T):
-    _full_size("20b_decode", T=T, n_sample=min(T, 4), backward=(T == 64))
-
-
-@pytest.mark.timeout(900)
-def test_gpt_oss_20b_layer_16384_tokens_lora():
-    _full_size("20b_16384_lora", n_sample=4)
+    _whole_layer("20b_decode", T=T)
 
 
 @pytest.mark.timeout(900)
 def test_gpt_oss_120b_layer_zipf_8192_tokens():
-    _full_size("120b_8192_zipf", n_sample=4)
+    s = syn.spec("120b_8192_zipf")
+    T = s.T
+    dl, xb, r = _device_and_routing(s, T)
+    x = bf16_tensor(xb).to(DEV)
+    out, sv = mxfp4_moe_forward(dl, x, saved=True)
+    dyb = syn.upstream_grad(s, T)
+    dx, _, _ = mxfp4_moe_backward_dx(dl, sv, bf16_tensor(dyb).to(DEV))
+    torch.cuda.synchronize()
+    assert_routing_equal(sv, r)
+    hist = np.diff(r.offsets)
+    e_hot = int(np.argmax(hist))
+    single = np.nonzero((hist > 32) & (hist <= 128))[0]
+    e_one = int(single[0]) if len(single) else int(np.nonzero(hist > 0)[0][-1])
+    assert hist[e_hot] > 20 * 128 and hist[e_hot] % 128 != 0
+    rng = np.random.default_rng(0)
+    toks = np.sort(rng.choice(T, size=4, replace=False))
+    need = np.union1d(np.unique(r.idx[toks]), [e_hot, e_one])
+    _say(f"hottest expert {e_hot} ({hist[e_hot]} rows), single-tile expert {e_one} "
+         f"({hist[e_one]} rows); oracle over {len(need)} experts")
+    ol, _ = oracle_layer(s, experts=need, threads=16)
+    assert_bytes_equal(dl, ol, need)
+    cache_dequant(ol, need)
+    pos = _sorted_positions(r, T * s.k)
+    h_gpu, a_gpu = to_f64(sv.h), to_f64(sv.a)
+    for e in (e_hot, e_one):
+        _, _, cache = moe.forward(ol, xb, routing=r, experts=[e])
+        fl = np.array(sorted(cache.keys()))
+        assert len(fl) == hist[e]
+        p = pos[fl]
+        assert_close(h_gpu[p], np.stack([cache[int(f)][0] for f in fl]), f"saved h (expert {e}, all rows)")
+        assert_close(a_gpu[p], np.stack([cache[int(f)][1] for f in fl]), f"saved a (expert {e}, all rows)")
+        del cache
+    ref, _, _ = moe.forward(ol, xb, tokens=toks, routing=r)
+    assert_close(to_f64(out)[toks], ref[toks], "out (sampled tokens)")
+    dref, _, _ = moe.backward_dx(ol, xb, dyb, tokens=toks, routing=r)
+    assert_close(to_f64(dx)[toks], dref[toks], "dX (sampled tokens)")
+    assert torch.isfinite(out.float()).all() and torch.isfinite(dx.float()).all()
+
+
+@pytest.mark.timeout(900)
+def test_gpt_oss_20b_layer_16384_tokens_lora_checkpointing():
+    # Gradient checkpointing: a forward whose activations are dropped, the
+    # recompute forward that saves them, then dX + dA/dB.  The recompute
+    # must reproduce the first pass bit for bit (routing, permutation, h, a,
+    # the adapter projection v and out).
+    from mxfp4_weight_mixture_02_amd import SavedState
+    s = syn.spec("20b_16384_lora")
+    T = s.T
+    dl, xb, r = _device_and_routing(s, T)
+    x = bf16_tensor(xb).to(DEV)
+    _say("forward (activations dropped)")
+    out0, _ = mxfp4_moe_forward(dl, x, saved=None)
+    out1, sv1 = mxfp4_moe_forward(dl, x, saved=True)
+    _say("recompute forward")
+    sv2 = SavedState.empty(dl, T, DEV)
+    out2, _ = mxfp4_moe_forward(dl, x, saved=sv2)
+    torch.cuda.synchronize()
+    assert torch.equal(out0.view(torch.int16), out2.view(torch.int16))
+    assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
+    for n in ("topk_idx", "topk_w", "expert_offsets", "sorted_rows", "h", "a", "lora_v"):
+        assert torch.equal(getattr(sv1, n).view(torch.uint8), getattr(sv2, n).view(torch.uint8)), n
+    del sv1
+    assert_routing_equal(sv2, r)
+    _say("backward")
+    dyb = syn.upstream_grad(s, T)
+    dx, dA, dB = mxfp4_moe_backward_dx(dl, sv2, bf16_tensor(dyb).to(DEV))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(0)
+    toks = np.sort(rng.choice(T, size=64, replace=False))
+    hist = np.diff(r.offsets)
+    e_full = int(np.argmin(np.where(hist > 0, hist, np.iinfo(np.int64).max)))
+    need = np.union1d(np.unique(r.idx[toks]), [e_full])
+    _say(f"oracle over {len(need)} experts: 64 tokens, adapter gradients of expert {e_full} "
+         f"({hist[e_full]} rows)")
+    ol, _ = oracle_layer(s, experts=need, threads=16)
+    assert_bytes_equal(dl, ol, need)
+    cache_dequant(ol, need)
+    ref, _, cache = moe.forward(ol, xb, tokens=toks, routing=r)
+    assert_close(to_f64(out2)[toks], ref[toks], "out (64 tokens)")
+    pos = _sorted_positions(r, T * s.k)
+    fl = np.array(sorted(cache.keys()))
+    aref = np.stack([cache[int(f)][1] for f in fl])
+    assert_close(to_f64(sv2.a)[pos[fl]], aref, "saved a (64 tokens)")
+    assert_close(to_f64(sv2.h)[pos[fl]], np.stack([cache[int(f)][0] for f in fl]), "saved h (64 tokens)")
+    ef = np.searchsorted(r.offsets, pos[fl], side="right") - 1
+    vref = np.stack([moe._lora_v(ol, ef[i], aref[i][None])[0] for i in range(len(fl))])
+    assert_close(to_f64(sv2.lora_v)[pos[fl]], vref, "saved lora_v (64 tokens)")
+    dref, _, _ = moe.backward_dx(ol, xb, dyb, tokens=toks, routing=r, want_lora=False)
+    assert_close(to_f64(dx)[toks], dref[toks], "dX (64 tokens)")
+    _, dAr, dBr = moe.backward_dx(ol, xb, dyb, routing=r, experts=[e_full])
+    assert_close(to_f64(dA[e_full]), dAr[e_full], "dA (one expert, all rows)")
+    assert_close(to_f64(dB[e_full]), dBr[e_full], "dB (one expert, all rows)")
+    # every expert: <dA, A> = <dB, B> (both are s * dL/ds)
+    ipA = float((dA.double() * dl.lora_A.double()).sum())
+    ipB = float((dB.double() * dl.lora_B.double()).sum())
+    assert abs(ipA - ipB) <= 1e-2 * max(abs(ipA), abs(ipB)), (ipA, ipB)
+    assert torch.isfinite(out2.float()).all() and torch.isfinite(dx.float()).all()

@@ -1,5 +1,6 @@
-"""Pins of the oracle's MoE block against things other than itself: exact
-sums (math.fsum), brute-force top-k, scipy's softmax, a brute-force double
+"""Pins of the oracle's MoE block against things other than itself: the
+bf16 decode against its bit-field definition and torch's conversion over
+all 65536 patterns, exact sums (math.fsum), brute-force top-k, scipy's softmax, a brute-force double
 loop for the permutation, torch's silu, a per-token brute-force expert loop,
 the dense-MLP special case (E = 1, k = 1) written with torch, closed forms
 for zero weights and for bias perturbations, and float64 central finite
@@ -30,10 +31,51 @@ def tiny_x():
     return syn.tokens(TINY)
 
 
+# ------------------------------------------------------------- bf16 decode
+
+def _bf16_closed_form(b):
+    """Value of one bf16 bit pattern from its fields: sign bit 15, an 8-bit
+    exponent (bits 14..7, bias 127) and a 7-bit fraction with a hidden 1
+    unless the exponent field is 0 (subnormal); exponent 255 is Inf or
+    NaN."""
+    sign = -1.0 if b >> 15 else 1.0
+    e = (b >> 7) & 0xFF
+    m = b & 0x7F
+    if e == 0xFF:
+        return sign * math.inf if m == 0 else math.nan
+    if e == 0:
+        return sign * math.ldexp(m, -126 - 7)
+    return sign * math.ldexp(128 + m, e - 127 - 7)
+
+
+def _same_values(got, ref):
+    got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))   # -0.0 stays -0.0
+
+
+def test_bf16_decode_every_pattern_closed_form():
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    _same_values(moe.bf16_to_f64(bits), [_bf16_closed_form(int(b)) for b in bits])
+
+
+def test_bf16_decode_every_pattern_torch():
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    _same_values(moe.bf16_to_f64(bits), ref)
+    # shapes are kept, and float64 input is taken as already decoded
+    assert moe.bf16_to_f64(bits.reshape(256, 256)).shape == (256, 256)
+    probe = np.array([0.1, -3.0])
+    assert moe.bf16_to_f64(probe) is probe
+
+
 # ------------------------------------------------------------------ router
 
 def test_router_logits_exact_sum(tiny, tiny_x):
-    x = moe.bf16_to_f64(tiny_x)
+    # x decoded from its bit fields here, independently of bf16_to_f64
+    x = np.array([[_bf16_closed_form(int(b)) for b in row] for row in tiny_x])
     got = moe.router_logits(tiny, tiny_x)
     for t in range(x.shape[0]):
         for e in range(tiny.E):
