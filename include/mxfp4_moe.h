@@ -22,7 +22,8 @@
  * Conventions for every entry point
  *  - All tensors are dense, row-major (last dimension contiguous), in
  *    device memory owned by the caller.  The library allocates no device
- *    memory; scratch comes in through `workspace`.
+ *    memory; scratch comes in through `workspace` (mxfp4_moe_forward_noalloc
+ *    uses a fixed static device array instead).
  *  - bf16 tensors are passed as uint16_t bit patterns.
  *  - `stream` is a hipStream_t (NULL = the default stream).  Work is
  *    enqueued on it asynchronously with no host synchronisation, so calls
@@ -171,6 +172,27 @@ size_t mxfp4_moe_workspace_bytes(const mxfp4_moe_dims* dims, int mode);
 int mxfp4_moe_forward(const mxfp4_moe_dims* dims, const mxfp4_moe_weights* w,
                       const uint16_t* x, uint16_t* out, const mxfp4_moe_saved* saved,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Forward that allocates nothing and takes no workspace, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation.  Same arguments, checks,
+ * kernels and results (bit for bit) as mxfp4_moe_forward, except that its
+ * scratch is a static device array of MXFP4_NOALLOC_SCRATCH_BYTES inside
+ * the library (one copy per GPU, held until the process ends; its address
+ * is looked up once per device with hipGetSymbolAddress, on the first call
+ * made with that device current).  Dims whose forward needs more scratch
+ * than that -- mxfp4_moe_workspace_bytes() of MXFP4_WS_FORWARD or
+ * MXFP4_WS_FORWARD_SAVED -- are refused with MXFP4_EUNSUPPORTED before
+ * anything is enqueued (16 MiB covers every decode-size forward, T * k <=
+ * 256, and the 20b layer up to about 350 tokens).  The stream must belong
+ * to the current device.  Calls on one GPU share its array: calls that
+ * overlap (several streams, or several threads) race; calls ordered on one
+ * stream do not.  Nothing in the array needs to start zeroed (every byte a
+ * call reads was written earlier in that call). */
+#define MXFP4_NOALLOC_SCRATCH_BYTES (16u << 20)
+int mxfp4_moe_forward_noalloc(const mxfp4_moe_dims* dims, const mxfp4_moe_weights* w,
+                              const uint16_t* x, uint16_t* out, const mxfp4_moe_saved* saved,
+                              void* stream);
 
 /* Activation-gradient backward of the expert block for the loss
  * sum(dY * out), base weights and biases frozen ([P1]: LoRA training needs

@@ -220,64 +220,10 @@ int launch_timed(F&& enqueue, const char* name, hipStream_t s) {
     if (rc_ != MXFP4_OK) return rc_;                                  \
   } while (0)
 
-}  // namespace
-
-extern "C" {
-
-const char* mxfp4_last_error(void) { return g_err; }
-
-int mxfp4_moe_kernel_timing(int enable) {
-  std::lock_guard<std::mutex> g(g_timer.mu);
-  g_timer.drain();
-  g_timer.totals.clear();
-  g_timer.on = enable != 0;
-  return ok();
-}
-
-int mxfp4_moe_kernel_times(const char** names, double* total_ms, int* launches, int max_kernels) {
-  std::lock_guard<std::mutex> g(g_timer.mu);
-  g_timer.drain();
-  const int n = (int)g_timer.totals.size();
-  for (int i = 0; i < n && i < max_kernels; ++i) {
-    if (names) names[i] = g_timer.totals[i].name;
-    if (total_ms) total_ms[i] = g_timer.totals[i].ms;
-    if (launches) launches[i] = g_timer.totals[i].launches;
-  }
-  ok();
-  return n;
-}
-
-size_t mxfp4_moe_workspace_bytes(const mxfp4_moe_dims* dims, int mode) {
-  if (check_dims(dims) != MXFP4_OK) return 0;
-  if (mode < MXFP4_WS_FORWARD || mode > MXFP4_WS_BACKWARD) {
-    fail(MXFP4_EINVAL, "unknown workspace mode %d", mode);
-    return 0;
-  }
-  ok();
-  return layout(*dims, mode).total;
-}
-
-int mxfp4_moe_saved_bytes(const mxfp4_moe_dims* dims, mxfp4_moe_saved_sizes* out) {
-  const int rc = check_dims(dims);
-  if (rc) return rc;
-  if (!out) return fail(MXFP4_EINVAL, "out is required");
-  const mxfp4_moe_dims& d = *dims;
-  const size_t T = (size_t)d.T, R = T * (size_t)d.k, I = (size_t)d.I;
-  mxfp4_moe_saved_sizes z;
-  z.topk_idx = T * d.k * sizeof(int32_t);
-  z.topk_w = T * d.k * sizeof(float);
-  z.expert_offsets = ((size_t)d.E + 1) * sizeof(int32_t);
-  z.sorted_rows = R * sizeof(int32_t);
-  z.h = R * 2 * I * sizeof(uint16_t);
-  z.a = R * I * sizeof(uint16_t);
-  z.lora_v = R * (size_t)d.lora_rank * sizeof(float);
-  *out = z;
-  return ok();
-}
-
-int mxfp4_moe_forward(const mxfp4_moe_dims* dims, const mxfp4_moe_weights* w, const uint16_t* x,
-                      uint16_t* out, const mxfp4_moe_saved* saved, void* workspace,
-                      size_t workspace_bytes, void* stream) {
+// Validation shared by the two forward entry points (everything but the
+// scratch memory).
+int check_forward(const mxfp4_moe_dims* dims, const mxfp4_moe_weights* w, const uint16_t* x,
+                  const uint16_t* out, const mxfp4_moe_saved* saved) {
   int rc = check_dims(dims);
   if (rc) return rc;
   rc = check_weights(w, *dims);
@@ -294,13 +240,16 @@ int mxfp4_moe_forward(const mxfp4_moe_dims* dims, const mxfp4_moe_weights* w, co
     if (d.lora_rank && (!saved->lora_v || !aligned(saved->lora_v, 16)))
       return fail(MXFP4_EINVAL, "lora_rank > 0: saved lora_v is required, 16-byte aligned");
   }
+  return MXFP4_OK;
+}
+
+// The forward's launches on stream s, with the workspace laid out by
+// layout(d, mode) at `workspace` (validated by the caller).
+int enqueue_forward(const mxfp4_moe_dims& d, const mxfp4_moe_weights* w, const uint16_t* x,
+                    uint16_t* out, const mxfp4_moe_saved* saved, void* workspace,
+                    hipStream_t s) {
   const int mode = saved ? MXFP4_WS_FORWARD_SAVED : MXFP4_WS_FORWARD;
   const Layout L = layout(d, mode);
-  if (!workspace || workspace_bytes < L.total)
-    return fail(MXFP4_EWORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, L.total);
-  if (!aligned(workspace, ALIGN)) return fail(MXFP4_EINVAL, "workspace must be 256-byte aligned");
-
-  hipStream_t s = static_cast<hipStream_t>(stream);
   const int T = (int)d.T, H = (int)d.H, I = (int)d.I, E = d.E, k = d.k;
   const int64_t R = d.T * d.k;
   int32_t* topk_idx = saved ? saved->topk_idx : at<int32_t>(workspace, L.topk_idx);
@@ -359,6 +308,116 @@ int mxfp4_moe_forward(const mxfp4_moe_dims* dims, const mxfp4_moe_weights* w, co
          "down");
   LAUNCH(mxmoe::launch_combine(y_w, d.T, H, k, out, s), "combine");
   return ok();
+}
+
+// Scratch of the no-allocation forward: one file-scope device array, of
+// which every GPU the library runs on holds its own copy until the process
+// ends.  Host code never uses the array's name as an address (on the host
+// it is only a stand-in for the symbol): device_scratch() looks up this
+// device's address once, with hipGetSymbolAddress, and kernels get that.
+static __device__ __align__(256) uint8_t scratch[MXFP4_NOALLOC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[MAX_DEVICES] = {};
+
+int device_scratch(void** out) {
+  int dev = 0;
+  int rc = hip_status(hipGetDevice(&dev), "hipGetDevice");
+  if (rc) return rc;
+  if (dev < 0 || dev >= MAX_DEVICES) return fail(MXFP4_EUNSUPPORTED, "device %d >= %d", dev, MAX_DEVICES);
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    rc = hip_status(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    if (rc) return rc;
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return MXFP4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mxfp4_last_error(void) { return g_err; }
+
+int mxfp4_moe_kernel_timing(int enable) {
+  std::lock_guard<std::mutex> g(g_timer.mu);
+  g_timer.drain();
+  g_timer.totals.clear();
+  g_timer.on = enable != 0;
+  return ok();
+}
+
+int mxfp4_moe_kernel_times(const char** names, double* total_ms, int* launches, int max_kernels) {
+  std::lock_guard<std::mutex> g(g_timer.mu);
+  g_timer.drain();
+  const int n = (int)g_timer.totals.size();
+  for (int i = 0; i < n && i < max_kernels; ++i) {
+    if (names) names[i] = g_timer.totals[i].name;
+    if (total_ms) total_ms[i] = g_timer.totals[i].ms;
+    if (launches) launches[i] = g_timer.totals[i].launches;
+  }
+  ok();
+  return n;
+}
+
+size_t mxfp4_moe_workspace_bytes(const mxfp4_moe_dims* dims, int mode) {
+  if (check_dims(dims) != MXFP4_OK) return 0;
+  if (mode < MXFP4_WS_FORWARD || mode > MXFP4_WS_BACKWARD) {
+    fail(MXFP4_EINVAL, "unknown workspace mode %d", mode);
+    return 0;
+  }
+  ok();
+  return layout(*dims, mode).total;
+}
+
+int mxfp4_moe_saved_bytes(const mxfp4_moe_dims* dims, mxfp4_moe_saved_sizes* out) {
+  const int rc = check_dims(dims);
+  if (rc) return rc;
+  if (!out) return fail(MXFP4_EINVAL, "out is required");
+  const mxfp4_moe_dims& d = *dims;
+  const size_t T = (size_t)d.T, R = T * (size_t)d.k, I = (size_t)d.I;
+  mxfp4_moe_saved_sizes z;
+  z.topk_idx = T * d.k * sizeof(int32_t);
+  z.topk_w = T * d.k * sizeof(float);
+  z.expert_offsets = ((size_t)d.E + 1) * sizeof(int32_t);
+  z.sorted_rows = R * sizeof(int32_t);
+  z.h = R * 2 * I * sizeof(uint16_t);
+  z.a = R * I * sizeof(uint16_t);
+  z.lora_v = R * (size_t)d.lora_rank * sizeof(float);
+  *out = z;
+  return ok();
+}
+
+int mxfp4_moe_forward(const mxfp4_moe_dims* dims, const mxfp4_moe_weights* w, const uint16_t* x,
+                      uint16_t* out, const mxfp4_moe_saved* saved, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  int rc = check_forward(dims, w, x, out, saved);
+  if (rc) return rc;
+  const Layout L = layout(*dims, saved ? MXFP4_WS_FORWARD_SAVED : MXFP4_WS_FORWARD);
+  if (!workspace || workspace_bytes < L.total)
+    return fail(MXFP4_EWORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, L.total);
+  if (!aligned(workspace, ALIGN)) return fail(MXFP4_EINVAL, "workspace must be 256-byte aligned");
+  return enqueue_forward(*dims, w, x, out, saved, workspace, static_cast<hipStream_t>(stream));
+}
+
+int mxfp4_moe_forward_noalloc(const mxfp4_moe_dims* dims, const mxfp4_moe_weights* w,
+                              const uint16_t* x, uint16_t* out, const mxfp4_moe_saved* saved,
+                              void* stream) {
+  int rc = check_forward(dims, w, x, out, saved);
+  if (rc) return rc;
+  const Layout L = layout(*dims, saved ? MXFP4_WS_FORWARD_SAVED : MXFP4_WS_FORWARD);
+  if (L.total > MXFP4_NOALLOC_SCRATCH_BYTES)
+    return fail(MXFP4_EUNSUPPORTED,
+                "these dims need %zu bytes of scratch; the static scratch holds %zu (use "
+                "mxfp4_moe_forward with a workspace)", L.total, (size_t)MXFP4_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  rc = device_scratch(&ws);
+  if (rc) return rc;
+  return enqueue_forward(*dims, w, x, out, saved, ws, static_cast<hipStream_t>(stream));
 }
 
 int mxfp4_moe_backward_dx(const mxfp4_moe_dims* dims, const mxfp4_moe_weights* w,

@@ -72,6 +72,9 @@ def lib() -> ctypes.CDLL:
         L.mxfp4_moe_forward.restype = i32
         L.mxfp4_moe_forward.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Weights), vp, vp,
                                         ctypes.POINTER(Saved), vp, ctypes.c_size_t, vp]
+        L.mxfp4_moe_forward_noalloc.restype = i32
+        L.mxfp4_moe_forward_noalloc.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Weights), vp,
+                                                vp, ctypes.POINTER(Saved), vp]
         L.mxfp4_moe_backward_dx.restype = i32
         L.mxfp4_moe_backward_dx.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Weights),
                                             ctypes.POINTER(Saved), vp, vp, vp, vp, vp,
@@ -330,6 +333,31 @@ def mxfp4_moe_forward(layer: MoeLayer, x: torch.Tensor, saved: SavedState | bool
                                  _ptr(ws), ws.numel(), _stream())
     _check("mxfp4_moe_forward", rc)
     return out, saved
+
+
+def mxfp4_moe_forward_noalloc(layer: MoeLayer, x: torch.Tensor, out: torch.Tensor,
+                              saved: SavedState | None = None):
+    """The forward through mxfp4_moe_forward_noalloc: the library's static
+    scratch instead of a workspace, so nothing is allocated (the caller
+    passes ``out`` and, for a saved forward, the saved-state buffers).
+    Returns out."""
+    layer.check_shapes()
+    if x.dim() != 2:
+        raise ValueError(f"x must be [T, H], got {tuple(x.shape)}")
+    T = x.shape[0]
+    _shape(x, (T, layer.H), torch.bfloat16, "x")
+    _shape(out, (T, layer.H), torch.bfloat16, "out")
+    if saved is not None:
+        saved.check_shapes(layer, T)
+    _dev(x, torch.bfloat16, "x")
+    _dev(out, torch.bfloat16, "out")
+    d = layer.dims(T)
+    w = layer.weights()
+    sv = saved.struct() if saved is not None else None
+    rc = lib().mxfp4_moe_forward_noalloc(ctypes.byref(d), ctypes.byref(w), _ptr(x), _ptr(out),
+                                         ctypes.byref(sv) if sv is not None else None, _stream())
+    _check("mxfp4_moe_forward_noalloc", rc)
+    return out
 
 
 def mxfp4_moe_backward_dx(layer: MoeLayer, saved: SavedState, dy: torch.Tensor,

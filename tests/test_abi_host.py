@@ -10,7 +10,7 @@ from mxfp4_weight_mixture_02_amd import native
 from mxfp4_weight_mixture_02_amd.native import Dims, Saved, SavedSizes, Weights
 
 EXPECTED = {"mxfp4_moe_workspace_bytes", "mxfp4_moe_saved_bytes", "mxfp4_moe_forward",
-            "mxfp4_moe_backward_dx",
+            "mxfp4_moe_forward_noalloc", "mxfp4_moe_backward_dx",
             "mxfp4_quantize", "mxfp4_dequantize", "mxfp4_last_error",
             "mxfp4_moe_kernel_timing", "mxfp4_moe_kernel_times"}
 
@@ -123,6 +123,23 @@ def test_forward_validation(L):
     rc = L.mxfp4_moe_forward(ctypes.byref(d), ctypes.byref(w), FAKE, FAKE, ctypes.byref(sv),
                              FAKE, ws, None)
     assert rc == -1 and "saved" in _err(L)
+
+
+def test_noalloc_forward_validation(L):
+    # the same argument checks as mxfp4_moe_forward, then the scratch limit,
+    # all before the device is touched
+    d = _dims()
+    w = _weights()
+    rc = L.mxfp4_moe_forward_noalloc(ctypes.byref(d), ctypes.byref(w), None, FAKE, None, None)
+    assert rc == -1 and "x and out" in _err(L)
+    rc = L.mxfp4_moe_forward_noalloc(ctypes.byref(_dims(H=80)), ctypes.byref(w), FAKE, FAKE, None,
+                                     None)
+    assert rc == -2
+    big = _dims(T=2048, H=2880, I=2880, E=32, k=4)
+    need = L.mxfp4_moe_workspace_bytes(ctypes.byref(big), 0)
+    assert need > (16 << 20)
+    rc = L.mxfp4_moe_forward_noalloc(ctypes.byref(big), ctypes.byref(w), FAKE, FAKE, None, None)
+    assert rc == -2 and "scratch" in _err(L)
 
 
 def test_backward_validation(L):
