@@ -44,6 +44,7 @@ struct Layout {
   // offsets into the workspace; SIZE_MAX = not placed
   size_t topk_idx = SIZE_MAX, topk_w = SIZE_MAX, offsets = SIZE_MAX, sorted_rows = SIZE_MAX,
          a = SIZE_MAX, blk_hist = SIZE_MAX, tiles = SIZE_MAX, num_tiles = SIZE_MAX,
+         tiles_l = SIZE_MAX, num_tiles_l = SIZE_MAX,
          y_w = SIZE_MAX, dh = SIZE_MAX, dw_part = SIZE_MAX, dxr = SIZE_MAX,
          lora_v = SIZE_MAX, lora_At = SIZE_MAX, lora_Bt = SIZE_MAX, lora_dvu = SIZE_MAX,
          logits = SIZE_MAX, logit_part = SIZE_MAX;
@@ -83,7 +84,7 @@ int check_dims(const mxfp4_moe_dims* d) {
 Layout layout(const mxfp4_moe_dims& d, int mode) {
   Layout L;
   const size_t R = (size_t)(d.T * d.k);
-  const int maxt = mxmoe::max_tiles((int64_t)R, d.E);
+  const int maxt = mxmoe::max_tiles((int64_t)R, d.E, mxmoe::MT);
   if (mode == MXFP4_WS_FORWARD || mode == MXFP4_WS_FORWARD_SAVED) {
     if (mode == MXFP4_WS_FORWARD) {
       L.topk_idx = L.put(R * 4);
@@ -101,8 +102,14 @@ Layout layout(const mxfp4_moe_dims& d, int mode) {
     L.num_tiles = L.put(4);
     L.y_w = L.put(R * (size_t)d.H * 2);
   } else {
-    L.tiles = L.put((size_t)maxt * sizeof(mxmoe::Tile));
+    // the backward GEMMs' tiles (BMT rows); with LoRA also the MT-row tiles
+    // of the adapter projection
+    L.tiles = L.put((size_t)mxmoe::max_tiles((int64_t)R, d.E, mxmoe::BMT) * sizeof(mxmoe::Tile));
     L.num_tiles = L.put(4);
+    if (d.lora_rank) {
+      L.tiles_l = L.put((size_t)maxt * sizeof(mxmoe::Tile));
+      L.num_tiles_l = L.put(4);
+    }
     L.dh = L.put(R * (size_t)d.I * 2 * 2);
     L.dw_part = L.put(R * (size_t)mxmoe::bwd_down_ntiles((int)d.I) * 4);
     L.dxr = L.put(R * (size_t)d.H * 2);
@@ -263,7 +270,7 @@ int enqueue_forward(const mxfp4_moe_dims& d, const mxfp4_moe_weights* w, const u
   int32_t* num_tiles = at<int32_t>(workspace, L.num_tiles);
   uint16_t* y_w = at<uint16_t>(workspace, L.y_w);
   float* lora_v = !d.lora_rank ? nullptr : saved ? saved->lora_v : at<float>(workspace, L.lora_v);
-  const int maxt = mxmoe::max_tiles(R, E);
+  const int maxt = mxmoe::max_tiles(R, E, mxmoe::MT);
 
   float* logits = at<float>(workspace, L.logits);
   if (mxmoe::plan_fits(d.T, E, k)) {
@@ -453,19 +460,24 @@ int mxfp4_moe_backward_dx(const mxfp4_moe_dims* dims, const mxfp4_moe_weights* w
   uint16_t* dh = at<uint16_t>(workspace, L.dh);
   float* dw_part = at<float>(workspace, L.dw_part);
   uint16_t* dxr = at<uint16_t>(workspace, L.dxr);
-  const int maxt = mxmoe::max_tiles(R, E);
+  const int maxt = mxmoe::max_tiles(R, E, mxmoe::BMT);
   const int r = d.lora_rank;
+  mxmoe::Tile* tiles_l = r ? at<mxmoe::Tile>(workspace, L.tiles_l) : nullptr;
+  int32_t* num_tiles_l = r ? at<int32_t>(workspace, L.num_tiles_l) : nullptr;
   uint16_t* lora_At = r ? at<uint16_t>(workspace, L.lora_At) : nullptr;
   uint16_t* lora_Bt = r ? at<uint16_t>(workspace, L.lora_Bt) : nullptr;
   float* lora_dvu = r ? at<float>(workspace, L.lora_dvu) : nullptr;
 
-  LAUNCH(mxmoe::launch_build_tiles(saved->expert_offsets, E, tiles, num_tiles, s), "bwd_tiles");
+  LAUNCH(mxmoe::launch_build_tiles(saved->expert_offsets, E, mxmoe::BMT, tiles, num_tiles,
+                                   mxmoe::MT, tiles_l, num_tiles_l, s),
+         "bwd_tiles");
   if (r) {
     LAUNCH(mxmoe::launch_transpose_bf16(w->lora_A, E, r, I, lora_At, s), "lora_transpose");
     LAUNCH(mxmoe::launch_transpose_bf16(w->lora_B, E, H, r, lora_Bt, s), "lora_transpose");
     // dv_u = s dY_t B_e over the token rows of dY
-    LAUNCH(mxmoe::launch_lora_proj(dy, true, saved->sorted_rows, k, lora_Bt, H, tiles, num_tiles,
-                                   maxt, d.lora_scale, lora_dvu, s),
+    LAUNCH(mxmoe::launch_lora_proj(dy, true, saved->sorted_rows, k, lora_Bt, H, tiles_l,
+                                   num_tiles_l, mxmoe::max_tiles(R, E, mxmoe::MT), d.lora_scale,
+                                   lora_dvu, s),
            "lora_dvu");
   }
   LAUNCH(mxmoe::launch_bwd_down(dy, w->dn_codes, w->dn_scales, saved->topk_w, saved->sorted_rows,

@@ -202,7 +202,8 @@ __device__ __forceinline__ bool xcd_work_item(int live_row_tiles, int col_tiles,
   return true;
 }
 
-constexpr int MT = 128;      // routed rows per GEMM tile
+constexpr int MT = 128;      // routed rows per forward GEMM tile
+constexpr int BMT = 256;     // routed rows per backward GEMM tile
 constexpr int LORA_R = 16;   // supported LoRA rank: one 16-deep MFMA contraction
 
 }  // namespace mxmoe

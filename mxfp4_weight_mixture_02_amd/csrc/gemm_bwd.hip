@@ -1,9 +1,9 @@
 // Backward (dX) grouped expert GEMMs on gfx950 MFMA, over the same packed
-// MXFP4 weights the forward reads, now contracted over their stored row
-// axis ("Add MXFP4 training support via a dequantize-on-the-fly fallback":
-// the backward of the frozen base only needs input and adapter gradients;
-// the fallback recomputes dequantisation, which here happens once per
-// workgroup tile in LDS).
+// MXFP4 weights the forward reads, contracted over their stored row axis
+// ("Add MXFP4 training support via a dequantize-on-the-fly fallback": the
+// backward of the frozen base only needs input and adapter gradients; the
+// fallback recomputes dequantisation, which here happens in registers right
+// before the matrix cores use it).
 //
 // bwd_down:    da_u[p, i] = sum_h dY[t(p), h] * deq(Wd[e, h, i])
 //              epilogue: dw partial sum_i da_u * a, then the SwiGLU backward
@@ -14,354 +14,490 @@
 // bwd_combine: dX[t] = sum_j dxr[(t,j)] + sum_j dl_j * Wr[idx_j], with the
 //              softmax-over-selected gradient dl_j = w_j (dw_j - sum_i w_i dw_i).
 //
-// Transposed operand.  The MFMA wants 8 consecutive contraction elements
-// per lane, but the packed rows run along the output axis and the UE8M0
-// scales are blocked along it too.  Each thread therefore loads 8x8 blocks
-// (8 stored rows x one dword of 8 codes), decodes each row with its own
-// scale (one scaled conversion per code pair), transposes the bf16 block in
-// registers with byte permutes, and writes 8 contraction-ordered 16-byte
-// rows into LDS; the MFMA A-operand is then one 16-byte LDS read.
+// Both GEMMs compute out[p][o] = sum_c act[p][c] * W[c][o] with W stored
+// [C rows][O cols] (codes packed along o, one UE8M0 scale per 32 o): the
+// contraction runs along the stored row axis, and the scales vary along the
+// output axis.
 //
-// Tiling.  A workgroup computes 512 output columns x 128 routed rows with 8
-// waves, two per SIMD; wave w owns output columns 64w..64w+63 (two
-// 32-column MFMA blocks) for all 128 rows (four 32-row blocks): 8
-// accumulators of 32x32 fp32.  Per K step of 64 a wave reads 2 A- and 4
-// B-fragments per 8 MFMAs from LDS; the second wave per SIMD hides the
-// other's LDS and load waits (measured faster than one wave with four
-// column blocks, which reads less LDS per MFMA).
+// Weight path.  The workgroup's slice of each 64-row step (64 stored rows x
+// 256 columns: 8 KB of packed codes) is copied into LDS as raw bytes, and
+// its 64 x 8 scale bytes into a transposed LDS table of scale operands
+// (s << 23, the form the scaled conversion takes).  The MFMA A-operand needs
+// 8 consecutive c of one output column per lane.  gfx950's 8-bit
+// transposing LDS read (ds_read_b64_tr_b8) gives each lane 8 rows x one
+// code byte, i.e. 8 consecutive c for the column pair (2m, 2m+1); the lane
+// decodes each byte with its own row's scale (one scaled fp4 -> bf16
+// conversion per byte, exact) and splits the 8 packed pairs into the even
+// and the odd column's fragment with byte permutes.  So the MFMA rows of one
+// such fragment pair are the even and the odd columns of a 64-column
+// double block, and LDS holds 4 bits per weight instead of 16: a quarter of
+// the bytes written and read of a decoded bf16 tile (gfx950's LDS writes run
+// at well under half its read rate).
 //
-// LDS: the transposed weights [512][64] bf16 and the activations [128][64]
-// bf16, both double-buffered, exactly 160 KB, no padding.  Row r's eight
-// 16-byte blocks are permuted by XOR with f(r) = (r ^ (r >> 3)) & 7 for
-// the weights and r & 7 for the activations; the MFMA reads (32
-// consecutive rows, one logical block), the transposed writes (rows 8j+c
-// for 64 consecutive j) and the activation writes (8 blocks of one row)
-// then each touch 8 distinct 16-byte bank groups per 8 lanes.
+// Activation path (the B-operand, contraction-contiguous in memory): a
+// thread loads 8 x 16 bytes of the workgroup's 256 rows per step into
+// registers, one step ahead, and stores them to an LDS stage; the MFMA reads
+// them with 16-byte LDS reads.
+//
+// Tiling.  A workgroup is 8 waves (two per SIMD, so one wave's decode and
+// LDS traffic overlap the other's MFMAs) and computes 256 routed rows (one
+// 256-row tile of an expert) x 256 output columns.  Wave w = (wo, wp) owns
+// the 64-column double block wo (two MFMA row blocks: its even and its odd
+// columns) and the 32-row blocks wp, wp + 2, wp + 4, wp + 6 of the tile
+// (interleaved, so a partial tile splits its live blocks evenly): 8
+// accumulators of 32 x 32 fp32, 128 registers.
+//
+// Pipeline (one barrier per 64-deep step k): stage step k + 1's codes,
+// scales and activations (loaded during step k - 1) into the other LDS
+// stage and reload the registers with step k + 2's; then for each 16-deep
+// sub-step the next sub-step's LDS reads, its decode, and this sub-step's
+// 16 MFMAs, interleaved; the barrier sits before the last sub-step's MFMAs,
+// after which the next step's first reads issue.  Step indices are clamped
+// at the end instead of branching around loads; rows past the tile and
+// columns past O read valid memory whose products are never stored.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace mxmoe {
 
-constexpr int BW = 8;                      // waves per workgroup, two per SIMD
-constexpr int BTHR = 64 * BW;
-constexpr int BRB = 2;                     // 32-column output blocks per wave
-constexpr int BNT = 32 * BRB * BW;         // output columns per workgroup (512)
-constexpr int BKC = 64;                    // contraction per step
-constexpr int BBLK = (BKC / 8) * (BNT / 8) / BTHR;   // 8x8 weight blocks per thread per step (1)
-constexpr int BPPT = MT * 8 / BTHR;        // 16-byte activation pieces per thread per step (2)
-constexpr int WS_BYTES = BNT * BKC * 2;    // one weight buffer (64 KB)
-constexpr int XS_BYTES = MT * BKC * 2;     // one activation buffer (16 KB)
-constexpr int BLDS = 2 * WS_BYTES + 2 * XS_BYTES;    // 160 KB
-static_assert(BNT == 512, "thread work assumed below");
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 
-__device__ __forceinline__ int ws_off(int row, int blk) {
-  return row * 128 + ((blk ^ ((row ^ (row >> 3)) & 7)) << 4);
-}
-__device__ __forceinline__ int xs_off(int row, int blk) {
-  return row * 128 + ((blk ^ (row & 7)) << 4);
-}
+constexpr int GW = 8;                       // waves per workgroup, two per SIMD
+constexpr int GTHR = 64 * GW;
+constexpr int GO = 256;                     // output columns per workgroup
+constexpr int GKC = 64;                     // contraction per step
+constexpr int GCB = GKC * (GO / 2);         // code tile per step: 64 rows x 128 bytes (8 KB)
+constexpr int GSB = (GO / 32) * GKC * 4;    // scale-operand table per step: 8 x 64 words (2 KB)
+constexpr int GXB = BMT * GKC * 2;          // activation stage (32 KB)
+constexpr int GSTAGE = GCB + GSB + GXB;     // one stage (42 KB)
+constexpr int GLDS_LOOP = 2 * GSTAGE;       // main loop: two stages (84 KB)
+static_assert(BMT == 256, "tile rows assumed below");
 
-// Raw codes and scales of one thread's 8x8 block for one K step.
-struct RawBlock {
-  uint32_t code[8];
-  uint32_t scale[8];
-};
+// Chunk swizzle of activation row p (16-byte chunks; distinct banks for the
+// 16-byte reads of 8 and of 16 consecutive rows).
+__device__ __forceinline__ int x_swz(int p) { return (p & 7) ^ ((p >> 3) & 1); }
 
-// Addresses are the expert's (workgroup-uniform) bases plus 32-bit offsets:
-// one register per address instead of a 64-bit pointer pair.
-__device__ __forceinline__ void load_block(RawBlock& rb, const uint8_t* __restrict__ cbase,
-                                           const uint8_t* __restrict__ sbase, uint32_t coff,
-                                           uint32_t soff, uint32_t crow, uint32_t srow) {
-#pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    rb.code[r] = *reinterpret_cast<const uint32_t*>(cbase + (coff + r * crow));
-    rb.scale[r] = sbase[soff + r * srow];
-  }
-}
-
-// Decode the 8x8 block (contraction rows 8cb.., output columns 8ob..) and
-// store it transposed: weight row 8ob + j gets the 8 contraction-ordered
-// bf16 of output column j, in logical block cb.
-// Column pair (2J, 2J+1) of the block's 8 rows, decoded with each row's
-// scale, split into two contraction-ordered weight rows with byte permutes.
-template <int J>
-__device__ __forceinline__ void store_block_col(const RawBlock& rb, uint8_t* ws, int ob, int cb) {
-  uint32_t d[8];
-#pragma unroll
-  for (int r = 0; r < 8; ++r)
-    d[r] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(
-                                            rb.code[r], scale_operand(rb.scale[r]), J));
-  u32x4 lo, hi;
-#pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    lo[m] = __builtin_amdgcn_perm(d[2 * m + 1], d[2 * m], 0x05040100u);
-    hi[m] = __builtin_amdgcn_perm(d[2 * m + 1], d[2 * m], 0x07060302u);
-  }
-  *reinterpret_cast<u32x4*>(ws + ws_off(8 * ob + 2 * J, cb)) = lo;
-  *reinterpret_cast<u32x4*>(ws + ws_off(8 * ob + 2 * J + 1, cb)) = hi;
-}
-
-// Decode the 8x8 block (contraction rows 8cb.., output columns 8ob..) and
-// store it transposed: weight row 8ob + j gets the 8 contraction-ordered
-// bf16 of output column j, in logical block cb.  One column pair at a time
-// keeps 8 decoded dwords live instead of 32.
-__device__ __forceinline__ void store_block_t(const RawBlock& rb, uint8_t* ws, int ob, int cb) {
-  store_block_col<0>(rb, ws, ob, cb);
-  store_block_col<1>(rb, ws, ob, cb);
-  store_block_col<2>(rb, ws, ob, cb);
-  store_block_col<3>(rb, ws, ob, cb);
-}
-
-// Per-thread state of the two-deep pipeline: registers of steps c+1 and c+2.
-struct BwdPipe {
-  u32x4 xv[2][BPPT];
-  RawBlock raw[2][BBLK];
-};
-
-struct BwdArgs {
-  const uint16_t* brow[BPPT];   // activation rows this thread stages (+ its 8-element piece)
-  const uint8_t* wcode;         // the expert's codes and scales (workgroup-uniform)
+// Per-lane addressing, fixed for the whole main loop (LDS offsets are
+// relative to a stage).
+struct GArgs {
+  const uint16_t* xbase;    // activations (workgroup-uniform)
+  uint32_t xoff[4];         // element offsets of the 4 activation pieces this lane stages (step 0)
+  const uint8_t* wcode;     // the expert's codes and scales (workgroup-uniform)
   const uint8_t* wscale;
-  uint32_t bcode[BBLK];         // byte offset of its weight blocks' first code row, at step 0
-  uint32_t bscale[BBLK];        // and of the first scale row (an expert is < 4 GiB)
-  uint32_t crow, srow;          // bytes between stored rows (codes, scales)
+  uint32_t coff;            // byte offset of this thread's 16-byte code piece (step 0)
+  uint32_t soff;            // byte offset of its scale byte (step 0)
+  uint32_t cstep, sstep;    // bytes per step of 64 stored rows
+  uint32_t csto;            // code-tile offset of its piece
+  uint32_t ssto;            // scale-table offset of its scale word
+  uint32_t aoff;            // code-tile offset of the transposing read (sub-step 0)
+  uint32_t sofs;            // scale-table offset of the lane's 8 scale words (sub-step 0)
+  uint32_t boff[4];         // activation-stage offsets of the B-fragment reads per sub-step (row block 0)
   int nsteps;
 };
 
-template <int PAR>
-__device__ __forceinline__ void bwd_issue(BwdPipe& pp, const BwdArgs& g, int c) {
-#pragma unroll
-  for (int j = 0; j < BPPT; ++j) pp.xv[PAR][j] = *reinterpret_cast<const u32x4*>(g.brow[j] + c * BKC);
-#pragma unroll
-  for (int i = 0; i < BBLK; ++i)
-    load_block(pp.raw[PAR][i], g.wcode, g.wscale, g.bcode[i] + (uint32_t)c * BKC * g.crow,
-               g.bscale[i] + (uint32_t)c * BKC * g.srow, g.crow, g.srow);
-}
+// One step's loads (a single register set: staged, then reloaded).
+struct GPipe {
+  u32x4 act[4];
+  u32x4 code;
+  uint32_t sc;
+};
 
-template <int PAR>
-__device__ __forceinline__ void bwd_stage(const BwdPipe& pp, uint8_t* lds) {
-  const int tid = threadIdx.x;
-  uint8_t* ws = lds + PAR * WS_BYTES;
-  uint8_t* xs = lds + 2 * WS_BYTES + PAR * XS_BYTES;
-#pragma unroll
-  for (int j = 0; j < BPPT; ++j) {
-    const int q = tid + j * BTHR;
-    *reinterpret_cast<u32x4*>(xs + xs_off(q >> 3, q & 7)) = pp.xv[PAR][j];
-  }
-#pragma unroll
-  for (int i = 0; i < BBLK; ++i) {
-    const int q = tid + i * BTHR;
-    store_block_t(pp.raw[PAR][i], ws, q & (BNT / 8 - 1), q / (BNT / 8));
-  }
-}
-
-template <int NRB, int PAR>
-__device__ __forceinline__ void bwd_step(BwdPipe& pp, const BwdArgs& g, int c, uint8_t* lds,
-                                         f32x16 (&acc)[BRB][4]) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int l32 = lane & 31, hlf = lane >> 5;
-  bwd_issue<PAR>(pp, g, min(c + 2, g.nsteps - 1));
-  __builtin_amdgcn_sched_barrier(0);  // keep the loads at the top of the step
-  bwd_stage<PAR ^ 1>(pp, lds);
-  const uint8_t* ws = lds + PAR * WS_BYTES;
-  const uint8_t* xs = lds + 2 * WS_BYTES + PAR * XS_BYTES;
-#pragma unroll
-  for (int st = 0; st < 4; ++st) {
-    const int lb = 4 * hlf + st;
-    bf16x8 a[BRB], b[NRB];
-#pragma unroll
-    for (int rb = 0; rb < BRB; ++rb)
-      a[rb] = *reinterpret_cast<const bf16x8*>(ws + ws_off(wave * 32 * BRB + rb * 32 + l32, lb));
-#pragma unroll
-    for (int tb = 0; tb < NRB; ++tb)
-      b[tb] = *reinterpret_cast<const bf16x8*>(xs + xs_off(tb * 32 + l32, lb));
-#pragma unroll
-    for (int rb = 0; rb < BRB; ++rb)
-#pragma unroll
-      for (int tb = 0; tb < NRB; ++tb)
-        acc[rb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[rb], b[tb], acc[rb][tb], 0, 0, 0);
-  }
-  // The next step reads what this one staged: wait for this wave's LDS
-  // stores (lgkmcnt) only.  A fenced __syncthreads would also drain the
-  // global loads of step c + 2 issued above; their registers get the
-  // compiler's own counted waits where they are used.
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
-  barrier_only();
-}
-
-// Pipeline: global loads run two K steps ahead.  In step c a thread issues
-// the loads of step c+2, stores the step c+1 data it loaded one step
-// earlier into the other LDS buffers (the weight blocks decoded and
-// transposed on the way), then the waves run the MFMAs of step c from LDS;
-// one barrier per step.  Step indices are clamped at the end instead of
-// branching around loads, so the compiler's wait counts stay exact.  The
-// loop is unrolled by two so every register set has a fixed name.
+// MFMA operand registers carried between sub-steps (and from one step to
+// the next): decoded A-fragments (even, odd) and B-fragments of two
+// sub-steps, and the raw transposed code bytes and scale words of the
+// sub-step being decoded.
 template <int NRB>
-__device__ __forceinline__ void bwd_loop(const BwdArgs& g, uint8_t* lds, f32x16 (&acc)[BRB][4]) {
-  BwdPipe pp;
-  bwd_issue<0>(pp, g, 0);
-  bwd_issue<1>(pp, g, min(1, g.nsteps - 1));
-  bwd_stage<0>(pp, lds);
-  __syncthreads();
-  int c = 0;
-  for (; c + 1 < g.nsteps; c += 2) {
-    bwd_step<NRB, 0>(pp, g, c, lds, acc);
-    bwd_step<NRB, 1>(pp, g, c + 1, lds, acc);
-  }
-  if (c < g.nsteps) bwd_step<NRB, 0>(pp, g, c, lds, acc);
-  __syncthreads();   // LDS is free for the epilogue
-}
+struct GFrags {
+  bf16x8 a[2][2];
+  bf16x8 b[2][NRB > 0 ? NRB : 1];
+  i32x2 raw;
+  f32x4 sc[2];
+};
 
-// Main loop shared by the two backward GEMMs.  W is stored [C rows][O
-// cols] (packed along O); this workgroup produces output columns o0..o0+511
-// for routed rows whose contraction vectors are brow[j] (length C).  Rows
-// past the tile point at its first row and weight blocks past the last
-// output column at the first one, so every load is unconditional (the
-// affected products are never stored); only the first NRB 32-row blocks
-// hold rows.
-__device__ __forceinline__ void bwd_mainloop(const uint16_t* const (&brow)[BPPT],
-                                             const uint8_t* __restrict__ wcode,
-                                             const uint8_t* __restrict__ wscale, int C, int O,
-                                             int o0, int nrb, uint8_t* lds,
-                                             f32x16 (&acc)[BRB][4]) {
-  const int tid = threadIdx.x;
-  BwdArgs g;
-  g.nsteps = C / BKC;
-  g.crow = O / 2;
-  g.srow = O / 32;
+// rowoff(p): element offset of activation row p (clamping rows past the
+// tile to a valid row).  C, O: contraction and output lengths; o0: the
+// workgroup's first output column.
+template <class RowOff>
+__device__ __forceinline__ void g_setup(GArgs& g, const uint16_t* xbase, RowOff rowoff,
+                                        const uint8_t* wcode, const uint8_t* wscale, int C,
+                                        int O, int o0) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wo = wave & 3;
+  g.xbase = xbase;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int p = 32 * wave + 8 * i + (lane >> 3);
+    g.xoff[i] = rowoff(p) + 8 * (uint32_t)((lane & 7) ^ x_swz(p));
+  }
   g.wcode = wcode;
   g.wscale = wscale;
+  // codes: row tid / 8, 16-byte chunk tid % 8 (32 columns)
+  const int c0 = tid >> 3, j = tid & 7;
+  const int col = (o0 + 32 * j < O) ? o0 + 32 * j : 0;   // past O: any valid column
+  g.coff = (uint32_t)c0 * (uint32_t)(O / 2) + col / 2;
+  g.csto = c0 * (GO / 2) + 16 * (j ^ (c0 & 7));
+  // scales: row tid / 8, scale block tid % 8 (the same 32 columns)
+  g.soff = (uint32_t)c0 * (uint32_t)(O / 32) + col / 32;
+  g.ssto = GCB + (j * GKC + c0) * 4;
+  g.cstep = (uint32_t)GKC * (O / 2);
+  g.sstep = (uint32_t)GKC * (O / 32);
+  // transposing read: 16-lane group grp reads rows 8 (grp / 2) .. + 7 of
+  // the sub-step, code chunk 2 wo + grp % 2 of double block wo; lane jj
+  // names row jj / 2, bytes 8 (jj % 2) .. + 7
+  const int grp = lane >> 4, jj = lane & 15;
+  const int row = 8 * (grp >> 1) + (jj >> 1);
+  const int chunk = 2 * wo + (grp & 1);
+  g.aoff = row * (GO / 2) + 16 * (chunk ^ (row & 7)) + 8 * (jj & 1);
+  // the lane's 8 rows 8 (grp / 2) .. + 7 of scale block 2 wo + grp % 2
+  g.sofs = GCB + ((2 * wo + (grp & 1)) * GKC + 8 * (grp >> 1)) * 4;
+  const int prel = lane & 31;
 #pragma unroll
-  for (int j = 0; j < BPPT; ++j) g.brow[j] = brow[j];
+  for (int s = 0; s < 4; ++s) g.boff[s] = GCB + GSB + prel * 128 + 16 * ((2 * s + (lane >> 5)) ^ x_swz(prel));
+  g.nsteps = C / GKC;
+}
+
+// Loads of step k into the register set.
+__device__ __forceinline__ void g_issue(GPipe& pp, const GArgs& g, int k) {
 #pragma unroll
-  for (int i = 0; i < BBLK; ++i) {
-    const int q = tid + i * BTHR;
-    const int cb = q / (BNT / 8), ob = q & (BNT / 8 - 1);
-    const int ocol = (o0 + 8 * ob < O) ? o0 + 8 * ob : 0;
-    g.bcode[i] = (uint32_t)(8 * cb) * g.crow + ocol / 2;
-    g.bscale[i] = (uint32_t)(8 * cb) * g.srow + ocol / 32;
+  for (int i = 0; i < 4; ++i)
+    pp.act[i] = *reinterpret_cast<const u32x4*>(g.xbase + (g.xoff[i] + (uint32_t)(k * GKC)));
+  pp.code = *reinterpret_cast<const u32x4*>(g.wcode + (g.coff + (uint32_t)k * g.cstep));
+  pp.sc = g.wscale[g.soff + (uint32_t)k * g.sstep];
+}
+
+// The register set into the LDS stage st: activations (instruction i of
+// wave w covers rows 8 (4 w + i) .. + 7, one 16-byte slot a lane), the code
+// piece, and the scale byte as a scale operand (s << 23).
+__device__ __forceinline__ void g_stage(const GPipe& pp, const GArgs& g, uint8_t* st) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    *reinterpret_cast<u32x4*>(st + GCB + GSB + ((tid >> 6) * 4 + i) * 1024 + 16 * (tid & 63)) = pp.act[i];
+  *reinterpret_cast<u32x4*>(st + g.csto) = pp.code;
+  *reinterpret_cast<uint32_t*>(st + g.ssto) = pp.sc << 23;
+}
+
+// LDS reads of sub-step s from stage st: the transposed code bytes and
+// scale words of the wave's double block, and its NRB B-fragments.
+template <int NRB>
+__device__ __forceinline__ void g_read(const GArgs& g, const uint8_t* st, int s, GFrags<NRB>& F,
+                                       int bi, int wp) {
+  F.raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+      (lds_i32x2*)(const_cast<uint8_t*>(st) + g.aoff + s * 16 * (GO / 2)));
+  F.sc[0] = *reinterpret_cast<const f32x4*>(st + g.sofs + s * 64);
+  F.sc[1] = *reinterpret_cast<const f32x4*>(st + g.sofs + s * 64 + 16);
+#pragma unroll
+  for (int j = 0; j < NRB; ++j)
+    F.b[bi][j] = *reinterpret_cast<const bf16x8*>(st + g.boff[s] + (wp + 2 * j) * 4096);
+}
+
+// Decode the raw bytes into A-fragment slot ai: fragment 0 holds the even
+// columns, 1 the odd ones.  Byte r of the 8 is row r of the lane's 8 (its
+// own scale word); its two nibbles are the column pair, so one scaled
+// conversion gives (even, odd) as packed bf16, and byte permutes gather the
+// evens and the odds.
+template <int NRB>
+__device__ __forceinline__ void g_decode(GFrags<NRB>& F, int ai) {
+  uint32_t pr[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    const uint32_t w = (uint32_t)F.raw[r >> 2];
+    const float sc = F.sc[r >> 2][r & 3];
+    switch (r & 3) {
+      case 0: pr[r] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0)); break;
+      case 1: pr[r] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1)); break;
+      case 2: pr[r] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2)); break;
+      default: pr[r] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3)); break;
+    }
   }
+  u32x4 ev, od;
 #pragma unroll
-  for (int rb = 0; rb < BRB; ++rb)
+  for (int m = 0; m < 4; ++m) {
+    ev[m] = __builtin_amdgcn_perm(pr[2 * m + 1], pr[2 * m], 0x05040100u);
+    od[m] = __builtin_amdgcn_perm(pr[2 * m + 1], pr[2 * m], 0x07060302u);
+  }
+  F.a[ai][0] = as_bf16x8(ev);
+  F.a[ai][1] = as_bf16x8(od);
+}
+
+// The 2 x NRB MFMAs of one sub-step (independent accumulators).
+template <int NRB>
+__device__ __forceinline__ void g_mfmas(const GFrags<NRB>& F, int ai, int bi,
+                                        f32x16 (&acc)[2][4]) {
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[rb][tb][r] = 0.0f;
-  switch (nrb) {
-    case 1: bwd_loop<1>(g, lds, acc); break;
-    case 2: bwd_loop<2>(g, lds, acc); break;
-    case 3: bwd_loop<3>(g, lds, acc); break;
-    default: bwd_loop<4>(g, lds, acc); break;
+    for (int j = 0; j < NRB; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F.a[ai][i], F.b[bi][j], acc[i][j], 0, 0, 0);
+}
+
+// Issue order inside one region: its LDS reads first, then its MFMAs, each
+// of the first NF followed by FPER VALU instructions (the decode), the rest
+// back to back.
+template <int NR, int NM, int NF, int FPER>
+__device__ __forceinline__ void g_order() {
+  __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+#pragma unroll
+  for (int m = 0; m < NM; ++m) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (m < NF) __builtin_amdgcn_sched_group_barrier(0x002, FPER, 0);
   }
 }
 
-// LORA: add dv_u A_e (a template parameter: a runtime branch around these
-// MFMAs makes the compiler spill accumulators).
-template <bool LORA>
-__global__ __launch_bounds__(BTHR) void bwd_down_kernel(
-    const uint16_t* __restrict__ dy, const uint8_t* __restrict__ codes,
-    const uint8_t* __restrict__ scales, const float* __restrict__ topk_w,
-    const int32_t* __restrict__ sorted_rows, const Tile* __restrict__ tiles,
-    const int32_t* __restrict__ num_tiles, const uint16_t* __restrict__ hsv,
-    const uint16_t* __restrict__ asv, int H, int I, int k, float alpha, float limit,
-    const uint16_t* __restrict__ lora_At, const float* __restrict__ lora_dvu,
-    uint16_t* __restrict__ dh, float* __restrict__ dw_part) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[BLDS];
+// One step k (stage cur = k % 2), in scheduling regions fenced by
+// sched_barrier.  On entry sub-step 0's operands are decoded (A, slot 0)
+// and read (B, slot 0), and the register set holds step k + 1's loads.
+//   (0) the register set into the other stage; reload it with step k + 2;
+//   (1..3) sub-step s + 1's reads, then sub-step s's MFMAs with the decode of
+//       s + 1 interleaved;
+//   wait for this wave's LDS traffic and meet the other waves: the other
+//   stage is complete and every wave is done reading this one, so
+//   (4) step k + 1's sub-step 0 reads, then sub-step 3's MFMAs with that
+//       decode interleaved.
+template <int NRB>
+__device__ __forceinline__ void g_step(GPipe& pp, GFrags<NRB>& F, const GArgs& g, int k,
+                                       uint8_t* lds, int wp, f32x16 (&acc)[2][4]) {
+  constexpr int NM = 2 * NRB, NR = 3 + NRB;
+  uint8_t* cur = lds + (k & 1) * GSTAGE;
+  uint8_t* nxt = lds + ((k & 1) ^ 1) * GSTAGE;
+  __builtin_amdgcn_sched_barrier(0);
+  g_stage(pp, g, nxt);
+  g_issue(pp, g, min(k + 2, g.nsteps - 1));
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int s = 0; s < 3; ++s) {
+    if constexpr (NRB > 0) {
+      g_read<NRB>(g, cur, s + 1, F, (s + 1) & 1, wp);
+      g_mfmas<NRB>(F, s & 1, s & 1, acc);
+      g_decode<NRB>(F, (s + 1) & 1);
+      g_order<NR, NM, NM, 2>();
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+  barrier_only();
+  if constexpr (NRB > 0) {
+    g_read<NRB>(g, nxt, 0, F, 0, wp);
+    g_mfmas<NRB>(F, 1, 1, acc);
+    g_decode<NRB>(F, 0);
+    g_order<NR, NM, NM, 2>();
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int NRB>
+__device__ __forceinline__ void g_loop(const GArgs& g, uint8_t* lds, int wp, f32x16 (&acc)[2][4]) {
+  GPipe pp;
+  GFrags<NRB> F;
+  g_issue(pp, g, 0);
+  g_stage(pp, g, lds);
+  g_issue(pp, g, min(1, g.nsteps - 1));
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+  barrier_only();
+  if constexpr (NRB > 0) {
+    g_read<NRB>(g, lds, 0, F, 0, wp);
+    g_decode<NRB>(F, 0);
+  }
+  for (int k = 0; k < g.nsteps; ++k) g_step<NRB>(pp, F, g, k, lds, wp, acc);
+  // the last step read (unused) operands of the other stage; every wave
+  // must be past its LDS reads before the epilogue reuses LDS
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+  __syncthreads();
+}
+
+__device__ __forceinline__ void zero_acc(f32x16 (&acc)[2][4]) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+}
+
+// Live 32-row blocks of wave row-group wp (blocks wp, wp + 2, ...) in a
+// tile of `rows` rows.
+__device__ __forceinline__ int live_blocks(int rows, int wp) {
+  const int nb = (rows + 31) >> 5;
+  return max(0, min(4, (nb - wp + 1) >> 1));
+}
+
+// Accumulator layout.  Fragment par covers the columns 2 m + par of the
+// wave's double block (m: MFMA row); lane l holds rows m = 8 (r / 4) + 4 (l /
+// 32) + r % 4 of column l % 32 (a routed row).  So for q = r / 4 a lane
+// holds 8 consecutive columns of its wave's 64, 16 q + 8 (l / 32) + 0..7:
+// registers 4q..4q+3 of fragment 0 give the even ones and of fragment 1 the
+// odd ones.  cols8 returns them as 8 fp32 in column order.
+__device__ __forceinline__ void cols8(const f32x16 (&acc)[2][4], int q, int j, float (&v)[8]) {
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    v[2 * m] = acc[0][j][4 * q + m];
+    v[2 * m + 1] = acc[1][j][4 * q + m];
+  }
+}
+
+// bwd_gate_up body for a wave with NRB live row blocks: main loop, then the
+// epilogue through a private LDS strip per wave (32 rows x 128 columns of
+// bf16 per row block), stored as whole 16-byte row pieces to the routed
+// rows' own dxr slots.
+template <int NRB>
+__device__ __forceinline__ void bwd_gate_up_body(const GArgs& g, uint8_t* lds, const Tile& tl,
+                                                 const int32_t* __restrict__ sorted_rows, int H,
+                                                 int o0, uint16_t* __restrict__ dxr) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wo = wave & 3, wp = wave >> 2;
+  const int l32 = lane & 31, hlf = lane >> 5;
+  f32x16 acc[2][4];
+  zero_acc(acc);
+  g_loop<NRB>(g, lds, wp, acc);
+  const int ow = o0 + 64 * wo;                // this wave's first output column
+  if (NRB == 0 || ow >= H) return;
+  uint8_t* st = lds + wave * 4096;            // 32 rows x 128 bytes
+#pragma unroll
+  for (int j = 0; j < NRB; ++j) {
+    const int pb = wp + 2 * j;
+    const int32_t f = sorted_rows[tl.row0 + min(32 * pb + l32, tl.rows - 1)];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float v[8];
+      cols8(acc, q, j, v);
+      const u32x4 w = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                       pack_bf16x2(v[6], v[7])};
+      *reinterpret_cast<u32x4*>(st + stg_off<128>(l32, 2 * q + hlf)) = w;
+    }
+    wave_lds_sync();
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int r = 8 * it + (lane >> 3), c = lane & 7;
+      const int rt = 32 * pb + r;
+      const int64_t fr = __shfl(f, r);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(st + stg_off<128>(r, c));
+      if (rt < tl.rows && ow + 8 * c < H)
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dxr + fr * H + ow + 8 * c));
+    }
+    wave_lds_sync();
+  }
+}
+
+__global__ __launch_bounds__(GTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_gate_up_kernel(
+    const uint16_t* __restrict__ dh, const uint8_t* __restrict__ codes,
+    const uint8_t* __restrict__ scales, const int32_t* __restrict__ sorted_rows,
+    const Tile* __restrict__ tiles, const int32_t* __restrict__ num_tiles, int H, int I,
+    uint16_t* __restrict__ dxr) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[GLDS_LOOP];
   int mt, ot;
-  const int otiles = (I + BNT - 1) / BNT;
-  if (!xcd_work_item(*num_tiles, otiles, &mt, &ot)) return;
+  if (!xcd_work_item(*num_tiles, (H + GO - 1) / GO, &mt, &ot)) return;
   const Tile tl = tiles[mt];
-  const int o0 = ot * BNT;
+  const int o0 = ot * GO, N2 = 2 * I;
+  const int wp = (threadIdx.x >> 6) >> 2;
+  // Wgu is stored [2I rows][H cols]: contraction over n (C = 2I), output h (O = H);
+  // the activations are dh's rows in sorted order
+  GArgs g;
+  g_setup(g, dh, [&](int p) { return (uint32_t)(tl.row0 + min(p, tl.rows - 1)) * (uint32_t)N2; },
+          codes + (int64_t)tl.expert * N2 * (H / 2), scales + (int64_t)tl.expert * N2 * (H / 32),
+          N2, H, o0);
+  switch (live_blocks(tl.rows, wp)) {
+    case 0: bwd_gate_up_body<0>(g, lds, tl, sorted_rows, H, o0, dxr); break;
+    case 1: bwd_gate_up_body<1>(g, lds, tl, sorted_rows, H, o0, dxr); break;
+    case 2: bwd_gate_up_body<2>(g, lds, tl, sorted_rows, H, o0, dxr); break;
+    case 3: bwd_gate_up_body<3>(g, lds, tl, sorted_rows, H, o0, dxr); break;
+    default: bwd_gate_up_body<4>(g, lds, tl, sorted_rows, H, o0, dxr); break;
+  }
+}
+
+// bwd_down body: main loop; with LORA the adapter term dv_u A_e (a 16-deep
+// MFMA contraction per fragment, dv_u as hi + lo bf16); then per live row
+// block the epilogue through a private LDS region: the block's saved a (32
+// x 128) and h (32 x 256) rows staged with row-contiguous loads, read back
+// as 8 consecutive columns per lane, the dw partial sum_i da_u * a (masked
+// to i < I), the SwiGLU backward with da = w * da_u written over h, and dh
+// stored as whole row pieces.  The two waves of a row group (wo = 0, 1) add
+// their dw partials in wave order through LDS.
+template <bool LORA, int NRB>
+__device__ __forceinline__ void bwd_down_body(
+    const GArgs& g, uint8_t* lds, const Tile& tl, int ot, int otiles, int o0,
+    const float* __restrict__ topk_w, const int32_t* __restrict__ sorted_rows,
+    const uint16_t* __restrict__ hsv, const uint16_t* __restrict__ asv, int I, float alpha,
+    float limit, const uint16_t* __restrict__ lora_At, const float* __restrict__ lora_dvu,
+    uint16_t* __restrict__ dh, float* __restrict__ dw_part) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wo = wave & 3, wp = wave >> 2;
   const int l32 = lane & 31, hlf = lane >> 5;
   const int e = tl.expert;
-
-  const uint16_t* brow[BPPT];
+  f32x16 acc[2][4];
+  zero_acc(acc);
+  g_loop<NRB>(g, lds, wp, acc);
+  const int ow = o0 + 64 * wo;                // this wave's first column of I
+  if (LORA && NRB > 0) {
 #pragma unroll
-  for (int j = 0; j < BPPT; ++j) {
-    const int q = tid + j * BTHR;
-    const int r = q >> 3;
-    const int f = sorted_rows[tl.row0 + (r < tl.rows ? r : 0)];
-    brow[j] = dy + (int64_t)(f / k) * H + (q & 7) * 8;
-  }
-  // Wd is stored [H rows][I cols]: contraction over h (C = H), output i (O = I)
-  const uint8_t* wcode = codes + (int64_t)e * H * (I / 2);
-  const uint8_t* wscale = scales + (int64_t)e * H * (I / 32);
-  f32x16 acc[BRB][4];
-  bwd_mainloop(brow, wcode, wscale, H, I, o0, (tl.rows + 31) / 32, lds, acc);
-  if (LORA) {
-    // + dv_u A_e (dv_u = s dY B_e, unweighted like the accumulators): a
-    // 16-deep contraction, A-operand = rows of A_e^T, B-operand = dv_u as
-    // hi + lo bf16.  Through the accumulators it also reaches the dw
-    // partial: sum_i (dv_u A_e)_i a_i = dv_u . v, the adapter's share of dY . y.
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-      const float* vp = lora_dvu + (int64_t)(tl.row0 + min(tb * 32 + l32, tl.rows - 1)) * LORA_R + 8 * hlf;
+    for (int j = 0; j < NRB; ++j) {
+      const int pb = wp + 2 * j;
+      const float* vp = lora_dvu + (int64_t)(tl.row0 + min(32 * pb + l32, tl.rows - 1)) * LORA_R + 8 * hlf;
       bf16x8 vh, vl;
       split_bf16x8(*reinterpret_cast<const f32x4*>(vp), *reinterpret_cast<const f32x4*>(vp + 4),
                    1.0f, &vh, &vl);
 #pragma unroll
-      for (int rb = 0; rb < BRB; ++rb) {
-        const int i = o0 + wave * 32 * BRB + rb * 32 + l32;
+      for (int i = 0; i < 2; ++i) {
+        // fragment i's MFMA row l32 is column 2 l32 + i of the wave's 64
+        const int col = ow + 2 * l32 + i;
         const bf16x8 aw = as_bf16x8(*reinterpret_cast<const u32x4*>(
-            lora_At + ((int64_t)e * I + (i < I ? i : 0)) * LORA_R + 8 * hlf));
-        acc[rb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw, vh, acc[rb][tb], 0, 0, 0);
-        acc[rb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw, vl, acc[rb][tb], 0, 0, 0);
+            lora_At + ((int64_t)e * I + (col < I ? col : 0)) * LORA_R + 8 * hlf));
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw, vh, acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw, vl, acc[i][j], 0, 0, 0);
       }
     }
   }
-
-  // Epilogue through LDS (the main loop ended with a barrier).  Per 32-row
-  // block a wave stages its rows of a (64 bf16) and h (128 bf16) with
-  // row-contiguous loads, reads them back in the accumulator layout, writes
-  // dh over h in place and stores dh rows whole.
   const int N2 = 2 * I;
-  const int ow = o0 + wave * 32 * BRB;        // this wave's first output column
-  const bool active = ow < I;                 // I % 64 == 0: a wave's 64 columns are all in or out
+  const bool active = ow < I;
   uint8_t* ast = lds + wave * 12288;          // a strip: 32 rows x 64 bf16 (128-byte rows)
   uint8_t* hst = ast + 4096;                  // h / dh strip: 32 rows x 128 bf16 (256-byte rows)
-  float* red = reinterpret_cast<float*>(lds + BW * 12288);   // [BW][MT]
+  float* red = reinterpret_cast<float*>(lds + GW * 12288);   // [GW][BMT / 2]
 #pragma unroll
-  for (int tb = 0; tb < 4; ++tb) {
+  for (int j = 0; j < NRB; ++j) {
+    const int pb = wp + 2 * j;
     float dwp = 0.0f;
-    if (active && tb * 32 < tl.rows) {
+    if (active) {
 #pragma unroll
       for (int it = 0; it < 4; ++it) {
-        const int r = it * 8 + (lane >> 3), c = lane & 7;
-        const int64_t p = tl.row0 + min(tb * 32 + r, tl.rows - 1);
+        const int r = 8 * it + (lane >> 3), c = lane & 7;
+        const int64_t p = tl.row0 + min(32 * pb + r, tl.rows - 1);
+        const int col = min(ow + 8 * c, I - 8);
         *reinterpret_cast<u32x4*>(ast + stg_off<128>(r, c)) =
-            *reinterpret_cast<const u32x4*>(asv + p * I + ow + 8 * c);
+            *reinterpret_cast<const u32x4*>(asv + p * I + col);
       }
 #pragma unroll
       for (int it = 0; it < 8; ++it) {
-        const int r = it * 4 + (lane >> 4), c = lane & 15;
-        const int64_t p = tl.row0 + min(tb * 32 + r, tl.rows - 1);
+        const int r = 4 * it + (lane >> 4), c = lane & 15;
+        const int64_t p = tl.row0 + min(32 * pb + r, tl.rows - 1);
+        const int col = min(2 * ow + 8 * c, N2 - 8);
         *reinterpret_cast<u32x4*>(hst + stg_off<256>(r, c)) =
-            *reinterpret_cast<const u32x4*>(hsv + p * N2 + 2 * ow + 8 * c);
+            *reinterpret_cast<const u32x4*>(hsv + p * N2 + col);
       }
-      const float wf = topk_w[sorted_rows[tl.row0 + min(tb * 32 + l32, tl.rows - 1)]];
+      const float wf = topk_w[sorted_rows[tl.row0 + min(32 * pb + l32, tl.rows - 1)]];
       wave_lds_sync();
 #pragma unroll
-      for (int rb = 0; rb < BRB; ++rb) {
+      for (int q = 0; q < 4; ++q) {
+        const int cb = 2 * q + hlf;                    // 8-column chunk of the wave's 64
+        const int o = ow + 8 * cb;                     // first of this lane's 8 columns
+        float v[8];
+        cols8(acc, q, j, v);
+        const u32x4 av = *reinterpret_cast<const u32x4*>(ast + stg_off<128>(l32, cb));
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int c4 = 8 * rb + 2 * q + hlf;    // columns 4 c4 .. 4 c4 + 3 of the strip
-          const u32x2 av = *reinterpret_cast<const u32x2*>(ast + stg_off<128>(l32, c4 >> 1) + 8 * (c4 & 1));
-          uint8_t* hp = hst + stg_off<256>(l32, c4);
+        for (int half = 0; half < 2; ++half) {
+          uint8_t* hp = hst + stg_off<256>(l32, 2 * cb + half);
           const u32x4 hv = *reinterpret_cast<const u32x4*>(hp);
           u32x4 out;
 #pragma unroll
           for (int m = 0; m < 4; ++m) {
-            const float du_ = acc[rb][tb][4 * q + m];
-            const uint32_t aw = av[m >> 1];
-            const float a_m = bf16_to_f32((uint16_t)((m & 1) ? (aw >> 16) : (aw & 0xFFFFu)));
-            dwp += du_ * a_m;
+            const int c = 4 * half + m;                // column o + c
+            const float du_ = v[c];
+            const uint32_t aw = av[c >> 1];
+            const float a_c = bf16_to_f32((uint16_t)((c & 1) ? (aw >> 16) : (aw & 0xFFFFu)));
+            dwp += (o + c < I) ? du_ * a_c : 0.0f;
             const uint32_t hw = hv[m];
-            const float g = bf16_to_f32((uint16_t)(hw & 0xFFFFu));
-            const float u = bf16_to_f32((uint16_t)(hw >> 16));
             float dg, dup;
-            swiglu_grad(g, u, wf * du_, alpha, limit, &dg, &dup);
+            swiglu_grad(bf16_to_f32((uint16_t)(hw & 0xFFFFu)), bf16_to_f32((uint16_t)(hw >> 16)),
+                        wf * du_, alpha, limit, &dg, &dup);
             out[m] = pack_bf16x2(dg, dup);
           }
           *reinterpret_cast<u32x4*>(hp) = out;
@@ -370,83 +506,68 @@ __global__ __launch_bounds__(BTHR) void bwd_down_kernel(
       wave_lds_sync();
 #pragma unroll
       for (int it = 0; it < 8; ++it) {
-        const int r = it * 4 + (lane >> 4), c = lane & 15;
-        const int rt = tb * 32 + r;
+        const int r = 4 * it + (lane >> 4), c = lane & 15;
+        const int rt = 32 * pb + r;
         const u32x4 v = *reinterpret_cast<const u32x4*>(hst + stg_off<256>(r, c));
-        if (rt < tl.rows) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dh + (int64_t)(tl.row0 + rt) * N2 + 2 * ow + 8 * c));
+        if (rt < tl.rows && 2 * ow + 8 * c < N2)
+          __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dh + (int64_t)(tl.row0 + rt) * N2 + 2 * ow + 8 * c));
       }
       wave_lds_sync();
-      if (tb * 32 + l32 >= tl.rows) dwp = 0.0f;
     }
     dwp += __shfl_xor(dwp, 32);
-    if (hlf == 0) red[wave * MT + tb * 32 + l32] = dwp;
+    if (hlf == 0) red[wave * (BMT / 2) + 32 * j + l32] = dwp;
   }
   __syncthreads();
+  // row p of the tile: row group wp = (p / 32) % 2, slot 32 j + p % 32 with
+  // j = p / 64; the four waves of the group, wo = 0..3, are added in order
   if (tid < tl.rows) {
-    float s = 0.0f;
+    const int p = tid, gp = (p >> 5) & 1, slot = 32 * (p >> 6) + (p & 31);
+    float sum = 0.0f;
 #pragma unroll
-    for (int w = 0; w < BW; ++w) s += red[w * MT + tid];
-    const int64_t f = sorted_rows[tl.row0 + tid];
-    dw_part[f * otiles + ot] = s;
+    for (int w = 0; w < 4; ++w) sum += red[(4 * gp + w) * (BMT / 2) + slot];
+    const int64_t f = sorted_rows[tl.row0 + p];
+    dw_part[f * otiles + ot] = sum;
   }
 }
 
-__global__ __launch_bounds__(BTHR) void bwd_gate_up_kernel(
-    const uint16_t* __restrict__ dh, const uint8_t* __restrict__ codes,
-    const uint8_t* __restrict__ scales, const int32_t* __restrict__ sorted_rows,
-    const Tile* __restrict__ tiles, const int32_t* __restrict__ num_tiles, int H, int I,
-    uint16_t* __restrict__ dxr) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[BLDS];
+template <bool LORA>
+__global__ __launch_bounds__(GTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_down_kernel(
+    const uint16_t* __restrict__ dy, const uint8_t* __restrict__ codes,
+    const uint8_t* __restrict__ scales, const float* __restrict__ topk_w,
+    const int32_t* __restrict__ sorted_rows, const Tile* __restrict__ tiles,
+    const int32_t* __restrict__ num_tiles, const uint16_t* __restrict__ hsv,
+    const uint16_t* __restrict__ asv, int H, int I, int k, float alpha, float limit,
+    const uint16_t* __restrict__ lora_At, const float* __restrict__ lora_dvu,
+    uint16_t* __restrict__ dh, float* __restrict__ dw_part) {
+  // the epilogue's strips (8 x 12 KB) and dw reduction cover the main loop's stages
+  __shared__ __attribute__((aligned(16))) uint8_t lds[GW * 12288 + GW * (BMT / 2) * 4];
+  static_assert(GW * 12288 + GW * (BMT / 2) * 4 >= GLDS_LOOP, "epilogue LDS covers the loop's");
   int mt, ot;
-  const int otiles = (H + BNT - 1) / BNT;
+  const int otiles = (I + GO - 1) / GO;
   if (!xcd_work_item(*num_tiles, otiles, &mt, &ot)) return;
   const Tile tl = tiles[mt];
-  const int o0 = ot * BNT;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int l32 = lane & 31, hlf = lane >> 5;
-  const int e = tl.expert;
-  const int N2 = 2 * I;
-
-  const uint16_t* brow[BPPT];
-#pragma unroll
-  for (int j = 0; j < BPPT; ++j) {
-    const int q = tid + j * BTHR;
-    const int r = q >> 3;
-    brow[j] = dh + (int64_t)(tl.row0 + (r < tl.rows ? r : 0)) * N2 + (q & 7) * 8;
+  const int o0 = ot * GO;
+  const int wp = (threadIdx.x >> 6) >> 2;
+  // Wd is stored [H rows][I cols]: contraction over h (C = H), output i (O =
+  // I); the activations are the routed rows' tokens' dY rows
+  GArgs g;
+  g_setup(g, dy,
+          [&](int p) {
+            return (uint32_t)(sorted_rows[tl.row0 + min(p, tl.rows - 1)] / k) * (uint32_t)H;
+          },
+          codes + (int64_t)tl.expert * H * (I / 2), scales + (int64_t)tl.expert * H * (I / 32), H,
+          I, o0);
+#define BWD_DOWN_BODY(N)                                                                       \
+  bwd_down_body<LORA, N>(g, lds, tl, ot, otiles, o0, topk_w, sorted_rows, hsv, asv, I, alpha, \
+                         limit, lora_At, lora_dvu, dh, dw_part)
+  switch (live_blocks(tl.rows, wp)) {
+    case 0: BWD_DOWN_BODY(0); break;
+    case 1: BWD_DOWN_BODY(1); break;
+    case 2: BWD_DOWN_BODY(2); break;
+    case 3: BWD_DOWN_BODY(3); break;
+    default: BWD_DOWN_BODY(4); break;
   }
-  // Wgu is stored [2I rows][H cols]: contraction over n (C = 2I), output h (O = H)
-  const uint8_t* wcode = codes + (int64_t)e * N2 * (H / 2);
-  const uint8_t* wscale = scales + (int64_t)e * N2 * (H / 32);
-  f32x16 acc[BRB][4];
-  bwd_mainloop(brow, wcode, wscale, N2, H, o0, (tl.rows + 31) / 32, lds, acc);
-
-  // Epilogue through LDS (the main loop ended with a barrier).
-  const int ow = o0 + wave * 32 * BRB;
-  if (ow >= H) return;                        // H % 64 == 0: a wave's columns are all in or out
-  uint8_t* yst = lds + wave * 4096;           // 32 rows x 64 bf16 (128-byte rows)
-#pragma unroll
-  for (int tb = 0; tb < 4; ++tb) {
-    if (tb * 32 >= tl.rows) break;
-    const int32_t f = sorted_rows[tl.row0 + min(tb * 32 + l32, tl.rows - 1)];
-#pragma unroll
-    for (int rb = 0; rb < BRB; ++rb)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f32x16& a = acc[rb][tb];
-        const u32x2 v = {pack_bf16x2(a[4 * q], a[4 * q + 1]), pack_bf16x2(a[4 * q + 2], a[4 * q + 3])};
-        *reinterpret_cast<u32x2*>(yst + stg_off<128>(l32, 4 * rb + q) + 8 * hlf) = v;
-      }
-    wave_lds_sync();
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int r = it * 8 + (lane >> 3), c = lane & 7;
-      const int rt = tb * 32 + r;
-      const int64_t fr = __shfl(f, r);
-      const u32x4 v = *reinterpret_cast<const u32x4*>(yst + stg_off<128>(r, c));
-      if (rt < tl.rows) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dxr + fr * H + ow + 8 * c));
-    }
-    wave_lds_sync();
-  }
+#undef BWD_DOWN_BODY
 }
 
 // One workgroup (256 threads) per token.  Slot j's dw = the sum of its
@@ -546,7 +667,7 @@ __global__ __launch_bounds__(256) void bwd_combine_kernel(
   }
 }
 
-int bwd_down_ntiles(int I) { return (I + BNT - 1) / BNT; }
+int bwd_down_ntiles(int I) { return (I + GO - 1) / GO; }
 
 hipError_t launch_bwd_down(const uint16_t* dy, const uint8_t* codes, const uint8_t* scales,
                            const float* topk_w, const int32_t* sorted_rows, const Tile* tiles,
@@ -554,14 +675,14 @@ hipError_t launch_bwd_down(const uint16_t* dy, const uint8_t* codes, const uint8
                            const uint16_t* a, int H, int I, int k, float alpha, float limit,
                            const uint16_t* lora_At, const float* lora_dvu, uint16_t* dh,
                            float* dw_part, hipStream_t s) {
-  if (H % BKC || I % 64) return hipErrorInvalidValue;
+  if (H % GKC || I % 64) return hipErrorInvalidValue;
   dim3 grid(bwd_down_ntiles(I) * max_tiles);
   if (lora_At)
-    hipLaunchKernelGGL(bwd_down_kernel<true>, grid, dim3(BTHR), 0, s, dy, codes, scales, topk_w,
+    hipLaunchKernelGGL(bwd_down_kernel<true>, grid, dim3(GTHR), 0, s, dy, codes, scales, topk_w,
                        sorted_rows, tiles, num_tiles, h, a, H, I, k, alpha, limit, lora_At,
                        lora_dvu, dh, dw_part);
   else
-    hipLaunchKernelGGL(bwd_down_kernel<false>, grid, dim3(BTHR), 0, s, dy, codes, scales, topk_w,
+    hipLaunchKernelGGL(bwd_down_kernel<false>, grid, dim3(GTHR), 0, s, dy, codes, scales, topk_w,
                        sorted_rows, tiles, num_tiles, h, a, H, I, k, alpha, limit, lora_At,
                        lora_dvu, dh, dw_part);
   return hipGetLastError();
@@ -571,9 +692,9 @@ hipError_t launch_bwd_gate_up(const uint16_t* dh, const uint8_t* codes, const ui
                               const int32_t* sorted_rows, const Tile* tiles,
                               const int32_t* num_tiles, int max_tiles, int H, int I,
                               uint16_t* dxr, hipStream_t s) {
-  if ((2 * I) % BKC || H % 64) return hipErrorInvalidValue;
-  dim3 grid(((H + BNT - 1) / BNT) * max_tiles);
-  hipLaunchKernelGGL(bwd_gate_up_kernel, grid, dim3(BTHR), 0, s, dh, codes, scales, sorted_rows,
+  if ((2 * I) % GKC || H % 64) return hipErrorInvalidValue;
+  dim3 grid(((H + GO - 1) / GO) * max_tiles);
+  hipLaunchKernelGGL(bwd_gate_up_kernel, grid, dim3(GTHR), 0, s, dh, codes, scales, sorted_rows,
                      tiles, num_tiles, H, I, dxr);
   return hipGetLastError();
 }

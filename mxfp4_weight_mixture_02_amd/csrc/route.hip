@@ -455,10 +455,10 @@ __global__ __launch_bounds__(1024) void plan_kernel(
   }
 }
 
-// Tiles of at most MT sorted rows, expert by expert, from the E + 1
+// Tiles of at most mt sorted rows, expert by expert, from the E + 1
 // offsets in LDS (offs); start is LDS scratch of E + 1 entries.  Called by
 // every thread of one workgroup; ends with the tile list written.
-__device__ __forceinline__ void write_tiles(const int32_t* offs, int E, int32_t* start,
+__device__ __forceinline__ void write_tiles(const int32_t* offs, int E, int mt, int32_t* start,
                                             Tile* __restrict__ tiles,
                                             int32_t* __restrict__ num_tiles) {
   const int tid = threadIdx.x;
@@ -466,7 +466,7 @@ __device__ __forceinline__ void write_tiles(const int32_t* offs, int E, int32_t*
     int32_t run = 0;
     for (int e = 0; e < E; ++e) {
       start[e] = run;
-      run += (offs[e + 1] - offs[e] + MT - 1) / MT;
+      run += (offs[e + 1] - offs[e] + mt - 1) / mt;
     }
     start[E] = run;
     *num_tiles = run;
@@ -474,15 +474,16 @@ __device__ __forceinline__ void write_tiles(const int32_t* offs, int E, int32_t*
   __syncthreads();
   if (tid < E) {
     const int32_t o = offs[tid], n = offs[tid + 1] - o;
-    for (int32_t q = 0; q * MT < n; ++q) {
+    for (int32_t q = 0; q * mt < n; ++q) {
       Tile tl;
       tl.expert = tid;
-      tl.row0 = o + q * MT;
-      tl.rows = min(MT, n - q * MT);
+      tl.row0 = o + q * mt;
+      tl.rows = min(mt, n - q * mt);
       tl.pad = 0;
       tiles[start[tid] + q] = tl;
     }
   }
+  __syncthreads();
 }
 
 // One workgroup of 1024 threads.  In place, blk_hist[b][e] becomes the
@@ -533,7 +534,7 @@ __global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ blk_hi
   __syncthreads();
   if (tid <= E) offsets[tid] = off[tid];
   // the GEMMs' tile list from the offsets (no separate launch)
-  write_tiles(off, E, tstart, tiles, num_tiles);
+  write_tiles(off, E, MT, tstart, tiles, num_tiles);
   if (c < C) {
     int32_t run = off[e] + part[tid];
     const int b1 = min(nblk, (c + 1) * per);
@@ -574,15 +575,18 @@ __global__ __launch_bounds__(64) void scatter_kernel(const int32_t* __restrict__
   }
 }
 
-// Upper bound on the tile count: sum_e ceil(n_e / MT) <= R / MT + (number
+// Upper bound on the tile count: sum_e ceil(n_e / mt) <= R / mt + (number
 // of non-empty experts), and at most min(E, R) experts are non-empty.
-int max_tiles(int64_t R, int E) { return (int)((R + MT - 1) / MT + (R < E ? R : E)); }
+int max_tiles(int64_t R, int E, int mt) { return (int)((R + mt - 1) / mt + (R < E ? R : E)); }
 
-// Tiles of at most MT sorted rows, expert by expert (one workgroup), from
-// offsets in global memory (the backward rebuilds the forward's list).
+// Tile lists from offsets in global memory (the backward rebuilds them):
+// tiles of at most mt rows, and with tiles2 != nullptr a second list of at
+// most mt2 rows (one workgroup).
 __global__ __launch_bounds__(256) void tiles_kernel(const int32_t* __restrict__ offsets, int E,
-                                                    Tile* __restrict__ tiles,
-                                                    int32_t* __restrict__ num_tiles) {
+                                                    int mt, Tile* __restrict__ tiles,
+                                                    int32_t* __restrict__ num_tiles, int mt2,
+                                                    Tile* __restrict__ tiles2,
+                                                    int32_t* __restrict__ num_tiles2) {
   __shared__ int32_t start[257];
   __shared__ int32_t offs[257];
   const int tid = threadIdx.x;
@@ -590,7 +594,8 @@ __global__ __launch_bounds__(256) void tiles_kernel(const int32_t* __restrict__ 
   // memory would pay a round trip per expert)
   for (int e = tid; e <= E; e += 256) offs[e] = offsets[e];
   __syncthreads();
-  write_tiles(offs, E, start, tiles, num_tiles);
+  write_tiles(offs, E, mt, start, tiles, num_tiles);
+  if (tiles2) write_tiles(offs, E, mt2, start, tiles2, num_tiles2);
 }
 
 hipError_t launch_logits(const uint16_t* x, const float* wr, const float* br, int T, int H,
@@ -650,9 +655,11 @@ hipError_t launch_scatter(const int32_t* topk_idx, const int32_t* blk_base, int 
   return hipGetLastError();
 }
 
-hipError_t launch_build_tiles(const int32_t* offsets, int E, Tile* tiles, int32_t* num_tiles,
+hipError_t launch_build_tiles(const int32_t* offsets, int E, int mt, Tile* tiles,
+                              int32_t* num_tiles, int mt2, Tile* tiles2, int32_t* num_tiles2,
                               hipStream_t s) {
-  hipLaunchKernelGGL(tiles_kernel, dim3(1), dim3(256), 0, s, offsets, E, tiles, num_tiles);
+  hipLaunchKernelGGL(tiles_kernel, dim3(1), dim3(256), 0, s, offsets, E, mt, tiles, num_tiles,
+                     mt2, tiles2, num_tiles2);
   return hipGetLastError();
 }
 
