@@ -181,25 +181,44 @@ struct Tile {
   int32_t pad;
 };
 
-// Work item of a grouped-GEMM workgroup.  Workgroups are dealt to the 8
-// XCDs round-robin by block index, and each XCD has its own L2.  With L live
-// work items (row tiles x column tiles, column tile fastest), XCD i gets the
-// contiguous range of items [start_i, start_i + L/8 (+1)), so the column
-// tiles of a row tile (same activations) and consecutive row tiles of an
-// expert (same weights) run together on one L2.  Returns false for blocks
-// past the live items.
-__device__ __forceinline__ bool xcd_work_item(int live_row_tiles, int col_tiles, int* row_tile,
-                                              int* col_tile) {
-  const int L = live_row_tiles * col_tiles;
+// Work items of the grouped GEMMs.  Workgroups are dealt to the 8 XCDs
+// round-robin by block index, and each XCD has its own L2.
+//
+// Tile list in expert order (forward): with L live work items (row tiles x
+// column tiles, column tile fastest), XCD i gets the contiguous range of
+// items [start_i, start_i + L/8 (+1)), so the column tiles of a row tile
+// (same activations) and consecutive row tiles of an expert (same weights)
+// run together on one L2.  Returns false for blocks past the live items.
+__device__ __forceinline__ bool xcd_item_range(const Tile* __restrict__ tiles,
+                                               const int32_t* __restrict__ num_tiles,
+                                               int col_tiles, Tile* tl, int* col_tile) {
+  const int L = *num_tiles * col_tiles;
   const int b = blockIdx.x;
   if (b >= L) return false;
   const int xcd = b & 7, idx = b >> 3;
   const int base = L >> 3, extra = L & 7;
-  const int start = xcd * base + min(xcd, extra);
-  const int item = start + idx;
-  *row_tile = item / col_tiles;
+  const int item = xcd * base + min(xcd, extra) + idx;
+  *tl = tiles[item / col_tiles];
   *col_tile = item % col_tiles;
   return true;
+}
+
+// Tile list dealt to the XCDs (backward): XCD x's row tiles sit at x, 8 +
+// x, 16 + x, ... (the XCDs' shares balanced, each ending on its shortest
+// tiles; empty tiles have rows = 0), so block b runs on XCD x = b % 8 and
+// takes its XCD's (b / 8)-th item, column tile fastest: the column tiles of
+// a row tile (same activations) run together on one L2.  Returns false for
+// blocks past the XCD's items and for empty tiles.
+__device__ __forceinline__ bool xcd_work_item(const Tile* __restrict__ tiles,
+                                              const int32_t* __restrict__ num_tiles,
+                                              int col_tiles, Tile* tl, int* col_tile) {
+  const int b = blockIdx.x;
+  const int x = b & 7, idx = b >> 3;
+  const int p = 8 * (idx / col_tiles) + x;
+  if (p >= *num_tiles) return false;
+  *tl = tiles[p];
+  *col_tile = idx % col_tiles;
+  return tl->rows > 0;
 }
 
 constexpr int MT = 128;      // routed rows per forward GEMM tile

@@ -385,9 +385,9 @@ __global__ __launch_bounds__(GTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
     const Tile* __restrict__ tiles, const int32_t* __restrict__ num_tiles, int H, int I,
     uint16_t* __restrict__ dxr) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[GLDS_LOOP];
-  int mt, ot;
-  if (!xcd_work_item(*num_tiles, (H + GO - 1) / GO, &mt, &ot)) return;
-  const Tile tl = tiles[mt];
+  Tile tl;
+  int ot;
+  if (!xcd_work_item(tiles, num_tiles, (H + GO - 1) / GO, &tl, &ot)) return;
   const int o0 = ot * GO, N2 = 2 * I;
   const int wp = (threadIdx.x >> 6) >> 2;
   // Wgu is stored [2I rows][H cols]: contraction over n (C = 2I), output h (O = H);
@@ -542,10 +542,10 @@ __global__ __launch_bounds__(GTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
   // the epilogue's strips (8 x 12 KB) and dw reduction cover the main loop's stages
   __shared__ __attribute__((aligned(16))) uint8_t lds[GW * 12288 + GW * (BMT / 2) * 4];
   static_assert(GW * 12288 + GW * (BMT / 2) * 4 >= GLDS_LOOP, "epilogue LDS covers the loop's");
-  int mt, ot;
+  Tile tl;
+  int ot;
   const int otiles = (I + GO - 1) / GO;
-  if (!xcd_work_item(*num_tiles, otiles, &mt, &ot)) return;
-  const Tile tl = tiles[mt];
+  if (!xcd_work_item(tiles, num_tiles, otiles, &tl, &ot)) return;
   const int o0 = ot * GO;
   const int wp = (threadIdx.x >> 6) >> 2;
   // Wd is stored [H rows][I cols]: contraction over h (C = H), output i (O =

@@ -75,6 +75,7 @@ __global__ __launch_bounds__(512) void dec_kernel(
   const int tile = blockIdx.x / nblk, rbk = blockIdx.x % nblk;
   if (tile >= *num_tiles) return;
   const Tile tl = tiles[tile];
+  if (tl.rows <= 0) return;   // empty slot of the XCD deal
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hlf = lane >> 5;
   const int e = tl.expert;
@@ -186,6 +187,7 @@ __global__ __launch_bounds__(64 * KW) void dec_ksplit_kernel(
   const int tile = blockIdx.x / nrb, rb = blockIdx.x % nrb;
   if (tile >= *num_tiles) return;
   const Tile tl = tiles[tile];
+  if (tl.rows <= 0) return;   // empty slot of the XCD deal
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hlf = lane >> 5;
   const int e = tl.expert;

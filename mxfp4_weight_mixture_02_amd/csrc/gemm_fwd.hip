@@ -323,9 +323,9 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   constexpr int XCHUNKS = S::XCH, FNT = S::NT;
   __shared__ __attribute__((aligned(16))) uint8_t lds[S::LDS];
   const int N = 2 * I;
-  int mt, nt;
-  if (!xcd_work_item(*num_tiles, (N + FNT - 1) / FNT, &mt, &nt)) return;
-  const Tile tl = tiles[mt];
+  Tile tl;
+  int nt;
+  if (!xcd_item_range(tiles, num_tiles, (N + FNT - 1) / FNT, &tl, &nt)) return;
   const int n0 = nt * FNT;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hlf = lane >> 5;
@@ -410,9 +410,9 @@ __global__ __launch_bounds__(FwdShape<8>::NTHR) void down_kernel(
   constexpr int XCHUNKS = S::XCH, FNT = S::NT;
   __shared__ __attribute__((aligned(16))) uint8_t lds[S::LDS];
   const int N = H;
-  int mt, nt;
-  if (!xcd_work_item(*num_tiles, (N + FNT - 1) / FNT, &mt, &nt)) return;
-  const Tile tl = tiles[mt];
+  Tile tl;
+  int nt;
+  if (!xcd_item_range(tiles, num_tiles, (N + FNT - 1) / FNT, &tl, &nt)) return;
   const int n0 = nt * FNT;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hlf = lane >> 5;

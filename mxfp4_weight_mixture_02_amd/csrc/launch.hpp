@@ -40,7 +40,8 @@ hipError_t launch_scan(int32_t* blk_hist, int nblk, int E, int32_t* offsets, Til
 hipError_t launch_scatter(const int32_t* topk_idx, const int32_t* blk_base, int T, int k, int E,
                           int32_t* sorted_rows, hipStream_t s);
 int max_tiles(int64_t R, int E, int mt);
-// tile lists of at most mt (and, with tiles2, mt2) rows from the offsets
+// tile lists from the offsets: at most mt rows per tile, dealt to the XCDs
+// (the backward GEMMs' order), and with tiles2 at most mt2 rows in expert order
 hipError_t launch_build_tiles(const int32_t* offsets, int E, int mt, Tile* tiles,
                               int32_t* num_tiles, int mt2, Tile* tiles2, int32_t* num_tiles2,
                               hipStream_t s);

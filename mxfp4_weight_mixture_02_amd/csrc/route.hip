@@ -455,9 +455,12 @@ __global__ __launch_bounds__(1024) void plan_kernel(
   }
 }
 
-// Tiles of at most mt sorted rows, expert by expert, from the E + 1
-// offsets in LDS (offs); start is LDS scratch of E + 1 entries.  Called by
-// every thread of one workgroup; ends with the tile list written.
+// Tile lists from the E + 1 offsets in LDS (offs); start is LDS scratch of
+// E + 1 entries.  Called by every thread of one workgroup; ends with the
+// list written.
+//
+// write_tiles: tiles of at most mt sorted rows, expert by expert (the
+// forward's list: its GEMMs give each XCD a contiguous range of it).
 __device__ __forceinline__ void write_tiles(const int32_t* offs, int E, int mt, int32_t* start,
                                             Tile* __restrict__ tiles,
                                             int32_t* __restrict__ num_tiles) {
@@ -472,15 +475,95 @@ __device__ __forceinline__ void write_tiles(const int32_t* offs, int E, int mt, 
     *num_tiles = run;
   }
   __syncthreads();
-  if (tid < E) {
-    const int32_t o = offs[tid], n = offs[tid + 1] - o;
-    for (int32_t q = 0; q * mt < n; ++q) {
-      Tile tl;
-      tl.expert = tid;
-      tl.row0 = o + q * mt;
-      tl.rows = min(mt, n - q * mt);
-      tl.pad = 0;
-      tiles[start[tid] + q] = tl;
+  for (int e = tid; e < E; e += blockDim.x) {
+    const int32_t o = offs[e], n = offs[e + 1] - o;
+    for (int32_t q = 0; q * mt < n; ++q)
+      tiles[start[e] + q] = Tile{e, o + q * mt, min(mt, n - q * mt), 0};
+  }
+  __syncthreads();
+}
+
+// write_dealt_tiles: the same tiles in the order the backward GEMMs deal
+// them to the 8 XCDs.  XCD x's tiles sit at x, 8 + x, 16 + x, ... (a
+// workgroup on XCD x reads only those).  The F full tiles (expert by
+// expert) are split into 8 contiguous ranges, one per XCD, so the row tiles
+// of an expert that run together share its weights in one L2.  Each
+// expert's ragged last tile then follows, dealt longest first (rows
+// descending, ties by expert) in snake order (round r runs over the XCDs
+// downward when r is even, upward when odd, starting with the XCDs whose
+// full range is one shorter), so the XCDs' totals balance and every XCD
+// ends on its shortest tiles.  Slots past an XCD's share up to the longest
+// share hold empty tiles (rows = 0); *num_tiles = 8 x the longest share.
+struct TileDeal {
+  int full_base, full_ext, ragged;   // F / 8, F % 8, number of ragged tiles
+  __device__ int full_count(int x) const { return full_base + (x < full_ext); }
+  __device__ int ragged_xcd(int j) const {
+    const int r = j >> 3, pos = j & 7;
+    return (r & 1) ? pos : 7 - pos;
+  }
+  __device__ int ragged_count(int x) const {
+    int n = ragged >> 3;
+    for (int pos = 0; pos < (ragged & 7); ++pos) n += ragged_xcd(8 * (ragged >> 3) + pos) == x;
+    return n;
+  }
+  // list index of full tile i (0 <= i < F)
+  __device__ int full_slot(int i) const {
+    const int boundary = full_ext * (full_base + 1);
+    int x, q;
+    if (i < boundary) {
+      x = i / (full_base + 1);
+      q = i % (full_base + 1);
+    } else {
+      x = full_ext + (i - boundary) / full_base;
+      q = (i - boundary) % full_base;
+    }
+    return 8 * q + x;
+  }
+  // list index of the ragged tile of rank j
+  __device__ int ragged_slot(int j) const {
+    const int x = ragged_xcd(j);
+    return 8 * (full_count(x) + (j >> 3)) + x;
+  }
+};
+
+__device__ __forceinline__ void write_dealt_tiles(const int32_t* offs, int E, int mt,
+                                                  int32_t* start, Tile* __restrict__ tiles,
+                                                  int32_t* __restrict__ num_tiles) {
+  const int tid = threadIdx.x;
+  __shared__ TileDeal deal;
+  if (tid == 0) {
+    int32_t run = 0, ragged = 0;
+    for (int e = 0; e < E; ++e) {
+      const int32_t n = offs[e + 1] - offs[e];
+      start[e] = run;
+      run += n / mt;
+      ragged += (n % mt) != 0;
+    }
+    start[E] = run;
+    TileDeal d{run >> 3, run & 7, ragged};
+    int cnt[8], longest = 0;
+    for (int x = 0; x < 8; ++x) {
+      cnt[x] = d.full_count(x) + d.ragged_count(x);
+      longest = max(longest, cnt[x]);
+    }
+    for (int x = 0; x < 8; ++x)
+      for (int q = cnt[x]; q < longest; ++q) tiles[8 * q + x] = Tile{0, 0, 0, 0};
+    *num_tiles = 8 * longest;
+    deal = d;
+  }
+  __syncthreads();
+  const TileDeal d = deal;
+  for (int e = tid; e < E; e += blockDim.x) {
+    const int32_t o = offs[e], n = offs[e + 1] - o;
+    const int32_t nfull = n / mt, rem = n % mt;
+    for (int32_t q = 0; q < nfull; ++q) tiles[d.full_slot(start[e] + q)] = Tile{e, o + q * mt, mt, 0};
+    if (rem) {
+      int32_t rank = 0;
+      for (int e2 = 0; e2 < E; ++e2) {
+        const int32_t r2 = (offs[e2 + 1] - offs[e2]) % mt;
+        rank += (r2 > rem) || (r2 == rem && e2 < e);
+      }
+      tiles[d.ragged_slot(rank)] = Tile{e, o + nfull * mt, rem, 0};
     }
   }
   __syncthreads();
@@ -577,11 +660,17 @@ __global__ __launch_bounds__(64) void scatter_kernel(const int32_t* __restrict__
 
 // Upper bound on the tile count: sum_e ceil(n_e / mt) <= R / mt + (number
 // of non-empty experts), and at most min(E, R) experts are non-empty.
-int max_tiles(int64_t R, int E, int mt) { return (int)((R + mt - 1) / mt + (R < E ? R : E)); }
+int max_tiles(int64_t R, int E, int mt) {
+  // full tiles plus at most one ragged tile per expert; the XCD deal pads
+  // each of the 8 shares to the longest, which is at most
+  // ceil(F / 8) + ceil(ragged / 8)
+  const int64_t f = R / mt, g = (R < E ? R : E);
+  return (int)(8 * ((f + 7) / 8 + (g + 7) / 8));
+}
 
 // Tile lists from offsets in global memory (the backward rebuilds them):
-// tiles of at most mt rows, and with tiles2 != nullptr a second list of at
-// most mt2 rows (one workgroup).
+// tiles of at most mt rows dealt to the XCDs, and with tiles2 != nullptr a
+// second list of at most mt2 rows in expert order (one workgroup).
 __global__ __launch_bounds__(256) void tiles_kernel(const int32_t* __restrict__ offsets, int E,
                                                     int mt, Tile* __restrict__ tiles,
                                                     int32_t* __restrict__ num_tiles, int mt2,
@@ -594,7 +683,7 @@ __global__ __launch_bounds__(256) void tiles_kernel(const int32_t* __restrict__ 
   // memory would pay a round trip per expert)
   for (int e = tid; e <= E; e += 256) offs[e] = offsets[e];
   __syncthreads();
-  write_tiles(offs, E, mt, start, tiles, num_tiles);
+  write_dealt_tiles(offs, E, mt, start, tiles, num_tiles);
   if (tiles2) write_tiles(offs, E, mt2, start, tiles2, num_tiles2);
 }
 
