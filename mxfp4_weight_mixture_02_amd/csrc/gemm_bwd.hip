@@ -21,8 +21,8 @@
 //
 // Weight path.  The workgroup's slice of each 64-row step (64 stored rows x
 // 256 columns: 8 KB of packed codes) is copied into LDS as raw bytes, and
-// its 64 x 8 scale bytes into a transposed LDS table of scale operands
-// (s << 23, the form the scaled conversion takes).  The MFMA A-operand needs
+// its 64 x 8 scale bytes into a transposed LDS table (per scale block, the
+// rows in the order the lanes read them).  The MFMA A-operand needs
 // 8 consecutive c of one output column per lane.  gfx950's 8-bit
 // transposing LDS read (ds_read_b64_tr_b8) gives each lane 8 rows x one
 // code byte, i.e. 8 consecutive c for the column pair (2m, 2m+1); the lane
@@ -68,10 +68,10 @@ constexpr int GTHR = 64 * GW;
 constexpr int GO = 256;                     // output columns per workgroup
 constexpr int GKC = 64;                     // contraction per step
 constexpr int GCB = GKC * (GO / 2);         // code tile per step: 64 rows x 128 bytes (8 KB)
-constexpr int GSB = (GO / 32) * GKC * 4;    // scale-operand table per step: 8 x 64 words (2 KB)
+constexpr int GSB = (GO / 32) * GKC;        // scale table per step: 8 blocks x 64 rows (512 bytes)
 constexpr int GXB = BMT * GKC * 2;          // activation stage (32 KB)
-constexpr int GSTAGE = GCB + GSB + GXB;     // one stage (42 KB)
-constexpr int GLDS_LOOP = 2 * GSTAGE;       // main loop: two stages (84 KB)
+constexpr int GSTAGE = GCB + GSB + GXB;     // one stage (40.5 KB)
+constexpr int GLDS_LOOP = 2 * GSTAGE;       // main loop: two stages (81 KB)
 static_assert(BMT == 256, "tile rows assumed below");
 
 // Chunk swizzle of activation row p (16-byte chunks; distinct banks for the
@@ -89,9 +89,9 @@ struct GArgs {
   uint32_t soff;            // byte offset of its scale byte (step 0)
   uint32_t cstep, sstep;    // bytes per step of 64 stored rows
   uint32_t csto;            // code-tile offset of its piece
-  uint32_t ssto;            // scale-table offset of its scale word
+  uint32_t ssto;            // scale-table offset of its scale byte
   uint32_t aoff;            // code-tile offset of the transposing read (sub-step 0)
-  uint32_t sofs;            // scale-table offset of the lane's 8 scale words (sub-step 0)
+  uint32_t sofs;            // scale-table offset of the lane's 32 scale bytes (whole step)
   uint32_t boff[4];         // activation-stage offsets of the B-fragment reads per sub-step (row block 0)
   int nsteps;
 };
@@ -105,14 +105,14 @@ struct GPipe {
 
 // MFMA operand registers carried between sub-steps (and from one step to
 // the next): decoded A-fragments (even, odd) and B-fragments of two
-// sub-steps, and the raw transposed code bytes and scale words of the
-// sub-step being decoded.
+// sub-steps, the raw transposed code bytes of the sub-step being decoded,
+// and the step's 32 scale bytes of the lane (8 rows x 4 sub-steps).
 template <int NRB>
 struct GFrags {
   bf16x8 a[2][2];
   bf16x8 b[2][NRB > 0 ? NRB : 1];
-  i32x2 raw;
-  f32x4 sc[2];
+  i32x2 raw[2];
+  u32x4 sc[2];
 };
 
 // rowoff(p): element offset of activation row p (clamping rows past the
@@ -137,9 +137,12 @@ __device__ __forceinline__ void g_setup(GArgs& g, const uint16_t* xbase, RowOff 
   const int col = (o0 + 32 * j < O) ? o0 + 32 * j : 0;   // past O: any valid column
   g.coff = (uint32_t)c0 * (uint32_t)(O / 2) + col / 2;
   g.csto = c0 * (GO / 2) + 16 * (j ^ (c0 & 7));
-  // scales: row tid / 8, scale block tid % 8 (the same 32 columns)
+  // scales: row tid / 8, scale block tid % 8 (the same 32 columns).  The
+  // table holds block b's 64 rows at b * 64, row 16 s + 8 h + r (sub-step
+  // s, half h, r < 8) at 32 h + 8 s + r: a lane's rows of all 4 sub-steps
+  // are 32 consecutive bytes
   g.soff = (uint32_t)c0 * (uint32_t)(O / 32) + col / 32;
-  g.ssto = GCB + (j * GKC + c0) * 4;
+  g.ssto = GCB + j * GKC + 32 * ((c0 >> 3) & 1) + 8 * (c0 >> 4) + (c0 & 7);
   g.cstep = (uint32_t)GKC * (O / 2);
   g.sstep = (uint32_t)GKC * (O / 32);
   // transposing read: 16-lane group grp reads rows 8 (grp / 2) .. + 7 of
@@ -149,8 +152,8 @@ __device__ __forceinline__ void g_setup(GArgs& g, const uint16_t* xbase, RowOff 
   const int row = 8 * (grp >> 1) + (jj >> 1);
   const int chunk = 2 * wo + (grp & 1);
   g.aoff = row * (GO / 2) + 16 * (chunk ^ (row & 7)) + 8 * (jj & 1);
-  // the lane's 8 rows 8 (grp / 2) .. + 7 of scale block 2 wo + grp % 2
-  g.sofs = GCB + ((2 * wo + (grp & 1)) * GKC + 8 * (grp >> 1)) * 4;
+  // the lane's rows 16 s + 8 (grp / 2) .. + 7 of scale block 2 wo + grp % 2
+  g.sofs = GCB + (2 * wo + (grp & 1)) * GKC + 32 * (grp >> 1);
   const int prel = lane & 31;
 #pragma unroll
   for (int s = 0; s < 4; ++s) g.boff[s] = GCB + GSB + prel * 128 + 16 * ((2 * s + (lane >> 5)) ^ x_swz(prel));
@@ -168,42 +171,53 @@ __device__ __forceinline__ void g_issue(GPipe& pp, const GArgs& g, int k) {
 
 // The register set into the LDS stage st: activations (instruction i of
 // wave w covers rows 8 (4 w + i) .. + 7, one 16-byte slot a lane), the code
-// piece, and the scale byte as a scale operand (s << 23).
+// piece and the scale byte.
 __device__ __forceinline__ void g_stage(const GPipe& pp, const GArgs& g, uint8_t* st) {
   const int tid = threadIdx.x;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     *reinterpret_cast<u32x4*>(st + GCB + GSB + ((tid >> 6) * 4 + i) * 1024 + 16 * (tid & 63)) = pp.act[i];
   *reinterpret_cast<u32x4*>(st + g.csto) = pp.code;
-  *reinterpret_cast<uint32_t*>(st + g.ssto) = pp.sc << 23;
+  st[g.ssto] = (uint8_t)pp.sc;
 }
 
-// LDS reads of sub-step s from stage st: the transposed code bytes and
-// scale words of the wave's double block, and its NRB B-fragments.
-template <int NRB>
-__device__ __forceinline__ void g_read(const GArgs& g, const uint8_t* st, int s, GFrags<NRB>& F,
-                                       int bi, int wp) {
-  F.raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+// LDS reads from stage st: the transposed code bytes of sub-step s (the
+// wave's double block) into raw slot s % 2, the step's scale bytes, and
+// sub-step s's NRB B-fragments into slot bi.
+__device__ __forceinline__ void g_read_raw(const GArgs& g, const uint8_t* st, int s, i32x2 (&raw)[2]) {
+  raw[s & 1] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
       (lds_i32x2*)(const_cast<uint8_t*>(st) + g.aoff + s * 16 * (GO / 2)));
-  F.sc[0] = *reinterpret_cast<const f32x4*>(st + g.sofs + s * 64);
-  F.sc[1] = *reinterpret_cast<const f32x4*>(st + g.sofs + s * 64 + 16);
+}
+
+__device__ __forceinline__ void g_read_scales(const GArgs& g, const uint8_t* st, u32x4 (&sc)[2]) {
+  sc[0] = *reinterpret_cast<const u32x4*>(st + g.sofs);
+  sc[1] = *reinterpret_cast<const u32x4*>(st + g.sofs + 16);
+}
+
+template <int NRB>
+__device__ __forceinline__ void g_read_b(const GArgs& g, const uint8_t* st, int s, GFrags<NRB>& F,
+                                         int bi, int wp) {
 #pragma unroll
   for (int j = 0; j < NRB; ++j)
     F.b[bi][j] = *reinterpret_cast<const bf16x8*>(st + g.boff[s] + (wp + 2 * j) * 4096);
 }
 
-// Decode the raw bytes into A-fragment slot ai: fragment 0 holds the even
-// columns, 1 the odd ones.  Byte r of the 8 is row r of the lane's 8 (its
-// own scale word); its two nibbles are the column pair, so one scaled
-// conversion gives (even, odd) as packed bf16, and byte permutes gather the
-// evens and the odds.
+// Decode sub-step s's raw bytes into A-fragment slot ai: fragment 0 holds
+// the even columns, 1 the odd ones.  Byte r of the 8 is row r of the lane's
+// 8 (its own scale byte); its two nibbles are the column pair, so one
+// scaled conversion gives (even, odd) as packed bf16, and byte permutes
+// gather the evens and the odds.  The conversion reads the scale operand's
+// exponent field (bits 23..30) only, so one shift moves scale byte r % 4 of
+// its word there, whatever the other bits hold.
 template <int NRB>
-__device__ __forceinline__ void g_decode(GFrags<NRB>& F, int ai) {
+__device__ __forceinline__ void g_decode(GFrags<NRB>& F, int ai, int s) {
   uint32_t pr[8];
 #pragma unroll
   for (int r = 0; r < 8; ++r) {
-    const uint32_t w = (uint32_t)F.raw[r >> 2];
-    const float sc = F.sc[r >> 2][r & 3];
+    const uint32_t w = (uint32_t)F.raw[s & 1][r >> 2];
+    const int d = 2 * s + (r >> 2);
+    const uint32_t sw = F.sc[d >> 2][d & 3];
+    const float sc = __builtin_bit_cast(float, (r & 3) == 3 ? sw >> 1 : sw << (23 - 8 * (r & 3)));
     switch (r & 3) {
       case 0: pr[r] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0)); break;
       case 1: pr[r] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1)); break;
@@ -247,18 +261,23 @@ __device__ __forceinline__ void g_order() {
 
 // One step k (stage cur = k % 2), in scheduling regions fenced by
 // sched_barrier.  On entry sub-step 0's operands are decoded (A, slot 0)
-// and read (B, slot 0), and the register set holds step k + 1's loads.
+// and read (B, slot 0), sub-step 1's code bytes are read, and the register
+// set holds step k + 1's loads.
 //   (0) the register set into the other stage; reload it with step k + 2;
-//   (1..3) sub-step s + 1's reads, then sub-step s's MFMAs with the decode of
-//       s + 1 interleaved;
+//   (1..3) sub-step s + 2's code bytes and s + 1's B-fragments, then
+//       sub-step s's MFMAs with the decode of s + 1 interleaved (its code
+//       bytes were read a region earlier, so the decode does not wait for
+//       LDS);
 //   wait for this wave's LDS traffic and meet the other waves: the other
 //   stage is complete and every wave is done reading this one, so
-//   (4) step k + 1's sub-step 0 reads, then sub-step 3's MFMAs with that
-//       decode interleaved.
+//   (4) step k + 1's scale bytes, sub-step 0 and 1 code bytes and sub-step
+//       0 B-fragments, then sub-step 3's MFMAs with the decode of step k +
+//       1's sub-step 0 interleaved.
 template <int NRB>
 __device__ __forceinline__ void g_step(GPipe& pp, GFrags<NRB>& F, const GArgs& g, int k,
                                        uint8_t* lds, int wp, f32x16 (&acc)[2][4]) {
-  constexpr int NM = 2 * NRB, NR = 3 + NRB;
+  // 24 decode instructions spread over the MFMAs
+  constexpr int NM = 2 * NRB, FPER = (24 + NM - 1) / (NM > 0 ? NM : 1);
   uint8_t* cur = lds + (k & 1) * GSTAGE;
   uint8_t* nxt = lds + ((k & 1) ^ 1) * GSTAGE;
   __builtin_amdgcn_sched_barrier(0);
@@ -268,20 +287,27 @@ __device__ __forceinline__ void g_step(GPipe& pp, GFrags<NRB>& F, const GArgs& g
 #pragma unroll
   for (int s = 0; s < 3; ++s) {
     if constexpr (NRB > 0) {
-      g_read<NRB>(g, cur, s + 1, F, (s + 1) & 1, wp);
+      if (s < 2) g_read_raw(g, cur, s + 2, F.raw);
+      g_read_b<NRB>(g, cur, s + 1, F, (s + 1) & 1, wp);
       g_mfmas<NRB>(F, s & 1, s & 1, acc);
-      g_decode<NRB>(F, (s + 1) & 1);
-      g_order<NR, NM, NM, 2>();
+      g_decode<NRB>(F, (s + 1) & 1, s + 1);
+      if (s < 2)
+        g_order<1 + NRB, NM, NM, FPER>();
+      else
+        g_order<NRB, NM, NM, FPER>();
     }
     __builtin_amdgcn_sched_barrier(0);
   }
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
   barrier_only();
   if constexpr (NRB > 0) {
-    g_read<NRB>(g, nxt, 0, F, 0, wp);
+    g_read_scales(g, nxt, F.sc);
+    g_read_raw(g, nxt, 0, F.raw);
+    g_read_raw(g, nxt, 1, F.raw);
+    g_read_b<NRB>(g, nxt, 0, F, 0, wp);
     g_mfmas<NRB>(F, 1, 1, acc);
-    g_decode<NRB>(F, 0);
-    g_order<NR, NM, NM, 2>();
+    g_decode<NRB>(F, 0, 0);
+    g_order<4 + NRB, NM, NM, FPER>();
   }
   __builtin_amdgcn_sched_barrier(0);
 }
@@ -296,8 +322,11 @@ __device__ __forceinline__ void g_loop(const GArgs& g, uint8_t* lds, int wp, f32
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
   barrier_only();
   if constexpr (NRB > 0) {
-    g_read<NRB>(g, lds, 0, F, 0, wp);
-    g_decode<NRB>(F, 0);
+    g_read_scales(g, lds, F.sc);
+    g_read_raw(g, lds, 0, F.raw);
+    g_read_raw(g, lds, 1, F.raw);
+    g_read_b<NRB>(g, lds, 0, F, 0, wp);
+    g_decode<NRB>(F, 0, 0);
   }
   for (int k = 0; k < g.nsteps; ++k) g_step<NRB>(pp, F, g, k, lds, wp, acc);
   // the last step read (unused) operands of the other stage; every wave
