@@ -68,51 +68,50 @@ constexpr int GTHR = 64 * GW;
 constexpr int GO = 256;                     // output columns per workgroup
 constexpr int GKC = 64;                     // contraction per step
 constexpr int GCB = GKC * (GO / 2);         // code tile per step: 64 rows x 128 bytes (8 KB)
-constexpr int GSB = (GO / 32) * GKC;        // scale table per step: 8 blocks x 64 rows (512 bytes)
+constexpr int GSB = (GO / 32) * GKC * 4;    // scale table per step: 8 blocks x 64 rows, a word each (2 KB)
 constexpr int GXB = BMT * GKC * 2;          // activation stage (32 KB)
-constexpr int GSTAGE = GCB + GSB + GXB;     // one stage (40.5 KB)
-constexpr int GLDS_LOOP = 2 * GSTAGE;       // main loop: two stages (81 KB)
+constexpr int GSTAGE = GCB + GSB + GXB;     // one stage (42 KB)
+constexpr int GNST = 3;                     // stages in flight
+constexpr int GLDS_LOOP = GNST * GSTAGE;    // main loop (126 KB)
+constexpr int GDMA = 6;                     // LDS-DMA loads per wave per step
 static_assert(BMT == 256, "tile rows assumed below");
+
+typedef __attribute__((address_space(1))) const void* gptr_t;
+typedef __attribute__((address_space(3))) void* lptr_t;
 
 // Chunk swizzle of activation row p (16-byte chunks; distinct banks for the
 // 16-byte reads of 8 and of 16 consecutive rows).
 __device__ __forceinline__ int x_swz(int p) { return (p & 7) ^ ((p >> 3) & 1); }
 
 // Per-lane addressing, fixed for the whole main loop (LDS offsets are
-// relative to a stage).
+// relative to a stage).  Every step's tile is copied global -> LDS by
+// LDS-DMA loads: a lane names its source, and the data lands at the
+// instruction's LDS base + 16 (or, for a byte, 4) x lane.
 struct GArgs {
   const uint16_t* xbase;    // activations (workgroup-uniform)
-  uint32_t xoff[4];         // element offsets of the 4 activation pieces this lane stages (step 0)
+  uint32_t xoff[4];         // element offsets of the 4 activation pieces this lane copies (step 0)
   const uint8_t* wcode;     // the expert's codes and scales (workgroup-uniform)
   const uint8_t* wscale;
-  uint32_t coff;            // byte offset of this thread's 16-byte code piece (step 0)
+  uint32_t coff;            // byte offset of this lane's 16-byte code piece (step 0)
   uint32_t soff;            // byte offset of its scale byte (step 0)
   uint32_t cstep, sstep;    // bytes per step of 64 stored rows
-  uint32_t csto;            // code-tile offset of its piece
-  uint32_t ssto;            // scale-table offset of its scale byte
   uint32_t aoff;            // code-tile offset of the transposing read (sub-step 0)
-  uint32_t sofs;            // scale-table offset of the lane's 32 scale bytes (whole step)
+  uint32_t sofs;            // scale-table offset of the lane's 8 scale words (sub-step 0)
   uint32_t boff[4];         // activation-stage offsets of the B-fragment reads per sub-step (row block 0)
+  int wave;                 // wave index (uniform)
   int nsteps;
-};
-
-// One step's loads (a single register set: staged, then reloaded).
-struct GPipe {
-  u32x4 act[4];
-  u32x4 code;
-  uint32_t sc;
 };
 
 // MFMA operand registers carried between sub-steps (and from one step to
 // the next): decoded A-fragments (even, odd) and B-fragments of two
-// sub-steps, the raw transposed code bytes of the sub-step being decoded,
-// and the step's 32 scale bytes of the lane (8 rows x 4 sub-steps).
+// sub-steps, and the raw transposed code bytes and scale words of two
+// sub-steps (read a region before their decode).
 template <int NRB>
 struct GFrags {
   bf16x8 a[2][2];
   bf16x8 b[2][NRB > 0 ? NRB : 1];
   i32x2 raw[2];
-  u32x4 sc[2];
+  u32x4 sc[2][2];
 };
 
 // rowoff(p): element offset of activation row p (clamping rows past the
@@ -122,9 +121,13 @@ template <class RowOff>
 __device__ __forceinline__ void g_setup(GArgs& g, const uint16_t* xbase, RowOff rowoff,
                                         const uint8_t* wcode, const uint8_t* wscale, int C,
                                         int O, int o0) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wo = wave & 3;
+  g.wave = wave;
   g.xbase = xbase;
+  // activations: instruction i of wave w fills rows 8 (4 w + i) .. + 7,
+  // slot lane % 8 of row p holding chunk (lane % 8) ^ x_swz(p)
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int p = 32 * wave + 8 * i + (lane >> 3);
@@ -132,17 +135,20 @@ __device__ __forceinline__ void g_setup(GArgs& g, const uint16_t* xbase, RowOff 
   }
   g.wcode = wcode;
   g.wscale = wscale;
-  // codes: row tid / 8, 16-byte chunk tid % 8 (32 columns)
-  const int c0 = tid >> 3, j = tid & 7;
+  // codes: LDS slot tid of the tile is row c0 = tid / 8, slot tid % 8,
+  // holding 16-byte chunk j = (tid % 8) ^ (c0 % 8) (32 columns)
+  const int c0 = tid >> 3, j = (tid & 7) ^ (c0 & 7);
   const int col = (o0 + 32 * j < O) ? o0 + 32 * j : 0;   // past O: any valid column
   g.coff = (uint32_t)c0 * (uint32_t)(O / 2) + col / 2;
-  g.csto = c0 * (GO / 2) + 16 * (j ^ (c0 & 7));
-  // scales: row tid / 8, scale block tid % 8 (the same 32 columns).  The
-  // table holds block b's 64 rows at b * 64, row 16 s + 8 h + r (sub-step
-  // s, half h, r < 8) at 32 h + 8 s + r: a lane's rows of all 4 sub-steps
-  // are 32 consecutive bytes
-  g.soff = (uint32_t)c0 * (uint32_t)(O / 32) + col / 32;
-  g.ssto = GCB + j * GKC + 32 * ((c0 >> 3) & 1) + 8 * (c0 >> 4) + (c0 & 7);
+  // scales: table word tid = 64 b + 32 h + 8 s + r holds row 16 s + 8 h + r
+  // (sub-step s, half h, r < 8) of scale block b = wave, so a lane's 8 rows
+  // of one sub-step are 8 consecutive words
+  {
+    const int r = lane & 7, ss = (lane >> 3) & 3, h = lane >> 5;
+    const int row = 16 * ss + 8 * h + r;
+    const int scol = (o0 + 32 * wave < O) ? o0 + 32 * wave : 0;
+    g.soff = (uint32_t)row * (uint32_t)(O / 32) + scol / 32;
+  }
   g.cstep = (uint32_t)GKC * (O / 2);
   g.sstep = (uint32_t)GKC * (O / 32);
   // transposing read: 16-lane group grp reads rows 8 (grp / 2) .. + 7 of
@@ -152,51 +158,41 @@ __device__ __forceinline__ void g_setup(GArgs& g, const uint16_t* xbase, RowOff 
   const int row = 8 * (grp >> 1) + (jj >> 1);
   const int chunk = 2 * wo + (grp & 1);
   g.aoff = row * (GO / 2) + 16 * (chunk ^ (row & 7)) + 8 * (jj & 1);
-  // the lane's rows 16 s + 8 (grp / 2) .. + 7 of scale block 2 wo + grp % 2
-  g.sofs = GCB + (2 * wo + (grp & 1)) * GKC + 32 * (grp >> 1);
+  // the lane's 8 rows 8 (grp / 2) .. + 7 of scale block 2 wo + grp % 2
+  g.sofs = GCB + ((2 * wo + (grp & 1)) * GKC + 32 * (grp >> 1)) * 4;
   const int prel = lane & 31;
 #pragma unroll
   for (int s = 0; s < 4; ++s) g.boff[s] = GCB + GSB + prel * 128 + 16 * ((2 * s + (lane >> 5)) ^ x_swz(prel));
   g.nsteps = C / GKC;
 }
 
-// Loads of step k into the register set.
-__device__ __forceinline__ void g_issue(GPipe& pp, const GArgs& g, int k) {
+// Step k's tile into LDS stage st (GDMA loads of this wave).
+__device__ __forceinline__ void g_dma(const GArgs& g, uint8_t* __restrict__ st, int k) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    pp.act[i] = *reinterpret_cast<const u32x4*>(g.xbase + (g.xoff[i] + (uint32_t)(k * GKC)));
-  pp.code = *reinterpret_cast<const u32x4*>(g.wcode + (g.coff + (uint32_t)k * g.cstep));
-  pp.sc = g.wscale[g.soff + (uint32_t)k * g.sstep];
+    __builtin_amdgcn_global_load_lds((gptr_t)(g.xbase + (g.xoff[i] + (uint32_t)(k * GKC))),
+                                     (lptr_t)(st + GCB + GSB + (g.wave * 4 + i) * 1024), 16, 0, 0);
+  __builtin_amdgcn_global_load_lds((gptr_t)(g.wcode + (g.coff + (uint32_t)k * g.cstep)),
+                                   (lptr_t)(st + g.wave * 1024), 16, 0, 0);
+  __builtin_amdgcn_global_load_lds((gptr_t)(g.wscale + (g.soff + (uint32_t)k * g.sstep)),
+                                   (lptr_t)(st + GCB + g.wave * 256), 1, 0, 0);
 }
 
-// The register set into the LDS stage st: activations (instruction i of
-// wave w covers rows 8 (4 w + i) .. + 7, one 16-byte slot a lane), the code
-// piece and the scale byte.
-__device__ __forceinline__ void g_stage(const GPipe& pp, const GArgs& g, uint8_t* st) {
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    *reinterpret_cast<u32x4*>(st + GCB + GSB + ((tid >> 6) * 4 + i) * 1024 + 16 * (tid & 63)) = pp.act[i];
-  *reinterpret_cast<u32x4*>(st + g.csto) = pp.code;
-  st[g.ssto] = (uint8_t)pp.sc;
-}
-
-// LDS reads from stage st: the transposed code bytes of sub-step s (the
-// wave's double block) into raw slot s % 2, the step's scale bytes, and
-// sub-step s's NRB B-fragments into slot bi.
-__device__ __forceinline__ void g_read_raw(const GArgs& g, const uint8_t* st, int s, i32x2 (&raw)[2]) {
-  raw[s & 1] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+// LDS reads from stage st: the transposed code bytes and the 8 scale words
+// of sub-step s (the wave's double block) into slot s % 2, and sub-step s's
+// NRB B-fragments into slot bi.
+template <int NRB>
+__device__ __forceinline__ void g_read_a(const GArgs& g, const uint8_t* __restrict__ st, int s,
+                                         GFrags<NRB>& F) {
+  F.raw[s & 1] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
       (lds_i32x2*)(const_cast<uint8_t*>(st) + g.aoff + s * 16 * (GO / 2)));
-}
-
-__device__ __forceinline__ void g_read_scales(const GArgs& g, const uint8_t* st, u32x4 (&sc)[2]) {
-  sc[0] = *reinterpret_cast<const u32x4*>(st + g.sofs);
-  sc[1] = *reinterpret_cast<const u32x4*>(st + g.sofs + 16);
+  F.sc[s & 1][0] = *reinterpret_cast<const u32x4*>(st + g.sofs + s * 32);
+  F.sc[s & 1][1] = *reinterpret_cast<const u32x4*>(st + g.sofs + s * 32 + 16);
 }
 
 template <int NRB>
-__device__ __forceinline__ void g_read_b(const GArgs& g, const uint8_t* st, int s, GFrags<NRB>& F,
-                                         int bi, int wp) {
+__device__ __forceinline__ void g_read_b(const GArgs& g, const uint8_t* __restrict__ st, int s,
+                                         GFrags<NRB>& F, int bi, int wp) {
 #pragma unroll
   for (int j = 0; j < NRB; ++j)
     F.b[bi][j] = *reinterpret_cast<const bf16x8*>(st + g.boff[s] + (wp + 2 * j) * 4096);
@@ -204,20 +200,17 @@ __device__ __forceinline__ void g_read_b(const GArgs& g, const uint8_t* st, int 
 
 // Decode sub-step s's raw bytes into A-fragment slot ai: fragment 0 holds
 // the even columns, 1 the odd ones.  Byte r of the 8 is row r of the lane's
-// 8 (its own scale byte); its two nibbles are the column pair, so one
-// scaled conversion gives (even, odd) as packed bf16, and byte permutes
-// gather the evens and the odds.  The conversion reads the scale operand's
-// exponent field (bits 23..30) only, so one shift moves scale byte r % 4 of
-// its word there, whatever the other bits hold.
+// 8 (its own scale word, the UE8M0 byte moved to the exponent field: the
+// scaled conversion reads only that field of its scale operand); its two
+// nibbles are the column pair, so one scaled conversion gives (even, odd)
+// as packed bf16, and byte permutes gather the evens and the odds.
 template <int NRB>
 __device__ __forceinline__ void g_decode(GFrags<NRB>& F, int ai, int s) {
   uint32_t pr[8];
 #pragma unroll
   for (int r = 0; r < 8; ++r) {
     const uint32_t w = (uint32_t)F.raw[s & 1][r >> 2];
-    const int d = 2 * s + (r >> 2);
-    const uint32_t sw = F.sc[d >> 2][d & 3];
-    const float sc = __builtin_bit_cast(float, (r & 3) == 3 ? sw >> 1 : sw << (23 - 8 * (r & 3)));
+    const float sc = __builtin_bit_cast(float, F.sc[s & 1][r >> 2][r & 3] << 23);
     switch (r & 3) {
       case 0: pr[r] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0)); break;
       case 1: pr[r] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1)); break;
@@ -259,78 +252,122 @@ __device__ __forceinline__ void g_order() {
   }
 }
 
-// One step k (stage cur = k % 2), in scheduling regions fenced by
-// sched_barrier.  On entry sub-step 0's operands are decoded (A, slot 0)
-// and read (B, slot 0), sub-step 1's code bytes are read, and the register
-// set holds step k + 1's loads.
-//   (0) the register set into the other stage; reload it with step k + 2;
-//   (1..3) sub-step s + 2's code bytes and s + 1's B-fragments, then
-//       sub-step s's MFMAs with the decode of s + 1 interleaved (its code
-//       bytes were read a region earlier, so the decode does not wait for
-//       LDS);
-//   wait for this wave's LDS traffic and meet the other waves: the other
-//   stage is complete and every wave is done reading this one, so
-//   (4) step k + 1's scale bytes, sub-step 0 and 1 code bytes and sub-step
-//       0 B-fragments, then sub-step 3's MFMAs with the decode of step k +
-//       1's sub-step 0 interleaved.
+// The same with the first half of the MFMAs back to back after the reads
+// and the VALU work spread over the second half (its inputs are this
+// region's reads, which then have half the MFMAs' time to arrive).
+template <int NR, int NM, int FPER>
+__device__ __forceinline__ void g_order_late() {
+  __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, NM / 2, 0);
+#pragma unroll
+  for (int m = NM / 2; m < NM; ++m) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 2 * FPER, 0);
+  }
+}
+
+// The same with the region's first MFMA issued before its LDS reads (its
+// operands come from the previous region, so waiting for them does not
+// wait for this region's reads).
+template <int NR, int NM, int NF, int FPER>
+__device__ __forceinline__ void g_order_mfirst() {
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+  __builtin_amdgcn_sched_group_barrier(0x002, FPER, 0);
+#pragma unroll
+  for (int m = 1; m < NM; ++m) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (m < NF) __builtin_amdgcn_sched_group_barrier(0x002, FPER, 0);
+  }
+}
+
+// One step k (stages: cur = k % 3 holds step k, nxt = (k + 1) % 3 step k +
+// 1, dst = (k + 2) % 3 was last read in step k - 1), in scheduling regions
+// fenced by sched_barrier.  On entry sub-step 0's operands are decoded (A,
+// slot 0) and read (B, slot 0) and sub-step 1's code bytes and scales are
+// read; step k + 1's copy is in flight.
+//   (0) start step k + 2's copy into dst;
+//   (1..3) sub-step s + 2's code bytes and scales and s + 1's B-fragments,
+//       then sub-step s's MFMAs with the decode of s + 1 interleaved (its
+//       operands were read a region earlier);
+//   wait for this wave's copy of step k + 1 and its LDS reads, and meet the
+//   other waves: nxt is complete and every wave is done reading cur, so
+//   (4) step k + 1's sub-step 0 and 1 code bytes and scales and sub-step 0
+//       B-fragments, then sub-step 3's MFMAs with the decode of step k + 1's
+//       sub-step 0 interleaved.
 template <int NRB>
-__device__ __forceinline__ void g_step(GPipe& pp, GFrags<NRB>& F, const GArgs& g, int k,
-                                       uint8_t* lds, int wp, f32x16 (&acc)[2][4]) {
-  // 24 decode instructions spread over the MFMAs
-  constexpr int NM = 2 * NRB, FPER = (24 + NM - 1) / (NM > 0 ? NM : 1);
-  uint8_t* cur = lds + (k & 1) * GSTAGE;
-  uint8_t* nxt = lds + ((k & 1) ^ 1) * GSTAGE;
+__device__ __forceinline__ void g_step(GFrags<NRB>& F, const GArgs& g, int k,
+                                       const uint8_t* __restrict__ cur,
+                                       const uint8_t* __restrict__ nxt, uint8_t* __restrict__ dst,
+                                       int wp, f32x16 (&acc)[2][4]) {
+  // 16 decode instructions spread over the MFMAs
+  constexpr int NM = 2 * NRB, FPER = (16 + NM - 1) / (NM > 0 ? NM : 1);
   __builtin_amdgcn_sched_barrier(0);
-  g_stage(pp, g, nxt);
-  g_issue(pp, g, min(k + 2, g.nsteps - 1));
+  g_dma(g, dst, min(k + 2, g.nsteps - 1));
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int s = 0; s < 3; ++s) {
     if constexpr (NRB > 0) {
-      if (s < 2) g_read_raw(g, cur, s + 2, F.raw);
+      if (s < 2) g_read_a<NRB>(g, cur, s + 2, F);
       g_read_b<NRB>(g, cur, s + 1, F, (s + 1) & 1, wp);
       g_mfmas<NRB>(F, s & 1, s & 1, acc);
       g_decode<NRB>(F, (s + 1) & 1, s + 1);
-      if (s < 2)
-        g_order<1 + NRB, NM, NM, FPER>();
+      if (s == 0)
+        g_order<3 + NRB, NM, NM, FPER>();
+      else if (s == 1)
+        g_order_mfirst<3 + NRB, NM, NM, FPER>();
       else
-        g_order<NRB, NM, NM, FPER>();
+        g_order_mfirst<NRB, NM, NM, FPER>();
     }
     __builtin_amdgcn_sched_barrier(0);
   }
-  __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(GDMA, 0));
   barrier_only();
   if constexpr (NRB > 0) {
-    g_read_scales(g, nxt, F.sc);
-    g_read_raw(g, nxt, 0, F.raw);
-    g_read_raw(g, nxt, 1, F.raw);
+    g_read_a<NRB>(g, nxt, 0, F);
+    g_read_a<NRB>(g, nxt, 1, F);
     g_read_b<NRB>(g, nxt, 0, F, 0, wp);
     g_mfmas<NRB>(F, 1, 1, acc);
     g_decode<NRB>(F, 0, 0);
-    g_order<4 + NRB, NM, NM, FPER>();
+    g_order_late<6 + NRB, NM, FPER>();
   }
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// Steps k .. k + n - 1 (n <= 3) with k % 3 == 0: stage i holds step k + i.
+// The three stages are distinct, which lets the compiler see that a stage's
+// reads do not depend on the copies into the others.
+template <int NRB>
+__device__ __forceinline__ void g_trip(GFrags<NRB>& F, const GArgs& g, int k, int n,
+                                       uint8_t* __restrict__ st0, uint8_t* __restrict__ st1,
+                                       uint8_t* __restrict__ st2, int wp, f32x16 (&acc)[2][4]) {
+  g_step<NRB>(F, g, k, st0, st1, st2, wp, acc);
+  if (n > 1) g_step<NRB>(F, g, k + 1, st1, st2, st0, wp, acc);
+  if (n > 2) g_step<NRB>(F, g, k + 2, st2, st0, st1, wp, acc);
+}
+
 template <int NRB>
 __device__ __forceinline__ void g_loop(const GArgs& g, uint8_t* lds, int wp, f32x16 (&acc)[2][4]) {
-  GPipe pp;
   GFrags<NRB> F;
-  g_issue(pp, g, 0);
-  g_stage(pp, g, lds);
-  g_issue(pp, g, min(1, g.nsteps - 1));
-  __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+  uint8_t* st0 = lds;
+  uint8_t* st1 = lds + GSTAGE;
+  uint8_t* st2 = lds + 2 * GSTAGE;
+  g_dma(g, st0, 0);
+  g_dma(g, st1, min(1, g.nsteps - 1));
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(GDMA, 0));
   barrier_only();
   if constexpr (NRB > 0) {
-    g_read_scales(g, lds, F.sc);
-    g_read_raw(g, lds, 0, F.raw);
-    g_read_raw(g, lds, 1, F.raw);
-    g_read_b<NRB>(g, lds, 0, F, 0, wp);
+    g_read_a<NRB>(g, st0, 0, F);
+    g_read_a<NRB>(g, st0, 1, F);
+    g_read_b<NRB>(g, st0, 0, F, 0, wp);
     g_decode<NRB>(F, 0, 0);
   }
-  for (int k = 0; k < g.nsteps; ++k) g_step<NRB>(pp, F, g, k, lds, wp, acc);
-  // the last step read (unused) operands of the other stage; every wave
-  // must be past its LDS reads before the epilogue reuses LDS
+  // three steps per trip, so each step's stages are fixed pointers
+  int k = 0;
+  for (; k + 3 <= g.nsteps; k += 3) g_trip<NRB>(F, g, k, 3, st0, st1, st2, wp, acc);
+  if (k < g.nsteps) g_trip<NRB>(F, g, k, g.nsteps - k, st0, st1, st2, wp, acc);
+  // the last steps copied and read (unused) operands of other stages; every
+  // wave must be past them before the epilogue reuses LDS
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
   __syncthreads();
 }
@@ -568,9 +605,9 @@ __global__ __launch_bounds__(GTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
     const uint16_t* __restrict__ asv, int H, int I, int k, float alpha, float limit,
     const uint16_t* __restrict__ lora_At, const float* __restrict__ lora_dvu,
     uint16_t* __restrict__ dh, float* __restrict__ dw_part) {
-  // the epilogue's strips (8 x 12 KB) and dw reduction cover the main loop's stages
-  __shared__ __attribute__((aligned(16))) uint8_t lds[GW * 12288 + GW * (BMT / 2) * 4];
-  static_assert(GW * 12288 + GW * (BMT / 2) * 4 >= GLDS_LOOP, "epilogue LDS covers the loop's");
+  // the epilogue's strips (8 x 12 KB) and dw reduction reuse the main loop's stages
+  __shared__ __attribute__((aligned(16))) uint8_t lds[GLDS_LOOP];
+  static_assert(GW * 12288 + GW * (BMT / 2) * 4 <= GLDS_LOOP, "the epilogue fits the loop's LDS");
   Tile tl;
   int ot;
   const int otiles = (I + GO - 1) / GO;
