@@ -52,11 +52,12 @@ extern "C" {
 
 /* Layer shape and activation constants.
  *  T tokens, H hidden, I intermediate, E experts, k experts per token.
- *  Requirements: T >= 1; H % 64 == 0 and I % 64 == 0 (whole 32-element
- *  scale blocks, [P3] group-32 guard, in 64-element K steps);
- *  1 <= k <= min(E, 8); E <= 256; T * k < 2^31; T * H < 2^31;
- *  H, I <= 5120; lora_rank in {0, 16}.  Weight, scale, bias, activation
- *  and output pointers 16-byte aligned.
+ *  Requirements: T >= 1; H % 32 == 0 and I % 32 == 0 (whole 32-element
+ *  scale blocks, [P3] group-32 guard; the kernels run 64-element K steps
+ *  and read zeros past an odd multiple of 32); 1 <= k <= min(E, 8);
+ *  E <= 256; T * k < 2^31; T * H < 2^31; H, I <= 5120;
+ *  lora_rank in {0, 8, 16, 32, 64}.  Weight, scale, bias, activation and
+ *  output pointers 16-byte aligned.
  *  swiglu_alpha, swiglu_limit: the clamped SwiGLU constants (GPT-OSS uses
  *  1.702 and 7).  lora_scale multiplies the LoRA delta (1.0 when
  *  lora_alpha equals the rank). */
@@ -86,9 +87,10 @@ typedef struct mxfp4_moe_dims {
  *            the down projection ([P1] "What this does": adapters train on
  *            the frozen MXFP4 base), y += scale * (a A_e^T) B_e^T.  Both
  *            NULL when lora_rank == 0 (MXFP4_EINVAL otherwise), both
- *            required and 16-byte aligned when lora_rank == 16.  Inside the
+ *            required and 16-byte aligned when lora_rank > 0.  Inside the
  *            down GEMMs, scale * v and the rank-space gradient enter the
- *            bf16 matrix cores as a hi + lo bf16 pair (about 17 bits). */
+ *            bf16 matrix cores as a hi + lo bf16 pair (about 17 bits), in
+ *            16-deep chunks of the rank (rank 8 zero-padded to one). */
 typedef struct mxfp4_moe_weights {
   const float* router_w;
   const float* router_b;

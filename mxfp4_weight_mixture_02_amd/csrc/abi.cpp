@@ -61,8 +61,8 @@ int check_dims(const mxfp4_moe_dims* d) {
   if (d->T < 1 || d->H < 1 || d->I < 1 || d->E < 1 || d->k < 1)
     return fail(MXFP4_EINVAL, "T, H, I, E and k must be >= 1 (T=%lld H=%lld I=%lld E=%d k=%d)",
                 (long long)d->T, (long long)d->H, (long long)d->I, d->E, d->k);
-  if (d->H % 64 || d->I % 64)
-    return fail(MXFP4_EUNSUPPORTED, "H and I must be multiples of 64 (H=%lld I=%lld)",
+  if (d->H % 32 || d->I % 32)
+    return fail(MXFP4_EUNSUPPORTED, "H and I must be multiples of 32 (H=%lld I=%lld)",
                 (long long)d->H, (long long)d->I);
   if (d->E > 256) return fail(MXFP4_EUNSUPPORTED, "E=%d > 256", d->E);
   if (d->k > d->E || d->k > 8) return fail(MXFP4_EUNSUPPORTED, "k=%d must be <= min(E, 8)", d->k);
@@ -73,9 +73,9 @@ int check_dims(const mxfp4_moe_dims* d) {
                 (long long)d->I);
   if (d->T * d->H >= (int64_t(1) << 31))
     return fail(MXFP4_EUNSUPPORTED, "T*H = %lld elements exceed int32", (long long)(d->T * d->H));
-  if (d->lora_rank != 0 && d->lora_rank != mxmoe::LORA_R)
-    return fail(MXFP4_EUNSUPPORTED, "lora_rank=%d: supported ranks are 0 and %d", d->lora_rank,
-                mxmoe::LORA_R);
+  if (d->lora_rank != 0 && !mxmoe::lora_rank_ok(d->lora_rank))
+    return fail(MXFP4_EUNSUPPORTED, "lora_rank=%d: supported ranks are 0, 8, 16, 32 and 64",
+                d->lora_rank);
   if (d->lora_rank && !(d->lora_scale == d->lora_scale && d->lora_scale - d->lora_scale == 0.0f))
     return fail(MXFP4_EINVAL, "lora_scale must be finite");
   return MXFP4_OK;
@@ -288,16 +288,21 @@ int enqueue_forward(const mxfp4_moe_dims& d, const mxfp4_moe_weights* w, const u
            "scan");
     LAUNCH(mxmoe::launch_scatter(topk_idx, blk_hist, T, k, E, sorted_rows, s), "scatter");
   }
-  // few rows per expert: the weight-streaming decode kernels (no LoRA there)
-  const bool decode = R <= DECODE_MAX_ROWS && !d.lora_rank && H <= mxmoe::dec_max_k() &&
-                      I <= mxmoe::dec_max_k();
+  // few rows per expert: the weight-streaming decode kernels
+  const bool decode = R <= DECODE_MAX_ROWS && H <= mxmoe::dec_max_k() && I <= mxmoe::dec_max_k();
   if (decode) {
     LAUNCH(mxmoe::launch_dec_gate_up(x, w->gu_codes, w->gu_scales, w->gu_bias, sorted_rows, tiles,
                                      num_tiles, maxt, R, H, I, k, d.swiglu_alpha, d.swiglu_limit,
                                      h, a, s),
            "dec_gate_up");
+    if (d.lora_rank)
+      LAUNCH(mxmoe::launch_lora_proj(a, false, sorted_rows, k, w->lora_A, I, d.lora_rank, tiles,
+                                     num_tiles, maxt, 1.0f, lora_v, s),
+             "lora_v");
     LAUNCH(mxmoe::launch_dec_down(a, w->dn_codes, w->dn_scales, w->dn_bias, topk_w, sorted_rows,
-                                  tiles, num_tiles, maxt, R, H, I, y_w, s),
+                                  tiles, num_tiles, maxt, R, H, I,
+                                  d.lora_rank ? w->lora_B : nullptr, lora_v, d.lora_scale,
+                                  d.lora_rank, y_w, s),
            "dec_down");
     LAUNCH(mxmoe::launch_combine(y_w, d.T, H, k, out, s), "combine");
     return ok();
@@ -306,12 +311,12 @@ int enqueue_forward(const mxfp4_moe_dims& d, const mxfp4_moe_weights* w, const u
                                num_tiles, maxt, H, I, k, d.swiglu_alpha, d.swiglu_limit, h, a, s),
          "gate_up");
   if (d.lora_rank)
-    LAUNCH(mxmoe::launch_lora_proj(a, false, sorted_rows, k, w->lora_A, I, tiles, num_tiles, maxt,
-                                   1.0f, lora_v, s),
+    LAUNCH(mxmoe::launch_lora_proj(a, false, sorted_rows, k, w->lora_A, I, d.lora_rank, tiles,
+                                   num_tiles, maxt, 1.0f, lora_v, s),
            "lora_v");
   LAUNCH(mxmoe::launch_down(a, w->dn_codes, w->dn_scales, w->dn_bias, topk_w, sorted_rows, tiles,
                             num_tiles, maxt, H, I, d.lora_rank ? w->lora_B : nullptr, lora_v,
-                            d.lora_scale, y_w, s),
+                            d.lora_scale, d.lora_rank, y_w, s),
          "down");
   LAUNCH(mxmoe::launch_combine(y_w, d.T, H, k, out, s), "combine");
   return ok();
@@ -475,22 +480,23 @@ int mxfp4_moe_backward_dx(const mxfp4_moe_dims* dims, const mxfp4_moe_weights* w
     LAUNCH(mxmoe::launch_transpose_bf16(w->lora_A, E, r, I, lora_At, s), "lora_transpose");
     LAUNCH(mxmoe::launch_transpose_bf16(w->lora_B, E, H, r, lora_Bt, s), "lora_transpose");
     // dv_u = s dY_t B_e over the token rows of dY
-    LAUNCH(mxmoe::launch_lora_proj(dy, true, saved->sorted_rows, k, lora_Bt, H, tiles_l,
+    LAUNCH(mxmoe::launch_lora_proj(dy, true, saved->sorted_rows, k, lora_Bt, H, r, tiles_l,
                                    num_tiles_l, mxmoe::max_tiles(R, E, mxmoe::MT), d.lora_scale,
                                    lora_dvu, s),
            "lora_dvu");
   }
   LAUNCH(mxmoe::launch_bwd_down(dy, w->dn_codes, w->dn_scales, saved->topk_w, saved->sorted_rows,
                                 tiles, num_tiles, maxt, saved->h, saved->a, H, I, k,
-                                d.swiglu_alpha, d.swiglu_limit, lora_At, lora_dvu, dh, dw_part, s),
+                                d.swiglu_alpha, d.swiglu_limit, lora_At, lora_dvu, r, dh, dw_part,
+                                s),
          "bwd_down");
   if (r) {
     // dA_e[j, i] = sum_p w_p dv_u[p, j] a[p, i];  dB_e[h, j] = s sum_p w_p dY[t(p), h] v[p, j]
-    LAUNCH(mxmoe::launch_lora_grad(saved->a, false, I, saved->sorted_rows, k, lora_dvu,
+    LAUNCH(mxmoe::launch_lora_grad(saved->a, false, I, saved->sorted_rows, k, lora_dvu, r,
                                    saved->topk_w, 1.0f, saved->expert_offsets, E, dA,
                                    (int64_t)r * I, 1, I, s),
            "lora_grad");
-    LAUNCH(mxmoe::launch_lora_grad(dy, true, H, saved->sorted_rows, k, saved->lora_v,
+    LAUNCH(mxmoe::launch_lora_grad(dy, true, H, saved->sorted_rows, k, saved->lora_v, r,
                                    saved->topk_w, d.lora_scale, saved->expert_offsets, E, dB,
                                    (int64_t)H * r, r, 1, s),
            "lora_grad");

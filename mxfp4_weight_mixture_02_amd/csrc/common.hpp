@@ -111,6 +111,16 @@ __device__ __forceinline__ void swiglu_grad(float g, float u, float da, float al
   *du = (u >= -limit && u <= limit) ? duc : 0.0f;
 }
 
+// Global and LDS pointer types of the global -> LDS load builtin.
+typedef __attribute__((address_space(1))) const void* gptr_t;
+typedef __attribute__((address_space(3))) void* lptr_t;
+
+// 64 zero bytes in device memory: the source of the loads that fall past
+// the end of a contraction whose length is an odd multiple of 32 (the last
+// 64-deep step's upper half), so that both MFMA operands are exact zeros
+// there.  E2M1 code 0 is +0, and scale byte 0 is a finite 2^-127.
+static __device__ __attribute__((aligned(16))) const uint8_t g_zero64[64] = {};
+
 // s_waitcnt immediate: wait until at most vm vector-memory and lgkm LDS /
 // scalar-memory operations of this wave are outstanding (expcnt untouched).
 __device__ constexpr int waitcnt_imm(int vm, int lgkm) {
@@ -223,6 +233,29 @@ __device__ __forceinline__ bool xcd_work_item(const Tile* __restrict__ tiles,
 
 constexpr int MT = 128;      // routed rows per forward GEMM tile
 constexpr int BMT = 256;     // routed rows per backward GEMM tile
-constexpr int LORA_R = 16;   // supported LoRA rank: one 16-deep MFMA contraction
+// LoRA ranks: 8, 16, 32 or 64, contracted in 16-deep MFMA chunks (rank 8
+// zero-padded to one chunk).
+constexpr int LORA_RMAX = 64;
+__host__ __device__ constexpr bool lora_rank_ok(int r) {
+  return r == 8 || r == 16 || r == 32 || r == 64;
+}
+__host__ __device__ constexpr int lora_chunks(int r) { return (r + 15) / 16; }
+
+// The 8 rank values 16 j + 8 h .. + 7 of a bf16 row of rank r as one MFMA
+// operand fragment (zeros past r).
+__device__ __forceinline__ bf16x8 lora_frag(const uint16_t* row, int r, int j, int h) {
+  const int c = 16 * j + 8 * h;
+  return as_bf16x8(c < r ? *reinterpret_cast<const u32x4*>(row + c) : u32x4{0u, 0u, 0u, 0u});
+}
+
+// The same 8 values of an fp32 row, times s, as a hi + lo bf16 pair.
+__device__ __forceinline__ void lora_frag_split(const float* row, int r, int j, int h, float s,
+                                                bf16x8* hi, bf16x8* lo) {
+  const int c = 16 * j + 8 * h;
+  const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+  const f32x4 v0 = c < r ? *reinterpret_cast<const f32x4*>(row + c) : z;
+  const f32x4 v1 = c < r ? *reinterpret_cast<const f32x4*>(row + c + 4) : z;
+  split_bf16x8(v0, v1, s, hi, lo);
+}
 
 }  // namespace mxmoe

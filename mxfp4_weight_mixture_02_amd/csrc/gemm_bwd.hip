@@ -76,9 +76,6 @@ constexpr int GLDS_LOOP = GNST * GSTAGE;    // main loop (126 KB)
 constexpr int GDMA = 6;                     // LDS-DMA loads per wave per step
 static_assert(BMT == 256, "tile rows assumed below");
 
-typedef __attribute__((address_space(1))) const void* gptr_t;
-typedef __attribute__((address_space(3))) void* lptr_t;
-
 // Chunk swizzle of activation row p (16-byte chunks; distinct banks for the
 // 16-byte reads of 8 and of 16 consecutive rows).
 __device__ __forceinline__ int x_swz(int p) { return (p & 7) ^ ((p >> 3) & 1); }
@@ -98,8 +95,10 @@ struct GArgs {
   uint32_t aoff;            // code-tile offset of the transposing read (sub-step 0)
   uint32_t sofs;            // scale-table offset of the lane's 8 scale words (sub-step 0)
   uint32_t boff[4];         // activation-stage offsets of the B-fragment reads per sub-step (row block 0)
+  uint32_t tailmask;        // pieces past C in a half last step: 1 activations, 2 code, 4 scale
   int wave;                 // wave index (uniform)
-  int nsteps;
+  int nsteps;               // ceil(C / 64)
+  int half_last;            // C % 64 == 32: the last step holds 32 stored rows
 };
 
 // MFMA operand registers carried between sub-steps (and from one step to
@@ -163,19 +162,37 @@ __device__ __forceinline__ void g_setup(GArgs& g, const uint16_t* xbase, RowOff 
   const int prel = lane & 31;
 #pragma unroll
   for (int s = 0; s < 4; ++s) g.boff[s] = GCB + GSB + prel * 128 + 16 * ((2 * s + (lane >> 5)) ^ x_swz(prel));
-  g.nsteps = C / GKC;
+  g.nsteps = (C + GKC - 1) / GKC;
+  g.half_last = (C % GKC) != 0;
+  // in a half last step the activation slots of k >= 32 (chunk >= 4), the
+  // code rows >= 32 and the scale rows >= 32 lie past C
+  {
+    const int ch = (lane & 7) ^ ((lane >> 3) & 7);   // the chunk of all 4 of the lane's pieces
+    g.tailmask = (ch >= 4 ? 1u : 0u) | (c0 >= 32 ? 2u : 0u) | (((lane >> 3) & 3) >= 2 ? 4u : 0u);
+  }
 }
 
-// Step k's tile into LDS stage st (GDMA loads of this wave).
+// Step k's tile into LDS stage st (GDMA loads of this wave).  In a half
+// last step the pieces past C are read from a block of zeros.
 __device__ __forceinline__ void g_dma(const GArgs& g, uint8_t* __restrict__ st, int k) {
+  const uint16_t* xp[4];
+  const uint8_t* cp = g.wcode + (g.coff + (uint32_t)k * g.cstep);
+  const uint8_t* sp = g.wscale + (g.soff + (uint32_t)k * g.sstep);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) xp[i] = g.xbase + (g.xoff[i] + (uint32_t)(k * GKC));
+  if (g.half_last && k == g.nsteps - 1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (g.tailmask & 1u) xp[i] = reinterpret_cast<const uint16_t*>(g_zero64);
+    if (g.tailmask & 2u) cp = g_zero64;
+    if (g.tailmask & 4u) sp = g_zero64;
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    __builtin_amdgcn_global_load_lds((gptr_t)(g.xbase + (g.xoff[i] + (uint32_t)(k * GKC))),
-                                     (lptr_t)(st + GCB + GSB + (g.wave * 4 + i) * 1024), 16, 0, 0);
-  __builtin_amdgcn_global_load_lds((gptr_t)(g.wcode + (g.coff + (uint32_t)k * g.cstep)),
-                                   (lptr_t)(st + g.wave * 1024), 16, 0, 0);
-  __builtin_amdgcn_global_load_lds((gptr_t)(g.wscale + (g.soff + (uint32_t)k * g.sstep)),
-                                   (lptr_t)(st + GCB + g.wave * 256), 1, 0, 0);
+    __builtin_amdgcn_global_load_lds((gptr_t)xp[i], (lptr_t)(st + GCB + GSB + (g.wave * 4 + i) * 1024),
+                                     16, 0, 0);
+  __builtin_amdgcn_global_load_lds((gptr_t)cp, (lptr_t)(st + g.wave * 1024), 16, 0, 0);
+  __builtin_amdgcn_global_load_lds((gptr_t)sp, (lptr_t)(st + GCB + g.wave * 256), 1, 0, 0);
 }
 
 // LDS reads from stage st: the transposed code bytes and the 8 scale words
@@ -485,7 +502,7 @@ __device__ __forceinline__ void bwd_down_body(
     const float* __restrict__ topk_w, const int32_t* __restrict__ sorted_rows,
     const uint16_t* __restrict__ hsv, const uint16_t* __restrict__ asv, int I, float alpha,
     float limit, const uint16_t* __restrict__ lora_At, const float* __restrict__ lora_dvu,
-    uint16_t* __restrict__ dh, float* __restrict__ dw_part) {
+    int lora_r, uint16_t* __restrict__ dh, float* __restrict__ dw_part) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wo = wave & 3, wp = wave >> 2;
   const int l32 = lane & 31, hlf = lane >> 5;
@@ -495,21 +512,22 @@ __device__ __forceinline__ void bwd_down_body(
   g_loop<NRB>(g, lds, wp, acc);
   const int ow = o0 + 64 * wo;                // this wave's first column of I
   if (LORA && NRB > 0) {
+    for (int q = 0; q < lora_chunks(lora_r); ++q) {
 #pragma unroll
-    for (int j = 0; j < NRB; ++j) {
-      const int pb = wp + 2 * j;
-      const float* vp = lora_dvu + (int64_t)(tl.row0 + min(32 * pb + l32, tl.rows - 1)) * LORA_R + 8 * hlf;
-      bf16x8 vh, vl;
-      split_bf16x8(*reinterpret_cast<const f32x4*>(vp), *reinterpret_cast<const f32x4*>(vp + 4),
-                   1.0f, &vh, &vl);
+      for (int j = 0; j < NRB; ++j) {
+        const int pb = wp + 2 * j;
+        bf16x8 vh, vl;
+        lora_frag_split(lora_dvu + (int64_t)(tl.row0 + min(32 * pb + l32, tl.rows - 1)) * lora_r,
+                        lora_r, q, hlf, 1.0f, &vh, &vl);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        // fragment i's MFMA row l32 is column 2 l32 + i of the wave's 64
-        const int col = ow + 2 * l32 + i;
-        const bf16x8 aw = as_bf16x8(*reinterpret_cast<const u32x4*>(
-            lora_At + ((int64_t)e * I + (col < I ? col : 0)) * LORA_R + 8 * hlf));
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw, vh, acc[i][j], 0, 0, 0);
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw, vl, acc[i][j], 0, 0, 0);
+        for (int i = 0; i < 2; ++i) {
+          // fragment i's MFMA row l32 is column 2 l32 + i of the wave's 64
+          const int col = ow + 2 * l32 + i;
+          const bf16x8 aw =
+              lora_frag(lora_At + ((int64_t)e * I + (col < I ? col : 0)) * lora_r, lora_r, q, hlf);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw, vh, acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw, vl, acc[i][j], 0, 0, 0);
+        }
       }
     }
   }
@@ -603,7 +621,7 @@ __global__ __launch_bounds__(GTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
     const int32_t* __restrict__ sorted_rows, const Tile* __restrict__ tiles,
     const int32_t* __restrict__ num_tiles, const uint16_t* __restrict__ hsv,
     const uint16_t* __restrict__ asv, int H, int I, int k, float alpha, float limit,
-    const uint16_t* __restrict__ lora_At, const float* __restrict__ lora_dvu,
+    const uint16_t* __restrict__ lora_At, const float* __restrict__ lora_dvu, int lora_r,
     uint16_t* __restrict__ dh, float* __restrict__ dw_part) {
   // the epilogue's strips (8 x 12 KB) and dw reduction reuse the main loop's stages
   __shared__ __attribute__((aligned(16))) uint8_t lds[GLDS_LOOP];
@@ -625,7 +643,7 @@ __global__ __launch_bounds__(GTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
           I, o0);
 #define BWD_DOWN_BODY(N)                                                                       \
   bwd_down_body<LORA, N>(g, lds, tl, ot, otiles, o0, topk_w, sorted_rows, hsv, asv, I, alpha, \
-                         limit, lora_At, lora_dvu, dh, dw_part)
+                         limit, lora_At, lora_dvu, lora_r, dh, dw_part)
   switch (live_blocks(tl.rows, wp)) {
     case 0: BWD_DOWN_BODY(0); break;
     case 1: BWD_DOWN_BODY(1); break;
@@ -739,18 +757,18 @@ hipError_t launch_bwd_down(const uint16_t* dy, const uint8_t* codes, const uint8
                            const float* topk_w, const int32_t* sorted_rows, const Tile* tiles,
                            const int32_t* num_tiles, int max_tiles, const uint16_t* h,
                            const uint16_t* a, int H, int I, int k, float alpha, float limit,
-                           const uint16_t* lora_At, const float* lora_dvu, uint16_t* dh,
-                           float* dw_part, hipStream_t s) {
-  if (H % GKC || I % 64) return hipErrorInvalidValue;
+                           const uint16_t* lora_At, const float* lora_dvu, int lora_r,
+                           uint16_t* dh, float* dw_part, hipStream_t s) {
+  if (H % 32 || I % 32 || (lora_At && !lora_rank_ok(lora_r))) return hipErrorInvalidValue;
   dim3 grid(bwd_down_ntiles(I) * max_tiles);
   if (lora_At)
     hipLaunchKernelGGL(bwd_down_kernel<true>, grid, dim3(GTHR), 0, s, dy, codes, scales, topk_w,
                        sorted_rows, tiles, num_tiles, h, a, H, I, k, alpha, limit, lora_At,
-                       lora_dvu, dh, dw_part);
+                       lora_dvu, lora_r, dh, dw_part);
   else
     hipLaunchKernelGGL(bwd_down_kernel<false>, grid, dim3(GTHR), 0, s, dy, codes, scales, topk_w,
                        sorted_rows, tiles, num_tiles, h, a, H, I, k, alpha, limit, lora_At,
-                       lora_dvu, dh, dw_part);
+                       lora_dvu, 0, dh, dw_part);
   return hipGetLastError();
 }
 
@@ -758,7 +776,7 @@ hipError_t launch_bwd_gate_up(const uint16_t* dh, const uint8_t* codes, const ui
                               const int32_t* sorted_rows, const Tile* tiles,
                               const int32_t* num_tiles, int max_tiles, int H, int I,
                               uint16_t* dxr, hipStream_t s) {
-  if ((2 * I) % GKC || H % 64) return hipErrorInvalidValue;
+  if (I % 32 || H % 32) return hipErrorInvalidValue;
   dim3 grid(((H + GO - 1) / GO) * max_tiles);
   hipLaunchKernelGGL(bwd_gate_up_kernel, grid, dim3(GTHR), 0, s, dh, codes, scales, sorted_rows,
                      tiles, num_tiles, H, I, dxr);

@@ -30,24 +30,29 @@ struct DecChunk {
   u32x4 c[DD];
 };
 
-// Codes of chunk ch (steps DD*ch ..), clamped to the last step.
-__device__ __forceinline__ void dec_issue(DecChunk& b, const uint8_t* wrow, int ch, int nsteps) {
+// Codes of chunk ch (steps DD*ch ..), clamped to the last step.  ztail: the
+// lane's half of the last step lies past K (K an odd multiple of 32); its
+// codes then come from a block of zeros.
+__device__ __forceinline__ void dec_issue(DecChunk& b, const uint8_t* wrow, int ch, int nsteps,
+                                          bool ztail) {
 #pragma unroll
   for (int i = 0; i < DD; ++i) {
     const int c = min(ch * DD + i, nsteps - 1);
-    b.c[i] = *reinterpret_cast<const u32x4*>(wrow + c * 32);
+    const uint8_t* ptr = (ztail && c == nsteps - 1) ? g_zero64 : wrow + c * 32;
+    b.c[i] = *reinterpret_cast<const u32x4*>(ptr);
   }
 }
 
-// srow: this lane's row of the scale panel in LDS (+ lane half)
+// srow: this lane's row of the scale panel in LDS (+ lane half); smax: the
+// largest index it may read (K / 32 - 1 - lane half)
 __device__ __forceinline__ void dec_compute(const DecChunk& b, const uint16_t* xb,
-                                            const uint8_t* srow, int ch, int nsteps,
+                                            const uint8_t* srow, int smax, int ch, int nsteps,
                                             f32x16& acc) {
 #pragma unroll
   for (int i = 0; i < DD; ++i) {
     const int c = ch * DD + i;
     if (c < nsteps) {
-      const float sc = scale_operand(srow[2 * c]);
+      const float sc = scale_operand(srow[min(2 * c, smax)]);
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const bf16x8 a = as_bf16x8(dequant8_bf16(b.c[i][s], sc));
@@ -65,10 +70,12 @@ __global__ __launch_bounds__(512) void dec_kernel(
     const uint16_t* __restrict__ bias, const float* __restrict__ topk_w,
     const int32_t* __restrict__ sorted_rows, const Tile* __restrict__ tiles,
     const int32_t* __restrict__ num_tiles, int K, int N, int k, int DG, float alpha, float limit,
-    uint16_t* __restrict__ h_out, uint16_t* __restrict__ a_out, uint16_t* __restrict__ y_w) {
+    uint16_t* __restrict__ h_out, uint16_t* __restrict__ a_out, uint16_t* __restrict__ y_w,
+    const uint16_t* __restrict__ lora_B, const float* __restrict__ lora_v, float lora_scale,
+    int lora_r) {
   // LDS: the scale panel of the workgroup's weight rows [32 * wpb][K / 32]
   // (one contiguous span of the scale tensor, copied in 16-byte pieces), then
-  // the activation group [DG][K + DEC_XPAD] bf16
+  // the activation group [DG][Kp + DEC_XPAD] bf16 (K rounded up to 64, zeros past K)
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int wpb = blockDim.x >> 6;
   const int nblk = (N + 32 * wpb - 1) / (32 * wpb);
@@ -79,14 +86,17 @@ __global__ __launch_bounds__(512) void dec_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hlf = lane >> 5;
   const int e = tl.expert;
-  const int xrow = K + DEC_XPAD;
+  const int Kp = (K + 63) & ~63;               // K rounded up to whole 64-wide steps
+  const int xrow = Kp + DEC_XPAD;
   const int n0 = (rbk * wpb + wave) * 32;      // this wave's first weight row
   const bool live = n0 < N;                    // N % 32 == 0: a block is all in or out
   const int n = live ? n0 + l32 : l32;
   const uint8_t* wrow = codes + ((int64_t)e * N + n) * (K / 2) + hlf * 16;
-  const int nsteps = K / 64;
+  const int nsteps = Kp / 64;
+  const bool ztail = (K & 63) && hlf;          // this lane's half of the last step lies past K
+  const int smax = K / 32 - 1 - hlf;
   const int nch = (nsteps + DD - 1) / DD;
-  const int npieces = K / 8;
+  const int npieces = Kp / 8;                  // staged pieces per row; those past K are zeros
   uint8_t* panel = lds;
   uint16_t* xs = reinterpret_cast<uint16_t*>(lds + 32 * wpb * (K / 32));
   {
@@ -105,6 +115,7 @@ __global__ __launch_bounds__(512) void dec_kernel(
         ng * npieces, tid, blockDim.x,
         [&](int q) {
           const int p = q / npieces, col = (q % npieces) * 8;
+          if (col >= K) return u32x4{0u, 0u, 0u, 0u};
           const int rt = tl.row0 + g0 + p;
           const int64_t sr = GATE_UP ? (int64_t)(sorted_rows[rt] / k) : (int64_t)rt;
           return *reinterpret_cast<const u32x4*>(src + sr * K + col);
@@ -120,13 +131,26 @@ __global__ __launch_bounds__(512) void dec_kernel(
       // B-operand column l32 reads row min(l32 % DG, ng - 1)
       const uint16_t* xb = xs + min(l32 % DG, ng - 1) * xrow + 32 * hlf;
       DecChunk b0, b1;
-      dec_issue(b0, wrow, 0, nsteps);
+      dec_issue(b0, wrow, 0, nsteps, ztail);
       for (int ch = 0; ch < nch; ch += 2) {
-        dec_issue(b1, wrow, min(ch + 1, nch - 1), nsteps);
-        dec_compute(b0, xb, srow, ch, nsteps, acc);
+        dec_issue(b1, wrow, min(ch + 1, nch - 1), nsteps, ztail);
+        dec_compute(b0, xb, srow, smax, ch, nsteps, acc);
         if (ch + 1 >= nch) break;
-        dec_issue(b0, wrow, min(ch + 2, nch - 1), nsteps);
-        dec_compute(b1, xb, srow, ch + 1, nsteps, acc);
+        dec_issue(b0, wrow, min(ch + 2, nch - 1), nsteps, ztail);
+        dec_compute(b1, xb, srow, smax, ch + 1, nsteps, acc);
+      }
+      if (!GATE_UP && lora_B) {
+        // + s v B_e^T over the rank (as the down GEMM): A-operand = B_e row
+        // n, B-operand column l32 = the group row it repeats
+        const float* vrow = lora_v + (int64_t)(tl.row0 + g0 + min(l32 % DG, ng - 1)) * lora_r;
+        const uint16_t* brow = lora_B + ((int64_t)e * N + n) * lora_r;
+        for (int j = 0; j < lora_chunks(lora_r); ++j) {
+          bf16x8 vh, vl;
+          lora_frag_split(vrow, lora_r, j, hlf, lora_scale, &vh, &vl);
+          const bf16x8 bw = lora_frag(brow, lora_r, j, hlf);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bw, vh, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bw, vl, acc, 0, 0, 0);
+        }
       }
       // lane: column p = l32 of the group, weight rows nb + i (registers 4q + i)
       const int p = g0 + l32;
@@ -179,8 +203,9 @@ __global__ __launch_bounds__(64 * KW) void dec_ksplit_kernel(
     const float* __restrict__ topk_w, const int32_t* __restrict__ sorted_rows,
     const Tile* __restrict__ tiles, const int32_t* __restrict__ num_tiles, int K, int N, int k,
     int DG, float alpha, float limit, uint16_t* __restrict__ h_out, uint16_t* __restrict__ a_out,
-    uint16_t* __restrict__ y_w) {
-  // LDS: scale panel [32][K / 32], then the activation group [DG][K + DEC_XPAD]
+    uint16_t* __restrict__ y_w, const uint16_t* __restrict__ lora_B,
+    const float* __restrict__ lora_v, float lora_scale, int lora_r) {
+  // LDS: scale panel [32][K / 32], then the activation group [DG][Kp + DEC_XPAD]
   // bf16, which the partial sums [KW][16][64] fp32 reuse after the MFMAs
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int nrb = N / 32;
@@ -191,12 +216,15 @@ __global__ __launch_bounds__(64 * KW) void dec_ksplit_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hlf = lane >> 5;
   const int e = tl.expert;
-  const int xrow = K + DEC_XPAD;
+  const int Kp = (K + 63) & ~63;               // K rounded up to whole 64-wide steps
+  const int xrow = Kp + DEC_XPAD;
   uint8_t* panel = lds;
   uint16_t* xs = reinterpret_cast<uint16_t*>(lds + K);   // the panel is 32 x K/32 = K bytes
   float* red = reinterpret_cast<float*>(xs);
 
-  const int nsteps = K / 64;
+  const int nsteps = Kp / 64;
+  const bool ztail = (K & 63) && hlf;          // this lane's half of the last step lies past K
+  const int smax = K / 32 - 1 - hlf;
   const int per = (nsteps + KW - 1) / KW;
   const int c0 = min(wave * per, nsteps), cnt = min(per, nsteps - c0);
   const int n = rb * 32 + l32;
@@ -205,7 +233,8 @@ __global__ __launch_bounds__(64 * KW) void dec_ksplit_kernel(
 #pragma unroll
   for (int i = 0; i < KSTEPS; ++i) {
     const int c = c0 + min(i, cnt - 1);               // clamped: never past the row
-    cv[i] = *reinterpret_cast<const u32x4*>(wrow + c * 32);
+    const uint8_t* ptr = (ztail && c == nsteps - 1) ? g_zero64 : wrow + c * 32;
+    cv[i] = *reinterpret_cast<const u32x4*>(ptr);
   }
   {
     const u32x4* ps = reinterpret_cast<const u32x4*>(scales + ((int64_t)e * N + rb * 32) * (K / 32));
@@ -213,7 +242,7 @@ __global__ __launch_bounds__(64 * KW) void dec_ksplit_kernel(
                  [&](int q, u32x4 v) { reinterpret_cast<u32x4*>(panel)[q] = v; });
   }
   const uint8_t* srow = panel + l32 * (K / 32) + hlf;
-  const int npieces = K / 8;
+  const int npieces = Kp / 8;                  // staged pieces per row; those past K are zeros
 
   for (int g0 = 0; g0 < tl.rows; g0 += DG) {
     const int ng = min(DG, tl.rows - g0);
@@ -221,6 +250,7 @@ __global__ __launch_bounds__(64 * KW) void dec_ksplit_kernel(
         ng * npieces, tid, 64 * KW,
         [&](int q) {
           const int p = q / npieces, col = (q % npieces) * 8;
+          if (col >= K) return u32x4{0u, 0u, 0u, 0u};
           const int rt = tl.row0 + g0 + p;
           const int64_t sr = GATE_UP ? (int64_t)(sorted_rows[rt] / k) : (int64_t)rt;
           return *reinterpret_cast<const u32x4*>(src + sr * K + col);
@@ -237,13 +267,25 @@ __global__ __launch_bounds__(64 * KW) void dec_ksplit_kernel(
     for (int i = 0; i < KSTEPS; ++i) {
       if (i < cnt) {
         const int c = c0 + i;
-        const float sc = scale_operand(srow[2 * c]);
+        const float sc = scale_operand(srow[min(2 * c, smax)]);
 #pragma unroll
         for (int s4 = 0; s4 < 4; ++s4) {
           const bf16x8 a = as_bf16x8(dequant8_bf16(cv[i][s4], sc));
           const bf16x8 b = *reinterpret_cast<const bf16x8*>(xb + 64 * c + 8 * s4);
           acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
         }
+      }
+    }
+    if (!GATE_UP && lora_B && wave == 0) {
+      // + s v B_e^T over the rank, added to one wave's partial sum
+      const float* vrow = lora_v + (int64_t)(tl.row0 + g0 + min(l32 % DG, ng - 1)) * lora_r;
+      const uint16_t* brow = lora_B + ((int64_t)e * N + n) * lora_r;
+      for (int j = 0; j < lora_chunks(lora_r); ++j) {
+        bf16x8 vh, vl;
+        lora_frag_split(vrow, lora_r, j, hlf, lora_scale, &vh, &vl);
+        const bf16x8 bw = lora_frag(brow, lora_r, j, hlf);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bw, vh, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bw, vl, acc, 0, 0, 0);
       }
     }
     __syncthreads();   // every wave is done reading xs
@@ -298,12 +340,15 @@ static hipError_t dec_launch_stream(int64_t R, int max_tiles, int K, int N, hipS
                              const uint16_t* bias, const float* topk_w,
                              const int32_t* sorted_rows, const Tile* tiles,
                              const int32_t* num_tiles, int k, float alpha, float limit,
-                             uint16_t* h_out, uint16_t* a_out, uint16_t* y_w) {
-  if (K % 64 || K > DEC_MAXK || N % 32) return hipErrorInvalidValue;
+                             uint16_t* h_out, uint16_t* a_out, uint16_t* y_w,
+                             const uint16_t* lora_B, const float* lora_v, float lora_scale,
+                             int lora_r) {
+  if (K % 32 || K > DEC_MAXK || N % 32) return hipErrorInvalidValue;
+  const int Kp = (K + 63) & ~63;
   const int wpb = R <= 64 ? 4 : 8;
   const int dg = R <= 64 ? (int)(R < 8 ? R : 8) : 16;   // an expert owns at most R rows
   const int nblk = (N + 32 * wpb - 1) / (32 * wpb);
-  const size_t lds = (size_t)32 * wpb * (K / 32) + (size_t)dg * (K + DEC_XPAD) * 2;
+  const size_t lds = (size_t)32 * wpb * (K / 32) + (size_t)dg * (Kp + DEC_XPAD) * 2;
   // dynamic LDS above 64 KB (16 staged rows) must be allowed explicitly
   static bool lds_attr_set = false;
   if (!lds_attr_set) {
@@ -315,7 +360,7 @@ static hipError_t dec_launch_stream(int64_t R, int max_tiles, int K, int N, hipS
   }
   const dim3 grid(max_tiles * nblk), block(64 * wpb);
 #define DEC_ARGS src, codes, scales, bias, topk_w, sorted_rows, tiles, num_tiles, K, N, k, dg, \
-                 alpha, limit, h_out, a_out, y_w
+                 alpha, limit, h_out, a_out, y_w, lora_B, lora_v, lora_scale, lora_r
   hipLaunchKernelGGL((dec_kernel<GATE_UP>), grid, block, lds, s, DEC_ARGS);
 #undef DEC_ARGS
   return hipGetLastError();
@@ -327,20 +372,24 @@ static hipError_t dec_launch(int64_t R, int max_tiles, int K, int N, hipStream_t
                              const uint16_t* bias, const float* topk_w,
                              const int32_t* sorted_rows, const Tile* tiles,
                              const int32_t* num_tiles, int k, float alpha, float limit,
-                             uint16_t* h_out, uint16_t* a_out, uint16_t* y_w) {
-  if (K % 64 || K > DEC_MAXK || N % 32) return hipErrorInvalidValue;
+                             uint16_t* h_out, uint16_t* a_out, uint16_t* y_w,
+                             const uint16_t* lora_B, const float* lora_v, float lora_scale,
+                             int lora_r) {
+  if (K % 32 || K > DEC_MAXK || N % 32 || (lora_B && !lora_rank_ok(lora_r)))
+    return hipErrorInvalidValue;
   if (R <= 16) {
     const int dg = (int)(R < 8 ? R : 8);
-    const size_t xb = (size_t)dg * (K + DEC_XPAD) * 2, rb = (size_t)KW * 16 * 64 * 4;
+    const int Kp = (K + 63) & ~63;
+    const size_t xb = (size_t)dg * (Kp + DEC_XPAD) * 2, rb = (size_t)KW * 16 * 64 * 4;
     hipLaunchKernelGGL(dec_ksplit_kernel<GATE_UP>, dim3(max_tiles * (N / 32)), dim3(64 * KW),
                        (size_t)K + (xb > rb ? xb : rb), s, src, codes, scales, bias, topk_w,
                        sorted_rows, tiles, num_tiles, K, N, k, dg, alpha, limit, h_out, a_out,
-                       y_w);
+                       y_w, lora_B, lora_v, lora_scale, lora_r);
     return hipGetLastError();
   }
   return dec_launch_stream<GATE_UP>(R, max_tiles, K, N, s, src, codes, scales, bias, topk_w,
                                     sorted_rows, tiles, num_tiles, k, alpha, limit, h_out, a_out,
-                                    y_w);
+                                    y_w, lora_B, lora_v, lora_scale, lora_r);
 }
 
 hipError_t launch_dec_gate_up(const uint16_t* x, const uint8_t* codes, const uint8_t* scales,
@@ -349,15 +398,18 @@ hipError_t launch_dec_gate_up(const uint16_t* x, const uint8_t* codes, const uin
                               float alpha, float limit, uint16_t* h_out, uint16_t* a_out,
                               hipStream_t s) {
   return dec_launch<true>(R, max_tiles, H, 2 * I, s, x, codes, scales, bias, nullptr, sorted_rows,
-                          tiles, num_tiles, k, alpha, limit, h_out, a_out, nullptr);
+                          tiles, num_tiles, k, alpha, limit, h_out, a_out, nullptr, nullptr,
+                          nullptr, 0.0f, 0);
 }
 
 hipError_t launch_dec_down(const uint16_t* a, const uint8_t* codes, const uint8_t* scales,
                            const uint16_t* bias, const float* topk_w, const int32_t* sorted_rows,
                            const Tile* tiles, const int32_t* num_tiles, int max_tiles, int64_t R,
-                           int H, int I, uint16_t* y_w, hipStream_t s) {
+                           int H, int I, const uint16_t* lora_B, const float* lora_v,
+                           float lora_scale, int lora_r, uint16_t* y_w, hipStream_t s) {
   return dec_launch<false>(R, max_tiles, I, H, s, a, codes, scales, bias, topk_w, sorted_rows,
-                           tiles, num_tiles, 1, 0.0f, 0.0f, nullptr, nullptr, y_w);
+                           tiles, num_tiles, 1, 0.0f, 0.0f, nullptr, nullptr, y_w, lora_B, lora_v,
+                           lora_scale, lora_r);
 }
 
 }  // namespace mxmoe

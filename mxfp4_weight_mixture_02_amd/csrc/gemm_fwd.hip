@@ -86,25 +86,43 @@ struct FwdPipe {
   uint32_t wp[FRB];                // byte offsets of this lane's codes per row block (+ lane half)
   const uint8_t* srow[FRB];        // its scale panel rows in LDS
   uint8_t* xs;                     // LDS stages
-  int nsteps;
+  int nsteps;                      // ceil(K / 64)
+  int kb32;                        // K / 32: scale bytes per weight row
+  int tail;                        // K % 64 == 32: the last step's upper 32 K lie past K
+  uint32_t tmask;                  // pieces past K in that step: bit j activation chunk j, bit 8 codes
 };
 
 // Loads of step c into stage/slot SL: activations global -> LDS directly,
 // codes into registers.
 // (codes: u32x4 [NST][FRB], taken as a deduced type)
+// In the half last step of a K that is an odd multiple of 32, the pieces
+// past K are read from a block of zeros (both MFMA operands exactly 0).
 template <int W, int SL, class Codes>
 __device__ __forceinline__ void fwd_issue(const FwdPipe& p, Codes& codes, int c) {
   constexpr int XCH = FwdShape<W>::XCH;
   const int wave = threadIdx.x >> 6;
+  const uint16_t* xp[XCH];
+  const uint8_t* wp[FRB];
+#pragma unroll
+  for (int j = 0; j < XCH; ++j) xp[j] = p.xbase + (p.xrow[j] + (uint32_t)(c * FKS + p.xcol[j]));
+#pragma unroll
+  for (int rb = 0; rb < FRB; ++rb) wp[rb] = p.wbase + (p.wp[rb] + (uint32_t)c * 32);
+  if (p.tail && c == p.nsteps - 1) {
+#pragma unroll
+    for (int j = 0; j < XCH; ++j)
+      if (p.tmask & (1u << j)) xp[j] = reinterpret_cast<const uint16_t*>(g_zero64);
+#pragma unroll
+    for (int rb = 0; rb < FRB; ++rb)
+      if (p.tmask & 256u) wp[rb] = g_zero64;
+  }
 #pragma unroll
   for (int j = 0; j < XCH; ++j)
-    __builtin_amdgcn_global_load_lds(p.xbase + (p.xrow[j] + (uint32_t)(c * FKS + p.xcol[j])),
-                                     p.xs + SL * XSTAGE + (XCH * wave + j) * 1024, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((gptr_t)xp[j], (lptr_t)(p.xs + SL * XSTAGE + (XCH * wave + j) * 1024),
+                                     16, 0, 0);
   // the counted waits below assume this issue order: activations, then codes
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int rb = 0; rb < FRB; ++rb)
-    codes[SL][rb] = *reinterpret_cast<const u32x4*>(p.wbase + (p.wp[rb] + (uint32_t)c * 32));
+  for (int rb = 0; rb < FRB; ++rb) codes[SL][rb] = *reinterpret_cast<const u32x4*>(wp[rb]);
 }
 
 template <int W, int SL, int NRB, class Codes>
@@ -138,7 +156,7 @@ __device__ __forceinline__ void fwd_compute(const FwdPipe& p, const Codes& codes
     if (s == 1) {
       const int cn = min(c + 1, p.nsteps - 1);
 #pragma unroll
-      for (int rb = 0; rb < FRB; ++rb) scn[rb] = p.srow[rb][2 * cn + hlf];
+      for (int rb = 0; rb < FRB; ++rb) scn[rb] = p.srow[rb][min(2 * cn + hlf, p.kb32 - 1)];
     }
 #pragma unroll
     for (int rb = 0; rb < FRB; ++rb)
@@ -213,7 +231,7 @@ __device__ __forceinline__ void fwd_loop(const FwdPipe& p, f32x16 (&acc)[FRB][4]
   const int hlf = (threadIdx.x & 63) >> 5;
   float sc[FRB];
 #pragma unroll
-  for (int rb = 0; rb < FRB; ++rb) sc[rb] = scale_operand(p.srow[rb][hlf]);
+  for (int rb = 0; rb < FRB; ++rb) sc[rb] = scale_operand(p.srow[rb][min(hlf, p.kb32 - 1)]);
   int c = 0;
   for (; c + NST <= p.nsteps; c += NST) {
     fwd_step<W, 0, NRB>(p, codes, c + 0, sc, acc);
@@ -263,11 +281,14 @@ __device__ __forceinline__ void fwd_body(const uint16_t* xbase, const uint32_t* 
 
   static_assert(XCH <= XCH_MAX, "activation chunks per wave");
   FwdPipe p;
+  p.tmask = hlf ? 256u : 0u;
 #pragma unroll
   for (int j = 0; j < XCH; ++j) {
     const int row = (XCH * wave + j) * 8 + lane / 8;   // row of the tile this lane stages
+    const int blk = (lane & 7) ^ ((row >> 1) & 7);     // global column block of its slot
     p.xrow[j] = xrow[j];
-    p.xcol[j] = 8 * ((lane & 7) ^ ((row >> 1) & 7));   // global column block of its slot
+    p.xcol[j] = 8 * blk;
+    if (blk >= 4) p.tmask |= 1u << j;
   }
   const int64_t rowbytes = K / 2;
   // row blocks past the workgroup's rows (the last column tile can hold
@@ -281,7 +302,9 @@ __device__ __forceinline__ void fwd_body(const uint16_t* xbase, const uint32_t* 
   p.xbase = xbase;
   p.wbase = codes_e;
   p.xs = lds;
-  p.nsteps = K / FKS;
+  p.nsteps = (K + FKS - 1) / FKS;
+  p.kb32 = KB32;
+  p.tail = (K % FKS) != 0;
   switch (nrb) {
     case 1: fwd_loop<W, 1>(p, acc); break;
     case 2: fwd_loop<W, 2>(p, acc); break;
@@ -294,13 +317,14 @@ __device__ __forceinline__ void fwd_body(const uint16_t* xbase, const uint32_t* 
 // base: four consecutive bf16 per (rb, q), one 8-byte load each (base is a
 // multiple of 4 elements and the bias 16-byte aligned); zeros without bias.
 __device__ __forceinline__ void load_bias_rows(const uint16_t* __restrict__ bias, int64_t base,
-                                               float (&bv)[FRB][4][4]) {
+                                               int nblk, float (&bv)[FRB][4][4]) {
   u32x2 raw[FRB][4];
 #pragma unroll
   for (int rb = 0; rb < FRB; ++rb)
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      raw[rb][q] = bias ? *reinterpret_cast<const u32x2*>(bias + base + rb * 32 + 8 * q) : u32x2{0u, 0u};
+      raw[rb][q] = (bias && rb < nblk) ? *reinterpret_cast<const u32x2*>(bias + base + rb * 32 + 8 * q)
+                                       : u32x2{0u, 0u};
 #pragma unroll
   for (int rb = 0; rb < FRB; ++rb)
 #pragma unroll
@@ -351,7 +375,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   uint8_t* hst = lds + wave * 6144;           // h strip: 32 rows x 64 bf16 (128-byte rows)
   uint8_t* ast = hst + 4096;                  // a strip: 32 rows x 32 bf16 (64-byte rows)
   float bv[FRB][4][4];
-  load_bias_rows(bias, (int64_t)e * N + n0 + wcol + 4 * hlf, bv);
+  load_bias_rows(bias, (int64_t)e * N + n0 + wcol + 4 * hlf, FRB, bv);
 #pragma unroll
   for (int tb = 0; tb < 4; ++tb) {
     if (tb * 32 >= tl.rows) break;
@@ -395,7 +419,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   }
 }
 
-// LORA: add the rank-16 delta s (v B_e^T) (a template parameter: a runtime
+// LORA: add the rank-r delta s (v B_e^T) (a template parameter: a runtime
 // branch around these MFMAs makes the compiler spill accumulators inside
 // the main loop).
 template <bool LORA>
@@ -405,7 +429,7 @@ __global__ __launch_bounds__(FwdShape<8>::NTHR) void down_kernel(
     const float* __restrict__ topk_w, const int32_t* __restrict__ sorted_rows,
     const Tile* __restrict__ tiles, const int32_t* __restrict__ num_tiles, int H, int I,
     const uint16_t* __restrict__ lora_B, const float* __restrict__ lora_v, float lora_scale,
-    uint16_t* __restrict__ y_w) {
+    int lora_r, uint16_t* __restrict__ y_w) {
   using S = FwdShape<8>;
   constexpr int XCHUNKS = S::XCH, FNT = S::NT;
   __shared__ __attribute__((aligned(16))) uint8_t lds[S::LDS];
@@ -430,31 +454,33 @@ __global__ __launch_bounds__(FwdShape<8>::NTHR) void down_kernel(
   fwd_body<8>(a + (int64_t)tl.row0 * I, xrow, codes + (int64_t)e * N * (I / 2), scales + (int64_t)e * N * (I / 32), I, n0,
            nrows, wrow_local, (tl.rows + 31) / 32, lds, acc);
   if (LORA) {
-    // + s v B_e^T: one more 16-deep contraction over the rank, A-operand =
-    // B_e rows (this lane's weight rows), B-operand = s v as hi + lo bf16;
-    // one token block at a time to keep few registers live
+    // + s v B_e^T: 16-deep contractions over the rank, A-operand = B_e rows
+    // (this lane's weight rows), B-operand = s v as hi + lo bf16; one token
+    // block at a time to keep few registers live
+    for (int j = 0; j < lora_chunks(lora_r); ++j) {
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-      const float* vp = lora_v + (int64_t)(tl.row0 + min(tb * 32 + l32, tl.rows - 1)) * LORA_R + 8 * hlf;
-      bf16x8 vh, vl;
-      split_bf16x8(*reinterpret_cast<const f32x4*>(vp), *reinterpret_cast<const f32x4*>(vp + 4),
-                   lora_scale, &vh, &vl);
+      for (int tb = 0; tb < 4; ++tb) {
+        bf16x8 vh, vl;
+        lora_frag_split(lora_v + (int64_t)(tl.row0 + min(tb * 32 + l32, tl.rows - 1)) * lora_r,
+                        lora_r, j, hlf, lora_scale, &vh, &vl);
 #pragma unroll
-      for (int rb = 0; rb < FRB; ++rb) {
-        const int r = min(wrow_local + 32 * rb, nrows - 1);
-        const bf16x8 bw = as_bf16x8(*reinterpret_cast<const u32x4*>(
-            lora_B + ((int64_t)e * N + n0 + r) * LORA_R + 8 * hlf));
-        acc[rb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bw, vh, acc[rb][tb], 0, 0, 0);
-        acc[rb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bw, vl, acc[rb][tb], 0, 0, 0);
+        for (int rb = 0; rb < FRB; ++rb) {
+          const int r = min(wrow_local + 32 * rb, nrows - 1);
+          const bf16x8 bw = lora_frag(lora_B + ((int64_t)e * N + n0 + r) * lora_r, lora_r, j, hlf);
+          acc[rb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bw, vh, acc[rb][tb], 0, 0, 0);
+          acc[rb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bw, vl, acc[rb][tb], 0, 0, 0);
+        }
       }
     }
   }
   barrier_only();   // as in gate_up: LDS is free for the epilogue
   const int wcol = wave * 32 * FRB;
   if (n0 + wcol >= N) return;
+  // N % 32 == 0: the wave's second 32-row block may lie past N
+  const int nblk = min(FRB, (N - n0 - wcol) / 32);
   uint8_t* yst = lds + wave * 4096;           // y strip: 32 rows x 64 bf16 (128-byte rows)
   float bv[FRB][4][4];
-  load_bias_rows(bias, (int64_t)e * N + n0 + wcol + 4 * hlf, bv);
+  load_bias_rows(bias, (int64_t)e * N + n0 + wcol + 4 * hlf, nblk, bv);
 #pragma unroll
   for (int tb = 0; tb < 4; ++tb) {
     if (tb * 32 >= tl.rows) break;
@@ -477,7 +503,8 @@ __global__ __launch_bounds__(FwdShape<8>::NTHR) void down_kernel(
       const int rt = tb * 32 + r;
       const int64_t fr = __shfl(f, r);
       const u32x4 v = *reinterpret_cast<const u32x4*>(yst + stg_off<128>(r, c));
-      if (rt < tl.rows) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(y_w + fr * N + n0 + wcol + 8 * c));
+      if (rt < tl.rows && 8 * c < 32 * nblk)
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(y_w + fr * N + n0 + wcol + 8 * c));
     }
     wave_lds_sync();
   }
@@ -511,7 +538,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
 }
 
 // K step of the forward GEMMs for a contraction length K (0: unsupported).
-int fwd_step_k(int K) { return (K % FKS == 0 && K <= FwdShape<8>::MAXK) ? FKS : 0; }
+int fwd_step_k(int K) { return (K % 32 == 0 && K <= FwdShape<8>::MAXK) ? FKS : 0; }
 
 hipError_t launch_gate_up(const uint16_t* x, const uint8_t* codes, const uint8_t* scales,
                           const uint16_t* bias, const int32_t* sorted_rows, const Tile* tiles,
@@ -536,17 +563,18 @@ hipError_t launch_gate_up(const uint16_t* x, const uint8_t* codes, const uint8_t
 hipError_t launch_down(const uint16_t* a, const uint8_t* codes, const uint8_t* scales,
                        const uint16_t* bias, const float* topk_w, const int32_t* sorted_rows,
                        const Tile* tiles, const int32_t* num_tiles, int max_tiles, int H, int I,
-                       const uint16_t* lora_B, const float* lora_v, float lora_scale,
+                       const uint16_t* lora_B, const float* lora_v, float lora_scale, int lora_r,
                        uint16_t* y_w, hipStream_t s) {
-  if (!fwd_step_k(I)) return hipErrorInvalidValue;
+  if (!fwd_step_k(I) || (lora_B && !lora_rank_ok(lora_r))) return hipErrorInvalidValue;
   using S = FwdShape<8>;
   dim3 grid(((H + S::NT - 1) / S::NT) * max_tiles), block(S::NTHR);
   if (lora_B)
     hipLaunchKernelGGL(down_kernel<true>, grid, block, 0, s, a, codes, scales, bias, topk_w,
-                       sorted_rows, tiles, num_tiles, H, I, lora_B, lora_v, lora_scale, y_w);
+                       sorted_rows, tiles, num_tiles, H, I, lora_B, lora_v, lora_scale, lora_r,
+                       y_w);
   else
     hipLaunchKernelGGL(down_kernel<false>, grid, block, 0, s, a, codes, scales, bias, topk_w,
-                       sorted_rows, tiles, num_tiles, H, I, lora_B, lora_v, lora_scale, y_w);
+                       sorted_rows, tiles, num_tiles, H, I, lora_B, lora_v, lora_scale, 0, y_w);
   return hipGetLastError();
 }
 

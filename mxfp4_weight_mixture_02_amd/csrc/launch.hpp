@@ -53,12 +53,12 @@ hipError_t launch_gate_up(const uint16_t* x, const uint8_t* codes, const uint8_t
                           const int32_t* num_tiles, int max_tiles, int H, int I, int k,
                           float alpha, float limit, uint16_t* h_out, uint16_t* a_out,
                           hipStream_t s);
-// lora_B/lora_v/lora_scale: the rank-16 delta s (v B_e^T) added before the
-// bias (lora_B == nullptr: none).
+// lora_B/lora_v/lora_scale/lora_r: the rank-r delta s (v B_e^T) added
+// before the bias (lora_B == nullptr: none).
 hipError_t launch_down(const uint16_t* a, const uint8_t* codes, const uint8_t* scales,
                        const uint16_t* bias, const float* topk_w, const int32_t* sorted_rows,
                        const Tile* tiles, const int32_t* num_tiles, int max_tiles, int H, int I,
-                       const uint16_t* lora_B, const float* lora_v, float lora_scale,
+                       const uint16_t* lora_B, const float* lora_v, float lora_scale, int lora_r,
                        uint16_t* y_w, hipStream_t s);
 hipError_t launch_combine(const uint16_t* y_w, int64_t T, int H, int k, uint16_t* out,
                           hipStream_t s);
@@ -70,11 +70,12 @@ hipError_t launch_dec_gate_up(const uint16_t* x, const uint8_t* codes, const uin
                               const int32_t* num_tiles, int max_tiles, int64_t R, int H, int I, int k,
                               float alpha, float limit, uint16_t* h_out, uint16_t* a_out,
                               hipStream_t s);
+// with lora_B: + the rank-r delta s (v B_e^T), as launch_down
 hipError_t launch_dec_down(const uint16_t* a, const uint8_t* codes, const uint8_t* scales,
                            const uint16_t* bias, const float* topk_w, const int32_t* sorted_rows,
                            const Tile* tiles, const int32_t* num_tiles, int max_tiles, int64_t R,
-                           int H, int I,
-                           uint16_t* y_w, hipStream_t s);
+                           int H, int I, const uint16_t* lora_B, const float* lora_v,
+                           float lora_scale, int lora_r, uint16_t* y_w, hipStream_t s);
 
 // gemm_bwd.hip
 int bwd_down_ntiles(int I);
@@ -82,8 +83,8 @@ hipError_t launch_bwd_down(const uint16_t* dy, const uint8_t* codes, const uint8
                            const float* topk_w, const int32_t* sorted_rows, const Tile* tiles,
                            const int32_t* num_tiles, int max_tiles, const uint16_t* h,
                            const uint16_t* a, int H, int I, int k, float alpha, float limit,
-                           const uint16_t* lora_At, const float* lora_dvu, uint16_t* dh,
-                           float* dw_part, hipStream_t s);
+                           const uint16_t* lora_At, const float* lora_dvu, int lora_r,
+                           uint16_t* dh, float* dw_part, hipStream_t s);
 hipError_t launch_bwd_gate_up(const uint16_t* dh, const uint8_t* codes, const uint8_t* scales,
                               const int32_t* sorted_rows, const Tile* tiles,
                               const int32_t* num_tiles, int max_tiles, int H, int I,
@@ -94,13 +95,16 @@ hipError_t launch_bwd_combine(const uint16_t* dy, const uint16_t* dxr, const flo
                               int k, uint16_t* dx, hipStream_t s);
 
 // lora.hip
+// out [R, r] fp32 = scale * src rows . M_e rows (M: [E, r, C] bf16)
 hipError_t launch_lora_proj(const uint16_t* src, bool gather, const int32_t* sorted_rows, int k,
-                            const uint16_t* M, int C, const Tile* tiles, const int32_t* num_tiles,
-                            int max_tiles, float scale, float* out, hipStream_t s);
+                            const uint16_t* M, int C, int r, const Tile* tiles,
+                            const int32_t* num_tiles, int max_tiles, float scale, float* out,
+                            hipStream_t s);
 hipError_t launch_transpose_bf16(const uint16_t* in, int64_t batches, int R1, int R2,
                                  uint16_t* out, hipStream_t s);
+// P: [R, r] fp32
 hipError_t launch_lora_grad(const uint16_t* Q, bool gather, int C, const int32_t* sorted_rows,
-                            int k, const float* P, const float* topk_w, float scale,
+                            int k, const float* P, int r, const float* topk_w, float scale,
                             const int32_t* offsets, int E, float* out, int64_t e_stride,
                             int c_stride, int j_stride, hipStream_t s);
 

@@ -52,8 +52,9 @@ def _err(L):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(T=0), -1), (dict(k=0), -1), (dict(E=0), -1),
-    (dict(H=96), -2), (dict(I=48), -2), (dict(E=300, k=2), -2),
+    (dict(H=80), -2), (dict(I=48), -2), (dict(E=300, k=2), -2),
     (dict(k=5, E=4), -2), (dict(k=9, E=16), -2), (dict(lora_rank=7), -2),
+    (dict(lora_rank=24), -2), (dict(lora_rank=128), -2), (dict(H=5152), -2),
     (dict(T=2 ** 29, k=4, E=8), -2),
 ])
 def test_workspace_query_rejects_bad_dims(L, kw, code):
@@ -90,7 +91,7 @@ def test_saved_bytes_validation(L):
     z = SavedSizes()
     z.h = 12345
     assert L.mxfp4_moe_saved_bytes(ctypes.byref(_dims(T=0)), ctypes.byref(z)) == -1
-    assert L.mxfp4_moe_saved_bytes(ctypes.byref(_dims(H=96)), ctypes.byref(z)) == -2
+    assert L.mxfp4_moe_saved_bytes(ctypes.byref(_dims(H=80)), ctypes.byref(z)) == -2
     assert z.h == 12345 and _err(L)                      # untouched on error
     assert L.mxfp4_moe_saved_bytes(ctypes.byref(_dims()), None) == -1
     assert L.mxfp4_moe_saved_bytes(ctypes.byref(_dims()), ctypes.byref(z)) == 0 and _err(L) == ""
@@ -181,8 +182,9 @@ def test_lora_validation(L):
     d0 = _dims()
     assert f0 > L.mxfp4_moe_workspace_bytes(ctypes.byref(d0), 0)
     assert b > L.mxfp4_moe_workspace_bytes(ctypes.byref(d0), 2)
-    for r in (8, 32):
-        assert L.mxfp4_moe_workspace_bytes(ctypes.byref(_dims(lora_rank=r)), 0) == 0
+    # ranks 8, 32 and 64 too, with workspace growing in the rank
+    sizes = [L.mxfp4_moe_workspace_bytes(ctypes.byref(_dims(lora_rank=r)), 2) for r in (8, 16, 32, 64)]
+    assert all(b > 0 for b in sizes) and sizes == sorted(sizes) and len(set(sizes)) == 4
     nan = _dims(lora_rank=16, lora_scale=float("nan"))
     assert L.mxfp4_moe_workspace_bytes(ctypes.byref(nan), 0) == 0
     # adapters missing / given without a rank / misaligned
@@ -207,3 +209,13 @@ def test_lora_validation(L):
     rc = L.mxfp4_moe_backward_dx(ctypes.byref(d), ctypes.byref(w), ctypes.byref(sv), FAKE, FAKE,
                                  None, FAKE, FAKE, b, None)
     assert rc == -1 and "dA and dB" in _err(L)
+
+
+@pytest.mark.parametrize("H,I", [(96, 160), (32, 32), (2912, 2880), (5120, 4000)])
+def test_odd_multiples_of_32_are_accepted(L, H, I):
+    # H and I need only whole 32-element scale blocks, not whole 64-wide K steps
+    d = _dims(H=H, I=I)
+    for mode in (0, 1, 2):
+        assert L.mxfp4_moe_workspace_bytes(ctypes.byref(d), mode) > 0, _err(L)
+    z = SavedSizes()
+    assert L.mxfp4_moe_saved_bytes(ctypes.byref(d), ctypes.byref(z)) == 0

@@ -233,6 +233,36 @@ def test_lora_empty_expert_gets_zero_gradients():
     _run_layer(s, lora_scale=4.0)
 
 
+@pytest.mark.parametrize("T,H,I", [
+    (300, 96, 160),    # both odd multiples of 32, several row tiles: the GEMMs' half last K step
+    (300, 2912, 224),  # 46 steps of 64 in gate_up and bwd_down, a half 46th; down N = 2912
+    (300, 32, 32),     # a single half step everywhere
+    (5, 96, 160),      # R = 10: the K-split decode kernel
+    (40, 160, 96),     # R = 80: the streaming decode kernel
+])
+def test_hidden_sizes_odd_multiples_of_32(T, H, I):
+    _say(f"odd multiples of 32: T={T} H={H} I={I}")
+    _run_layer(syn.spec("tiny", T=T, H=H, I=I, E=3, k=2))
+
+
+@pytest.mark.parametrize("r", [8, 32, 64])
+def test_lora_ranks(r):
+    # every supported rank: 8 (one zero-padded 16-deep chunk), 32 (one full
+    # 32-wide rank block), 64 (two), through the GEMM epilogues, the rank
+    # projection and the adapter gradients
+    _say(f"lora rank {r}")
+    _run_layer(syn.spec("tiny", T=300, H=192, I=320, E=3, k=2, lora_rank=r), lora_scale=4.0)
+
+
+@pytest.mark.parametrize("T,r", [(3, 16), (5, 64), (40, 8), (100, 32)])
+def test_lora_at_decode_sizes(T, r):
+    # R = T * k <= 256 routed rows: the decode kernels carry the adapter term
+    # (R <= 16 the K-split kernel, else the streaming one); odd multiples of
+    # 32 for H and I on the way
+    _say(f"lora decode T={T} r={r}")
+    _run_layer(syn.spec("tiny", T=T, H=96, I=160, E=3, k=2, lora_rank=r), lora_scale=4.0)
+
+
 def test_forward_is_deterministic():
     s = syn.spec("tiny", T=200, H=128, I=192, E=8, k=4)
     dl = device_layer(s)
