@@ -37,7 +37,7 @@ import numpy as np
 __all__ = ["LayerSpec", "CONFIGS", "DECODE_TOKENS", "spec", "rng",
            "bf16_bits", "f32_from_bf16_bits", "router_weight", "router_bias",
            "gate_up_weight", "down_weight", "gate_up_bias", "down_bias",
-           "lora_a", "lora_b", "tokens", "upstream_grad", "all_experts"]
+           "lora_a", "lora_b", "lora_gu_a", "lora_gu_b", "tokens", "upstream_grad", "all_experts"]
 
 
 @dataclass(frozen=True)
@@ -50,7 +50,9 @@ class LayerSpec:
     k: int            # experts per token
     seed: int         # weight seed (decode shares the 20b layer's weights)
     zipf_s: float = 0.0      # router-bias skew; 0 = unbiased router
-    lora_rank: int = 0       # LoRA rank on the down projection; 0 = none
+    lora_rank: int = 0       # LoRA rank; 0 = none
+    lora_down: bool = True   # with lora_rank: an adapter on the down projection
+    lora_gate_up: bool = False   # with lora_rank: an adapter on the gate_up projection
     swiglu_alpha: float = 1.702
     swiglu_limit: float = 7.0
     extra: dict = field(default_factory=dict, compare=False, hash=False)
@@ -143,6 +145,16 @@ def lora_a(s: LayerSpec) -> np.ndarray:
 def lora_b(s: LayerSpec) -> np.ndarray:
     """bf16 bits [E, H, r]."""
     return bf16_bits(_normal(s.seed, "lora_B", 0, (s.E, s.H, s.lora_rank), 0.01))
+
+
+def lora_gu_a(s: LayerSpec) -> np.ndarray:
+    """bf16 bits [E, r, H] (the gate_up adapter's A)."""
+    return bf16_bits(_normal(s.seed, "lora_gu_A", 0, (s.E, s.lora_rank, s.H), 0.01))
+
+
+def lora_gu_b(s: LayerSpec) -> np.ndarray:
+    """bf16 bits [E, 2I, r] (rows in the interleaved gate|up order)."""
+    return bf16_bits(_normal(s.seed, "lora_gu_B", 0, (s.E, 2 * s.I, s.lora_rank), 0.01))
 
 
 def tokens(s: LayerSpec, T: int | None = None, scale: float = 1.0) -> np.ndarray:

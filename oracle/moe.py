@@ -17,6 +17,10 @@ Layouts (row-major, last dim contiguous):
   dn_codes   uint8 [E, H, I/2], dn_scales uint8 [E, H, I/32]
   dn_bias    bf16 bits [E, H], or None
   lora_A     bf16 bits [E, r, I], lora_B bf16 bits [E, H, r], or None
+             (adapter on the down projection)
+  lora_gu_A  bf16 bits [E, r, H], lora_gu_B bf16 bits [E, 2I, r], or None
+             (adapter on the gate_up projection, B's rows interleaved like
+             the gate_up rows); both adapters share lora_scale
 
 Flat routed rows are f = t * k + j for token t and slot j.
 """
@@ -56,6 +60,8 @@ class Layer:
     lora_A: np.ndarray | None = None
     lora_B: np.ndarray | None = None
     lora_scale: float = 1.0
+    lora_gu_A: np.ndarray | None = None
+    lora_gu_B: np.ndarray | None = None
     #: precision the logits are rounded to before the top-k decision;
     #: float64 only for finite-difference probes of the router path
     logit_dtype: type = np.float32
@@ -88,7 +94,13 @@ class Layer:
 
     @property
     def has_lora(self):
+        """An adapter on the down projection."""
         return self.lora_A is not None
+
+    @property
+    def has_lora_gu(self):
+        """An adapter on the gate_up projection."""
+        return self.lora_gu_A is not None
 
 
 # ----------------------------------------------------------------- router
@@ -204,11 +216,25 @@ def _lora_v(layer, e, a):
     return a @ bf16_to_f64(layer.lora_A[e]).T            # [rows, r]
 
 
+def _lora_vg(layer, e, xt):
+    """The gate_up adapter's rank-space activations x A_gu^T, [rows, r]."""
+    return xt @ bf16_to_f64(layer.lora_gu_A[e]).T
+
+
+def _gate_up_pre(layer, e, xt, Wgu):
+    """h = x Wgu^T + b (+ s (x A_gu^T) B_gu^T with the gate_up adapter)."""
+    h = xt @ Wgu.T + layer.gu_b(e)
+    if layer.has_lora_gu:
+        h = h + layer.lora_scale * _lora_vg(layer, e, xt) @ bf16_to_f64(layer.lora_gu_B[e]).T
+    return h
+
+
 def forward(layer: Layer, x_bits, tokens=None, routing: Routing | None = None, experts=None):
     """Expert-block forward.  Returns (out float64 [T, H], routing, cache).
 
     out[t] = sum_j w[t, j] * y_(t, j), where for expert e = idx[t, j]
       h = x[t] @ Wgu[e].T + bgu[e]                (2I values)
+          (+ s * (x[t] @ Agu_e.T) @ Bgu_e.T with the gate_up adapter)
       a = swiglu(h[0::2], h[1::2])                (stride-2 split, [P3])
       y = a @ Wd[e].T + bd[e] (+ s * (a @ A_e.T) @ B_e.T with LoRA)
 
@@ -216,8 +242,9 @@ def forward(layer: Layer, x_bits, tokens=None, routing: Routing | None = None, e
     tokens; the other rows of ``out`` stay zero.  ``experts`` (optional)
     restricts it to those experts: ``out`` then holds only their share.
     Routing is always for all tokens (it is what the permutation is defined
-    on).  ``cache`` maps each flat row f that was computed to (h, a, y) for
-    the backward and tests.
+    on).  ``cache`` maps each flat row f that was computed to (h, a, y, vg)
+    for the backward and tests (vg = x A_gu^T, None without the gate_up
+    adapter).
     """
     x = bf16_to_f64(x_bits)
     T, H = x.shape
@@ -236,22 +263,23 @@ def forward(layer: Layer, x_bits, tokens=None, routing: Routing | None = None, e
         if rows.size == 0:
             continue
         t = rows // k
-        h = x[t] @ layer.gate_up(e).T + layer.gu_b(e)
+        h = _gate_up_pre(layer, e, x[t], layer.gate_up(e))
         a = swiglu(h[:, 0::2], h[:, 1::2], layer.alpha, layer.limit)
         y = a @ layer.down(e).T + layer.dn_b(e)
         if layer.has_lora:
             y = y + layer.lora_scale * _lora_v(layer, e, a) @ bf16_to_f64(layer.lora_B[e]).T
+        vg = _lora_vg(layer, e, x[t]) if layer.has_lora_gu else None
         wr = r.w.reshape(-1)[rows]
         np.add.at(out, t, wr[:, None] * y)
         for i, f in enumerate(rows):
-            cache[int(f)] = (h[i], a[i], y[i])
+            cache[int(f)] = (h[i], a[i], y[i], None if vg is None else vg[i])
     return out, r, cache
 
 
 # ---------------------------------------------------------------- backward
 
 def backward_dx(layer: Layer, x_bits, dy_bits, tokens=None, routing: Routing | None = None,
-                want_lora=True, experts=None):
+                want_lora=True, experts=None, gu_grads: dict | None = None):
     """Gradient of L = sum(dY * out) with respect to x (and the LoRA
     adapters), base weights and biases frozen ([P1]: only the input and
     adapter gradients are needed for LoRA training).
@@ -262,11 +290,14 @@ def backward_dx(layer: Layer, x_bits, dy_bits, tokens=None, routing: Routing | N
       da    = g_y @ Wd[e]   (+ LoRA: dv = s * g_y @ B_e; da += dv @ A_e)
       dg, du = swiglu_backward(h[0::2], h[1::2], da)
       dh    = interleave(dg, du)
-      dx_f  = dh @ Wgu[e]
+      dx_f  = dh @ Wgu[e]   (+ gate_up adapter: dvg = s * dh @ Bgu_e; dx_f += dvg @ Agu_e)
     Router (softmax over the selected logits, reading: dX includes it):
       dl_j  = w_j * (dw_j - sum_i w_i dw_i)
       dX[t] = sum_j dx_(t, j) + sum_j dl_j * Wr[idx[t, j]]
     LoRA: dB_e = s * sum_f g_y^T v_f, dA_e = sum_f dv^T a_f.
+    Gate_up adapter (filled into ``gu_grads`` as "dA_gu" [E, r, H] and
+    "dB_gu" [E, 2I, r] when a dict is given): dB_gu_e = s * sum_f dh^T vg_f
+    with vg = x A_gu^T, dA_gu_e = sum_f dvg^T x_t.
 
     ``tokens`` restricts dX to those tokens (then dA/dB cover only them).
     ``experts`` restricts the expert loop to those experts: dA/dB are then
@@ -288,6 +319,9 @@ def backward_dx(layer: Layer, x_bits, dy_bits, tokens=None, routing: Routing | N
     lora = layer.has_lora and want_lora
     dA = np.zeros(layer.lora_A.shape) if lora else None
     dB = np.zeros(layer.lora_B.shape) if lora else None
+    lora_gu = layer.has_lora_gu and want_lora and gu_grads is not None
+    dAg = np.zeros(layer.lora_gu_A.shape) if lora_gu else None
+    dBg = np.zeros(layer.lora_gu_B.shape) if lora_gu else None
     wflat = r.w.reshape(-1)
     for e in range(layer.E):
         if experts is not None and e not in experts:
@@ -298,7 +332,7 @@ def backward_dx(layer: Layer, x_bits, dy_bits, tokens=None, routing: Routing | N
         t = rows // k
         Wgu = layer.gate_up(e)
         Wd = layer.down(e)
-        h = x[t] @ Wgu.T + layer.gu_b(e)
+        h = _gate_up_pre(layer, e, x[t], Wgu)
         g, u = h[:, 0::2], h[:, 1::2]
         a = swiglu(g, u, layer.alpha, layer.limit)
         y = a @ Wd.T + layer.dn_b(e)
@@ -320,7 +354,18 @@ def backward_dx(layer: Layer, x_bits, dy_bits, tokens=None, routing: Routing | N
         dh = np.empty_like(h)
         dh[:, 0::2] = dg
         dh[:, 1::2] = du
-        np.add.at(dX, t, dh @ Wgu)
+        dxf = dh @ Wgu
+        if layer.has_lora_gu:
+            Ag = bf16_to_f64(layer.lora_gu_A[e])
+            Bg = bf16_to_f64(layer.lora_gu_B[e])
+            dvg = layer.lora_scale * dh @ Bg
+            dxf = dxf + dvg @ Ag
+            if lora_gu:
+                dBg[e] += layer.lora_scale * dh.T @ (x[t] @ Ag.T)
+                dAg[e] += dvg.T @ x[t]
+        np.add.at(dX, t, dxf)
+    if lora_gu:
+        gu_grads["dA_gu"], gu_grads["dB_gu"] = dAg, dBg
     if experts is not None:
         return dX, dA, dB
     # router path through the softmax over the selected logits

@@ -94,9 +94,12 @@ def oracle_layer(s, experts=None, with_bias=True, threads=8):
                   dn_codes=dn_c, dn_scales=dn_s,
                   dn_bias=syn.down_bias(s) if with_bias else None,
                   k=s.k, alpha=s.swiglu_alpha, limit=s.swiglu_limit)
-    if s.lora_rank:
+    if s.lora_rank and s.lora_down:
         L.lora_A = syn.lora_a(s)
         L.lora_B = syn.lora_b(s)
+    if s.lora_rank and s.lora_gate_up:
+        L.lora_gu_A = syn.lora_gu_a(s)
+        L.lora_gu_B = syn.lora_gu_b(s)
     return L, experts
 
 

@@ -28,9 +28,12 @@ def oracle_layer(s, with_bias=True, **kw) -> moe.Layer:
         gu_codes=gc, gu_scales=gs, gu_bias=syn.gate_up_bias(s) if with_bias else None,
         dn_codes=dc, dn_scales=ds, dn_bias=syn.down_bias(s) if with_bias else None,
         k=s.k, alpha=s.swiglu_alpha, limit=s.swiglu_limit)
-    if s.lora_rank:
+    if s.lora_rank and s.lora_down:
         L.lora_A = syn.lora_a(s)
         L.lora_B = syn.lora_b(s)
+    if s.lora_rank and s.lora_gate_up:
+        L.lora_gu_A = syn.lora_gu_a(s)
+        L.lora_gu_B = syn.lora_gu_b(s)
     for key, v in kw.items():
         setattr(L, key, v)
     return L

@@ -212,6 +212,10 @@ def _brute_forward(L, x_bits):
             Wgu = mxfp4.dequantize(L.gu_codes[e], L.gu_scales[e])
             Wd = mxfp4.dequantize(L.dn_codes[e], L.dn_scales[e])
             h = np.array([np.dot(Wgu[n], x[t]) for n in range(2 * L.I)]) + L.gu_b(e)
+            if L.has_lora_gu:
+                Ag = moe.bf16_to_f64(L.lora_gu_A[e])
+                Bg = moe.bf16_to_f64(L.lora_gu_B[e])
+                h = h + L.lora_scale * Bg @ (Ag @ x[t])
             act = moe.swiglu(h[0::2], h[1::2], L.alpha, L.limit)
             y = np.array([np.dot(Wd[m], act) for m in range(L.H)]) + L.dn_b(e)
             if L.has_lora:
@@ -311,8 +315,9 @@ def _fd_layer(s, x_scale=1.0, lora=False):
     L = oracle_layer(s)
     L.logit_dtype = np.float64
     if lora:
-        L.lora_A = moe.bf16_to_f64(L.lora_A)
-        L.lora_B = moe.bf16_to_f64(L.lora_B)
+        for name in ("lora_A", "lora_B", "lora_gu_A", "lora_gu_B"):
+            if getattr(L, name) is not None:
+                setattr(L, name, moe.bf16_to_f64(getattr(L, name)))
     x = moe.bf16_to_f64(syn.tokens(s, scale=x_scale))
     dY = moe.bf16_to_f64(syn.upstream_grad(s))
     return L, x, dY
@@ -449,3 +454,88 @@ def test_lora_gradients_against_scale_derivative():
     assert abs(slope) > 1e-6
     assert abs(ipB - sc * slope) <= 1e-10 * abs(sc * slope)
     assert abs(ipA - sc * slope) <= 1e-10 * abs(sc * slope)
+
+
+# ------------------------------------------------ adapter on gate_up (both)
+
+def test_forward_with_gate_up_lora_matches_brute_force():
+    s = syn.spec("tiny", lora_rank=8, lora_gate_up=True)
+    L = oracle_layer(s)
+    L.lora_scale = 3.0
+    x = syn.tokens(s)
+    out, _, cache = moe.forward(L, x)
+    np.testing.assert_allclose(out, _brute_forward(L, x), rtol=1e-12, atol=1e-14)
+    # the cached vg is x A_gu^T of the row's token
+    xf = moe.bf16_to_f64(x)
+    r = moe.route(L, x)
+    for f in r.sorted_rows[:5]:
+        e = int(np.searchsorted(r.offsets, np.nonzero(r.sorted_rows == f)[0][0], side="right") - 1)
+        ref = moe.bf16_to_f64(L.lora_gu_A[e]) @ xf[f // s.k]
+        np.testing.assert_allclose(cache[int(f)][3], ref, rtol=1e-13, atol=1e-16)
+
+
+def test_gate_up_adapter_changes_the_output():
+    # the adapter term is not lost: switching it off moves the output
+    s = syn.spec("tiny", lora_rank=16, lora_gate_up=True, lora_down=False)
+    L = oracle_layer(s)
+    L.lora_scale = 8.0
+    x = syn.tokens(s)
+    r = moe.route(L, x)
+    out, _, _ = moe.forward(L, x, routing=r)
+    L0 = copy.copy(L)
+    L0.lora_gu_A = L0.lora_gu_B = None
+    out0, _, _ = moe.forward(L0, x, routing=r)
+    assert np.abs(out - out0).max() > 1e-3 * np.abs(out0).max()
+
+
+@pytest.mark.parametrize("down", [False, True])
+def test_backward_gate_up_lora_finite_differences(down):
+    s = syn.spec("tiny", lora_rank=8, lora_gate_up=True, lora_down=down)
+    L, x, dY = _fd_layer(s, lora=True)
+    L.lora_scale = 2.0
+    g = {}
+    dX, dA, dB = moe.backward_dx(L, x, dY, gu_grads=g)
+    assert (dA is not None) == down and (dB is not None) == down
+    rng = np.random.default_rng(13)
+    grads = [("lora_gu_A", g["dA_gu"]), ("lora_gu_B", g["dB_gu"])]
+    if down:
+        grads += [("lora_A", dA), ("lora_B", dB)]
+    for name, grad in grads:
+        base = getattr(L, name)
+        assert grad.shape == base.shape
+        for _ in range(6):
+            pos = tuple(int(rng.integers(0, n)) for n in base.shape)
+            eps = 1e-4
+            P = base.copy()
+            P[pos] += eps
+            Lp = copy.copy(L)
+            setattr(Lp, name, P)
+            M = base.copy()
+            M[pos] -= eps
+            Lm = copy.copy(L)
+            setattr(Lm, name, M)
+            fd = (_loss(Lp, x, dY) - _loss(Lm, x, dY)) / (2 * eps)
+            assert abs(fd - grad[pos]) <= 1e-6 * max(1.0, abs(fd)), (name, pos, fd, grad[pos])
+    # dX carries the gate_up adapter's input gradient
+    v = rng.standard_normal(x.shape)
+    eps = 1e-6
+    fd = (_loss(L, x + eps * v, dY) - _loss(L, x - eps * v, dY)) / (2 * eps)
+    assert abs(fd - np.sum(dX * v)) <= 1e-6 * max(1.0, abs(fd))
+
+
+def test_gate_up_adapter_gradients_partition_over_experts():
+    s = syn.spec("tiny", lora_rank=16, lora_gate_up=True)
+    L = oracle_layer(s)
+    L.lora_scale = 3.0
+    x = syn.tokens(s)
+    dY = syn.upstream_grad(s)
+    r = moe.route(L, x)
+    g = {}
+    moe.backward_dx(L, x, dY, routing=r, gu_grads=g)
+    for e in range(s.E):
+        ge = {}
+        moe.backward_dx(L, x, dY, routing=r, experts=[e], gu_grads=ge)
+        np.testing.assert_allclose(ge["dA_gu"][e], g["dA_gu"][e], rtol=1e-12, atol=1e-15)
+        np.testing.assert_allclose(ge["dB_gu"][e], g["dB_gu"][e], rtol=1e-12, atol=1e-15)
+        others = [i for i in range(s.E) if i != e]
+        assert not np.any(ge["dA_gu"][others]) and not np.any(ge["dB_gu"][others])
