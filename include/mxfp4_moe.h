@@ -59,8 +59,12 @@ extern "C" {
  *  lora_rank in {0, 8, 16, 32, 64}.  Weight, scale, bias, activation and
  *  output pointers 16-byte aligned.
  *  swiglu_alpha, swiglu_limit: the clamped SwiGLU constants (GPT-OSS uses
- *  1.702 and 7).  lora_scale multiplies the LoRA delta (1.0 when
- *  lora_alpha equals the rank). */
+ *  1.702 and 7).  lora_scale multiplies the LoRA deltas (1.0 when
+ *  lora_alpha equals the rank).  lora_targets: which projections carry a
+ *  rank-lora_rank adapter, MXFP4_LORA_DOWN | MXFP4_LORA_GATE_UP (0 means
+ *  MXFP4_LORA_DOWN); ignored when lora_rank == 0. */
+#define MXFP4_LORA_DOWN 1
+#define MXFP4_LORA_GATE_UP 2
 typedef struct mxfp4_moe_dims {
   int64_t T;
   int64_t H;
@@ -71,6 +75,7 @@ typedef struct mxfp4_moe_dims {
   float swiglu_limit;
   int32_t lora_rank;
   float lora_scale;
+  int32_t lora_targets;
 } mxfp4_moe_dims;
 
 /* Frozen layer parameters ([P3] MXFP4 layout; weights never written).
@@ -90,7 +95,12 @@ typedef struct mxfp4_moe_dims {
  *            required and 16-byte aligned when lora_rank > 0.  Inside the
  *            down GEMMs, scale * v and the rank-space gradient enter the
  *            bf16 matrix cores as a hi + lo bf16 pair (about 17 bits), in
- *            16-deep chunks of the rank (rank 8 zero-padded to one). */
+ *            16-deep chunks of the rank (rank 8 zero-padded to one).
+ *  lora_gu_A bf16 [E, r, H] and lora_gu_B bf16 [E, 2I, r] (rows in the
+ *            interleaved gate/up order): the adapter on the gate_up
+ *            projection, h += scale * (x A_gu_e^T) B_gu_e^T before the
+ *            bias; both required (16-byte aligned) iff MXFP4_LORA_GATE_UP
+ *            is a target, else NULL. */
 typedef struct mxfp4_moe_weights {
   const float* router_w;
   const float* router_b;
@@ -102,6 +112,8 @@ typedef struct mxfp4_moe_weights {
   const uint16_t* dn_bias;
   const uint16_t* lora_A;
   const uint16_t* lora_B;
+  const uint16_t* lora_gu_A;
+  const uint16_t* lora_gu_B;
 } mxfp4_moe_weights;
 
 /* State the forward saves for the backward (caller-owned device buffers,
@@ -116,8 +128,11 @@ typedef struct mxfp4_moe_weights {
  *  h              bf16  [R, 2I]  gate_up output incl. bias, sorted order
  *  a              bf16  [R, I]   SwiGLU output, sorted order
  *  lora_v         fp32  [R, r]   v = a A_e^T (sorted order, before the
- *                                lora_scale); required iff lora_rank > 0,
- *                                else ignored; 16-byte aligned */
+ *                                lora_scale); required iff the down
+ *                                projection has an adapter, else ignored;
+ *                                16-byte aligned
+ *  lora_vg        fp32  [R, r]   vg = x A_gu_e^T likewise, for the gate_up
+ *                                adapter */
 typedef struct mxfp4_moe_saved {
   int32_t* topk_idx;
   float* topk_w;
@@ -126,10 +141,12 @@ typedef struct mxfp4_moe_saved {
   uint16_t* h;
   uint16_t* a;
   float* lora_v;
+  float* lora_vg;
 } mxfp4_moe_saved;
 
 /* Byte sizes of the saved-state buffers for given dims (one field per
- * mxfp4_moe_saved buffer, same order; lora_v is 0 when lora_rank == 0).
+ * mxfp4_moe_saved buffer, same order; lora_v and lora_vg are 0 without
+ * the matching adapter).
  * The caller allocates them (each 16-byte aligned) and passes their
  * addresses in mxfp4_moe_saved; the library never allocates them ([P1]
  * "What this does": the transients belong to the caller's framework). */
@@ -141,6 +158,7 @@ typedef struct mxfp4_moe_saved_sizes {
   size_t h;
   size_t a;
   size_t lora_v;
+  size_t lora_vg;
 } mxfp4_moe_saved_sizes;
 
 /* Fills *out for dims.  Returns MXFP4_OK, MXFP4_EINVAL (null out, or dims
@@ -164,7 +182,8 @@ size_t mxfp4_moe_workspace_bytes(const mxfp4_moe_dims* dims, int mode);
  *   logits l[t,e] = sum_h x[t,h] Wr[e,h] + br[e]  (products summed in fp64,
  *                   rounded once to fp32 before the top-k decision)
  *   top-k experts, softmax over the k selected logits -> w[t,j]
- *   h = x Wgu_e^T + bgu_e;  a = min(g,L) sig(alpha min(g,L)) (clamp(u,-L,L)+1)
+ *   h = x Wgu_e^T + bgu_e (+ lora_scale (x A_gu_e^T) B_gu_e^T);
+ *   a = min(g,L) sig(alpha min(g,L)) (clamp(u,-L,L)+1)
  *       with g = h[2i], u = h[2i+1]
  *   y = a Wd_e^T + bd_e (+ lora_scale (a A_e^T) B_e^T)
  *   out[t] = sum_j w[t,j] y_(t,j)   (each term w y rounded to bf16, then
@@ -202,18 +221,23 @@ int mxfp4_moe_forward_noalloc(const mxfp4_moe_dims* dims, const mxfp4_moe_weight
  *   per routed row f = (t, j), expert e:
  *     dw_f = dY_t . y_f;   da = w_f dY_t Wd_e (+ LoRA: dv = s w_f dY_t B_e,
  *     da += dv A_e);  (dg, du) = SwiGLU'(h) * da (no gradient through a
- *     clamped input beyond its bound);  dx_f = dh Wgu_e
+ *     clamped input beyond its bound);  dx_f = dh Wgu_e (+ gate_up
+ *     adapter: dvg = s dh B_gu_e, dx_f += dvg A_gu_e)
  *   router: dl_j = w_j (dw_j - sum_i w_i dw_i)
  *   dX[t] = sum_j dx_(t,j) + sum_j dl_j Wr[idx_j]          (bf16 out;
  *           each dx_(t,j) rounded to bf16, the sum taken in fp32)
  *   dA_e = sum_f dv_f^T a_f  [E, r, I];  dB_e = s sum_f (w_f dY_t)^T v_f
- *   [E, H, r]; both fp32, overwritten, required iff lora_rank > 0.
+ *   [E, H, r]; both fp32, overwritten, required iff the down projection
+ *   has an adapter (else ignored).
+ *   dA_gu_e = sum_f dvg_f^T x_t [E, r, H];  dB_gu_e = s sum_f dh_f^T vg_f
+ *   [E, 2I, r]; fp32, overwritten, required iff gate_up has an adapter.
  * saved: the buffers a forward with the same dims, weights and x filled.
- * dy bf16 [T, H] in; dx bf16 [T, H] out. */
+ * x bf16 [T, H]: the forward's input, required only with the gate_up
+ * adapter (else may be NULL).  dy bf16 [T, H] in; dx bf16 [T, H] out. */
 int mxfp4_moe_backward_dx(const mxfp4_moe_dims* dims, const mxfp4_moe_weights* w,
-                          const mxfp4_moe_saved* saved, const uint16_t* dy, uint16_t* dx,
-                          float* dA, float* dB, void* workspace, size_t workspace_bytes,
-                          void* stream);
+                          const mxfp4_moe_saved* saved, const uint16_t* x, const uint16_t* dy,
+                          uint16_t* dx, float* dA, float* dB, float* dA_gu, float* dB_gu,
+                          void* workspace, size_t workspace_bytes, void* stream);
 
 /* Row-wise MXFP4 quantisation, one launch ([P3] note on the row-wise
  * quantizers).  w fp32 [rows, K] -> codes uint8 [rows, K/2] (low nibble =

@@ -47,6 +47,7 @@ struct Layout {
          tiles_l = SIZE_MAX, num_tiles_l = SIZE_MAX,
          y_w = SIZE_MAX, dh = SIZE_MAX, dw_part = SIZE_MAX, dxr = SIZE_MAX,
          lora_v = SIZE_MAX, lora_At = SIZE_MAX, lora_Bt = SIZE_MAX, lora_dvu = SIZE_MAX,
+         lora_vg = SIZE_MAX, lora_guAt = SIZE_MAX, lora_guBt = SIZE_MAX, lora_dvg = SIZE_MAX,
          logits = SIZE_MAX, logit_part = SIZE_MAX;
   size_t total = 0;
   size_t put(size_t bytes) {
@@ -55,6 +56,14 @@ struct Layout {
     return at;
   }
 };
+
+// Which projections carry an adapter (lora_targets 0 means the down one).
+bool lora_dn(const mxfp4_moe_dims& d) {
+  return d.lora_rank && (d.lora_targets == 0 || (d.lora_targets & MXFP4_LORA_DOWN));
+}
+bool lora_gu(const mxfp4_moe_dims& d) {
+  return d.lora_rank && (d.lora_targets & MXFP4_LORA_GATE_UP);
+}
 
 int check_dims(const mxfp4_moe_dims* d) {
   if (!d) return fail(MXFP4_EINVAL, "dims is NULL");
@@ -78,6 +87,9 @@ int check_dims(const mxfp4_moe_dims* d) {
                 d->lora_rank);
   if (d->lora_rank && !(d->lora_scale == d->lora_scale && d->lora_scale - d->lora_scale == 0.0f))
     return fail(MXFP4_EINVAL, "lora_scale must be finite");
+  if (d->lora_targets & ~(MXFP4_LORA_DOWN | MXFP4_LORA_GATE_UP))
+    return fail(MXFP4_EINVAL, "lora_targets=%d: only MXFP4_LORA_DOWN and MXFP4_LORA_GATE_UP",
+                d->lora_targets);
   return MXFP4_OK;
 }
 
@@ -92,7 +104,8 @@ Layout layout(const mxfp4_moe_dims& d, int mode) {
       L.offsets = L.put((size_t)(d.E + 1) * 4);
       L.sorted_rows = L.put(R * 4);
       L.a = L.put(R * (size_t)d.I * 2);
-      if (d.lora_rank) L.lora_v = L.put(R * (size_t)d.lora_rank * 4);
+      if (lora_dn(d)) L.lora_v = L.put(R * (size_t)d.lora_rank * 4);
+      if (lora_gu(d)) L.lora_vg = L.put(R * (size_t)d.lora_rank * 4);
     }
     L.logits = L.put((size_t)d.T * d.E * 4);
     if (mxmoe::plan_fits(d.T, d.E, d.k))
@@ -113,10 +126,15 @@ Layout layout(const mxfp4_moe_dims& d, int mode) {
     L.dh = L.put(R * (size_t)d.I * 2 * 2);
     L.dw_part = L.put(R * (size_t)mxmoe::bwd_down_ntiles((int)d.I) * 4);
     L.dxr = L.put(R * (size_t)d.H * 2);
-    if (d.lora_rank) {
+    if (lora_dn(d)) {
       L.lora_At = L.put((size_t)d.E * d.I * d.lora_rank * 2);
       L.lora_Bt = L.put((size_t)d.E * d.H * d.lora_rank * 2);
       L.lora_dvu = L.put(R * (size_t)d.lora_rank * 4);
+    }
+    if (lora_gu(d)) {
+      L.lora_guAt = L.put((size_t)d.E * d.H * d.lora_rank * 2);
+      L.lora_guBt = L.put((size_t)d.E * 2 * d.I * d.lora_rank * 2);
+      L.lora_dvg = L.put(R * (size_t)d.lora_rank * 4);
     }
   }
   return L;
@@ -129,13 +147,24 @@ T* at(void* ws, size_t off) {
 
 int check_weights(const mxfp4_moe_weights* w, const mxfp4_moe_dims& d) {
   if (!w) return fail(MXFP4_EINVAL, "weights is NULL");
-  if (d.lora_rank) {
+  if (lora_dn(d)) {
     if (!w->lora_A || !w->lora_B)
-      return fail(MXFP4_EINVAL, "lora_rank=%d needs lora_A and lora_B", d.lora_rank);
+      return fail(MXFP4_EINVAL, "lora_rank=%d on the down projection needs lora_A and lora_B",
+                  d.lora_rank);
     if (!aligned(w->lora_A, 16) || !aligned(w->lora_B, 16))
       return fail(MXFP4_EINVAL, "lora_A and lora_B must be 16-byte aligned");
   } else if (w->lora_A || w->lora_B) {
-    return fail(MXFP4_EINVAL, "lora_A/lora_B given but lora_rank is 0");
+    return fail(MXFP4_EINVAL, "lora_A/lora_B given but lora_rank is 0 or the down projection is "
+                              "not a lora target");
+  }
+  if (lora_gu(d)) {
+    if (!w->lora_gu_A || !w->lora_gu_B)
+      return fail(MXFP4_EINVAL, "lora_rank=%d on gate_up needs lora_gu_A and lora_gu_B",
+                  d.lora_rank);
+    if (!aligned(w->lora_gu_A, 16) || !aligned(w->lora_gu_B, 16))
+      return fail(MXFP4_EINVAL, "lora_gu_A and lora_gu_B must be 16-byte aligned");
+  } else if (w->lora_gu_A || w->lora_gu_B) {
+    return fail(MXFP4_EINVAL, "lora_gu_A/lora_gu_B given but gate_up is not a lora target");
   }
   if (!w->router_w || !w->gu_codes || !w->gu_scales || !w->dn_codes || !w->dn_scales)
     return fail(MXFP4_EINVAL, "router_w, gu_codes, gu_scales, dn_codes and dn_scales are required");
@@ -244,8 +273,10 @@ int check_forward(const mxfp4_moe_dims* dims, const mxfp4_moe_weights* w, const 
       return fail(MXFP4_EINVAL, "saved: topk_idx, topk_w, expert_offsets, sorted_rows, h, a are required");
     if (!aligned(saved->h, 16) || !aligned(saved->a, 16))
       return fail(MXFP4_EINVAL, "saved h and a must be 16-byte aligned");
-    if (d.lora_rank && (!saved->lora_v || !aligned(saved->lora_v, 16)))
-      return fail(MXFP4_EINVAL, "lora_rank > 0: saved lora_v is required, 16-byte aligned");
+    if (lora_dn(d) && (!saved->lora_v || !aligned(saved->lora_v, 16)))
+      return fail(MXFP4_EINVAL, "down adapter: saved lora_v is required, 16-byte aligned");
+    if (lora_gu(d) && (!saved->lora_vg || !aligned(saved->lora_vg, 16)))
+      return fail(MXFP4_EINVAL, "gate_up adapter: saved lora_vg is required, 16-byte aligned");
   }
   return MXFP4_OK;
 }
@@ -269,7 +300,9 @@ int enqueue_forward(const mxfp4_moe_dims& d, const mxfp4_moe_weights* w, const u
   mxmoe::Tile* tiles = at<mxmoe::Tile>(workspace, L.tiles);
   int32_t* num_tiles = at<int32_t>(workspace, L.num_tiles);
   uint16_t* y_w = at<uint16_t>(workspace, L.y_w);
-  float* lora_v = !d.lora_rank ? nullptr : saved ? saved->lora_v : at<float>(workspace, L.lora_v);
+  float* lora_v = !lora_dn(d) ? nullptr : saved ? saved->lora_v : at<float>(workspace, L.lora_v);
+  float* lora_vg = !lora_gu(d) ? nullptr : saved ? saved->lora_vg : at<float>(workspace, L.lora_vg);
+  const int r = d.lora_rank;
   const int maxt = mxmoe::max_tiles(R, E, mxmoe::MT);
 
   float* logits = at<float>(workspace, L.logits);
@@ -288,35 +321,41 @@ int enqueue_forward(const mxfp4_moe_dims& d, const mxfp4_moe_weights* w, const u
            "scan");
     LAUNCH(mxmoe::launch_scatter(topk_idx, blk_hist, T, k, E, sorted_rows, s), "scatter");
   }
+  // the gate_up adapter's rank-space activations vg = x A_gu^T
+  if (lora_vg)
+    LAUNCH(mxmoe::launch_lora_proj(x, true, sorted_rows, k, w->lora_gu_A, H, r, tiles, num_tiles,
+                                   maxt, 1.0f, lora_vg, s),
+           "lora_vg");
+  const uint16_t* gu_B = lora_vg ? w->lora_gu_B : nullptr;
+  const uint16_t* dn_B = lora_v ? w->lora_B : nullptr;
   // few rows per expert: the weight-streaming decode kernels
   const bool decode = R <= DECODE_MAX_ROWS && H <= mxmoe::dec_max_k() && I <= mxmoe::dec_max_k();
   if (decode) {
     LAUNCH(mxmoe::launch_dec_gate_up(x, w->gu_codes, w->gu_scales, w->gu_bias, sorted_rows, tiles,
                                      num_tiles, maxt, R, H, I, k, d.swiglu_alpha, d.swiglu_limit,
-                                     h, a, s),
+                                     gu_B, lora_vg, d.lora_scale, r, h, a, s),
            "dec_gate_up");
-    if (d.lora_rank)
-      LAUNCH(mxmoe::launch_lora_proj(a, false, sorted_rows, k, w->lora_A, I, d.lora_rank, tiles,
-                                     num_tiles, maxt, 1.0f, lora_v, s),
+    if (lora_v)
+      LAUNCH(mxmoe::launch_lora_proj(a, false, sorted_rows, k, w->lora_A, I, r, tiles, num_tiles,
+                                     maxt, 1.0f, lora_v, s),
              "lora_v");
     LAUNCH(mxmoe::launch_dec_down(a, w->dn_codes, w->dn_scales, w->dn_bias, topk_w, sorted_rows,
-                                  tiles, num_tiles, maxt, R, H, I,
-                                  d.lora_rank ? w->lora_B : nullptr, lora_v, d.lora_scale,
-                                  d.lora_rank, y_w, s),
+                                  tiles, num_tiles, maxt, R, H, I, dn_B, lora_v, d.lora_scale, r,
+                                  y_w, s),
            "dec_down");
     LAUNCH(mxmoe::launch_combine(y_w, d.T, H, k, out, s), "combine");
     return ok();
   }
   LAUNCH(mxmoe::launch_gate_up(x, w->gu_codes, w->gu_scales, w->gu_bias, sorted_rows, tiles,
-                               num_tiles, maxt, H, I, k, d.swiglu_alpha, d.swiglu_limit, h, a, s),
+                               num_tiles, maxt, H, I, k, d.swiglu_alpha, d.swiglu_limit, gu_B,
+                               lora_vg, d.lora_scale, r, h, a, s),
          "gate_up");
-  if (d.lora_rank)
-    LAUNCH(mxmoe::launch_lora_proj(a, false, sorted_rows, k, w->lora_A, I, d.lora_rank, tiles,
-                                   num_tiles, maxt, 1.0f, lora_v, s),
+  if (lora_v)
+    LAUNCH(mxmoe::launch_lora_proj(a, false, sorted_rows, k, w->lora_A, I, r, tiles, num_tiles,
+                                   maxt, 1.0f, lora_v, s),
            "lora_v");
   LAUNCH(mxmoe::launch_down(a, w->dn_codes, w->dn_scales, w->dn_bias, topk_w, sorted_rows, tiles,
-                            num_tiles, maxt, H, I, d.lora_rank ? w->lora_B : nullptr, lora_v,
-                            d.lora_scale, d.lora_rank, y_w, s),
+                            num_tiles, maxt, H, I, dn_B, lora_v, d.lora_scale, r, y_w, s),
          "down");
   LAUNCH(mxmoe::launch_combine(y_w, d.T, H, k, out, s), "combine");
   return ok();
@@ -399,7 +438,8 @@ int mxfp4_moe_saved_bytes(const mxfp4_moe_dims* dims, mxfp4_moe_saved_sizes* out
   z.sorted_rows = R * sizeof(int32_t);
   z.h = R * 2 * I * sizeof(uint16_t);
   z.a = R * I * sizeof(uint16_t);
-  z.lora_v = R * (size_t)d.lora_rank * sizeof(float);
+  z.lora_v = lora_dn(d) ? R * (size_t)d.lora_rank * sizeof(float) : 0;
+  z.lora_vg = lora_gu(d) ? R * (size_t)d.lora_rank * sizeof(float) : 0;
   *out = z;
   return ok();
 }
@@ -433,9 +473,9 @@ int mxfp4_moe_forward_noalloc(const mxfp4_moe_dims* dims, const mxfp4_moe_weight
 }
 
 int mxfp4_moe_backward_dx(const mxfp4_moe_dims* dims, const mxfp4_moe_weights* w,
-                          const mxfp4_moe_saved* saved, const uint16_t* dy, uint16_t* dx,
-                          float* dA, float* dB, void* workspace, size_t workspace_bytes,
-                          void* stream) {
+                          const mxfp4_moe_saved* saved, const uint16_t* x, const uint16_t* dy,
+                          uint16_t* dx, float* dA, float* dB, float* dA_gu, float* dB_gu,
+                          void* workspace, size_t workspace_bytes, void* stream) {
   int rc = check_dims(dims);
   if (rc) return rc;
   rc = check_weights(w, *dims);
@@ -447,10 +487,17 @@ int mxfp4_moe_backward_dx(const mxfp4_moe_dims* dims, const mxfp4_moe_weights* w
   if (!dy || !dx) return fail(MXFP4_EINVAL, "dy and dx are required");
   if (!aligned(dy, 16) || !aligned(dx, 16) || !aligned(saved->h, 16) || !aligned(saved->a, 16))
     return fail(MXFP4_EINVAL, "dy, dx, saved h and a must be 16-byte aligned");
-  if (d.lora_rank) {
+  if (lora_dn(d)) {
     if (!saved->lora_v || !aligned(saved->lora_v, 16))
-      return fail(MXFP4_EINVAL, "lora_rank > 0: saved lora_v is required, 16-byte aligned");
-    if (!dA || !dB) return fail(MXFP4_EINVAL, "lora_rank > 0: dA and dB are required");
+      return fail(MXFP4_EINVAL, "down adapter: saved lora_v is required, 16-byte aligned");
+    if (!dA || !dB) return fail(MXFP4_EINVAL, "down adapter: dA and dB are required");
+  }
+  if (lora_gu(d)) {
+    if (!saved->lora_vg || !aligned(saved->lora_vg, 16))
+      return fail(MXFP4_EINVAL, "gate_up adapter: saved lora_vg is required, 16-byte aligned");
+    if (!dA_gu || !dB_gu) return fail(MXFP4_EINVAL, "gate_up adapter: dA_gu and dB_gu are required");
+    if (!x || !aligned(x, 16))
+      return fail(MXFP4_EINVAL, "gate_up adapter: x (the forward's input) is required, 16-byte aligned");
   }
   const Layout L = layout(d, MXFP4_WS_BACKWARD);
   if (!workspace || workspace_bytes < L.total)
@@ -467,30 +514,39 @@ int mxfp4_moe_backward_dx(const mxfp4_moe_dims* dims, const mxfp4_moe_weights* w
   uint16_t* dxr = at<uint16_t>(workspace, L.dxr);
   const int maxt = mxmoe::max_tiles(R, E, mxmoe::BMT);
   const int r = d.lora_rank;
+  const bool dn = lora_dn(d), gu = lora_gu(d);
   mxmoe::Tile* tiles_l = r ? at<mxmoe::Tile>(workspace, L.tiles_l) : nullptr;
   int32_t* num_tiles_l = r ? at<int32_t>(workspace, L.num_tiles_l) : nullptr;
-  uint16_t* lora_At = r ? at<uint16_t>(workspace, L.lora_At) : nullptr;
-  uint16_t* lora_Bt = r ? at<uint16_t>(workspace, L.lora_Bt) : nullptr;
-  float* lora_dvu = r ? at<float>(workspace, L.lora_dvu) : nullptr;
+  uint16_t* lora_At = dn ? at<uint16_t>(workspace, L.lora_At) : nullptr;
+  uint16_t* lora_Bt = dn ? at<uint16_t>(workspace, L.lora_Bt) : nullptr;
+  float* lora_dvu = dn ? at<float>(workspace, L.lora_dvu) : nullptr;
+  uint16_t* lora_guAt = gu ? at<uint16_t>(workspace, L.lora_guAt) : nullptr;
+  uint16_t* lora_guBt = gu ? at<uint16_t>(workspace, L.lora_guBt) : nullptr;
+  float* lora_dvg = gu ? at<float>(workspace, L.lora_dvg) : nullptr;
+  const int maxt_l = mxmoe::max_tiles(R, E, mxmoe::MT);
 
   LAUNCH(mxmoe::launch_build_tiles(saved->expert_offsets, E, mxmoe::BMT, tiles, num_tiles,
                                    mxmoe::MT, tiles_l, num_tiles_l, s),
          "bwd_tiles");
-  if (r) {
+  if (dn) {
     LAUNCH(mxmoe::launch_transpose_bf16(w->lora_A, E, r, I, lora_At, s), "lora_transpose");
     LAUNCH(mxmoe::launch_transpose_bf16(w->lora_B, E, H, r, lora_Bt, s), "lora_transpose");
     // dv_u = s dY_t B_e over the token rows of dY
     LAUNCH(mxmoe::launch_lora_proj(dy, true, saved->sorted_rows, k, lora_Bt, H, r, tiles_l,
-                                   num_tiles_l, mxmoe::max_tiles(R, E, mxmoe::MT), d.lora_scale,
-                                   lora_dvu, s),
+                                   num_tiles_l, maxt_l, d.lora_scale, lora_dvu, s),
            "lora_dvu");
+  }
+  if (gu) {
+    LAUNCH(mxmoe::launch_transpose_bf16(w->lora_gu_A, E, r, H, lora_guAt, s), "lora_transpose");
+    LAUNCH(mxmoe::launch_transpose_bf16(w->lora_gu_B, E, 2 * I, r, lora_guBt, s),
+           "lora_transpose");
   }
   LAUNCH(mxmoe::launch_bwd_down(dy, w->dn_codes, w->dn_scales, saved->topk_w, saved->sorted_rows,
                                 tiles, num_tiles, maxt, saved->h, saved->a, H, I, k,
                                 d.swiglu_alpha, d.swiglu_limit, lora_At, lora_dvu, r, dh, dw_part,
                                 s),
          "bwd_down");
-  if (r) {
+  if (dn) {
     // dA_e[j, i] = sum_p w_p dv_u[p, j] a[p, i];  dB_e[h, j] = s sum_p w_p dY[t(p), h] v[p, j]
     LAUNCH(mxmoe::launch_lora_grad(saved->a, false, I, saved->sorted_rows, k, lora_dvu, r,
                                    saved->topk_w, 1.0f, saved->expert_offsets, E, dA,
@@ -501,8 +557,22 @@ int mxfp4_moe_backward_dx(const mxfp4_moe_dims* dims, const mxfp4_moe_weights* w
                                    (int64_t)H * r, r, 1, s),
            "lora_grad");
   }
+  if (gu) {
+    // dv_g = s dh B_gu (dh holds the routing weight already), then
+    // dA_gu_e[j, h] = sum_p dv_g[p, j] x[t(p), h];  dB_gu_e[n, j] = s sum_p dh[p, n] vg[p, j]
+    LAUNCH(mxmoe::launch_lora_proj(dh, false, saved->sorted_rows, k, lora_guBt, 2 * I, r, tiles_l,
+                                   num_tiles_l, maxt_l, d.lora_scale, lora_dvg, s),
+           "lora_dvg");
+    LAUNCH(mxmoe::launch_lora_grad(x, true, H, saved->sorted_rows, k, lora_dvg, r, nullptr, 1.0f,
+                                   saved->expert_offsets, E, dA_gu, (int64_t)r * H, 1, H, s),
+           "lora_grad");
+    LAUNCH(mxmoe::launch_lora_grad(dh, false, 2 * I, saved->sorted_rows, k, saved->lora_vg, r,
+                                   nullptr, d.lora_scale, saved->expert_offsets, E, dB_gu,
+                                   (int64_t)2 * I * r, r, 1, s),
+           "lora_grad");
+  }
   LAUNCH(mxmoe::launch_bwd_gate_up(dh, w->gu_codes, w->gu_scales, saved->sorted_rows, tiles,
-                                   num_tiles, maxt, H, I, dxr, s),
+                                   num_tiles, maxt, H, I, lora_guAt, lora_dvg, r, dxr, s),
          "bwd_gate_up");
   LAUNCH(mxmoe::launch_bwd_combine(dy, dxr, dw_part, mxmoe::bwd_down_ntiles(I), saved->topk_idx,
                                    saved->topk_w, w->dn_bias, w->router_w, d.T, H, k, dx, s),

@@ -419,14 +419,44 @@ __device__ __forceinline__ void cols8(const f32x16 (&acc)[2][4], int q, int j, f
   }
 }
 
+// + dv A over an adapter's rank into the accumulators: 16-deep MFMA
+// contractions, A-operand = rows of A^T (At, [O, r] per expert; fragment
+// i's MFMA row l32 is output column ow + 2 l32 + i), B-operand = dv [R, r]
+// (sorted order) as hi + lo bf16.
+template <int NRB>
+__device__ __forceinline__ void lora_term(f32x16 (&acc)[2][4], const Tile& tl, int wp, int ow,
+                                          int O, const uint16_t* __restrict__ At,
+                                          const float* __restrict__ dv, int r) {
+  const int lane = threadIdx.x & 63;
+  const int l32 = lane & 31, hlf = lane >> 5;
+  for (int q = 0; q < lora_chunks(r); ++q) {
+#pragma unroll
+    for (int j = 0; j < NRB; ++j) {
+      const int pb = wp + 2 * j;
+      bf16x8 vh, vl;
+      lora_frag_split(dv + (int64_t)(tl.row0 + min(32 * pb + l32, tl.rows - 1)) * r, r, q, hlf,
+                      1.0f, &vh, &vl);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int col = ow + 2 * l32 + i;
+        const bf16x8 aw = lora_frag(At + ((int64_t)tl.expert * O + (col < O ? col : 0)) * r, r, q, hlf);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw, vh, acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw, vl, acc[i][j], 0, 0, 0);
+      }
+    }
+  }
+}
+
 // bwd_gate_up body for a wave with NRB live row blocks: main loop, then the
 // epilogue through a private LDS strip per wave (32 rows x 128 columns of
 // bf16 per row block), stored as whole 16-byte row pieces to the routed
 // rows' own dxr slots.
-template <int NRB>
+template <bool LORA, int NRB>
 __device__ __forceinline__ void bwd_gate_up_body(const GArgs& g, uint8_t* lds, const Tile& tl,
                                                  const int32_t* __restrict__ sorted_rows, int H,
-                                                 int o0, uint16_t* __restrict__ dxr) {
+                                                 int o0, const uint16_t* __restrict__ lora_At,
+                                                 const float* __restrict__ lora_dv, int lora_r,
+                                                 uint16_t* __restrict__ dxr) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wo = wave & 3, wp = wave >> 2;
   const int l32 = lane & 31, hlf = lane >> 5;
@@ -434,6 +464,7 @@ __device__ __forceinline__ void bwd_gate_up_body(const GArgs& g, uint8_t* lds, c
   zero_acc(acc);
   g_loop<NRB>(g, lds, wp, acc);
   const int ow = o0 + 64 * wo;                // this wave's first output column
+  if (LORA && NRB > 0) lora_term<NRB>(acc, tl, wp, ow, H, lora_At, lora_dv, lora_r);
   if (NRB == 0 || ow >= H) return;
   uint8_t* st = lds + wave * 4096;            // 32 rows x 128 bytes
 #pragma unroll
@@ -462,10 +493,12 @@ __device__ __forceinline__ void bwd_gate_up_body(const GArgs& g, uint8_t* lds, c
   }
 }
 
+template <bool LORA>
 __global__ __launch_bounds__(GTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_gate_up_kernel(
     const uint16_t* __restrict__ dh, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, const int32_t* __restrict__ sorted_rows,
     const Tile* __restrict__ tiles, const int32_t* __restrict__ num_tiles, int H, int I,
+    const uint16_t* __restrict__ lora_At, const float* __restrict__ lora_dv, int lora_r,
     uint16_t* __restrict__ dxr) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[GLDS_LOOP];
   Tile tl;
@@ -480,11 +513,11 @@ __global__ __launch_bounds__(GTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
           codes + (int64_t)tl.expert * N2 * (H / 2), scales + (int64_t)tl.expert * N2 * (H / 32),
           N2, H, o0);
   switch (live_blocks(tl.rows, wp)) {
-    case 0: bwd_gate_up_body<0>(g, lds, tl, sorted_rows, H, o0, dxr); break;
-    case 1: bwd_gate_up_body<1>(g, lds, tl, sorted_rows, H, o0, dxr); break;
-    case 2: bwd_gate_up_body<2>(g, lds, tl, sorted_rows, H, o0, dxr); break;
-    case 3: bwd_gate_up_body<3>(g, lds, tl, sorted_rows, H, o0, dxr); break;
-    default: bwd_gate_up_body<4>(g, lds, tl, sorted_rows, H, o0, dxr); break;
+    case 0: bwd_gate_up_body<LORA, 0>(g, lds, tl, sorted_rows, H, o0, lora_At, lora_dv, lora_r, dxr); break;
+    case 1: bwd_gate_up_body<LORA, 1>(g, lds, tl, sorted_rows, H, o0, lora_At, lora_dv, lora_r, dxr); break;
+    case 2: bwd_gate_up_body<LORA, 2>(g, lds, tl, sorted_rows, H, o0, lora_At, lora_dv, lora_r, dxr); break;
+    case 3: bwd_gate_up_body<LORA, 3>(g, lds, tl, sorted_rows, H, o0, lora_At, lora_dv, lora_r, dxr); break;
+    default: bwd_gate_up_body<LORA, 4>(g, lds, tl, sorted_rows, H, o0, lora_At, lora_dv, lora_r, dxr); break;
   }
 }
 
@@ -511,26 +544,7 @@ __device__ __forceinline__ void bwd_down_body(
   zero_acc(acc);
   g_loop<NRB>(g, lds, wp, acc);
   const int ow = o0 + 64 * wo;                // this wave's first column of I
-  if (LORA && NRB > 0) {
-    for (int q = 0; q < lora_chunks(lora_r); ++q) {
-#pragma unroll
-      for (int j = 0; j < NRB; ++j) {
-        const int pb = wp + 2 * j;
-        bf16x8 vh, vl;
-        lora_frag_split(lora_dvu + (int64_t)(tl.row0 + min(32 * pb + l32, tl.rows - 1)) * lora_r,
-                        lora_r, q, hlf, 1.0f, &vh, &vl);
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          // fragment i's MFMA row l32 is column 2 l32 + i of the wave's 64
-          const int col = ow + 2 * l32 + i;
-          const bf16x8 aw =
-              lora_frag(lora_At + ((int64_t)e * I + (col < I ? col : 0)) * lora_r, lora_r, q, hlf);
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw, vh, acc[i][j], 0, 0, 0);
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw, vl, acc[i][j], 0, 0, 0);
-        }
-      }
-    }
-  }
+  if (LORA && NRB > 0) lora_term<NRB>(acc, tl, wp, ow, I, lora_At, lora_dvu, lora_r);
   const int N2 = 2 * I;
   const bool active = ow < I;
   uint8_t* ast = lds + wave * 12288;          // a strip: 32 rows x 64 bf16 (128-byte rows)
@@ -775,11 +789,16 @@ hipError_t launch_bwd_down(const uint16_t* dy, const uint8_t* codes, const uint8
 hipError_t launch_bwd_gate_up(const uint16_t* dh, const uint8_t* codes, const uint8_t* scales,
                               const int32_t* sorted_rows, const Tile* tiles,
                               const int32_t* num_tiles, int max_tiles, int H, int I,
+                              const uint16_t* lora_At, const float* lora_dv, int lora_r,
                               uint16_t* dxr, hipStream_t s) {
-  if (I % 32 || H % 32) return hipErrorInvalidValue;
+  if (I % 32 || H % 32 || (lora_At && !lora_rank_ok(lora_r))) return hipErrorInvalidValue;
   dim3 grid(((H + GO - 1) / GO) * max_tiles);
-  hipLaunchKernelGGL(bwd_gate_up_kernel, grid, dim3(GTHR), 0, s, dh, codes, scales, sorted_rows,
-                     tiles, num_tiles, H, I, dxr);
+  if (lora_At)
+    hipLaunchKernelGGL(bwd_gate_up_kernel<true>, grid, dim3(GTHR), 0, s, dh, codes, scales,
+                       sorted_rows, tiles, num_tiles, H, I, lora_At, lora_dv, lora_r, dxr);
+  else
+    hipLaunchKernelGGL(bwd_gate_up_kernel<false>, grid, dim3(GTHR), 0, s, dh, codes, scales,
+                       sorted_rows, tiles, num_tiles, H, I, lora_At, lora_dv, 0, dxr);
   return hipGetLastError();
 }
 

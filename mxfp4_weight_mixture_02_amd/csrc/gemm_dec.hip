@@ -139,9 +139,9 @@ __global__ __launch_bounds__(512) void dec_kernel(
         dec_issue(b0, wrow, min(ch + 2, nch - 1), nsteps, ztail);
         dec_compute(b1, xb, srow, smax, ch + 1, nsteps, acc);
       }
-      if (!GATE_UP && lora_B) {
-        // + s v B_e^T over the rank (as the down GEMM): A-operand = B_e row
-        // n, B-operand column l32 = the group row it repeats
+      if (lora_B) {
+        // + s v B_e^T over the rank (as the GEMMs' adapter term): A-operand
+        // = B_e row n, B-operand column l32 = the group row it repeats
         const float* vrow = lora_v + (int64_t)(tl.row0 + g0 + min(l32 % DG, ng - 1)) * lora_r;
         const uint16_t* brow = lora_B + ((int64_t)e * N + n) * lora_r;
         for (int j = 0; j < lora_chunks(lora_r); ++j) {
@@ -276,7 +276,7 @@ __global__ __launch_bounds__(64 * KW) void dec_ksplit_kernel(
         }
       }
     }
-    if (!GATE_UP && lora_B && wave == 0) {
+    if (lora_B && wave == 0) {
       // + s v B_e^T over the rank, added to one wave's partial sum
       const float* vrow = lora_v + (int64_t)(tl.row0 + g0 + min(l32 % DG, ng - 1)) * lora_r;
       const uint16_t* brow = lora_B + ((int64_t)e * N + n) * lora_r;
@@ -395,11 +395,12 @@ static hipError_t dec_launch(int64_t R, int max_tiles, int K, int N, hipStream_t
 hipError_t launch_dec_gate_up(const uint16_t* x, const uint8_t* codes, const uint8_t* scales,
                               const uint16_t* bias, const int32_t* sorted_rows, const Tile* tiles,
                               const int32_t* num_tiles, int max_tiles, int64_t R, int H, int I, int k,
-                              float alpha, float limit, uint16_t* h_out, uint16_t* a_out,
-                              hipStream_t s) {
+                              float alpha, float limit, const uint16_t* lora_B,
+                              const float* lora_v, float lora_scale, int lora_r, uint16_t* h_out,
+                              uint16_t* a_out, hipStream_t s) {
   return dec_launch<true>(R, max_tiles, H, 2 * I, s, x, codes, scales, bias, nullptr, sorted_rows,
-                          tiles, num_tiles, k, alpha, limit, h_out, a_out, nullptr, nullptr,
-                          nullptr, 0.0f, 0);
+                          tiles, num_tiles, k, alpha, limit, h_out, a_out, nullptr, lora_B, lora_v,
+                          lora_scale, lora_r);
 }
 
 hipError_t launch_dec_down(const uint16_t* a, const uint8_t* codes, const uint8_t* scales,

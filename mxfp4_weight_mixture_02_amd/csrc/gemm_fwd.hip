@@ -334,15 +334,46 @@ __device__ __forceinline__ void load_bias_rows(const uint16_t* __restrict__ bias
         bv[rb][q][i] = bf16_to_f32((uint16_t)(raw[rb][q][i >> 1] >> (16 * (i & 1))));
 }
 
+// + s v B_e^T, an adapter's rank-r delta, into the accumulators: 16-deep
+// contractions over the rank, A-operand = B_e rows (this lane's weight
+// rows, [N, r] per expert), B-operand = s v as hi + lo bf16 (v [R, r] in
+// sorted order); one token block at a time to keep few registers live.
+__device__ __forceinline__ void lora_delta(f32x16 (&acc)[FRB][4], const Tile& tl, int e, int N,
+                                           int n0, int nrows, int wrow_local,
+                                           const uint16_t* __restrict__ lora_B,
+                                           const float* __restrict__ lora_v, float lora_scale,
+                                           int lora_r) {
+  const int lane = threadIdx.x & 63;
+  const int l32 = lane & 31, hlf = lane >> 5;
+  for (int j = 0; j < lora_chunks(lora_r); ++j) {
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      bf16x8 vh, vl;
+      lora_frag_split(lora_v + (int64_t)(tl.row0 + min(tb * 32 + l32, tl.rows - 1)) * lora_r,
+                      lora_r, j, hlf, lora_scale, &vh, &vl);
+#pragma unroll
+      for (int rb = 0; rb < FRB; ++rb) {
+        const int r = min(wrow_local + 32 * rb, nrows - 1);
+        const bf16x8 bw = lora_frag(lora_B + ((int64_t)e * N + n0 + r) * lora_r, lora_r, j, hlf);
+        acc[rb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bw, vh, acc[rb][tb], 0, 0, 0);
+        acc[rb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bw, vl, acc[rb][tb], 0, 0, 0);
+      }
+    }
+  }
+}
+
 // Two waves per SIMD in either shape (amdgpu_waves_per_eu keeps the W = 4
 // kernel within the registers of two waves, so two workgroups fit a CU).
-template <int W>
+// LORA: add the gate_up adapter's rank-r delta s (vg B_gu^T) before the
+// bias, as the down GEMM adds its adapter's.
+template <int W, bool LORA>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2, 2))) void gate_up_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, const uint16_t* __restrict__ bias,
     const int32_t* __restrict__ sorted_rows, const Tile* __restrict__ tiles,
     const int32_t* __restrict__ num_tiles, int H, int I, int k, float alpha, float limit,
-    uint16_t* __restrict__ h_out, uint16_t* __restrict__ a_out) {
+    const uint16_t* __restrict__ lora_B, const float* __restrict__ lora_v, float lora_scale,
+    int lora_r, uint16_t* __restrict__ h_out, uint16_t* __restrict__ a_out) {
   using S = FwdShape<W>;
   constexpr int XCHUNKS = S::XCH, FNT = S::NT;
   __shared__ __attribute__((aligned(16))) uint8_t lds[S::LDS];
@@ -364,9 +395,10 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   }
   const int nrows = min(FNT, N - n0);
   f32x16 acc[FRB][4];
+  const int wrow_local = (wave * 32 * FRB < nrows ? wave * 32 * FRB : 0) + l32;
   fwd_body<W>(x, xrow, codes + (int64_t)e * N * (H / 2), scales + (int64_t)e * N * (H / 32), H, n0,
-           nrows, (wave * 32 * FRB < nrows ? wave * 32 * FRB : 0) + l32, (tl.rows + 31) / 32, lds,
-           acc);
+           nrows, wrow_local, (tl.rows + 31) / 32, lds, acc);
+  if (LORA) lora_delta(acc, tl, e, N, n0, nrows, wrow_local, lora_B, lora_v, lora_scale, lora_r);
   // Epilogue through LDS: every wave's loads have landed (fwd_loop drained
   // them) and every wave is past its last stage read.
   barrier_only();
@@ -453,26 +485,7 @@ __global__ __launch_bounds__(FwdShape<8>::NTHR) void down_kernel(
   const int wrow_local = (wave * 32 * FRB < nrows ? wave * 32 * FRB : 0) + l32;
   fwd_body<8>(a + (int64_t)tl.row0 * I, xrow, codes + (int64_t)e * N * (I / 2), scales + (int64_t)e * N * (I / 32), I, n0,
            nrows, wrow_local, (tl.rows + 31) / 32, lds, acc);
-  if (LORA) {
-    // + s v B_e^T: 16-deep contractions over the rank, A-operand = B_e rows
-    // (this lane's weight rows), B-operand = s v as hi + lo bf16; one token
-    // block at a time to keep few registers live
-    for (int j = 0; j < lora_chunks(lora_r); ++j) {
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
-        bf16x8 vh, vl;
-        lora_frag_split(lora_v + (int64_t)(tl.row0 + min(tb * 32 + l32, tl.rows - 1)) * lora_r,
-                        lora_r, j, hlf, lora_scale, &vh, &vl);
-#pragma unroll
-        for (int rb = 0; rb < FRB; ++rb) {
-          const int r = min(wrow_local + 32 * rb, nrows - 1);
-          const bf16x8 bw = lora_frag(lora_B + ((int64_t)e * N + n0 + r) * lora_r, lora_r, j, hlf);
-          acc[rb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bw, vh, acc[rb][tb], 0, 0, 0);
-          acc[rb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bw, vl, acc[rb][tb], 0, 0, 0);
-        }
-      }
-    }
-  }
+  if (LORA) lora_delta(acc, tl, e, N, n0, nrows, wrow_local, lora_B, lora_v, lora_scale, lora_r);
   barrier_only();   // as in gate_up: LDS is free for the epilogue
   const int wcol = wave * 32 * FRB;
   if (n0 + wcol >= N) return;
@@ -543,20 +556,22 @@ int fwd_step_k(int K) { return (K % 32 == 0 && K <= FwdShape<8>::MAXK) ? FKS : 0
 hipError_t launch_gate_up(const uint16_t* x, const uint8_t* codes, const uint8_t* scales,
                           const uint16_t* bias, const int32_t* sorted_rows, const Tile* tiles,
                           const int32_t* num_tiles, int max_tiles, int H, int I, int k,
-                          float alpha, float limit, uint16_t* h_out, uint16_t* a_out,
+                          float alpha, float limit, const uint16_t* lora_B, const float* lora_v,
+                          float lora_scale, int lora_r, uint16_t* h_out, uint16_t* a_out,
                           hipStream_t s) {
-  if (!fwd_step_k(H)) return hipErrorInvalidValue;
+  if (!fwd_step_k(H) || (lora_B && !lora_rank_ok(lora_r))) return hipErrorInvalidValue;
+#define GATE_UP(W, LORA)                                                                         \
+  hipLaunchKernelGGL((gate_up_kernel<W, LORA>),                                                  \
+                     dim3(((2 * I + FwdShape<W>::NT - 1) / FwdShape<W>::NT) * max_tiles),         \
+                     dim3(FwdShape<W>::NTHR), 0, s, x, codes, scales, bias, sorted_rows, tiles,   \
+                     num_tiles, H, I, k, alpha, limit, lora_B, lora_v, lora_scale, lora_r, h_out, \
+                     a_out)
   if (H <= FwdShape<4>::MAXK) {
-    using S = FwdShape<4>;
-    hipLaunchKernelGGL(gate_up_kernel<4>, dim3(((2 * I + S::NT - 1) / S::NT) * max_tiles),
-                       dim3(S::NTHR), 0, s, x, codes, scales, bias, sorted_rows, tiles, num_tiles,
-                       H, I, k, alpha, limit, h_out, a_out);
+    if (lora_B) GATE_UP(4, true); else GATE_UP(4, false);
   } else {
-    using S = FwdShape<8>;
-    hipLaunchKernelGGL(gate_up_kernel<8>, dim3(((2 * I + S::NT - 1) / S::NT) * max_tiles),
-                       dim3(S::NTHR), 0, s, x, codes, scales, bias, sorted_rows, tiles, num_tiles,
-                       H, I, k, alpha, limit, h_out, a_out);
+    if (lora_B) GATE_UP(8, true); else GATE_UP(8, false);
   }
+#undef GATE_UP
   return hipGetLastError();
 }
 

@@ -48,10 +48,13 @@ hipError_t launch_build_tiles(const int32_t* offsets, int E, int mt, Tile* tiles
 
 // gemm_fwd.hip
 int fwd_step_k(int K);   // K step of the forward GEMMs for contraction length K; 0 = unsupported
+// with lora_B: + the gate_up adapter's rank-r delta s (v B_gu^T) before the
+// bias (v [R, r] sorted, B_gu [E, 2I, r])
 hipError_t launch_gate_up(const uint16_t* x, const uint8_t* codes, const uint8_t* scales,
                           const uint16_t* bias, const int32_t* sorted_rows, const Tile* tiles,
                           const int32_t* num_tiles, int max_tiles, int H, int I, int k,
-                          float alpha, float limit, uint16_t* h_out, uint16_t* a_out,
+                          float alpha, float limit, const uint16_t* lora_B, const float* lora_v,
+                          float lora_scale, int lora_r, uint16_t* h_out, uint16_t* a_out,
                           hipStream_t s);
 // lora_B/lora_v/lora_scale/lora_r: the rank-r delta s (v B_e^T) added
 // before the bias (lora_B == nullptr: none).
@@ -68,8 +71,9 @@ int dec_max_k();   // largest contraction length the decode kernels take
 hipError_t launch_dec_gate_up(const uint16_t* x, const uint8_t* codes, const uint8_t* scales,
                               const uint16_t* bias, const int32_t* sorted_rows, const Tile* tiles,
                               const int32_t* num_tiles, int max_tiles, int64_t R, int H, int I, int k,
-                              float alpha, float limit, uint16_t* h_out, uint16_t* a_out,
-                              hipStream_t s);
+                              float alpha, float limit, const uint16_t* lora_B,
+                              const float* lora_v, float lora_scale, int lora_r, uint16_t* h_out,
+                              uint16_t* a_out, hipStream_t s);
 // with lora_B: + the rank-r delta s (v B_e^T), as launch_down
 hipError_t launch_dec_down(const uint16_t* a, const uint8_t* codes, const uint8_t* scales,
                            const uint16_t* bias, const float* topk_w, const int32_t* sorted_rows,
@@ -85,9 +89,12 @@ hipError_t launch_bwd_down(const uint16_t* dy, const uint8_t* codes, const uint8
                            const uint16_t* a, int H, int I, int k, float alpha, float limit,
                            const uint16_t* lora_At, const float* lora_dvu, int lora_r,
                            uint16_t* dh, float* dw_part, hipStream_t s);
+// with lora_At: + the gate_up adapter's input-gradient term dv_g A_gu
+// (lora_At = A_gu transposed, [E, H, r]; dv_g [R, r] sorted)
 hipError_t launch_bwd_gate_up(const uint16_t* dh, const uint8_t* codes, const uint8_t* scales,
                               const int32_t* sorted_rows, const Tile* tiles,
                               const int32_t* num_tiles, int max_tiles, int H, int I,
+                              const uint16_t* lora_At, const float* lora_dv, int lora_r,
                               uint16_t* dxr, hipStream_t s);
 hipError_t launch_bwd_combine(const uint16_t* dy, const uint16_t* dxr, const float* dw_part,
                               int n_dw_part, const int32_t* topk_idx, const float* topk_w,

@@ -118,7 +118,8 @@ __global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __r
 }
 
 // G[e][c][j] = sum over the sorted rows p of expert e of
-// (scale * topk_w[sorted_rows[p]] * P[p][j]) * Q[row(p)][c], written to
+// (scale * topk_w[sorted_rows[p]] * P[p][j]) * Q[row(p)][c] (topk_w NULL:
+// no routing weight), written to
 // out[e * e_stride + c * c_stride + j * j_stride]; row(p) as in lora_proj,
 // P [R, r].  A workgroup takes 128 columns of one expert and 16 rank
 // columns 16 z .. (blockIdx.z; past r: zeros, not written): lane l of each
@@ -163,7 +164,7 @@ __global__ __launch_bounds__(256) void lora_grad_kernel(
       f32x4 v[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) v[q] = 4 * q < nj ? *reinterpret_cast<const f32x4*>(pr + 4 * q) : z;
-      const float w = lane < n ? scale * topk_w[f] : 0.0f;
+      const float w = lane < n ? (topk_w ? scale * topk_w[f] : scale) : 0.0f;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         f32x4 t;

@@ -33,18 +33,21 @@ class Dims(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int64), ("H", ctypes.c_int64), ("I", ctypes.c_int64),
                 ("E", ctypes.c_int32), ("k", ctypes.c_int32),
                 ("swiglu_alpha", ctypes.c_float), ("swiglu_limit", ctypes.c_float),
-                ("lora_rank", ctypes.c_int32), ("lora_scale", ctypes.c_float)]
+                ("lora_rank", ctypes.c_int32), ("lora_scale", ctypes.c_float),
+                ("lora_targets", ctypes.c_int32)]
+
+LORA_DOWN, LORA_GATE_UP = 1, 2
 
 
 class Weights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("router_w", "router_b", "gu_codes", "gu_scales", "gu_bias",
-                 "dn_codes", "dn_scales", "dn_bias", "lora_A", "lora_B")]
+                 "dn_codes", "dn_scales", "dn_bias", "lora_A", "lora_B", "lora_gu_A", "lora_gu_B")]
 
 
 class Saved(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
-                ("topk_idx", "topk_w", "expert_offsets", "sorted_rows", "h", "a", "lora_v")]
+                ("topk_idx", "topk_w", "expert_offsets", "sorted_rows", "h", "a", "lora_v", "lora_vg")]
 
 
 class SavedSizes(ctypes.Structure):
@@ -77,8 +80,8 @@ def lib() -> ctypes.CDLL:
                                                 vp, ctypes.POINTER(Saved), vp]
         L.mxfp4_moe_backward_dx.restype = i32
         L.mxfp4_moe_backward_dx.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Weights),
-                                            ctypes.POINTER(Saved), vp, vp, vp, vp, vp,
-                                            ctypes.c_size_t, vp]
+                                            ctypes.POINTER(Saved), vp, vp, vp, vp, vp, vp, vp,
+                                            vp, ctypes.c_size_t, vp]
         L.mxfp4_quantize.restype = i32
         L.mxfp4_quantize.argtypes = [vp, i64, i64, vp, vp, vp]
         L.mxfp4_dequantize.restype = i32
@@ -168,9 +171,11 @@ class MoeLayer:
     k: int
     alpha: float = 1.702
     limit: float = 7.0
-    lora_A: torch.Tensor | None = None
-    lora_B: torch.Tensor | None = None
+    lora_A: torch.Tensor | None = None       # bf16 [E, r, I]   adapter on down
+    lora_B: torch.Tensor | None = None       # bf16 [E, H, r]
     lora_scale: float = 1.0
+    lora_gu_A: torch.Tensor | None = None    # bf16 [E, r, H]   adapter on gate_up
+    lora_gu_B: torch.Tensor | None = None    # bf16 [E, 2I, r]
 
     @property
     def E(self):
@@ -184,9 +189,20 @@ class MoeLayer:
     def I(self):
         return self.gu_codes.shape[1] // 2
 
+    @property
+    def lora_rank(self):
+        if self.lora_A is not None:
+            return self.lora_A.shape[1]
+        return 0 if self.lora_gu_A is None else self.lora_gu_A.shape[1]
+
+    @property
+    def lora_targets(self):
+        return (LORA_DOWN if self.lora_A is not None else 0) | \
+               (LORA_GATE_UP if self.lora_gu_A is not None else 0)
+
     def dims(self, T):
-        r = 0 if self.lora_A is None else self.lora_A.shape[1]
-        return Dims(T, self.H, self.I, self.E, self.k, self.alpha, self.limit, r, self.lora_scale)
+        return Dims(T, self.H, self.I, self.E, self.k, self.alpha, self.limit, self.lora_rank,
+                    self.lora_scale, self.lora_targets)
 
     def check_shapes(self):
         """Every parameter's shape and dtype against E, H, I (and the rank)."""
@@ -210,6 +226,14 @@ class MoeLayer:
             r = self.lora_A.shape[1]
             _shape(self.lora_A, (E, r, I), bf, "lora_A")
             _shape(self.lora_B, (E, H, r), bf, "lora_B")
+        if (self.lora_gu_A is None) != (self.lora_gu_B is None):
+            raise ValueError("lora_gu_A and lora_gu_B go together")
+        if self.lora_gu_A is not None:
+            if self.lora_gu_A.dim() != 3:
+                raise ValueError(f"lora_gu_A must be [E, r, H], got {tuple(self.lora_gu_A.shape)}")
+            r = self.lora_rank   # one rank for both adapters
+            _shape(self.lora_gu_A, (E, r, H), bf, "lora_gu_A")
+            _shape(self.lora_gu_B, (E, 2 * I, r), bf, "lora_gu_B")
 
     def weights(self):
         self.check_shapes()
@@ -217,7 +241,7 @@ class MoeLayer:
         _dev(self.router_b, torch.float32, "router_b")
         for n in ("gu_codes", "gu_scales", "dn_codes", "dn_scales"):
             _dev(getattr(self, n), torch.uint8, n)
-        for n in ("gu_bias", "dn_bias", "lora_A", "lora_B"):
+        for n in ("gu_bias", "dn_bias", "lora_A", "lora_B", "lora_gu_A", "lora_gu_B"):
             _dev(getattr(self, n), torch.bfloat16, n)
         return Weights(*[_ptr(getattr(self, n)) for n, _ in Weights._fields_])
 
@@ -230,18 +254,19 @@ class SavedState:
     sorted_rows: torch.Tensor    # int32 [T*k]
     h: torch.Tensor              # bf16 [T*k, 2I]
     a: torch.Tensor              # bf16 [T*k, I]
-    lora_v: torch.Tensor | None = None
+    lora_v: torch.Tensor | None = None    # fp32 [T*k, r] with the down adapter
+    lora_vg: torch.Tensor | None = None   # fp32 [T*k, r] with the gate_up adapter
 
     @staticmethod
     def empty(layer: MoeLayer, T: int, device):
         """Caller-owned buffers of the sizes mxfp4_moe_saved_bytes gives."""
         R = T * layer.k
-        r = 0 if layer.lora_A is None else layer.lora_A.shape[1]
+        r = layer.lora_rank
         nbytes = saved_bytes(layer, T)
         shapes = {"topk_idx": ((T, layer.k), torch.int32), "topk_w": ((T, layer.k), torch.float32),
                   "expert_offsets": ((layer.E + 1,), torch.int32), "sorted_rows": ((R,), torch.int32),
                   "h": ((R, 2 * layer.I), torch.bfloat16), "a": ((R, layer.I), torch.bfloat16),
-                  "lora_v": ((R, r), torch.float32)}
+                  "lora_v": ((R, r), torch.float32), "lora_vg": ((R, r), torch.float32)}
         bufs = {}
         for n, (shape, dt) in shapes.items():
             if nbytes[n] == 0:
@@ -256,14 +281,16 @@ class SavedState:
     def check_shapes(self, layer: MoeLayer, T: int):
         """Every buffer against the sizes a call with T tokens uses."""
         R = T * layer.k
-        r = 0 if layer.lora_A is None else layer.lora_A.shape[1]
+        r = layer.lora_rank
         _shape(self.topk_idx, (T, layer.k), torch.int32, "saved.topk_idx")
         _shape(self.topk_w, (T, layer.k), torch.float32, "saved.topk_w")
         _shape(self.expert_offsets, (layer.E + 1,), torch.int32, "saved.expert_offsets")
         _shape(self.sorted_rows, (R,), torch.int32, "saved.sorted_rows")
         _shape(self.h, (R, 2 * layer.I), torch.bfloat16, "saved.h")
         _shape(self.a, (R, layer.I), torch.bfloat16, "saved.a")
-        _shape(self.lora_v, (R, r), torch.float32, "saved.lora_v", optional=(r == 0))
+        _shape(self.lora_v, (R, r), torch.float32, "saved.lora_v", optional=(layer.lora_A is None))
+        _shape(self.lora_vg, (R, r), torch.float32, "saved.lora_vg",
+               optional=(layer.lora_gu_A is None))
 
     def struct(self):
         for n, _ in Saved._fields_:
@@ -362,9 +389,13 @@ def mxfp4_moe_forward_noalloc(layer: MoeLayer, x: torch.Tensor, out: torch.Tenso
 
 def mxfp4_moe_backward_dx(layer: MoeLayer, saved: SavedState, dy: torch.Tensor,
                           dx: torch.Tensor | None = None, workspace: Workspace | None = None,
-                          dA: torch.Tensor | None = None, dB: torch.Tensor | None = None):
-    """dX (and, with LoRA, dA/dB, overwritten) for the loss sum(dy * out).
-    Returns (dx, dA, dB)."""
+                          dA: torch.Tensor | None = None, dB: torch.Tensor | None = None,
+                          x: torch.Tensor | None = None, dA_gu: torch.Tensor | None = None,
+                          dB_gu: torch.Tensor | None = None):
+    """dX (and the adapter gradients, overwritten) for the loss sum(dy * out).
+    ``x`` (the forward's input) is needed only with the gate_up adapter.
+    Returns (dx, dA, dB), plus (dA_gu, dB_gu) when the layer has a gate_up
+    adapter."""
     layer.check_shapes()
     if dy.dim() != 2:
         raise ValueError(f"dy must be [T, H], got {tuple(dy.shape)}")
@@ -373,32 +404,44 @@ def mxfp4_moe_backward_dx(layer: MoeLayer, saved: SavedState, dy: torch.Tensor,
     if dx is not None:
         _shape(dx, (T, layer.H), torch.bfloat16, "dx")
     saved.check_shapes(layer, T)
-    lora = layer.lora_A is not None
-    if lora:
-        if dA is not None:
-            _shape(dA, tuple(layer.lora_A.shape), torch.float32, "dA")
-        if dB is not None:
-            _shape(dB, tuple(layer.lora_B.shape), torch.float32, "dB")
+    grads = {}
+    for name, base, on in (("dA", layer.lora_A, True), ("dB", layer.lora_B, True),
+                           ("dA_gu", layer.lora_gu_A, True), ("dB_gu", layer.lora_gu_B, True)):
+        g = {"dA": dA, "dB": dB, "dA_gu": dA_gu, "dB_gu": dB_gu}[name]
+        if base is None:
+            grads[name] = None
+            continue
+        if g is not None:
+            _shape(g, tuple(base.shape), torch.float32, name)
+        grads[name] = g
+    gu = layer.lora_gu_A is not None
+    if gu:
+        if x is None:
+            raise ValueError("x (the forward's input) is required with the gate_up adapter")
+        _shape(x, (T, layer.H), torch.bfloat16, "x")
     dy = _dev(dy, torch.bfloat16, "dy")
     if dx is None:
         dx = torch.empty_like(dy)
     _dev(dx, torch.bfloat16, "dx")
-    if lora:
-        if dA is None:
-            dA = torch.empty(layer.lora_A.shape, dtype=torch.float32, device=dy.device)
-        if dB is None:
-            dB = torch.empty(layer.lora_B.shape, dtype=torch.float32, device=dy.device)
-        _dev(dA, torch.float32, "dA")
-        _dev(dB, torch.float32, "dB")
-    else:
-        dA = dB = None
+    if gu:
+        _dev(x, torch.bfloat16, "x")
+    for name, base in (("dA", layer.lora_A), ("dB", layer.lora_B), ("dA_gu", layer.lora_gu_A),
+                       ("dB_gu", layer.lora_gu_B)):
+        if base is None:
+            continue
+        if grads[name] is None:
+            grads[name] = torch.empty(base.shape, dtype=torch.float32, device=dy.device)
+        _dev(grads[name], torch.float32, name)
     nbytes = workspace_bytes(layer, T, WS_BACKWARD)
     ws = (workspace or _WS).get(nbytes, dy.device)
     d = layer.dims(T)
     w = layer.weights()
     sv = saved.struct()
     rc = lib().mxfp4_moe_backward_dx(ctypes.byref(d), ctypes.byref(w), ctypes.byref(sv),
-                                     _ptr(dy), _ptr(dx), _ptr(dA), _ptr(dB), _ptr(ws),
-                                     ws.numel(), _stream())
+                                     _ptr(x if gu else None), _ptr(dy), _ptr(dx),
+                                     _ptr(grads["dA"]), _ptr(grads["dB"]), _ptr(grads["dA_gu"]),
+                                     _ptr(grads["dB_gu"]), _ptr(ws), ws.numel(), _stream())
     _check("mxfp4_moe_backward_dx", rc)
-    return dx, dA, dB
+    if gu:
+        return dx, grads["dA"], grads["dB"], grads["dA_gu"], grads["dB_gu"]
+    return dx, grads["dA"], grads["dB"]

@@ -66,9 +66,12 @@ def device_layer(s, with_bias=True, threads=8, experts=None):
         dn_codes=dn_c, dn_scales=dn_s,
         dn_bias=bf16_tensor(syn.down_bias(s)).to(DEV) if with_bias else None,
         k=s.k, alpha=s.swiglu_alpha, limit=s.swiglu_limit)
-    if s.lora_rank:
+    if s.lora_rank and s.lora_down:
         L.lora_A = bf16_tensor(syn.lora_a(s)).to(DEV)
         L.lora_B = bf16_tensor(syn.lora_b(s)).to(DEV)
+    if s.lora_rank and s.lora_gate_up:
+        L.lora_gu_A = bf16_tensor(syn.lora_gu_a(s)).to(DEV)
+        L.lora_gu_B = bf16_tensor(syn.lora_gu_b(s)).to(DEV)
     return L
 
 

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol(L):
 
 def _dims(**kw):
     d = dict(T=16, H=64, I=64, E=4, k=2, swiglu_alpha=1.702, swiglu_limit=7.0, lora_rank=0,
-             lora_scale=1.0)
+             lora_scale=1.0, lora_targets=0)
     d.update(kw)
     return Dims(**d)
 
@@ -147,12 +147,12 @@ def test_backward_validation(L):
     d = _dims()
     w = _weights()
     ws = L.mxfp4_moe_workspace_bytes(ctypes.byref(d), 2)
-    rc = L.mxfp4_moe_backward_dx(ctypes.byref(d), ctypes.byref(w), None, FAKE, FAKE, None, None,
-                                 FAKE, ws, None)
+    rc = L.mxfp4_moe_backward_dx(ctypes.byref(d), ctypes.byref(w), None, None, FAKE, FAKE, None,
+                                 None, None, None, FAKE, ws, None)
     assert rc == -1 and "saved" in _err(L)
     sv = Saved(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0)
-    rc = L.mxfp4_moe_backward_dx(ctypes.byref(d), ctypes.byref(w), ctypes.byref(sv), FAKE, FAKE,
-                                 None, None, FAKE, 0, None)
+    rc = L.mxfp4_moe_backward_dx(ctypes.byref(d), ctypes.byref(w), ctypes.byref(sv), None, FAKE,
+                                 FAKE, None, None, None, None, FAKE, 0, None)
     assert rc == -3
 
 
@@ -206,8 +206,8 @@ def test_lora_validation(L):
     assert rc == -1 and "lora_v" in _err(L)
     # backward without dA/dB
     sv = Saved(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
-    rc = L.mxfp4_moe_backward_dx(ctypes.byref(d), ctypes.byref(w), ctypes.byref(sv), FAKE, FAKE,
-                                 None, FAKE, FAKE, b, None)
+    rc = L.mxfp4_moe_backward_dx(ctypes.byref(d), ctypes.byref(w), ctypes.byref(sv), None, FAKE,
+                                 FAKE, None, FAKE, None, None, FAKE, b, None)
     assert rc == -1 and "dA and dB" in _err(L)
 
 
@@ -219,3 +219,45 @@ def test_odd_multiples_of_32_are_accepted(L, H, I):
         assert L.mxfp4_moe_workspace_bytes(ctypes.byref(d), mode) > 0, _err(L)
     z = SavedSizes()
     assert L.mxfp4_moe_saved_bytes(ctypes.byref(d), ctypes.byref(z)) == 0
+
+
+def test_gate_up_adapter_validation(L):
+    # lora_targets selects the adapted projections; the gate_up adapter
+    # needs its own pair, saved vg, its two gradients and the forward's x
+    both = _dims(lora_rank=16, lora_targets=3)
+    down = _dims(lora_rank=16, lora_targets=1)
+    gu = _dims(lora_rank=16, lora_targets=2)
+    for mode in (0, 2):
+        assert L.mxfp4_moe_workspace_bytes(ctypes.byref(both), mode) > \
+            L.mxfp4_moe_workspace_bytes(ctypes.byref(down), mode) > 0
+        assert L.mxfp4_moe_workspace_bytes(ctypes.byref(gu), mode) > 0
+    assert L.mxfp4_moe_workspace_bytes(ctypes.byref(_dims(lora_rank=16, lora_targets=4)), 0) == 0
+    assert "lora_targets" in _err(L)
+    z = SavedSizes()
+    assert L.mxfp4_moe_saved_bytes(ctypes.byref(gu), ctypes.byref(z)) == 0
+    R = 16 * 2
+    assert (z.lora_v, z.lora_vg) == (0, 4 * R * 16)
+    assert L.mxfp4_moe_saved_bytes(ctypes.byref(both), ctypes.byref(z)) == 0
+    assert (z.lora_v, z.lora_vg) == (4 * R * 16, 4 * R * 16)
+    f0 = L.mxfp4_moe_workspace_bytes(ctypes.byref(gu), 0)
+    rc = L.mxfp4_moe_forward(ctypes.byref(gu), ctypes.byref(_weights()), FAKE, FAKE, None, FAKE,
+                             f0, None)
+    assert rc == -1 and "lora_gu_A" in _err(L)
+    rc = L.mxfp4_moe_forward(ctypes.byref(down), ctypes.byref(_weights(lora_A=FAKE, lora_B=FAKE,
+                                                                        lora_gu_A=FAKE, lora_gu_B=FAKE)),
+                             FAKE, FAKE, None, FAKE, f0, None)
+    assert rc == -1 and "gate_up is not a lora target" in _err(L)
+    w = _weights(lora_gu_A=FAKE, lora_gu_B=FAKE)
+    f1 = L.mxfp4_moe_workspace_bytes(ctypes.byref(gu), 1)
+    sv = Saved(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 0)
+    rc = L.mxfp4_moe_forward(ctypes.byref(gu), ctypes.byref(w), FAKE, FAKE, ctypes.byref(sv),
+                             FAKE, f1, None)
+    assert rc == -1 and "lora_vg" in _err(L)
+    b = L.mxfp4_moe_workspace_bytes(ctypes.byref(gu), 2)
+    sv = Saved(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE)
+    rc = L.mxfp4_moe_backward_dx(ctypes.byref(gu), ctypes.byref(w), ctypes.byref(sv), None, FAKE,
+                                 FAKE, None, None, FAKE, None, FAKE, b, None)
+    assert rc == -1 and "dA_gu and dB_gu" in _err(L)
+    rc = L.mxfp4_moe_backward_dx(ctypes.byref(gu), ctypes.byref(w), ctypes.byref(sv), None, FAKE,
+                                 FAKE, None, None, FAKE, FAKE, FAKE, b, None)
+    assert rc == -1 and "x (the forward's input)" in _err(L)

@@ -111,20 +111,29 @@ def _run_layer(s, x_scale=1.0, with_bias=True, backward=True, T=None, lora_scale
     aref = np.stack([cache[int(f)][1] for f in rows])
     assert_close(to_f64(sv.h), href, "saved h")
     assert_close(to_f64(sv.a), aref, "saved a")
-    if s.lora_rank:
+    if ol.has_lora:
         ex = np.searchsorted(r.offsets, np.arange(T * s.k), side="right") - 1
         vref = np.stack([moe._lora_v(ol, ex[i], aref[i][None])[0] for i in range(T * s.k)])
         assert_close(to_f64(sv.lora_v), vref, "saved lora_v")
+    if ol.has_lora_gu:
+        vgref = np.stack([cache[int(f)][3] for f in rows])
+        assert_close(to_f64(sv.lora_vg), vgref, "saved lora_vg")
     res = {"out": out, "saved": sv, "routing": r}
     if backward:
         dyb = syn.upstream_grad(s, T)
-        dx, dA, dB = mxfp4_moe_backward_dx(dl, sv, bf16_tensor(dyb).to(DEV))
+        got = mxfp4_moe_backward_dx(dl, sv, bf16_tensor(dyb).to(DEV), x=x)
         torch.cuda.synchronize()
-        dref, dAref, dBref = moe.backward_dx(ol, xb, dyb)
+        g = {}
+        dref, dAref, dBref = moe.backward_dx(ol, xb, dyb, gu_grads=g)
+        dx, dA, dB = got[:3]
         assert_close(to_f64(dx), dref, "dX")
-        if s.lora_rank:
+        if ol.has_lora:
             assert_close(to_f64(dA), dAref, "dA")
             assert_close(to_f64(dB), dBref, "dB")
+        if ol.has_lora_gu:
+            assert len(got) == 5
+            assert_close(to_f64(got[3]), g["dA_gu"], "dA_gu")
+            assert_close(to_f64(got[4]), g["dB_gu"], "dB_gu")
         res["dx"] = dx
     return res
 
@@ -261,6 +270,17 @@ def test_lora_at_decode_sizes(T, r):
     # 32 for H and I on the way
     _say(f"lora decode T={T} r={r}")
     _run_layer(syn.spec("tiny", T=T, H=96, I=160, E=3, k=2, lora_rank=r), lora_scale=4.0)
+
+
+@pytest.mark.parametrize("T,r,down", [(300, 16, True), (300, 8, False), (100, 64, True),
+                                      (5, 32, True), (40, 16, False)])
+def test_lora_on_gate_up(T, r, down):
+    # the adapter on gate_up, alone or with the down one: forward (saved vg,
+    # the GEMM and decode epilogues), dX's adapter term in bwd_gate_up, and
+    # dA_gu / dB_gu; T = 5 and 40 run the decode kernels
+    _say(f"gate_up lora T={T} r={r} down={down}")
+    _run_layer(syn.spec("tiny", T=T, H=192, I=320, E=3, k=2, lora_rank=r, lora_gate_up=True,
+                        lora_down=down), lora_scale=4.0)
 
 
 def test_forward_is_deterministic():
