@@ -62,6 +62,10 @@ class Layer:
     lora_scale: float = 1.0
     lora_gu_A: np.ndarray | None = None
     lora_gu_B: np.ndarray | None = None
+    #: float64 weights used instead of the dequantized codes ([E, 2I, H] and
+    #: [E, H, I]); only for finite-difference probes of the weight gradients
+    gu_weight: np.ndarray | None = None
+    dn_weight: np.ndarray | None = None
     #: precision the logits are rounded to before the top-k decision;
     #: float64 only for finite-difference probes of the router path
     logit_dtype: type = np.float32
@@ -80,10 +84,14 @@ class Layer:
 
     def gate_up(self, e):
         """Dequantized gate_up weight of expert e, float64 [2I, H]."""
+        if self.gu_weight is not None:
+            return self.gu_weight[e]
         return mxfp4.dequantize(self.gu_codes[e], self.gu_scales[e])
 
     def down(self, e):
         """Dequantized down weight of expert e, float64 [H, I]."""
+        if self.dn_weight is not None:
+            return self.dn_weight[e]
         return mxfp4.dequantize(self.dn_codes[e], self.dn_scales[e])
 
     def gu_b(self, e):
@@ -279,7 +287,8 @@ def forward(layer: Layer, x_bits, tokens=None, routing: Routing | None = None, e
 # ---------------------------------------------------------------- backward
 
 def backward_dx(layer: Layer, x_bits, dy_bits, tokens=None, routing: Routing | None = None,
-                want_lora=True, experts=None, gu_grads: dict | None = None):
+                want_lora=True, experts=None, gu_grads: dict | None = None,
+                base_grads: dict | None = None):
     """Gradient of L = sum(dY * out) with respect to x (and the LoRA
     adapters), base weights and biases frozen ([P1]: only the input and
     adapter gradients are needed for LoRA training).
@@ -298,6 +307,12 @@ def backward_dx(layer: Layer, x_bits, dy_bits, tokens=None, routing: Routing | N
     Gate_up adapter (filled into ``gu_grads`` as "dA_gu" [E, r, H] and
     "dB_gu" [E, 2I, r] when a dict is given): dB_gu_e = s * sum_f dh^T vg_f
     with vg = x A_gu^T, dA_gu_e = sum_f dvg^T x_t.
+    Base weights and biases, as if they were trained (filled into
+    ``base_grads`` when a dict is given; [P1] "Relation to the backward
+    triton kernels": native MXFP4 training needs them): the gradients with
+    respect to the dequantized weights,
+      dW_gu_e = sum_f dh_f^T x_t [E, 2I, H],   db_gu_e = sum_f dh_f [E, 2I],
+      dW_dn_e = sum_f g_y^T a_f  [E, H, I],    db_dn_e = sum_f g_y  [E, H].
 
     ``tokens`` restricts dX to those tokens (then dA/dB cover only them).
     ``experts`` restricts the expert loop to those experts: dA/dB are then
@@ -322,6 +337,11 @@ def backward_dx(layer: Layer, x_bits, dy_bits, tokens=None, routing: Routing | N
     lora_gu = layer.has_lora_gu and want_lora and gu_grads is not None
     dAg = np.zeros(layer.lora_gu_A.shape) if lora_gu else None
     dBg = np.zeros(layer.lora_gu_B.shape) if lora_gu else None
+    base = base_grads is not None
+    if base:
+        E, I = layer.E, layer.I
+        dWg, dbg = np.zeros((E, 2 * I, H)), np.zeros((E, 2 * I))
+        dWd, dbd = np.zeros((E, H, I)), np.zeros((E, H))
     wflat = r.w.reshape(-1)
     for e in range(layer.E):
         if experts is not None and e not in experts:
@@ -344,6 +364,9 @@ def backward_dx(layer: Layer, x_bits, dy_bits, tokens=None, routing: Routing | N
         dw[rows] = np.einsum("rh,rh->r", dY[t], y)
         gy = wflat[rows][:, None] * dY[t]
         da = gy @ Wd
+        if base:
+            dWd[e] += gy.T @ a
+            dbd[e] += gy.sum(axis=0)
         if layer.has_lora:
             dv = layer.lora_scale * gy @ B
             da = da + dv @ A
@@ -355,6 +378,9 @@ def backward_dx(layer: Layer, x_bits, dy_bits, tokens=None, routing: Routing | N
         dh[:, 0::2] = dg
         dh[:, 1::2] = du
         dxf = dh @ Wgu
+        if base:
+            dWg[e] += dh.T @ x[t]
+            dbg[e] += dh.sum(axis=0)
         if layer.has_lora_gu:
             Ag = bf16_to_f64(layer.lora_gu_A[e])
             Bg = bf16_to_f64(layer.lora_gu_B[e])
@@ -366,6 +392,8 @@ def backward_dx(layer: Layer, x_bits, dy_bits, tokens=None, routing: Routing | N
         np.add.at(dX, t, dxf)
     if lora_gu:
         gu_grads["dA_gu"], gu_grads["dB_gu"] = dAg, dBg
+    if base:
+        base_grads.update(dW_gu=dWg, db_gu=dbg, dW_dn=dWd, db_dn=dbd)
     if experts is not None:
         return dX, dA, dB
     # router path through the softmax over the selected logits

@@ -539,3 +539,68 @@ def test_gate_up_adapter_gradients_partition_over_experts():
         np.testing.assert_allclose(ge["dB_gu"][e], g["dB_gu"][e], rtol=1e-12, atol=1e-15)
         others = [i for i in range(s.E) if i != e]
         assert not np.any(ge["dA_gu"][others]) and not np.any(ge["dB_gu"][others])
+
+
+# ---------------------------------------------- base-weight gradients (dW)
+
+@pytest.mark.parametrize("lora", [False, True])
+def test_base_weight_gradients_finite_differences(lora):
+    # gradients with respect to the dequantized weights and the biases:
+    # perturb one entry of a float64 weight copy (or a bias) and difference
+    # the loss
+    s = syn.spec("tiny", lora_rank=8 if lora else 0, lora_gate_up=lora)
+    L, x, dY = _fd_layer(s, lora=lora)
+    L.lora_scale = 2.0
+    L.gu_weight = np.stack([mxfp4.dequantize(L.gu_codes[e], L.gu_scales[e]) for e in range(s.E)])
+    L.dn_weight = np.stack([mxfp4.dequantize(L.dn_codes[e], L.dn_scales[e]) for e in range(s.E)])
+    L.gu_bias = moe.bf16_to_f64(L.gu_bias)
+    L.dn_bias = moe.bf16_to_f64(L.dn_bias)
+    g = {}
+    moe.backward_dx(L, x, dY, base_grads=g)
+    assert g["dW_gu"].shape == L.gu_weight.shape and g["dW_dn"].shape == L.dn_weight.shape
+    rng = np.random.default_rng(14)
+    for name, grad in (("gu_weight", g["dW_gu"]), ("dn_weight", g["dW_dn"]),
+                       ("gu_bias", g["db_gu"]), ("dn_bias", g["db_dn"])):
+        base = getattr(L, name)
+        nz = 0
+        for _ in range(8):
+            pos = tuple(int(rng.integers(0, n)) for n in base.shape)
+            eps = 1e-4
+            P = base.copy()
+            P[pos] += eps
+            Lp = copy.copy(L)
+            setattr(Lp, name, P)
+            M = base.copy()
+            M[pos] -= eps
+            Lm = copy.copy(L)
+            setattr(Lm, name, M)
+            fd = (_loss(Lp, x, dY) - _loss(Lm, x, dY)) / (2 * eps)
+            assert abs(fd - grad[pos]) <= 1e-6 * max(1.0, abs(fd)), (name, pos, fd, grad[pos])
+            nz += grad[pos] != 0
+        assert nz > 0, name
+
+
+def test_base_weight_gradients_closed_form_dense():
+    # E = 1, k = 1: w = 1 and every token goes to the one expert, so
+    # dW_dn = dY^T a and dW_gu = dh^T x over all tokens (torch autograd on
+    # the dense float64 MLP as the reference)
+    s = syn.spec("tiny", E=1, k=1)
+    L = oracle_layer(s)
+    x = syn.tokens(s)
+    dY = syn.upstream_grad(s)
+    g = {}
+    moe.backward_dx(L, x, dY, base_grads=g)
+    xt = torch.from_numpy(moe.bf16_to_f64(x))
+    Wg = torch.from_numpy(L.gate_up(0)).requires_grad_(True)
+    Wd = torch.from_numpy(L.down(0)).requires_grad_(True)
+    bg = torch.from_numpy(L.gu_b(0)).requires_grad_(True)
+    bd = torch.from_numpy(L.dn_b(0)).requires_grad_(True)
+    h = xt @ Wg.T + bg
+    gte, up = h[:, 0::2].clamp(max=L.limit), h[:, 1::2].clamp(-L.limit, L.limit)
+    act = gte * torch.sigmoid(L.alpha * gte) * (up + 1)
+    y = act @ Wd.T + bd
+    (y * torch.from_numpy(moe.bf16_to_f64(dY))).sum().backward()
+    np.testing.assert_allclose(g["dW_gu"][0], Wg.grad.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(g["dW_dn"][0], Wd.grad.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(g["db_gu"][0], bg.grad.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(g["db_dn"][0], bd.grad.numpy(), rtol=1e-10, atol=1e-12)
