@@ -170,6 +170,7 @@ int mxfp4_moe_saved_bytes(const mxfp4_moe_dims* dims, mxfp4_moe_saved_sizes* out
 #define MXFP4_WS_FORWARD 0        /* mxfp4_moe_forward, saved == NULL */
 #define MXFP4_WS_FORWARD_SAVED 1  /* mxfp4_moe_forward, saved != NULL */
 #define MXFP4_WS_BACKWARD 2       /* mxfp4_moe_backward_dx */
+#define MXFP4_WS_BACKWARD_FULL 3  /* mxfp4_moe_backward */
 
 /* Bytes of device workspace an entry point needs for these dims (0 if
  * the dims are invalid; mxfp4_last_error() then says why).  The workspace
@@ -238,6 +239,42 @@ int mxfp4_moe_backward_dx(const mxfp4_moe_dims* dims, const mxfp4_moe_weights* w
                           const mxfp4_moe_saved* saved, const uint16_t* x, const uint16_t* dy,
                           uint16_t* dx, float* dA, float* dB, float* dA_gu, float* dB_gu,
                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Gradients the full backward writes (fp32 ones overwritten; a NULL
+ * optional pointer skips that gradient):
+ *  dx     bf16 [T, H], required
+ *  dA, dB, dA_gu, dB_gu   the adapter gradients, as in mxfp4_moe_backward_dx
+ *  dW_gu  fp32 [E, 2I, H]  sum over expert e's routed rows of dh^T x_t
+ *  dW_dn  fp32 [E, H, I]   sum of (w dY_t)^T a
+ *  db_gu  fp32 [E, 2I]     sum of dh;   db_dn fp32 [E, H]  sum of w dY_t
+ * dW_* are the gradients with respect to the dequantized weights (the
+ * optimizer updates a master copy and requantizes it, e.g. with
+ * mxfp4_quantize); an expert with no rows gets zeros. */
+typedef struct mxfp4_moe_grads {
+  uint16_t* dx;
+  float* dA;
+  float* dB;
+  float* dA_gu;
+  float* dB_gu;
+  float* dW_gu;
+  float* dW_dn;
+  float* db_gu;
+  float* db_dn;
+} mxfp4_moe_grads;
+
+/* Full backward for fine-tuning the MXFP4 base itself ([P1] "Relation to
+ * the backward triton kernels": native MXFP4 training is the end goal;
+ * [P2] MxFp4MatMulFunction with forward and backward): everything
+ * mxfp4_moe_backward_dx computes, plus the base-weight and bias gradients
+ * grads names.  Same arguments and checks as mxfp4_moe_backward_dx; x is
+ * also required for dW_gu.  The workspace is mxfp4_moe_workspace_bytes(
+ * dims, MXFP4_WS_BACKWARD_FULL).  dW_gu and dW_dn are bf16 x bf16 matrix-
+ * core products summed in fp32 in a fixed order (deterministic); w a is
+ * rounded to bf16 before its product. */
+int mxfp4_moe_backward(const mxfp4_moe_dims* dims, const mxfp4_moe_weights* w,
+                       const mxfp4_moe_saved* saved, const uint16_t* x, const uint16_t* dy,
+                       const mxfp4_moe_grads* grads, void* workspace, size_t workspace_bytes,
+                       void* stream);
 
 /* Row-wise MXFP4 quantisation, one launch ([P3] note on the row-wise
  * quantizers).  w fp32 [rows, K] -> codes uint8 [rows, K/2] (low nibble =

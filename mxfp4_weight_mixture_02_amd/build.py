@@ -20,7 +20,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmxfp4_moe.so")
-SOURCES = ["abi.cpp", "quant.hip", "route.hip", "gemm_fwd.hip", "gemm_bwd.hip", "gemm_dec.hip", "lora.hip"]
+SOURCES = ["abi.cpp", "quant.hip", "route.hip", "gemm_fwd.hip", "gemm_bwd.hip", "gemm_dec.hip", "lora.hip",
+           "gemm_dw.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 FLAGS = [

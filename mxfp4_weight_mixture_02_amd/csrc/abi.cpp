@@ -48,6 +48,7 @@ struct Layout {
          y_w = SIZE_MAX, dh = SIZE_MAX, dw_part = SIZE_MAX, dxr = SIZE_MAX,
          lora_v = SIZE_MAX, lora_At = SIZE_MAX, lora_Bt = SIZE_MAX, lora_dvu = SIZE_MAX,
          lora_vg = SIZE_MAX, lora_guAt = SIZE_MAX, lora_guBt = SIZE_MAX, lora_dvg = SIZE_MAX,
+         wa = SIZE_MAX,
          logits = SIZE_MAX, logit_part = SIZE_MAX;
   size_t total = 0;
   size_t put(size_t bytes) {
@@ -136,6 +137,8 @@ Layout layout(const mxfp4_moe_dims& d, int mode) {
       L.lora_guBt = L.put((size_t)d.E * 2 * d.I * d.lora_rank * 2);
       L.lora_dvg = L.put(R * (size_t)d.lora_rank * 4);
     }
+    // the full backward's base-weight gradients: w_p a_p rows for dW_dn
+    if (mode == MXFP4_WS_BACKWARD_FULL) L.wa = L.put(R * (size_t)d.I * 2);
   }
   return L;
 }
@@ -417,7 +420,7 @@ int mxfp4_moe_kernel_times(const char** names, double* total_ms, int* launches, 
 
 size_t mxfp4_moe_workspace_bytes(const mxfp4_moe_dims* dims, int mode) {
   if (check_dims(dims) != MXFP4_OK) return 0;
-  if (mode < MXFP4_WS_FORWARD || mode > MXFP4_WS_BACKWARD) {
+  if (mode < MXFP4_WS_FORWARD || mode > MXFP4_WS_BACKWARD_FULL) {
     fail(MXFP4_EINVAL, "unknown workspace mode %d", mode);
     return 0;
   }
@@ -472,10 +475,18 @@ int mxfp4_moe_forward_noalloc(const mxfp4_moe_dims* dims, const mxfp4_moe_weight
   return enqueue_forward(*dims, w, x, out, saved, ws, static_cast<hipStream_t>(stream));
 }
 
-int mxfp4_moe_backward_dx(const mxfp4_moe_dims* dims, const mxfp4_moe_weights* w,
-                          const mxfp4_moe_saved* saved, const uint16_t* x, const uint16_t* dy,
-                          uint16_t* dx, float* dA, float* dB, float* dA_gu, float* dB_gu,
-                          void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The backward of both entry points: dX and the adapter gradients, and with
+// mode MXFP4_WS_BACKWARD_FULL the base-weight and bias gradients g names.
+int backward_impl(const mxfp4_moe_dims* dims, const mxfp4_moe_weights* w,
+                  const mxfp4_moe_saved* saved, const uint16_t* x, const uint16_t* dy,
+                  const mxfp4_moe_grads& g, int mode, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+  uint16_t* dx = g.dx;
+  float *dA = g.dA, *dB = g.dB, *dA_gu = g.dA_gu, *dB_gu = g.dB_gu;
   int rc = check_dims(dims);
   if (rc) return rc;
   rc = check_weights(w, *dims);
@@ -499,7 +510,12 @@ int mxfp4_moe_backward_dx(const mxfp4_moe_dims* dims, const mxfp4_moe_weights* w
     if (!x || !aligned(x, 16))
       return fail(MXFP4_EINVAL, "gate_up adapter: x (the forward's input) is required, 16-byte aligned");
   }
-  const Layout L = layout(d, MXFP4_WS_BACKWARD);
+  const bool full = mode == MXFP4_WS_BACKWARD_FULL;
+  if (full) {
+    if (g.dW_gu && (!x || !aligned(x, 16)))
+      return fail(MXFP4_EINVAL, "dW_gu needs x (the forward's input), 16-byte aligned");
+  }
+  const Layout L = layout(d, mode);
   if (!workspace || workspace_bytes < L.total)
     return fail(MXFP4_EWORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, L.total);
   if (!aligned(workspace, ALIGN)) return fail(MXFP4_EINVAL, "workspace must be 256-byte aligned");
@@ -577,7 +593,58 @@ int mxfp4_moe_backward_dx(const mxfp4_moe_dims* dims, const mxfp4_moe_weights* w
   LAUNCH(mxmoe::launch_bwd_combine(dy, dxr, dw_part, mxmoe::bwd_down_ntiles(I), saved->topk_idx,
                                    saved->topk_w, w->dn_bias, w->router_w, d.T, H, k, dx, s),
          "bwd_combine");
+  if (full) {
+    // base-weight and bias gradients (dh still in the workspace):
+    // dW_gu = sum dh^T x, db_gu = sum dh, dW_dn = sum dY^T (w a), db_dn = sum w dY
+    if (g.dW_gu)
+      LAUNCH(mxmoe::launch_dw(dh, 2 * I, false, x, H, true, saved->expert_offsets,
+                              saved->sorted_rows, k, E, 2 * I, H, g.dW_gu, s),
+             "dw_gate_up");
+    if (g.db_gu)
+      LAUNCH(mxmoe::launch_colsum(dh, 2 * I, false, saved->expert_offsets, saved->sorted_rows, k,
+                                  nullptr, E, 2 * I, g.db_gu, s),
+             "db_gate_up");
+    if (g.dW_dn) {
+      uint16_t* wa = at<uint16_t>(workspace, L.wa);
+      LAUNCH(mxmoe::launch_scale_rows(saved->a, R, I, saved->sorted_rows, saved->topk_w, wa, s),
+             "scale_rows");
+      LAUNCH(mxmoe::launch_dw(dy, H, true, wa, I, false, saved->expert_offsets, saved->sorted_rows,
+                              k, E, H, I, g.dW_dn, s),
+             "dw_down");
+    }
+    if (g.db_dn)
+      LAUNCH(mxmoe::launch_colsum(dy, H, true, saved->expert_offsets, saved->sorted_rows, k,
+                                  saved->topk_w, E, H, g.db_dn, s),
+             "db_down");
+  }
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int mxfp4_moe_backward_dx(const mxfp4_moe_dims* dims, const mxfp4_moe_weights* w,
+                          const mxfp4_moe_saved* saved, const uint16_t* x, const uint16_t* dy,
+                          uint16_t* dx, float* dA, float* dB, float* dA_gu, float* dB_gu,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  mxfp4_moe_grads g{};
+  g.dx = dx;
+  g.dA = dA;
+  g.dB = dB;
+  g.dA_gu = dA_gu;
+  g.dB_gu = dB_gu;
+  return backward_impl(dims, w, saved, x, dy, g, MXFP4_WS_BACKWARD, workspace, workspace_bytes,
+                       stream);
+}
+
+int mxfp4_moe_backward(const mxfp4_moe_dims* dims, const mxfp4_moe_weights* w,
+                       const mxfp4_moe_saved* saved, const uint16_t* x, const uint16_t* dy,
+                       const mxfp4_moe_grads* grads, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  if (!grads) return fail(MXFP4_EINVAL, "grads is NULL");
+  return backward_impl(dims, w, saved, x, dy, *grads, MXFP4_WS_BACKWARD_FULL, workspace,
+                       workspace_bytes, stream);
 }
 
 int mxfp4_quantize(const float* w, int64_t rows, int64_t K, uint8_t* codes, uint8_t* scales,

@@ -115,4 +115,18 @@ hipError_t launch_lora_grad(const uint16_t* Q, bool gather, int C, const int32_t
                             const int32_t* offsets, int E, float* out, int64_t e_stride,
                             int c_stride, int j_stride, hipStream_t s);
 
+// gemm_dw.hip: base-weight gradients.  out[e] (fp32 [M, N]) = sum over
+// expert e's sorted rows p of A[rowA(p)]^T B[rowB(p)] (bf16 row-major, the
+// gathered operand's row = sorted_rows[p] / k, else p).
+hipError_t launch_dw(const uint16_t* A, int lda, bool gatherA, const uint16_t* B, int ldb,
+                     bool gatherB, const int32_t* offsets, const int32_t* sorted_rows, int k,
+                     int E, int M, int N, float* out, hipStream_t s);
+// db[e][c] = sum_p w_p src[row(p)][c] (topk_w NULL: w = 1)
+hipError_t launch_colsum(const uint16_t* src, int ld, bool gather, const int32_t* offsets,
+                         const int32_t* sorted_rows, int k, const float* topk_w, int E, int C,
+                         float* db, hipStream_t s);
+// out[p] = bf16(topk_w[sorted_rows[p]] * in[p]) for R rows of C columns
+hipError_t launch_scale_rows(const uint16_t* in, int64_t R, int C, const int32_t* sorted_rows,
+                             const float* topk_w, uint16_t* out, hipStream_t s);
+
 }  // namespace mxmoe

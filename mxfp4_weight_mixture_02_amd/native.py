@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_PKG, "libmxfp4_moe.so")
 HEADER = os.path.join(os.path.dirname(_PKG), "include", "mxfp4_moe.h")
 
 MXFP4_OK = 0
-WS_FORWARD, WS_FORWARD_SAVED, WS_BACKWARD = 0, 1, 2
+WS_FORWARD, WS_FORWARD_SAVED, WS_BACKWARD, WS_BACKWARD_FULL = 0, 1, 2, 3
 ERRORS = {-1: "EINVAL", -2: "EUNSUPPORTED", -3: "EWORKSPACE", -4: "EHIP"}
 
 
@@ -54,6 +54,11 @@ class SavedSizes(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n, _ in Saved._fields_]
 
 
+class Grads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("dx", "dA", "dB", "dA_gu", "dB_gu", "dW_gu", "dW_dn", "db_gu", "db_dn")]
+
+
 _lib = None
 
 
@@ -82,6 +87,10 @@ def lib() -> ctypes.CDLL:
         L.mxfp4_moe_backward_dx.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Weights),
                                             ctypes.POINTER(Saved), vp, vp, vp, vp, vp, vp, vp,
                                             vp, ctypes.c_size_t, vp]
+        L.mxfp4_moe_backward.restype = i32
+        L.mxfp4_moe_backward.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Weights),
+                                         ctypes.POINTER(Saved), vp, vp, ctypes.POINTER(Grads), vp,
+                                         ctypes.c_size_t, vp]
         L.mxfp4_quantize.restype = i32
         L.mxfp4_quantize.argtypes = [vp, i64, i64, vp, vp, vp]
         L.mxfp4_dequantize.restype = i32
@@ -445,3 +454,39 @@ def mxfp4_moe_backward_dx(layer: MoeLayer, saved: SavedState, dy: torch.Tensor,
     if gu:
         return dx, grads["dA"], grads["dB"], grads["dA_gu"], grads["dB_gu"]
     return dx, grads["dA"], grads["dB"]
+
+
+def mxfp4_moe_backward(layer: MoeLayer, saved: SavedState, x: torch.Tensor, dy: torch.Tensor,
+                       base: bool = True, workspace: Workspace | None = None) -> dict:
+    """The full backward (mxfp4_moe_backward): dx, the adapter gradients the
+    layer has, and with ``base`` the base-weight and bias gradients dW_gu
+    [E, 2I, H], dW_dn [E, H, I], db_gu [E, 2I], db_dn [E, H] (fp32, with
+    respect to the dequantized weights).  Returns them by name."""
+    layer.check_shapes()
+    if dy.dim() != 2:
+        raise ValueError(f"dy must be [T, H], got {tuple(dy.shape)}")
+    T = dy.shape[0]
+    _shape(dy, (T, layer.H), torch.bfloat16, "dy")
+    _shape(x, (T, layer.H), torch.bfloat16, "x")
+    saved.check_shapes(layer, T)
+    _dev(dy, torch.bfloat16, "dy")
+    _dev(x, torch.bfloat16, "x")
+    E, H, I = layer.E, layer.H, layer.I
+    f32 = dict(dtype=torch.float32, device=dy.device)
+    out = {"dx": torch.empty_like(dy)}
+    for name, t in (("dA", layer.lora_A), ("dB", layer.lora_B), ("dA_gu", layer.lora_gu_A),
+                    ("dB_gu", layer.lora_gu_B)):
+        out[name] = torch.empty(t.shape, **f32) if t is not None else None
+    if base:
+        out.update(dW_gu=torch.empty((E, 2 * I, H), **f32), dW_dn=torch.empty((E, H, I), **f32),
+                   db_gu=torch.empty((E, 2 * I), **f32), db_dn=torch.empty((E, H), **f32))
+    g = Grads(*[_ptr(out.get(n)) for n, _ in Grads._fields_])
+    nbytes = workspace_bytes(layer, T, WS_BACKWARD_FULL)
+    ws = (workspace or _WS).get(nbytes, dy.device)
+    d = layer.dims(T)
+    w = layer.weights()
+    sv = saved.struct()
+    rc = lib().mxfp4_moe_backward(ctypes.byref(d), ctypes.byref(w), ctypes.byref(sv), _ptr(x),
+                                  _ptr(dy), ctypes.byref(g), _ptr(ws), ws.numel(), _stream())
+    _check("mxfp4_moe_backward", rc)
+    return {k: v for k, v in out.items() if v is not None}

@@ -7,10 +7,10 @@ import ctypes
 import pytest
 
 from mxfp4_weight_mixture_02_amd import native
-from mxfp4_weight_mixture_02_amd.native import Dims, Saved, SavedSizes, Weights
+from mxfp4_weight_mixture_02_amd.native import Dims, Grads, Saved, SavedSizes, Weights
 
 EXPECTED = {"mxfp4_moe_workspace_bytes", "mxfp4_moe_saved_bytes", "mxfp4_moe_forward",
-            "mxfp4_moe_forward_noalloc", "mxfp4_moe_backward_dx",
+            "mxfp4_moe_forward_noalloc", "mxfp4_moe_backward_dx", "mxfp4_moe_backward",
             "mxfp4_quantize", "mxfp4_dequantize", "mxfp4_last_error",
             "mxfp4_moe_kernel_timing", "mxfp4_moe_kernel_times"}
 
@@ -261,3 +261,24 @@ def test_gate_up_adapter_validation(L):
     rc = L.mxfp4_moe_backward_dx(ctypes.byref(gu), ctypes.byref(w), ctypes.byref(sv), None, FAKE,
                                  FAKE, None, None, FAKE, FAKE, FAKE, b, None)
     assert rc == -1 and "x (the forward's input)" in _err(L)
+
+
+def test_full_backward_validation(L):
+    # the base-weight gradients need the w a rows: a larger workspace mode
+    d = _dims()
+    b2 = L.mxfp4_moe_workspace_bytes(ctypes.byref(d), 2)
+    b3 = L.mxfp4_moe_workspace_bytes(ctypes.byref(d), 3)
+    assert b3 > b2 > 0
+    assert L.mxfp4_moe_workspace_bytes(ctypes.byref(d), 4) == 0
+    w = _weights()
+    sv = Saved(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    rc = L.mxfp4_moe_backward(ctypes.byref(d), ctypes.byref(w), ctypes.byref(sv), None, FAKE, None,
+                              FAKE, b3, None)
+    assert rc == -1 and "grads" in _err(L)
+    g = Grads(FAKE, 0, 0, 0, 0, FAKE, 0, 0, 0)
+    rc = L.mxfp4_moe_backward(ctypes.byref(d), ctypes.byref(w), ctypes.byref(sv), None, FAKE,
+                              ctypes.byref(g), FAKE, b3, None)
+    assert rc == -1 and "dW_gu needs x" in _err(L)
+    rc = L.mxfp4_moe_backward(ctypes.byref(d), ctypes.byref(w), ctypes.byref(sv), FAKE, FAKE,
+                              ctypes.byref(g), FAKE, b2, None)
+    assert rc == -3 and "workspace" in _err(L)

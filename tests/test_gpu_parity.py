@@ -20,8 +20,8 @@ import pytest
 import torch
 
 import moe_synth as syn
-from mxfp4_weight_mixture_02_amd import (Mxfp4Error, mxfp4_dequantize, mxfp4_moe_backward_dx,
-                                         mxfp4_moe_forward, mxfp4_quantize)
+from mxfp4_weight_mixture_02_amd import (Mxfp4Error, mxfp4_dequantize, mxfp4_moe_backward,
+                                         mxfp4_moe_backward_dx, mxfp4_moe_forward, mxfp4_quantize)
 from oracle import moe, mxfp4
 
 from gpu_helpers import (DEV, assert_bytes_equal, assert_close, assert_routing_equal, bf16_tensor,
@@ -281,6 +281,56 @@ def test_lora_on_gate_up(T, r, down):
     _say(f"gate_up lora T={T} r={r} down={down}")
     _run_layer(syn.spec("tiny", T=T, H=192, I=320, E=3, k=2, lora_rank=r, lora_gate_up=True,
                         lora_down=down), lora_scale=4.0)
+
+
+def _run_full_backward(s, lora_scale=1.0):
+    """Forward (saved), then the full backward: dX, the adapter gradients and
+    the base-weight and bias gradients against the oracle, whole tensors and
+    expert by expert."""
+    _say(f"full backward {s.name} T={s.T} H={s.H} I={s.I} E={s.E} k={s.k} r={s.lora_rank}")
+    dl = device_layer(s)
+    ol, _ = oracle_layer(s)
+    dl.lora_scale = ol.lora_scale = lora_scale
+    xb, dyb = syn.tokens(s), syn.upstream_grad(s)
+    x = bf16_tensor(xb).to(DEV)
+    _, sv = mxfp4_moe_forward(dl, x, saved=True)
+    got = mxfp4_moe_backward(dl, sv, x, bf16_tensor(dyb).to(DEV))
+    torch.cuda.synchronize()
+    g, base = {}, {}
+    dref, dAref, dBref = moe.backward_dx(ol, xb, dyb, gu_grads=g, base_grads=base)
+    assert_close(to_f64(got["dx"]), dref, "dX")
+    refs = dict(base, dA=dAref, dB=dBref, **g)
+    off = sv.expert_offsets.cpu().numpy()
+    for name in ("dW_gu", "dW_dn", "db_gu", "db_dn", "dA", "dB", "dA_gu", "dB_gu"):
+        if refs.get(name) is None:
+            assert name not in got
+            continue
+        gv = got[name].double().cpu().numpy()
+        assert_close(gv, refs[name], name)
+        if name.startswith("d") and name[1] in "Wb":
+            for e in range(s.E):
+                if off[e + 1] == off[e]:
+                    assert not gv[e].any(), f"{name}[{e}]: expert without rows"
+                else:
+                    assert_close(gv[e], refs[name][e], f"{name}[{e}]", max_rel=3e-2)
+    return got
+
+
+@pytest.mark.parametrize("shape", [
+    dict(),                                     # tiny: 4 experts, 16 tokens
+    dict(T=300, H=192, I=320, E=3, k=2),        # several 64-row steps per expert, ragged
+    dict(T=200, H=96, I=160, E=3, k=2),         # odd multiples of 32
+    dict(T=260, H=320, I=288, E=5, k=2),        # 2I = 576, H = 320: partial 256 tiles
+    dict(T=3, E=16, k=2),                       # most experts without rows
+])
+def test_full_backward_base_weight_gradients(shape):
+    _run_full_backward(syn.spec("tiny", **shape))
+
+
+@pytest.mark.parametrize("r,gu,dn", [(16, True, True), (8, False, True), (32, True, False)])
+def test_full_backward_with_adapters(r, gu, dn):
+    _run_full_backward(syn.spec("tiny", T=300, H=192, I=320, E=3, k=2, lora_rank=r,
+                                lora_gate_up=gu, lora_down=dn), lora_scale=4.0)
 
 
 def test_forward_is_deterministic():
