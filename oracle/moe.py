@@ -30,7 +30,7 @@ from dataclasses import dataclass
 
 import numpy as np
 
-from . import mxfp4
+from . import mxfp4, mxfp8
 
 
 def bf16_to_f64(bits) -> np.ndarray:
@@ -237,7 +237,24 @@ def _gate_up_pre(layer, e, xt, Wgu):
     return h
 
 
-def forward(layer: Layer, x_bits, tokens=None, routing: Routing | None = None, experts=None):
+def gate_up_input(x: np.ndarray, fmt: str) -> np.ndarray:
+    """The activations the gate_up product consumes under an activation
+    format ([P3] commit notes: activation_format "bf16" = weight-only, None =
+    the weights' block-scaled format): "bf16" keeps x; "mxfp8" is one MXFP8
+    quantization of each token row; "mxfp8x2" the hi + lo pair, x ~ deq(hi) +
+    deq(lo) (oracle/mxfp8.py)."""
+    if fmt == "bf16":
+        return x
+    if fmt == "mxfp8":
+        return mxfp8.dequantize(*mxfp8.quantize(x))
+    if fmt == "mxfp8x2":
+        hc, hs, lc, ls = mxfp8.quantize_hi_lo(x)
+        return mxfp8.dequantize(hc, hs) + mxfp8.dequantize(lc, ls)
+    raise ValueError(f"unknown activation format {fmt!r}")
+
+
+def forward(layer: Layer, x_bits, tokens=None, routing: Routing | None = None, experts=None,
+            act_format: str = "bf16"):
     """Expert-block forward.  Returns (out float64 [T, H], routing, cache).
 
     out[t] = sum_j w[t, j] * y_(t, j), where for expert e = idx[t, j]
@@ -249,6 +266,8 @@ def forward(layer: Layer, x_bits, tokens=None, routing: Routing | None = None, e
     ``tokens`` (optional index array) restricts the expert loop to those
     tokens; the other rows of ``out`` stay zero.  ``experts`` (optional)
     restricts it to those experts: ``out`` then holds only their share.
+    ``act_format`` quantizes the gate_up product's input (gate_up_input);
+    the router, the adapters and the down product keep their inputs.
     Routing is always for all tokens (it is what the permutation is defined
     on).  ``cache`` maps each flat row f that was computed to (h, a, y, vg)
     for the backward and tests (vg = x A_gu^T, None without the gate_up
@@ -264,6 +283,7 @@ def forward(layer: Layer, x_bits, tokens=None, routing: Routing | None = None, e
         mask[np.asarray(tokens)] = True
     out = np.zeros((T, H))
     cache = {}
+    xq = gate_up_input(x, act_format)
     for e in range(layer.E):
         if experts is not None and e not in experts:
             continue
@@ -271,7 +291,9 @@ def forward(layer: Layer, x_bits, tokens=None, routing: Routing | None = None, e
         if rows.size == 0:
             continue
         t = rows // k
-        h = _gate_up_pre(layer, e, x[t], layer.gate_up(e))
+        h = xq[t] @ layer.gate_up(e).T + layer.gu_b(e)
+        if layer.has_lora_gu:
+            h = h + layer.lora_scale * _lora_vg(layer, e, x[t]) @ bf16_to_f64(layer.lora_gu_B[e]).T
         a = swiglu(h[:, 0::2], h[:, 1::2], layer.alpha, layer.limit)
         y = a @ layer.down(e).T + layer.dn_b(e)
         if layer.has_lora:
