@@ -62,9 +62,21 @@ extern "C" {
  *  1.702 and 7).  lora_scale multiplies the LoRA deltas (1.0 when
  *  lora_alpha equals the rank).  lora_targets: which projections carry a
  *  rank-lora_rank adapter, MXFP4_LORA_DOWN | MXFP4_LORA_GATE_UP (0 means
- *  MXFP4_LORA_DOWN); ignored when lora_rank == 0. */
+ *  MXFP4_LORA_DOWN); ignored when lora_rank == 0.
+ *  activation_format: what the gate_up product consumes ([P3] commit notes:
+ *  activation_format "bf16" = weight-only, None = the weights' block-scaled
+ *  format): MXFP4_ACT_BF16 (0, default) decodes the weights to bf16 for the
+ *  matrix cores; MXFP4_ACT_MXFP8 quantizes each token row to MXFP8 (E4M3,
+ *  UE8M0 per 32) and runs the block-scaled MFMA on the packed FP4 weights as
+ *  stored; MXFP4_ACT_MXFP8X2 adds a second MXFP8 pass of the residual (x ~
+ *  hi + lo).  The block-scaled formats need H % 64 == 0 and no gate_up
+ *  adapter; the down product and the backward are unchanged (the backward
+ *  treats the quantization as the identity). */
 #define MXFP4_LORA_DOWN 1
 #define MXFP4_LORA_GATE_UP 2
+#define MXFP4_ACT_BF16 0
+#define MXFP4_ACT_MXFP8 1
+#define MXFP4_ACT_MXFP8X2 2
 typedef struct mxfp4_moe_dims {
   int64_t T;
   int64_t H;
@@ -76,6 +88,7 @@ typedef struct mxfp4_moe_dims {
   int32_t lora_rank;
   float lora_scale;
   int32_t lora_targets;
+  int32_t activation_format;
 } mxfp4_moe_dims;
 
 /* Frozen layer parameters ([P3] MXFP4 layout; weights never written).
@@ -286,6 +299,19 @@ int mxfp4_moe_backward(const mxfp4_moe_dims* dims, const mxfp4_moe_weights* w,
  * the contract. */
 int mxfp4_quantize(const float* w, int64_t rows, int64_t K, uint8_t* codes, uint8_t* scales,
                    void* stream);
+
+/* Row-wise MXFP8 activation quantisation (the forward's pre-pass for the
+ * block-scaled activation formats, exported for tests; [P3] note on the
+ * row-wise quantizers): x bf16 [rows, K] -> codes uint8 [rows, K] (OCP
+ * E4M3) and scales uint8 [rows, K/32] (UE8M0).  Per 32-block: e = the
+ * smallest integer with amax <= 448 * 2^e, clamped to [-127, 127] (amax = 0
+ * gives -127); scale byte e + 127; code = nearest E4M3 value to x / 2^e,
+ * ties to the even mantissa.  With lo_codes and lo_scales (both or
+ * neither) the residual x - deq(code) is quantized the same way.  K % 32
+ * == 0; x, codes and lo_codes 16-byte aligned.  Non-finite x is outside the
+ * contract. */
+int mxfp8_quantize(const uint16_t* x, int64_t rows, int64_t K, uint8_t* codes, uint8_t* scales,
+                   uint8_t* lo_codes, uint8_t* lo_scales, void* stream);
 
 /* Dequantisation (the decode used inside every GEMM, exported for tests):
  * out[n, k] = e2m1(code) * 2^(scale - 127), exactly (every such value is a

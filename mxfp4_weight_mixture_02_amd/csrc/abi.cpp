@@ -48,7 +48,7 @@ struct Layout {
          y_w = SIZE_MAX, dh = SIZE_MAX, dw_part = SIZE_MAX, dxr = SIZE_MAX,
          lora_v = SIZE_MAX, lora_At = SIZE_MAX, lora_Bt = SIZE_MAX, lora_dvu = SIZE_MAX,
          lora_vg = SIZE_MAX, lora_guAt = SIZE_MAX, lora_guBt = SIZE_MAX, lora_dvg = SIZE_MAX,
-         wa = SIZE_MAX,
+         wa = SIZE_MAX, xq = SIZE_MAX, xs = SIZE_MAX, xq_lo = SIZE_MAX, xs_lo = SIZE_MAX,
          logits = SIZE_MAX, logit_part = SIZE_MAX;
   size_t total = 0;
   size_t put(size_t bytes) {
@@ -91,6 +91,15 @@ int check_dims(const mxfp4_moe_dims* d) {
   if (d->lora_targets & ~(MXFP4_LORA_DOWN | MXFP4_LORA_GATE_UP))
     return fail(MXFP4_EINVAL, "lora_targets=%d: only MXFP4_LORA_DOWN and MXFP4_LORA_GATE_UP",
                 d->lora_targets);
+  if (d->activation_format < MXFP4_ACT_BF16 || d->activation_format > MXFP4_ACT_MXFP8X2)
+    return fail(MXFP4_EINVAL, "activation_format=%d unknown", d->activation_format);
+  if (d->activation_format != MXFP4_ACT_BF16) {
+    if (d->H % 64)
+      return fail(MXFP4_EUNSUPPORTED, "block-scaled activations need H %% 64 == 0 (H=%lld)",
+                  (long long)d->H);
+    if (d->lora_rank && (d->lora_targets & MXFP4_LORA_GATE_UP))
+      return fail(MXFP4_EUNSUPPORTED, "block-scaled activations with a gate_up adapter");
+  }
   return MXFP4_OK;
 }
 
@@ -115,6 +124,14 @@ Layout layout(const mxfp4_moe_dims& d, int mode) {
     L.tiles = L.put((size_t)maxt * sizeof(mxmoe::Tile));
     L.num_tiles = L.put(4);
     L.y_w = L.put(R * (size_t)d.H * 2);
+    if (d.activation_format != MXFP4_ACT_BF16) {
+      L.xq = L.put((size_t)d.T * d.H);
+      L.xs = L.put((size_t)d.T * d.H / 32);
+      if (d.activation_format == MXFP4_ACT_MXFP8X2) {
+        L.xq_lo = L.put((size_t)d.T * d.H);
+        L.xs_lo = L.put((size_t)d.T * d.H / 32);
+      }
+    }
   } else {
     // the backward GEMMs' tiles (BMT rows); with LoRA also the MT-row tiles
     // of the adapter projection
@@ -333,15 +350,34 @@ int enqueue_forward(const mxfp4_moe_dims& d, const mxfp4_moe_weights* w, const u
   const uint16_t* dn_B = lora_v ? w->lora_B : nullptr;
   // few rows per expert: the weight-streaming decode kernels
   const bool decode = R <= DECODE_MAX_ROWS && H <= mxmoe::dec_max_k() && I <= mxmoe::dec_max_k();
-  if (decode) {
+  if (d.activation_format != MXFP4_ACT_BF16) {
+    // block-scaled activations: quantize the token rows, then the scaled-MFMA gate_up
+    uint8_t* xq = at<uint8_t>(workspace, L.xq);
+    uint8_t* xs = at<uint8_t>(workspace, L.xs);
+    const bool two = d.activation_format == MXFP4_ACT_MXFP8X2;
+    uint8_t* xq_lo = two ? at<uint8_t>(workspace, L.xq_lo) : nullptr;
+    uint8_t* xs_lo = two ? at<uint8_t>(workspace, L.xs_lo) : nullptr;
+    LAUNCH(mxmoe::launch_mxfp8_quantize(x, T, H, xq, xs, xq_lo, xs_lo, s), "act_quantize");
+    LAUNCH(mxmoe::launch_mx_gate_up(xq, xs, xq_lo, xs_lo, w->gu_codes, w->gu_scales, w->gu_bias,
+                                    sorted_rows, tiles, num_tiles, maxt, H, I, k, d.swiglu_alpha,
+                                    d.swiglu_limit, h, a, s),
+           "mx_gate_up");
+  } else if (decode) {
     LAUNCH(mxmoe::launch_dec_gate_up(x, w->gu_codes, w->gu_scales, w->gu_bias, sorted_rows, tiles,
                                      num_tiles, maxt, R, H, I, k, d.swiglu_alpha, d.swiglu_limit,
                                      gu_B, lora_vg, d.lora_scale, r, h, a, s),
            "dec_gate_up");
-    if (lora_v)
-      LAUNCH(mxmoe::launch_lora_proj(a, false, sorted_rows, k, w->lora_A, I, r, tiles, num_tiles,
-                                     maxt, 1.0f, lora_v, s),
-             "lora_v");
+  } else {
+    LAUNCH(mxmoe::launch_gate_up(x, w->gu_codes, w->gu_scales, w->gu_bias, sorted_rows, tiles,
+                                 num_tiles, maxt, H, I, k, d.swiglu_alpha, d.swiglu_limit, gu_B,
+                                 lora_vg, d.lora_scale, r, h, a, s),
+           "gate_up");
+  }
+  if (lora_v)
+    LAUNCH(mxmoe::launch_lora_proj(a, false, sorted_rows, k, w->lora_A, I, r, tiles, num_tiles,
+                                   maxt, 1.0f, lora_v, s),
+           "lora_v");
+  if (decode) {
     LAUNCH(mxmoe::launch_dec_down(a, w->dn_codes, w->dn_scales, w->dn_bias, topk_w, sorted_rows,
                                   tiles, num_tiles, maxt, R, H, I, dn_B, lora_v, d.lora_scale, r,
                                   y_w, s),
@@ -349,14 +385,6 @@ int enqueue_forward(const mxfp4_moe_dims& d, const mxfp4_moe_weights* w, const u
     LAUNCH(mxmoe::launch_combine(y_w, d.T, H, k, out, s), "combine");
     return ok();
   }
-  LAUNCH(mxmoe::launch_gate_up(x, w->gu_codes, w->gu_scales, w->gu_bias, sorted_rows, tiles,
-                               num_tiles, maxt, H, I, k, d.swiglu_alpha, d.swiglu_limit, gu_B,
-                               lora_vg, d.lora_scale, r, h, a, s),
-         "gate_up");
-  if (lora_v)
-    LAUNCH(mxmoe::launch_lora_proj(a, false, sorted_rows, k, w->lora_A, I, r, tiles, num_tiles,
-                                   maxt, 1.0f, lora_v, s),
-           "lora_v");
   LAUNCH(mxmoe::launch_down(a, w->dn_codes, w->dn_scales, w->dn_bias, topk_w, sorted_rows, tiles,
                             num_tiles, maxt, H, I, dn_B, lora_v, d.lora_scale, r, y_w, s),
          "down");
@@ -657,6 +685,21 @@ int mxfp4_quantize(const float* w, int64_t rows, int64_t K, uint8_t* codes, uint
     return fail(MXFP4_EINVAL, "w must be 16-byte and codes 2-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
   LAUNCH(mxmoe::launch_quantize(w, rows, K, codes, scales, s), "quantize");
+  return ok();
+}
+
+int mxfp8_quantize(const uint16_t* x, int64_t rows, int64_t K, uint8_t* codes, uint8_t* scales,
+                   uint8_t* lo_codes, uint8_t* lo_scales, void* stream) {
+  if (!x || !codes || !scales) return fail(MXFP4_EINVAL, "x, codes and scales are required");
+  if (!lo_codes != !lo_scales) return fail(MXFP4_EINVAL, "lo_codes and lo_scales go together");
+  if (rows < 1 || K < 1) return fail(MXFP4_EINVAL, "rows and K must be >= 1");
+  if (K % 32) return fail(MXFP4_EUNSUPPORTED, "K=%lld is not a multiple of 32", (long long)K);
+  if (rows * K / 32 / 256 >= (int64_t(1) << 31)) return fail(MXFP4_EUNSUPPORTED, "tensor too large");
+  if (!aligned(x, 16) || !aligned(codes, 16) || (lo_codes && !aligned(lo_codes, 16)))
+    return fail(MXFP4_EINVAL, "x, codes and lo_codes must be 16-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  LAUNCH(mxmoe::launch_mxfp8_quantize(x, rows, K, codes, scales, lo_codes, lo_scales, s),
+         "mxfp8_quantize");
   return ok();
 }
 

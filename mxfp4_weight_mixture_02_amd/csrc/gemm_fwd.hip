@@ -362,46 +362,18 @@ __device__ __forceinline__ void lora_delta(f32x16 (&acc)[FRB][4], const Tile& tl
   }
 }
 
-// Two waves per SIMD in either shape (amdgpu_waves_per_eu keeps the W = 4
-// kernel within the registers of two waves, so two workgroups fit a CU).
-// LORA: add the gate_up adapter's rank-r delta s (vg B_gu^T) before the
-// bias, as the down GEMM adds its adapter's.
-template <int W, bool LORA>
-__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2, 2))) void gate_up_kernel(
-    const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
-    const uint8_t* __restrict__ scales, const uint16_t* __restrict__ bias,
-    const int32_t* __restrict__ sorted_rows, const Tile* __restrict__ tiles,
-    const int32_t* __restrict__ num_tiles, int H, int I, int k, float alpha, float limit,
-    const uint16_t* __restrict__ lora_B, const float* __restrict__ lora_v, float lora_scale,
-    int lora_r, uint16_t* __restrict__ h_out, uint16_t* __restrict__ a_out) {
-  using S = FwdShape<W>;
-  constexpr int XCHUNKS = S::XCH, FNT = S::NT;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[S::LDS];
-  const int N = 2 * I;
-  Tile tl;
-  int nt;
-  if (!xcd_item_range(tiles, num_tiles, (N + FNT - 1) / FNT, &tl, &nt)) return;
-  const int n0 = nt * FNT;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// The gate_up epilogue (after a barrier that frees LDS): bias, the saved
+// pre-activation h (when h_out) and the clamped SwiGLU a, through a private
+// LDS strip per wave, stored as whole row pieces.  acc: this wave's 64
+// weight rows (wcol = 64 w) by the tile's routed rows.
+__device__ __forceinline__ void gate_up_epilogue(const f32x16 (&acc)[FRB][4], const Tile& tl, int e,
+                                                 int N, int n0, int I,
+                                                 const uint16_t* __restrict__ bias, float alpha,
+                                                 float limit, uint8_t* lds,
+                                                 uint16_t* __restrict__ h_out,
+                                                 uint16_t* __restrict__ a_out) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l32 = lane & 31, hlf = lane >> 5;
-  const int e = tl.expert;
-
-  uint32_t xrow[XCHUNKS];   // element offsets into x (T * H < 2^31)
-#pragma unroll
-  for (int j = 0; j < XCHUNKS; ++j) {
-    const int r = (XCHUNKS * wave + j) * 8 + lane / 8;
-    const int f = sorted_rows[tl.row0 + (r < tl.rows ? r : 0)];
-    xrow[j] = (uint32_t)(f / k) * (uint32_t)H;
-  }
-  const int nrows = min(FNT, N - n0);
-  f32x16 acc[FRB][4];
-  const int wrow_local = (wave * 32 * FRB < nrows ? wave * 32 * FRB : 0) + l32;
-  fwd_body<W>(x, xrow, codes + (int64_t)e * N * (H / 2), scales + (int64_t)e * N * (H / 32), H, n0,
-           nrows, wrow_local, (tl.rows + 31) / 32, lds, acc);
-  if (LORA) lora_delta(acc, tl, e, N, n0, nrows, wrow_local, lora_B, lora_v, lora_scale, lora_r);
-  // Epilogue through LDS: every wave's loads have landed (fwd_loop drained
-  // them) and every wave is past its last stage read.
-  barrier_only();
   const int wcol = wave * 32 * FRB;           // this wave's first weight row in the tile
   if (n0 + wcol >= N) return;                 // N % 64 == 0: a wave's 64 rows are all in or all out
   uint8_t* hst = lds + wave * 6144;           // h strip: 32 rows x 64 bf16 (128-byte rows)
@@ -449,6 +421,211 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     }
     wave_lds_sync();
   }
+}
+
+// Two waves per SIMD in either shape (amdgpu_waves_per_eu keeps the W = 4
+// kernel within the registers of two waves, so two workgroups fit a CU).
+// LORA: add the gate_up adapter's rank-r delta s (vg B_gu^T) before the
+// bias, as the down GEMM adds its adapter's.
+template <int W, bool LORA>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2, 2))) void gate_up_kernel(
+    const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
+    const uint8_t* __restrict__ scales, const uint16_t* __restrict__ bias,
+    const int32_t* __restrict__ sorted_rows, const Tile* __restrict__ tiles,
+    const int32_t* __restrict__ num_tiles, int H, int I, int k, float alpha, float limit,
+    const uint16_t* __restrict__ lora_B, const float* __restrict__ lora_v, float lora_scale,
+    int lora_r, uint16_t* __restrict__ h_out, uint16_t* __restrict__ a_out) {
+  using S = FwdShape<W>;
+  constexpr int XCHUNKS = S::XCH, FNT = S::NT;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[S::LDS];
+  const int N = 2 * I;
+  Tile tl;
+  int nt;
+  if (!xcd_item_range(tiles, num_tiles, (N + FNT - 1) / FNT, &tl, &nt)) return;
+  const int n0 = nt * FNT;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hlf = lane >> 5;
+  const int e = tl.expert;
+
+  uint32_t xrow[XCHUNKS];   // element offsets into x (T * H < 2^31)
+#pragma unroll
+  for (int j = 0; j < XCHUNKS; ++j) {
+    const int r = (XCHUNKS * wave + j) * 8 + lane / 8;
+    const int f = sorted_rows[tl.row0 + (r < tl.rows ? r : 0)];
+    xrow[j] = (uint32_t)(f / k) * (uint32_t)H;
+  }
+  const int nrows = min(FNT, N - n0);
+  f32x16 acc[FRB][4];
+  const int wrow_local = (wave * 32 * FRB < nrows ? wave * 32 * FRB : 0) + l32;
+  fwd_body<W>(x, xrow, codes + (int64_t)e * N * (H / 2), scales + (int64_t)e * N * (H / 32), H, n0,
+           nrows, wrow_local, (tl.rows + 31) / 32, lds, acc);
+  if (LORA) lora_delta(acc, tl, e, N, n0, nrows, wrow_local, lora_B, lora_v, lora_scale, lora_r);
+  // Epilogue through LDS: every wave's loads have landed (fwd_loop drained
+  // them) and every wave is past its last stage read.
+  barrier_only();
+  gate_up_epilogue(acc, tl, e, N, n0, I, bias, alpha, limit, lds, h_out, a_out);
+}
+
+// Block-scaled variant of gate_up: the gfx950 scaled MFMA
+// (v_mfma_scale_f32_32x32x64_f8f6f4) takes the packed FP4 weight codes and
+// their UE8M0 scales as they are stored, and the token rows quantized to
+// MXFP8 (E4M3 codes, UE8M0 per 32; NH = 2: a hi and a lo pass, x ~ hi +
+// lo) -- the pages' activation_format None (activations in the weights'
+// block-scaled family) next to the weight-only bf16 path above.  No weight
+// is decoded: an MFMA contracts 64 K; a lane of half h (lanes 32h..32h+31)
+// holds its row's scale of K block h (K 32h..32h+31) and, for a weight
+// row, that block's 32 FP4 codes (16 bytes straight from global memory).
+// Paired with 4-bit elements, the FP8 operand of half h holds K 16h..16h+15
+// and 32+16h..32+16h+15 of its routed row (two 16-byte LDS chunks): the
+// layout found by one-hot probes of the instruction.
+// Tile: 128 routed rows x 256 weight rows, four waves of 64 weight rows (two
+// 32-row MFMA blocks) by the four 32-row blocks of routed rows; the same
+// accumulator layout and epilogue as gate_up_kernel.  K % 64 == 0.
+constexpr int MX_XB = MT * 64;                 // one pass's codes per stage (8 KB)
+constexpr int MX_SB = MT * 2;                  // its scale bytes (2 blocks per row)
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+template <int NH>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void mx_gate_up_kernel(
+    const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs,
+    const uint8_t* __restrict__ xq_lo, const uint8_t* __restrict__ xs_lo,
+    const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+    const uint16_t* __restrict__ bias, const int32_t* __restrict__ sorted_rows,
+    const Tile* __restrict__ tiles, const int32_t* __restrict__ num_tiles, int H, int I, int k,
+    float alpha, float limit, uint16_t* __restrict__ h_out, uint16_t* __restrict__ a_out) {
+  constexpr int NT = 256;
+  constexpr int STAGE = NH * (MX_XB + MX_SB);
+  constexpr int LDSB = 2 * STAGE > 4 * 6144 ? 2 * STAGE : 4 * 6144;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[LDSB];
+  const int N = 2 * I;
+  Tile tl;
+  int nt;
+  if (!xcd_item_range(tiles, num_tiles, (N + NT - 1) / NT, &tl, &nt)) return;
+  const int n0 = nt * NT;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hlf = lane >> 5;
+  const int e = tl.expert;
+  const int nsteps = H / 64, KB = H / 32;
+  // weight rows of this lane's two MFMA blocks (rows past N read row N - 1)
+  const uint8_t* wrow[FRB];
+  const uint8_t* srow[FRB];
+#pragma unroll
+  for (int rb = 0; rb < FRB; ++rb) {
+    const int n = min(n0 + wave * 64 + 32 * rb + l32, N - 1);
+    wrow[rb] = codes + ((int64_t)e * N + n) * (H / 2) + 16 * hlf;
+    srow[rb] = scales + ((int64_t)e * N + n) * KB + hlf;
+  }
+  // staging: thread = (tile row r, 32-byte half hh) of each pass's 64-byte step row
+  const int r = tid >> 1, hh = tid & 1;
+  const int64_t tok = sorted_rows[tl.row0 + min(r, tl.rows - 1)] / k;
+  const uint8_t* xsrc[NH];
+  const uint8_t* ssrc[NH];
+  xsrc[0] = xq + tok * H + 32 * hh;
+  ssrc[0] = xs + tok * KB;
+  if constexpr (NH == 2) {
+    xsrc[1] = xq_lo + tok * H + 32 * hh;
+    ssrc[1] = xs_lo + tok * KB;
+  }
+  // LDS row r of a pass: four 16-byte chunks, chunk c at c ^ ((r / 4) % 4)
+  auto chunk_off = [](int row, int c) { return row * 64 + 16 * (c ^ ((row >> 2) & 3)); };
+
+  u32x4 xr[NH][2];
+  uint32_t sr[NH];
+  auto load_act = [&](int c) {
+#pragma unroll
+    for (int h2 = 0; h2 < NH; ++h2) {
+      xr[h2][0] = *reinterpret_cast<const u32x4*>(xsrc[h2] + 64 * c);
+      xr[h2][1] = *reinterpret_cast<const u32x4*>(xsrc[h2] + 64 * c + 16);
+      sr[h2] = hh == 0 ? *reinterpret_cast<const uint16_t*>(ssrc[h2] + 2 * c) : 0u;
+    }
+  };
+  auto stage_act = [&](uint8_t* st) {
+#pragma unroll
+    for (int h2 = 0; h2 < NH; ++h2) {
+      uint8_t* base = st + h2 * (MX_XB + MX_SB);
+      *reinterpret_cast<u32x4*>(base + chunk_off(r, 2 * hh)) = xr[h2][0];
+      *reinterpret_cast<u32x4*>(base + chunk_off(r, 2 * hh + 1)) = xr[h2][1];
+      if (hh == 0) *reinterpret_cast<uint16_t*>(base + MX_XB + 2 * r) = (uint16_t)sr[h2];
+    }
+  };
+  // the lane's weight codes and scales of one step (loaded after the
+  // previous step's MFMAs, so they are in flight across its barrier)
+  u32x4 wa[FRB];
+  uint32_t wsc[FRB];
+  auto load_w = [&](int c) {
+#pragma unroll
+    for (int rb = 0; rb < FRB; ++rb) {
+      wa[rb] = *reinterpret_cast<const u32x4*>(wrow[rb] + 32 * c);
+      wsc[rb] = srow[rb][2 * c];
+    }
+  };
+
+  f32x16 acc[FRB][4];
+#pragma unroll
+  for (int rb = 0; rb < FRB; ++rb)
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[rb][tb][q] = 0.0f;
+
+  load_act(0);
+  load_w(0);
+  stage_act(lds);
+  if (nsteps > 1) load_act(1);
+  __syncthreads();
+  for (int c = 0; c < nsteps; ++c) {
+    const int slot = c & 1;
+    const uint8_t* st = lds + slot * STAGE;
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      if (tb * 32 >= tl.rows) break;
+      const int p = tb * 32 + l32;
+#pragma unroll
+      for (int h2 = 0; h2 < NH; ++h2) {
+        const uint8_t* base = st + h2 * (MX_XB + MX_SB);
+        const u32x4 b0 = *reinterpret_cast<const u32x4*>(base + chunk_off(p, hlf));
+        const u32x4 b1 = *reinterpret_cast<const u32x4*>(base + chunk_off(p, hlf + 2));
+        const i32x8 bop = {(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3],
+                           (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+        const int sb = base[MX_XB + 2 * p + hlf];
+#pragma unroll
+        for (int rb = 0; rb < FRB; ++rb) {
+          const i32x8 aop = {(int)wa[rb][0], (int)wa[rb][1], (int)wa[rb][2], (int)wa[rb][3],
+                             0, 0, 0, 0};
+          // A = FP4 weights (format 4), B = FP8 E4M3 activations (format 0)
+          acc[rb][tb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              aop, bop, acc[rb][tb], 4, 0, 0, (int)wsc[rb], 0, sb);
+        }
+      }
+      // one routed-row block's operands live at a time
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (c + 1 < nsteps) {
+      load_w(c + 1);
+      stage_act(lds + (slot ^ 1) * STAGE);
+      if (c + 2 < nsteps) load_act(c + 2);
+    }
+    __syncthreads();
+  }
+  gate_up_epilogue(acc, tl, e, N, n0, I, bias, alpha, limit, lds, h_out, a_out);
+}
+
+hipError_t launch_mx_gate_up(const uint8_t* xq, const uint8_t* xs, const uint8_t* xq_lo,
+                             const uint8_t* xs_lo, const uint8_t* codes, const uint8_t* scales,
+                             const uint16_t* bias, const int32_t* sorted_rows, const Tile* tiles,
+                             const int32_t* num_tiles, int max_tiles, int H, int I, int k,
+                             float alpha, float limit, uint16_t* h_out, uint16_t* a_out,
+                             hipStream_t s) {
+  if (H % 64 || I % 32) return hipErrorInvalidValue;
+  const dim3 grid(((2 * I + 255) / 256) * max_tiles), block(256);
+  if (xq_lo)
+    hipLaunchKernelGGL(mx_gate_up_kernel<2>, grid, block, 0, s, xq, xs, xq_lo, xs_lo, codes, scales,
+                       bias, sorted_rows, tiles, num_tiles, H, I, k, alpha, limit, h_out, a_out);
+  else
+    hipLaunchKernelGGL(mx_gate_up_kernel<1>, grid, block, 0, s, xq, xs, xq_lo, xs_lo, codes, scales,
+                       bias, sorted_rows, tiles, num_tiles, H, I, k, alpha, limit, h_out, a_out);
+  return hipGetLastError();
 }
 
 // LORA: add the rank-r delta s (v B_e^T) (a template parameter: a runtime

@@ -13,6 +13,10 @@ struct Tile;
 // quant.hip
 hipError_t launch_quantize(const float* w, int64_t rows, int64_t K, uint8_t* codes,
                            uint8_t* scales, hipStream_t s);
+// MXFP8 (E4M3, UE8M0 per 32) of bf16 rows; with lo_codes also the residual
+hipError_t launch_mxfp8_quantize(const uint16_t* x, int64_t rows, int64_t K, uint8_t* codes,
+                                 uint8_t* scales, uint8_t* lo_codes, uint8_t* lo_scales,
+                                 hipStream_t s);
 hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows,
                              int64_t K, int out_bf16, void* out, hipStream_t s);
 
@@ -65,6 +69,14 @@ hipError_t launch_down(const uint16_t* a, const uint8_t* codes, const uint8_t* s
                        uint16_t* y_w, hipStream_t s);
 hipError_t launch_combine(const uint16_t* y_w, int64_t T, int H, int k, uint16_t* out,
                           hipStream_t s);
+// gate_up on the block-scaled MFMA: FP4 weights as stored, activations as
+// MXFP8 codes [T, H] + scales [T, H/32] (with xq_lo: a second, residual pass)
+hipError_t launch_mx_gate_up(const uint8_t* xq, const uint8_t* xs, const uint8_t* xq_lo,
+                             const uint8_t* xs_lo, const uint8_t* codes, const uint8_t* scales,
+                             const uint16_t* bias, const int32_t* sorted_rows, const Tile* tiles,
+                             const int32_t* num_tiles, int max_tiles, int H, int I, int k,
+                             float alpha, float limit, uint16_t* h_out, uint16_t* a_out,
+                             hipStream_t s);
 
 // gemm_dec.hip: forward GEMMs for few rows per expert (weight-streaming)
 int dec_max_k();   // largest contraction length the decode kernels take

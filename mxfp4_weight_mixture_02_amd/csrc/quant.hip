@@ -78,6 +78,112 @@ __global__ __launch_bounds__(256) void dequantize_kernel(const uint32_t* __restr
   }
 }
 
+// MXFP8 activation quantization ("Integrate finegrained kernels", commit
+// notes: MXFP8 through row-wise quantizers; activation_format None = the
+// weights' block-scaled format).  One thread per 32-element block of a bf16
+// row: scale exponent e = the smallest integer with amax <= 448 * 2^e
+// (clamped to [-127, 127], 0 for an all-zero block gives -127), elements
+// x * 2^-e rounded to the nearest OCP E4M3 value, ties to the even
+// mantissa.  With lo: the residual x - deq(code) (exact in fp32) is
+// quantized the same way into its own codes and scale.
+
+// E4M3 code (sign in bit 7) of v, |v| <= 448, round to nearest even.
+__device__ __forceinline__ uint32_t e4m3_encode(float v) {
+  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+  const float a = fabsf(v);
+  uint32_t code;
+  if (a < 0.015625f) {                       // below 2^-6: multiples of 2^-9
+    code = (uint32_t)rintf(a * 512.0f);      // 8 is the smallest normal
+  } else {
+    const uint32_t b = __float_as_uint(a);
+    int ex = (int)(b >> 23) - 127;
+    const uint32_t mant = b & 0x7FFFFFu;
+    uint32_t m3 = mant >> 20;
+    const uint32_t rem = mant & 0xFFFFFu;
+    if (rem > 0x80000u || (rem == 0x80000u && (m3 & 1u))) ++m3;
+    if (m3 == 8u) {
+      m3 = 0;
+      ++ex;
+    }
+    code = ((uint32_t)(ex + 7) << 3) | m3;
+  }
+  return sign | code;
+}
+
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  const float mag = e == 0 ? (float)m * 0.001953125f : ldexpf(1.0f + (float)m * 0.125f, (int)e - 7);
+  return (c & 0x80u) ? -mag : mag;
+}
+
+// e for a block with largest magnitude amax (finite, >= 0)
+__device__ __forceinline__ int mx8_exponent(float amax) {
+  if (amax == 0.0f) return -127;
+  int ex;
+  const float fr = frexpf(amax, &ex);        // amax = fr * 2^ex, fr in [0.5, 1)
+  // amax <= 1.75 * 2^(e + 8)  <=>  e >= ex - 9 + (fr > 0.875)
+  const int e = ex - 9 + (fr > 0.875f ? 1 : 0);
+  return max(-127, min(127, e));
+}
+
+// 32 values -> 32 codes (as 8 words) and the scale byte; v becomes the
+// residual v - deq.
+__device__ __forceinline__ uint32_t mx8_block(float (&v)[32], uint32_t (&w)[8]) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  const int e = mx8_exponent(amax);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) w[i] = 0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const uint32_t c = e4m3_encode(ldexpf(v[i], -e));
+    w[i >> 2] |= c << (8 * (i & 3));
+    v[i] -= ldexpf(e4m3_value(c), e);
+  }
+  return (uint32_t)(e + 127);
+}
+
+__global__ __launch_bounds__(256) void mxfp8_quantize_kernel(
+    const uint16_t* __restrict__ x, int64_t nblk, uint8_t* __restrict__ codes,
+    uint8_t* __restrict__ scales, uint8_t* __restrict__ lo_codes, uint8_t* __restrict__ lo_scales) {
+  const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (b >= nblk) return;
+  float v[32];
+  const u32x4* src = reinterpret_cast<const u32x4*>(x + b * 32);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const u32x4 r = src[q];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      v[8 * q + 2 * m] = bf16_to_f32((uint16_t)(r[m] & 0xFFFFu));
+      v[8 * q + 2 * m + 1] = bf16_to_f32((uint16_t)(r[m] >> 16));
+    }
+  }
+  uint32_t w[8];
+  scales[b] = (uint8_t)mx8_block(v, w);
+  u32x4* dst = reinterpret_cast<u32x4*>(codes + b * 32);
+  dst[0] = u32x4{w[0], w[1], w[2], w[3]};
+  dst[1] = u32x4{w[4], w[5], w[6], w[7]};
+  if (lo_codes) {
+    lo_scales[b] = (uint8_t)mx8_block(v, w);
+    u32x4* ld = reinterpret_cast<u32x4*>(lo_codes + b * 32);
+    ld[0] = u32x4{w[0], w[1], w[2], w[3]};
+    ld[1] = u32x4{w[4], w[5], w[6], w[7]};
+  }
+}
+
+hipError_t launch_mxfp8_quantize(const uint16_t* x, int64_t rows, int64_t K, uint8_t* codes,
+                                 uint8_t* scales, uint8_t* lo_codes, uint8_t* lo_scales,
+                                 hipStream_t s) {
+  if (K % 32) return hipErrorInvalidValue;
+  const int64_t nblk = rows * (K / 32);
+  if (nblk == 0) return hipSuccess;
+  hipLaunchKernelGGL(mxfp8_quantize_kernel, dim3((unsigned)((nblk + 255) / 256)), dim3(256), 0, s,
+                     x, nblk, codes, scales, lo_codes, lo_scales);
+  return hipGetLastError();
+}
+
 hipError_t launch_quantize(const float* w, int64_t rows, int64_t K, uint8_t* codes,
                            uint8_t* scales, hipStream_t s) {
   int64_t n4 = rows * K / 4;

@@ -34,9 +34,10 @@ class Dims(ctypes.Structure):
                 ("E", ctypes.c_int32), ("k", ctypes.c_int32),
                 ("swiglu_alpha", ctypes.c_float), ("swiglu_limit", ctypes.c_float),
                 ("lora_rank", ctypes.c_int32), ("lora_scale", ctypes.c_float),
-                ("lora_targets", ctypes.c_int32)]
+                ("lora_targets", ctypes.c_int32), ("activation_format", ctypes.c_int32)]
 
 LORA_DOWN, LORA_GATE_UP = 1, 2
+ACT_FORMATS = {"bf16": 0, "mxfp8": 1, "mxfp8x2": 2}
 
 
 class Weights(ctypes.Structure):
@@ -91,6 +92,8 @@ def lib() -> ctypes.CDLL:
         L.mxfp4_moe_backward.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Weights),
                                          ctypes.POINTER(Saved), vp, vp, ctypes.POINTER(Grads), vp,
                                          ctypes.c_size_t, vp]
+        L.mxfp8_quantize.restype = i32
+        L.mxfp8_quantize.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp]
         L.mxfp4_quantize.restype = i32
         L.mxfp4_quantize.argtypes = [vp, i64, i64, vp, vp, vp]
         L.mxfp4_dequantize.restype = i32
@@ -102,7 +105,7 @@ def lib() -> ctypes.CDLL:
 def header_symbols() -> list[str]:
     """Function names declared in include/mxfp4_moe.h."""
     txt = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(mxfp4_\w+)\s*\(", txt, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(mxfp[48]_\w+)\s*\(", txt, re.M)))
 
 
 def _check(fn, rc):
@@ -185,6 +188,7 @@ class MoeLayer:
     lora_scale: float = 1.0
     lora_gu_A: torch.Tensor | None = None    # bf16 [E, r, H]   adapter on gate_up
     lora_gu_B: torch.Tensor | None = None    # bf16 [E, 2I, r]
+    act_format: str = "bf16"                 # gate_up input: bf16 | mxfp8 | mxfp8x2
 
     @property
     def E(self):
@@ -210,8 +214,10 @@ class MoeLayer:
                (LORA_GATE_UP if self.lora_gu_A is not None else 0)
 
     def dims(self, T):
+        if self.act_format not in ACT_FORMATS:
+            raise ValueError(f"act_format must be one of {sorted(ACT_FORMATS)}")
         return Dims(T, self.H, self.I, self.E, self.k, self.alpha, self.limit, self.lora_rank,
-                    self.lora_scale, self.lora_targets)
+                    self.lora_scale, self.lora_targets, ACT_FORMATS[self.act_format])
 
     def check_shapes(self):
         """Every parameter's shape and dtype against E, H, I (and the rank)."""
@@ -490,3 +496,19 @@ def mxfp4_moe_backward(layer: MoeLayer, saved: SavedState, x: torch.Tensor, dy: 
                                   _ptr(dy), ctypes.byref(g), _ptr(ws), ws.numel(), _stream())
     _check("mxfp4_moe_backward", rc)
     return {k: v for k, v in out.items() if v is not None}
+
+
+def mxfp8_quantize(x: torch.Tensor, lo: bool = False):
+    """Row-wise MXFP8 of bf16 x [rows, K]: (codes uint8 [rows, K], scales
+    uint8 [rows, K/32]) and with ``lo`` also the residual's pair."""
+    if x.dim() != 2 or x.dtype != torch.bfloat16:
+        raise ValueError("x must be a 2-D bf16 tensor")
+    x = _dev(x.contiguous(), torch.bfloat16, "x")
+    rows, K = x.shape
+    u8 = dict(dtype=torch.uint8, device=x.device)
+    c, s = torch.empty((rows, K), **u8), torch.empty((rows, K // 32), **u8)
+    lc = torch.empty((rows, K), **u8) if lo else None
+    ls = torch.empty((rows, K // 32), **u8) if lo else None
+    _check("mxfp8_quantize", lib().mxfp8_quantize(_ptr(x), rows, K, _ptr(c), _ptr(s), _ptr(lc),
+                                                  _ptr(ls), _stream()))
+    return (c, s, lc, ls) if lo else (c, s)

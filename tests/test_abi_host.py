@@ -11,7 +11,7 @@ from mxfp4_weight_mixture_02_amd.native import Dims, Grads, Saved, SavedSizes, W
 
 EXPECTED = {"mxfp4_moe_workspace_bytes", "mxfp4_moe_saved_bytes", "mxfp4_moe_forward",
             "mxfp4_moe_forward_noalloc", "mxfp4_moe_backward_dx", "mxfp4_moe_backward",
-            "mxfp4_quantize", "mxfp4_dequantize", "mxfp4_last_error",
+            "mxfp4_quantize", "mxfp4_dequantize", "mxfp8_quantize", "mxfp4_last_error",
             "mxfp4_moe_kernel_timing", "mxfp4_moe_kernel_times"}
 
 
@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol(L):
 
 def _dims(**kw):
     d = dict(T=16, H=64, I=64, E=4, k=2, swiglu_alpha=1.702, swiglu_limit=7.0, lora_rank=0,
-             lora_scale=1.0, lora_targets=0)
+             lora_scale=1.0, lora_targets=0, activation_format=0)
     d.update(kw)
     return Dims(**d)
 
@@ -282,3 +282,22 @@ def test_full_backward_validation(L):
     rc = L.mxfp4_moe_backward(ctypes.byref(d), ctypes.byref(w), ctypes.byref(sv), FAKE, FAKE,
                               ctypes.byref(g), FAKE, b2, None)
     assert rc == -3 and "workspace" in _err(L)
+
+
+def test_activation_format_validation(L):
+    for fmt in (1, 2):
+        d = _dims(activation_format=fmt)
+        f0 = L.mxfp4_moe_workspace_bytes(ctypes.byref(d), 0)
+        assert f0 > L.mxfp4_moe_workspace_bytes(ctypes.byref(_dims()), 0)
+        assert L.mxfp4_moe_workspace_bytes(ctypes.byref(d), 2) == \
+            L.mxfp4_moe_workspace_bytes(ctypes.byref(_dims()), 2)
+    assert L.mxfp4_moe_workspace_bytes(ctypes.byref(_dims(activation_format=3)), 0) == 0
+    assert "activation_format" in _err(L)
+    assert L.mxfp4_moe_workspace_bytes(ctypes.byref(_dims(activation_format=1, H=96)), 0) == 0
+    assert "H % 64" in _err(L)
+    d = _dims(activation_format=2, lora_rank=16, lora_targets=2)
+    assert L.mxfp4_moe_workspace_bytes(ctypes.byref(d), 0) == 0 and "gate_up adapter" in _err(L)
+    assert L.mxfp8_quantize(None, 4, 64, FAKE, FAKE, None, None, None) == -1
+    assert L.mxfp8_quantize(FAKE, 4, 48, FAKE, FAKE, None, None, None) == -2
+    assert L.mxfp8_quantize(FAKE, 4, 64, FAKE, FAKE, FAKE, None, None) == -1
+    assert L.mxfp8_quantize(FAKE + 8, 4, 64, FAKE, FAKE, None, None, None) == -1

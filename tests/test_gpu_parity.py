@@ -21,8 +21,9 @@ import torch
 
 import moe_synth as syn
 from mxfp4_weight_mixture_02_amd import (Mxfp4Error, mxfp4_dequantize, mxfp4_moe_backward,
-                                         mxfp4_moe_backward_dx, mxfp4_moe_forward, mxfp4_quantize)
-from oracle import moe, mxfp4
+                                         mxfp4_moe_backward_dx, mxfp4_moe_forward, mxfp4_quantize,
+                                         mxfp8_quantize)
+from oracle import moe, mxfp4, mxfp8
 
 from gpu_helpers import (DEV, assert_bytes_equal, assert_close, assert_routing_equal, bf16_tensor,
                          cache_dequant, device_layer, min_topk_gap, oracle_layer, to_f64)
@@ -331,6 +332,58 @@ def test_full_backward_base_weight_gradients(shape):
 def test_full_backward_with_adapters(r, gu, dn):
     _run_full_backward(syn.spec("tiny", T=300, H=192, I=320, E=3, k=2, lora_rank=r,
                                 lora_gate_up=gu, lora_down=dn), lora_scale=4.0)
+
+
+def test_mxfp8_quantize_bytes_match_oracle():
+    # row-wise MXFP8 (hi and the residual lo) against the oracle, byte for
+    # byte: normal activations, wide exponent ranges, an all-zero block,
+    # values on the E4M3 grid and its midpoints, subnormal-range values
+    rng = np.random.default_rng(21)
+    rows = [rng.standard_normal(256),
+            rng.standard_normal(256) * 2.0 ** rng.integers(-40, 40, 256),
+            np.zeros(256),
+            np.repeat(mxfp8.e4m3_decode(rng.integers(0, 0x7E, 8)), 32) * 2.0 ** -3,
+            rng.standard_normal(256) * 1e-3,
+            np.linspace(-448, 448, 256)]
+    x = np.stack(rows)
+    xb = (x.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)   # truncate to bf16 bits
+    xt = bf16_tensor(xb).to(DEV)
+    hc, hs, lc, ls = mxfp8_quantize(xt, lo=True)
+    torch.cuda.synchronize()
+    ref = mxfp8.quantize_hi_lo(moe.bf16_to_f64(xb))
+    for name, g, r in zip(("codes", "scales", "lo codes", "lo scales"), (hc, hs, lc, ls), ref):
+        gn = g.cpu().numpy()
+        bad = np.flatnonzero(gn.ravel() != r.ravel())
+        assert bad.size == 0, f"{name}: {bad.size} bytes differ, first at {bad[:5]}"
+
+
+@pytest.mark.parametrize("fmt", ["mxfp8x2", "mxfp8"])
+@pytest.mark.parametrize("shape", [dict(T=300, H=192, I=320, E=3, k=2),
+                                   dict(T=40, H=128, I=96, E=4, k=2),
+                                   dict(T=5, H=256, I=160, E=3, k=2)])
+def test_block_scaled_activation_forward(fmt, shape):
+    # the scaled-MFMA gate_up on the packed FP4 weights and MXFP8 token rows,
+    # against the oracle's forward with the same quantized activations;
+    # with the hi + lo pair it also meets the bar against the bf16 forward
+    s = syn.spec("tiny", **shape)
+    _say(f"block-scaled activations {fmt} {shape}")
+    dl = device_layer(s)
+    dl.act_format = fmt
+    ol, _ = oracle_layer(s)
+    xb = syn.tokens(s)
+    out, sv = mxfp4_moe_forward(dl, bf16_tensor(xb).to(DEV), saved=True)
+    torch.cuda.synchronize()
+    ref, r, cache = moe.forward(ol, xb, act_format=fmt)
+    assert_routing_equal(sv, r)
+    assert_close(to_f64(out), ref, f"out ({fmt})")
+    href = np.stack([cache[int(f)][0] for f in r.sorted_rows])
+    assert_close(to_f64(sv.h), href, f"saved h ({fmt})")
+    plain, _, _ = moe.forward(ol, xb, routing=r)
+    g = to_f64(out)
+    rel = np.abs(g - plain).max() / np.abs(plain).max()
+    print(f"{fmt}: max_rel against the bf16 forward {rel:.3e}", flush=True)
+    if fmt == "mxfp8x2":
+        assert_close(g, plain, "out (mxfp8x2 vs bf16 oracle)")
 
 
 def test_forward_is_deterministic():
