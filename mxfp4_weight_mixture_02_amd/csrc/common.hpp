@@ -188,17 +188,27 @@ struct Tile {
   int32_t expert;
   int32_t row0;  // first sorted position
   int32_t rows;  // 1..MT
-  int32_t pad;
+  // forward lists: this tile's index q among its expert's tiles (bits 0-15)
+  // and that expert's tile count n (bits 16-31, 0xFFFF when n >= 0xFFFF);
+  // 0 in the backward's dealt list
+  int32_t pos;
 };
+__host__ __device__ constexpr int32_t tile_pos(int32_t q, int32_t n) {
+  return (int32_t)(((uint32_t)(n < 0xFFFF ? n : 0xFFFF) << 16) | ((uint32_t)q & 0xFFFFu));
+}
 
 // Work items of the grouped GEMMs.  Workgroups are dealt to the 8 XCDs
 // round-robin by block index, and each XCD has its own L2.
 //
 // Tile list in expert order (forward): with L live work items (row tiles x
-// column tiles, column tile fastest), XCD i gets the contiguous range of
-// items [start_i, start_i + L/8 (+1)), so the column tiles of a row tile
-// (same activations) and consecutive row tiles of an expert (same weights)
-// run together on one L2.  Returns false for blocks past the live items.
+// column tiles), XCD i gets the contiguous range of items [start_i,
+// start_i + L/8 (+1)).  Within it each expert's items go row tile fastest
+// (item t_e C + c n_e + q is row tile q of column tile c, for an expert
+// with n_e tiles from list index t_e), so the row tiles of an expert load
+// the same weight columns at the same time and the XCD's L2 serves them
+// once, while the column tiles of a row tile (same activations) still run
+// close together.  Experts with 0xFFFF or more tiles go column tile
+// fastest.  Returns false for blocks past the live items.
 __device__ __forceinline__ bool xcd_item_range(const Tile* __restrict__ tiles,
                                                const int32_t* __restrict__ num_tiles,
                                                int col_tiles, Tile* tl, int* col_tile) {
@@ -208,8 +218,18 @@ __device__ __forceinline__ bool xcd_item_range(const Tile* __restrict__ tiles,
   const int xcd = b & 7, idx = b >> 3;
   const int base = L >> 3, extra = L & 7;
   const int item = xcd * base + min(xcd, extra) + idx;
-  *tl = tiles[item / col_tiles];
-  *col_tile = item % col_tiles;
+  const int j = item / col_tiles;
+  const Tile t = tiles[j];
+  const uint32_t n = (uint32_t)t.pos >> 16, q = (uint32_t)t.pos & 0xFFFFu;
+  if (n == 0 || n == 0xFFFF) {
+    *tl = t;
+    *col_tile = item % col_tiles;
+    return true;
+  }
+  const int te = j - (int)q;
+  const int local = item - te * col_tiles;
+  *tl = tiles[te + local % (int)n];
+  *col_tile = local / (int)n;
   return true;
 }
 

@@ -495,6 +495,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const Tile* __restrict__ tiles, const int32_t* __restrict__ num_tiles, int H, int I, int k,
     float alpha, float limit, uint16_t* __restrict__ h_out, uint16_t* __restrict__ a_out) {
   constexpr int NT = 256;
+  constexpr int MX_PD = NH == 1 ? 3 : 2;        // weight steps in flight per lane
   constexpr int STAGE = NH * (MX_XB + MX_SB);
   constexpr int LDSB = 2 * STAGE > 4 * 6144 ? 2 * STAGE : 4 * 6144;
   __shared__ __attribute__((aligned(16))) uint8_t lds[LDSB];
@@ -549,11 +550,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       if (hh == 0) *reinterpret_cast<uint16_t*>(base + MX_XB + 2 * r) = (uint16_t)sr[h2];
     }
   };
-  // the lane's weight codes and scales of one step (loaded after the
-  // previous step's MFMAs, so they are in flight across its barrier)
-  u32x4 wa[FRB];
-  uint32_t wsc[FRB];
-  auto load_w = [&](int c) {
+  // the lane's weight codes and scales MX_PD steps ahead: ring slot j
+  // holds step c with c % MX_PD == j (the step loop is unrolled by MX_PD,
+  // so slots are never moved while their loads are in flight)
+  u32x4 wq[MX_PD][FRB];
+  uint32_t wsq[MX_PD][FRB];
+  auto load_w = [&](int c, u32x4 (&wa)[FRB], uint32_t (&wsc)[FRB]) {
 #pragma unroll
     for (int rb = 0; rb < FRB; ++rb) {
       wa[rb] = *reinterpret_cast<const u32x4*>(wrow[rb] + 32 * c);
@@ -569,14 +571,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[rb][tb][q] = 0.0f;
 
-  load_act(0);
-  load_w(0);
-  stage_act(lds);
-  if (nsteps > 1) load_act(1);
-  __syncthreads();
-  for (int c = 0; c < nsteps; ++c) {
-    const int slot = c & 1;
-    const uint8_t* st = lds + slot * STAGE;
+  auto step = [&](int c, const u32x4 (&wa)[FRB], const uint32_t (&wsc)[FRB]) {
+    const uint8_t* st = lds + (c & 1) * STAGE;
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
       if (tb * 32 >= tl.rows) break;
@@ -597,16 +593,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           acc[rb][tb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
               aop, bop, acc[rb][tb], 4, 0, 0, (int)wsc[rb], 0, sb);
         }
+        if (NH > 1) __builtin_amdgcn_sched_barrier(0);
       }
       // one routed-row block's operands live at a time
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (c + 1 < nsteps) {
-      load_w(c + 1);
-      stage_act(lds + (slot ^ 1) * STAGE);
-      if (c + 2 < nsteps) load_act(c + 2);
+  };
+
+  load_act(0);
+#pragma unroll
+  for (int j = 0; j < MX_PD; ++j) load_w(min(j, nsteps - 1), wq[j], wsq[j]);
+  stage_act(lds);
+  if (nsteps > 1) load_act(1);
+  __syncthreads();
+  // steps past nsteps (the last group's tail) compute nothing; their weight
+  // loads re-read the last step, in bounds
+  for (int c0 = 0; c0 < nsteps; c0 += MX_PD) {
+#pragma unroll
+    for (int j = 0; j < MX_PD; ++j) {
+      const int c = c0 + j;
+      if (c < nsteps) step(c, wq[j], wsq[j]);
+      load_w(min(c + MX_PD, nsteps - 1), wq[j], wsq[j]);
+      if (c + 1 < nsteps) {
+        stage_act(lds + ((c + 1) & 1) * STAGE);
+        if (c + 2 < nsteps) load_act(c + 2);
+      }
+      __syncthreads();
     }
-    __syncthreads();
   }
   gate_up_epilogue(acc, tl, e, N, n0, I, bias, alpha, limit, lds, h_out, a_out);
 }

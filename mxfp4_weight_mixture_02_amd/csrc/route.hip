@@ -439,7 +439,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(
       tl.expert = tid;
       tl.row0 = off[tid] + q * MT;
       tl.rows = min(MT, n - q * MT);
-      tl.pad = 0;
+      tl.pos = tile_pos(q, (n + MT - 1) / MT);
       tiles[tstart[tid] + q] = tl;
     }
   }
@@ -477,8 +477,9 @@ __device__ __forceinline__ void write_tiles(const int32_t* offs, int E, int mt, 
   __syncthreads();
   for (int e = tid; e < E; e += blockDim.x) {
     const int32_t o = offs[e], n = offs[e + 1] - o;
-    for (int32_t q = 0; q * mt < n; ++q)
-      tiles[start[e] + q] = Tile{e, o + q * mt, min(mt, n - q * mt), 0};
+    const int32_t nt = (n + mt - 1) / mt;
+    for (int32_t q = 0; q < nt; ++q)
+      tiles[start[e] + q] = Tile{e, o + q * mt, min(mt, n - q * mt), tile_pos(q, nt)};
   }
   __syncthreads();
 }
