@@ -21,8 +21,10 @@
 //
 // Weight path.  The workgroup's slice of each 64-row step (64 stored rows x
 // 256 columns: 8 KB of packed codes) is copied into LDS as raw bytes, and
-// its 64 x 8 scale bytes into a transposed LDS table (per scale block, the
-// rows in the order the lanes read them).  The MFMA A-operand needs
+// its 64 x 8 scale bytes into a transposed LDS table of words (per scale
+// block, a lane's four sub-steps' words side by side, so one 16-byte read
+// per step gives a lane its row's scale for every sub-step; the 16 lanes
+// that decode the same 8 rows then broadcast them with DPP row_newbcast).  The MFMA A-operand needs
 // 8 consecutive c of one output column per lane.  gfx950's 8-bit
 // transposing LDS read (ds_read_b64_tr_b8) gives each lane 8 rows x one
 // code byte, i.e. 8 consecutive c for the column pair (2m, 2m+1); the lane
@@ -93,7 +95,7 @@ struct GArgs {
   uint32_t soff;            // byte offset of its scale byte (step 0)
   uint32_t cstep, sstep;    // bytes per step of 64 stored rows
   uint32_t aoff;            // code-tile offset of the transposing read (sub-step 0)
-  uint32_t sofs;            // scale-table offset of the lane's 8 scale words (sub-step 0)
+  uint32_t sofs;            // scale-table offset of the lane's four scale words
   uint32_t boff[4];         // activation-stage offsets of the B-fragment reads per sub-step (row block 0)
   uint32_t tailmask;        // pieces past C in a half last step: 1 activations, 2 code, 4 scale
   int wave;                 // wave index (uniform)
@@ -110,7 +112,7 @@ struct GFrags {
   bf16x8 a[2][2];
   bf16x8 b[2][NRB > 0 ? NRB : 1];
   i32x2 raw[2];
-  u32x4 sc[2][2];
+  u32x4 sq;          // this step's scale words of the lane's row, one per sub-step
 };
 
 // rowoff(p): element offset of activation row p (clamping rows past the
@@ -139,11 +141,11 @@ __device__ __forceinline__ void g_setup(GArgs& g, const uint16_t* xbase, RowOff 
   const int c0 = tid >> 3, j = (tid & 7) ^ (c0 & 7);
   const int col = (o0 + 32 * j < O) ? o0 + 32 * j : 0;   // past O: any valid column
   g.coff = (uint32_t)c0 * (uint32_t)(O / 2) + col / 2;
-  // scales: table word tid = 64 b + 32 h + 8 s + r holds row 16 s + 8 h + r
-  // (sub-step s, half h, r < 8) of scale block b = wave, so a lane's 8 rows
-  // of one sub-step are 8 consecutive words
+  // scales: table word tid = 64 b + 32 h + 4 r + s holds row 16 s + 8 h + r
+  // (sub-step s, half h, r < 8) of scale block b = wave, so the four
+  // sub-steps' words of one row are consecutive
   {
-    const int r = lane & 7, ss = (lane >> 3) & 3, h = lane >> 5;
+    const int ss = lane & 3, r = (lane >> 2) & 7, h = lane >> 5;
     const int row = 16 * ss + 8 * h + r;
     const int scol = (o0 + 32 * wave < O) ? o0 + 32 * wave : 0;
     g.soff = (uint32_t)row * (uint32_t)(O / 32) + scol / 32;
@@ -157,8 +159,9 @@ __device__ __forceinline__ void g_setup(GArgs& g, const uint16_t* xbase, RowOff 
   const int row = 8 * (grp >> 1) + (jj >> 1);
   const int chunk = 2 * wo + (grp & 1);
   g.aoff = row * (GO / 2) + 16 * (chunk ^ (row & 7)) + 8 * (jj & 1);
-  // the lane's 8 rows 8 (grp / 2) .. + 7 of scale block 2 wo + grp % 2
-  g.sofs = GCB + ((2 * wo + (grp & 1)) * GKC + 32 * (grp >> 1)) * 4;
+  // the words of row 8 (grp / 2) + jj % 8 of scale block 2 wo + grp % 2
+  // (lanes jj and jj + 8 read the same ones)
+  g.sofs = GCB + ((2 * wo + (grp & 1)) * GKC + 32 * (grp >> 1) + 4 * (jj & 7)) * 4;
   const int prel = lane & 31;
 #pragma unroll
   for (int s = 0; s < 4; ++s) g.boff[s] = GCB + GSB + prel * 128 + 16 * ((2 * s + (lane >> 5)) ^ x_swz(prel));
@@ -168,7 +171,7 @@ __device__ __forceinline__ void g_setup(GArgs& g, const uint16_t* xbase, RowOff 
   // code rows >= 32 and the scale rows >= 32 lie past C
   {
     const int ch = (lane & 7) ^ ((lane >> 3) & 7);   // the chunk of all 4 of the lane's pieces
-    g.tailmask = (ch >= 4 ? 1u : 0u) | (c0 >= 32 ? 2u : 0u) | (((lane >> 3) & 3) >= 2 ? 4u : 0u);
+    g.tailmask = (ch >= 4 ? 1u : 0u) | (c0 >= 32 ? 2u : 0u) | ((lane & 3) >= 2 ? 4u : 0u);
   }
 }
 
@@ -195,16 +198,20 @@ __device__ __forceinline__ void g_dma(const GArgs& g, uint8_t* __restrict__ st, 
   __builtin_amdgcn_global_load_lds((gptr_t)sp, (lptr_t)(st + GCB + g.wave * 256), 1, 0, 0);
 }
 
-// LDS reads from stage st: the transposed code bytes and the 8 scale words
-// of sub-step s (the wave's double block) into slot s % 2, and sub-step s's
-// NRB B-fragments into slot bi.
+// LDS reads from stage st: the transposed code bytes of sub-step s (the
+// wave's double block) into slot s % 2; the lane's scale words of the
+// step; and sub-step s's NRB B-fragments into slot bi.
 template <int NRB>
 __device__ __forceinline__ void g_read_a(const GArgs& g, const uint8_t* __restrict__ st, int s,
                                          GFrags<NRB>& F) {
   F.raw[s & 1] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
       (lds_i32x2*)(const_cast<uint8_t*>(st) + g.aoff + s * 16 * (GO / 2)));
-  F.sc[s & 1][0] = *reinterpret_cast<const u32x4*>(st + g.sofs + s * 32);
-  F.sc[s & 1][1] = *reinterpret_cast<const u32x4*>(st + g.sofs + s * 32 + 16);
+}
+
+template <int NRB>
+__device__ __forceinline__ void g_read_s(const GArgs& g, const uint8_t* __restrict__ st,
+                                         GFrags<NRB>& F) {
+  F.sq = *reinterpret_cast<const u32x4*>(st + g.sofs);
 }
 
 template <int NRB>
@@ -215,19 +222,30 @@ __device__ __forceinline__ void g_read_b(const GArgs& g, const uint8_t* __restri
     F.b[bi][j] = *reinterpret_cast<const bf16x8*>(st + g.boff[s] + (wp + 2 * j) * 4096);
 }
 
+// row_newbcast:R -- lane R of each 16-lane row to the whole row
+template <int R>
+__device__ __forceinline__ uint32_t row_bcast(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x150 + R, 0xF, 0xF, false);
+}
+
 // Decode sub-step s's raw bytes into A-fragment slot ai: fragment 0 holds
 // the even columns, 1 the odd ones.  Byte r of the 8 is row r of the lane's
-// 8 (its own scale word, the UE8M0 byte moved to the exponent field: the
-// scaled conversion reads only that field of its scale operand); its two
-// nibbles are the column pair, so one scaled conversion gives (even, odd)
-// as packed bf16, and byte permutes gather the evens and the odds.
+// 8, whose scale word lane r of the 16-lane group holds (the UE8M0 byte
+// moved to the exponent field: the scaled conversion reads only that field
+// of its scale operand); its two nibbles are the column pair, so one scaled
+// conversion gives (even, odd) as packed bf16, and byte permutes gather the
+// evens and the odds.
 template <int NRB>
 __device__ __forceinline__ void g_decode(GFrags<NRB>& F, int ai, int s) {
   uint32_t pr[8];
+  const uint32_t own = F.sq[s] << 23;
+  const uint32_t scw[8] = {row_bcast<0>(own), row_bcast<1>(own), row_bcast<2>(own),
+                           row_bcast<3>(own), row_bcast<4>(own), row_bcast<5>(own),
+                           row_bcast<6>(own), row_bcast<7>(own)};
 #pragma unroll
   for (int r = 0; r < 8; ++r) {
     const uint32_t w = (uint32_t)F.raw[s & 1][r >> 2];
-    const float sc = __builtin_bit_cast(float, F.sc[s & 1][r >> 2][r & 3] << 23);
+    const float sc = __builtin_bit_cast(float, scw[r]);
     switch (r & 3) {
       case 0: pr[r] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0)); break;
       case 1: pr[r] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1)); break;
@@ -317,8 +335,8 @@ __device__ __forceinline__ void g_step(GFrags<NRB>& F, const GArgs& g, int k,
                                        const uint8_t* __restrict__ cur,
                                        const uint8_t* __restrict__ nxt, uint8_t* __restrict__ dst,
                                        int wp, f32x16 (&acc)[2][4]) {
-  // 16 decode instructions spread over the MFMAs
-  constexpr int NM = 2 * NRB, FPER = (16 + NM - 1) / (NM > 0 ? NM : 1);
+  // 25 decode instructions spread over the MFMAs
+  constexpr int NM = 2 * NRB, FPER = (25 + NM - 1) / (NM > 0 ? NM : 1);
   __builtin_amdgcn_sched_barrier(0);
   g_dma(g, dst, min(k + 2, g.nsteps - 1));
   __builtin_amdgcn_sched_barrier(0);
@@ -330,9 +348,9 @@ __device__ __forceinline__ void g_step(GFrags<NRB>& F, const GArgs& g, int k,
       g_mfmas<NRB>(F, s & 1, s & 1, acc);
       g_decode<NRB>(F, (s + 1) & 1, s + 1);
       if (s == 0)
-        g_order<3 + NRB, NM, NM, FPER>();
+        g_order<1 + NRB, NM, NM, FPER>();
       else if (s == 1)
-        g_order_mfirst<3 + NRB, NM, NM, FPER>();
+        g_order_mfirst<1 + NRB, NM, NM, FPER>();
       else
         g_order_mfirst<NRB, NM, NM, FPER>();
     }
@@ -341,12 +359,13 @@ __device__ __forceinline__ void g_step(GFrags<NRB>& F, const GArgs& g, int k,
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(GDMA, 0));
   barrier_only();
   if constexpr (NRB > 0) {
+    g_read_s<NRB>(g, nxt, F);
     g_read_a<NRB>(g, nxt, 0, F);
     g_read_a<NRB>(g, nxt, 1, F);
     g_read_b<NRB>(g, nxt, 0, F, 0, wp);
     g_mfmas<NRB>(F, 1, 1, acc);
     g_decode<NRB>(F, 0, 0);
-    g_order_late<6 + NRB, NM, FPER>();
+    g_order_late<3 + NRB, NM, FPER>();
   }
   __builtin_amdgcn_sched_barrier(0);
 }
@@ -374,6 +393,7 @@ __device__ __forceinline__ void g_loop(const GArgs& g, uint8_t* lds, int wp, f32
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(GDMA, 0));
   barrier_only();
   if constexpr (NRB > 0) {
+    g_read_s<NRB>(g, st0, F);
     g_read_a<NRB>(g, st0, 0, F);
     g_read_a<NRB>(g, st0, 1, F);
     g_read_b<NRB>(g, st0, 0, F, 0, wp);
