@@ -252,7 +252,7 @@ __device__ __forceinline__ bool xcd_work_item(const Tile* __restrict__ tiles,
 }
 
 constexpr int MT = 128;      // routed rows per forward GEMM tile
-constexpr int BMT = 256;     // routed rows per backward GEMM tile
+constexpr int BMT = 128;     // routed rows per backward GEMM tile
 // LoRA ranks: 8, 16, 32 or 64, contracted in 16-deep MFMA chunks (rank 8
 // zero-padded to one chunk).
 constexpr int LORA_RMAX = 64;

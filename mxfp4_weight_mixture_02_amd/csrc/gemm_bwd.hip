@@ -36,18 +36,20 @@
 // the bytes written and read of a decoded bf16 tile (gfx950's LDS writes run
 // at well under half its read rate).
 //
-// Activation path (the B-operand, contraction-contiguous in memory): a
-// thread loads 8 x 16 bytes of the workgroup's 256 rows per step into
-// registers, one step ahead, and stores them to an LDS stage; the MFMA reads
-// them with 16-byte LDS reads.
+// Activation path (the B-operand, contraction-contiguous in memory): each
+// step's 128 rows x 64 bf16 (16 KB) are copied into an LDS stage by LDS-DMA
+// loads, 16-byte chunks swizzled per row; the MFMA reads them with 16-byte
+// LDS reads.
 //
-// Tiling.  A workgroup is 8 waves (two per SIMD, so one wave's decode and
-// LDS traffic overlap the other's MFMAs) and computes 256 routed rows (one
-// 256-row tile of an expert) x 256 output columns.  Wave w = (wo, wp) owns
-// the 64-column double block wo (two MFMA row blocks: its even and its odd
-// columns) and the 32-row blocks wp, wp + 2, wp + 4, wp + 6 of the tile
-// (interleaved, so a partial tile splits its live blocks evenly): 8
-// accumulators of 32 x 32 fp32, 128 registers.
+// Tiling.  A workgroup is 4 waves (one per SIMD) and computes 128 routed
+// rows (one 128-row tile of an expert) x 256 output columns; two
+// workgroups share a CU (78 KB of LDS each), so each SIMD interleaves
+// waves of two independent workgroups, and a workgroup's barrier only
+// meets waves on different SIMDs (with two waves of one workgroup per SIMD
+// the one the SIMD favours reached every barrier early and the other
+// finished each step alone).  Wave wo owns the 64-column double block wo
+// (two MFMA row blocks: its even and its odd columns) and the four 32-row
+// blocks of the tile: 8 accumulators of 32 x 32 fp32, 128 registers.
 //
 // Pipeline (one barrier per 64-deep step k): stage step k + 1's codes,
 // scales and activations (loaded during step k - 1) into the other LDS
@@ -65,18 +67,18 @@ namespace mxmoe {
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 
-constexpr int GW = 8;                       // waves per workgroup, two per SIMD
+constexpr int GW = 4;                       // waves per workgroup, one per SIMD
 constexpr int GTHR = 64 * GW;
 constexpr int GO = 256;                     // output columns per workgroup
 constexpr int GKC = 64;                     // contraction per step
 constexpr int GCB = GKC * (GO / 2);         // code tile per step: 64 rows x 128 bytes (8 KB)
 constexpr int GSB = (GO / 32) * GKC * 4;    // scale table per step: 8 blocks x 64 rows, a word each (2 KB)
-constexpr int GXB = BMT * GKC * 2;          // activation stage (32 KB)
-constexpr int GSTAGE = GCB + GSB + GXB;     // one stage (42 KB)
+constexpr int GXB = BMT * GKC * 2;          // activation stage (16 KB)
+constexpr int GSTAGE = GCB + GSB + GXB;     // one stage (26 KB)
 constexpr int GNST = 3;                     // stages in flight
-constexpr int GLDS_LOOP = GNST * GSTAGE;    // main loop (126 KB)
-constexpr int GDMA = 6;                     // LDS-DMA loads per wave per step
-static_assert(BMT == 256, "tile rows assumed below");
+constexpr int GLDS_LOOP = GNST * GSTAGE;    // main loop (78 KB: two workgroups per CU)
+constexpr int GDMA = 8;                     // LDS-DMA loads per wave per step
+static_assert(BMT == 128, "tile rows assumed below");
 
 // Chunk swizzle of activation row p (16-byte chunks; distinct banks for the
 // 16-byte reads of 8 and of 16 consecutive rows).
@@ -91,8 +93,8 @@ struct GArgs {
   uint32_t xoff[4];         // element offsets of the 4 activation pieces this lane copies (step 0)
   const uint8_t* wcode;     // the expert's codes and scales (workgroup-uniform)
   const uint8_t* wscale;
-  uint32_t coff;            // byte offset of this lane's 16-byte code piece (step 0)
-  uint32_t soff;            // byte offset of its scale byte (step 0)
+  uint32_t coff[2];         // byte offsets of this lane's two 16-byte code pieces (step 0)
+  uint32_t soff[2];         // byte offsets of its two scale bytes (step 0)
   uint32_t cstep, sstep;    // bytes per step of 64 stored rows
   uint32_t aoff;            // code-tile offset of the transposing read (sub-step 0)
   uint32_t sofs;            // scale-table offset of the lane's four scale words
@@ -136,19 +138,25 @@ __device__ __forceinline__ void g_setup(GArgs& g, const uint16_t* xbase, RowOff 
   }
   g.wcode = wcode;
   g.wscale = wscale;
-  // codes: LDS slot tid of the tile is row c0 = tid / 8, slot tid % 8,
-  // holding 16-byte chunk j = (tid % 8) ^ (c0 % 8) (32 columns)
+  // codes: LDS slot 256 m + tid of the tile (copy m = 0, 1) is row c0 =
+  // 32 m + tid / 8, slot tid % 8, holding 16-byte chunk j = (tid % 8) ^
+  // (c0 % 8) (32 columns)
   const int c0 = tid >> 3, j = (tid & 7) ^ (c0 & 7);
   const int col = (o0 + 32 * j < O) ? o0 + 32 * j : 0;   // past O: any valid column
-  g.coff = (uint32_t)c0 * (uint32_t)(O / 2) + col / 2;
-  // scales: table word tid = 64 b + 32 h + 4 r + s holds row 16 s + 8 h + r
-  // (sub-step s, half h, r < 8) of scale block b = wave, so the four
-  // sub-steps' words of one row are consecutive
+  g.coff[0] = (uint32_t)c0 * (uint32_t)(O / 2) + col / 2;
+  g.coff[1] = g.coff[0] + 32u * (uint32_t)(O / 2);
+  // scales: table word 64 b + 32 h + 4 r + s holds row 16 s + 8 h + r
+  // (sub-step s, half h, r < 8) of scale block b (copy m of wave w: b = 4 m
+  // + w), so the four sub-steps' words of one row are consecutive
   {
     const int ss = lane & 3, r = (lane >> 2) & 7, h = lane >> 5;
     const int row = 16 * ss + 8 * h + r;
-    const int scol = (o0 + 32 * wave < O) ? o0 + 32 * wave : 0;
-    g.soff = (uint32_t)row * (uint32_t)(O / 32) + scol / 32;
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int b = 4 * m + wave;
+      const int scol = (o0 + 32 * b < O) ? o0 + 32 * b : 0;
+      g.soff[m] = (uint32_t)row * (uint32_t)(O / 32) + scol / 32;
+    }
   }
   g.cstep = (uint32_t)GKC * (O / 2);
   g.sstep = (uint32_t)GKC * (O / 32);
@@ -168,10 +176,10 @@ __device__ __forceinline__ void g_setup(GArgs& g, const uint16_t* xbase, RowOff 
   g.nsteps = (C + GKC - 1) / GKC;
   g.half_last = (C % GKC) != 0;
   // in a half last step the activation slots of k >= 32 (chunk >= 4), the
-  // code rows >= 32 and the scale rows >= 32 lie past C
+  // code rows >= 32 (all of copy 1) and the scale rows >= 32 lie past C
   {
     const int ch = (lane & 7) ^ ((lane >> 3) & 7);   // the chunk of all 4 of the lane's pieces
-    g.tailmask = (ch >= 4 ? 1u : 0u) | (c0 >= 32 ? 2u : 0u) | ((lane & 3) >= 2 ? 4u : 0u);
+    g.tailmask = (ch >= 4 ? 1u : 0u) | 2u | ((lane & 3) >= 2 ? 4u : 0u);
   }
 }
 
@@ -179,23 +187,34 @@ __device__ __forceinline__ void g_setup(GArgs& g, const uint16_t* xbase, RowOff 
 // last step the pieces past C are read from a block of zeros.
 __device__ __forceinline__ void g_dma(const GArgs& g, uint8_t* __restrict__ st, int k) {
   const uint16_t* xp[4];
-  const uint8_t* cp = g.wcode + (g.coff + (uint32_t)k * g.cstep);
-  const uint8_t* sp = g.wscale + (g.soff + (uint32_t)k * g.sstep);
+  const uint8_t* cp[2];
+  const uint8_t* sp[2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    cp[m] = g.wcode + (g.coff[m] + (uint32_t)k * g.cstep);
+    sp[m] = g.wscale + (g.soff[m] + (uint32_t)k * g.sstep);
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) xp[i] = g.xbase + (g.xoff[i] + (uint32_t)(k * GKC));
   if (g.half_last && k == g.nsteps - 1) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       if (g.tailmask & 1u) xp[i] = reinterpret_cast<const uint16_t*>(g_zero64);
-    if (g.tailmask & 2u) cp = g_zero64;
-    if (g.tailmask & 4u) sp = g_zero64;
+    if (g.tailmask & 2u) cp[1] = g_zero64;
+    if (g.tailmask & 4u) {
+      sp[0] = g_zero64;
+      sp[1] = g_zero64;
+    }
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     __builtin_amdgcn_global_load_lds((gptr_t)xp[i], (lptr_t)(st + GCB + GSB + (g.wave * 4 + i) * 1024),
                                      16, 0, 0);
-  __builtin_amdgcn_global_load_lds((gptr_t)cp, (lptr_t)(st + g.wave * 1024), 16, 0, 0);
-  __builtin_amdgcn_global_load_lds((gptr_t)sp, (lptr_t)(st + GCB + g.wave * 256), 1, 0, 0);
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    __builtin_amdgcn_global_load_lds((gptr_t)cp[m], (lptr_t)(st + (4 * m + g.wave) * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((gptr_t)sp[m], (lptr_t)(st + GCB + (4 * m + g.wave) * 256), 1, 0, 0);
+  }
 }
 
 // LDS reads from stage st: the transposed code bytes of sub-step s (the
@@ -216,10 +235,10 @@ __device__ __forceinline__ void g_read_s(const GArgs& g, const uint8_t* __restri
 
 template <int NRB>
 __device__ __forceinline__ void g_read_b(const GArgs& g, const uint8_t* __restrict__ st, int s,
-                                         GFrags<NRB>& F, int bi, int wp) {
+                                         GFrags<NRB>& F, int bi) {
 #pragma unroll
   for (int j = 0; j < NRB; ++j)
-    F.b[bi][j] = *reinterpret_cast<const bf16x8*>(st + g.boff[s] + (wp + 2 * j) * 4096);
+    F.b[bi][j] = *reinterpret_cast<const bf16x8*>(st + g.boff[s] + j * 4096);
 }
 
 // row_newbcast:R -- lane R of each 16-lane row to the whole row
@@ -334,7 +353,7 @@ template <int NRB>
 __device__ __forceinline__ void g_step(GFrags<NRB>& F, const GArgs& g, int k,
                                        const uint8_t* __restrict__ cur,
                                        const uint8_t* __restrict__ nxt, uint8_t* __restrict__ dst,
-                                       int wp, f32x16 (&acc)[2][4]) {
+                                       f32x16 (&acc)[2][4]) {
   // 25 decode instructions spread over the MFMAs
   constexpr int NM = 2 * NRB, FPER = (25 + NM - 1) / (NM > 0 ? NM : 1);
   __builtin_amdgcn_sched_barrier(0);
@@ -344,7 +363,7 @@ __device__ __forceinline__ void g_step(GFrags<NRB>& F, const GArgs& g, int k,
   for (int s = 0; s < 3; ++s) {
     if constexpr (NRB > 0) {
       if (s < 2) g_read_a<NRB>(g, cur, s + 2, F);
-      g_read_b<NRB>(g, cur, s + 1, F, (s + 1) & 1, wp);
+      g_read_b<NRB>(g, cur, s + 1, F, (s + 1) & 1);
       g_mfmas<NRB>(F, s & 1, s & 1, acc);
       g_decode<NRB>(F, (s + 1) & 1, s + 1);
       if (s == 0)
@@ -362,7 +381,7 @@ __device__ __forceinline__ void g_step(GFrags<NRB>& F, const GArgs& g, int k,
     g_read_s<NRB>(g, nxt, F);
     g_read_a<NRB>(g, nxt, 0, F);
     g_read_a<NRB>(g, nxt, 1, F);
-    g_read_b<NRB>(g, nxt, 0, F, 0, wp);
+    g_read_b<NRB>(g, nxt, 0, F, 0);
     g_mfmas<NRB>(F, 1, 1, acc);
     g_decode<NRB>(F, 0, 0);
     g_order_late<3 + NRB, NM, FPER>();
@@ -376,14 +395,14 @@ __device__ __forceinline__ void g_step(GFrags<NRB>& F, const GArgs& g, int k,
 template <int NRB>
 __device__ __forceinline__ void g_trip(GFrags<NRB>& F, const GArgs& g, int k, int n,
                                        uint8_t* __restrict__ st0, uint8_t* __restrict__ st1,
-                                       uint8_t* __restrict__ st2, int wp, f32x16 (&acc)[2][4]) {
-  g_step<NRB>(F, g, k, st0, st1, st2, wp, acc);
-  if (n > 1) g_step<NRB>(F, g, k + 1, st1, st2, st0, wp, acc);
-  if (n > 2) g_step<NRB>(F, g, k + 2, st2, st0, st1, wp, acc);
+                                       uint8_t* __restrict__ st2, f32x16 (&acc)[2][4]) {
+  g_step<NRB>(F, g, k, st0, st1, st2, acc);
+  if (n > 1) g_step<NRB>(F, g, k + 1, st1, st2, st0, acc);
+  if (n > 2) g_step<NRB>(F, g, k + 2, st2, st0, st1, acc);
 }
 
 template <int NRB>
-__device__ __forceinline__ void g_loop(const GArgs& g, uint8_t* lds, int wp, f32x16 (&acc)[2][4]) {
+__device__ __forceinline__ void g_loop(const GArgs& g, uint8_t* lds, f32x16 (&acc)[2][4]) {
   GFrags<NRB> F;
   uint8_t* st0 = lds;
   uint8_t* st1 = lds + GSTAGE;
@@ -396,13 +415,13 @@ __device__ __forceinline__ void g_loop(const GArgs& g, uint8_t* lds, int wp, f32
     g_read_s<NRB>(g, st0, F);
     g_read_a<NRB>(g, st0, 0, F);
     g_read_a<NRB>(g, st0, 1, F);
-    g_read_b<NRB>(g, st0, 0, F, 0, wp);
+    g_read_b<NRB>(g, st0, 0, F, 0);
     g_decode<NRB>(F, 0, 0);
   }
   // three steps per trip, so each step's stages are fixed pointers
   int k = 0;
-  for (; k + 3 <= g.nsteps; k += 3) g_trip<NRB>(F, g, k, 3, st0, st1, st2, wp, acc);
-  if (k < g.nsteps) g_trip<NRB>(F, g, k, g.nsteps - k, st0, st1, st2, wp, acc);
+  for (; k + 3 <= g.nsteps; k += 3) g_trip<NRB>(F, g, k, 3, st0, st1, st2, acc);
+  if (k < g.nsteps) g_trip<NRB>(F, g, k, g.nsteps - k, st0, st1, st2, acc);
   // the last steps copied and read (unused) operands of other stages; every
   // wave must be past them before the epilogue reuses LDS
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
@@ -418,12 +437,8 @@ __device__ __forceinline__ void zero_acc(f32x16 (&acc)[2][4]) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 }
 
-// Live 32-row blocks of wave row-group wp (blocks wp, wp + 2, ...) in a
-// tile of `rows` rows.
-__device__ __forceinline__ int live_blocks(int rows, int wp) {
-  const int nb = (rows + 31) >> 5;
-  return max(0, min(4, (nb - wp + 1) >> 1));
-}
+// Live 32-row blocks in a tile of `rows` rows.
+__device__ __forceinline__ int live_blocks(int rows) { return min(4, (rows + 31) >> 5); }
 
 // Accumulator layout.  Fragment par covers the columns 2 m + par of the
 // wave's double block (m: MFMA row); lane l holds rows m = 8 (r / 4) + 4 (l /
@@ -444,7 +459,7 @@ __device__ __forceinline__ void cols8(const f32x16 (&acc)[2][4], int q, int j, f
 // i's MFMA row l32 is output column ow + 2 l32 + i), B-operand = dv [R, r]
 // (sorted order) as hi + lo bf16.
 template <int NRB>
-__device__ __forceinline__ void lora_term(f32x16 (&acc)[2][4], const Tile& tl, int wp, int ow,
+__device__ __forceinline__ void lora_term(f32x16 (&acc)[2][4], const Tile& tl, int ow,
                                           int O, const uint16_t* __restrict__ At,
                                           const float* __restrict__ dv, int r) {
   const int lane = threadIdx.x & 63;
@@ -452,7 +467,7 @@ __device__ __forceinline__ void lora_term(f32x16 (&acc)[2][4], const Tile& tl, i
   for (int q = 0; q < lora_chunks(r); ++q) {
 #pragma unroll
     for (int j = 0; j < NRB; ++j) {
-      const int pb = wp + 2 * j;
+      const int pb = j;
       bf16x8 vh, vl;
       lora_frag_split(dv + (int64_t)(tl.row0 + min(32 * pb + l32, tl.rows - 1)) * r, r, q, hlf,
                       1.0f, &vh, &vl);
@@ -478,18 +493,18 @@ __device__ __forceinline__ void bwd_gate_up_body(const GArgs& g, uint8_t* lds, c
                                                  const float* __restrict__ lora_dv, int lora_r,
                                                  uint16_t* __restrict__ dxr) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wo = wave & 3, wp = wave >> 2;
+  const int wo = wave;
   const int l32 = lane & 31, hlf = lane >> 5;
   f32x16 acc[2][4];
   zero_acc(acc);
-  g_loop<NRB>(g, lds, wp, acc);
+  g_loop<NRB>(g, lds, acc);
   const int ow = o0 + 64 * wo;                // this wave's first output column
-  if (LORA && NRB > 0) lora_term<NRB>(acc, tl, wp, ow, H, lora_At, lora_dv, lora_r);
+  if (LORA && NRB > 0) lora_term<NRB>(acc, tl, ow, H, lora_At, lora_dv, lora_r);
   if (NRB == 0 || ow >= H) return;
   uint8_t* st = lds + wave * 4096;            // 32 rows x 128 bytes
 #pragma unroll
   for (int j = 0; j < NRB; ++j) {
-    const int pb = wp + 2 * j;
+    const int pb = j;
     const int32_t f = sorted_rows[tl.row0 + min(32 * pb + l32, tl.rows - 1)];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -525,15 +540,13 @@ __global__ __launch_bounds__(GTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
   int ot;
   if (!xcd_work_item(tiles, num_tiles, (H + GO - 1) / GO, &tl, &ot)) return;
   const int o0 = ot * GO, N2 = 2 * I;
-  const int wp = (threadIdx.x >> 6) >> 2;
   // Wgu is stored [2I rows][H cols]: contraction over n (C = 2I), output h (O = H);
   // the activations are dh's rows in sorted order
   GArgs g;
   g_setup(g, dh, [&](int p) { return (uint32_t)(tl.row0 + min(p, tl.rows - 1)) * (uint32_t)N2; },
           codes + (int64_t)tl.expert * N2 * (H / 2), scales + (int64_t)tl.expert * N2 * (H / 32),
           N2, H, o0);
-  switch (live_blocks(tl.rows, wp)) {
-    case 0: bwd_gate_up_body<LORA, 0>(g, lds, tl, sorted_rows, H, o0, lora_At, lora_dv, lora_r, dxr); break;
+  switch (live_blocks(tl.rows)) {
     case 1: bwd_gate_up_body<LORA, 1>(g, lds, tl, sorted_rows, H, o0, lora_At, lora_dv, lora_r, dxr); break;
     case 2: bwd_gate_up_body<LORA, 2>(g, lds, tl, sorted_rows, H, o0, lora_At, lora_dv, lora_r, dxr); break;
     case 3: bwd_gate_up_body<LORA, 3>(g, lds, tl, sorted_rows, H, o0, lora_At, lora_dv, lora_r, dxr); break;
@@ -557,22 +570,22 @@ __device__ __forceinline__ void bwd_down_body(
     float limit, const uint16_t* __restrict__ lora_At, const float* __restrict__ lora_dvu,
     int lora_r, uint16_t* __restrict__ dh, float* __restrict__ dw_part) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wo = wave & 3, wp = wave >> 2;
+  const int wo = wave;
   const int l32 = lane & 31, hlf = lane >> 5;
   const int e = tl.expert;
   f32x16 acc[2][4];
   zero_acc(acc);
-  g_loop<NRB>(g, lds, wp, acc);
+  g_loop<NRB>(g, lds, acc);
   const int ow = o0 + 64 * wo;                // this wave's first column of I
-  if (LORA && NRB > 0) lora_term<NRB>(acc, tl, wp, ow, I, lora_At, lora_dvu, lora_r);
+  if (LORA && NRB > 0) lora_term<NRB>(acc, tl, ow, I, lora_At, lora_dvu, lora_r);
   const int N2 = 2 * I;
   const bool active = ow < I;
   uint8_t* ast = lds + wave * 12288;          // a strip: 32 rows x 64 bf16 (128-byte rows)
   uint8_t* hst = ast + 4096;                  // h / dh strip: 32 rows x 128 bf16 (256-byte rows)
-  float* red = reinterpret_cast<float*>(lds + GW * 12288);   // [GW][BMT / 2]
+  float* red = reinterpret_cast<float*>(lds + GW * 12288);   // [GW][BMT]
 #pragma unroll
   for (int j = 0; j < NRB; ++j) {
-    const int pb = wp + 2 * j;
+    const int pb = j;
     float dwp = 0.0f;
     if (active) {
 #pragma unroll
@@ -633,16 +646,15 @@ __device__ __forceinline__ void bwd_down_body(
       wave_lds_sync();
     }
     dwp += __shfl_xor(dwp, 32);
-    if (hlf == 0) red[wave * (BMT / 2) + 32 * j + l32] = dwp;
+    if (hlf == 0) red[wave * BMT + 32 * j + l32] = dwp;
   }
   __syncthreads();
-  // row p of the tile: row group wp = (p / 32) % 2, slot 32 j + p % 32 with
-  // j = p / 64; the four waves of the group, wo = 0..3, are added in order
+  // row p of the tile: the four waves' partials, wo = 0..3, added in order
   if (tid < tl.rows) {
-    const int p = tid, gp = (p >> 5) & 1, slot = 32 * (p >> 6) + (p & 31);
+    const int p = tid;
     float sum = 0.0f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) sum += red[(4 * gp + w) * (BMT / 2) + slot];
+    for (int w = 0; w < GW; ++w) sum += red[w * BMT + p];
     const int64_t f = sorted_rows[tl.row0 + p];
     dw_part[f * otiles + ot] = sum;
   }
@@ -659,13 +671,12 @@ __global__ __launch_bounds__(GTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
     uint16_t* __restrict__ dh, float* __restrict__ dw_part) {
   // the epilogue's strips (8 x 12 KB) and dw reduction reuse the main loop's stages
   __shared__ __attribute__((aligned(16))) uint8_t lds[GLDS_LOOP];
-  static_assert(GW * 12288 + GW * (BMT / 2) * 4 <= GLDS_LOOP, "the epilogue fits the loop's LDS");
+  static_assert(GW * 12288 + GW * BMT * 4 <= GLDS_LOOP, "the epilogue fits the loop's LDS");
   Tile tl;
   int ot;
   const int otiles = (I + GO - 1) / GO;
   if (!xcd_work_item(tiles, num_tiles, otiles, &tl, &ot)) return;
   const int o0 = ot * GO;
-  const int wp = (threadIdx.x >> 6) >> 2;
   // Wd is stored [H rows][I cols]: contraction over h (C = H), output i (O =
   // I); the activations are the routed rows' tokens' dY rows
   GArgs g;
@@ -678,8 +689,7 @@ __global__ __launch_bounds__(GTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
 #define BWD_DOWN_BODY(N)                                                                       \
   bwd_down_body<LORA, N>(g, lds, tl, ot, otiles, o0, topk_w, sorted_rows, hsv, asv, I, alpha, \
                          limit, lora_At, lora_dvu, lora_r, dh, dw_part)
-  switch (live_blocks(tl.rows, wp)) {
-    case 0: BWD_DOWN_BODY(0); break;
+  switch (live_blocks(tl.rows)) {
     case 1: BWD_DOWN_BODY(1); break;
     case 2: BWD_DOWN_BODY(2); break;
     case 3: BWD_DOWN_BODY(3); break;
