@@ -59,6 +59,8 @@
 // after which the next step's first reads issue.  Step indices are clamped
 // at the end instead of branching around loads; rows past the tile and
 // columns past O read valid memory whose products are never stored.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -73,12 +75,14 @@ constexpr int GO = 256;                     // output columns per workgroup
 constexpr int GKC = 64;                     // contraction per step
 constexpr int GCB = GKC * (GO / 2);         // code tile per step: 64 rows x 128 bytes (8 KB)
 constexpr int GSB = (GO / 32) * GKC * 4;    // scale table per step: 8 blocks x 64 rows, a word each (2 KB)
-constexpr int GXB = BMT * GKC * 2;          // activation stage (16 KB)
-constexpr int GSTAGE = GCB + GSB + GXB;     // one stage (26 KB)
+constexpr int GRB = BMT / 32;               // 32-row blocks per tile (and per wave)
+constexpr int GXB = BMT * GKC * 2;          // activation stage
+constexpr int GXI = GXB / (1024 * GW);      // activation DMA loads per wave per step
+constexpr int GSTAGE = GCB + GSB + GXB;     // one stage
 constexpr int GNST = 3;                     // stages in flight
-constexpr int GLDS_LOOP = GNST * GSTAGE;    // main loop (78 KB: two workgroups per CU)
-constexpr int GDMA = 8;                     // LDS-DMA loads per wave per step
-static_assert(BMT == 128, "tile rows assumed below");
+constexpr int GLDS_LOOP = GNST * GSTAGE;    // main loop
+constexpr int GDMA = GXI + 4;               // LDS-DMA loads per wave per step
+static_assert(BMT == 128 || BMT == 256, "tile rows assumed below");
 
 // Chunk swizzle of activation row p (16-byte chunks; distinct banks for the
 // 16-byte reads of 8 and of 16 consecutive rows).
@@ -90,7 +94,7 @@ __device__ __forceinline__ int x_swz(int p) { return (p & 7) ^ ((p >> 3) & 1); }
 // instruction's LDS base + 16 (or, for a byte, 4) x lane.
 struct GArgs {
   const uint16_t* xbase;    // activations (workgroup-uniform)
-  uint32_t xoff[4];         // element offsets of the 4 activation pieces this lane copies (step 0)
+  uint32_t xoff[GXI];       // element offsets of the activation pieces this lane copies (step 0)
   const uint8_t* wcode;     // the expert's codes and scales (workgroup-uniform)
   const uint8_t* wscale;
   uint32_t coff[2];         // byte offsets of this lane's two 16-byte code pieces (step 0)
@@ -129,11 +133,11 @@ __device__ __forceinline__ void g_setup(GArgs& g, const uint16_t* xbase, RowOff 
   const int wo = wave & 3;
   g.wave = wave;
   g.xbase = xbase;
-  // activations: instruction i of wave w fills rows 8 (4 w + i) .. + 7,
+  // activations: instruction i of wave w fills rows 8 (GXI w + i) .. + 7,
   // slot lane % 8 of row p holding chunk (lane % 8) ^ x_swz(p)
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int p = 32 * wave + 8 * i + (lane >> 3);
+  for (int i = 0; i < GXI; ++i) {
+    const int p = 8 * GXI * wave + 8 * i + (lane >> 3);
     g.xoff[i] = rowoff(p) + 8 * (uint32_t)((lane & 7) ^ x_swz(p));
   }
   g.wcode = wcode;
@@ -178,7 +182,7 @@ __device__ __forceinline__ void g_setup(GArgs& g, const uint16_t* xbase, RowOff 
   // in a half last step the activation slots of k >= 32 (chunk >= 4), the
   // code rows >= 32 (all of copy 1) and the scale rows >= 32 lie past C
   {
-    const int ch = (lane & 7) ^ ((lane >> 3) & 7);   // the chunk of all 4 of the lane's pieces
+    const int ch = (lane & 7) ^ ((lane >> 3) & 7);   // the chunk of all the lane's pieces
     g.tailmask = (ch >= 4 ? 1u : 0u) | 2u | ((lane & 3) >= 2 ? 4u : 0u);
   }
 }
@@ -186,7 +190,7 @@ __device__ __forceinline__ void g_setup(GArgs& g, const uint16_t* xbase, RowOff 
 // Step k's tile into LDS stage st (GDMA loads of this wave).  In a half
 // last step the pieces past C are read from a block of zeros.
 __device__ __forceinline__ void g_dma(const GArgs& g, uint8_t* __restrict__ st, int k) {
-  const uint16_t* xp[4];
+  const uint16_t* xp[GXI];
   const uint8_t* cp[2];
   const uint8_t* sp[2];
 #pragma unroll
@@ -195,10 +199,10 @@ __device__ __forceinline__ void g_dma(const GArgs& g, uint8_t* __restrict__ st, 
     sp[m] = g.wscale + (g.soff[m] + (uint32_t)k * g.sstep);
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) xp[i] = g.xbase + (g.xoff[i] + (uint32_t)(k * GKC));
+  for (int i = 0; i < GXI; ++i) xp[i] = g.xbase + (g.xoff[i] + (uint32_t)(k * GKC));
   if (g.half_last && k == g.nsteps - 1) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < GXI; ++i)
       if (g.tailmask & 1u) xp[i] = reinterpret_cast<const uint16_t*>(g_zero64);
     if (g.tailmask & 2u) cp[1] = g_zero64;
     if (g.tailmask & 4u) {
@@ -207,8 +211,8 @@ __device__ __forceinline__ void g_dma(const GArgs& g, uint8_t* __restrict__ st, 
     }
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    __builtin_amdgcn_global_load_lds((gptr_t)xp[i], (lptr_t)(st + GCB + GSB + (g.wave * 4 + i) * 1024),
+  for (int i = 0; i < GXI; ++i)
+    __builtin_amdgcn_global_load_lds((gptr_t)xp[i], (lptr_t)(st + GCB + GSB + (g.wave * GXI + i) * 1024),
                                      16, 0, 0);
 #pragma unroll
   for (int m = 0; m < 2; ++m) {
@@ -285,7 +289,7 @@ __device__ __forceinline__ void g_decode(GFrags<NRB>& F, int ai, int s) {
 // The 2 x NRB MFMAs of one sub-step (independent accumulators).
 template <int NRB>
 __device__ __forceinline__ void g_mfmas(const GFrags<NRB>& F, int ai, int bi,
-                                        f32x16 (&acc)[2][4]) {
+                                        f32x16 (&acc)[2][GRB]) {
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -353,7 +357,7 @@ template <int NRB>
 __device__ __forceinline__ void g_step(GFrags<NRB>& F, const GArgs& g, int k,
                                        const uint8_t* __restrict__ cur,
                                        const uint8_t* __restrict__ nxt, uint8_t* __restrict__ dst,
-                                       f32x16 (&acc)[2][4]) {
+                                       f32x16 (&acc)[2][GRB]) {
   // 25 decode instructions spread over the MFMAs
   constexpr int NM = 2 * NRB, FPER = (25 + NM - 1) / (NM > 0 ? NM : 1);
   __builtin_amdgcn_sched_barrier(0);
@@ -395,14 +399,14 @@ __device__ __forceinline__ void g_step(GFrags<NRB>& F, const GArgs& g, int k,
 template <int NRB>
 __device__ __forceinline__ void g_trip(GFrags<NRB>& F, const GArgs& g, int k, int n,
                                        uint8_t* __restrict__ st0, uint8_t* __restrict__ st1,
-                                       uint8_t* __restrict__ st2, f32x16 (&acc)[2][4]) {
+                                       uint8_t* __restrict__ st2, f32x16 (&acc)[2][GRB]) {
   g_step<NRB>(F, g, k, st0, st1, st2, acc);
   if (n > 1) g_step<NRB>(F, g, k + 1, st1, st2, st0, acc);
   if (n > 2) g_step<NRB>(F, g, k + 2, st2, st0, st1, acc);
 }
 
 template <int NRB>
-__device__ __forceinline__ void g_loop(const GArgs& g, uint8_t* lds, f32x16 (&acc)[2][4]) {
+__device__ __forceinline__ void g_loop(const GArgs& g, uint8_t* lds, f32x16 (&acc)[2][GRB]) {
   GFrags<NRB> F;
   uint8_t* st0 = lds;
   uint8_t* st1 = lds + GSTAGE;
@@ -428,17 +432,30 @@ __device__ __forceinline__ void g_loop(const GArgs& g, uint8_t* lds, f32x16 (&ac
   __syncthreads();
 }
 
-__device__ __forceinline__ void zero_acc(f32x16 (&acc)[2][4]) {
+__device__ __forceinline__ void zero_acc(f32x16 (&acc)[2][GRB]) {
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < GRB; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 }
 
 // Live 32-row blocks in a tile of `rows` rows.
-__device__ __forceinline__ int live_blocks(int rows) { return min(4, (rows + 31) >> 5); }
+__device__ __forceinline__ int live_blocks(int rows) { return min(GRB, (rows + 31) >> 5); }
+
+// f(integral_constant<int, n>) for n = live (1 <= live <= N): the body
+// instantiated for each live block count.
+template <int N, class F>
+__device__ __forceinline__ void with_blocks(int live, F&& f) {
+  if constexpr (N >= 1) {
+    if (live == N) {
+      f(std::integral_constant<int, N>{});
+      return;
+    }
+    with_blocks<N - 1>(live, f);
+  }
+}
 
 // Accumulator layout.  Fragment par covers the columns 2 m + par of the
 // wave's double block (m: MFMA row); lane l holds rows m = 8 (r / 4) + 4 (l /
@@ -446,7 +463,7 @@ __device__ __forceinline__ int live_blocks(int rows) { return min(4, (rows + 31)
 // holds 8 consecutive columns of its wave's 64, 16 q + 8 (l / 32) + 0..7:
 // registers 4q..4q+3 of fragment 0 give the even ones and of fragment 1 the
 // odd ones.  cols8 returns them as 8 fp32 in column order.
-__device__ __forceinline__ void cols8(const f32x16 (&acc)[2][4], int q, int j, float (&v)[8]) {
+__device__ __forceinline__ void cols8(const f32x16 (&acc)[2][GRB], int q, int j, float (&v)[8]) {
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
     v[2 * m] = acc[0][j][4 * q + m];
@@ -459,7 +476,7 @@ __device__ __forceinline__ void cols8(const f32x16 (&acc)[2][4], int q, int j, f
 // i's MFMA row l32 is output column ow + 2 l32 + i), B-operand = dv [R, r]
 // (sorted order) as hi + lo bf16.
 template <int NRB>
-__device__ __forceinline__ void lora_term(f32x16 (&acc)[2][4], const Tile& tl, int ow,
+__device__ __forceinline__ void lora_term(f32x16 (&acc)[2][GRB], const Tile& tl, int ow,
                                           int O, const uint16_t* __restrict__ At,
                                           const float* __restrict__ dv, int r) {
   const int lane = threadIdx.x & 63;
@@ -495,7 +512,7 @@ __device__ __forceinline__ void bwd_gate_up_body(const GArgs& g, uint8_t* lds, c
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wo = wave;
   const int l32 = lane & 31, hlf = lane >> 5;
-  f32x16 acc[2][4];
+  f32x16 acc[2][GRB];
   zero_acc(acc);
   g_loop<NRB>(g, lds, acc);
   const int ow = o0 + 64 * wo;                // this wave's first output column
@@ -546,12 +563,10 @@ __global__ __launch_bounds__(GTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
   g_setup(g, dh, [&](int p) { return (uint32_t)(tl.row0 + min(p, tl.rows - 1)) * (uint32_t)N2; },
           codes + (int64_t)tl.expert * N2 * (H / 2), scales + (int64_t)tl.expert * N2 * (H / 32),
           N2, H, o0);
-  switch (live_blocks(tl.rows)) {
-    case 1: bwd_gate_up_body<LORA, 1>(g, lds, tl, sorted_rows, H, o0, lora_At, lora_dv, lora_r, dxr); break;
-    case 2: bwd_gate_up_body<LORA, 2>(g, lds, tl, sorted_rows, H, o0, lora_At, lora_dv, lora_r, dxr); break;
-    case 3: bwd_gate_up_body<LORA, 3>(g, lds, tl, sorted_rows, H, o0, lora_At, lora_dv, lora_r, dxr); break;
-    default: bwd_gate_up_body<LORA, 4>(g, lds, tl, sorted_rows, H, o0, lora_At, lora_dv, lora_r, dxr); break;
-  }
+  with_blocks<GRB>(live_blocks(tl.rows), [&](auto nrb) {
+    bwd_gate_up_body<LORA, decltype(nrb)::value>(g, lds, tl, sorted_rows, H, o0, lora_At, lora_dv,
+                                                 lora_r, dxr);
+  });
 }
 
 // bwd_down body: main loop; with LORA the adapter term dv_u A_e (a 16-deep
@@ -573,7 +588,7 @@ __device__ __forceinline__ void bwd_down_body(
   const int wo = wave;
   const int l32 = lane & 31, hlf = lane >> 5;
   const int e = tl.expert;
-  f32x16 acc[2][4];
+  f32x16 acc[2][GRB];
   zero_acc(acc);
   g_loop<NRB>(g, lds, acc);
   const int ow = o0 + 64 * wo;                // this wave's first column of I
@@ -686,16 +701,11 @@ __global__ __launch_bounds__(GTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
           },
           codes + (int64_t)tl.expert * H * (I / 2), scales + (int64_t)tl.expert * H * (I / 32), H,
           I, o0);
-#define BWD_DOWN_BODY(N)                                                                       \
-  bwd_down_body<LORA, N>(g, lds, tl, ot, otiles, o0, topk_w, sorted_rows, hsv, asv, I, alpha, \
-                         limit, lora_At, lora_dvu, lora_r, dh, dw_part)
-  switch (live_blocks(tl.rows)) {
-    case 1: BWD_DOWN_BODY(1); break;
-    case 2: BWD_DOWN_BODY(2); break;
-    case 3: BWD_DOWN_BODY(3); break;
-    default: BWD_DOWN_BODY(4); break;
-  }
-#undef BWD_DOWN_BODY
+  with_blocks<GRB>(live_blocks(tl.rows), [&](auto nrb) {
+    bwd_down_body<LORA, decltype(nrb)::value>(g, lds, tl, ot, otiles, o0, topk_w, sorted_rows, hsv,
+                                              asv, I, alpha, limit, lora_At, lora_dvu, lora_r, dh,
+                                              dw_part);
+  });
 }
 
 // One workgroup (256 threads) per token.  Slot j's dw = the sum of its
