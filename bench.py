@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--cpu-sample-tokens", type=int, default=16)
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the 120b skewed-routing and 16384-token LoRA workloads")
+    ap.add_argument("--act-format", default="bf16", choices=("bf16", "mxfp8", "mxfp8x2"),
+                    help="what the gate_up product consumes in the timed step (the headline "
+                         "is bf16; the block-scaled formats are for profiling runs)")
     ap.add_argument("--profile", action="store_true",
                     help="for rocprofv3 runs: one 256 MiB device-to-device copy (a known-size "
                          "calibration for the traffic counters), then warmup + steps of the "
@@ -138,6 +141,7 @@ def main():
     layer = MoeLayer(torch.from_numpy(syn.router_weight(s)).to(dev),
                      torch.from_numpy(syn.router_bias(s)).to(dev), gu_c, gu_s,
                      bf(syn.gate_up_bias(s)), dn_c, dn_s, bf(syn.down_bias(s)), k=k)
+    layer.act_format = args.act_format
     x = bf(syn.tokens(s))
     dy = bf(syn.upstream_grad(s))
     saved = SavedState.empty(layer, T, dev)
@@ -298,6 +302,41 @@ def main():
                                "kernel_us": kd}
         del copies
 
+    # ---- the gate_up product per activation format (bf16 weight-only, the
+    # block-scaled MXFP8 and hi + lo MXFP8 forms), same layer and tokens:
+    # event-timed kernels over two passes in opposite orders (the clock
+    # drifts), and each forward's distance from the bf16 one
+    block_scaled = {}
+    if not args.no_extra:
+        fmts = ("bf16", "mxfp8", "mxfp8x2")
+        acc = {f: {} for f in fmts}
+        outs = {}
+        for order in (fmts, fmts[::-1]):
+            for f in order:
+                layer.act_format = f
+                for _ in range(5):
+                    mxfp4_moe_forward(layer, x, saved=saved, out=out, workspace=wsf)
+                torch.cuda.synchronize()
+                L.mxfp4_moe_kernel_timing(1)
+                for _ in range(10):
+                    mxfp4_moe_forward(layer, x, saved=saved, out=out, workspace=wsf)
+                torch.cuda.synchronize()
+                for n, (ms, c) in kernel_times(L).items():
+                    acc[f].setdefault(n, []).append(ms / c * 1e3)
+                L.mxfp4_moe_kernel_timing(0)
+                outs[f] = out.float().clone()
+        layer.act_format = args.act_format
+        ref = outs["bf16"]
+        for f in fmts:
+            g = outs[f]
+            kt = {n: sum(v) / len(v) for n, v in acc[f].items()}
+            block_scaled[f] = {
+                "gate_up_kernel": "mx_gate_up" if f != "bf16" else "gate_up",
+                "gate_up_us": round(kt.get("mx_gate_up", kt.get("gate_up", 0.0)), 1),
+                "act_quantize_us": round(kt.get("act_quantize", 0.0), 1),
+                "max_rel_vs_bf16": float(f"{float((g - ref).abs().max() / ref.abs().max()):.3e}"),
+                "cos_vs_bf16": round(float((g * ref).sum() / (g.norm() * ref.norm())), 8)}
+
     # ---- the other full-size workloads (not the headline): the gpt-oss-120b
     # layer with Zipf-skewed routing (forward + dX) and the 16384-token LoRA
     # training step (forward, recompute forward, dX backward with dA/dB)
@@ -323,8 +362,10 @@ def main():
         "ms_per_step_graph": round(dt_graph * 1e3, 4),
         "ms_per_step_with_kernel_events": round(dt_inst * 1e3, 4),
         "kernel_us": kernels, "decode": decode, "roofline": roofline,
-        "workloads": extra,
+        "workloads": extra, "block_scaled_gate_up": block_scaled,
     }
+    if args.act_format != "bf16":
+        line["act_format"] = args.act_format
 
     # ---- CPU oracle on a bounded sample of the same workload
     if not args.no_cpu_baseline:
