@@ -190,7 +190,8 @@ struct Tile {
   int32_t rows;  // 1..MT
   // forward lists: this tile's index q among its expert's tiles (bits 0-15)
   // and that expert's tile count n (bits 16-31, 0xFFFF when n >= 0xFFFF);
-  // 0 in the backward's dealt list
+  // the backward's dealt list: the same for the expert's run of tiles on
+  // the tile's XCD; 0 for an empty slot
   int32_t pos;
 };
 __host__ __device__ constexpr int32_t tile_pos(int32_t q, int32_t n) {
@@ -236,18 +237,30 @@ __device__ __forceinline__ bool xcd_item_range(const Tile* __restrict__ tiles,
 // Tile list dealt to the XCDs (backward): XCD x's row tiles sit at x, 8 +
 // x, 16 + x, ... (the XCDs' shares balanced, each ending on its shortest
 // tiles; empty tiles have rows = 0), so block b runs on XCD x = b % 8 and
-// takes its XCD's (b / 8)-th item, column tile fastest: the column tiles of
-// a row tile (same activations) run together on one L2.  Returns false for
-// blocks past the XCD's items and for empty tiles.
+// takes its XCD's (b / 8)-th item.  An expert's full tiles on one XCD are
+// consecutive slots (a run, recorded in each tile's pos), and a run's items
+// go row tile fastest, so the run's row tiles read the same weight columns
+// at the same time from one L2; otherwise column tile fastest (the column
+// tiles of a row tile share its activations).  Returns false for blocks
+// past the XCD's items and for empty tiles.
 __device__ __forceinline__ bool xcd_work_item(const Tile* __restrict__ tiles,
                                               const int32_t* __restrict__ num_tiles,
                                               int col_tiles, Tile* tl, int* col_tile) {
   const int b = blockIdx.x;
   const int x = b & 7, idx = b >> 3;
-  const int p = 8 * (idx / col_tiles) + x;
-  if (p >= *num_tiles) return false;
-  *tl = tiles[p];
-  *col_tile = idx % col_tiles;
+  const int q = idx / col_tiles;
+  if (8 * q + x >= *num_tiles) return false;
+  const Tile t = tiles[8 * q + x];
+  const uint32_t n = (uint32_t)t.pos >> 16, qi = (uint32_t)t.pos & 0xFFFFu;
+  if (n <= 1 || n == 0xFFFF) {
+    *tl = t;
+    *col_tile = idx % col_tiles;
+    return t.rows > 0;
+  }
+  const int q0 = q - (int)qi;                 // the run's first slot
+  const int local = idx - q0 * col_tiles;
+  *tl = tiles[8 * (q0 + local % (int)n) + x];
+  *col_tile = local / (int)n;
   return tl->rows > 0;
 }
 

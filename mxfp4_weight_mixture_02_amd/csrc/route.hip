@@ -507,6 +507,14 @@ struct TileDeal {
     for (int pos = 0; pos < (ragged & 7); ++pos) n += ragged_xcd(8 * (ragged >> 3) + pos) == x;
     return n;
   }
+  // XCD x's range of full tiles [full_lo(x), full_lo(x) + full_count(x))
+  __device__ int full_lo(int x) const {
+    return x < full_ext ? x * (full_base + 1) : full_ext * (full_base + 1) + (x - full_ext) * full_base;
+  }
+  __device__ int full_xcd(int i) const {
+    const int boundary = full_ext * (full_base + 1);
+    return i < boundary ? i / (full_base + 1) : full_ext + (i - boundary) / full_base;
+  }
   // list index of full tile i (0 <= i < F)
   __device__ int full_slot(int i) const {
     const int boundary = full_ext * (full_base + 1);
@@ -557,14 +565,22 @@ __device__ __forceinline__ void write_dealt_tiles(const int32_t* offs, int E, in
   for (int e = tid; e < E; e += blockDim.x) {
     const int32_t o = offs[e], n = offs[e + 1] - o;
     const int32_t nfull = n / mt, rem = n % mt;
-    for (int32_t q = 0; q < nfull; ++q) tiles[d.full_slot(start[e] + q)] = Tile{e, o + q * mt, mt, 0};
+    // an expert's full tiles on one XCD form a run of consecutive slots; a
+    // tile records its index in the run and the run's length (the GEMMs
+    // order a run's items row tile fastest)
+    for (int32_t q = 0; q < nfull; ++q) {
+      const int i = start[e] + q, x = d.full_xcd(i);
+      const int lo = max(start[e], d.full_lo(x));
+      const int hi = min(start[e] + nfull, d.full_lo(x) + d.full_count(x));
+      tiles[d.full_slot(i)] = Tile{e, o + q * mt, mt, tile_pos(i - lo, hi - lo)};
+    }
     if (rem) {
       int32_t rank = 0;
       for (int e2 = 0; e2 < E; ++e2) {
         const int32_t r2 = (offs[e2 + 1] - offs[e2]) % mt;
         rank += (r2 > rem) || (r2 == rem && e2 < e);
       }
-      tiles[d.ragged_slot(rank)] = Tile{e, o + nfull * mt, rem, 0};
+      tiles[d.ragged_slot(rank)] = Tile{e, o + nfull * mt, rem, tile_pos(0, 1)};
     }
   }
   __syncthreads();
