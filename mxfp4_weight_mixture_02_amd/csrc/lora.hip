@@ -1,8 +1,10 @@
-// Rank-r LoRA (r = 8, 16, 32 or 64) on the down projection of every
-// expert ("Add MXFP4 training support via a dequantize-on-the-fly
-// fallback", "What this does": adapters train on top of the frozen MXFP4
-// base, whose backward only has to deliver input and adapter gradients).
-// Per expert e with A_e [r, I], B_e [H, r]:
+// Rank-r LoRA (r = 8, 16, 32 or 64) on the down and/or the gate_up
+// projection of every expert ("Add MXFP4 training support via a
+// dequantize-on-the-fly fallback", "What this does": adapters train on top
+// of the frozen MXFP4 base, whose backward only has to deliver input and
+// adapter gradients).  For the down projection, per expert e with
+// A_e [r, I], B_e [H, r] (the gate_up adapter is the same with x for a, h
+// for y, A_gu [r, H] and B_gu [2I, r], its delta added before the bias):
 //
 //   forward   v = a A_e^T                     (this file, lora_proj)
 //             y += s (v B_e^T)                (down GEMM epilogue, gemm_fwd.hip)
