@@ -588,6 +588,11 @@ __device__ __forceinline__ void bwd_down_body(
   const int wo = wave;
   const int l32 = lane & 31, hlf = lane >> 5;
   const int e = tl.expert;
+  // the routing weight of this lane's row in each block, loaded before the
+  // main loop (two dependent loads, in flight under it)
+  float wfv[NRB > 0 ? NRB : 1];
+#pragma unroll
+  for (int j = 0; j < NRB; ++j) wfv[j] = topk_w[sorted_rows[tl.row0 + min(32 * j + l32, tl.rows - 1)]];
   f32x16 acc[2][GRB];
   zero_acc(acc);
   g_loop<NRB>(g, lds, acc);
@@ -619,7 +624,7 @@ __device__ __forceinline__ void bwd_down_body(
         *reinterpret_cast<u32x4*>(hst + stg_off<256>(r, c)) =
             *reinterpret_cast<const u32x4*>(hsv + p * N2 + col);
       }
-      const float wf = topk_w[sorted_rows[tl.row0 + min(32 * pb + l32, tl.rows - 1)]];
+      const float wf = wfv[j];
       wave_lds_sync();
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
