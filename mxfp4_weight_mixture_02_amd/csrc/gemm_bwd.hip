@@ -512,6 +512,10 @@ __device__ __forceinline__ void bwd_gate_up_body(const GArgs& g, uint8_t* lds, c
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wo = wave;
   const int l32 = lane & 31, hlf = lane >> 5;
+  // each row block's flat row for this lane, loaded before the main loop
+  int32_t fv[NRB > 0 ? NRB : 1];
+#pragma unroll
+  for (int j = 0; j < NRB; ++j) fv[j] = sorted_rows[tl.row0 + min(32 * j + l32, tl.rows - 1)];
   f32x16 acc[2][GRB];
   zero_acc(acc);
   g_loop<NRB>(g, lds, acc);
@@ -522,7 +526,7 @@ __device__ __forceinline__ void bwd_gate_up_body(const GArgs& g, uint8_t* lds, c
 #pragma unroll
   for (int j = 0; j < NRB; ++j) {
     const int pb = j;
-    const int32_t f = sorted_rows[tl.row0 + min(32 * pb + l32, tl.rows - 1)];
+    const int32_t f = fv[j];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       float v[8];

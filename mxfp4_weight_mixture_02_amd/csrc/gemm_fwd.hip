@@ -684,11 +684,19 @@ __global__ __launch_bounds__(FwdShape<8>::NTHR) void down_kernel(
   uint8_t* yst = lds + wave * 4096;           // y strip: 32 rows x 64 bf16 (128-byte rows)
   float bv[FRB][4][4];
   load_bias_rows(bias, (int64_t)e * N + n0 + wcol + 4 * hlf, nblk, bv);
+  // the row blocks' flat rows and routing weights for this lane: one batch
+  // of loads each (not a dependent pair per block)
+  int32_t fv[4];
+  float wfv[4];
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb) fv[tb] = sorted_rows[tl.row0 + min(tb * 32 + l32, tl.rows - 1)];
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb) wfv[tb] = topk_w[fv[tb]];
 #pragma unroll
   for (int tb = 0; tb < 4; ++tb) {
     if (tb * 32 >= tl.rows) break;
-    const int32_t f = sorted_rows[tl.row0 + min(tb * 32 + l32, tl.rows - 1)];
-    const float wf = topk_w[f];
+    const int32_t f = fv[tb];
+    const float wf = wfv[tb];
 #pragma unroll
     for (int rb = 0; rb < FRB; ++rb)
 #pragma unroll
