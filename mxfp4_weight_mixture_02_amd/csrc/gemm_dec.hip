@@ -107,6 +107,20 @@ __global__ __launch_bounds__(512) void dec_kernel(
                  [&](int q, u32x4 v) { reinterpret_cast<u32x4*>(panel)[q] = v; });
   }
   const uint8_t* srow = panel + (live ? wave * 32 + l32 : 0) * (K / 32) + hlf;
+  // the epilogue's bias pairs and (down) the first group's flat row and
+  // routing weight, fetched now so they arrive while the codes stream (each
+  // was a memory round trip, two dependent ones for the weight, at the end)
+  u32x2 bwv[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    bwv[q] = (bias && live) ? *reinterpret_cast<const u32x2*>(bias + (int64_t)e * N + n0 + 8 * q + 4 * hlf)
+                            : u32x2{0u, 0u};
+  int64_t f0 = 0;
+  float wf0 = 0.0f;
+  if (!GATE_UP) {
+    f0 = sorted_rows[tl.row0 + min(l32, tl.rows - 1)];
+    wf0 = topk_w[f0];
+  }
 
   for (int g0 = 0; g0 < tl.rows; g0 += DG) {
     // stage the group's activation rows (only the ones that exist)
@@ -160,7 +174,7 @@ __global__ __launch_bounds__(512) void dec_kernel(
         for (int q = 0; q < 4; ++q) {
           const int nb = n0 + 8 * q + 4 * hlf;
           float v[4];
-          const u32x2 bw = bias ? *reinterpret_cast<const u32x2*>(bias + (int64_t)e * N + nb) : u32x2{0u, 0u};
+          const u32x2 bw = bwv[q];
 #pragma unroll
           for (int i = 0; i < 4; ++i)
             v[i] = acc[4 * q + i] + bf16_to_f32((uint16_t)(bw[i >> 1] >> (16 * (i & 1))));
@@ -174,8 +188,8 @@ __global__ __launch_bounds__(512) void dec_kernel(
             *reinterpret_cast<uint32_t*>(a_out + rho * I + nb / 2) =
                 pack_bf16x2(swiglu(v[0], v[1], alpha, limit), swiglu(v[2], v[3], alpha, limit));
           } else {
-            const int64_t f = sorted_rows[rho];
-            const float wf = topk_w[f];
+            const int64_t f = g0 == 0 ? f0 : (int64_t)sorted_rows[rho];
+            const float wf = g0 == 0 ? wf0 : topk_w[f];
             const u32x2 y = {pack_bf16x2(wf * v[0], wf * v[1]), pack_bf16x2(wf * v[2], wf * v[3])};
             *reinterpret_cast<u32x2*>(y_w + f * N + nb) = y;
           }
@@ -243,6 +257,16 @@ __global__ __launch_bounds__(64 * KW) void dec_ksplit_kernel(
   }
   const uint8_t* srow = panel + l32 * (K / 32) + hlf;
   const int npieces = Kp / 8;                  // staged pieces per row; those past K are zeros
+  // the epilogue's bias pair and (down) the first group's flat row and
+  // routing weight, fetched now so they arrive under the code loads
+  const int nbw = rb * 32 + 8 * wave + 4 * hlf;
+  const u32x2 bw0 = bias ? *reinterpret_cast<const u32x2*>(bias + (int64_t)e * N + nbw) : u32x2{0u, 0u};
+  int64_t f0 = 0;
+  float wf0 = 0.0f;
+  if (!GATE_UP) {
+    f0 = sorted_rows[tl.row0 + min(l32, tl.rows - 1)];
+    wf0 = topk_w[f0];
+  }
 
   for (int g0 = 0; g0 < tl.rows; g0 += DG) {
     const int ng = min(DG, tl.rows - g0);
@@ -303,9 +327,9 @@ __global__ __launch_bounds__(64 * KW) void dec_ksplit_kernel(
     // lane: column p = l32 of the group, weight rows nb + i
     const int p = g0 + l32;
     if (l32 < DG && p < tl.rows) {
-      const int nb = rb * 32 + 8 * wave + 4 * hlf;
+      const int nb = nbw;
       {
-        const u32x2 bw = bias ? *reinterpret_cast<const u32x2*>(bias + (int64_t)e * N + nb) : u32x2{0u, 0u};
+        const u32x2 bw = bw0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) v[i] += bf16_to_f32((uint16_t)(bw[i >> 1] >> (16 * (i & 1))));
       }
@@ -320,8 +344,8 @@ __global__ __launch_bounds__(64 * KW) void dec_ksplit_kernel(
         *reinterpret_cast<uint32_t*>(a_out + rho * I + nb / 2) =
             pack_bf16x2(swiglu(v[0], v[1], alpha, limit), swiglu(v[2], v[3], alpha, limit));
       } else {
-        const int64_t f = sorted_rows[rho];
-        const float wf = topk_w[f];
+        const int64_t f = g0 == 0 ? f0 : (int64_t)sorted_rows[rho];
+        const float wf = g0 == 0 ? wf0 : topk_w[f];
         const u32x2 y = {pack_bf16x2(wf * v[0], wf * v[1]), pack_bf16x2(wf * v[2], wf * v[3])};
         *reinterpret_cast<u32x2*>(y_w + f * N + nb) = y;
       }
