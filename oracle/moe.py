@@ -229,9 +229,11 @@ def _lora_vg(layer, e, xt):
     return xt @ bf16_to_f64(layer.lora_gu_A[e]).T
 
 
-def _gate_up_pre(layer, e, xt, Wgu):
-    """h = x Wgu^T + b (+ s (x A_gu^T) B_gu^T with the gate_up adapter)."""
-    h = xt @ Wgu.T + layer.gu_b(e)
+def _gate_up_pre(layer, e, xt, Wgu, xqt=None):
+    """h = x Wgu^T + b (+ s (x A_gu^T) B_gu^T with the gate_up adapter).
+    ``xqt``, when given, is the product's input under a block-scaled
+    activation format (gate_up_input); the adapter still reads x."""
+    h = (xt if xqt is None else xqt) @ Wgu.T + layer.gu_b(e)
     if layer.has_lora_gu:
         h = h + layer.lora_scale * _lora_vg(layer, e, xt) @ bf16_to_f64(layer.lora_gu_B[e]).T
     return h
@@ -310,7 +312,7 @@ def forward(layer: Layer, x_bits, tokens=None, routing: Routing | None = None, e
 
 def backward_dx(layer: Layer, x_bits, dy_bits, tokens=None, routing: Routing | None = None,
                 want_lora=True, experts=None, gu_grads: dict | None = None,
-                base_grads: dict | None = None):
+                base_grads: dict | None = None, act_format: str = "bf16"):
     """Gradient of L = sum(dY * out) with respect to x (and the LoRA
     adapters), base weights and biases frozen ([P1]: only the input and
     adapter gradients are needed for LoRA training).
@@ -336,6 +338,13 @@ def backward_dx(layer: Layer, x_bits, dy_bits, tokens=None, routing: Routing | N
       dW_gu_e = sum_f dh_f^T x_t [E, 2I, H],   db_gu_e = sum_f dh_f [E, 2I],
       dW_dn_e = sum_f g_y^T a_f  [E, H, I],    db_dn_e = sum_f g_y  [E, H].
 
+    ``act_format`` names the forward's gate_up input format
+    (gate_up_input).  The backward keeps the h that forward computed from
+    the quantized input and treats the quantizer as the identity
+    (straight-through): every product above that needs the gate_up input
+    (dW_gu, the adapters) reads x, and dX is the exact gradient of the
+    forward with the quantization error x_q - x held constant.
+
     ``tokens`` restricts dX to those tokens (then dA/dB cover only them).
     ``experts`` restricts the expert loop to those experts: dA/dB are then
     exact for them (zero elsewhere) and dX holds only their share, so the
@@ -359,6 +368,7 @@ def backward_dx(layer: Layer, x_bits, dy_bits, tokens=None, routing: Routing | N
     lora_gu = layer.has_lora_gu and want_lora and gu_grads is not None
     dAg = np.zeros(layer.lora_gu_A.shape) if lora_gu else None
     dBg = np.zeros(layer.lora_gu_B.shape) if lora_gu else None
+    xq = gate_up_input(x, act_format)
     base = base_grads is not None
     if base:
         E, I = layer.E, layer.I
@@ -374,7 +384,7 @@ def backward_dx(layer: Layer, x_bits, dy_bits, tokens=None, routing: Routing | N
         t = rows // k
         Wgu = layer.gate_up(e)
         Wd = layer.down(e)
-        h = _gate_up_pre(layer, e, x[t], Wgu)
+        h = _gate_up_pre(layer, e, x[t], Wgu, xq[t])
         g, u = h[:, 0::2], h[:, 1::2]
         a = swiglu(g, u, layer.alpha, layer.limit)
         y = a @ Wd.T + layer.dn_b(e)

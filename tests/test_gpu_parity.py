@@ -386,6 +386,36 @@ def test_block_scaled_activation_forward(fmt, shape):
         assert_close(g, plain, "out (mxfp8x2 vs bf16 oracle)")
 
 
+@pytest.mark.parametrize("fmt", ["mxfp8", "mxfp8x2"])
+@pytest.mark.parametrize("shape", [dict(T=300, H=192, I=320, E=3, k=2, lora_rank=16),
+                                   dict(T=1, H=128, I=96, E=8, k=4),
+                                   dict(T=40, H=128, I=96, E=4, k=2, lora_rank=8)])
+def test_block_scaled_forward_then_backward(fmt, shape):
+    # the dX backward run on a block-scaled forward's saved state (its h
+    # came from the quantized activations; the backward is straight-through)
+    # against the oracle's backward for the same format, with a down adapter
+    # and at a one-token decode size; the forward's out as well
+    s = syn.spec("tiny", **shape)
+    _say(f"block-scaled forward + backward {fmt} {shape}")
+    dl = device_layer(s)
+    dl.act_format = fmt
+    ol, _ = oracle_layer(s)
+    dl.lora_scale = ol.lora_scale = 2.0
+    xb = syn.tokens(s)
+    dyb = syn.upstream_grad(s)
+    out, sv = mxfp4_moe_forward(dl, bf16_tensor(xb).to(DEV), saved=True)
+    dx, dA, dB = mxfp4_moe_backward_dx(dl, sv, bf16_tensor(dyb).to(DEV))
+    torch.cuda.synchronize()
+    ref, r, _ = moe.forward(ol, xb, act_format=fmt)
+    assert_routing_equal(sv, r)
+    assert_close(to_f64(out), ref, f"out ({fmt})")
+    dref, dAref, dBref = moe.backward_dx(ol, xb, dyb, routing=r, act_format=fmt)
+    assert_close(to_f64(dx), dref, f"dX ({fmt})")
+    if ol.has_lora:
+        assert_close(to_f64(dA), dAref, f"dA ({fmt})")
+        assert_close(to_f64(dB), dBref, f"dB ({fmt})")
+
+
 def test_forward_is_deterministic():
     s = syn.spec("tiny", T=200, H=128, I=192, E=8, k=4)
     dl = device_layer(s)

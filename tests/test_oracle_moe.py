@@ -356,6 +356,58 @@ def test_backward_dx_finite_differences(x_scale):
     assert checked >= 6
 
 
+def test_backward_block_scaled_is_straight_through(monkeypatch):
+    # Under a block-scaled activation format the backward is the exact
+    # gradient of the forward with the quantization error c = x_q - x held
+    # constant.  Central differences of that surrogate (gate_up input x + c;
+    # the router and the adapter read x) must match dX and the down
+    # adapter's gradients, and dX must differ from the bf16 backward's by
+    # far more than the check's tolerance, so a backward that recomputed h
+    # from the unquantized x would fail.  The format enters only through
+    # gate_up_input (pinned in the MXFP8 tests); single-pass MXFP8 is the
+    # one whose error the differences can see (the hi + lo pair is
+    # accurate to about 2^-18 of a block's amax).  Elements spread over
+    # 2^-16..1 give every block an error.
+    fmt = "mxfp8"
+    s = syn.spec("tiny", lora_rank=8)
+    L, x, dY = _fd_layer(s, lora=True)
+    x = x * 2.0 ** np.random.default_rng(14).integers(-16, 1, x.shape)
+    dX, dA, dB = moe.backward_dx(L, x, dY, act_format=fmt)
+    plain, _, _ = moe.backward_dx(L, x, dY)
+    c = moe.gate_up_input(x, fmt) - x
+    assert np.abs(c).max() > 0
+    assert np.abs(dX - plain).max() > 1e-4 * np.abs(plain).max()
+    monkeypatch.setattr(moe, "gate_up_input", lambda xx, f: xx + c)
+    r0 = moe.route(L, x)
+    rng = np.random.default_rng(13)
+    checked = 0
+    for _ in range(8):
+        v = rng.standard_normal(x.shape)
+        eps = 1e-6
+        xp, xm = x + eps * v, x - eps * v
+        if not (np.array_equal(moe.route(L, xp).idx, r0.idx) and
+                np.array_equal(moe.route(L, xm).idx, r0.idx)):
+            continue
+        fd = (_loss(L, xp, dY) - _loss(L, xm, dY)) / (2 * eps)
+        an = float(np.sum(dX * v))
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (fd, an)
+        checked += 1
+    assert checked >= 4
+    for name, grad in (("lora_A", dA), ("lora_B", dB)):
+        base = getattr(L, name)
+        for _ in range(4):
+            pos = tuple(int(rng.integers(0, n)) for n in base.shape)
+            eps = 1e-4
+            Lp, Lm = copy.copy(L), copy.copy(L)
+            P, M = base.copy(), base.copy()
+            P[pos] += eps
+            M[pos] -= eps
+            setattr(Lp, name, P)
+            setattr(Lm, name, M)
+            fd = (_loss(Lp, x, dY) - _loss(Lm, x, dY)) / (2 * eps)
+            assert abs(fd - grad[pos]) <= 1e-6 * max(1.0, abs(fd)), (name, pos, fd, grad[pos])
+
+
 def test_backward_router_term_is_needed():
     # without the router path the gradient is wrong (finite differences
     # include it), and the expert path alone is non-zero: no silent gradient
