@@ -115,6 +115,15 @@ __device__ __forceinline__ void swiglu_grad(float g, float u, float da, float al
 typedef __attribute__((address_space(1))) const void* gptr_t;
 typedef __attribute__((address_space(3))) void* lptr_t;
 
+// 16 bytes from device memory through a global-address-space pointer.  A
+// generic pointer that the compiler cannot prove global (one chosen between
+// a tensor and g_zero64, say) becomes a flat load, which also counts as an
+// LDS operation: every wait for an LDS read would then wait for it as well,
+// draining the loads kept in flight for later steps.
+__device__ __forceinline__ u32x4 gload16(const void* p) {
+  return *(const __attribute__((address_space(1))) u32x4*)p;
+}
+
 // 64 zero bytes in device memory: the source of the loads that fall past
 // the end of a contraction whose length is an odd multiple of 32 (the last
 // 64-deep step's upper half), so that both MFMA operands are exact zeros

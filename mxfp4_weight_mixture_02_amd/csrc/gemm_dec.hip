@@ -39,7 +39,7 @@ __device__ __forceinline__ void dec_issue(DecChunk& b, const uint8_t* wrow, int 
   for (int i = 0; i < DD; ++i) {
     const int c = min(ch * DD + i, nsteps - 1);
     const uint8_t* ptr = (ztail && c == nsteps - 1) ? g_zero64 : wrow + c * 32;
-    b.c[i] = *reinterpret_cast<const u32x4*>(ptr);
+    b.c[i] = gload16(ptr);
   }
 }
 
@@ -248,7 +248,7 @@ __global__ __launch_bounds__(64 * KW) void dec_ksplit_kernel(
   for (int i = 0; i < KSTEPS; ++i) {
     const int c = c0 + min(i, cnt - 1);               // clamped: never past the row
     const uint8_t* ptr = (ztail && c == nsteps - 1) ? g_zero64 : wrow + c * 32;
-    cv[i] = *reinterpret_cast<const u32x4*>(ptr);
+    cv[i] = gload16(ptr);
   }
   {
     const u32x4* ps = reinterpret_cast<const u32x4*>(scales + ((int64_t)e * N + rb * 32) * (K / 32));

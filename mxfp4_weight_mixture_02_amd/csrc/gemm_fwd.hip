@@ -122,7 +122,7 @@ __device__ __forceinline__ void fwd_issue(const FwdPipe& p, Codes& codes, int c)
   // the counted waits below assume this issue order: activations, then codes
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int rb = 0; rb < FRB; ++rb) codes[SL][rb] = *reinterpret_cast<const u32x4*>(wp[rb]);
+  for (int rb = 0; rb < FRB; ++rb) codes[SL][rb] = gload16(wp[rb]);
 }
 
 template <int W, int SL, int NRB, class Codes>

@@ -55,8 +55,7 @@ __global__ __launch_bounds__(256) void lora_proj_kernel(
   // pieces 16 s + 8 hlf .. of step c, zeros past C
   auto ld = [&](const uint16_t* base, int c, int s) {
     const bool past = 64 * c + 16 * s >= C;
-    return *reinterpret_cast<const u32x4*>(past ? reinterpret_cast<const uint16_t*>(g_zero64)
-                                                : base + 64 * c + 16 * s);
+    return gload16(past ? reinterpret_cast<const uint16_t*>(g_zero64) : base + 64 * c + 16 * s);
   };
   // 64 columns per step, the next step's loads in flight during the MFMAs
   u32x4 a[2][4], b[2][NB][4];
