@@ -62,10 +62,10 @@ def parse():
 # only while both are unchanged.
 TRAFFIC = {
     # kernel: (source file, SHA-256 prefix of that file and of common.hpp, bytes per launch)
-    "gate_up": ("gemm_fwd.hip", "72721ac8fe41ab6a", "5d6169e00764c088", 591.9e6),
-    "down": ("gemm_fwd.hip", "72721ac8fe41ab6a", "5d6169e00764c088", 277.5e6),
-    "bwd_down": ("gemm_bwd.hip", "ee8d69f9d5fc8bcc", "5d6169e00764c088", 591.5e6),
-    "bwd_gate_up": ("gemm_bwd.hip", "ee8d69f9d5fc8bcc", "5d6169e00764c088", 793.6e6),
+    "gate_up": ("gemm_fwd.hip", "f519fc7214966982", "6b087c6cabe41278", 591.4e6),
+    "down": ("gemm_fwd.hip", "f519fc7214966982", "6b087c6cabe41278", 279.5e6),
+    "bwd_down": ("gemm_bwd.hip", "ee8d69f9d5fc8bcc", "6b087c6cabe41278", 591.6e6),
+    "bwd_gate_up": ("gemm_bwd.hip", "ee8d69f9d5fc8bcc", "6b087c6cabe41278", 794.0e6),
 }
 
 
