@@ -99,16 +99,20 @@ __device__ __forceinline__ float swiglu(float g, float u, float alpha, float lim
   return gc * sig * (uc + 1.0f);
 }
 
-// d/dg and d/du of swiglu times da; no gradient beyond a clamp bound.
+// d/dg and d/du of swiglu times da; no gradient beyond a clamp bound.  An
+// input lies within its bounds exactly when the clamp leaves it unchanged
+// (a NaN input is changed, so it gets no gradient either); alpha * gc is
+// shared by the sigmoid and the gate derivative, whose 1 + alpha gc (1 - s)
+// is one fused multiply-add.
 __device__ __forceinline__ void swiglu_grad(float g, float u, float da, float alpha, float limit,
                                             float* dg, float* du) {
-  float gc = fminf(g, limit);
-  float uc = fminf(fmaxf(u, -limit), limit);
-  float sig = sigmoid_hw(alpha * gc);
-  float dgc = da * (uc + 1.0f) * sig * (1.0f + alpha * gc * (1.0f - sig));
-  float duc = da * gc * sig;
-  *dg = (g <= limit) ? dgc : 0.0f;
-  *du = (u >= -limit && u <= limit) ? duc : 0.0f;
+  const float gc = fminf(g, limit);
+  const float uc = fminf(fmaxf(u, -limit), limit);
+  const float ag = alpha * gc;
+  const float sig = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(ag * -1.4426950408889634f));
+  const float ds = da * sig;
+  *dg = (gc == g) ? ds * (uc + 1.0f) * fmaf(ag, 1.0f - sig, 1.0f) : 0.0f;
+  *du = (uc == u) ? ds * gc : 0.0f;
 }
 
 // Global and LDS pointer types of the global -> LDS load builtin.

@@ -245,10 +245,13 @@ __device__ __forceinline__ void g_read_b(const GArgs& g, const uint8_t* __restri
     F.b[bi][j] = *reinterpret_cast<const bf16x8*>(st + g.boff[s] + j * 4096);
 }
 
-// row_newbcast:R -- lane R of each 16-lane row to the whole row
+// row_newbcast:R -- lane R of each 16-lane row to the whole row.  Every
+// lane has a valid source, so no "old" value is needed: the plain DPP move
+// leaves it undefined, where a defined one costs a register copy per
+// broadcast.
 template <int R>
 __device__ __forceinline__ uint32_t row_bcast(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x150 + R, 0xF, 0xF, false);
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x150 + R, 0xF, 0xF, false);
 }
 
 // Decode sub-step s's raw bytes into A-fragment slot ai: fragment 0 holds
@@ -612,13 +615,15 @@ __device__ __forceinline__ void bwd_down_body(
     const int pb = j;
     float dwp = 0.0f;
     if (active) {
+      // a pieces past I are staged as zeros, so the dw partial needs no
+      // per-column test (the accumulator columns there are finite copies)
 #pragma unroll
       for (int it = 0; it < 4; ++it) {
         const int r = 8 * it + (lane >> 3), c = lane & 7;
         const int64_t p = tl.row0 + min(32 * pb + r, tl.rows - 1);
-        const int col = min(ow + 8 * c, I - 8);
-        *reinterpret_cast<u32x4*>(ast + stg_off<128>(r, c)) =
-            *reinterpret_cast<const u32x4*>(asv + p * I + col);
+        const int col = ow + 8 * c;
+        const u32x4 av = *reinterpret_cast<const u32x4*>(asv + p * I + min(col, I - 8));
+        *reinterpret_cast<u32x4*>(ast + stg_off<128>(r, c)) = col < I ? av : u32x4{0u, 0u, 0u, 0u};
       }
 #pragma unroll
       for (int it = 0; it < 8; ++it) {
@@ -633,7 +638,6 @@ __device__ __forceinline__ void bwd_down_body(
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int cb = 2 * q + hlf;                    // 8-column chunk of the wave's 64
-        const int o = ow + 8 * cb;                     // first of this lane's 8 columns
         float v[8];
         cols8(acc, q, j, v);
         const u32x4 av = *reinterpret_cast<const u32x4*>(ast + stg_off<128>(l32, cb));
@@ -644,11 +648,11 @@ __device__ __forceinline__ void bwd_down_body(
           u32x4 out;
 #pragma unroll
           for (int m = 0; m < 4; ++m) {
-            const int c = 4 * half + m;                // column o + c
+            const int c = 4 * half + m;                // column ow + 8 cb + c
             const float du_ = v[c];
             const uint32_t aw = av[c >> 1];
             const float a_c = bf16_to_f32((uint16_t)((c & 1) ? (aw >> 16) : (aw & 0xFFFFu)));
-            dwp += (o + c < I) ? du_ * a_c : 0.0f;
+            dwp += du_ * a_c;
             const uint32_t hw = hv[m];
             float dg, dup;
             swiglu_grad(bf16_to_f32((uint16_t)(hw & 0xFFFFu)), bf16_to_f32((uint16_t)(hw >> 16)),
