@@ -101,17 +101,20 @@ __device__ __forceinline__ float swiglu(float g, float u, float alpha, float lim
 
 // d/dg and d/du of swiglu times da; no gradient beyond a clamp bound.  An
 // input lies within its bounds exactly when the clamp leaves it unchanged
-// (a NaN input is changed, so it gets no gradient either); alpha * gc is
-// shared by the sigmoid and the gate derivative, whose 1 + alpha gc (1 - s)
-// is one fused multiply-add.
+// (a NaN input never compares equal, so it gets no gradient either; the
+// gate's lower bound is the most negative finite float, so g = -inf, whose
+// sigmoid factor is 0 times an infinity, gets none too); the clamps are
+// single median-of-three operations, alpha * gc is shared by the
+// sigmoid and the gate derivative, and both (uc + 1) ds and
+// 1 + alpha gc (1 - s) are fused multiply-adds.
 __device__ __forceinline__ void swiglu_grad(float g, float u, float da, float alpha, float limit,
                                             float* dg, float* du) {
-  const float gc = fminf(g, limit);
-  const float uc = fminf(fmaxf(u, -limit), limit);
+  const float gc = __builtin_amdgcn_fmed3f(g, -3.402823466e38f, limit);
+  const float uc = __builtin_amdgcn_fmed3f(u, -limit, limit);
   const float ag = alpha * gc;
   const float sig = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(ag * -1.4426950408889634f));
   const float ds = da * sig;
-  *dg = (gc == g) ? ds * (uc + 1.0f) * fmaf(ag, 1.0f - sig, 1.0f) : 0.0f;
+  *dg = (gc == g) ? fmaf(ds, uc, ds) * fmaf(ag, 1.0f - sig, 1.0f) : 0.0f;
   *du = (uc == u) ? ds * gc : 0.0f;
 }
 
