@@ -95,6 +95,11 @@ __device__ __forceinline__ int x_swz(int p) { return (p & 7) ^ ((p >> 3) & 1); }
 struct GArgs {
   const uint16_t* xbase;    // activations (workgroup-uniform)
   uint32_t xoff[GXI];       // element offsets of the activation pieces this lane copies (step 0)
+  // buffer descriptors over the activations (xbytes from xbase), the
+  // expert's codes and its scales: the copies of every step but a half
+  // last one name a descriptor, the lane's fixed byte offset and the
+  // step's uniform offset, so they need no per-step vector arithmetic
+  __amdgpu_buffer_rsrc_t rx, rc, rs;
   const uint8_t* wcode;     // the expert's codes and scales (workgroup-uniform)
   const uint8_t* wscale;
   uint32_t coff[2];         // byte offsets of this lane's two 16-byte code pieces (step 0)
@@ -124,10 +129,13 @@ struct GFrags {
 // rowoff(p): element offset of activation row p (clamping rows past the
 // tile to a valid row).  C, O: contraction and output lengths; o0: the
 // workgroup's first output column.
+// Buffer descriptor word 3 for raw (untyped) dword access on this target.
+constexpr int BUF_RSRC_W3 = 0x00020000;
+
 template <class RowOff>
-__device__ __forceinline__ void g_setup(GArgs& g, const uint16_t* xbase, RowOff rowoff,
-                                        const uint8_t* wcode, const uint8_t* wscale, int C,
-                                        int O, int o0) {
+__device__ __forceinline__ void g_setup(GArgs& g, const uint16_t* xbase, uint32_t xbytes,
+                                        RowOff rowoff, const uint8_t* wcode,
+                                        const uint8_t* wscale, int C, int O, int o0) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wo = wave & 3;
@@ -142,6 +150,9 @@ __device__ __forceinline__ void g_setup(GArgs& g, const uint16_t* xbase, RowOff 
   }
   g.wcode = wcode;
   g.wscale = wscale;
+  g.rx = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(xbase), (short)0, (int)xbytes, BUF_RSRC_W3);
+  g.rc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(wcode), (short)0, C * (O / 2), BUF_RSRC_W3);
+  g.rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(wscale), (short)0, C * (O / 32), BUF_RSRC_W3);
   // codes: LDS slot 256 m + tid of the tile (copy m = 0, 1) is row c0 =
   // 32 m + tid / 8, slot tid % 8, holding 16-byte chunk j = (tid % 8) ^
   // (c0 % 8) (32 columns)
@@ -190,6 +201,21 @@ __device__ __forceinline__ void g_setup(GArgs& g, const uint16_t* xbase, RowOff 
 // Step k's tile into LDS stage st (GDMA loads of this wave).  In a half
 // last step the pieces past C are read from a block of zeros.
 __device__ __forceinline__ void g_dma(const GArgs& g, uint8_t* __restrict__ st, int k) {
+  if (!(g.half_last && k == g.nsteps - 1)) {
+#pragma unroll
+    for (int i = 0; i < GXI; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          g.rx, (lptr_t)(st + GCB + GSB + (g.wave * GXI + i) * 1024), 16, 2 * g.xoff[i],
+          k * (2 * GKC), 0, 0);
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(g.rc, (lptr_t)(st + (4 * m + g.wave) * 1024), 16,
+                                               g.coff[m], k * g.cstep, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(g.rs, (lptr_t)(st + GCB + (4 * m + g.wave) * 256), 1,
+                                               g.soff[m], k * g.sstep, 0, 0);
+    }
+    return;
+  }
   const uint16_t* xp[GXI];
   const uint8_t* cp[2];
   const uint8_t* sp[2];
@@ -567,7 +593,9 @@ __global__ __launch_bounds__(GTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
   // Wgu is stored [2I rows][H cols]: contraction over n (C = 2I), output h (O = H);
   // the activations are dh's rows in sorted order
   GArgs g;
-  g_setup(g, dh, [&](int p) { return (uint32_t)(tl.row0 + min(p, tl.rows - 1)) * (uint32_t)N2; },
+  // the tile's dh rows (a contiguous range in sorted order) from its first
+  g_setup(g, dh + (int64_t)tl.row0 * N2, (uint32_t)tl.rows * (uint32_t)N2 * 2u,
+          [&](int p) { return (uint32_t)min(p, tl.rows - 1) * (uint32_t)N2; },
           codes + (int64_t)tl.expert * N2 * (H / 2), scales + (int64_t)tl.expert * N2 * (H / 32),
           N2, H, o0);
   with_blocks<GRB>(live_blocks(tl.rows), [&](auto nrb) {
@@ -708,7 +736,8 @@ __global__ __launch_bounds__(GTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
   // Wd is stored [H rows][I cols]: contraction over h (C = H), output i (O =
   // I); the activations are the routed rows' tokens' dY rows
   GArgs g;
-  g_setup(g, dy,
+  // dy's token rows: T * H < 2^31, so every byte offset fits the descriptor
+  g_setup(g, dy, 0xFFFFFFFFu,
           [&](int p) {
             return (uint32_t)(sorted_rows[tl.row0 + min(p, tl.rows - 1)] / k) * (uint32_t)H;
           },
