@@ -100,7 +100,9 @@ struct FwdPipe {
 template <int W, int SL, class Codes>
 __device__ __forceinline__ void fwd_issue(const FwdPipe& p, Codes& codes, int c) {
   constexpr int XCH = FwdShape<W>::XCH;
-  const int wave = threadIdx.x >> 6;
+  // uniform by construction; read into a scalar so the copies' LDS bases
+  // (M0) are formed with scalar instructions
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint16_t* xp[XCH];
   const uint8_t* wp[FRB];
 #pragma unroll
