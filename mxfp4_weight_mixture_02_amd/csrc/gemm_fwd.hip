@@ -128,15 +128,18 @@ __device__ __forceinline__ void fwd_issue(const FwdPipe& p, Codes& codes, int c)
 }
 
 template <int W, int SL, int NRB, class Codes>
-__device__ __forceinline__ void fwd_compute(const FwdPipe& p, const Codes& codes, int c,
+__device__ __forceinline__ void fwd_compute(const FwdPipe& p, Codes& codes, int c,
                                             float (&sc)[FRB], f32x16 (&acc)[FRB][4]) {
+  constexpr int NST = FwdShape<W>::NST;
   const int lane = threadIdx.x & 63;
   const int l32 = lane & 31, hlf = lane >> 5;
   const uint8_t* st = p.xs + SL * XSTAGE;
   // Sub-step s's B-operand fragments and decoded weights are double
   // buffered: sub-step s + 1's LDS reads and decodes are issued while the
   // MFMAs of sub-step s run, so neither the LDS latency nor the conversions
-  // sit between two MFMAs.
+  // sit between two MFMAs.  The loads of step c + NST - 1 go out after
+  // sub-step 0's MFMAs, so their address arithmetic runs while those
+  // MFMAs execute instead of ahead of the step's first one.
   bf16x8 b[2][NRB], a[2][FRB];
   auto read_b = [&](int s, bf16x8(&bb)[NRB]) {
     const int g = 4 * hlf + s;
@@ -185,24 +188,29 @@ __device__ __forceinline__ void fwd_compute(const FwdPipe& p, const Codes& codes
       }
     }
     __builtin_amdgcn_sched_barrier(0);
+    if (s == 0) {
+      // the loads of step c + NST - 1 into the slot step c - 1 used (every
+      // wave passed the barrier after it)
+      fwd_issue<W, (SL + NST - 1) % NST>(p, codes, min(c + NST - 1, p.nsteps - 1));
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 #pragma unroll
   for (int rb = 0; rb < FRB; ++rb) sc[rb] = scale_operand(scn[rb]);
 }
 
-// One pipeline step: issue step c + NST - 1, compute step c, wait for this
-// wave's loads of step c + 1, barrier.  A lane issues LPS vector loads per
-// step (activations first, then codes), in step order, so after issuing
-// step c + NST - 1 the loads newer than all of step c + 1's number
-// LPS * (NST - 2).  Waiting for step c + 1's codes too (not only its
-// activations) keeps the compiler's own wait for the code registers from
-// falling back to a full drain at the top of the unrolled loop.
+// One pipeline step: compute step c (which issues step c + NST - 1 after
+// its first sub-step), wait for this wave's loads of step c + 1, barrier.
+// A lane issues LPS vector loads per step (activations first, then codes),
+// in step order, so after issuing step c + NST - 1 the loads newer than all
+// of step c + 1's number LPS * (NST - 2).  Waiting for step c + 1's codes
+// too (not only its activations) keeps the compiler's own wait for the
+// code registers from falling back to a full drain at the top of the
+// unrolled loop.
 template <int W, int SL, int NRB, class Codes>
 __device__ __forceinline__ void fwd_step(const FwdPipe& p, Codes& codes, int c, float (&sc)[FRB],
                                          f32x16 (&acc)[FRB][4]) {
   constexpr int NST = FwdShape<W>::NST;
-  fwd_issue<W, (SL + NST - 1) % NST>(p, codes, min(c + NST - 1, p.nsteps - 1));
-  __builtin_amdgcn_sched_barrier(0);
   fwd_compute<W, SL, NRB>(p, codes, c, sc, acc);
   __builtin_amdgcn_sched_barrier(0);
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(FwdShape<W>::LPS * (NST - 2)));
