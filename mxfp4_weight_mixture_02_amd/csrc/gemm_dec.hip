@@ -243,6 +243,51 @@ __global__ __launch_bounds__(64 * KW) void dec_ksplit_kernel(
   const int c0 = min(wave * per, nsteps), cnt = min(per, nsteps - c0);
   const int n = rb * 32 + l32;
   const uint8_t* wrow = codes + ((int64_t)e * N + n) * (K / 2) + hlf * 16;
+  const int npieces = Kp / 8;                  // staged pieces per row; those past K are zeros
+  // activation piece q of group g0: row q / npieces of the group, 8 columns;
+  // no branch around the load, so no merge of loaded registers forces a
+  // wait for every load in flight
+  auto xload = [&](int g0, int q) -> u32x4 {
+    const int pr = q / npieces, col = (q % npieces) * 8;
+    const int rt = tl.row0 + g0 + pr;
+    const int64_t sr = GATE_UP ? (int64_t)(sorted_rows[rt] / k) : (int64_t)rt;
+    const u32x4 v = gload16(src + sr * K + min(col, K - 8));
+    return col < K ? v : u32x4{0u, 0u, 0u, 0u};
+  };
+  // Loads in this order: the row indices, the scale-panel piece, the bias,
+  // up to XP activation pieces of the first group, then the codes.  The
+  // wait counter retires loads in issue order, so storing the staged pieces
+  // waits for them alone while the codes stay in flight (issued first, the
+  // codes would be waited for before the panel could be stored).
+  constexpr int XP = 4;
+  const int npanel = K / 16;                   // <= 192 pieces, one per thread
+  const int nx0 = min(DG, tl.rows) * npieces;
+  int xq[XP];
+  int64_t xsr[XP];
+#pragma unroll
+  for (int u = 0; u < XP; ++u) xq[u] = min(tid + u * 64 * KW, nx0 - 1);
+  int64_t f0 = 0;
+  float wf0 = 0.0f;
+  if (!GATE_UP) f0 = sorted_rows[tl.row0 + min(l32, tl.rows - 1)];
+#pragma unroll
+  for (int u = 0; u < XP; ++u) {
+    const int rt = tl.row0 + xq[u] / npieces;
+    xsr[u] = GATE_UP ? (int64_t)(sorted_rows[rt] / k) : (int64_t)rt;
+  }
+  const u32x4* ps = reinterpret_cast<const u32x4*>(scales + ((int64_t)e * N + rb * 32) * (K / 32));
+  const u32x4 pv = gload16(ps + min(tid, npanel - 1));
+  // the epilogue's bias pair, ahead of the codes so waiting for it does not
+  // wait for them
+  const int nbw = rb * 32 + 8 * wave + 4 * hlf;
+  const void* bptr = bias ? static_cast<const void*>(bias + (int64_t)e * N + nbw) : static_cast<const void*>(g_zero64);
+  const u32x2 bw0 = *(const __attribute__((address_space(1))) u32x2*)bptr;
+  __builtin_amdgcn_sched_barrier(0);
+  if (!GATE_UP) wf0 = topk_w[f0];
+  u32x4 xv[XP];
+#pragma unroll
+  for (int u = 0; u < XP; ++u)
+    xv[u] = gload16(src + xsr[u] * K + min((xq[u] % npieces) * 8, K - 8));
+  __builtin_amdgcn_sched_barrier(0);
   u32x4 cv[KSTEPS];
 #pragma unroll
   for (int i = 0; i < KSTEPS; ++i) {
@@ -250,38 +295,23 @@ __global__ __launch_bounds__(64 * KW) void dec_ksplit_kernel(
     const uint8_t* ptr = (ztail && c == nsteps - 1) ? g_zero64 : wrow + c * 32;
     cv[i] = gload16(ptr);
   }
-  {
-    const u32x4* ps = reinterpret_cast<const u32x4*>(scales + ((int64_t)e * N + rb * 32) * (K / 32));
-    stage_lds<1>(K / 16, tid, 64 * KW, [&](int q) { return ps[q]; },
-                 [&](int q, u32x4 v) { reinterpret_cast<u32x4*>(panel)[q] = v; });
-  }
+  __builtin_amdgcn_sched_barrier(0);
+  auto xstore = [&](int q, u32x4 v) {
+    *reinterpret_cast<u32x4*>(xs + (q / npieces) * xrow + (q % npieces) * 8) = v;
+  };
+  reinterpret_cast<u32x4*>(panel)[min(tid, npanel - 1)] = pv;   // the clamped threads repeat the last piece
+  // unconditional stores (a store under a branch lets the compiler sink its
+  // load there, behind the codes); the clamped threads repeat the last piece
+#pragma unroll
+  for (int u = 0; u < XP; ++u)
+    xstore(xq[u], (xq[u] % npieces) * 8 < K ? xv[u] : u32x4{0u, 0u, 0u, 0u});
+  for (int q = tid + XP * 64 * KW; q < nx0; q += 64 * KW) xstore(q, xload(0, q));
   const uint8_t* srow = panel + l32 * (K / 32) + hlf;
-  const int npieces = Kp / 8;                  // staged pieces per row; those past K are zeros
-  // the epilogue's bias pair and (down) the first group's flat row and
-  // routing weight, fetched now so they arrive under the code loads
-  const int nbw = rb * 32 + 8 * wave + 4 * hlf;
-  const u32x2 bw0 = bias ? *reinterpret_cast<const u32x2*>(bias + (int64_t)e * N + nbw) : u32x2{0u, 0u};
-  int64_t f0 = 0;
-  float wf0 = 0.0f;
-  if (!GATE_UP) {
-    f0 = sorted_rows[tl.row0 + min(l32, tl.rows - 1)];
-    wf0 = topk_w[f0];
-  }
 
   for (int g0 = 0; g0 < tl.rows; g0 += DG) {
     const int ng = min(DG, tl.rows - g0);
-    stage_lds<8>(
-        ng * npieces, tid, 64 * KW,
-        [&](int q) {
-          const int p = q / npieces, col = (q % npieces) * 8;
-          if (col >= K) return u32x4{0u, 0u, 0u, 0u};
-          const int rt = tl.row0 + g0 + p;
-          const int64_t sr = GATE_UP ? (int64_t)(sorted_rows[rt] / k) : (int64_t)rt;
-          return *reinterpret_cast<const u32x4*>(src + sr * K + col);
-        },
-        [&](int q, u32x4 v) {
-          *reinterpret_cast<u32x4*>(xs + (q / npieces) * xrow + (q % npieces) * 8) = v;
-        });
+    if (g0 > 0)
+      stage_lds<8>(ng * npieces, tid, 64 * KW, [&](int q) { return xload(g0, q); }, xstore);
     __syncthreads();
     f32x16 acc;
 #pragma unroll
