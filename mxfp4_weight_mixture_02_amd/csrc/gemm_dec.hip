@@ -99,44 +99,91 @@ __global__ __launch_bounds__(512) void dec_kernel(
   const int npieces = Kp / 8;                  // staged pieces per row; those past K are zeros
   uint8_t* panel = lds;
   uint16_t* xs = reinterpret_cast<uint16_t*>(lds + 32 * wpb * (K / 32));
-  {
-    const int r0 = rbk * wpb * 32;
-    const int n16 = min(32 * wpb, N - r0) * (K / 32) / 16;
-    const u32x4* ps = reinterpret_cast<const u32x4*>(scales + ((int64_t)e * N + r0) * (K / 32));
-    stage_lds<4>(n16, tid, blockDim.x, [&](int q) { return ps[q]; },
-                 [&](int q, u32x4 v) { reinterpret_cast<u32x4*>(panel)[q] = v; });
-  }
-  const uint8_t* srow = panel + (live ? wave * 32 + l32 : 0) * (K / 32) + hlf;
-  // the epilogue's bias pairs and (down) the first group's flat row and
-  // routing weight, fetched now so they arrive while the codes stream (each
-  // was a memory round trip, two dependent ones for the weight, at the end)
-  u32x2 bwv[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q)
-    bwv[q] = (bias && live) ? *reinterpret_cast<const u32x2*>(bias + (int64_t)e * N + n0 + 8 * q + 4 * hlf)
-                            : u32x2{0u, 0u};
+  const int nthr = blockDim.x;
+  // Load order: the row indices, the scale panel, the bias, a group's
+  // activation pieces, then the group's first chunk of codes, and only then
+  // the LDS stores of the staged pieces.  The wait counter retires loads in
+  // issue order, so the stores wait for the staged loads alone while the
+  // codes stay in flight.  Per thread at most PP panel pieces (wpb * K / 16
+  // over 64 * wpb threads) and XP activation pieces (DG <= 16 rows at 8
+  // waves, DG <= 8 at 4, of K <= DEC_MAXK): the launch keeps to these.  No
+  // load of this staging sits under a branch: at a branch merge the wait
+  // counter's bookkeeping takes the path with fewer loads in flight, so a
+  // conditional code issue would make the stores wait for the codes.
+  constexpr int PP = DEC_MAXK / 1024;
+  constexpr int XP = 12;
+  // gate_up: the token row of each group row, one per lane, shared by shuffle
+  auto group_rows = [&](int g0) -> int {
+    return GATE_UP ? sorted_rows[tl.row0 + g0 + min(lane, min(DG, tl.rows - g0) - 1)] / k : 0;
+  };
+  int grow = group_rows(0);
   int64_t f0 = 0;
   float wf0 = 0.0f;
-  if (!GATE_UP) {
-    f0 = sorted_rows[tl.row0 + min(l32, tl.rows - 1)];
-    wf0 = topk_w[f0];
+  if (!GATE_UP) f0 = sorted_rows[tl.row0 + min(l32, tl.rows - 1)];
+  const int r0 = rbk * wpb * 32;
+  const int n16 = min(32 * wpb, N - r0) * (K / 32) / 16;
+  const u32x4* ps = reinterpret_cast<const u32x4*>(scales + ((int64_t)e * N + r0) * (K / 32));
+  u32x4 pv[PP];
+#pragma unroll
+  for (int u = 0; u < PP; ++u) pv[u] = gload16(ps + min(tid + u * nthr, n16 - 1));
+  // the epilogue's bias pairs, fetched now so they arrive under the codes
+  u32x2 bwv[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const void* bp = (bias && live) ? static_cast<const void*>(bias + (int64_t)e * N + n0 + 8 * q + 4 * hlf)
+                                    : static_cast<const void*>(g_zero64);
+    bwv[q] = *(const __attribute__((address_space(1))) u32x2*)bp;
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  if (!GATE_UP) wf0 = topk_w[f0];
+  // activation piece q of group g0: group row q / npieces, 8 columns (zeros
+  // past K); no branch around the load
+  auto xsrc = [&](int g0, int q) -> const uint16_t* {
+    const int pr = q / npieces, col = (q % npieces) * 8;
+    const int64_t sr = GATE_UP ? (int64_t)__shfl(grow, pr) : (int64_t)(tl.row0 + g0 + pr);
+    return src + sr * K + min(col, K - 8);
+  };
+  auto xstore = [&](int q, u32x4 v) {
+    if ((q % npieces) * 8 >= K) v = u32x4{0u, 0u, 0u, 0u};
+    *reinterpret_cast<u32x4*>(xs + (q / npieces) * xrow + (q % npieces) * 8) = v;
+  };
+  u32x4 xv[XP];
+  auto xload_all = [&](int g0, int nx) {
+#pragma unroll
+    for (int u = 0; u < XP; ++u) xv[u] = gload16(xsrc(g0, min(tid + u * nthr, nx - 1)));
+  };
+  // unconditional stores (a store under a branch lets the compiler sink its
+  // load there, behind the codes); the clamped threads repeat the last piece
+  auto xstore_all = [&](int g0, int nx) {
+#pragma unroll
+    for (int u = 0; u < XP; ++u) xstore(min(tid + u * nthr, nx - 1), xv[u]);
+  };
+  const uint8_t* srow = panel + (live ? wave * 32 + l32 : 0) * (K / 32) + hlf;
+
+  DecChunk b0, b1;
+  {
+    const int nx = min(DG, tl.rows) * npieces;
+    xload_all(0, nx);
+    __builtin_amdgcn_sched_barrier(0);
+    dec_issue(b0, wrow, 0, nsteps, ztail);     // a wave past N reads rows it then leaves unused
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < PP; ++u)
+      reinterpret_cast<u32x4*>(panel)[min(tid + u * nthr, n16 - 1)] = pv[u];
+    xstore_all(0, nx);
   }
 
   for (int g0 = 0; g0 < tl.rows; g0 += DG) {
-    // stage the group's activation rows (only the ones that exist)
     const int ng = min(DG, tl.rows - g0);
-    stage_lds<8>(
-        ng * npieces, tid, blockDim.x,
-        [&](int q) {
-          const int p = q / npieces, col = (q % npieces) * 8;
-          if (col >= K) return u32x4{0u, 0u, 0u, 0u};
-          const int rt = tl.row0 + g0 + p;
-          const int64_t sr = GATE_UP ? (int64_t)(sorted_rows[rt] / k) : (int64_t)rt;
-          return *reinterpret_cast<const u32x4*>(src + sr * K + col);
-        },
-        [&](int q, u32x4 v) {
-          *reinterpret_cast<u32x4*>(xs + (q / npieces) * xrow + (q % npieces) * 8) = v;
-        });
+    if (g0 > 0) {
+      // the group's staging as the first one's, its codes issued in between
+      grow = group_rows(g0);
+      xload_all(g0, ng * npieces);
+      __builtin_amdgcn_sched_barrier(0);
+      dec_issue(b0, wrow, 0, nsteps, ztail);
+      __builtin_amdgcn_sched_barrier(0);
+      xstore_all(g0, ng * npieces);
+    }
     __syncthreads();
     f32x16 acc;
 #pragma unroll
@@ -144,8 +191,6 @@ __global__ __launch_bounds__(512) void dec_kernel(
     if (live) {
       // B-operand column l32 reads row min(l32 % DG, ng - 1)
       const uint16_t* xb = xs + min(l32 % DG, ng - 1) * xrow + 32 * hlf;
-      DecChunk b0, b1;
-      dec_issue(b0, wrow, 0, nsteps, ztail);
       for (int ch = 0; ch < nch; ch += 2) {
         dec_issue(b1, wrow, min(ch + 1, nch - 1), nsteps, ztail);
         dec_compute(b0, xb, srow, smax, ch, nsteps, acc);
@@ -401,6 +446,8 @@ static hipError_t dec_launch_stream(int64_t R, int max_tiles, int K, int N, hipS
   const int Kp = (K + 63) & ~63;
   const int wpb = R <= 64 ? 4 : 8;
   const int dg = R <= 64 ? (int)(R < 8 ? R : 8) : 16;   // an expert owns at most R rows
+  // the kernel stages a group in one pass of 12 pieces per thread: 2 * dg <= wpb * 4
+  static_assert(16 * (DEC_MAXK / 8) <= 12 * 512 && 8 * (DEC_MAXK / 8) <= 12 * 256, "staging pass");
   const int nblk = (N + 32 * wpb - 1) / (32 * wpb);
   const size_t lds = (size_t)32 * wpb * (K / 32) + (size_t)dg * (Kp + DEC_XPAD) * 2;
   // dynamic LDS above 64 KB (16 staged rows) must be allowed explicitly
