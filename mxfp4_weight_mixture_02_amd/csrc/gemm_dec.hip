@@ -26,6 +26,7 @@ int dec_max_k() { return DEC_MAXK; }
 
 constexpr int DD = 9;                    // K steps (64 wide) per streamed chunk
 
+
 struct DecChunk {
   u32x4 c[DD];
 };
@@ -45,9 +46,10 @@ __device__ __forceinline__ void dec_issue(DecChunk& b, const uint8_t* wrow, int 
 
 // srow: this lane's row of the scale panel in LDS (+ lane half); smax: the
 // largest index it may read (K / 32 - 1 - lane half)
+// cs: the first step staged in LDS (the activation segment's start)
 __device__ __forceinline__ void dec_compute(const DecChunk& b, const uint16_t* xb,
                                             const uint8_t* srow, int smax, int ch, int nsteps,
-                                            f32x16& acc) {
+                                            int cs, f32x16& acc) {
 #pragma unroll
   for (int i = 0; i < DD; ++i) {
     const int c = ch * DD + i;
@@ -56,7 +58,7 @@ __device__ __forceinline__ void dec_compute(const DecChunk& b, const uint16_t* x
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const bf16x8 a = as_bf16x8(dequant8_bf16(b.c[i][s], sc));
-        const bf16x8 bb = *reinterpret_cast<const bf16x8*>(xb + 64 * c + 8 * s);
+        const bf16x8 bb = *reinterpret_cast<const bf16x8*>(xb + 64 * (c - cs) + 8 * s);
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bb, acc, 0, 0, 0);
       }
     }
@@ -69,13 +71,15 @@ __global__ __launch_bounds__(512) void dec_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
     const uint16_t* __restrict__ bias, const float* __restrict__ topk_w,
     const int32_t* __restrict__ sorted_rows, const Tile* __restrict__ tiles,
-    const int32_t* __restrict__ num_tiles, int K, int N, int k, int DG, float alpha, float limit,
-    uint16_t* __restrict__ h_out, uint16_t* __restrict__ a_out, uint16_t* __restrict__ y_w,
-    const uint16_t* __restrict__ lora_B, const float* __restrict__ lora_v, float lora_scale,
-    int lora_r) {
+    const int32_t* __restrict__ num_tiles, int K, int N, int k, int DG, int seg_ch, float alpha,
+    float limit, uint16_t* __restrict__ h_out, uint16_t* __restrict__ a_out,
+    uint16_t* __restrict__ y_w, const uint16_t* __restrict__ lora_B,
+    const float* __restrict__ lora_v, float lora_scale, int lora_r) {
   // LDS: the scale panel of the workgroup's weight rows [32 * wpb][K / 32]
   // (one contiguous span of the scale tensor, copied in 16-byte pieces), then
-  // the activation group [DG][Kp + DEC_XPAD] bf16 (K rounded up to 64, zeros past K)
+  // the activation group [DG][xcols + DEC_XPAD] bf16: one segment of seg_ch
+  // chunks of K (xcols = seg_ch * DD * 64 columns, or K rounded up to 64 if
+  // that is less; zeros past K), restaged as the codes stream past it
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int wpb = blockDim.x >> 6;
   const int nblk = (N + 32 * wpb - 1) / (32 * wpb);
@@ -87,7 +91,8 @@ __global__ __launch_bounds__(512) void dec_kernel(
   const int l32 = lane & 31, hlf = lane >> 5;
   const int e = tl.expert;
   const int Kp = (K + 63) & ~63;               // K rounded up to whole 64-wide steps
-  const int xrow = Kp + DEC_XPAD;
+  const int scols = seg_ch * DD * 64;          // columns per staged segment
+  const int xrow = min(Kp, scols) + DEC_XPAD;
   const int n0 = (rbk * wpb + wave) * 32;      // this wave's first weight row
   const bool live = n0 < N;                    // N % 32 == 0: a block is all in or out
   const int n = live ? n0 + l32 : l32;
@@ -96,7 +101,8 @@ __global__ __launch_bounds__(512) void dec_kernel(
   const bool ztail = (K & 63) && hlf;          // this lane's half of the last step lies past K
   const int smax = K / 32 - 1 - hlf;
   const int nch = (nsteps + DD - 1) / DD;
-  const int npieces = Kp / 8;                  // staged pieces per row; those past K are zeros
+  // staged pieces per row of segment sg; those past K are zeros
+  auto spieces = [&](int sg) { return (min(Kp, (sg + 1) * scols) - sg * scols) / 8; };
   uint8_t* panel = lds;
   uint16_t* xs = reinterpret_cast<uint16_t*>(lds + 32 * wpb * (K / 32));
   const int nthr = blockDim.x;
@@ -105,8 +111,8 @@ __global__ __launch_bounds__(512) void dec_kernel(
   // the LDS stores of the staged pieces.  The wait counter retires loads in
   // issue order, so the stores wait for the staged loads alone while the
   // codes stay in flight.  Per thread at most PP panel pieces (wpb * K / 16
-  // over 64 * wpb threads) and XP activation pieces (DG <= 16 rows at 8
-  // waves, DG <= 8 at 4, of K <= DEC_MAXK): the launch keeps to these.  No
+  // over 64 * wpb threads) and XP activation pieces (DG * xcols / 8 over
+  // 64 * wpb threads): the launch keeps to these.  No
   // load of this staging sits under a branch: at a branch merge the wait
   // counter's bookkeeping takes the path with fewer loads in flight, so a
   // conditional code issue would make the stores wait for the codes.
@@ -136,41 +142,44 @@ __global__ __launch_bounds__(512) void dec_kernel(
   }
   __builtin_amdgcn_sched_barrier(0);
   if (!GATE_UP) wf0 = topk_w[f0];
-  // activation piece q of group g0: group row q / npieces, 8 columns (zeros
-  // past K); no branch around the load
-  auto xsrc = [&](int g0, int q) -> const uint16_t* {
-    const int pr = q / npieces, col = (q % npieces) * 8;
+  // activation piece q of group g0, segment sg: group row q / np, 8 columns
+  // from the segment's start (zeros past K); no branch around the load
+  auto xsrc = [&](int g0, int sg, int np, int q) -> const uint16_t* {
+    const int pr = q / np, col = sg * scols + (q % np) * 8;
     const int64_t sr = GATE_UP ? (int64_t)__shfl(grow, pr) : (int64_t)(tl.row0 + g0 + pr);
     return src + sr * K + min(col, K - 8);
   };
-  auto xstore = [&](int q, u32x4 v) {
-    if ((q % npieces) * 8 >= K) v = u32x4{0u, 0u, 0u, 0u};
-    *reinterpret_cast<u32x4*>(xs + (q / npieces) * xrow + (q % npieces) * 8) = v;
-  };
   u32x4 xv[XP];
-  auto xload_all = [&](int g0, int nx) {
+  auto xload_all = [&](int g0, int sg, int ng) {
+    const int np = spieces(sg), nx = ng * np;
 #pragma unroll
-    for (int u = 0; u < XP; ++u) xv[u] = gload16(xsrc(g0, min(tid + u * nthr, nx - 1)));
+    for (int u = 0; u < XP; ++u) xv[u] = gload16(xsrc(g0, sg, np, min(tid + u * nthr, nx - 1)));
   };
   // unconditional stores (a store under a branch lets the compiler sink its
   // load there, behind the codes); the clamped threads repeat the last piece
-  auto xstore_all = [&](int g0, int nx) {
+  auto xstore_all = [&](int sg, int ng) {
+    const int np = spieces(sg), nx = ng * np;
 #pragma unroll
-    for (int u = 0; u < XP; ++u) xstore(min(tid + u * nthr, nx - 1), xv[u]);
+    for (int u = 0; u < XP; ++u) {
+      const int q = min(tid + u * nthr, nx - 1);
+      const int col = (q % np) * 8;
+      *reinterpret_cast<u32x4*>(xs + (q / np) * xrow + col) =
+          sg * scols + col < K ? xv[u] : u32x4{0u, 0u, 0u, 0u};
+    }
   };
   const uint8_t* srow = panel + (live ? wave * 32 + l32 : 0) * (K / 32) + hlf;
 
   DecChunk b0, b1;
   {
-    const int nx = min(DG, tl.rows) * npieces;
-    xload_all(0, nx);
+    const int ng = min(DG, tl.rows);
+    xload_all(0, 0, ng);
     __builtin_amdgcn_sched_barrier(0);
     dec_issue(b0, wrow, 0, nsteps, ztail);     // a wave past N reads rows it then leaves unused
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < PP; ++u)
       reinterpret_cast<u32x4*>(panel)[min(tid + u * nthr, n16 - 1)] = pv[u];
-    xstore_all(0, nx);
+    xstore_all(0, ng);
   }
 
   for (int g0 = 0; g0 < tl.rows; g0 += DG) {
@@ -178,26 +187,36 @@ __global__ __launch_bounds__(512) void dec_kernel(
     if (g0 > 0) {
       // the group's staging as the first one's, its codes issued in between
       grow = group_rows(g0);
-      xload_all(g0, ng * npieces);
+      xload_all(g0, 0, ng);
       __builtin_amdgcn_sched_barrier(0);
       dec_issue(b0, wrow, 0, nsteps, ztail);
       __builtin_amdgcn_sched_barrier(0);
-      xstore_all(g0, ng * npieces);
+      xstore_all(0, ng);
     }
     __syncthreads();
     f32x16 acc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
-    if (live) {
-      // B-operand column l32 reads row min(l32 % DG, ng - 1)
-      const uint16_t* xb = xs + min(l32 % DG, ng - 1) * xrow + 32 * hlf;
-      for (int ch = 0; ch < nch; ch += 2) {
-        dec_issue(b1, wrow, min(ch + 1, nch - 1), nsteps, ztail);
-        dec_compute(b0, xb, srow, smax, ch, nsteps, acc);
-        if (ch + 1 >= nch) break;
-        dec_issue(b0, wrow, min(ch + 2, nch - 1), nsteps, ztail);
-        dec_compute(b1, xb, srow, smax, ch + 1, nsteps, acc);
+    // every wave runs the stream (the segment restaging has workgroup
+    // barriers); a wave past N computes on rows it leaves unused
+    // B-operand column l32 reads row min(l32 % DG, ng - 1)
+    const uint16_t* xb = xs + min(l32 % DG, ng - 1) * xrow + 32 * hlf;
+    for (int ch = 0; ch < nch; ch += 2) {
+      if (ch > 0 && ch % seg_ch == 0) {
+        // next segment (seg_ch is even): every wave is past the last one
+        __syncthreads();
+        xload_all(g0, ch / seg_ch, ng);
+        xstore_all(ch / seg_ch, ng);
+        __syncthreads();
       }
+      const int cs = (ch / seg_ch) * seg_ch * DD;
+      dec_issue(b1, wrow, min(ch + 1, nch - 1), nsteps, ztail);
+      dec_compute(b0, xb, srow, smax, ch, nsteps, cs, acc);
+      if (ch + 1 >= nch) break;
+      dec_issue(b0, wrow, min(ch + 2, nch - 1), nsteps, ztail);
+      dec_compute(b1, xb, srow, smax, ch + 1, nsteps, cs, acc);
+    }
+    if (live) {
       if (lora_B) {
         // + s v B_e^T over the rank (as the GEMMs' adapter term): A-operand
         // = B_e row n, B-operand column l32 = the group row it repeats
@@ -429,10 +448,11 @@ __global__ __launch_bounds__(64 * KW) void dec_ksplit_kernel(
   }
 }
 
-// Launch shape from the routed-row count: few rows -> 2 waves (64 weight
-// rows) per workgroup so the grid covers the chip; more rows -> up to 8
-// waves (256 weight rows) sharing one staging of the activation group (at
-// most R rows, 8 or 16 at a time).  Splitting K over waves measured slower.
+// Launch shape from the routed-row count: few rows -> 4 waves (128 weight
+// rows) per workgroup; more rows -> 8 waves (256 weight rows, gate_up) or 4
+// with the group staged in segments of K (down), sharing one staging of the
+// activation group (at most R rows, 8 or 16 at a time).  Splitting K over
+// waves measured slower.
 template <bool GATE_UP>
 static hipError_t dec_launch_stream(int64_t R, int max_tiles, int K, int N, hipStream_t s,
                              const uint16_t* src, const uint8_t* codes, const uint8_t* scales,
@@ -444,12 +464,21 @@ static hipError_t dec_launch_stream(int64_t R, int max_tiles, int K, int N, hipS
                              int lora_r) {
   if (K % 32 || K > DEC_MAXK || N % 32) return hipErrorInvalidValue;
   const int Kp = (K + 63) & ~63;
-  const int wpb = R <= 64 ? 4 : 8;
+  const int nch = (Kp / 64 + DD - 1) / DD;
+  // More rows: groups of 16.  gate_up: 8 waves share the whole-K staging
+  // (one workgroup per CU).  down: 4 waves, the group staged two chunks of
+  // K at a time, so that two workgroups fit a CU's LDS and one's staging and
+  // epilogue overlap the other's stream (measured faster for down, slower
+  // for gate_up, whose epilogue and grid are twice as large).
+  const bool seg = R > 64 && !GATE_UP;
+  const int wpb = R > 64 && GATE_UP ? 8 : 4;
   const int dg = R <= 64 ? (int)(R < 8 ? R : 8) : 16;   // an expert owns at most R rows
-  // the kernel stages a group in one pass of 12 pieces per thread: 2 * dg <= wpb * 4
-  static_assert(16 * (DEC_MAXK / 8) <= 12 * 512 && 8 * (DEC_MAXK / 8) <= 12 * 256, "staging pass");
+  const int seg_ch = seg ? 2 : nch;
+  const int xcols = seg_ch * DD * 64 < Kp ? seg_ch * DD * 64 : Kp;
+  // one staging pass of at most 12 pieces per thread, even segments
+  if (dg * (xcols / 8) > 12 * 64 * wpb || (seg_ch < nch && seg_ch % 2)) return hipErrorInvalidValue;
   const int nblk = (N + 32 * wpb - 1) / (32 * wpb);
-  const size_t lds = (size_t)32 * wpb * (K / 32) + (size_t)dg * (Kp + DEC_XPAD) * 2;
+  const size_t lds = (size_t)32 * wpb * (K / 32) + (size_t)dg * (xcols + DEC_XPAD) * 2;
   // dynamic LDS above 64 KB (16 staged rows) must be allowed explicitly
   static bool lds_attr_set = false;
   if (!lds_attr_set) {
@@ -461,7 +490,7 @@ static hipError_t dec_launch_stream(int64_t R, int max_tiles, int K, int N, hipS
   }
   const dim3 grid(max_tiles * nblk), block(64 * wpb);
 #define DEC_ARGS src, codes, scales, bias, topk_w, sorted_rows, tiles, num_tiles, K, N, k, dg, \
-                 alpha, limit, h_out, a_out, y_w, lora_B, lora_v, lora_scale, lora_r
+                 seg_ch, alpha, limit, h_out, a_out, y_w, lora_B, lora_v, lora_scale, lora_r
   hipLaunchKernelGGL((dec_kernel<GATE_UP>), grid, block, lds, s, DEC_ARGS);
 #undef DEC_ARGS
   return hipGetLastError();

@@ -249,6 +249,7 @@ def test_lora_empty_expert_gets_zero_gradients():
     (300, 32, 32),     # a single half step everywhere
     (5, 96, 160),      # R = 10: the K-split decode kernel
     (40, 160, 96),     # R = 80: the streaming decode kernel
+    (40, 160, 1248),   # R = 80, down K = 1248: staged in segments of 18 steps, a half 20th
 ])
 def test_hidden_sizes_odd_multiples_of_32(T, H, I):
     _say(f"odd multiples of 32: T={T} H={H} I={I}")
