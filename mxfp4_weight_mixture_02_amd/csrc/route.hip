@@ -324,7 +324,8 @@ __global__ __launch_bounds__(1024) void plan_kernel(
     int32_t* __restrict__ num_tiles) {
   __shared__ int32_t lg[PLAN_LOGITS];   // logit keys
   __shared__ double pst[PLAN_PARTS];
-  __shared__ float zs[16][8];
+  __shared__ float brs[256];             // the router bias (E <= 256)
+  __shared__ float zr[PLAN_MAX_ROWS];    // the selected logits, slot t * k + rank
   __shared__ int32_t ex[PLAN_MAX_ROWS];
   __shared__ int32_t cnt[256];
   __shared__ int32_t off[257];
@@ -340,6 +341,8 @@ __global__ __launch_bounds__(1024) void plan_kernel(
 #pragma unroll
     for (int u = 0; u < PLAN_PARTS / 1024; ++u)
       if (u < nu) v[u] = part[min(tid + u * 1024, P - 1)];
+    // the bias with the partials: one memory round trip for both
+    if (tid < E) brs[tid] = br ? br[tid] : 0.0f;
 #pragma unroll
     for (int u = 0; u < PLAN_PARTS / 1024; ++u)
       if (u < nu && tid + u * 1024 < P) pst[tid + u * 1024] = v[u];
@@ -356,7 +359,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(
         for (int j = 0; j < 16; ++j)
           if (h0 + j < hs_parts) sum += v[j];
       }
-      lg[q] = order_key((float)(sum + (br ? (double)br[q % E] : 0.0)));
+      lg[q] = order_key((float)(sum + (double)brs[q % E]));
     }
   } else {
     // few logits: G consecutive lanes per logit (G = 2 .. 16, G * TE <=
@@ -377,19 +380,44 @@ __global__ __launch_bounds__(1024) void plan_kernel(
       }
     }
     for (int m = 1; m < G; m <<= 1) sum += __shfl_xor(sum, m);
-    if (q < TE && g == 0) lg[q] = order_key((float)(sum + (br ? (double)br[q % E] : 0.0)));
+    if (q < TE && g == 0) lg[q] = order_key((float)(sum + (double)brs[q % E]));
   }
   __syncthreads();
-  if (E <= 64)
-    for (int t = wave; t < T; t += 16)
-      topk_rank<1>(lg + t * E, E, k, t, lane, topk_idx, topk_w, ex, nullptr, zs[wave]);
-  else if (E <= 128)
-    for (int t = wave; t < T; t += 16)
-      topk_rank<2>(lg + t * E, E, k, t, lane, topk_idx, topk_w, ex, nullptr, zs[wave]);
-  else
-    for (int t = wave; t < T; t += 16)
-      topk_rank<4>(lg + t * E, E, k, t, lane, topk_idx, topk_w, ex, nullptr, zs[wave]);
+  // Top-k of every token at once: thread (t, e) counts the experts that
+  // beat e in token t's row (a larger key, or an equal key and a lower
+  // index) and, ranked below k, fills slot t * k + rank.
+  for (int q = tid; q < TE; q += 1024) {
+    const int t = q / E, e = q - t * E;
+    const int32_t* row = lg + t * E;
+    const int32_t ve = row[e];
+    int r = 0;
+#pragma unroll 8
+    for (int e2 = 0; e2 < E; ++e2) {
+      const int32_t o = row[e2];
+      r += (int)(o > ve) | ((int)(o == ve) & (int)(e2 < e));
+    }
+    if (r < k) {
+      const int f = t * k + r;
+      topk_idx[f] = e;
+      ex[f] = e;
+      zr[f] = key_value(ve);
+    }
+  }
   __syncthreads();
+  // the softmax over each token's k selected logits (rank 0 is the largest),
+  // terms added in rank order
+  if (tid < R) {
+    const int t = tid / k, j = tid - t * k;
+    const float* z = zr + t * k;
+    const float sel0 = z[0];
+    float zsum = 0.0f, zl = 0.0f;
+    for (int i = 0; i < k; ++i) {
+      const float zi = expf(z[i] - sel0);
+      zsum += zi;
+      if (i == j) zl = zi;
+    }
+    topk_w[tid] = zl / zsum;
+  }
   for (int e = wave; e < E; e += 16) {
     int c = 0;
     for (int f0 = 0; f0 < R; f0 += 64) {
