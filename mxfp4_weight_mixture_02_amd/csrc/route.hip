@@ -489,18 +489,44 @@ __global__ __launch_bounds__(1024) void plan_kernel(
 //
 // write_tiles: tiles of at most mt sorted rows, expert by expert (the
 // forward's list: its GEMMs give each XCD a contiguous range of it).
+// Exclusive scan of cnt(e) over e < E (E <= 256) by one wave: lane l owns
+// e = 4l .. 4l + 3; out[e] = sum of cnt(e') over e' < e, out[E] = the total,
+// which is also returned to every lane.
+template <class Cnt>
+__device__ __forceinline__ int32_t wave_scan_experts(int E, int lane, Cnt cnt, int32_t* out) {
+  int32_t c[4], sum = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = 4 * lane + q;
+    c[q] = e < E ? cnt(e) : 0;
+    sum += c[q];
+  }
+  int32_t inc = sum;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int32_t o = __shfl_up(inc, d);
+    if (lane >= d) inc += o;
+  }
+  int32_t run = inc - sum;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = 4 * lane + q;
+    if (e < E) out[e] = run;
+    run += c[q];
+  }
+  const int32_t total = __shfl(inc, 63);
+  if (lane == 0) out[E] = total;
+  return total;
+}
+
 __device__ __forceinline__ void write_tiles(const int32_t* offs, int E, int mt, int32_t* start,
                                             Tile* __restrict__ tiles,
                                             int32_t* __restrict__ num_tiles) {
   const int tid = threadIdx.x;
-  if (tid == 0) {
-    int32_t run = 0;
-    for (int e = 0; e < E; ++e) {
-      start[e] = run;
-      run += (offs[e + 1] - offs[e] + mt - 1) / mt;
-    }
-    start[E] = run;
-    *num_tiles = run;
+  if (tid < 64) {
+    const int32_t total = wave_scan_experts(
+        E, tid, [&](int e) { return (offs[e + 1] - offs[e] + mt - 1) / mt; }, start);
+    if (tid == 0) *num_tiles = total;
   }
   __syncthreads();
   for (int e = tid; e < E; e += blockDim.x) {
@@ -568,25 +594,32 @@ __device__ __forceinline__ void write_dealt_tiles(const int32_t* offs, int E, in
                                                   int32_t* __restrict__ num_tiles) {
   const int tid = threadIdx.x;
   __shared__ TileDeal deal;
-  if (tid == 0) {
-    int32_t run = 0, ragged = 0;
-    for (int e = 0; e < E; ++e) {
-      const int32_t n = offs[e + 1] - offs[e];
-      start[e] = run;
-      run += n / mt;
-      ragged += (n % mt) != 0;
+  __shared__ int32_t rems[256];   // each expert's ragged tile rows (0: none)
+  for (int e = tid; e < E; e += blockDim.x) rems[e] = (offs[e + 1] - offs[e]) % mt;
+  if (tid < 64) {
+    const int lane = tid;
+    const int32_t run = wave_scan_experts(
+        E, lane, [&](int e) { return (offs[e + 1] - offs[e]) / mt; }, start);
+    int32_t rg = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = 4 * lane + q;
+      rg += e < E && (offs[e + 1] - offs[e]) % mt != 0;
     }
-    start[E] = run;
-    TileDeal d{run >> 3, run & 7, ragged};
-    int cnt[8], longest = 0;
-    for (int x = 0; x < 8; ++x) {
-      cnt[x] = d.full_count(x) + d.ragged_count(x);
-      longest = max(longest, cnt[x]);
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) rg += __shfl_xor(rg, m);
+    const TileDeal d{run >> 3, run & 7, rg};
+    // lane x < 8: XCD x's tile count; the longest share over the 8 lanes
+    const int cnt = lane < 8 ? d.full_count(lane) + d.ragged_count(lane) : 0;
+    int longest = cnt;
+#pragma unroll
+    for (int m = 1; m < 8; m <<= 1) longest = max(longest, __shfl_xor(longest, m));
+    if (lane < 8)
+      for (int q = cnt; q < longest; ++q) tiles[8 * q + lane] = Tile{0, 0, 0, 0};
+    if (lane == 0) {
+      *num_tiles = 8 * longest;
+      deal = d;
     }
-    for (int x = 0; x < 8; ++x)
-      for (int q = cnt[x]; q < longest; ++q) tiles[8 * q + x] = Tile{0, 0, 0, 0};
-    *num_tiles = 8 * longest;
-    deal = d;
   }
   __syncthreads();
   const TileDeal d = deal;
@@ -605,7 +638,7 @@ __device__ __forceinline__ void write_dealt_tiles(const int32_t* offs, int E, in
     if (rem) {
       int32_t rank = 0;
       for (int e2 = 0; e2 < E; ++e2) {
-        const int32_t r2 = (offs[e2 + 1] - offs[e2]) % mt;
+        const int32_t r2 = rems[e2];
         rank += (r2 > rem) || (r2 == rem && e2 < e);
       }
       tiles[d.ragged_slot(rank)] = Tile{e, o + nfull * mt, rem, tile_pos(0, 1)};
