@@ -275,9 +275,9 @@ __device__ __forceinline__ void topk_rank(const int32_t* lt, int E, int k, int t
   }
 }
 
-// RT tokens per workgroup, two per wave (rank-count selection on the
-// tokens' logits staged in LDS); writes the workgroup's expert histogram
-// for the scan.
+// RT tokens per workgroup (rank-count selection on the tokens' logits
+// staged in LDS; with E <= 64 all of the block's (token, expert) pairs at
+// once); writes the workgroup's expert histogram for the scan.
 template <int NQ>
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T, int E,
                                                    int k, int32_t* __restrict__ topk_idx,
@@ -285,6 +285,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
                                                    int32_t* __restrict__ blk_hist) {
   __shared__ int32_t hist[256];
   __shared__ int32_t lgs[RT * 256];   // logit keys
+  __shared__ float zr[RT * 8];        // the selected logits, [token][rank]
   __shared__ float zs[4][8];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t0 = blockIdx.x * RT;
@@ -300,12 +301,51 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
       if (tid + u * 256 < n) lgs[tid + u * 256] = order_key(v[u]);
   }
   __syncthreads();
+  if (NQ > 1) {
+    // many experts: two tokens per wave, each lane ranking NQ experts
+    // against the row read 32 keys at a time
 #pragma unroll
-  for (int q = 0; q < RT / 4; ++q) {
-    const int i = wave * (RT / 4) + q;
-    if (i < nt) topk_rank<NQ>(lgs + i * E, E, k, t0 + i, lane, topk_idx, topk_w, nullptr, hist, zs[wave]);
+    for (int q = 0; q < RT / 4; ++q) {
+      const int i = wave * (RT / 4) + q;
+      if (i < nt) topk_rank<NQ>(lgs + i * E, E, k, t0 + i, lane, topk_idx, topk_w, nullptr, hist, zs[wave]);
+    }
+    __syncthreads();
+    if (tid < E) blk_hist[(int64_t)blockIdx.x * E + tid] = hist[tid];
+    return;
+  }
+  // E <= 64: every (token, expert) pair of the block at once: the pair's
+  // rank among the token's row (a larger key, or an equal key and a lower
+  // index beats it); ranked below k it fills slot rank of the token
+  for (int q = tid; q < nt * E; q += 256) {
+    const int i = q / E, e = q - i * E;
+    const int32_t* row = lgs + i * E;
+    const int32_t ve = row[e];
+    int r = 0;
+#pragma unroll 8
+    for (int e2 = 0; e2 < E; ++e2) {
+      const int32_t o = row[e2];
+      r += (int)(o > ve) | ((int)(o == ve) & (int)(e2 < e));
+    }
+    if (r < k) {
+      topk_idx[(int64_t)(t0 + i) * k + r] = e;
+      zr[i * 8 + r] = key_value(ve);
+      atomicAdd(&hist[e], 1);   // counts only: order does not matter
+    }
   }
   __syncthreads();
+  // the softmax over each token's k selected logits, added in rank order
+  if (tid < nt * k) {
+    const int i = tid / k, j = tid - i * k;
+    const float* z = zr + i * 8;
+    const float sel0 = z[0];
+    float zsum = 0.0f, zl = 0.0f;
+    for (int m = 0; m < k; ++m) {
+      const float zm = expf(z[m] - sel0);
+      zsum += zm;
+      if (m == j) zl = zm;
+    }
+    topk_w[(int64_t)t0 * k + tid] = zl / zsum;
+  }
   if (tid < E) blk_hist[(int64_t)blockIdx.x * E + tid] = hist[tid];
 }
 
