@@ -110,17 +110,23 @@ __global__ __launch_bounds__(64 * LG_W) void logits_kernel(const uint16_t* __res
 // part[hs][t][e] is range hs's fp64 partial sum, and plan_kernel adds the
 // ranges in order, adds the bias and rounds once to fp32.  Within a range,
 // chunk c - c0 goes to accumulator (c - c0) mod 4 (four independent MFMA
-// chains instead of one), and the four are added in a fixed order.
-__global__ __launch_bounds__(64) void logits_part_kernel(const uint16_t* __restrict__ x,
-                                                         const float* __restrict__ wr, int T,
-                                                         int H, int E, int hs_parts,
-                                                         double* __restrict__ part) {
-  const int lane = threadIdx.x;
+// chains instead of one), and the four are added in a fixed order.  With
+// few ranges (many logits: the plan's LDS bounds ranges x logits) the
+// workgroup has LPW waves, each over a contiguous sub-range, whose sums
+// are added in wave order through LDS.
+constexpr int LPW = 4;
+__global__ __launch_bounds__(64 * LPW) void logits_part_kernel(const uint16_t* __restrict__ x,
+                                                               const float* __restrict__ wr, int T,
+                                                               int H, int E, int hs_parts,
+                                                               double* __restrict__ part) {
+  __shared__ double red[LPW][4][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const int ntt = (T + 15) / 16;
   const int hs = blockIdx.x % hs_parts, tile = blockIdx.x / hs_parts;
   const int tt = tile % ntt, et = tile / ntt;
   const int nch = H / LG_CH;
-  const int c0 = hs * nch / hs_parts, c1 = (hs + 1) * nch / hs_parts;
+  const int r0 = hs * nch / hs_parts, r1 = (hs + 1) * nch / hs_parts;
+  const int c0 = r0 + wave * (r1 - r0) / nw, c1 = r0 + (wave + 1) * (r1 - r0) / nw;
   const int i = lane & 15, kk = lane >> 4;
   const int t = min(tt * 16 + i, T - 1), e = min(et * 16 + i, E - 1);
   const uint16_t* xp = x + (int64_t)t * H + 8 * kk;
@@ -140,7 +146,19 @@ __global__ __launch_bounds__(64) void logits_part_kernel(const uint16_t* __restr
     for (int q = 0; q < LP_P; ++q)
       if (cb + q < c1) lg_mfma(xv[q], w0[q], w1[q], acc[q % 4]);
   }
-  const f64x4 sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  f64x4 sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  if (nw > 1) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[wave][r][lane] = sum[r];
+    __syncthreads();
+    if (wave > 0) return;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      double v = red[0][r][lane];
+      for (int w = 1; w < nw; ++w) v += red[w][r][lane];
+      sum[r] = v;
+    }
+  }
   const int ex = et * 16 + i;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
@@ -833,7 +851,9 @@ hipError_t launch_plan_logits(const uint16_t* x, const float* wr, int T, int H, 
   if (H % LG_CH) return hipErrorInvalidValue;
   const int hs = plan_hs_parts(T, E, H);
   const int blocks = ((T + 15) / 16) * ((E + 15) / 16) * hs;
-  hipLaunchKernelGGL(logits_part_kernel, dim3(blocks), dim3(64), 0, s, x, wr, T, H, E, hs, part);
+  // fewer than 32 ranges: 4 waves per range
+  hipLaunchKernelGGL(logits_part_kernel, dim3(blocks), dim3(hs < 32 ? 64 * LPW : 64), 0, s, x, wr,
+                     T, H, E, hs, part);
   return hipGetLastError();
 }
 
